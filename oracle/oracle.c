@@ -1,0 +1,407 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU oracle for the group-quantised
+ * 4-bit-weight matrix multiply (AWQ W4A16) and its QQQ-style W4A8 variant.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the reference that the GPU library is
+ * checked against.  Only the test suite, the smoke check and the benchmark's
+ * cpu_baseline leg may load it.  It shares no code, header, table or helper with
+ * the GPU library, and the GPU library never loads it.
+ *
+ * Everything is scalar C: integers for bit work, int64 for integer dot
+ * products, IEEE double for floating point.  No blocking, fusion or reordering:
+ * each output is the sum over k in increasing k order.  Threads only split the
+ * set of output columns.
+ *
+ * Sources (web pages; cited by title and passage):
+ *  [P1] vLLM pull request "Speed up AWQ 2.5x with updated kernel": the reviewer's
+ *       list of differences between the first-generation AWQ GEMM packing and
+ *       the newer one (the order map [0,2,4,6,1,3,5,7] of the old GEMM format),
+ *       and the dispatch snippet that passes (inputs, qweight, scales, qzeros,
+ *       group_size) to the kernels.
+ *  [P2] AutoAWQ pull request "Marlin symmetric quantization and inference": the
+ *       symmetric (no zero point) variant.
+ *  [P5] vLLM pull request "Support W4A8 quantization for vllm" (QQQ): the
+ *       dynamic per-token int8 activation quantisation (the dynamic_quant helper
+ *       in the consistency script: row abs-max divided by 127, round, clamp to
+ *       [-128,127]); the per-group quantiser's affine form scale*(q - zero);
+ *       the kernel review notes (int4 placed in the top nibble of an int8,
+ *       int32 global reduce, per-token s1 and per-channel s2 applied to the
+ *       output, per-group scales used in addition to per-channel ones).
+ *
+ * Readings where the pages leave a point open (each is listed in the design
+ * notes of the repository):
+ *  - Order map direction: nibble i (bits 4i..4i+3, word read as uint32) of a
+ *    packed AWQ word holds output column 8j + AWQ_ORDER[i].
+ *  - qzeros are packed exactly like qweight; a missing qzeros means z = 8.
+ *  - W4A8 weights: two's-complement int4 packed along K, nibble i of word
+ *    [kb][n] holds k = 8kb + K8_ORDER[i].
+ *  - W4A8 per-group scales s3 are small integers (1..16) so that q*s3 is an
+ *    int8 and the whole-K accumulation stays an exact int32; per-channel is the
+ *    case with no s3 (w8 = q).
+ *  - A row whose fp16 scale s1 rounds to zero quantises to all zeros.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_EINVAL (-1)
+
+/* [P1] first-generation AWQ GEMM order map: nibble i holds column 8j + AWQ_ORDER[i]. */
+static const int AWQ_ORDER[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+/* W4A8 K-packed layout: nibble i of word [kb][n] holds k = 8kb + K8_ORDER[i]. */
+static const int K8_ORDER[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+
+/* ------------------------------------------------------------------ */
+/* Floating-point formats, decoded from their IEEE-754 bit definitions. */
+
+/* binary16 -> double (exact). */
+double orc_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m | 0x400), e - 25); /* (1024 + m) * 2^(e-15-10) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 -> double (exact): the top 16 bits of a binary32. */
+double orc_bf16_to_f64(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* double -> binary16, round to nearest, ties to even (one rounding of the
+ * double value).  Overflow goes to infinity, NaN to the quiet NaN 0x7e00. */
+uint16_t orc_f64_to_f16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return 0x7e00;
+    if (a >= 65520.0) return sign | 0x7c00; /* halfway to 2^16 rounds up to inf */
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: the quantum is 2^-24; a result of 1024 quanta is the
+         * smallest normal, whose encoding is the same integer 0x400. */
+        double r = nearbyint(ldexp(a, 24));
+        return sign | (uint16_t)r;
+    }
+    int e2;
+    frexp(a, &e2);          /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;         /* unbiased exponent */
+    double r = nearbyint(ldexp(a, 10 - E)); /* significand in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return sign | 0x7c00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)r - 1024);
+}
+
+static double decode_act(uint16_t bits, int dtype) {
+    return dtype == 1 ? orc_bf16_to_f64(bits) : orc_f16_to_f64(bits);
+}
+
+/* ------------------------------------------------------------------ */
+/* Packing (AWQ N-packed and W4A8 K-packed).                          */
+
+/* unpack AWQ words [rows, cols/8] -> values [rows, cols] in 0..15. */
+int orc_unpack_n8(const int32_t *packed, uint8_t *vals, int64_t rows, int64_t cols) {
+    if (cols % 8) return ORC_EINVAL;
+    int64_t wc = cols / 8;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t j = 0; j < wc; j++) {
+            uint32_t w = (uint32_t)packed[r * wc + j];
+            for (int i = 0; i < 8; i++)
+                vals[r * cols + 8 * j + AWQ_ORDER[i]] = (uint8_t)((w >> (4 * i)) & 0xF);
+        }
+    return ORC_OK;
+}
+
+/* pack values [rows, cols] (expected 0..15) -> AWQ words [rows, cols/8].
+ * Values above 15 are clamped to 15; the number clamped is returned in
+ * *n_clamped (a missing clamp was a real packing bug reported in [P5]). */
+int orc_pack_n8(const uint8_t *vals, int32_t *packed, int64_t rows, int64_t cols,
+                int64_t *n_clamped) {
+    if (cols % 8) return ORC_EINVAL;
+    int64_t wc = cols / 8, bad = 0;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t j = 0; j < wc; j++) {
+            uint32_t w = 0;
+            for (int i = 0; i < 8; i++) {
+                unsigned v = vals[r * cols + 8 * j + AWQ_ORDER[i]];
+                if (v > 15) {
+                    v = 15;
+                    bad++;
+                }
+                w |= (uint32_t)v << (4 * i);
+            }
+            packed[r * wc + j] = (int32_t)w;
+        }
+    if (n_clamped) *n_clamped = bad;
+    return ORC_OK;
+}
+
+static int sext4(unsigned v) { return (int)(v ^ 8u) - 8; }
+
+/* unpack W4A8 words [K/8, N] -> int4 values [K, N] in -8..7. */
+int orc_unpack_k8(const int32_t *packed, int8_t *vals, int64_t K, int64_t N) {
+    if (K % 8) return ORC_EINVAL;
+    for (int64_t kb = 0; kb < K / 8; kb++)
+        for (int64_t n = 0; n < N; n++) {
+            uint32_t w = (uint32_t)packed[kb * N + n];
+            for (int i = 0; i < 8; i++)
+                vals[(8 * kb + K8_ORDER[i]) * N + n] = (int8_t)sext4((w >> (4 * i)) & 0xF);
+        }
+    return ORC_OK;
+}
+
+/* pack int4 values [K, N] (expected -8..7) -> W4A8 words [K/8, N]; out-of-range
+ * values are clamped and counted. */
+int orc_pack_k8(const int8_t *vals, int32_t *packed, int64_t K, int64_t N, int64_t *n_clamped) {
+    if (K % 8) return ORC_EINVAL;
+    int64_t bad = 0;
+    for (int64_t kb = 0; kb < K / 8; kb++)
+        for (int64_t n = 0; n < N; n++) {
+            uint32_t w = 0;
+            for (int i = 0; i < 8; i++) {
+                int v = vals[(8 * kb + K8_ORDER[i]) * N + n];
+                if (v < -8) { v = -8; bad++; }
+                if (v > 7) { v = 7; bad++; }
+                w |= ((uint32_t)v & 0xFu) << (4 * i);
+            }
+            packed[kb * N + n] = (int32_t)w;
+        }
+    if (n_clamped) *n_clamped = bad;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* W4A16: Y = X . dequant(qweight, qzeros, scales),  w = (q - z) * s.  */
+
+typedef struct {
+    const double *x; /* [M, K], decoded activations */
+    const int32_t *qweight, *qzeros;
+    const uint16_t *scales;
+    int64_t M, N, K;
+    int G, dtype;
+    double *y;          /* [M, N] */
+    int64_t j0, j1;     /* word-column range [j0, j1) handled by this thread */
+} w4a16_job;
+
+/* Dequantise the 8 columns packed in word-column j into w[8][K] (double). */
+static void dequant_word_column(const w4a16_job *t, int64_t j, double *w) {
+    int64_t wc = t->N / 8;
+    for (int64_t k = 0; k < t->K; k++) {
+        int64_t g = k / t->G;
+        uint32_t qw = (uint32_t)t->qweight[k * wc + j];
+        uint32_t zw = t->qzeros ? (uint32_t)t->qzeros[g * wc + j] : 0x88888888u;
+        for (int i = 0; i < 8; i++) {
+            int col = AWQ_ORDER[i];
+            int q = (int)((qw >> (4 * i)) & 0xF);
+            int z = (int)((zw >> (4 * i)) & 0xF);
+            double s = decode_act(t->scales[g * t->N + 8 * j + col], t->dtype);
+            w[col * t->K + k] = (double)(q - z) * s;
+        }
+    }
+}
+
+static void *w4a16_worker(void *arg) {
+    w4a16_job *t = (w4a16_job *)arg;
+    double *w = (double *)malloc(sizeof(double) * 8 * (size_t)t->K);
+    if (!w) return (void *)1;
+    for (int64_t j = t->j0; j < t->j1; j++) {
+        dequant_word_column(t, j, w);
+        for (int c = 0; c < 8; c++) {
+            const double *wc = w + (size_t)c * t->K;
+            for (int64_t m = 0; m < t->M; m++) {
+                const double *xr = t->x + m * t->K;
+                double acc = 0.0;
+                for (int64_t k = 0; k < t->K; k++) acc += xr[k] * wc[k];
+                t->y[m * t->N + 8 * j + c] = acc;
+            }
+        }
+    }
+    free(w);
+    return NULL;
+}
+
+static int check_w4a16_shape(int64_t M, int64_t N, int64_t K, int G) {
+    if (M < 0 || N <= 0 || K <= 0 || G <= 0) return ORC_EINVAL;
+    if (N % 8 || K % G) return ORC_EINVAL;
+    return ORC_OK;
+}
+
+/* Y64[m,n] = sum_k x[m,k] * (q[k,n] - z[k/G,n]) * s[k/G,n], all in double.
+ * x, scales: fp16 (dtype 0) or bf16 (dtype 1) bit patterns.  qzeros may be NULL
+ * (symmetric, z = 8). */
+int orc_w4a16(const uint16_t *x, const int32_t *qweight, const uint16_t *scales,
+              const int32_t *qzeros, int64_t M, int64_t N, int64_t K, int G, int dtype,
+              double *y, int nthreads) {
+    if (check_w4a16_shape(M, N, K, G)) return ORC_EINVAL;
+    if (nthreads < 1) nthreads = 1;
+    double *xd = (double *)malloc(sizeof(double) * (size_t)(M * K + 1));
+    if (!xd) return ORC_EINVAL;
+    for (int64_t i = 0; i < M * K; i++) xd[i] = decode_act(x[i], dtype);
+    int64_t wc = N / 8;
+    if (nthreads > wc) nthreads = (int)wc;
+    w4a16_job *jobs = (w4a16_job *)calloc((size_t)nthreads, sizeof(w4a16_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    int rc = ORC_OK;
+    for (int i = 0; i < nthreads; i++) {
+        w4a16_job *t = &jobs[i];
+        t->x = xd; t->qweight = qweight; t->qzeros = qzeros; t->scales = scales;
+        t->M = M; t->N = N; t->K = K; t->G = G; t->dtype = dtype; t->y = y;
+        t->j0 = wc * i / nthreads;
+        t->j1 = wc * (i + 1) / nthreads;
+    }
+    for (int i = 1; i < nthreads; i++) pthread_create(&th[i], NULL, w4a16_worker, &jobs[i]);
+    if (w4a16_worker(&jobs[0])) rc = ORC_EINVAL;
+    for (int i = 1; i < nthreads; i++) {
+        void *r;
+        pthread_join(th[i], &r);
+        if (r) rc = ORC_EINVAL;
+    }
+    free(th); free(jobs); free(xd);
+    return rc;
+}
+
+/* The dequantised weight matrix W[k,n] = (q - z) * s in double, [K, N]. */
+int orc_dequant(const int32_t *qweight, const uint16_t *scales, const int32_t *qzeros,
+                int64_t N, int64_t K, int G, int dtype, double *w_out) {
+    if (check_w4a16_shape(0, N, K, G)) return ORC_EINVAL;
+    w4a16_job t;
+    memset(&t, 0, sizeof t);
+    t.qweight = qweight; t.qzeros = qzeros; t.scales = scales;
+    t.N = N; t.K = K; t.G = G; t.dtype = dtype;
+    double *w = (double *)malloc(sizeof(double) * 8 * (size_t)K);
+    if (!w) return ORC_EINVAL;
+    for (int64_t j = 0; j < N / 8; j++) {
+        dequant_word_column(&t, j, w);
+        for (int c = 0; c < 8; c++)
+            for (int64_t k = 0; k < K; k++) w_out[k * N + 8 * j + c] = w[(size_t)c * K + k];
+    }
+    free(w);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* W4A8 (QQQ): per-token int8 activations, int4 weights, exact integer  */
+/* accumulation, output scaled by s1[m] * s2[n].                        */
+
+/* Dynamic per-token quantisation of fp16 activations [M, K] ([P5], the
+ * dynamic_quant helper):
+ *   amax  = max_k |x[m,k]|                         (exact in fp16)
+ *   s1    = float( fp16( float(amax) / 127 ) )      (the quotient is taken on
+ *                                                    the fp16 tensor, then widened)
+ *   a8    = clamp( round_half_even( float(x) / s1 ), -128, 127 )   (fp32 divide)
+ * A row with s1 == 0 gives a8 = 0. */
+int orc_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *a8, float *s1) {
+    if (M < 0 || K <= 0) return ORC_EINVAL;
+    for (int64_t m = 0; m < M; m++) {
+        const uint16_t *row = x + m * K;
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double v = fabs(orc_f16_to_f64(row[k]));
+            if (v > amax) amax = v;
+        }
+        float q32 = (float)amax / 127.0f;                  /* fp32, correctly rounded */
+        float s = (float)orc_f16_to_f64(orc_f64_to_f16((double)q32)); /* to fp16 and back */
+        s1[m] = s;
+        for (int64_t k = 0; k < K; k++) {
+            if (s == 0.0f) {
+                a8[m * K + k] = 0;
+                continue;
+            }
+            float xf = (float)orc_f16_to_f64(row[k]);
+            float r = rintf(xf / s); /* round half to even (default rounding mode) */
+            if (r < -128.0f) r = -128.0f;
+            if (r > 127.0f) r = 127.0f;
+            a8[m * K + k] = (int8_t)r;
+        }
+    }
+    return ORC_OK;
+}
+
+typedef struct {
+    const int8_t *a8;
+    const int32_t *b;
+    const float *s1;
+    const uint16_t *s2, *s3;
+    int64_t M, N, K;
+    int G;
+    int64_t *acc;
+    double *y;
+    int64_t n0, n1;
+    int err;
+} w4a8_job;
+
+static void *w4a8_worker(void *arg) {
+    w4a8_job *t = (w4a8_job *)arg;
+    int64_t K = t->K, N = t->N;
+    int *w8 = (int *)malloc(sizeof(int) * (size_t)K);
+    if (!w8) { t->err = 1; return NULL; }
+    for (int64_t n = t->n0; n < t->n1; n++) {
+        /* dequantise column n to int8 weights w8[k] = q[k,n] (* s3[k/G,n]) */
+        for (int64_t kb = 0; kb < K / 8; kb++) {
+            uint32_t w = (uint32_t)t->b[kb * N + n];
+            for (int i = 0; i < 8; i++) {
+                int64_t k = 8 * kb + K8_ORDER[i];
+                int q = sext4((w >> (4 * i)) & 0xF);
+                int mult = 1;
+                if (t->s3) {
+                    double s3 = orc_f16_to_f64(t->s3[(k / t->G) * N + n]);
+                    mult = (int)s3;
+                    if ((double)mult != s3 || mult < 1 || mult > 16) { t->err = 1; mult = 0; }
+                }
+                w8[k] = q * mult;
+            }
+        }
+        double s2 = orc_f16_to_f64(t->s2[n]);
+        for (int64_t m = 0; m < t->M; m++) {
+            const int8_t *ar = t->a8 + m * K;
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; k++) acc += (int64_t)ar[k] * (int64_t)w8[k];
+            if (t->acc) t->acc[m * N + n] = acc;
+            if (t->y) t->y[m * N + n] = (double)acc * (double)t->s1[m] * s2;
+        }
+    }
+    free(w8);
+    return NULL;
+}
+
+/* acc[m,n] = sum_k a8[m,k] * w8[k,n]  (int64), with w8 = q for per-channel
+ * weights (s3 == NULL) or w8 = q * s3[k/G, n] for per-group weights, and
+ * Y64[m,n] = acc * s1[m] * s2[n] in double.  Either output may be NULL. */
+int orc_w4a8(const int8_t *a8, const int32_t *b, const float *s1, const uint16_t *s2,
+             const uint16_t *s3, int64_t M, int64_t N, int64_t K, int G, int64_t *acc,
+             double *y, int nthreads) {
+    if (M < 0 || N <= 0 || K <= 0 || K % 8) return ORC_EINVAL;
+    if (s3 && (G <= 0 || K % G)) return ORC_EINVAL;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > N) nthreads = (int)N;
+    w4a8_job *jobs = (w4a8_job *)calloc((size_t)nthreads, sizeof(w4a8_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    for (int i = 0; i < nthreads; i++) {
+        w4a8_job *t = &jobs[i];
+        t->a8 = a8; t->b = b; t->s1 = s1; t->s2 = s2; t->s3 = s3;
+        t->M = M; t->N = N; t->K = K; t->G = G; t->acc = acc; t->y = y;
+        t->n0 = N * i / nthreads;
+        t->n1 = N * (i + 1) / nthreads;
+    }
+    for (int i = 1; i < nthreads; i++) pthread_create(&th[i], NULL, w4a8_worker, &jobs[i]);
+    w4a8_worker(&jobs[0]);
+    int rc = ORC_OK;
+    for (int i = 1; i < nthreads; i++) pthread_join(th[i], NULL);
+    for (int i = 0; i < nthreads; i++)
+        if (jobs[i].err) rc = ORC_EINVAL;
+    free(th); free(jobs);
+    return rc;
+}

@@ -1,0 +1,57 @@
+"""Plant mistakes in copies of the oracle (on the CPU) and check the pins catch them.
+
+Each mutant is oracle.c with one textual change, compiled into a temporary
+directory.  A mutant that no pin rejects means the pins are too weak."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "order_map_other_reading": ("static const int AWQ_ORDER[8] = {0, 2, 4, 6, 1, 3, 5, 7};",
+                                "static const int AWQ_ORDER[8] = {0, 4, 1, 5, 2, 6, 3, 7};"),
+    "zero_point_dropped": ("w[col * t->K + k] = (double)(q - z) * s;",
+                           "w[col * t->K + k] = (double)(q) * s;"),
+    "zero_point_sign": ("w[col * t->K + k] = (double)(q - z) * s;",
+                        "w[col * t->K + k] = (double)(z - q) * s;"),
+    "group_index": ("int64_t g = k / t->G;", "int64_t g = (k / t->G) / 2;"),
+    "scale_column_index": ("t->scales[g * t->N + 8 * j + col]", "t->scales[g * t->N + 8 * j + i]"),
+    "matmul_dropped_term": ("for (int64_t k = 0; k < t->K; k++) acc += xr[k] * wc[k];",
+                            "for (int64_t k = 1; k < t->K; k++) acc += xr[k] * wc[k];"),
+    "k8_order": ("static const int K8_ORDER[8] = {0, 4, 1, 5, 2, 6, 3, 7};",
+                 "static const int K8_ORDER[8] = {0, 1, 2, 3, 4, 5, 6, 7};"),
+    "int4_offset_binary": ("static int sext4(unsigned v) { return (int)(v ^ 8u) - 8; }",
+                           "static int sext4(unsigned v) { return (int)v - 8; }"),
+    "round_half_away": ("float r = rintf(xf / s);", "float r = roundf(xf / s);"),
+    "s1_not_fp16": ("float s = (float)orc_f16_to_f64(orc_f64_to_f16((double)q32));",
+                    "float s = q32;"),
+    "clamp_low_bound": ("if (r < -128.0f) r = -128.0f;", "if (r < -127.0f) r = -127.0f;"),
+    "group_scale_dropped": ("w8[k] = q * mult;", "w8[k] = q;"),
+    "w4a8_s1_dropped": ("(double)acc * (double)t->s1[m] * s2;", "(double)acc * s2;"),
+    "f16_subnormal_exponent": ("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);"),
+    "f16_ties_away": ("double r = nearbyint(ldexp(a, 10 - E));",
+                      "double r = floor(ldexp(a, 10 - E) + 0.5);"),
+    "pack_no_clamp": ("if (v > 15) {\n                    v = 15;", "if (v > 15) {\n                    v = v & 15;"),
+    "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mpath = tmp_path / "oracle_mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = oracle.compile_oracle(str(mpath), str(tmp_path / "libmut.so"))
+    mut = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mut)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
