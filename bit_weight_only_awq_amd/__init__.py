@@ -1,0 +1,12 @@
+"""MI355X (gfx950) 4-bit-weight GEMM library: AWQ W4A16 GEMV/GEMM and QQQ-style W4A8.
+
+The compute lives in libawq4.so (hand-written HIP, C ABI in include/awq4.h);
+this package is its thin torch binding.  Importing the package does not need
+a GPU; calling an op needs the built library and a gfx950 device.
+"""
+from ._lib import AWQError, lib  # noqa: F401
+from .ops import (gemm_w4a16, gemv_w4a16, linear_w4a16, linear_w4a8, pack, quant_act,  # noqa: F401
+                  unpack, w4a8_gemm, workspace_bytes)
+
+__all__ = ["AWQError", "lib", "gemm_w4a16", "gemv_w4a16", "linear_w4a16", "linear_w4a8", "pack", "quant_act",
+           "unpack", "w4a8_gemm", "workspace_bytes"]

@@ -1,0 +1,261 @@
+// api.cpp -- the extern "C" entry points declared in include/awq4.h.
+//
+// Every entry point validates its arguments with pure host code first (no HIP
+// call, so validation works without a GPU and a rejected call writes
+// nothing), then plans the launch as a pure function of the shape, and only
+// then enqueues kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/awq4.h"
+#include "launch.hpp"
+
+namespace awq4 {
+
+static constexpr int64_t kMaxDim = int64_t(1) << 20;
+static constexpr int kTargetWorkgroups = 512;  // 256 CUs x 2 workgroups of 4 waves
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry) {
+    (void)G;
+    W4A16Plan p{};
+    const int64_t nw = N / 8;
+    const int64_t T = K / 32;
+    int64_t tiles;
+    if (M <= 32) {
+        p.kind = 0;
+        p.mt = M <= 16 ? 1 : 2;
+        if (M <= 4 && nw % 4 == 0)
+            p.blk = 4;
+        else if (M <= 16 && nw % 2 == 0)
+            p.blk = 2;
+        else
+            p.blk = 1;
+        p.tiles_n = (int)cdiv(nw, 16 * p.blk);
+        p.tiles_m = 1;
+        tiles = p.tiles_n;
+        int64_t s = cdiv(kTargetWorkgroups, tiles);
+        // every wave should own at least one 32-k step, and the fp32 partials
+        // (written and read once per split) should stay small next to the weights
+        s = std::min<int64_t>(s, std::max<int64_t>(1, T / 4));
+        s = std::min<int64_t>(s, std::max<int64_t>(1, K / (64 * M)));
+        p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+    } else {
+        p.kind = 1;
+        p.blk = 1;
+        p.mt = M >= 128 ? 4 : (M >= 64 ? 2 : 1);
+        const int64_t bm = 32 * p.mt;
+        p.tiles_n = (int)cdiv(N, 256);
+        p.tiles_m = (int)cdiv(M, bm);
+        tiles = (int64_t)p.tiles_n * p.tiles_m;
+        int64_t s = 1;
+        if (tiles < 256) {
+            s = cdiv(kTargetWorkgroups, tiles);
+            s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
+            s = std::min<int64_t>(s, 16);
+        }
+        p.splits = (int)std::max<int64_t>(1, s);
+    }
+    (void)gemv_entry;
+    if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
+    if (tiles > kMaxSplitTiles) p.splits = 1;
+    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)p.splits * M * N * 4 : 0;
+    return p;
+}
+
+W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
+    (void)G;
+    W4A8Plan p{};
+    const int64_t T = K / 64;
+    int64_t tiles;
+    if (M <= 32) {
+        p.kind = 0;
+        p.mt = M <= 16 ? 1 : 2;
+        p.blk = (M <= 16 && N % 128 == 0) ? 2 : 1;
+        p.tiles_n = (int)cdiv(N, 64 * p.blk);
+        p.tiles_m = 1;
+        tiles = p.tiles_n;
+        int64_t s = cdiv(kTargetWorkgroups, tiles);
+        s = std::min<int64_t>(s, std::max<int64_t>(1, T / 4));
+        s = std::min<int64_t>(s, std::max<int64_t>(1, K / (32 * M)));
+        p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+    } else {
+        p.kind = 1;
+        p.blk = 1;
+        p.mt = M >= 128 ? 4 : (M >= 64 ? 2 : 1);
+        p.tiles_n = (int)cdiv(N, 128);
+        p.tiles_m = (int)cdiv(M, 32 * p.mt);
+        tiles = (int64_t)p.tiles_n * p.tiles_m;
+        int64_t s = 1;
+        if (tiles < 256) {
+            s = cdiv(kTargetWorkgroups, tiles);
+            s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
+            s = std::min<int64_t>(s, 16);
+        }
+        p.splits = (int)std::max<int64_t>(1, s);
+    }
+    if (tiles > kMaxSplitTiles) p.splits = 1;
+    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)p.splits * M * N * 4 : 0;
+    return p;
+}
+
+static int check_w4a16(const void *x, const int32_t *qweight, const void *scales, const int32_t *qzeros, void *y,
+                       int64_t M, int64_t N, int64_t K, int G, int dtype, int split_k) {
+    if (!x || !qweight || !scales || !y) return AWQ_EINVAL;
+    if (M < 1 || N < 8 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return AWQ_EINVAL;
+    if (N % 8 != 0) return AWQ_EINVAL;
+    if (G != 32 && G != 64 && G != 128) return AWQ_EINVAL;
+    if (K % G != 0) return AWQ_EINVAL;
+    if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
+    if (split_k < 0 || split_k > K / 32) return AWQ_EINVAL;
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y)) return AWQ_EALIGN;
+    if (qzeros && !aligned16(qzeros)) return AWQ_EALIGN;
+    return AWQ_OK;
+}
+
+static int check_workspace(void *ws, size_t have, size_t need) {
+    if (need == 0) return AWQ_OK;
+    if (!ws || have < need) return AWQ_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return AWQ_EALIGN;
+    return AWQ_OK;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_EHIP; }
+
+static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, const int32_t *qzeros, void *y,
+                     int64_t M, int64_t N, int64_t K, int G, int dtype, int split_k, void *workspace,
+                     size_t workspace_bytes, void *stream, bool gemv) {
+    int rc = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, G, dtype, split_k);
+    if (rc != AWQ_OK) return rc;
+    if (gemv && M > 8) return AWQ_EUNSUPPORTED;
+    W4A16Plan p = plan_w4a16(M, N, K, G, split_k, gemv);
+    rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
+    if (rc != AWQ_OK) return rc;
+    if (p.splits > 1) {
+        p.counters = static_cast<int *>(workspace);
+        p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+    }
+    W4A16Args a{x, qweight, scales, qzeros, y, M, N, K, G, dtype};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return hip_status(p.kind == 0 ? launch_w4a16_skinny(a, p, st) : launch_w4a16_tiled(a, p, st));
+}
+
+}  // namespace awq4
+
+using namespace awq4;
+
+extern "C" {
+
+const char *awq_status_str(int status) {
+    switch (status) {
+        case AWQ_OK: return "AWQ_OK";
+        case AWQ_EINVAL: return "AWQ_EINVAL: invalid argument";
+        case AWQ_EUNSUPPORTED: return "AWQ_EUNSUPPORTED: unsupported shape or mode";
+        case AWQ_EWORKSPACE: return "AWQ_EWORKSPACE: workspace missing or too small";
+        case AWQ_EALIGN: return "AWQ_EALIGN: pointer not 16-byte aligned";
+        case AWQ_EHIP: return "AWQ_EHIP: HIP launch error";
+        default: return "AWQ_UNKNOWN";
+    }
+}
+
+int awq_version(void) { return 100; }
+
+static int check_pack_shape(int64_t rows, int64_t cols, int layout) {
+    if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return AWQ_EINVAL;
+    if (layout == AWQ_LAYOUT_N8) return cols % 8 ? AWQ_EINVAL : AWQ_OK;
+    if (layout == W4A8_LAYOUT_K8) return rows % 8 ? AWQ_EINVAL : AWQ_OK;
+    return AWQ_EINVAL;
+}
+
+int awq_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int layout, int32_t *clamp_count,
+             void *stream) {
+    int rc = check_pack_shape(rows, cols, layout);
+    if (rc != AWQ_OK) return rc;
+    if (rows == 0 || cols == 0) return AWQ_OK;  // nothing to do (empty tensors may have null data)
+    if (!vals || !packed) return AWQ_EINVAL;
+    if (!aligned16(vals) || !aligned16(packed)) return AWQ_EALIGN;
+    return hip_status(launch_pack(vals, packed, rows, cols, layout, clamp_count, static_cast<hipStream_t>(stream)));
+}
+
+int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, int layout, void *stream) {
+    int rc = check_pack_shape(rows, cols, layout);
+    if (rc != AWQ_OK) return rc;
+    if (rows == 0 || cols == 0) return AWQ_OK;
+    if (!vals || !packed) return AWQ_EINVAL;
+    if (!aligned16(vals) || !aligned16(packed)) return AWQ_EALIGN;
+    return hip_status(launch_unpack(packed, vals, rows, cols, layout, static_cast<hipStream_t>(stream)));
+}
+
+size_t awq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int group_size, int split_k) {
+    if (op == AWQ_OP_GEMM_W4A16 || op == AWQ_OP_GEMV_W4A16) {
+        int64_t dummy = 16;  // any aligned non-null value: only shapes are checked here
+        if (check_w4a16(&dummy, (const int32_t *)&dummy, &dummy, nullptr, &dummy, M, N, K, group_size,
+                        AWQ_DTYPE_F16, split_k) == AWQ_EINVAL)
+            return 0;
+        if (op == AWQ_OP_GEMV_W4A16 && M > 8) return 0;
+        return plan_w4a16(M, N, K, group_size, split_k, op == AWQ_OP_GEMV_W4A16).workspace_bytes;
+    }
+    if (op == AWQ_OP_W4A8_GEMM) {
+        if (M < 1 || N < 8 || N % 8 || K < 64 || K % 64 || M > kMaxDim || N > kMaxDim || K > 131072) return 0;
+        if (group_size != -1 && ((group_size != 32 && group_size != 64 && group_size != 128) || K % group_size))
+            return 0;
+        return plan_w4a8(M, N, K, group_size).workspace_bytes;
+    }
+    return 0;
+}
+
+int awq_gemm_w4a16(const void *x, const int32_t *qweight, const void *scales, const int32_t *qzeros, void *y,
+                   int64_t M, int64_t N, int64_t K, int group_size, int dtype, int split_k, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return run_w4a16(x, qweight, scales, qzeros, y, M, N, K, group_size, dtype, split_k, workspace,
+                     workspace_bytes, stream, false);
+}
+
+int awq_gemv_w4a16(const void *x, const int32_t *qweight, const void *scales, const int32_t *qzeros, void *y,
+                   int64_t M, int64_t N, int64_t K, int group_size, int dtype, int split_k, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return run_w4a16(x, qweight, scales, qzeros, y, M, N, K, group_size, dtype, split_k, workspace,
+                     workspace_bytes, stream, true);
+}
+
+int w4a8_quant_act(const void *x_f16, int8_t *a8, float *s1, int64_t M, int64_t K, void *stream) {
+    if (!x_f16 || !a8 || !s1) return AWQ_EINVAL;
+    if (M < 1 || K < 1 || M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 30)) return AWQ_EINVAL;
+    if (!aligned16(x_f16) || !aligned16(a8) || !aligned16(s1)) return AWQ_EALIGN;
+    return hip_status(launch_w4a8_quant(x_f16, a8, s1, M, K, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const void *s2_f16, const void *s3_f16,
+              void *y_f16, int32_t *acc_out, int64_t M, int64_t N, int64_t K, int group_size, void *workspace,
+              size_t workspace_bytes, void *stream) {
+    if (!a8 || !b_packed || !s1 || !s2_f16 || !y_f16) return AWQ_EINVAL;
+    if (M < 1 || N < 8 || K < 1 || M > kMaxDim || N > kMaxDim) return AWQ_EINVAL;
+    if (N % 8) return AWQ_EINVAL;
+    if (group_size == -1) {
+        if (s3_f16) return AWQ_EINVAL;
+    } else {
+        if (group_size != 32 && group_size != 64 && group_size != 128) return AWQ_EINVAL;
+        if (!s3_f16 || K % group_size) return AWQ_EINVAL;
+    }
+    // 64 k per matrix-core step; |acc| <= 128 * 128 * K must stay below 2^31
+    if (K % 64 || K > 131072) return AWQ_EUNSUPPORTED;
+    if (!aligned16(a8) || !aligned16(b_packed) || !aligned16(s1) || !aligned16(s2_f16) || !aligned16(y_f16))
+        return AWQ_EALIGN;
+    if ((s3_f16 && !aligned16(s3_f16)) || (acc_out && !aligned16(acc_out))) return AWQ_EALIGN;
+    W4A8Plan p = plan_w4a8(M, N, K, group_size);
+    int rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
+    if (rc != AWQ_OK) return rc;
+    if (p.splits > 1) {
+        p.counters = static_cast<int *>(workspace);
+        p.partials = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
+    }
+    W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
+    return hip_status(launch_w4a8(a, p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// device.hpp -- gfx950 device helpers for the 4-bit-weight kernels.
+//
+// Packed-word facts used here (first-generation AWQ GEMM format, vLLM pull
+// request "Speed up AWQ 2.5x with updated kernel", list of format
+// differences): a 32-bit word packs eight output columns 8j..8j+7 of one
+// k-row; nibble i holds column 8j + {0,2,4,6,1,3,5,7}[i].  Hence byte b of a
+// word holds columns (0,2), (4,6), (1,3), (5,7) for b = 0..3 (low nibble
+// first), and the zero-point word of a group uses the same map.
+//
+// Matrix-core operand model (v_mfma_*_16x16x32 / 16x16x64): lane l supplies
+// row (A) or column (B) l % 16 and a chunk of the reduction index chosen by
+// l / 16; C lane l holds rows 4*(l/16) + r, r = 0..3, of column l % 16.  The
+// reduction index order inside a lane is free as long as A and B agree, so
+// the kernels assign lane group g = l/16 the consecutive k range g*8..g*8+7
+// (fp16/bf16) or g*16..g*16+15 (int8) of each step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq4 {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+template <typename T, typename F>
+__device__ __forceinline__ T bit_as(F v) {
+    static_assert(sizeof(T) == sizeof(F), "size mismatch");
+    return __builtin_bit_cast(T, v);
+}
+
+// v_perm_b32: result byte i = byte sel[i] of the 8-byte value {hi:lo}
+// (selector 0..3 = bytes of lo, 4..7 = bytes of hi).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Interleave two words of the same 8 columns at consecutive k (lo = k even,
+// hi = k odd) so that each 16-bit half holds one k:
+//   pair_x -> halves hold nibbles of columns {0,2,4,6} (bytes 0,1 of each word)
+//   pair_y -> halves hold nibbles of columns {1,3,5,7} (bytes 2,3 of each word)
+__device__ __forceinline__ uint32_t pair_x(uint32_t lo, uint32_t hi) { return perm_b32(hi, lo, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_y(uint32_t lo, uint32_t hi) { return perm_b32(hi, lo, 0x07060302u); }
+
+// Where column t (0..7) of a word sits after pair_x / pair_y:
+//   source  = pair_y if t is odd, else pair_x
+//   pos     = t >> 1 : nibble position inside each 16-bit half
+//   shift   = 8 for pos 2,3 (upper byte of the half), else 0
+//   hi      = pos is odd (upper nibble of that byte)
+// and the nibble index of column t inside a (zero-point) word.
+__host__ __device__ constexpr int col_src_y(int t) { return t & 1; }
+__host__ __device__ constexpr int col_shift(int t) { return ((t >> 1) & 2) ? 8 : 0; }
+__host__ __device__ constexpr int col_hi(int t) { return (t >> 1) & 1; }
+__host__ __device__ constexpr int col_nibble(int t) { return (t >> 1) + 4 * (t & 1); }
+
+// ---------------------------------------------------------------------------
+// fp16 dequantisation of two k-values of one column, exact up to the final
+// multiply by the scale (one rounding, to nearest even):
+//   lo nibble: as_f16(0x6400 | q) = 1024 + q;     (1024 + q) - (1024 + z) = q - z
+//   hi nibble: as_f16(0x6400 | 16q) = 1024 + 16q; (1024 + 16q)/16 - (64 + z) = q - z
+// zc holds -(1024 + z) or -(64 + z) in both halves; sc holds s in both halves.
+template <int HI>
+__device__ __forceinline__ uint32_t dq_f16(uint32_t v, uint32_t zc, uint32_t sc) {
+    const uint32_t mask = HI ? 0x00F000F0u : 0x000F000Fu;
+    f16x2 h = bit_as<f16x2>((v & mask) | 0x64006400u);
+    f16x2 z = bit_as<f16x2>(zc);
+    f16x2 d;
+    if (HI) {
+        const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+        d = h * sixteenth + z;
+    } else {
+        d = h + z;
+    }
+    return bit_as<uint32_t>(d * bit_as<f16x2>(sc));
+}
+
+// fp16 zero-point constant for column t from the group's zero nibble z.
+template <int HI>
+__device__ __forceinline__ uint32_t zconst_f16(uint32_t z) {
+    uint32_t h = HI ? (0xD400u | (z << 4)) : (0xE400u | z);  // -(64+z) or -(1024+z)
+    return h | (h << 16);
+}
+
+// bf16 dequantisation of two k-values of one column, computed exactly in
+// fp32 and rounded once:  q*s' - z*s  with s' = s (lo nibble) or s/16 (hi
+// nibble, whose byte holds 16q).  Returns the bf16 pair (even k low half).
+__device__ __forceinline__ uint32_t dq_bf16(uint32_t v, uint32_t mask, float s_eff, float zs) {
+    uint32_t m = v & mask;
+    float q0 = (float)(m & 0xFFu);          // v_cvt_f32_ubyte0
+    float q1 = (float)((m >> 16) & 0xFFu);  // v_cvt_f32_ubyte2
+    float w0 = __builtin_fmaf(q0, s_eff, -zs);
+    float w1 = __builtin_fmaf(q1, s_eff, -zs);
+    __bf16 b0 = (__bf16)w0;
+    __bf16 b1 = (__bf16)w1;
+    return (uint32_t)bit_as<uint16_t>(b0) | ((uint32_t)bit_as<uint16_t>(b1) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return bit_as<float>(b << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) { return (float)bit_as<f16>((uint16_t)b); }
+
+__device__ __forceinline__ uint16_t f32_to_out_bits(float v, int dt) {
+    if (dt == DT_BF16) return bit_as<uint16_t>((__bf16)v);
+    return bit_as<uint16_t>((f16)v);
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core wrappers.
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bit_as<f16x8>(a), bit_as<f16x8>(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_as<bf16x8>(a), bit_as<bf16x8>(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_as<i32x4>(a), bit_as<i32x4>(b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K completion.  Every workgroup of a tile has written its partial
+// tile; the one that arrives last (counted on an agent-scope atomic) sums the
+// partials in split order 0..S-1 and writes the output, then re-arms the
+// counter to zero for the next call.  Returns true in the last workgroup.
+// All threads of the workgroup must call it.
+__device__ __forceinline__ bool splitk_arrive(int *counter, int S) {
+    __shared__ int s_last;
+    __threadfence();  // release this thread's partial-tile writes
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int old = atomicAdd(counter, 1);
+        int last = (old == S - 1);
+        if (last) atomicExch(counter, 0);
+        s_last = last;
+    }
+    __syncthreads();
+    bool last = s_last != 0;
+    if (last) __threadfence();  // acquire the other workgroups' partials
+    return last;
+}
+
+}  // namespace awq4

@@ -1,0 +1,77 @@
+// launch.hpp -- internal interface between the C-ABI layer (api.cpp) and the
+// kernel launchers (*.hip).  Arguments are validated by api.cpp before any
+// launcher is called; launchers only enqueue work on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq4 {
+
+struct W4A16Args {
+    const void *x;
+    const int32_t *qweight;
+    const void *scales;
+    const int32_t *qzeros;  // nullptr = symmetric (z = 8)
+    void *y;
+    int64_t M, N, K;
+    int G;
+    int dtype;
+};
+
+// Kernel choice and grid for one W4A16 call (pure function of the shape).
+struct W4A16Plan {
+    int kind;     // 0 = skinny, 1 = tiled
+    int blk;      // skinny: word-columns per lane (1, 2, 4)
+    int mt;       // skinny: row tiles (M <= 16*mt); tiled: row tiles per wave
+    int tiles_n;  // grid x
+    int tiles_m;  // tiled: grid y
+    int splits;   // split-K factor (1 = none)
+    size_t workspace_bytes;
+    // filled in by the caller from the workspace pointer
+    int *counters;
+    float *partials;
+};
+
+struct W4A8Args {
+    const int8_t *a8;
+    const int32_t *b;
+    const float *s1;
+    const void *s2;
+    const void *s3;  // nullptr = per-channel
+    void *y;
+    int32_t *acc_out;  // may be nullptr
+    int64_t M, N, K;
+    int G;  // -1 = per-channel
+};
+
+struct W4A8Plan {
+    int kind;  // 0 = skinny, 1 = tiled
+    int blk;   // skinny: 64-column sets per lane-row (1, 2)
+    int mt;    // row tiles (skinny: M <= 16*mt; tiled: per wave)
+    int tiles_n, tiles_m, splits;
+    size_t workspace_bytes;
+    int *counters;
+    int32_t *partials;
+};
+
+// Every workspace starts with a fixed counter region (one int per output tile
+// of a split-K launch).  Its size does not depend on the call, so calls of
+// different shapes that share a workspace always find their counters zero.
+constexpr size_t kCounterBytes = 16384;
+constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
+
+W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry);
+W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);
+
+hipError_t launch_w4a16_skinny(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
+hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
+hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st);
+hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
+hipError_t launch_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int layout,
+                       int32_t *clamp_count, hipStream_t st);
+hipError_t launch_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, int layout,
+                         hipStream_t st);
+
+}  // namespace awq4

@@ -1,0 +1,369 @@
+// w4a8.hip -- QQQ-style W4A8 kernels for gfx950.
+//
+// Method (vLLM pull request "Support W4A8 quantization for vllm"): activations
+// are quantised per token on the fly (row abs-max / 127 as an fp16 scale s1,
+// round half to even, clamp to int8); weights are symmetric int4; the int4 is
+// turned into an int8 by placing it in the upper nibble (a x16 that the
+// epilogue removes exactly); products accumulate in int32 on the matrix
+// cores and split-K partials are reduced in int32 through a temporary
+// buffer; s1 (per token) and s2 (per output channel) are applied to the
+// output.  Grouped weights additionally carry integer group scales s3 that
+// multiply the int4 value into an int8 (this library's reading of how the
+// per-group and per-channel scales combine; see awq4.h).
+//
+// Weight layout W4A8_LAYOUT_K8: int32 [K/8, N]; nibble i of word [kb][n]
+// holds k = 8kb + {0,4,1,5,2,6,3,7}[i], two's complement, so
+//   (w << 4) & 0xF0F0F0F0  -> bytes 0..3 = 16*q for k = 8kb + 0..3
+//    w       & 0xF0F0F0F0  -> bytes 0..3 = 16*q for k = 8kb + 4..7
+// and two consecutive words give a lane the 16 consecutive k bytes that one
+// v_mfma_i32_16x16x64_i8 B operand needs.  Lane j of a wave loads 16 bytes =
+// 4 consecutive columns per k-row; column i of those becomes B column j of
+// the i-th MFMA (output column = 4*j + i within a 64-column set).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace awq4 {
+
+// ---------------------------------------------------------------------------
+// Activation quantisation: one workgroup (256 threads) per row.
+__global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ a8,
+                                                         float *__restrict__ s1, int K) {
+    __shared__ uint32_t wmax[4];
+    const int m = blockIdx.x;
+    const uint16_t *row = x + (size_t)m * K;
+    int8_t *out = a8 + (size_t)m * K;
+    const int K8 = (K & 7) ? 0 : K;  // vector path only when every row is 16-byte aligned
+    // |x| as an integer: for finite fp16 the magnitude order equals the order of the low 15 bits.
+    uint32_t mx = 0;
+    for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
+        u32x4 v = *(const u32x4 *)(row + k);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            mx = max(mx, v[p] & 0x7FFFu);
+            mx = max(mx, (v[p] >> 16) & 0x7FFFu);
+        }
+    }
+    for (int k = K8 + threadIdx.x; k < K; k += 256) mx = max(mx, (uint32_t)row[k] & 0x7FFFu);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const float amax = f16_bits_to_f32(mx);
+    const float q32 = amax / 127.0f;        // correctly rounded fp32 divide
+    const float s = (float)(f16)q32;        // to fp16 (nearest even) and back
+    if (threadIdx.x == 0) s1[m] = s;
+    for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
+        u32x4 v = *(const u32x4 *)(row + k);
+        u32x2 o = {0, 0};
+        if (s != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                float r = rintf(f16_bits_to_f32(h) / s);
+                r = fminf(fmaxf(r, -128.0f), 127.0f);
+                o[e >> 2] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (e & 3));
+            }
+        }
+        *(u32x2 *)(out + k) = o;
+    }
+    for (int k = K8 + threadIdx.x; k < K; k += 256) {
+        float r = 0.0f;
+        if (s != 0.0f) r = fminf(fmaxf(rintf(f16_bits_to_f32(row[k]) / s), -128.0f), 127.0f);
+        out[k] = (int8_t)r;
+    }
+}
+
+hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st) {
+    hipLaunchKernelGGL(w4a8_quant_kernel, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a8, s1, (int)K);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// int4 -> int8 B operand for one column from two consecutive K8 words.
+//  per-channel: bytes = 16*q  (two instructions per word)
+//  per-group:   bytes = q*s3 with s3 in 1..16: with u = q + 8 in 0..15,
+//               u*s3 + (128 - 8*s3) lies in 0..240 per byte (no carries
+//               between bytes), and flipping bit 7 subtracts 128.
+template <bool GROUP>
+__device__ __forceinline__ u32x4 make_b8(uint32_t w0, uint32_t w1, uint32_t s3) {
+    u32x4 b;
+    if (!GROUP) {
+        b[0] = (w0 << 4) & 0xF0F0F0F0u;
+        b[1] = w0 & 0xF0F0F0F0u;
+        b[2] = (w1 << 4) & 0xF0F0F0F0u;
+        b[3] = w1 & 0xF0F0F0F0u;
+    } else {
+        const uint32_t c = (128u - 8u * s3) * 0x01010101u;
+        const uint32_t u0 = w0 ^ 0x88888888u, u1 = w1 ^ 0x88888888u;
+        b[0] = ((u0 & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
+        b[1] = (((u0 >> 4) & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
+        b[2] = ((u1 & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
+        b[3] = (((u1 >> 4) & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
+    }
+    return b;
+}
+
+__device__ __forceinline__ uint32_t s3_int(const uint16_t *__restrict__ s3, size_t idx) {
+    return (uint32_t)f16_bits_to_f32(s3[idx]);
+}
+
+// Final value of one output: undo the x16 of per-channel weights, scale, store.
+template <bool GROUP>
+__device__ __forceinline__ void w4a8_store(int32_t acc, int m, int n, int N, const float *__restrict__ s1,
+                                           const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
+                                           int32_t *__restrict__ acc_out) {
+    const int32_t a = GROUP ? acc : (acc >> 4);  // exact: per-channel acc is a multiple of 16
+    const float v = (float)a * s1[m] * f16_bits_to_f32(s2[n]);
+    y[(size_t)m * N + n] = bit_as<uint16_t>((f16)v);
+    if (acc_out) acc_out[(size_t)m * N + n] = a;
+}
+
+// ---------------------------------------------------------------------------
+// Skinny W4A8 kernel: M <= 16*MT; 4 waves split the K slice of a 64*BLK
+// column tile; LDS reduce (int32, exact); split-K over grid y.
+template <int BLK, int MT, bool GROUP>
+__global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
+                                                   const float *__restrict__ s1, const uint16_t *__restrict__ s2,
+                                                   const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
+                                                   int32_t *__restrict__ acc_out, int32_t *__restrict__ part,
+                                                   int *__restrict__ counters, int M, int N, int K, int G, int S) {
+    extern __shared__ int32_t ired[];
+    constexpr int COLS = 64 * BLK;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, gq = lane >> 4;
+    const int tile = blockIdx.x, split = blockIdx.y;
+    const int T = K >> 6;  // 64-k steps
+    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
+    const int w_lo = s_lo + (s_hi - s_lo) * wave / 4, w_hi = s_lo + (s_hi - s_lo) * (wave + 1) / 4;
+    int ncol[BLK];
+    bool ok[BLK];
+#pragma unroll
+    for (int b = 0; b < BLK; ++b) {
+        ncol[b] = tile * COLS + 64 * b + 4 * j;
+        ok[b] = ncol[b] < N;  // N % 8 == 0 and the 4 columns start at a multiple of 4
+    }
+    i32x4 acc[MT][BLK][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int b = 0; b < BLK; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][b][i] = (i32x4){0, 0, 0, 0};
+
+    for (int st = w_lo; st < w_hi; ++st) {
+        const int k0 = st * 64 + 16 * gq;  // this lane group's 16 k
+        const int kb = k0 >> 3;
+        u32x4 w0[BLK], w1[BLK];
+#pragma unroll
+        for (int b = 0; b < BLK; ++b) {
+            if (ok[b]) {
+                w0[b] = __builtin_nontemporal_load((const u32x4 *)(bq + (size_t)kb * N + ncol[b]));
+                w1[b] = __builtin_nontemporal_load((const u32x4 *)(bq + (size_t)(kb + 1) * N + ncol[b]));
+            } else {
+                w0[b] = (u32x4){0, 0, 0, 0};
+                w1[b] = (u32x4){0, 0, 0, 0};
+            }
+        }
+        u32x4 a[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = 16 * mt + j;
+            a[mt] = (m < M) ? *(const u32x4 *)(a8 + (size_t)m * K + k0) : (u32x4){0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int b = 0; b < BLK; ++b) {
+            uint32_t g3[4] = {16, 16, 16, 16};
+            if (GROUP && ok[b]) {
+                const size_t gi = (size_t)(k0 / G) * N + ncol[b];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) g3[i] = s3_int(s3, gi + i);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4 bop = make_b8<GROUP>(w0[b][i], w1[b][i], g3[i]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt][b][i] = mfma_i8(a[mt], bop, acc[mt][b][i]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * mt + 4 * gq + r;
+            if (m < M) {
+#pragma unroll
+                for (int b = 0; b < BLK; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ired[((size_t)wave * M + m) * COLS + 64 * b + 4 * j + i] = acc[mt][b][i][r];
+            }
+        }
+    __syncthreads();
+    const int total = M * COLS;
+    const int n_base = tile * COLS;
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int m = idx / COLS, c = idx - m * COLS;
+        const int32_t v = ired[(size_t)(0 * M + m) * COLS + c] + ired[(size_t)(1 * M + m) * COLS + c] +
+                          ired[(size_t)(2 * M + m) * COLS + c] + ired[(size_t)(3 * M + m) * COLS + c];
+        const int n = n_base + c;
+        if (n < N) {
+            if (S == 1)
+                w4a8_store<GROUP>(v, m, n, N, s1, s2, y, acc_out);
+            else
+                part[((size_t)split * M + m) * N + n] = v;
+        }
+    }
+    if (S == 1) return;
+    if (!splitk_arrive(&counters[tile], S)) return;
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int m = idx / COLS, c = idx - m * COLS;
+        const int n = n_base + c;
+        if (n >= N) continue;
+        int32_t v = 0;
+        for (int s = 0; s < S; ++s) v += __builtin_nontemporal_load(&part[((size_t)s * M + m) * N + n]);
+        w4a8_store<GROUP>(v, m, n, N, s1, s2, y, acc_out);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled W4A8 kernel: 2 x 2 waves, wave tile (16*MTW) x 64, workgroup tile
+// (32*MTW) x 128; split-K over grid z.
+template <int MTW, bool GROUP>
+__global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
+                                                  const float *__restrict__ s1, const uint16_t *__restrict__ s2,
+                                                  const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
+                                                  int32_t *__restrict__ acc_out, int32_t *__restrict__ part,
+                                                  int *__restrict__ counters, int M, int N, int K, int G, int S) {
+    constexpr int BM = 32 * MTW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, gq = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
+    const int ncol = tn * 128 + wn * 64 + 4 * j;
+    const bool ok = ncol < N;
+    const int m0 = tm * BM + wm * 16 * MTW;
+    const int T = K >> 6;
+    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
+
+    i32x4 acc[MTW][4];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = (i32x4){0, 0, 0, 0};
+    bool row_ok[MTW];
+    const int8_t *arow[MTW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+        const int m = m0 + 16 * mt + j;
+        row_ok[mt] = m < M;
+        arow[mt] = a8 + (size_t)(row_ok[mt] ? m : 0) * K + 16 * gq;
+    }
+
+    for (int st = s_lo; st < s_hi; ++st) {
+        const int k0 = st * 64 + 16 * gq;
+        const int kb = k0 >> 3;
+        u32x4 w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
+        if (ok) {
+            w0 = *(const u32x4 *)(bq + (size_t)kb * N + ncol);
+            w1 = *(const u32x4 *)(bq + (size_t)(kb + 1) * N + ncol);
+        }
+        u32x4 a[MTW];
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+            a[mt] = row_ok[mt] ? *(const u32x4 *)(arow[mt] + st * 64) : (u32x4){0, 0, 0, 0};
+        uint32_t g3[4] = {16, 16, 16, 16};
+        if (GROUP && ok) {
+            const size_t gi = (size_t)(k0 / G) * N + ncol;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g3[i] = s3_int(s3, gi + i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x4 bop = make_b8<GROUP>(w0[i], w1[i], g3[i]);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) acc[mt][i] = mfma_i8(a[mt], bop, acc[mt][i]);
+        }
+    }
+
+    if (S == 1) {
+        if (!ok) return;
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w4a8_store<GROUP>(acc[mt][i][r], m, ncol + i, N, s1, s2, y, acc_out);
+                }
+            }
+        return;
+    }
+    if (ok) {
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M)
+                    *(i32x4 *)(part + ((size_t)split * M + m) * N + ncol) =
+                        (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+            }
+    }
+    if (!splitk_arrive(&counters[tm * gridDim.x + tn], S)) return;
+    if (!ok) return;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 16 * mt + 4 * gq + r;
+            if (m >= M) continue;
+            i32x4 v = {0, 0, 0, 0};
+            for (int s = 0; s < S; ++s)
+                v += __builtin_nontemporal_load((const i32x4 *)(part + ((size_t)s * M + m) * N + ncol));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w4a8_store<GROUP>(v[i], m, ncol + i, N, s1, s2, y, acc_out);
+        }
+}
+
+// ---------------------------------------------------------------------------
+template <int BLK, int MT, bool GROUP>
+static hipError_t launch_skinny8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    size_t lds = (size_t)4 * a.M * 64 * BLK * sizeof(int32_t);
+    hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
+                       (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
+                       (uint16_t *)a.y, a.acc_out, p.partials, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G,
+                       p.splits);
+    return hipGetLastError();
+}
+
+template <int MTW, bool GROUP>
+static hipError_t launch_tiled8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    hipLaunchKernelGGL((w4a8_tiled<MTW, GROUP>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
+                       (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
+                       (uint16_t *)a.y, a.acc_out, p.partials, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G,
+                       p.splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    const bool grp = a.s3 != nullptr;
+    if (p.kind == 0) {
+        switch (p.blk * 10 + p.mt) {
+            case 11: return grp ? launch_skinny8<1, 1, true>(a, p, st) : launch_skinny8<1, 1, false>(a, p, st);
+            case 21: return grp ? launch_skinny8<2, 1, true>(a, p, st) : launch_skinny8<2, 1, false>(a, p, st);
+            case 12: return grp ? launch_skinny8<1, 2, true>(a, p, st) : launch_skinny8<1, 2, false>(a, p, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (p.mt) {
+        case 1: return grp ? launch_tiled8<1, true>(a, p, st) : launch_tiled8<1, false>(a, p, st);
+        case 2: return grp ? launch_tiled8<2, true>(a, p, st) : launch_tiled8<2, false>(a, p, st);
+        case 4: return grp ? launch_tiled8<4, true>(a, p, st) : launch_tiled8<4, false>(a, p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace awq4

@@ -1,0 +1,169 @@
+"""Thin torch-facing binding of libawq4.so: argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor placement/dtypes, allocates outputs and the per-device
+workspace through torch, and passes raw pointers and the current stream.
+"""
+from __future__ import annotations
+
+import threading
+
+import torch
+
+from . import _lib as L
+
+_F16 = {torch.float16: L.AWQ_DTYPE_F16, torch.bfloat16: L.AWQ_DTYPE_BF16}
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on a CUDA (HIP) device")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+# ----------------------------------------------------------------------------- workspace
+
+class Workspace:
+    """One zero-initialised workspace per device, grown on demand and shared by
+    every call ordered on one stream (the library leaves its counters zero)."""
+
+    def __init__(self):
+        self._bufs: dict[int, torch.Tensor] = {}
+        self._lock = threading.Lock()
+
+    def get(self, device: torch.device, nbytes: int) -> torch.Tensor | None:
+        if nbytes == 0:
+            return None
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        with self._lock:
+            buf = self._bufs.get(idx)
+            if buf is None or buf.numel() < nbytes:
+                size = max(nbytes, 2 * (buf.numel() if buf is not None else 0), 1 << 20)
+                buf = torch.zeros(size, dtype=torch.uint8, device=torch.device("cuda", idx))
+                self._bufs[idx] = buf
+            return buf
+
+
+WORKSPACE = Workspace()
+
+
+def workspace_bytes(op: int, M: int, N: int, K: int, group_size: int, split_k: int = 0) -> int:
+    return int(L.lib().awq_workspace_bytes(op, M, N, K, group_size, split_k))
+
+
+# ----------------------------------------------------------------------------- packing
+
+def pack(vals: torch.Tensor, layout: str = "n8", clamp_count: torch.Tensor | None = None) -> torch.Tensor:
+    """Pack 4-bit values: layout "n8" (AWQ, uint8 [rows, cols] -> int32 [rows, cols/8])
+    or "k8" (W4A8, int8 [K, N] -> int32 [K/8, N])."""
+    _need_cuda(vals, clamp_count)
+    rows, cols = vals.shape
+    if layout == "n8":
+        out = torch.empty(rows, cols // 8, dtype=torch.int32, device=vals.device)
+        lay = L.AWQ_LAYOUT_N8
+    else:
+        out = torch.empty(rows // 8, cols, dtype=torch.int32, device=vals.device)
+        lay = L.W4A8_LAYOUT_K8
+    L.check("awq_pack", L.lib().awq_pack(_ptr(vals), _ptr(out), rows, cols, lay, _ptr(clamp_count),
+                                         _stream(vals.device)))
+    return out
+
+
+def unpack(packed: torch.Tensor, layout: str = "n8") -> torch.Tensor:
+    _need_cuda(packed)
+    if layout == "n8":
+        rows, cols = packed.shape[0], packed.shape[1] * 8
+        out = torch.empty(rows, cols, dtype=torch.uint8, device=packed.device)
+        lay = L.AWQ_LAYOUT_N8
+    else:
+        rows, cols = packed.shape[0] * 8, packed.shape[1]
+        out = torch.empty(rows, cols, dtype=torch.int8, device=packed.device)
+        lay = L.W4A8_LAYOUT_K8
+    L.check("awq_unpack", L.lib().awq_unpack(_ptr(packed), _ptr(out), rows, cols, lay, _stream(packed.device)))
+    return out
+
+
+# ----------------------------------------------------------------------------- W4A16
+
+def _w4a16(fn_name: str, op: int, x, qweight, scales, qzeros, group_size, split_k, out):
+    _need_cuda(x, qweight, scales, qzeros, out)
+    if x.dtype not in _F16:
+        raise ValueError("x must be fp16 or bf16")
+    if scales.dtype != x.dtype:
+        raise ValueError("scales must have the activation dtype")
+    M, K = x.shape
+    N = qweight.shape[1] * 8
+    if out is None:
+        out = torch.empty(M, N, dtype=x.dtype, device=x.device)
+    need = workspace_bytes(op, M, N, K, group_size, split_k)
+    ws = WORKSPACE.get(x.device, need)
+    fn = getattr(L.lib(), fn_name)
+    L.check(fn_name, fn(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out), M, N, K, group_size,
+                        _F16[x.dtype], split_k, _ptr(ws), 0 if ws is None else ws.numel(), _stream(x.device)))
+    return out
+
+
+def gemm_w4a16(x, qweight, scales, qzeros, group_size: int = 128, split_k: int = 0, out=None):
+    """Y = X . dequant(qweight, qzeros, scales) (prefill path, any M)."""
+    return _w4a16("awq_gemm_w4a16", L.AWQ_OP_GEMM_W4A16, x, qweight, scales, qzeros, group_size, split_k, out)
+
+
+def gemv_w4a16(x, qweight, scales, qzeros, group_size: int = 128, split_k: int = 0, out=None):
+    """Decode path, M <= 8."""
+    return _w4a16("awq_gemv_w4a16", L.AWQ_OP_GEMV_W4A16, x, qweight, scales, qzeros, group_size, split_k, out)
+
+
+def linear_w4a16(x, qweight, scales, qzeros, group_size: int = 128, out=None):
+    """The AWQ linear-layer dispatch: more than 8 rows -> GEMM, else GEMV."""
+    if x.shape[0] > 8:
+        return gemm_w4a16(x, qweight, scales, qzeros, group_size, out=out)
+    return gemv_w4a16(x, qweight, scales, qzeros, group_size, out=out)
+
+
+# ----------------------------------------------------------------------------- W4A8
+
+def quant_act(x: torch.Tensor, a8: torch.Tensor | None = None, s1: torch.Tensor | None = None):
+    """Per-token int8 quantisation of fp16 activations -> (a8 int8 [M,K], s1 fp32 [M])."""
+    _need_cuda(x, a8, s1)
+    if x.dtype != torch.float16:
+        raise ValueError("W4A8 activations must be fp16")
+    M, K = x.shape
+    if a8 is None:
+        a8 = torch.empty(M, K, dtype=torch.int8, device=x.device)
+    if s1 is None:
+        s1 = torch.empty(M, dtype=torch.float32, device=x.device)
+    L.check("w4a8_quant_act", L.lib().w4a8_quant_act(_ptr(x), _ptr(a8), _ptr(s1), M, K, _stream(x.device)))
+    return a8, s1
+
+
+def w4a8_gemm(a8, b, s1, s2, s3=None, group_size: int = -1, want_acc: bool = False, out=None):
+    """y = fp16(acc * s1 * s2), acc = a8 . w8 (exact int32). Returns y or (y, acc)."""
+    _need_cuda(a8, b, s1, s2, s3, out)
+    M, K = a8.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.float16, device=a8.device)
+    acc = torch.empty(M, N, dtype=torch.int32, device=a8.device) if want_acc else None
+    need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size)
+    ws = WORKSPACE.get(a8.device, need)
+    L.check("w4a8_gemm", L.lib().w4a8_gemm(_ptr(a8), _ptr(b), _ptr(s1), _ptr(s2), _ptr(s3), _ptr(out), _ptr(acc),
+                                           M, N, K, group_size, _ptr(ws), 0 if ws is None else ws.numel(),
+                                           _stream(a8.device)))
+    return (out, acc) if want_acc else out
+
+
+def linear_w4a8(x, b, s2, s3=None, group_size: int = -1):
+    """Quantise the activations per token, then the W4A8 GEMM."""
+    a8, s1 = quant_act(x)
+    return w4a8_gemm(a8, b, s1, s2, s3, group_size)

@@ -1,0 +1,193 @@
+/*
+ * awq4.h -- C ABI of the MI355X (gfx950) 4-bit-weight GEMM library.
+ *
+ * The library computes the group-quantised 4-bit-weight linear layer
+ *     Y = X . dequant(Wq),   w[k,n] = (q[k,n] - z[k/G,n]) * s[k/G,n]
+ * in the first-generation AWQ GEMM weight format, in a decode regime (GEMV,
+ * M <= 8) and a prefill regime (GEMM, any M), plus the QQQ-style W4A8 variant
+ * (per-token int8 activations x symmetric int4 weights, exact int32
+ * accumulation, per-token and per-channel (optionally per-group) scales).
+ *
+ * Sources (web pages, cited by title and passage):
+ *  [P1] vLLM pull request "Speed up AWQ 2.5x with updated kernel": the list of
+ *       differences between the old and new AWQ packings (old GEMM order map
+ *       [0,2,4,6,1,3,5,7]), and the dispatch snippet (M > 8 -> GEMM, else GEMV;
+ *       kernels take inputs, qweight, scales, qzeros, group_size, and the GEMM
+ *       a split_k_iters count).
+ *  [P2] AutoAWQ pull request "Marlin symmetric quantization and inference":
+ *       the symmetric variant without zero points; one workspace per device
+ *       rather than per layer.
+ *  [P5] vLLM pull request "Support W4A8 quantization for vllm" (QQQ): dynamic
+ *       per-token activation quantisation; int4 -> int8 by placing the nibble
+ *       in the upper four bits; int32 global reduce through a temporary
+ *       buffer; s1 (per token) and s2 (per channel) applied to the output,
+ *       with per-group scales in addition for grouped weights; the GEMM
+ *       signature (a, b_q_weight, s1, s2, s3, workspace, size_m, size_n,
+ *       size_k) with const operands; a missing clamp in packing as a real bug.
+ *
+ * Conventions for every entry point:
+ *  - All tensors are dense, row-major and contiguous, in device memory owned
+ *    by the caller.  Device pointers must be 16-byte aligned (AWQ_EALIGN).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it; no entry point synchronises or allocates device
+ *    memory, so all of them are asynchronous and safe to call from several
+ *    host threads on different streams.  Faults inside a kernel surface at
+ *    the caller's next synchronisation, as for any HIP launch.
+ *  - Arguments are validated before anything is enqueued; a call that
+ *    returns an error has written nothing.  Validation needs no GPU.
+ *  - Return value: AWQ_OK or a negative AWQ_E* status.
+ *  - Results are deterministic: the same inputs give the same bits on every
+ *    run (split-K partials are summed in a fixed order).
+ */
+#ifndef AWQ4_H
+#define AWQ4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define AWQ_OK 0
+#define AWQ_EINVAL (-1)       /* bad shape, null pointer, unknown enum value */
+#define AWQ_EUNSUPPORTED (-2) /* valid request this library does not implement (e.g. GEMV with M > 8) */
+#define AWQ_EWORKSPACE (-3)   /* workspace missing or smaller than awq_workspace_bytes() */
+#define AWQ_EALIGN (-4)       /* a device pointer is not 16-byte aligned */
+#define AWQ_EHIP (-5)         /* the HIP runtime reported an error when launching */
+
+/* Activation / scale / output dtypes. */
+#define AWQ_DTYPE_F16 0
+#define AWQ_DTYPE_BF16 1
+
+/* Packed layouts for awq_pack / awq_unpack. */
+#define AWQ_LAYOUT_N8 0  /* AWQ: uint8 vals [rows, cols] in 0..15 -> int32 [rows, cols/8];
+                            nibble i of word [r][j] holds column 8j + {0,2,4,6,1,3,5,7}[i] ([P1]) */
+#define W4A8_LAYOUT_K8 1 /* W4A8: int8 vals [K=rows, N=cols] in -8..7 -> int32 [K/8, N];
+                            nibble i of word [kb][n] holds k = 8kb + {0,4,1,5,2,6,3,7}[i],
+                            two's complement (this library's own layout) */
+
+/* Operation ids for awq_workspace_bytes. */
+#define AWQ_OP_GEMM_W4A16 0
+#define AWQ_OP_GEMV_W4A16 1
+#define AWQ_OP_W4A8_GEMM 2
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *awq_status_str(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int awq_version(void);
+
+/*
+ * awq_pack -- pack 4-bit values into 32-bit words ([P1] order map for
+ * AWQ_LAYOUT_N8; K-packed two's complement for W4A8_LAYOUT_K8).  Used for
+ * qweight and qzeros alike.
+ *   vals:        device, uint8 [rows, cols] (N8) or int8 [rows, cols] (K8).
+ *   packed:      device, int32 [rows, cols/8] (N8) or [rows/8, cols] (K8).
+ *   clamp_count: device int32 or NULL.  Values outside 0..15 (N8) / -8..7 (K8)
+ *                are clamped into range (the lesson of the missing clamp in
+ *                [P5]) and their number is atomically added to *clamp_count,
+ *                which the caller zeroes beforehand.
+ * rows == 0 or cols == 0 is a no-op that returns AWQ_OK.
+ * Errors: AWQ_EINVAL if a pointer is NULL, rows/cols < 0, cols % 8 (N8) or
+ * rows % 8 (K8) is non-zero, or the layout is unknown.
+ */
+int awq_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int layout,
+             int32_t *clamp_count, void *stream);
+
+/*
+ * awq_unpack -- inverse of awq_pack: words -> uint8 (N8, 0..15) or int8
+ * (K8, -8..7) values [rows, cols].  Same shape rules and errors as awq_pack.
+ */
+int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, int layout,
+               void *stream);
+
+/*
+ * awq_workspace_bytes -- bytes of device workspace the given call needs
+ * (0 if none).  split_k as passed to the call (0 = automatic).  For W4A8,
+ * group_size is the one passed to w4a8_gemm.
+ * Workspace rules ([P2]: one workspace per device, reused by every layer):
+ *  - it is caller-owned, at least 256-byte aligned, and may be shared by any
+ *    number of calls that are ordered on one stream;
+ *  - its first 16 KiB are a counter region (one int32 per output tile of a
+ *    split-K launch, whatever the call's shape); the rest holds fp32 / int32
+ *    partial sums;
+ *  - it must be zero-filled once when allocated; every call leaves the
+ *    counter region zero again, so no per-call clearing is needed;
+ *  - calls that overlap in time (different streams) need separate workspaces.
+ * Returns 0 for invalid arguments.
+ */
+size_t awq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int group_size, int split_k);
+
+/*
+ * awq_gemm_w4a16 -- Y = X . dequant(qweight, qzeros, scales) for any M >= 1
+ * (the prefill path of the [P1] dispatch; also correct for small M).
+ *   x:       device, [M, K] fp16 or bf16 (dtype).
+ *   qweight: device, int32 [K, N/8], AWQ_LAYOUT_N8.
+ *   scales:  device, [K/G, N] in the activation dtype.
+ *   qzeros:  device, int32 [K/G, N/8], AWQ_LAYOUT_N8; NULL = symmetric
+ *            weights with z = 8 ([P2]).
+ *   y:       device, [M, N] in the activation dtype (written, not accumulated).
+ *   group_size G in {32, 64, 128}; K % G == 0; N % 8 == 0; M, N, K >= 1.
+ *   split_k: number of K slices reduced through the workspace (0 = chosen by
+ *            the library, 1 = none, at most K/32).
+ * Numerics: each weight is dequantised exactly to (q - z) and multiplied by s
+ * with one rounding to the activation dtype; products accumulate in fp32 on
+ * the matrix cores; the output is rounded to nearest even.
+ * Errors: AWQ_EINVAL (shapes, pointers, dtype, G), AWQ_EALIGN, AWQ_EWORKSPACE,
+ * AWQ_EHIP.
+ */
+int awq_gemm_w4a16(const void *x, const int32_t *qweight, const void *scales,
+                   const int32_t *qzeros, void *y, int64_t M, int64_t N, int64_t K,
+                   int group_size, int dtype, int split_k, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * awq_gemv_w4a16 -- the decode path of the [P1] dispatch: same tensors,
+ * formats, numerics and errors as awq_gemm_w4a16, for 1 <= M <= 8
+ * (AWQ_EUNSUPPORTED otherwise).  The weight stream is split over K across
+ * the whole GPU and reduced through the workspace.
+ */
+int awq_gemv_w4a16(const void *x, const int32_t *qweight, const void *scales,
+                   const int32_t *qzeros, void *y, int64_t M, int64_t N, int64_t K,
+                   int group_size, int dtype, int split_k, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * w4a8_quant_act -- dynamic per-token int8 quantisation of fp16 activations
+ * ([P5], the dynamic_quant helper):
+ *   s1[m]   = float( fp16( max_k |x[m,k]| / 127 ) )
+ *   a8[m,k] = clamp( round_half_even( float(x[m,k]) / s1[m] ), -128, 127 )
+ * with a correctly rounded fp32 divide; a row whose s1 is 0 gives a8 = 0.
+ *   x: device fp16 [M, K]; a8: device int8 [M, K]; s1: device fp32 [M].
+ * Errors: AWQ_EINVAL (M, K < 1, pointers), AWQ_EALIGN, AWQ_EHIP.
+ */
+int w4a8_quant_act(const void *x_f16, int8_t *a8, float *s1, int64_t M, int64_t K, void *stream);
+
+/*
+ * w4a8_gemm -- QQQ-style W4A8 GEMM ([P5]):
+ *   acc[m,n] = sum_k a8[m,k] * w8[k,n]   (exact, int32)
+ *   y[m,n]   = fp16( acc[m,n] * s1[m] * s2[n] )   (fp32 arithmetic, RNE)
+ * with w8 = q for per-channel weights (s3 == NULL, group_size == -1) and
+ * w8 = q * s3[k/G, n] for per-group weights, where s3 holds small integers
+ * 1..16 stored as fp16 so that w8 stays an int8.
+ *   a8:       device int8 [M, K] (from w4a8_quant_act).
+ *   b_packed: device int32 [K/8, N], W4A8_LAYOUT_K8 (q in -8..7).
+ *   s1:       device fp32 [M];  s2: device fp16 [N];  s3: device fp16 [K/G, N] or NULL.
+ *   y:        device fp16 [M, N].
+ *   acc_out:  device int32 [M, N] or NULL: if given, the exact accumulators
+ *             are written too (for checking).
+ *   K % 64 == 0; N % 8 == 0; group_size -1 (per-channel) or one of 32, 64, 128.
+ * Errors: AWQ_EINVAL, AWQ_EALIGN, AWQ_EWORKSPACE, AWQ_EUNSUPPORTED
+ * (K % 64 != 0), AWQ_EHIP.
+ */
+int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const void *s2_f16,
+              const void *s3_f16, void *y_f16, int32_t *acc_out, int64_t M, int64_t N,
+              int64_t K, int group_size, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ4_H */

@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/awq4.h declares, and argument validation returns the documented status
+codes before anything is enqueued (so these calls never reach HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_weight_only_awq_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared_functions()
+    for n in ("awq_pack", "awq_unpack", "awq_gemm_w4a16", "awq_gemv_w4a16", "w4a8_quant_act", "w4a8_gemm",
+              "awq_workspace_bytes", "awq_status_str", "awq_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    lib = L.lib()
+    for code in (L.AWQ_OK, L.AWQ_EINVAL, L.AWQ_EUNSUPPORTED, L.AWQ_EWORKSPACE, L.AWQ_EALIGN, L.AWQ_EHIP):
+        s = lib.awq_status_str(code).decode()
+        assert s.startswith("AWQ_")
+    assert lib.awq_status_str(12345).decode() == "AWQ_UNKNOWN"
+    assert lib.awq_version() == 100
+
+
+# Fake "device" pointers: validation only looks at null-ness and alignment, and
+# every call below is rejected before any launch.
+A = 0x10000
+MIS = 0x10002
+
+
+def _w4a16(fn, x=A, qw=A, s=A, qz=A, y=A, M=1, N=4096, K=4096, G=128, dt=0, split=0, ws=None, wsb=0):
+    return getattr(L.lib(), fn)(x, qw, s, qz, y, M, N, K, G, dt, split, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["awq_gemm_w4a16", "awq_gemv_w4a16"])
+def test_w4a16_validation(fn):
+    E = L
+    assert _w4a16(fn, x=None) == E.AWQ_EINVAL
+    assert _w4a16(fn, qw=None) == E.AWQ_EINVAL
+    assert _w4a16(fn, s=None) == E.AWQ_EINVAL
+    assert _w4a16(fn, y=None) == E.AWQ_EINVAL
+    assert _w4a16(fn, M=0) == E.AWQ_EINVAL
+    assert _w4a16(fn, N=12) == E.AWQ_EINVAL          # N % 8
+    assert _w4a16(fn, G=16) == E.AWQ_EINVAL          # unsupported group
+    assert _w4a16(fn, G=256) == E.AWQ_EINVAL
+    assert _w4a16(fn, K=4000) == E.AWQ_EINVAL        # K % G
+    assert _w4a16(fn, dt=2) == E.AWQ_EINVAL
+    assert _w4a16(fn, split=-1) == E.AWQ_EINVAL
+    assert _w4a16(fn, split=129) == E.AWQ_EINVAL     # > K/32
+    assert _w4a16(fn, x=MIS) == E.AWQ_EALIGN
+    assert _w4a16(fn, qz=MIS) == E.AWQ_EALIGN
+    # a valid split-K request without workspace
+    assert _w4a16(fn, M=1, split=8) == E.AWQ_EWORKSPACE
+    assert _w4a16(fn, M=1, split=8, ws=A, wsb=16) == E.AWQ_EWORKSPACE
+
+
+def test_gemv_rejects_more_than_8_rows():
+    assert _w4a16("awq_gemv_w4a16", M=9) == L.AWQ_EUNSUPPORTED
+
+
+def test_workspace_bytes():
+    lib = L.lib()
+    op_gemm, op_gemv, op8 = L.AWQ_OP_GEMM_W4A16, L.AWQ_OP_GEMV_W4A16, L.AWQ_OP_W4A8_GEMM
+    # no split requested -> no workspace
+    assert lib.awq_workspace_bytes(op_gemm, 2048, 4096, 4096, 128, 1) == 0
+    # split 8 of a M=1, N=4096 GEMV: the fixed 16 KiB counter region + 8 fp32 partial rows
+    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == 16384 + 8 * 4096 * 4
+    # automatic split for decode needs a workspace
+    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 0) > 0
+    # invalid shapes -> 0
+    assert lib.awq_workspace_bytes(op_gemv, 9, 4096, 4096, 128, 0) == 0
+    assert lib.awq_workspace_bytes(op_gemm, 1, 4095, 4096, 128, 0) == 0
+    assert lib.awq_workspace_bytes(op8, 1, 8192, 21760, -1, 0) > 0
+    assert lib.awq_workspace_bytes(op8, 1, 8192, 21700, -1, 0) == 0
+    assert lib.awq_workspace_bytes(99, 1, 8192, 4096, 128, 0) == 0
+
+
+def test_w4a8_validation():
+    lib = L.lib()
+
+    def g(a8=A, b=A, s1=A, s2=A, s3=None, y=A, acc=None, M=1, N=8192, K=21760, G=-1, ws=None, wsb=0):
+        return lib.w4a8_gemm(a8, b, s1, s2, s3, y, acc, M, N, K, G, ws, wsb, None)
+
+    assert g(a8=None) == L.AWQ_EINVAL
+    assert g(s2=None) == L.AWQ_EINVAL
+    assert g(N=12) == L.AWQ_EINVAL
+    assert g(G=128) == L.AWQ_EINVAL            # grouped without s3
+    assert g(s3=A) == L.AWQ_EINVAL             # per-channel with s3
+    assert g(s3=A, G=48) == L.AWQ_EINVAL
+    assert g(K=21700) == L.AWQ_EUNSUPPORTED    # K % 64
+    assert g(K=262144) == L.AWQ_EUNSUPPORTED   # int32 accumulator bound
+    assert g(acc=MIS) == L.AWQ_EALIGN
+    assert g() == L.AWQ_EWORKSPACE             # decode split needs a workspace
+    assert lib.w4a8_quant_act(None, A, A, 1, 16, None) == L.AWQ_EINVAL
+    assert lib.w4a8_quant_act(A, A, A, 0, 16, None) == L.AWQ_EINVAL
+    assert lib.w4a8_quant_act(MIS, A, A, 1, 16, None) == L.AWQ_EALIGN
+
+
+def test_pack_validation():
+    lib = L.lib()
+    assert lib.awq_pack(A, A, 4, 12, L.AWQ_LAYOUT_N8, None, None) == L.AWQ_EINVAL
+    assert lib.awq_pack(A, A, 12, 8, L.W4A8_LAYOUT_K8, None, None) == L.AWQ_EINVAL
+    assert lib.awq_pack(A, A, 8, 8, 7, None, None) == L.AWQ_EINVAL
+    assert lib.awq_pack(None, A, 8, 8, L.AWQ_LAYOUT_N8, None, None) == L.AWQ_EINVAL
+    assert lib.awq_pack(MIS, A, 8, 8, L.AWQ_LAYOUT_N8, None, None) == L.AWQ_EALIGN
+    assert lib.awq_pack(None, None, 0, 8, L.AWQ_LAYOUT_N8, None, None) == L.AWQ_OK  # empty: no-op
+    assert lib.awq_unpack(A, A, 8, -8, L.AWQ_LAYOUT_N8, None) == L.AWQ_EINVAL
+    assert lib.awq_unpack(None, None, 8, 0, L.W4A8_LAYOUT_K8, None) == L.AWQ_OK

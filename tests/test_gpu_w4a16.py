@@ -1,0 +1,181 @@
+"""GPU W4A16 GEMV / GEMM vs the fp64 CPU oracle.
+
+Shapes are the workloads the pages measure on (opt-125m fc1; Llama-2-7B decode
+layers; Llama-3-8B prefill layers; the K=4096, N=14336 group-size / dtype /
+symmetric variants) plus ragged and degenerate edge cases.  Full-size prefill
+cases are checked on sampled rows (every column tile is still covered)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_awq_amd as awq
+import synthgen
+from gpu_helpers import THREADS, check_fp, dev, orc, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = 0, 1
+
+
+def _run(case, entry="gemm", split_k=0, rows=None):
+    x, qw, s, qz = to_dev(case.x, case.qweight, case.scales, case.qzeros)
+    fn = awq.gemm_w4a16 if entry == "gemm" else awq.gemv_w4a16
+    y = fn(x, qw, s, qz, case.G, split_k=split_k)
+    torch.cuda.synchronize()
+    xs = case.x if rows is None else case.x[torch.as_tensor(rows)]
+    y64 = orc().w4a16(xs, case.qweight, case.scales, case.qzeros, case.G,
+                      BF16 if case.dtype == "bf16" else F16, nthreads=THREADS)
+    yg = y.cpu() if rows is None else y.cpu()[torch.as_tensor(rows)]
+    return yg, y64, y
+
+
+def test_opt125m_fc1_m16():
+    """opt-125m fc1: M=16, K=768, N=3072, g128, seed 0 -- checked in full."""
+    c = synthgen.w4a16_case(16, 768, 3072, 128, seed=0)
+    yg, y64, _ = _run(c)
+    check_fp(yg, y64, "f16", "opt125m fc1")
+
+
+LLAMA2_7B = [(4096, 12288), (4096, 4096), (4096, 22016), (11008, 4096)]
+
+
+@pytest.mark.parametrize("K,N", LLAMA2_7B)
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_gemv_llama2_7b(M, K, N):
+    c = synthgen.w4a16_case(M, K, N, 128)
+    yg, y64, _ = _run(c, "gemv")
+    check_fp(yg, y64, "f16", f"gemv M={M} K={K} N={N}")
+
+
+LLAMA3_8B = [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)]
+
+
+@pytest.mark.parametrize("K,N", LLAMA3_8B)
+@pytest.mark.parametrize("M", [64, 256, 1024, 2048, 4096])
+def test_gemm_llama3_8b_sampled(M, K, N):
+    c = synthgen.w4a16_case(M, K, N, 128)
+    rows = sample_rows(M, seed=M + N)
+    yg, y64, _ = _run(c, "gemm", rows=rows)
+    check_fp(yg, y64, "f16", f"gemm M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M", [1, 512])
+def test_group_dtype_sym_variants(M, G, dtype, sym):
+    c = synthgen.w4a16_case(M, 4096, 14336, G, dtype=dtype, sym=sym)
+    rows = None if M == 1 else sample_rows(M, seed=G)
+    yg, y64, _ = _run(c, "gemv" if M == 1 else "gemm", rows=rows)
+    check_fp(yg, y64, dtype, f"variant M={M} G={G} {dtype} sym={sym}")
+
+
+def test_symmetric_equals_zero_point_8():
+    """qzeros = NULL must equal qzeros filled with 0x88888888, bit for bit."""
+    for M in (1, 40, 300):
+        c = synthgen.w4a16_case(M, 1024, 2048, 64, sym=True)
+        x, qw, s = to_dev(c.x, c.qweight, c.scales)
+        z8 = torch.full((1024 // 64, 2048 // 8), -0x77777778, dtype=torch.int32, device=dev())
+        a = awq.gemm_w4a16(x, qw, s, None, 64)
+        b = awq.gemm_w4a16(x, qw, s, z8, 64)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), M
+
+
+def test_exact_special_case_bit_identical():
+    """z = 0, s = 2^-3, x in {-1,0,1}: every sum is an exact dyadic, so the fp16
+    output must equal the rounded oracle value bit for bit (pins layout and
+    indexing of every kernel variant)."""
+    g = torch.Generator().manual_seed(3)
+    for (M, K, N) in [(1, 128, 1024), (3, 256, 136), (8, 128, 4096), (16, 384, 512), (29, 256, 264),
+                      (64, 256, 768), (200, 512, 520)]:
+        X = torch.randint(-1, 2, (M, K), generator=g).to(torch.float16)
+        qw = torch.randint(-(2 ** 31), 2 ** 31, (K, N // 8), generator=g, dtype=torch.int64).to(torch.int32)
+        qz = torch.zeros(K // 128, N // 8, dtype=torch.int32)
+        s = torch.full((K // 128, N), 0.125, dtype=torch.float16)
+        y64 = orc().w4a16(X, qw, s, qz, 128)
+        exp = torch.from_numpy(y64).to(torch.float16)
+        for entry in (("gemv", "gemm") if M <= 8 else ("gemm",)):
+            fn = awq.gemv_w4a16 if entry == "gemv" else awq.gemm_w4a16
+            for split in (0, 1, 3):
+                if split > K // 32:
+                    continue
+                y = fn(*to_dev(X, qw, s, qz), 128, split_k=split)
+                torch.cuda.synchronize()
+                assert torch.equal(y.cpu(), exp), (M, K, N, entry, split)
+
+
+@pytest.mark.parametrize("M,K,N,G", [(1, 32, 8, 32), (5, 96, 24, 32), (17, 64, 136, 64), (33, 128, 264, 128),
+                                     (100, 192, 72, 64), (129, 256, 1032, 128), (2, 4096, 8, 128),
+                                     (300, 128, 40, 32)])
+def test_ragged_and_small_shapes(M, K, N, G):
+    c = synthgen.w4a16_case(M, K, N, G)
+    yg, y64, _ = _run(c)
+    check_fp(yg, y64, "f16", f"ragged gemm {M}x{K}x{N} g{G}")
+    if M <= 8:
+        yg, y64, _ = _run(c, "gemv")
+        check_fp(yg, y64, "f16", f"ragged gemv {M}x{K}x{N} g{G}")
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 16, 128])
+def test_explicit_split_k(split):
+    c = synthgen.w4a16_case(4, 4096, 1024, 128)
+    yg, y64, _ = _run(c, "gemv", split_k=split)
+    check_fp(yg, y64, "f16", f"gemv split={split}")
+    c = synthgen.w4a16_case(96, 4096, 512, 128)
+    yg, y64, _ = _run(c, "gemm", split_k=split)
+    check_fp(yg, y64, "f16", f"gemm split={split}")
+
+
+def test_deterministic_and_workspace_reuse():
+    """Same inputs give the same bits; the shared workspace's counters are left
+    re-armed, so back-to-back split-K calls stay correct."""
+    c = synthgen.w4a16_case(1, 4096, 4096, 128)
+    x, qw, s, qz = to_dev(c.x, c.qweight, c.scales, c.qzeros)
+    outs = [awq.gemv_w4a16(x, qw, s, qz, 128) for _ in range(5)]
+    c2 = synthgen.w4a16_case(3, 4096, 4096, 128)
+    o2 = awq.gemv_w4a16(*to_dev(c2.x, c2.qweight, c2.scales, c2.qzeros), 128)
+    outs.append(awq.gemv_w4a16(x, qw, s, qz, 128))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    check_fp(outs[0].cpu(), orc().w4a16(c.x, c.qweight, c.scales, c.qzeros, 128, nthreads=THREADS), "f16")
+    check_fp(o2.cpu(), orc().w4a16(c2.x, c2.qweight, c2.scales, c2.qzeros, 128, nthreads=THREADS), "f16")
+
+
+def test_shared_workspace_across_shapes():
+    """Calls of different shapes and tile counts share one workspace in turn
+    (few tiles / many splits, then many tiles / few splits): each must find
+    its split-K counters zero and be correct (regression test for a counter
+    region whose size depended on the call)."""
+    seq = [("gemv", 4, 4096, 1024), ("gemm", 64, 4096, 512), ("gemv", 8, 4096, 22016),
+           ("gemm", 1024, 4096, 4096), ("gemv", 1, 4096, 4096), ("gemm", 512, 4096, 14336),
+           ("gemv", 2, 11008, 4096)]
+    for entry, M, K, N in seq:
+        c = synthgen.w4a16_case(M, K, N, 128)
+        rows = None if M <= 64 else sample_rows(M, seed=1)
+        yg, y64, _ = _run(c, entry, rows=rows)
+        check_fp(yg, y64, "f16", f"{entry} M={M} K={K} N={N}")
+
+
+def test_output_guard_band():
+    """The kernels write exactly M*N outputs: a sentinel band after y survives."""
+    for (M, K, N) in [(1, 4096, 4096), (7, 1024, 1032), (70, 512, 776)]:
+        c = synthgen.w4a16_case(M, K, N, 128)
+        x, qw, s, qz = to_dev(c.x, c.qweight, c.scales, c.qzeros)
+        buf = torch.full((M * N + 4096,), float("nan"), dtype=torch.float16, device=dev())
+        y = buf[:M * N].view(M, N)
+        (awq.gemv_w4a16 if M <= 8 else awq.gemm_w4a16)(x, qw, s, qz, 128, out=y)
+        torch.cuda.synchronize()
+        assert torch.isnan(buf[M * N:]).all()
+        check_fp(y.cpu(), orc().w4a16(c.x, c.qweight, c.scales, c.qzeros, 128, nthreads=THREADS), "f16")
+
+
+def test_linear_dispatch_rule():
+    """More than 8 rows goes to the GEMM entry, up to 8 to the GEMV entry."""
+    c = synthgen.w4a16_case(9, 512, 256, 128)
+    y = awq.linear_w4a16(*to_dev(c.x, c.qweight, c.scales, c.qzeros), 128)
+    torch.cuda.synchronize()
+    check_fp(y.cpu(), orc().w4a16(c.x, c.qweight, c.scales, c.qzeros, 128), "f16")
+    with pytest.raises(awq.AWQError):
+        awq.gemv_w4a16(*to_dev(c.x, c.qweight, c.scales, c.qzeros), 128)

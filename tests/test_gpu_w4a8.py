@@ -1,0 +1,98 @@
+"""GPU W4A8 (QQQ-style) vs the CPU oracle: activation quantisation and the int32
+accumulators bit-exact, the fp16 output within the fp16 tolerance of the fp64
+result computed from the same quantised activations."""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_only_awq_amd as awq
+import synthgen
+from gpu_helpers import THREADS, check_fp, dev, orc, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_check(x_cpu):
+    a8, s1 = awq.quant_act(x_cpu.to(dev()))
+    torch.cuda.synchronize()
+    ea8, es1 = orc().quant_act(x_cpu)
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), es1.view(np.uint32))
+    assert np.array_equal(a8.cpu().numpy(), ea8)
+    return a8, s1, ea8, es1
+
+
+@pytest.mark.parametrize("M,K", [(1, 21760), (16, 21760), (64, 21760), (256, 4096), (3, 7), (5, 1000)])
+def test_quant_act_bit_exact(M, K):
+    x = synthgen.activations(M, K, seed=M * 131 + K)
+    x = x * torch.logspace(-4, 3, M).to(torch.float16)[:, None]  # rows across magnitudes
+    _quant_check(x.to(torch.float16))
+
+
+def test_quant_act_edge_rows():
+    """Worked examples, a zero row, a subnormal-scale row (clamp active) and
+    ties: bit-exact with the oracle."""
+    rows = [[127, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -127],
+            [0.0] * 8,
+            [2.0 ** -14, -(2.0 ** -14), 0, 0, 2.0 ** -15, 0, 0, 0],
+            [65504.0, -65504.0, 1, 2, 3, 4, 5, 6]]
+    x = torch.tensor(rows, dtype=torch.float16)
+    a8, s1, ea8, es1 = _quant_check(x)
+    assert a8.cpu()[0].tolist() == [127, 2, 4, -2, -4, 0, 2, -127]
+    assert a8.cpu()[2, :2].tolist() == [127, -128]
+    assert float(s1.cpu()[1]) == 0.0
+
+
+def _w4a8_case_check(M, K, N, G, full_rows=False):
+    c = synthgen.w4a8_case(M, K, N, G)
+    x, b, s2, s3 = to_dev(c.x, c.b, c.s2, c.s3)
+    a8, s1 = awq.quant_act(x)
+    y, acc = awq.w4a8_gemm(a8, b, s1, s2, s3, G, want_acc=True)
+    torch.cuda.synchronize()
+    ea8, es1 = orc().quant_act(c.x)
+    assert np.array_equal(a8.cpu().numpy(), ea8)
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), es1.view(np.uint32))
+    rows = np.arange(M) if (full_rows or M <= 16) else sample_rows(M, seed=M)
+    eacc, y64 = orc().w4a8(ea8[rows], c.b, es1[rows], c.s2, c.s3, G, nthreads=THREADS)
+    assert np.abs(eacc).max() < 2 ** 31
+    gacc = acc.cpu().numpy()[rows].astype(np.int64)
+    assert np.array_equal(gacc, eacc), f"acc mismatch at {np.argwhere(gacc != eacc)[:5]}"
+    check_fp(y.cpu()[torch.as_tensor(rows)], y64, "f16", f"w4a8 M={M} K={K} N={N} G={G}")
+
+
+@pytest.mark.parametrize("G", [-1, 128])
+@pytest.mark.parametrize("M", [1, 16, 64, 256, 1024])
+def test_w4a8_qqq_shape(M, G):
+    """The QQQ GEMM shape N=8192, K=21760 (per-channel and g128)."""
+    _w4a8_case_check(M, 21760, 8192, G)
+
+
+@pytest.mark.parametrize("G", [-1, 32, 64, 128])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2048, 4096, 4096), (1, 4096, 14336), (5, 64, 8),
+                                   (17, 128, 136), (40, 256, 24), (129, 512, 1032), (33, 4096, 520)])
+def test_w4a8_shapes(M, K, N, G):
+    if G > 0 and K % G:
+        pytest.skip("K not a multiple of G")
+    _w4a8_case_check(M, K, N, G)
+
+
+def test_w4a8_group16_equals_channel():
+    """Per-group with every s3 = 16 and s2/16 reproduces per-channel exactly."""
+    c = synthgen.w4a8_case(37, 1024, 512, -1)
+    x, b, s2 = to_dev(c.x, c.b, c.s2)
+    a8, s1 = awq.quant_act(x)
+    y1, acc1 = awq.w4a8_gemm(a8, b, s1, s2, None, -1, want_acc=True)
+    s3 = torch.full((1024 // 64, 512), 16.0, dtype=torch.float16, device=dev())
+    y2, acc2 = awq.w4a8_gemm(a8, b, s1, s2 / 16, s3, 64, want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(acc2, 16 * acc1)
+    assert torch.equal(y1, y2)
+
+
+def test_w4a8_deterministic():
+    c = synthgen.w4a8_case(1, 21760, 8192, -1)
+    x, b, s2 = to_dev(c.x, c.b, c.s2)
+    a8, s1 = awq.quant_act(x)
+    ys = [awq.w4a8_gemm(a8, b, s1, s2) for _ in range(4)]
+    torch.cuda.synchronize()
+    for yy in ys[1:]:
+        assert torch.equal(yy, ys[0])
