@@ -22,32 +22,25 @@ static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry) {
-    (void)G;
+    (void)gemv_entry;
     W4A16Plan p{};
     const int64_t nw = N / 8;
     const int64_t T = K / 32;
     int64_t tiles;
-    if (M <= 32) {
+    if (M <= 16) {
+        // decode kernel: one 32*cs-wide K chunk per wave, 4 chunks per
+        // workgroup; the K split is fixed by the chunking (split_k is ignored)
         p.kind = 0;
-        p.mt = M <= 16 ? 1 : 2;
-        if (M <= 4 && nw % 4 == 0)
-            p.blk = 4;
-        else if (M <= 16 && nw % 2 == 0)
-            p.blk = 2;
-        else
-            p.blk = 1;
+        p.blk = nw % 2 == 0 ? 2 : 1;  // 128 B per k-row per wave: whole cache lines
+        p.cs = G >= 64 ? 2 : 1;
         p.tiles_n = (int)cdiv(nw, 16 * p.blk);
         p.tiles_m = 1;
+        p.splits = (int)cdiv(K / (32 * p.cs), 4);
         tiles = p.tiles_n;
-        int64_t s = cdiv(kTargetWorkgroups, tiles);
-        // every wave should own at least one 32-k step, and the fp32 partials
-        // (written and read once per split) should stay small next to the weights
-        s = std::min<int64_t>(s, std::max<int64_t>(1, T / 4));
-        s = std::min<int64_t>(s, std::max<int64_t>(1, K / (64 * M)));
-        p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
     } else {
         p.kind = 1;
         p.blk = 1;
+        p.cs = 1;
         p.mt = M >= 128 ? 4 : (M >= 64 ? 2 : 1);
         const int64_t bm = 32 * p.mt;
         p.tiles_n = (int)cdiv(N, 256);
@@ -60,11 +53,10 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
             s = std::min<int64_t>(s, 16);
         }
         p.splits = (int)std::max<int64_t>(1, s);
+        if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
+        if (tiles > kMaxSplitTiles) p.splits = 1;
     }
-    (void)gemv_entry;
-    if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
-    if (tiles > kMaxSplitTiles) p.splits = 1;
-    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)p.splits * M * N * 4 : 0;
+    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)M * N * sizeof(int64_t) : 0;
     return p;
 }
 
@@ -82,7 +74,6 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         tiles = p.tiles_n;
         int64_t s = cdiv(kTargetWorkgroups, tiles);
         s = std::min<int64_t>(s, std::max<int64_t>(1, T / 4));
-        s = std::min<int64_t>(s, std::max<int64_t>(1, K / (32 * M)));
         p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
     } else {
         p.kind = 1;
@@ -100,7 +91,7 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         p.splits = (int)std::max<int64_t>(1, s);
     }
     if (tiles > kMaxSplitTiles) p.splits = 1;
-    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)p.splits * M * N * 4 : 0;
+    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)M * N * sizeof(int32_t) : 0;
     return p;
 }
 
@@ -138,11 +129,11 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     if (rc != AWQ_OK) return rc;
     if (p.splits > 1) {
         p.counters = static_cast<int *>(workspace);
-        p.partials = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
+        p.acc64 = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + kCounterBytes);
     }
     W4A16Args a{x, qweight, scales, qzeros, y, M, N, K, G, dtype};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return hip_status(p.kind == 0 ? launch_w4a16_skinny(a, p, st) : launch_w4a16_tiled(a, p, st));
+    return hip_status(p.kind == 0 ? launch_w4a16_decode(a, p, st) : launch_w4a16_tiled(a, p, st));
 }
 
 }  // namespace awq4
@@ -252,7 +243,7 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
     if (rc != AWQ_OK) return rc;
     if (p.splits > 1) {
         p.counters = static_cast<int *>(workspace);
-        p.partials = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
+        p.acc32 = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
     }
     W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
     return hip_status(launch_w4a8(a, p, static_cast<hipStream_t>(stream)));

@@ -125,25 +125,69 @@ __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K completion.  Every workgroup of a tile has written its partial
-// tile; the one that arrives last (counted on an agent-scope atomic) sums the
-// partials in split order 0..S-1 and writes the output, then re-arms the
-// counter to zero for the next call.  Returns true in the last workgroup.
-// All threads of the workgroup must call it.
-__device__ __forceinline__ bool splitk_arrive(int *counter, int S) {
+// Split-K completion without cache-flushing fences.
+//
+// Workgroups that share an output tile add their partial sums into a zeroed
+// accumulator in the workspace with device-scope read-modify-write atomics,
+// which are coherent across all XCDs.  fp32 partials are added as int64 fixed
+// point (exact, so the sum does not depend on the order of arrival and every
+// run gives the same bits); int32 partials are added as they are.  Each
+// atomic returns its old value, so once a thread has consumed the returns its
+// adds have been performed.  After a barrier one thread counts the workgroup
+// in; the last of the S workgroups reads every accumulator back with an
+// atomic exchange against zero (leaving it ready for the next call), writes
+// the output, and re-arms the counter.
+
+// Fixed-point scale of the int64 accumulators: fp16 outputs need |y| < 2^31,
+// bf16 outputs get a wider range at 2^-16 resolution.
+template <int DT>
+struct FixedPoint {
+    static constexpr double kScale = DT == DT_BF16 ? 65536.0 : 4294967296.0;
+    static constexpr double kLimit = 9.0e18;  // saturate before int64 overflow
+};
+
+template <int DT>
+__device__ __forceinline__ int64_t to_fixed(float v) {
+    double d = (double)v * FixedPoint<DT>::kScale;
+    d = fmin(fmax(d, -FixedPoint<DT>::kLimit), FixedPoint<DT>::kLimit);
+    return (int64_t)__builtin_rint(d);
+}
+
+template <int DT>
+__device__ __forceinline__ float from_fixed(int64_t v) {
+    return (float)((double)v * (1.0 / FixedPoint<DT>::kScale));
+}
+
+// Adds v and returns the previous value (returning form: the caller consumes
+// it, which waits until the add has been performed).
+__device__ __forceinline__ int64_t atomic_add_i64(int64_t *p, int64_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t atomic_add_i32(int32_t *p, int32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int64_t atomic_take_i64(int64_t *p) {
+    return __hip_atomic_exchange(p, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t atomic_take_i32(int32_t *p) {
+    return __hip_atomic_exchange(p, (int32_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every thread of the workgroup after its atomic adds; `seen` is
+// any value derived from the atomics' returns (consuming it orders the adds
+// before the count).  Returns true in the last of S workgroups of the tile.
+__device__ __forceinline__ bool splitk_count(int *counter, int S, int64_t seen) {
     __shared__ int s_last;
-    __threadfence();  // release this thread's partial-tile writes
+    if (seen == INT64_MIN) s_last = 2;  // never true in practice; keeps the returns live
     __syncthreads();
     if (threadIdx.x == 0) {
-        int old = atomicAdd(counter, 1);
-        int last = (old == S - 1);
-        if (last) atomicExch(counter, 0);
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == S - 1;
+        if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last;
     }
     __syncthreads();
-    bool last = s_last != 0;
-    if (last) __threadfence();  // acquire the other workgroups' partials
-    return last;
+    return s_last == 1;
 }
 
 }  // namespace awq4

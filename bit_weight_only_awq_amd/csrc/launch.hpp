@@ -22,16 +22,17 @@ struct W4A16Args {
 
 // Kernel choice and grid for one W4A16 call (pure function of the shape).
 struct W4A16Plan {
-    int kind;     // 0 = skinny, 1 = tiled
-    int blk;      // skinny: word-columns per lane (1, 2, 4)
-    int mt;       // skinny: row tiles (M <= 16*mt); tiled: row tiles per wave
+    int kind;     // 0 = decode kernel, 1 = tiled kernel
+    int blk;      // decode: word-columns per lane (1, 2, 4)
+    int cs;       // decode: 32-k steps per wave chunk (1, 2)
+    int mt;       // tiled: row tiles per wave (1, 2, 4)
     int tiles_n;  // grid x
     int tiles_m;  // tiled: grid y
-    int splits;   // split-K factor (1 = none)
+    int splits;   // workgroups along K (1 = none); decode: grid y
     size_t workspace_bytes;
     // filled in by the caller from the workspace pointer
     int *counters;
-    float *partials;
+    int64_t *acc64;
 };
 
 struct W4A8Args {
@@ -53,19 +54,21 @@ struct W4A8Plan {
     int tiles_n, tiles_m, splits;
     size_t workspace_bytes;
     int *counters;
-    int32_t *partials;
+    int32_t *acc32;
 };
 
-// Every workspace starts with a fixed counter region (one int per output tile
-// of a split-K launch).  Its size does not depend on the call, so calls of
-// different shapes that share a workspace always find their counters zero.
-constexpr size_t kCounterBytes = 16384;
+// Workspace layout: a fixed counter region (one int per output tile of a
+// split-K launch) followed by the split-K accumulators (int64 fixed point for
+// W4A16, int32 for W4A8, one per output element).  Every call leaves both
+// zero again, and the counter region does not move with the shape, so calls
+// of different shapes can share one workspace.
+constexpr size_t kCounterBytes = 65536;
 constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry);
 W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);
 
-hipError_t launch_w4a16_skinny(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
+hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);

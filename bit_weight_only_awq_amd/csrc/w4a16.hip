@@ -7,80 +7,101 @@
 // nibbles of the first-generation AWQ order map and z = 8 when qzeros is
 // absent.
 //
-// Design (both kernels): no transpose through LDS.  A lane loads the packed
-// words of ONE word-column (8 output columns) at 8 consecutive k, pairs
-// consecutive-k words byte-wise with v_perm so that every 16-bit half holds
-// one k, and extracts column t from the pairs with one mask, giving the
-// matrix-core B operand of 8 consecutive k of that column directly.  Column t
+// Operand construction (both kernels): no transpose through LDS.  A lane
+// loads the packed words of ONE word-column (8 output columns) at 8
+// consecutive k, pairs consecutive-k words byte-wise with v_perm so that every
+// 16-bit half holds one k, and extracts column t from the pairs with one mask:
+// that is the matrix-core B operand of 8 consecutive k of column t.  Column t
 // of the word of lane j becomes B column j of the t-th MFMA, so one set of 8
-// MFMAs covers the 16 word-columns of a wave (128 output columns) and
-// output column = 8 * word_column(j) + t.  Dequantisation stays exact up to
-// one rounding (see device.hpp).
+// MFMAs covers the 16 word-columns of a wave (128 output columns), and output
+// column = 8 * word_column(j) + t.
 //
-//  * skinny kernel (decode, M <= 32): a workgroup of 4 waves owns 128*BLK
-//    output columns; its waves split a K slice, are reduced through LDS in a
-//    fixed order, and workgroups along K (split-K) are combined by the last
-//    one to arrive.  Weight loads are 4*BLK bytes per lane per k-row, fully
-//    coalesced per wave.
+//  * decode kernel (M <= 16): a wave owns one K chunk (32*CS values inside one
+//    quantisation group) of a 128*BLK column tile and issues every weight load
+//    of the chunk before using any, so the whole weight stream is in flight
+//    across the GPU.  The B operand is the exact integer (q - z); the group
+//    scale multiplies the fp32 sums once per chunk.  The 4 waves of a
+//    workgroup (4 consecutive chunks) are reduced through LDS, workgroups
+//    along K through fixed-point atomics (device.hpp).
 //  * tiled kernel (prefill): a workgroup of 4 waves (2 x 2) owns a
 //    (2*16*MTW) x 256 output tile; each wave runs the full K of its slice with
-//    MTW row tiles x 8 column MFMAs per 32-k step; optional split-K over the
-//    grid's z dimension.
+//    MTW row tiles x 8 column MFMAs per 32-k step, B = (q - z) * s rounded
+//    once to the activation type; optional split-K over the grid's z.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace awq4 {
 
-// Per-group dequant constants of one word-column for the 8 columns t.
-template <int DT, bool SYM>
-struct GroupConsts {
-    uint32_t zc[8];  // fp16: packed zero constant
-    uint32_t sc[8];  // fp16: packed scale
-    float sf[8];     // bf16: effective scale (s or s/16)
-    float zs[8];     // bf16: z*s
+// Zero-point constants of one word-column for its 8 columns (fp16 path:
+// packed -(1024+z) / -(64+z); bf16 path: z as float).
+template <int DT>
+struct ZeroConsts {
+    uint32_t zc[8];
+    float zf[8];
 };
 
 template <int DT, bool SYM>
-__device__ __forceinline__ void load_group(GroupConsts<DT, SYM> &c, const uint16_t *__restrict__ sc,
-                                           const uint32_t *__restrict__ qz, int N, int nw, int g, int wcol,
-                                           bool valid) {
-    u32x4 s4 = {0, 0, 0, 0};
-    uint32_t zw = 0x88888888u;
-    if (valid) {
-        s4 = *(const u32x4 *)(sc + (size_t)g * N + 8 * wcol);
-        if (!SYM) zw = qz[(size_t)g * nw + wcol];
-    }
+__device__ __forceinline__ void zero_consts(ZeroConsts<DT> &c, uint32_t zw) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        uint32_t sb = (s4[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;  // scale of column 8*wcol + t
-        uint32_t z = (zw >> (4 * col_nibble(t))) & 0xFu;
-        if (DT == DT_F16) {
+        const uint32_t z = SYM ? 8u : ((zw >> (4 * col_nibble(t))) & 0xFu);
+        if (DT == DT_F16)
             c.zc[t] = col_hi(t) ? zconst_f16<1>(z) : zconst_f16<0>(z);
-            c.sc[t] = sb | (sb << 16);
-        } else {
-            float s = bf16_bits_to_f32(sb);
-            c.sf[t] = col_hi(t) ? s * 0.0625f : s;
-            c.zs[t] = (float)z * s;
-        }
+        else
+            c.zf[t] = (float)z;
     }
 }
 
-// B operand (8 consecutive k of column t) from the pair registers px/py.
-template <int DT, bool SYM, int t>
-__device__ __forceinline__ u32x4 make_b(const uint32_t (&px)[4], const uint32_t (&py)[4],
-                                        const GroupConsts<DT, SYM> &c) {
-    u32x4 b;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        uint32_t src = col_src_y(t) ? py[p] : px[p];
-        uint32_t v = col_shift(t) ? (src >> 8) : src;
-        if (DT == DT_F16) {
-            b[p] = col_hi(t) ? dq_f16<1>(v, c.zc[t], c.sc[t]) : dq_f16<0>(v, c.zc[t], c.sc[t]);
+// Scale of column t from the 8 scales of a word-column (16 bytes).
+template <int DT>
+__device__ __forceinline__ uint32_t scale_bits(u32x4 s4, int t) {
+    return (s4[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+}
+template <int DT>
+__device__ __forceinline__ float scale_f32(u32x4 s4, int t) {
+    const uint32_t b = scale_bits<DT>(s4, t);
+    return DT == DT_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
+}
+
+// Exact (q - z) pair of column t from one pair register, as fp16 or bf16.
+template <int DT, int t>
+__device__ __forceinline__ uint32_t qz_pair(uint32_t src, const ZeroConsts<DT> &c) {
+    const uint32_t v = col_shift(t) ? (src >> 8) : src;
+    if (DT == DT_F16) {
+        const uint32_t mask = col_hi(t) ? 0x00F000F0u : 0x000F000Fu;
+        f16x2 h = bit_as<f16x2>((v & mask) | 0x64006400u);
+        f16x2 z = bit_as<f16x2>(c.zc[t]);
+        f16x2 d;
+        if (col_hi(t)) {
+            const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
+            d = h * sixteenth + z;
         } else {
-            b[p] = dq_bf16(v, col_hi(t) ? 0x00F000F0u : 0x000F000Fu, c.sf[t], c.zs[t]);
+            d = h + z;
         }
+        return bit_as<uint32_t>(d);
+    } else {
+        const uint32_t m = v & (col_hi(t) ? 0x00F000F0u : 0x000F000Fu);
+        const float mul = col_hi(t) ? 0.0625f : 1.0f;
+        const float d0 = __builtin_fmaf((float)(m & 0xFFu), mul, -c.zf[t]);          // exact
+        const float d1 = __builtin_fmaf((float)((m >> 16) & 0xFFu), mul, -c.zf[t]);  // exact
+        return (uint32_t)bit_as<uint16_t>((__bf16)d0) | ((uint32_t)bit_as<uint16_t>((__bf16)d1) << 16);
     }
-    return b;
+}
+
+// (q - z) * s pair of column t, rounded once to the activation type.
+template <int DT, int t>
+__device__ __forceinline__ uint32_t w_pair(uint32_t src, const ZeroConsts<DT> &c, uint32_t sc2, float sf) {
+    if (DT == DT_F16) {
+        return bit_as<uint32_t>(bit_as<f16x2>(qz_pair<DT, t>(src, c)) * bit_as<f16x2>(sc2));
+    } else {
+        const uint32_t v = col_shift(t) ? (src >> 8) : src;
+        const uint32_t m = v & (col_hi(t) ? 0x00F000F0u : 0x000F000Fu);
+        const float sm = col_hi(t) ? sf * 0.0625f : sf;
+        const float zs = c.zf[t] * sf;
+        const float w0 = __builtin_fmaf((float)(m & 0xFFu), sm, -zs);  // exact, one rounding below
+        const float w1 = __builtin_fmaf((float)((m >> 16) & 0xFFu), sm, -zs);
+        return (uint32_t)bit_as<uint16_t>((__bf16)w0) | ((uint32_t)bit_as<uint16_t>((__bf16)w1) << 16);
+    }
 }
 
 template <int DT>
@@ -90,165 +111,178 @@ __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // Load BLK consecutive packed words of one k-row (zero words out of range).
-// The skinny kernel streams each word exactly once (non-temporal hint); the
-// tiled kernel re-reads words from other row tiles and keeps them cacheable.
-template <int BLK, bool NT = true>
+// NT: streamed exactly once (non-temporal hint).
+template <int BLK, bool NT>
 __device__ __forceinline__ void load_words(const uint32_t *__restrict__ p, bool valid, uint32_t (&w)[BLK]) {
     if (!valid) {
 #pragma unroll
         for (int b = 0; b < BLK; ++b) w[b] = 0;
         return;
     }
-    if (!NT) {
-#pragma unroll
-        for (int b = 0; b < BLK; ++b) w[b] = p[b];
-        return;
-    }
     if (BLK == 4) {
-        u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+        u32x4 v = NT ? __builtin_nontemporal_load((const u32x4 *)p) : *(const u32x4 *)p;
 #pragma unroll
         for (int b = 0; b < BLK; ++b) w[b] = v[b];
     } else if (BLK == 2) {
-        u32x2 v = __builtin_nontemporal_load((const u32x2 *)p);
+        u32x2 v = NT ? __builtin_nontemporal_load((const u32x2 *)p) : *(const u32x2 *)p;
 #pragma unroll
         for (int b = 0; b < BLK; ++b) w[b] = v[b];
     } else {
-        w[0] = __builtin_nontemporal_load(p);
+        w[0] = NT ? __builtin_nontemporal_load(p) : *p;
     }
 }
 
+template <int DT>
+__device__ __forceinline__ u32x4 pack8_out(f32x4 v0, f32x4 v1) {
+    u32x4 o;
+    o[0] = (uint32_t)f32_to_out_bits(v0[0], DT) | ((uint32_t)f32_to_out_bits(v0[1], DT) << 16);
+    o[1] = (uint32_t)f32_to_out_bits(v0[2], DT) | ((uint32_t)f32_to_out_bits(v0[3], DT) << 16);
+    o[2] = (uint32_t)f32_to_out_bits(v1[0], DT) | ((uint32_t)f32_to_out_bits(v1[1], DT) << 16);
+    o[3] = (uint32_t)f32_to_out_bits(v1[2], DT) | ((uint32_t)f32_to_out_bits(v1[3], DT) << 16);
+    return o;
+}
+
 // ===========================================================================
-// Skinny kernel: M <= 16*MT, grid (col tiles, splits), 256 threads.
-// Dynamic LDS: 3 * M * (128*BLK) floats.
-template <int BLK, int MT, int DT, bool SYM>
-__global__ __launch_bounds__(256) void w4a16_skinny(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
+// Decode kernel.  grid = (column tiles, ceil(chunks / 4)), 256 threads.
+// Dynamic LDS: 3 * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
+// counters[column tiles] and int64 fixed-point accumulators acc64[M][N].
+template <int BLK, int CS, int DT, bool SYM>
+__global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
                                                     const uint16_t *__restrict__ sc,
                                                     const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
-                                                    float *__restrict__ part, int *__restrict__ counters, int M,
-                                                    int N, int K, int G, int S) {
+                                                    int64_t *__restrict__ acc64, int *__restrict__ counters, int M,
+                                                    int N, int K, int G) {
     extern __shared__ float red[];
     constexpr int COLS = 128 * BLK;
+    constexpr int CK = 32 * CS;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, gq = lane >> 4;
     const int nw = N >> 3;
-    const int tile = blockIdx.x, split = blockIdx.y;
+    const int tile = blockIdx.x;
     const int wcol0 = tile * 16 * BLK + j * BLK;  // lane's first word-column
     const bool col_ok = wcol0 < nw;
-    const int T = K >> 5;
-    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
-    const int w_lo = s_lo + (s_hi - s_lo) * wave / 4, w_hi = s_lo + (s_hi - s_lo) * (wave + 1) / 4;
+    const int chunk = blockIdx.y * 4 + wave;
+    const bool active = chunk < K / CK;
 
-    f32x4 acc[MT][BLK][8];
+    f32x4 acc[BLK][8];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int b = 0; b < BLK; ++b)
 #pragma unroll
-        for (int b = 0; b < BLK; ++b)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) acc[mt][b][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 8; ++t) acc[b][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    GroupConsts<DT, SYM> gc[BLK];
-    int gcur = -1;
-    for (int st = w_lo; st < w_hi; ++st) {
-        const int k0 = st * 32;
-        uint32_t w[8][BLK];
+    if (active) {
+        const int k0 = chunk * CK;
+        const int g = k0 / G;  // the chunk lies inside one group
+        // every load of the chunk is issued before any is used
+        uint32_t w[CS][8][BLK];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) load_words<BLK>(qw + (size_t)(k0 + 8 * gq + e) * nw + wcol0, col_ok, w[e]);
-        u32x4 a[MT];
+        for (int s = 0; s < CS; ++s)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = mt * 16 + j;
-            a[mt] = (m < M) ? *(const u32x4 *)(x + (size_t)m * K + k0 + 8 * gq) : (u32x4){0, 0, 0, 0};
-        }
-        const int g = k0 / G;
-        if (g != gcur) {
-            gcur = g;
-#pragma unroll
-            for (int b = 0; b < BLK; ++b) load_group<DT, SYM>(gc[b], sc, qz, N, nw, g, wcol0 + b, col_ok);
-        }
+            for (int e = 0; e < 8; ++e)
+                load_words<BLK, true>(qw + (size_t)(k0 + 32 * s + 8 * gq + e) * nw + wcol0, col_ok, w[s][e]);
+        u32x4 s4[BLK];
+        uint32_t zw[BLK];
 #pragma unroll
         for (int b = 0; b < BLK; ++b) {
-            uint32_t px[4], py[4];
+            s4[b] = col_ok ? *(const u32x4 *)(sc + (size_t)g * N + 8 * (wcol0 + b)) : (u32x4){0, 0, 0, 0};
+            zw[b] = (!SYM && col_ok) ? qz[(size_t)g * nw + wcol0 + b] : 0x88888888u;
+        }
+        u32x4 a[CS];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                px[p] = pair_x(w[2 * p][b], w[2 * p + 1][b]);
-                py[p] = pair_y(w[2 * p][b], w[2 * p + 1][b]);
-            }
-#define AWQ4_COL(T_)                                                                  \
-    {                                                                                 \
-        u32x4 bop = make_b<DT, SYM, T_>(px, py, gc[b]);                               \
-        _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) acc[mt][b][T_] =            \
-            mma<DT>(a[mt], bop, acc[mt][b][T_]);                                      \
+        for (int s = 0; s < CS; ++s)
+            a[s] = (j < M) ? *(const u32x4 *)(x + (size_t)j * K + k0 + 32 * s + 8 * gq) : (u32x4){0, 0, 0, 0};
+
+#pragma unroll
+        for (int b = 0; b < BLK; ++b) {
+            ZeroConsts<DT> zc;
+            zero_consts<DT, SYM>(zc, zw[b]);
+#pragma unroll
+            for (int s = 0; s < CS; ++s) {
+                uint32_t px[4], py[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    px[p] = pair_x(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                    py[p] = pair_y(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                }
+#define AWQ4_COL(T_)                                                                        \
+    {                                                                                       \
+        u32x4 bop;                                                                          \
+        _Pragma("unroll") for (int p = 0; p < 4; ++p) bop[p] =                              \
+            qz_pair<DT, T_>(col_src_y(T_) ? py[p] : px[p], zc);                             \
+        acc[b][T_] = mma<DT>(a[s], bop, acc[b][T_]);                                        \
     }
-            AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
+                AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
 #undef AWQ4_COL
+            }
+            // the group scale, once per chunk, on the fp32 sums
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc[b][t] *= scale_f32<DT>(s4[b], t);
         }
     }
 
     // Reduce the 4 waves: waves 1..3 park their partials in LDS
-    // (red[wave-1][m][c], c = local column); wave 0 adds them, in wave order,
-    // to its own registers and writes 8 consecutive columns per store.
+    // (red[wave-1][m][c]); wave 0 adds them in wave order.  With split-K the
+    // sum is parked in slot 0 (each lane of wave 0 overwrites only entries it
+    // has just read) for the whole workgroup to add out.
+    float *slot = red;
     if (wave > 0) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mt * 16 + 4 * gq + r;
-                if (m < M) {
-#pragma unroll
-                    for (int b = 0; b < BLK; ++b) {
-                        float *dst = red + ((size_t)(wave - 1) * M + m) * COLS + 8 * (j * BLK + b);
-                        *(f32x4 *)dst = (f32x4){acc[mt][b][0][r], acc[mt][b][1][r], acc[mt][b][2][r], acc[mt][b][3][r]};
-                        *(f32x4 *)(dst + 4) = (f32x4){acc[mt][b][4][r], acc[mt][b][5][r], acc[mt][b][6][r], acc[mt][b][7][r]};
-                    }
-                }
-            }
-    }
-    __syncthreads();
-    if (wave == 0 && col_ok) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = mt * 16 + 4 * gq + r;
-                if (m >= M) continue;
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * gq + r;
+            if (m < M) {
 #pragma unroll
                 for (int b = 0; b < BLK; ++b) {
-                    f32x4 v0 = {acc[mt][b][0][r], acc[mt][b][1][r], acc[mt][b][2][r], acc[mt][b][3][r]};
-                    f32x4 v1 = {acc[mt][b][4][r], acc[mt][b][5][r], acc[mt][b][6][r], acc[mt][b][7][r]};
-#pragma unroll
-                    for (int w = 0; w < 3; ++w) {
-                        const float *src = red + ((size_t)w * M + m) * COLS + 8 * (j * BLK + b);
-                        v0 += *(const f32x4 *)src;
-                        v1 += *(const f32x4 *)(src + 4);
-                    }
-                    const int n0 = 8 * (wcol0 + b);
-                    if (S == 1) {
-                        u32x4 o;
-                        o[0] = (uint32_t)f32_to_out_bits(v0[0], DT) | ((uint32_t)f32_to_out_bits(v0[1], DT) << 16);
-                        o[1] = (uint32_t)f32_to_out_bits(v0[2], DT) | ((uint32_t)f32_to_out_bits(v0[3], DT) << 16);
-                        o[2] = (uint32_t)f32_to_out_bits(v1[0], DT) | ((uint32_t)f32_to_out_bits(v1[1], DT) << 16);
-                        o[3] = (uint32_t)f32_to_out_bits(v1[2], DT) | ((uint32_t)f32_to_out_bits(v1[3], DT) << 16);
-                        *(u32x4 *)(y + (size_t)m * N + n0) = o;
-                    } else {
-                        float *dst = part + ((size_t)split * M + m) * N + n0;
-                        *(f32x4 *)dst = v0;
-                        *(f32x4 *)(dst + 4) = v1;
-                    }
+                    float *dst = red + ((size_t)(wave - 1) * M + m) * COLS + 8 * (j * BLK + b);
+                    *(f32x4 *)dst = (f32x4){acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
+                    *(f32x4 *)(dst + 4) = (f32x4){acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
                 }
             }
+        }
     }
-    if (S == 1) return;
-    if (!splitk_arrive(&counters[tile], S)) return;
-    // Last workgroup of this column tile: sum the S partials in split order.
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * gq + r;
+            if (m >= M) continue;
+#pragma unroll
+            for (int b = 0; b < BLK; ++b) {
+                f32x4 v0 = {acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
+                f32x4 v1 = {acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
+#pragma unroll
+                for (int w = 0; w < 3; ++w) {
+                    const float *src = red + ((size_t)w * M + m) * COLS + 8 * (j * BLK + b);
+                    v0 += *(const f32x4 *)src;
+                    v1 += *(const f32x4 *)(src + 4);
+                }
+                const int n0 = 8 * (wcol0 + b);
+                if (gridDim.y == 1) {
+                    if (col_ok) *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
+                } else {
+                    float *dst = slot + (size_t)m * COLS + 8 * (j * BLK + b);
+                    *(f32x4 *)dst = v0;
+                    *(f32x4 *)(dst + 4) = v1;
+                }
+            }
+        }
+    }
+    if (gridDim.y == 1) return;
+    __syncthreads();
+    // every thread adds a share of the workgroup's M x COLS partial
     const int n_base = tile * COLS;
     const int total = M * COLS;
+    int64_t seen = 0;
     for (int idx = threadIdx.x; idx < total; idx += 256) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int n = n_base + c;
-        if (n >= N) continue;
-        float v = 0.f;
-        for (int s = 0; s < S; ++s) v += __builtin_nontemporal_load(&part[((size_t)s * M + m) * N + n]);
-        y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
+        if (n < N) seen ^= atomic_add_i64(&acc64[(size_t)m * N + n], to_fixed<DT>(slot[idx]));
+    }
+    if (!splitk_count(&counters[tile], gridDim.y, seen)) return;
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int m = idx / COLS, c = idx - m * COLS;
+        const int n = n_base + c;
+        if (n < N)
+            y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(atomic_take_i64(&acc64[(size_t)m * N + n])), DT);
     }
 }
 
@@ -258,7 +292,7 @@ __global__ __launch_bounds__(256) void w4a16_skinny(const uint16_t *__restrict__
 template <int MTW, int DT, bool SYM>
 __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
                                                    const uint16_t *__restrict__ sc, const uint32_t *__restrict__ qz,
-                                                   uint16_t *__restrict__ y, float *__restrict__ part,
+                                                   uint16_t *__restrict__ y, int64_t *__restrict__ acc64,
                                                    int *__restrict__ counters, int M, int N, int K, int G, int S) {
     constexpr int BM = 32 * MTW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -287,7 +321,9 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
         xrow[mt] = x + (size_t)(row_ok[mt] ? m : 0) * K + 8 * gq;
     }
 
-    GroupConsts<DT, SYM> gc;
+    ZeroConsts<DT> zc;
+    uint32_t sc2[8];
+    float sf[8];
     int gcur = -1;
     for (int st = s_lo; st < s_hi; ++st) {
         const int k0 = st * 32;
@@ -305,7 +341,19 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
         const int g = k0 / G;
         if (g != gcur) {
             gcur = g;
-            load_group<DT, SYM>(gc, sc, qz, N, nw, g, wcol, col_ok);
+            uint32_t zw = 0x88888888u;
+            u32x4 s4 = {0, 0, 0, 0};
+            if (col_ok) {
+                s4 = *(const u32x4 *)(sc + (size_t)g * N + 8 * wcol);
+                if (!SYM) zw = qz[(size_t)g * nw + wcol];
+            }
+            zero_consts<DT, SYM>(zc, zw);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t b = scale_bits<DT>(s4, t);
+                sc2[t] = b | (b << 16);
+                sf[t] = scale_f32<DT>(s4, t);
+            }
         }
         uint32_t px[4], py[4];
 #pragma unroll
@@ -315,7 +363,9 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
         }
 #define AWQ4_COL(T_)                                                                                  \
     {                                                                                                 \
-        u32x4 bop = make_b<DT, SYM, T_>(px, py, gc);                                                  \
+        u32x4 bop;                                                                                    \
+        _Pragma("unroll") for (int p = 0; p < 4; ++p) bop[p] =                                        \
+            w_pair<DT, T_>(col_src_y(T_) ? py[p] : px[p], zc, sc2[T_], sf[T_]);                       \
         _Pragma("unroll") for (int mt = 0; mt < MTW; ++mt) acc[mt][T_] = mma<DT>(a[mt], bop, acc[mt][T_]); \
     }
         AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
@@ -332,16 +382,14 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + 16 * mt + 4 * gq + r;
                 if (m < M) {
-                    u32x4 o;
-#pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        o[p] = (uint32_t)f32_to_out_bits(acc[mt][2 * p][r], DT) |
-                               ((uint32_t)f32_to_out_bits(acc[mt][2 * p + 1][r], DT) << 16);
-                    *(u32x4 *)(y + (size_t)m * N + n0) = o;
+                    f32x4 v0 = {acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                    f32x4 v1 = {acc[mt][4][r], acc[mt][5][r], acc[mt][6][r], acc[mt][7][r]};
+                    *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
                 }
             }
         return;
     }
+    int64_t seen = 0;
     if (col_ok) {
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
@@ -349,13 +397,13 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + 16 * mt + 4 * gq + r;
                 if (m < M) {
-                    float *dst = part + ((size_t)split * M + m) * N + n0;
-                    *(f32x4 *)dst = (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
-                    *(f32x4 *)(dst + 4) = (f32x4){acc[mt][4][r], acc[mt][5][r], acc[mt][6][r], acc[mt][7][r]};
+                    int64_t *dst = acc64 + (size_t)m * N + n0;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) seen ^= atomic_add_i64(dst + t, to_fixed<DT>(acc[mt][t][r]));
                 }
             }
     }
-    if (!splitk_arrive(&counters[tm * gridDim.x + tn], S)) return;
+    if (!splitk_count(&counters[tm * gridDim.x + tn], S, seen)) return;
     if (!col_ok) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
@@ -363,48 +411,46 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
-            f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < S; ++s) {
-                const float *src = part + ((size_t)s * M + m) * N + n0;
-                v0 += __builtin_nontemporal_load((const f32x4 *)src);
-                v1 += __builtin_nontemporal_load((const f32x4 *)(src + 4));
+            int64_t *src = acc64 + (size_t)m * N + n0;
+            f32x4 v0, v1;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v0[t] = from_fixed<DT>(atomic_take_i64(src + t));
+                v1[t] = from_fixed<DT>(atomic_take_i64(src + 4 + t));
             }
-            u32x4 o;
-            o[0] = (uint32_t)f32_to_out_bits(v0[0], DT) | ((uint32_t)f32_to_out_bits(v0[1], DT) << 16);
-            o[1] = (uint32_t)f32_to_out_bits(v0[2], DT) | ((uint32_t)f32_to_out_bits(v0[3], DT) << 16);
-            o[2] = (uint32_t)f32_to_out_bits(v1[0], DT) | ((uint32_t)f32_to_out_bits(v1[1], DT) << 16);
-            o[3] = (uint32_t)f32_to_out_bits(v1[2], DT) | ((uint32_t)f32_to_out_bits(v1[3], DT) << 16);
-            *(u32x4 *)(y + (size_t)m * N + n0) = o;
+            *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
         }
 }
 
 // ===========================================================================
 // Host launchers.
 
-template <int BLK, int MT, int DT, bool SYM>
-static hipError_t launch_skinny_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+template <int BLK, int CS, int DT, bool SYM>
+static hipError_t launch_decode_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     dim3 grid(p.tiles_n, p.splits);
-    size_t lds = (size_t)3 * a.M * 128 * BLK * sizeof(float);
-    hipLaunchKernelGGL((w4a16_skinny<BLK, MT, DT, SYM>), grid, dim3(256), lds, st, (const uint16_t *)a.x,
+    const size_t lds = (size_t)3 * a.M * 128 * BLK * sizeof(float);
+    hipLaunchKernelGGL((w4a16_decode<BLK, CS, DT, SYM>), grid, dim3(256), lds, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
-                       (uint16_t *)a.y, p.partials, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
+                       (uint16_t *)a.y, p.acc64, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G);
     return hipGetLastError();
 }
 
-template <int BLK, int MT>
-static hipError_t launch_skinny_dt(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+template <int BLK, int CS>
+static hipError_t launch_decode_dt(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     const bool sym = a.qzeros == nullptr;
-    if (a.dtype == DT_F16) return sym ? launch_skinny_t<BLK, MT, DT_F16, true>(a, p, st)
-                                      : launch_skinny_t<BLK, MT, DT_F16, false>(a, p, st);
-    return sym ? launch_skinny_t<BLK, MT, DT_BF16, true>(a, p, st) : launch_skinny_t<BLK, MT, DT_BF16, false>(a, p, st);
+    if (a.dtype == DT_F16) return sym ? launch_decode_t<BLK, CS, DT_F16, true>(a, p, st)
+                                      : launch_decode_t<BLK, CS, DT_F16, false>(a, p, st);
+    return sym ? launch_decode_t<BLK, CS, DT_BF16, true>(a, p, st) : launch_decode_t<BLK, CS, DT_BF16, false>(a, p, st);
 }
 
-hipError_t launch_w4a16_skinny(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
-    switch (p.blk * 10 + p.mt) {
-        case 11: return launch_skinny_dt<1, 1>(a, p, st);
-        case 21: return launch_skinny_dt<2, 1>(a, p, st);
-        case 41: return launch_skinny_dt<4, 1>(a, p, st);
-        case 12: return launch_skinny_dt<1, 2>(a, p, st);
+hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    switch (p.blk * 10 + p.cs) {
+        case 11: return launch_decode_dt<1, 1>(a, p, st);
+        case 12: return launch_decode_dt<1, 2>(a, p, st);
+        case 21: return launch_decode_dt<2, 1>(a, p, st);
+        case 22: return launch_decode_dt<2, 2>(a, p, st);
+        case 41: return launch_decode_dt<4, 1>(a, p, st);
+        case 42: return launch_decode_dt<4, 2>(a, p, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -414,7 +460,7 @@ static hipError_t launch_tiled_t(const W4A16Args &a, const W4A16Plan &p, hipStre
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
     hipLaunchKernelGGL((w4a16_tiled<MTW, DT, SYM>), grid, dim3(256), 0, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
-                       (uint16_t *)a.y, p.partials, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
+                       (uint16_t *)a.y, p.acc64, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 

@@ -83,8 +83,10 @@ def test_workspace_bytes():
     op_gemm, op_gemv, op8 = L.AWQ_OP_GEMM_W4A16, L.AWQ_OP_GEMV_W4A16, L.AWQ_OP_W4A8_GEMM
     # no split requested -> no workspace
     assert lib.awq_workspace_bytes(op_gemm, 2048, 4096, 4096, 128, 1) == 0
-    # split 8 of a M=1, N=4096 GEMV: the fixed 16 KiB counter region + 8 fp32 partial rows
-    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == 16384 + 8 * 4096 * 4
+    # a M=1, N=4096 GEMV: the fixed 64 KiB counter region + one int64 accumulator per output
+    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == 65536 + 4096 * 8
+    # the tiled kernel with an explicit split: same layout
+    assert lib.awq_workspace_bytes(op_gemm, 64, 4096, 4096, 128, 4) == 65536 + 64 * 4096 * 8
     # automatic split for decode needs a workspace
     assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 0) > 0
     # invalid shapes -> 0
