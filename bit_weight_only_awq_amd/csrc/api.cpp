@@ -37,7 +37,8 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.tiles_m = 1;
         p.splits = (int)cdiv(K / (32 * p.cs), 4);
         tiles = p.tiles_n;
-    } else {
+    }
+    if (M > 16 || p.splits > kMaxSplitK) {
         p.kind = 1;
         p.blk = 1;
         p.cs = 1;
@@ -54,9 +55,10 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         }
         p.splits = (int)std::max<int64_t>(1, s);
         if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
-        if (tiles > kMaxSplitTiles) p.splits = 1;
+        p.splits = (int)std::min<int64_t>(p.splits, kMaxSplitK);
     }
-    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)M * N * sizeof(int64_t) : 0;
+    (void)tiles;
+    p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;
     return p;
 }
 
@@ -90,8 +92,8 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         }
         p.splits = (int)std::max<int64_t>(1, s);
     }
-    if (tiles > kMaxSplitTiles) p.splits = 1;
-    p.workspace_bytes = p.splits > 1 ? kCounterBytes + (size_t)M * N * sizeof(int32_t) : 0;
+    (void)tiles;
+    p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;
     return p;
 }
 
@@ -103,7 +105,7 @@ static int check_w4a16(const void *x, const int32_t *qweight, const void *scales
     if (G != 32 && G != 64 && G != 128) return AWQ_EINVAL;
     if (K % G != 0) return AWQ_EINVAL;
     if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
-    if (split_k < 0 || split_k > K / 32) return AWQ_EINVAL;
+    if (split_k < 0 || split_k > K / 32 || split_k > kMaxSplitK) return AWQ_EINVAL;
     if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y)) return AWQ_EALIGN;
     if (qzeros && !aligned16(qzeros)) return AWQ_EALIGN;
     return AWQ_OK;
@@ -112,7 +114,7 @@ static int check_w4a16(const void *x, const int32_t *qweight, const void *scales
 static int check_workspace(void *ws, size_t have, size_t need) {
     if (need == 0) return AWQ_OK;
     if (!ws || have < need) return AWQ_EWORKSPACE;
-    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return AWQ_EALIGN;
+    if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return AWQ_EALIGN;
     return AWQ_OK;
 }
 
@@ -128,8 +130,7 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
     if (rc != AWQ_OK) return rc;
     if (p.splits > 1) {
-        p.counters = static_cast<int *>(workspace);
-        p.acc64 = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + kCounterBytes);
+        p.acc = static_cast<uint64_t *>(workspace);
     }
     W4A16Args a{x, qweight, scales, qzeros, y, M, N, K, G, dtype};
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -242,8 +243,7 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
     int rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
     if (rc != AWQ_OK) return rc;
     if (p.splits > 1) {
-        p.counters = static_cast<int *>(workspace);
-        p.acc32 = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
+        p.acc = static_cast<uint64_t *>(workspace);
     }
     W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
     return hip_status(launch_w4a8(a, p, static_cast<hipStream_t>(stream)));

@@ -125,31 +125,39 @@ __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K completion without cache-flushing fences.
+// Split-K completion with one counting atomic per output element.
 //
-// Workgroups that share an output tile add their partial sums into a zeroed
-// accumulator in the workspace with device-scope read-modify-write atomics,
-// which are coherent across all XCDs.  fp32 partials are added as int64 fixed
-// point (exact, so the sum does not depend on the order of arrival and every
-// run gives the same bits); int32 partials are added as they are.  Each
-// atomic returns its old value, so once a thread has consumed the returns its
-// adds have been performed.  After a barrier one thread counts the workgroup
-// in; the last of the S workgroups reads every accumulator back with an
-// atomic exchange against zero (leaving it ready for the next call), writes
-// the output, and re-arms the counter.
+// Every output element of a split-K launch owns one 64-bit accumulator in the
+// workspace (zero between calls):
+//   bits 63..56  number of contributions received so far
+//   bits 55..0   sum over the contributions of (value + kBias)
+// A contribution adds (1 << 56) + value + kBias with 0 <= value + kBias < 2^48,
+// so up to 255 contributions never carry into the count.  The add is a
+// device-scope read-modify-write atomic returning the old word; the
+// contribution that brings the count to S therefore holds the exact total
+// (old + its own add), writes the output, and clears the accumulator for the
+// next call.  Only single-location atomicity is relied on -- no fences, no
+// separate counters -- and the integer sum does not depend on the order of
+// arrival, so every run gives the same bits.  fp32 partials are converted to
+// fixed point first; int32 partials are used as they are.
 
-// Fixed-point scale of the int64 accumulators: fp16 outputs need |y| < 2^31,
-// bf16 outputs get a wider range at 2^-16 resolution.
+constexpr int kCountShift = 56;
+constexpr uint64_t kValueMask = (uint64_t(1) << kCountShift) - 1;
+constexpr int64_t kBias = int64_t(1) << 47;
+constexpr int kMaxSplits = 255;
+
+// Fixed-point resolution: fp16 outputs (|y| <= 65504) use 2^-28 with range
+// 2^19; bf16 outputs use 2^-16 with range 2^31.
 template <int DT>
 struct FixedPoint {
-    static constexpr double kScale = DT == DT_BF16 ? 65536.0 : 4294967296.0;
-    static constexpr double kLimit = 9.0e18;  // saturate before int64 overflow
+    static constexpr double kScale = DT == DT_BF16 ? 65536.0 : 268435456.0;
 };
 
 template <int DT>
 __device__ __forceinline__ int64_t to_fixed(float v) {
+    const double lim = (double)(kBias - 1);
     double d = (double)v * FixedPoint<DT>::kScale;
-    d = fmin(fmax(d, -FixedPoint<DT>::kLimit), FixedPoint<DT>::kLimit);
+    d = fmin(fmax(d, -lim), lim);
     return (int64_t)__builtin_rint(d);
 }
 
@@ -158,36 +166,16 @@ __device__ __forceinline__ float from_fixed(int64_t v) {
     return (float)((double)v * (1.0 / FixedPoint<DT>::kScale));
 }
 
-// Adds v and returns the previous value (returning form: the caller consumes
-// it, which waits until the add has been performed).
-__device__ __forceinline__ int64_t atomic_add_i64(int64_t *p, int64_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t atomic_add_i32(int32_t *p, int32_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int64_t atomic_take_i64(int64_t *p) {
-    return __hip_atomic_exchange(p, (int64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t atomic_take_i32(int32_t *p) {
-    return __hip_atomic_exchange(p, (int32_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Called by every thread of the workgroup after its atomic adds; `seen` is
-// any value derived from the atomics' returns (consuming it orders the adds
-// before the count).  Returns true in the last of S workgroups of the tile.
-__device__ __forceinline__ bool splitk_count(int *counter, int S, int64_t seen) {
-    __shared__ int s_last;
-    if (seen == INT64_MIN) s_last = 2;  // never true in practice; keeps the returns live
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = old == S - 1;
-        if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last;
-    }
-    __syncthreads();
-    return s_last == 1;
+// Adds one contribution (value in -kBias+1 .. kBias-1) to *acc.  Returns true
+// in the final contribution, with the exact total in *total.
+__device__ __forceinline__ bool splitk_contribute(uint64_t *acc, int64_t value, int S, int64_t *total) {
+    const uint64_t add = (uint64_t(1) << kCountShift) + (uint64_t)(value + kBias);
+    const uint64_t old = __hip_atomic_fetch_add(acc, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t now = old + add;
+    if ((int)(now >> kCountShift) != S) return false;
+    *total = (int64_t)(now & kValueMask) - (int64_t)S * kBias;
+    __hip_atomic_store(acc, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
 }
 
 }  // namespace awq4

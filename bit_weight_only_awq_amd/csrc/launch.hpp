@@ -31,8 +31,7 @@ struct W4A16Plan {
     int splits;   // workgroups along K (1 = none); decode: grid y
     size_t workspace_bytes;
     // filled in by the caller from the workspace pointer
-    int *counters;
-    int64_t *acc64;
+    uint64_t *acc;
 };
 
 struct W4A8Args {
@@ -53,17 +52,12 @@ struct W4A8Plan {
     int mt;    // row tiles (skinny: M <= 16*mt; tiled: per wave)
     int tiles_n, tiles_m, splits;
     size_t workspace_bytes;
-    int *counters;
-    int32_t *acc32;
+    uint64_t *acc;
 };
 
-// Workspace layout: a fixed counter region (one int per output tile of a
-// split-K launch) followed by the split-K accumulators (int64 fixed point for
-// W4A16, int32 for W4A8, one per output element).  Every call leaves both
-// zero again, and the counter region does not move with the shape, so calls
-// of different shapes can share one workspace.
-constexpr size_t kCounterBytes = 65536;
-constexpr int64_t kMaxSplitTiles = kCounterBytes / 4;
+// Workspace of a split-K launch: one 64-bit counting accumulator per output
+// element (M x N), zero between calls (device.hpp).  Splits are capped at 255.
+constexpr int kMaxSplitK = 255;
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry);
 W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);

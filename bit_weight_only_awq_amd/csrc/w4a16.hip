@@ -19,10 +19,12 @@
 //  * decode kernel (M <= 16): a wave owns one K chunk (32*CS values inside one
 //    quantisation group) of a 128*BLK column tile and issues every weight load
 //    of the chunk before using any, so the whole weight stream is in flight
-//    across the GPU.  The B operand is the exact integer (q - z); the group
-//    scale multiplies the fp32 sums once per chunk.  The 4 waves of a
+//    across the GPU.  fp16: the B operand is the masked nibble pair read as
+//    fp16 subnormals (exact on the matrix cores, one AND per pair); zero point
+//    and scale are applied once per chunk on the fp32 sums.  bf16: the B
+//    operand is the exact integer (q - z), scaled once per chunk.  The 4 waves of a
 //    workgroup (4 consecutive chunks) are reduced through LDS, workgroups
-//    along K through fixed-point atomics (device.hpp).
+//    along K through counting fixed-point atomics (device.hpp).
 //  * tiled kernel (prefill): a workgroup of 4 waves (2 x 2) owns a
 //    (2*16*MTW) x 256 output tile; each wave runs the full K of its slice with
 //    MTW row tiles x 8 column MFMAs per 32-k step, B = (q - z) * s rounded
@@ -145,13 +147,12 @@ __device__ __forceinline__ u32x4 pack8_out(f32x4 v0, f32x4 v1) {
 // ===========================================================================
 // Decode kernel.  grid = (column tiles, ceil(chunks / 4)), 256 threads.
 // Dynamic LDS: 3 * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
-// counters[column tiles] and int64 fixed-point accumulators acc64[M][N].
+// one counting accumulator per output element, acc64[M][N] (device.hpp).
 template <int BLK, int CS, int DT, bool SYM>
 __global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
                                                     const uint16_t *__restrict__ sc,
                                                     const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
-                                                    int64_t *__restrict__ acc64, int *__restrict__ counters, int M,
-                                                    int N, int K, int G) {
+                                                    uint64_t *__restrict__ acc64, int M, int N, int K, int G) {
     extern __shared__ float red[];
     constexpr int COLS = 128 * BLK;
     constexpr int CK = 32 * CS;
@@ -192,18 +193,65 @@ __global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__
         for (int s = 0; s < CS; ++s)
             a[s] = (j < M) ? *(const u32x4 *)(x + (size_t)j * K + k0 + 32 * s + 8 * gq) : (u32x4){0, 0, 0, 0};
 
+        if (DT == DT_F16) {
+            // B operand = the masked nibble pair itself, read as fp16
+            // subnormals q * 2^-24 (or 16q * 2^-24 for an upper nibble): the
+            // matrix core multiplies them exactly.  The zero point and scale
+            // are applied per chunk:  s * (2^24 * sum(x q 2^-24) - z * sum(x)),
+            // with sum(x) from one extra MFMA against an all-ones operand.
+            const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+            f32x4 rs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < BLK; ++b) {
-            ZeroConsts<DT> zc;
-            zero_consts<DT, SYM>(zc, zw[b]);
+            for (int s = 0; s < CS; ++s) rs = mfma_f16(a[s], ones, rs);
 #pragma unroll
-            for (int s = 0; s < CS; ++s) {
-                uint32_t px[4], py[4];
+            for (int b = 0; b < BLK; ++b) {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    px[p] = pair_x(w[s][2 * p][b], w[s][2 * p + 1][b]);
-                    py[p] = pair_y(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                for (int s = 0; s < CS; ++s) {
+                    uint32_t px[4], py[4], px8[4], py8[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        px[p] = pair_x(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                        py[p] = pair_y(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                        px8[p] = px[p] >> 8;
+                        py8[p] = py[p] >> 8;
+                    }
+#define AWQ4_COL(T_)                                                                                \
+    {                                                                                               \
+        u32x4 bop;                                                                                  \
+        _Pragma("unroll") for (int p = 0; p < 4; ++p) {                                             \
+            const uint32_t src = col_src_y(T_) ? (col_shift(T_) ? py8[p] : py[p])                   \
+                                               : (col_shift(T_) ? px8[p] : px[p]);                  \
+            bop[p] = src & (col_hi(T_) ? 0x00F000F0u : 0x000F000Fu);                                \
+        }                                                                                           \
+        acc[b][T_] = mfma_f16(a[s], bop, acc[b][T_]);                                               \
+    }
+                    AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
+#undef AWQ4_COL
                 }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float st = scale_f32<DT>(s4[b], t);
+                    const float zt = SYM ? 8.0f : (float)((zw[b] >> (4 * col_nibble(t))) & 0xFu);
+                    const float at = st * (col_hi(t) ? 1048576.0f : 16777216.0f);  // s * 2^20 or s * 2^24
+                    const float bt = st * zt;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * gq + r < M) acc[b][t][r] = __builtin_fmaf(acc[b][t][r], at, -bt * rs[r]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < BLK; ++b) {
+                ZeroConsts<DT> zc;
+                zero_consts<DT, SYM>(zc, zw[b]);
+#pragma unroll
+                for (int s = 0; s < CS; ++s) {
+                    uint32_t px[4], py[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        px[p] = pair_x(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                        py[p] = pair_y(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                    }
 #define AWQ4_COL(T_)                                                                        \
     {                                                                                       \
         u32x4 bop;                                                                          \
@@ -211,12 +259,13 @@ __global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__
             qz_pair<DT, T_>(col_src_y(T_) ? py[p] : px[p], zc);                             \
         acc[b][T_] = mma<DT>(a[s], bop, acc[b][T_]);                                        \
     }
-                AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
+                    AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
 #undef AWQ4_COL
-            }
-            // the group scale, once per chunk, on the fp32 sums
+                }
+                // the group scale, once per chunk, on the fp32 sums
 #pragma unroll
-            for (int t = 0; t < 8; ++t) acc[b][t] *= scale_f32<DT>(s4[b], t);
+                for (int t = 0; t < 8; ++t) acc[b][t] *= scale_f32<DT>(s4[b], t);
+            }
         }
     }
 
@@ -268,21 +317,16 @@ __global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__
     }
     if (gridDim.y == 1) return;
     __syncthreads();
-    // every thread adds a share of the workgroup's M x COLS partial
+    // every thread contributes a share of the workgroup's M x COLS partial;
+    // the final contribution to an element writes it out
     const int n_base = tile * COLS;
     const int total = M * COLS;
-    int64_t seen = 0;
     for (int idx = threadIdx.x; idx < total; idx += 256) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int n = n_base + c;
-        if (n < N) seen ^= atomic_add_i64(&acc64[(size_t)m * N + n], to_fixed<DT>(slot[idx]));
-    }
-    if (!splitk_count(&counters[tile], gridDim.y, seen)) return;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-        const int m = idx / COLS, c = idx - m * COLS;
-        const int n = n_base + c;
-        if (n < N)
-            y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(atomic_take_i64(&acc64[(size_t)m * N + n])), DT);
+        int64_t sum;
+        if (n < N && splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(slot[idx]), gridDim.y, &sum))
+            y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
     }
 }
 
@@ -292,8 +336,8 @@ __global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__
 template <int MTW, int DT, bool SYM>
 __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
                                                    const uint16_t *__restrict__ sc, const uint32_t *__restrict__ qz,
-                                                   uint16_t *__restrict__ y, int64_t *__restrict__ acc64,
-                                                   int *__restrict__ counters, int M, int N, int K, int G, int S) {
+                                                   uint16_t *__restrict__ y, uint64_t *__restrict__ acc64, int M,
+                                                   int N, int K, int G, int S) {
     constexpr int BM = 32 * MTW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, gq = lane >> 4;
@@ -389,21 +433,6 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
             }
         return;
     }
-    int64_t seen = 0;
-    if (col_ok) {
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M) {
-                    int64_t *dst = acc64 + (size_t)m * N + n0;
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) seen ^= atomic_add_i64(dst + t, to_fixed<DT>(acc[mt][t][r]));
-                }
-            }
-    }
-    if (!splitk_count(&counters[tm * gridDim.x + tn], S, seen)) return;
     if (!col_ok) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
@@ -411,14 +440,12 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
-            int64_t *src = acc64 + (size_t)m * N + n0;
-            f32x4 v0, v1;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                v0[t] = from_fixed<DT>(atomic_take_i64(src + t));
-                v1[t] = from_fixed<DT>(atomic_take_i64(src + 4 + t));
+            for (int t = 0; t < 8; ++t) {
+                int64_t sum;
+                if (splitk_contribute(&acc64[(size_t)m * N + n0 + t], to_fixed<DT>(acc[mt][t][r]), S, &sum))
+                    y[(size_t)m * N + n0 + t] = f32_to_out_bits(from_fixed<DT>(sum), DT);
             }
-            *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
         }
 }
 
@@ -431,7 +458,7 @@ static hipError_t launch_decode_t(const W4A16Args &a, const W4A16Plan &p, hipStr
     const size_t lds = (size_t)3 * a.M * 128 * BLK * sizeof(float);
     hipLaunchKernelGGL((w4a16_decode<BLK, CS, DT, SYM>), grid, dim3(256), lds, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
-                       (uint16_t *)a.y, p.acc64, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G);
+                       (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G);
     return hipGetLastError();
 }
 
@@ -460,7 +487,7 @@ static hipError_t launch_tiled_t(const W4A16Args &a, const W4A16Plan &p, hipStre
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
     hipLaunchKernelGGL((w4a16_tiled<MTW, DT, SYM>), grid, dim3(256), 0, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
-                       (uint16_t *)a.y, p.acc64, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
+                       (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 

@@ -122,13 +122,13 @@ __device__ __forceinline__ void w4a8_store(int32_t acc, int m, int n, int N, con
 // ---------------------------------------------------------------------------
 // Skinny W4A8 kernel: M <= 16*MT; 4 waves split the K slice of a 64*BLK
 // column tile; LDS reduce (int32, exact); split-K over grid y through exact
-// int32 atomics (device.hpp).
+// counting atomics (device.hpp).
 template <int BLK, int MT, bool GROUP>
 __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                    const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                    const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
-                                                   int32_t *__restrict__ acc_out, int32_t *__restrict__ acc32,
-                                                   int *__restrict__ counters, int M, int N, int K, int G, int S) {
+                                                   int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
+                                                   int M, int N, int K, int G, int S) {
     extern __shared__ int32_t ired[];
     constexpr int COLS = 64 * BLK;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -204,25 +204,17 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
     __syncthreads();
     const int total = M * COLS;
     const int n_base = tile * COLS;
-    int64_t seen = 0;
     for (int idx = threadIdx.x; idx < total; idx += 256) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int32_t v = ired[(size_t)(0 * M + m) * COLS + c] + ired[(size_t)(1 * M + m) * COLS + c] +
                           ired[(size_t)(2 * M + m) * COLS + c] + ired[(size_t)(3 * M + m) * COLS + c];
         const int n = n_base + c;
-        if (n < N) {
-            if (S == 1)
-                w4a8_store<GROUP>(v, m, n, N, s1, s2, y, acc_out);
-            else
-                seen ^= atomic_add_i32(&acc32[(size_t)m * N + n], v);
-        }
-    }
-    if (S == 1) return;
-    if (!splitk_count(&counters[tile], S, seen)) return;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-        const int m = idx / COLS, c = idx - m * COLS;
-        const int n = n_base + c;
-        if (n < N) w4a8_store<GROUP>(atomic_take_i32(&acc32[(size_t)m * N + n]), m, n, N, s1, s2, y, acc_out);
+        if (n >= N) continue;
+        int64_t sum;
+        if (S == 1)
+            w4a8_store<GROUP>(v, m, n, N, s1, s2, y, acc_out);
+        else if (splitk_contribute(&acc64[(size_t)m * N + n], v, S, &sum))
+            w4a8_store<GROUP>((int32_t)sum, m, n, N, s1, s2, y, acc_out);
     }
 }
 
@@ -233,8 +225,8 @@ template <int MTW, bool GROUP>
 __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                   const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                   const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
-                                                  int32_t *__restrict__ acc_out, int32_t *__restrict__ acc32,
-                                                  int *__restrict__ counters, int M, int N, int K, int G, int S) {
+                                                  int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
+                                                  int M, int N, int K, int G, int S) {
     constexpr int BM = 32 * MTW;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, gq = lane >> 4;
@@ -300,20 +292,6 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
             }
         return;
     }
-    int64_t seen = 0;
-    if (ok) {
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) seen ^= atomic_add_i32(&acc32[(size_t)m * N + ncol + i], acc[mt][i][r]);
-                }
-            }
-    }
-    if (!splitk_count(&counters[tm * gridDim.x + tn], S, seen)) return;
     if (!ok) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
@@ -322,8 +300,11 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
             const int m = m0 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                w4a8_store<GROUP>(atomic_take_i32(&acc32[(size_t)m * N + ncol + i]), m, ncol + i, N, s1, s2, y, acc_out);
+            for (int i = 0; i < 4; ++i) {
+                int64_t sum;
+                if (splitk_contribute(&acc64[(size_t)m * N + ncol + i], acc[mt][i][r], S, &sum))
+                    w4a8_store<GROUP>((int32_t)sum, m, ncol + i, N, s1, s2, y, acc_out);
+            }
         }
 }
 
@@ -333,7 +314,7 @@ static hipError_t launch_skinny8(const W4A8Args &a, const W4A8Plan &p, hipStream
     size_t lds = (size_t)4 * a.M * 64 * BLK * sizeof(int32_t);
     hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
-                       (uint16_t *)a.y, a.acc_out, p.acc32, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G,
+                       (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G,
                        p.splits);
     return hipGetLastError();
 }
@@ -342,7 +323,7 @@ template <int MTW, bool GROUP>
 static hipError_t launch_tiled8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     hipLaunchKernelGGL((w4a8_tiled<MTW, GROUP>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
-                       (uint16_t *)a.y, a.acc_out, p.acc32, p.counters, (int)a.M, (int)a.N, (int)a.K, a.G,
+                       (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G,
                        p.splits);
     return hipGetLastError();
 }

@@ -108,13 +108,13 @@ int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, in
  * (0 if none).  split_k as passed to the call (0 = automatic).  For W4A8,
  * group_size is the one passed to w4a8_gemm.
  * Workspace rules ([P2]: one workspace per device, reused by every layer):
- *  - it is caller-owned, at least 256-byte aligned, and may be shared by any
- *    number of calls that are ordered on one stream;
- *  - its first 16 KiB are a counter region (one int32 per output tile of a
- *    split-K launch, whatever the call's shape); the rest holds fp32 / int32
- *    partial sums;
- *  - it must be zero-filled once when allocated; every call leaves the
- *    counter region zero again, so no per-call clearing is needed;
+ *  - it is caller-owned, 16-byte aligned, and may be shared by any number of
+ *    calls that are ordered on one stream;
+ *  - a split-K call uses one 64-bit accumulator per output element (M x N);
+ *    the last contribution to an element writes the output and clears its
+ *    accumulator, so the workspace is zero again after every call;
+ *  - it must be zero-filled once when allocated; no per-call clearing is
+ *    needed;
  *  - calls that overlap in time (different streams) need separate workspaces.
  * Returns 0 for invalid arguments.
  */
@@ -131,7 +131,9 @@ size_t awq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int group_si
  *   y:       device, [M, N] in the activation dtype (written, not accumulated).
  *   group_size G in {32, 64, 128}; K % G == 0; N % 8 == 0; M, N, K >= 1.
  *   split_k: number of K slices reduced through the workspace (0 = chosen by
- *            the library, 1 = none, at most K/32).
+ *            the library, 1 = none, at most min(K/32, 255)).  For M <= 16
+ *            the library's decode kernel fixes the K split itself and
+ *            ignores split_k.
  * Numerics: each weight is dequantised exactly to (q - z) and multiplied by s
  * with one rounding to the activation dtype; products accumulate in fp32 on
  * the matrix cores; the output is rounded to nearest even.

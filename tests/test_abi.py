@@ -67,6 +67,7 @@ def test_w4a16_validation(fn):
     assert _w4a16(fn, dt=2) == E.AWQ_EINVAL
     assert _w4a16(fn, split=-1) == E.AWQ_EINVAL
     assert _w4a16(fn, split=129) == E.AWQ_EINVAL     # > K/32
+    assert _w4a16(fn, K=16384, split=256) == E.AWQ_EINVAL  # > 255 splits
     assert _w4a16(fn, x=MIS) == E.AWQ_EALIGN
     assert _w4a16(fn, qz=MIS) == E.AWQ_EALIGN
     # a valid split-K request without workspace
@@ -83,10 +84,11 @@ def test_workspace_bytes():
     op_gemm, op_gemv, op8 = L.AWQ_OP_GEMM_W4A16, L.AWQ_OP_GEMV_W4A16, L.AWQ_OP_W4A8_GEMM
     # no split requested -> no workspace
     assert lib.awq_workspace_bytes(op_gemm, 2048, 4096, 4096, 128, 1) == 0
-    # a M=1, N=4096 GEMV: the fixed 64 KiB counter region + one int64 accumulator per output
-    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == 65536 + 4096 * 8
+    # a M=1, N=4096 GEMV: one 64-bit counting accumulator per output element
+    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == 4096 * 8
     # the tiled kernel with an explicit split: same layout
-    assert lib.awq_workspace_bytes(op_gemm, 64, 4096, 4096, 128, 4) == 65536 + 64 * 4096 * 8
+    assert lib.awq_workspace_bytes(op_gemm, 64, 4096, 4096, 128, 4) == 64 * 4096 * 8
+    assert lib.awq_workspace_bytes(op8, 1, 8192, 21760, -1, 0) == 8192 * 8
     # automatic split for decode needs a workspace
     assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 0) > 0
     # invalid shapes -> 0
