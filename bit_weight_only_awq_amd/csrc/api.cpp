@@ -33,9 +33,10 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.kind = 0;
         p.blk = nw % 2 == 0 ? 2 : 1;  // 128 B per k-row per wave: whole cache lines
         p.cs = G >= 64 ? 2 : 1;
+        p.waves = 4;
         p.tiles_n = (int)cdiv(nw, 16 * p.blk);
         p.tiles_m = 1;
-        p.splits = (int)cdiv(K / (32 * p.cs), 4);
+        p.splits = (int)cdiv(K / (32 * p.cs), p.waves);
         tiles = p.tiles_n;
     }
     if (M > 16 || p.splits > kMaxSplitK) {
@@ -56,6 +57,18 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.splits = (int)std::max<int64_t>(1, s);
         if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
         p.splits = (int)std::min<int64_t>(p.splits, kMaxSplitK);
+    }
+    if (M >= 128 && K % 64 == 0 && N % 32 == 0) {
+        // LDS-pipelined GEMM: 128 x 256 workgroup tiles, K in stages of 64
+        p.kind = 3;
+        p.tiles_n = (int)cdiv(N, 256);
+        p.tiles_m = (int)cdiv(M, 128);
+        tiles = (int64_t)p.tiles_n * p.tiles_m;
+        const int64_t stages = K / 64;
+        int64_t s = 1;
+        if (tiles < 128) s = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, stages / 4));
+        if (split_k > 0) s = std::min<int64_t>(split_k, stages);
+        p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
     }
     (void)tiles;
     p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;
@@ -134,7 +147,14 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     }
     W4A16Args a{x, qweight, scales, qzeros, y, M, N, K, G, dtype};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return hip_status(p.kind == 0 ? launch_w4a16_decode(a, p, st) : launch_w4a16_tiled(a, p, st));
+    hipError_t e;
+    switch (p.kind) {
+        case 0: e = launch_w4a16_decode(a, p, st); break;
+        case 2: e = launch_w4a16_stream(a, p, st); break;
+        case 3: e = launch_w4a16_gemm(a, p, st); break;
+        default: e = launch_w4a16_tiled(a, p, st); break;
+    }
+    return hip_status(e);
 }
 
 }  // namespace awq4

@@ -31,130 +31,93 @@
 //    once to the activation type; optional split-K over the grid's z.
 #include "device.hpp"
 #include "launch.hpp"
+#include "w4a16_ops.hpp"
 
 namespace awq4 {
 
-// Zero-point constants of one word-column for its 8 columns (fp16 path:
-// packed -(1024+z) / -(64+z); bf16 path: z as float).
-template <int DT>
-struct ZeroConsts {
-    uint32_t zc[8];
-    float zf[8];
-};
-
-template <int DT, bool SYM>
-__device__ __forceinline__ void zero_consts(ZeroConsts<DT> &c, uint32_t zw) {
+// Workgroup epilogue of the decode kernels: reduce the 4 waves' partials
+// (waves 1..3 park theirs in LDS, red[wave-1][m][c]; wave 0 adds them in wave
+// order), then either write the output (no split) or contribute the
+// workgroup's M x COLS partial to the counting accumulators (split-K).
+template <int BLK, int DT, int WAVES = 4>
+__device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red, uint16_t *__restrict__ y,
+                                                uint64_t *__restrict__ acc64, int M, int N, int wave, int gq,
+                                                int j, int wcol0, bool col_ok, int tile) {
+    constexpr int COLS = 128 * BLK;
+    // With split-K the sum is parked in slot 0 (each lane of wave 0
+    // overwrites only entries it has just read) for the whole workgroup to
+    // add out.
+    float *slot = red;
+    if (wave > 0) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const uint32_t z = SYM ? 8u : ((zw >> (4 * col_nibble(t))) & 0xFu);
-        if (DT == DT_F16)
-            c.zc[t] = col_hi(t) ? zconst_f16<1>(z) : zconst_f16<0>(z);
-        else
-            c.zf[t] = (float)z;
-    }
-}
-
-// Scale of column t from the 8 scales of a word-column (16 bytes).
-template <int DT>
-__device__ __forceinline__ uint32_t scale_bits(u32x4 s4, int t) {
-    return (s4[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-}
-template <int DT>
-__device__ __forceinline__ float scale_f32(u32x4 s4, int t) {
-    const uint32_t b = scale_bits<DT>(s4, t);
-    return DT == DT_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
-}
-
-// Exact (q - z) pair of column t from one pair register, as fp16 or bf16.
-template <int DT, int t>
-__device__ __forceinline__ uint32_t qz_pair(uint32_t src, const ZeroConsts<DT> &c) {
-    const uint32_t v = col_shift(t) ? (src >> 8) : src;
-    if (DT == DT_F16) {
-        const uint32_t mask = col_hi(t) ? 0x00F000F0u : 0x000F000Fu;
-        f16x2 h = bit_as<f16x2>((v & mask) | 0x64006400u);
-        f16x2 z = bit_as<f16x2>(c.zc[t]);
-        f16x2 d;
-        if (col_hi(t)) {
-            const f16x2 sixteenth = {(f16)0.0625f, (f16)0.0625f};
-            d = h * sixteenth + z;
-        } else {
-            d = h + z;
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * gq + r;
+            if (m < M) {
+#pragma unroll
+                for (int b = 0; b < BLK; ++b) {
+                    float *dst = red + ((size_t)(wave - 1) * M + m) * COLS + 8 * (j * BLK + b);
+                    *(f32x4 *)dst = (f32x4){acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
+                    *(f32x4 *)(dst + 4) = (f32x4){acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
+                }
+            }
         }
-        return bit_as<uint32_t>(d);
-    } else {
-        const uint32_t m = v & (col_hi(t) ? 0x00F000F0u : 0x000F000Fu);
-        const float mul = col_hi(t) ? 0.0625f : 1.0f;
-        const float d0 = __builtin_fmaf((float)(m & 0xFFu), mul, -c.zf[t]);          // exact
-        const float d1 = __builtin_fmaf((float)((m >> 16) & 0xFFu), mul, -c.zf[t]);  // exact
-        return (uint32_t)bit_as<uint16_t>((__bf16)d0) | ((uint32_t)bit_as<uint16_t>((__bf16)d1) << 16);
     }
-}
-
-// (q - z) * s pair of column t, rounded once to the activation type.
-template <int DT, int t>
-__device__ __forceinline__ uint32_t w_pair(uint32_t src, const ZeroConsts<DT> &c, uint32_t sc2, float sf) {
-    if (DT == DT_F16) {
-        return bit_as<uint32_t>(bit_as<f16x2>(qz_pair<DT, t>(src, c)) * bit_as<f16x2>(sc2));
-    } else {
-        const uint32_t v = col_shift(t) ? (src >> 8) : src;
-        const uint32_t m = v & (col_hi(t) ? 0x00F000F0u : 0x000F000Fu);
-        const float sm = col_hi(t) ? sf * 0.0625f : sf;
-        const float zs = c.zf[t] * sf;
-        const float w0 = __builtin_fmaf((float)(m & 0xFFu), sm, -zs);  // exact, one rounding below
-        const float w1 = __builtin_fmaf((float)((m >> 16) & 0xFFu), sm, -zs);
-        return (uint32_t)bit_as<uint16_t>((__bf16)w0) | ((uint32_t)bit_as<uint16_t>((__bf16)w1) << 16);
-    }
-}
-
-template <int DT>
-__device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-    if (DT == DT_F16) return mfma_f16(a, b, c);
-    return mfma_bf16(a, b, c);
-}
-
-// Load BLK consecutive packed words of one k-row (zero words out of range).
-// NT: streamed exactly once (non-temporal hint).
-template <int BLK, bool NT>
-__device__ __forceinline__ void load_words(const uint32_t *__restrict__ p, bool valid, uint32_t (&w)[BLK]) {
-    if (!valid) {
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-        for (int b = 0; b < BLK; ++b) w[b] = 0;
-        return;
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * gq + r;
+            if (m >= M) continue;
+#pragma unroll
+            for (int b = 0; b < BLK; ++b) {
+                f32x4 v0 = {acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
+                f32x4 v1 = {acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
+#pragma unroll
+                for (int w = 0; w < WAVES - 1; ++w) {
+                    const float *src = red + ((size_t)w * M + m) * COLS + 8 * (j * BLK + b);
+                    v0 += *(const f32x4 *)src;
+                    v1 += *(const f32x4 *)(src + 4);
+                }
+                const int n0 = 8 * (wcol0 + b);
+                if (gridDim.y == 1) {
+                    if (col_ok) *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
+                } else {
+                    float *dst = slot + (size_t)m * COLS + 8 * (j * BLK + b);
+                    *(f32x4 *)dst = v0;
+                    *(f32x4 *)(dst + 4) = v1;
+                }
+            }
+        }
     }
-    if (BLK == 4) {
-        u32x4 v = NT ? __builtin_nontemporal_load((const u32x4 *)p) : *(const u32x4 *)p;
-#pragma unroll
-        for (int b = 0; b < BLK; ++b) w[b] = v[b];
-    } else if (BLK == 2) {
-        u32x2 v = NT ? __builtin_nontemporal_load((const u32x2 *)p) : *(const u32x2 *)p;
-#pragma unroll
-        for (int b = 0; b < BLK; ++b) w[b] = v[b];
-    } else {
-        w[0] = NT ? __builtin_nontemporal_load(p) : *p;
+    if (gridDim.y == 1) return;
+    __syncthreads();
+    // every thread contributes a share of the workgroup's M x COLS partial;
+    // the final contribution to an element writes it out
+    const int n_base = tile * COLS;
+    const int total = M * COLS;
+    for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
+        const int m = idx / COLS, c = idx - m * COLS;
+        const int n = n_base + c;
+        int64_t sum;
+        if (n < N && splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(slot[idx]), gridDim.y, &sum))
+            y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
     }
 }
 
-template <int DT>
-__device__ __forceinline__ u32x4 pack8_out(f32x4 v0, f32x4 v1) {
-    u32x4 o;
-    o[0] = (uint32_t)f32_to_out_bits(v0[0], DT) | ((uint32_t)f32_to_out_bits(v0[1], DT) << 16);
-    o[1] = (uint32_t)f32_to_out_bits(v0[2], DT) | ((uint32_t)f32_to_out_bits(v0[3], DT) << 16);
-    o[2] = (uint32_t)f32_to_out_bits(v1[0], DT) | ((uint32_t)f32_to_out_bits(v1[1], DT) << 16);
-    o[3] = (uint32_t)f32_to_out_bits(v1[2], DT) | ((uint32_t)f32_to_out_bits(v1[3], DT) << 16);
-    return o;
-}
 
 // ===========================================================================
-// Decode kernel.  grid = (column tiles, ceil(chunks / 4)), 256 threads.
-// Dynamic LDS: 3 * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
+// Decode kernel.  grid = (column tiles, ceil(chunks / WAVES)), 64*WAVES
+// threads.  Dynamic LDS: (WAVES-1) * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
 // one counting accumulator per output element, acc64[M][N] (device.hpp).
-template <int BLK, int CS, int DT, bool SYM>
-__global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
+// The launch bound asks for 4 waves per SIMD (<= 128 registers): the whole
+// weight stream of a layer must be in flight at once, and this fits without
+// spills (measured faster than the compiler's own 3-wave allocation).
+template <int BLK, int CS, int DT, bool SYM, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 4) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
                                                     const uint16_t *__restrict__ sc,
                                                     const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
                                                     uint64_t *__restrict__ acc64, int M, int N, int K, int G) {
     extern __shared__ float red[];
-    constexpr int COLS = 128 * BLK;
     constexpr int CK = 32 * CS;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, gq = lane >> 4;
@@ -162,7 +125,7 @@ __global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__
     const int tile = blockIdx.x;
     const int wcol0 = tile * 16 * BLK + j * BLK;  // lane's first word-column
     const bool col_ok = wcol0 < nw;
-    const int chunk = blockIdx.y * 4 + wave;
+    const int chunk = blockIdx.y * WAVES + wave;
     const bool active = chunk < K / CK;
 
     f32x4 acc[BLK][8];
@@ -269,65 +232,134 @@ __global__ __launch_bounds__(256) void w4a16_decode(const uint16_t *__restrict__
         }
     }
 
-    // Reduce the 4 waves: waves 1..3 park their partials in LDS
-    // (red[wave-1][m][c]); wave 0 adds them in wave order.  With split-K the
-    // sum is parked in slot 0 (each lane of wave 0 overwrites only entries it
-    // has just read) for the whole workgroup to add out.
-    float *slot = red;
-    if (wave > 0) {
+    decode_epilogue<BLK, DT, WAVES>(acc, red, y, acc64, M, N, wave, gq, j, wcol0, col_ok, tile);
+}
+
+// ===========================================================================
+// Streaming decode kernel.  grid = (column tiles, S), 256 threads; the 4
+// waves split the workgroup's K slice into contiguous runs of 32-k steps and
+// each wave keeps the next step's weights in flight while it computes the
+// current one (the loop is unrolled by two, alternating two register sets).
+// fp16: per step, tmp = sum(x q 2^-24) and rs = sum(x) come from the matrix
+// cores and acc += s*(2^24 tmp - z rs) on the live rows; bf16: the operand is
+// (q - z) * s rounded once and accumulates directly.
+// Dynamic LDS: 3 * M * (128*BLK) floats (the decode epilogue).
+template <int BLK, int DT>
+struct StreamStep {
+    uint32_t w[8][BLK];
+    u32x4 a;
+    u32x4 s4[BLK];
+    uint32_t zw[BLK];
+};
+
+template <int BLK, int DT, bool SYM>
+__device__ __forceinline__ void stream_load(StreamStep<BLK, DT> &d, const uint16_t *__restrict__ x,
+                                            const uint32_t *__restrict__ qw, const uint16_t *__restrict__ sc,
+                                            const uint32_t *__restrict__ qz, int st, int M, int N, int K, int G,
+                                            int nw, int j, int gq, int wcol0, bool col_ok) {
+    const int k0 = st * 32;
+    const int g = k0 / G;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * gq + r;
-            if (m < M) {
+    for (int e = 0; e < 8; ++e) load_words<BLK, true>(qw + (size_t)(k0 + 8 * gq + e) * nw + wcol0, col_ok, d.w[e]);
+    d.a = (j < M) ? *(const u32x4 *)(x + (size_t)j * K + k0 + 8 * gq) : (u32x4){0, 0, 0, 0};
 #pragma unroll
-                for (int b = 0; b < BLK; ++b) {
-                    float *dst = red + ((size_t)(wave - 1) * M + m) * COLS + 8 * (j * BLK + b);
-                    *(f32x4 *)dst = (f32x4){acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
-                    *(f32x4 *)(dst + 4) = (f32x4){acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
+    for (int b = 0; b < BLK; ++b) {
+        d.s4[b] = col_ok ? *(const u32x4 *)(sc + (size_t)g * N + 8 * (wcol0 + b)) : (u32x4){0, 0, 0, 0};
+        d.zw[b] = (!SYM && col_ok) ? qz[(size_t)g * nw + wcol0 + b] : 0x88888888u;
+    }
+}
+
+template <int BLK, int DT, bool SYM>
+__device__ __forceinline__ void stream_compute(const StreamStep<BLK, DT> &d, f32x4 (&acc)[BLK][8], int M, int gq) {
+    if (DT == DT_F16) {
+        const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 rs = mfma_f16(d.a, ones, zero);
+#pragma unroll
+        for (int b = 0; b < BLK; ++b) {
+            uint32_t px[4], py[4], px8[4], py8[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                px[p] = pair_x(d.w[2 * p][b], d.w[2 * p + 1][b]);
+                py[p] = pair_y(d.w[2 * p][b], d.w[2 * p + 1][b]);
+                px8[p] = px[p] >> 8;
+                py8[p] = py[p] >> 8;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                u32x4 bop;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t src = col_src_y(t) ? (col_shift(t) ? py8[p] : py[p]) : (col_shift(t) ? px8[p] : px[p]);
+                    bop[p] = src & (col_hi(t) ? 0x00F000F0u : 0x000F000Fu);
                 }
+                const f32x4 tmp = mfma_f16(d.a, bop, zero);
+                const float st = scale_f32<DT>(d.s4[b], t);
+                const float zt = SYM ? 8.0f : (float)((d.zw[b] >> (4 * col_nibble(t))) & 0xFu);
+                const float at = st * (col_hi(t) ? 1048576.0f : 16777216.0f);  // s * 2^20 or s * 2^24
+                const float bt = st * zt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * gq + r < M) acc[b][t][r] = __builtin_fmaf(tmp[r], at, __builtin_fmaf(-bt, rs[r], acc[b][t][r]));
             }
         }
-    }
-    __syncthreads();
-    if (wave == 0) {
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * gq + r;
-            if (m >= M) continue;
+        for (int b = 0; b < BLK; ++b) {
+            ZeroConsts<DT> zc;
+            zero_consts<DT, SYM>(zc, d.zw[b]);
+            uint32_t px[4], py[4];
 #pragma unroll
-            for (int b = 0; b < BLK; ++b) {
-                f32x4 v0 = {acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
-                f32x4 v1 = {acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
-#pragma unroll
-                for (int w = 0; w < 3; ++w) {
-                    const float *src = red + ((size_t)w * M + m) * COLS + 8 * (j * BLK + b);
-                    v0 += *(const f32x4 *)src;
-                    v1 += *(const f32x4 *)(src + 4);
-                }
-                const int n0 = 8 * (wcol0 + b);
-                if (gridDim.y == 1) {
-                    if (col_ok) *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
-                } else {
-                    float *dst = slot + (size_t)m * COLS + 8 * (j * BLK + b);
-                    *(f32x4 *)dst = v0;
-                    *(f32x4 *)(dst + 4) = v1;
-                }
+            for (int p = 0; p < 4; ++p) {
+                px[p] = pair_x(d.w[2 * p][b], d.w[2 * p + 1][b]);
+                py[p] = pair_y(d.w[2 * p][b], d.w[2 * p + 1][b]);
             }
+#define AWQ4_COL(T_)                                                                            \
+    {                                                                                           \
+        const float sf = scale_f32<DT>(d.s4[b], T_);                                            \
+        u32x4 bop;                                                                              \
+        _Pragma("unroll") for (int p = 0; p < 4; ++p) bop[p] =                                  \
+            w_pair<DT, T_>(col_src_y(T_) ? py[p] : px[p], zc, 0u, sf);                          \
+        acc[b][T_] = mma<DT>(d.a, bop, acc[b][T_]);                                             \
+    }
+            AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
+#undef AWQ4_COL
         }
     }
-    if (gridDim.y == 1) return;
-    __syncthreads();
-    // every thread contributes a share of the workgroup's M x COLS partial;
-    // the final contribution to an element writes it out
-    const int n_base = tile * COLS;
-    const int total = M * COLS;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-        const int m = idx / COLS, c = idx - m * COLS;
-        const int n = n_base + c;
-        int64_t sum;
-        if (n < N && splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(slot[idx]), gridDim.y, &sum))
-            y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
+}
+
+template <int BLK, int DT, bool SYM>
+__global__ __launch_bounds__(256) void w4a16_stream(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
+                                                    const uint16_t *__restrict__ sc,
+                                                    const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
+                                                    uint64_t *__restrict__ acc64, int M, int N, int K, int G) {
+    extern __shared__ float red[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, gq = lane >> 4;
+    const int nw = N >> 3;
+    const int tile = blockIdx.x;
+    const int wcol0 = tile * 16 * BLK + j * BLK;
+    const bool col_ok = wcol0 < nw;
+    const int T = K >> 5, S = gridDim.y, split = blockIdx.y;
+    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
+    const int w_lo = s_lo + (s_hi - s_lo) * wave / 4, w_hi = s_lo + (s_hi - s_lo) * (wave + 1) / 4;
+
+    f32x4 acc[BLK][8];
+#pragma unroll
+    for (int b = 0; b < BLK; ++b)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[b][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    StreamStep<BLK, DT> d0, d1;
+    if (w_lo < w_hi) stream_load<BLK, DT, SYM>(d0, x, qw, sc, qz, w_lo, M, N, K, G, nw, j, gq, wcol0, col_ok);
+    for (int st = w_lo; st < w_hi; st += 2) {
+        if (st + 1 < w_hi) stream_load<BLK, DT, SYM>(d1, x, qw, sc, qz, st + 1, M, N, K, G, nw, j, gq, wcol0, col_ok);
+        stream_compute<BLK, DT, SYM>(d0, acc, M, gq);
+        if (st + 1 >= w_hi) break;
+        if (st + 2 < w_hi) stream_load<BLK, DT, SYM>(d0, x, qw, sc, qz, st + 2, M, N, K, G, nw, j, gq, wcol0, col_ok);
+        stream_compute<BLK, DT, SYM>(d1, acc, M, gq);
     }
+    decode_epilogue<BLK, DT>(acc, red, y, acc64, M, N, wave, gq, j, wcol0, col_ok, tile);
 }
 
 // ===========================================================================
@@ -452,32 +484,60 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
 // ===========================================================================
 // Host launchers.
 
-template <int BLK, int CS, int DT, bool SYM>
+template <int BLK, int CS, int DT, bool SYM, int WAVES>
 static hipError_t launch_decode_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     dim3 grid(p.tiles_n, p.splits);
+    const size_t lds = (size_t)(WAVES - 1) * a.M * 128 * BLK * sizeof(float);
+    hipLaunchKernelGGL((w4a16_decode<BLK, CS, DT, SYM, WAVES>), grid, dim3(64 * WAVES), lds, st,
+                       (const uint16_t *)a.x, (const uint32_t *)a.qweight, (const uint16_t *)a.scales,
+                       (const uint32_t *)a.qzeros, (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G);
+    return hipGetLastError();
+}
+
+template <int BLK, int CS, int WAVES>
+static hipError_t launch_decode_dt(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    const bool sym = a.qzeros == nullptr;
+    if (a.dtype == DT_F16) return sym ? launch_decode_t<BLK, CS, DT_F16, true, WAVES>(a, p, st)
+                                      : launch_decode_t<BLK, CS, DT_F16, false, WAVES>(a, p, st);
+    return sym ? launch_decode_t<BLK, CS, DT_BF16, true, WAVES>(a, p, st)
+               : launch_decode_t<BLK, CS, DT_BF16, false, WAVES>(a, p, st);
+}
+
+hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    switch (p.waves * 100 + p.blk * 10 + p.cs) {
+        case 411: return launch_decode_dt<1, 1, 4>(a, p, st);
+        case 412: return launch_decode_dt<1, 2, 4>(a, p, st);
+        case 421: return launch_decode_dt<2, 1, 4>(a, p, st);
+        case 422: return launch_decode_dt<2, 2, 4>(a, p, st);
+        case 424: return launch_decode_dt<2, 4, 4>(a, p, st);
+        case 821: return launch_decode_dt<2, 1, 8>(a, p, st);
+        case 822: return launch_decode_dt<2, 2, 8>(a, p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int BLK, int DT, bool SYM>
+static hipError_t launch_stream_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    dim3 grid(p.tiles_n, p.splits);
     const size_t lds = (size_t)3 * a.M * 128 * BLK * sizeof(float);
-    hipLaunchKernelGGL((w4a16_decode<BLK, CS, DT, SYM>), grid, dim3(256), lds, st, (const uint16_t *)a.x,
+    hipLaunchKernelGGL((w4a16_stream<BLK, DT, SYM>), grid, dim3(256), lds, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
                        (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G);
     return hipGetLastError();
 }
 
-template <int BLK, int CS>
-static hipError_t launch_decode_dt(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+template <int BLK>
+static hipError_t launch_stream_dt(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     const bool sym = a.qzeros == nullptr;
-    if (a.dtype == DT_F16) return sym ? launch_decode_t<BLK, CS, DT_F16, true>(a, p, st)
-                                      : launch_decode_t<BLK, CS, DT_F16, false>(a, p, st);
-    return sym ? launch_decode_t<BLK, CS, DT_BF16, true>(a, p, st) : launch_decode_t<BLK, CS, DT_BF16, false>(a, p, st);
+    if (a.dtype == DT_F16) return sym ? launch_stream_t<BLK, DT_F16, true>(a, p, st)
+                                      : launch_stream_t<BLK, DT_F16, false>(a, p, st);
+    return sym ? launch_stream_t<BLK, DT_BF16, true>(a, p, st) : launch_stream_t<BLK, DT_BF16, false>(a, p, st);
 }
 
-hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
-    switch (p.blk * 10 + p.cs) {
-        case 11: return launch_decode_dt<1, 1>(a, p, st);
-        case 12: return launch_decode_dt<1, 2>(a, p, st);
-        case 21: return launch_decode_dt<2, 1>(a, p, st);
-        case 22: return launch_decode_dt<2, 2>(a, p, st);
-        case 41: return launch_decode_dt<4, 1>(a, p, st);
-        case 42: return launch_decode_dt<4, 2>(a, p, st);
+hipError_t launch_w4a16_stream(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    switch (p.blk) {
+        case 1: return launch_stream_dt<1>(a, p, st);
+        case 2: return launch_stream_dt<2>(a, p, st);
         default: return hipErrorInvalidValue;
     }
 }
