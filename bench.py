@@ -40,7 +40,8 @@ G = 128
 M_DECODE, M_PREFILL = 1, 2048
 W4A8_K, W4A8_N, W4A8_M = 21760, 8192, (1, 1024)
 ROTATE_MB = 600
-KERNEL_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/w4a8.hip",
+KERNEL_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/gemm_w4a16.hip",
+                  "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp", "bit_weight_only_awq_amd/csrc/w4a8.hip",
                   "bit_weight_only_awq_amd/csrc/device.hpp", "bit_weight_only_awq_amd/csrc/api.cpp"]
 
 
@@ -281,7 +282,7 @@ def main():
                         "traffic": load_traffic("w4a16_decode_m1_llama2_7b", digest),
                         "avg_launch_us": round(t_dec / len(DECODE_LAYERS) * 1e6, 3),
                         "per_layer": dec_layer},
-           "gemm_m2048": {"kernel": "w4a16_tiled (prefill GEMM, M=2048, 4 Llama-3-8B layers back to back)",
+           "gemm_m2048": {"kernel": "w4a16_gemm (prefill GEMM, M=2048, 4 Llama-3-8B layers back to back)",
                           "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "per_layer": pre_layer},
            "w4a8_n8192_k21760": w8_res,

@@ -59,10 +59,10 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.splits = (int)std::min<int64_t>(p.splits, kMaxSplitK);
     }
     if (M >= 128 && K % 64 == 0 && N % 32 == 0) {
-        // LDS-pipelined GEMM: 128 x 256 workgroup tiles, K in stages of 64
+        // LDS-pipelined GEMM: 256 x 128 workgroup tiles, K in stages of 64
         p.kind = 3;
-        p.tiles_n = (int)cdiv(N, 256);
-        p.tiles_m = (int)cdiv(M, 128);
+        p.tiles_n = (int)cdiv(N, 128);
+        p.tiles_m = (int)cdiv(M, 256);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         const int64_t stages = K / 64;
         int64_t s = 1;

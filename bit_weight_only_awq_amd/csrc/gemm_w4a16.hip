@@ -6,32 +6,58 @@
 // zero points): Y = X . W with W[k,n] = (q - z) * s rounded once to the
 // activation type, fp32 accumulation on the matrix cores.
 //
-// Workgroup tile 128 (M) x 256 (N), K in stages of 64; 4 waves in a 2 x 2
-// grid, each owning 64 x 128 outputs (4 row tiles x 8 column MFMAs of
-// 16x16x32).  Per stage, X (fp16/bf16) and the packed weight words are staged
-// through LDS with double buffering: the global loads of stage s+1 (and the
-// scales / zero points it needs) are issued before stage s is computed, and
-// written to the other LDS buffer afterwards, so one barrier per stage
-// suffices.  Each wave dequantises its own B operands from the packed words in
-// LDS (lane j: one word-column, 8 consecutive k; see device.hpp), which keeps
-// the LDS traffic for B at 4 bits per weight.
+// Workgroup tile 256 (M) x 128 (N), K in stages of 64 (two 32-k steps); 4
+// waves in a 2 x 2 grid, each owning 128 x 64 outputs: 8 row tiles x 4 column
+// MFMAs of 16x16x32 per k-step.  A wave's 64 columns are 8 packed
+// word-columns; lanes j and j+8 read the same words and take the low / high
+// nibble of each byte, so every dequantised B operand feeds 8 MFMAs (the
+// dequantisation is the VALU work that bounds this kernel).  Column of MFMA u
+// in lane j: 8 * word_column + {0,1,4,5}[u] + 2 * (j >> 3).
+//
+// Data movement: every stage's X rows and packed words (with the stage's
+// scales and zero points) are copied straight from global memory into LDS by
+// the direct-to-LDS loads, with no register staging.  X has two LDS buffers
+// and is copied one stage ahead; the packed words and metadata have three and
+// are copied two stages ahead, so the words of the next k-step are always
+// readable.  Each wave software-pipelines its k-steps: while the 32 MFMAs of
+// step q run, it dequantises the B operands of step q+1 and reads the X
+// operands two row tiles ahead.  One wait and one barrier end each stage.
 #include "device.hpp"
 #include "launch.hpp"
 #include "w4a16_ops.hpp"
 
 namespace awq4 {
 
-constexpr int GB_M = 128, GB_N = 256, GB_K = 64;
-constexpr int GA_PITCH = GB_K * 2 + 16;          // bytes per X row in LDS (16 B pad: conflict-free row reads)
-constexpr int GA_BYTES = GB_M * GA_PITCH;        // 18432
-constexpr int GB_PITCH = (GB_N / 8) * 4;         // bytes per k-row of packed words (32 words)
-constexpr int GB_BYTES = GB_K * GB_PITCH;        // 8192
-constexpr int G_STAGE = GA_BYTES + GB_BYTES;     // 26624; two stages = 53248 bytes of LDS
+constexpr int GB_M = 256, GB_N = 128, GB_K = 64;
+constexpr int GA_PITCH = GB_K * 2;                 // 128 bytes per X row (8 segments of 16 B, swizzled)
+constexpr int GA_BYTES = GB_M * GA_PITCH;          // 32768 per X buffer
+constexpr int GB_PITCH = (GB_N / 8) * 4;           // 64 bytes per k-row of packed words (16 words)
+constexpr int GB_WORDS = GB_K * GB_PITCH;          // 4096
+constexpr int GM_SCALES = 2 * GB_N * 2;            // scales of both k-steps: 2 x 128 x 2 B
+constexpr int GM_ZEROS = 2 * (GB_N / 8) * 4;       // zero words of both k-steps: 2 x 16 x 4 B
+constexpr int GB_BYTES = GB_WORDS + GM_SCALES + GM_ZEROS;  // 4736 per word/metadata buffer
+constexpr int GA_BUFS = 2, GB_BUFS = 3;
+constexpr int G_LDS = GA_BUFS * GA_BYTES + GB_BUFS * GB_BYTES;  // 79744: two workgroups fit in 160 KB
 
-// Packed-word LDS swizzle: 16-byte segment s of k-row r is stored at segment
-// s ^ 4*((r >> 3) & 1), so lane groups reading rows 8 apart use both halves
-// of the banks.
-__device__ __forceinline__ int gseg(int r, int s) { return s ^ (((r >> 3) & 1) << 2); }
+// X rows: 16-byte segment s of row r is stored at position s ^ (r & 7), so the
+// 8 rows read by a lane octet cover all banks.
+__device__ __forceinline__ int aseg(int r, int s) { return s ^ (r & 7); }
+// Packed words: segment s (4 words) of k-row r is stored at s ^ 2*((r>>3)&1),
+// so the two lane groups of a half-wave (rows 8 apart) use disjoint banks.
+__device__ __forceinline__ int bseg(int r, int s) { return s ^ (((r >> 3) & 1) << 1); }
+
+// Output columns of MFMA u relative to the lane's word-column (before + 2h).
+__host__ __device__ constexpr int gemm_col(int u) { return (u & 1) + ((u >> 1) << 2); }
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i of the wave writes
+// bytes [16 i, 16 i + 16) after the wave-uniform LDS address `dst`.
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+// Wait until every vector-memory load of this wave has landed (the direct
+// LDS copies included).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int DT, bool SYM>
 __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
@@ -39,9 +65,11 @@ __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict_
                                                      const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
                                                      uint64_t *__restrict__ acc64, int M, int N, int K, int G,
                                                      int S) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * G_STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[G_LDS];
+    unsigned char *const Abase = lds;
+    unsigned char *const Bbase = lds + GA_BUFS * GA_BYTES;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int j = lane & 15, gq = lane >> 4;
+    const int j = lane & 15, gq = lane >> 4, h = j >> 3;
     const int wm = wave >> 1, wn = wave & 1;
     const int nw = N >> 3;
     const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
@@ -49,142 +77,211 @@ __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict_
     const int T = K / GB_K;
     const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
 
-    // global -> register prefetch assignment: 8 threads per 128-byte row
-    const int ld_row = tid >> 3, ld_seg = tid & 7;
-    // the word-column this lane dequantises and owns in the output
-    const int wcol = wc0 + wn * 16 + j;
+    // Copy assignment (byte offsets from the workgroup's corner; all fit in
+    // 32 bits: at most 256 X rows and 64 k-rows of words are addressed).
+    // X: wave w copies rows 64w + 8i + lane/8 (i < 8), lane%8 being the
+    // stored segment position; rows past M repeat row M-1 (their outputs are
+    // never stored).  Words: wave w copies k-rows 16w + lane/4, lane%4 being
+    // the stored segment; word-columns past the end repeat the last 4.
+    const char *const xg = (const char *)(x + (size_t)m0 * K);
+    const char *const wg = (const char *)(qw + wc0);
+    uint32_t xoff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 64 * wave + 8 * i + (lane >> 3);
+        const int m = min(m0 + r, M - 1);
+        xoff[i] = (uint32_t)(((m - m0) * K + 8 * aseg(r, lane & 7)) * 2);
+    }
+    uint32_t woff;
+    {
+        const int r = 16 * wave + (lane >> 2);
+        const int wc = min(wc0 + 4 * bseg(r, lane & 3), nw - 4);
+        woff = (uint32_t)((r * nw + wc - wc0) * 4);
+    }
+    // Metadata (wave 0): lanes 0..31 copy 8 scales each (k-step lane/16,
+    // word-column wc0 + lane%16), lanes 32..39 copy 4 zero words each.
+    const int meta_lanes = wave == 0 ? (SYM ? 32 : 40) : 0;
+    int meta_ks, meta_col;
+    if (lane < 32) {
+        meta_ks = lane >> 4;
+        meta_col = min(wc0 + (lane & 15), nw - 1);
+    } else {
+        meta_ks = (lane - 32) >> 2;
+        meta_col = min(wc0 + 4 * ((lane - 32) & 3), nw - 4);
+    }
+
+    auto copyA = [&](int st, int buf) {
+        const char *src = xg + (size_t)st * (GB_K * 2);
+        unsigned char *dst = Abase + buf * GA_BYTES + 64 * wave * GA_PITCH;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16(src + xoff[i], dst + 8 * i * GA_PITCH);
+    };
+    auto copyB = [&](int st) {
+        unsigned char *dst = Bbase + (st % GB_BUFS) * GB_BYTES;
+        dma16(wg + (size_t)st * GB_K * nw * 4 + woff, dst + 16 * wave * GB_PITCH);
+        if (lane < meta_lanes) {
+            const int g = (st * GB_K + 32 * meta_ks) / G;
+            const void *src = lane < 32 ? (const void *)(sc + (size_t)g * N + 8 * meta_col)
+                                        : (const void *)(qz + (size_t)g * nw + meta_col);
+            dma16(src, dst + GB_WORDS);
+        }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[mt][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // per-lane nibble selection: low nibble (h = 0) or high nibble (h = 1)
+    const uint32_t nmask = h ? 0x00F000F0u : 0x000F000Fu;
+    const uint32_t mul2 = h ? 0x2C002C00u : 0x3C003C00u;  // fp16 (1/16, 1/16) or (1, 1)
+    const int wcl = wn * 8 + (j & 7);  // word-column within the workgroup tile
+    const int wcol = wc0 + wcl;
     const bool col_ok = wcol < nw;
-
-    u32x4 pa[4], pb[2], ps4[2];
-    uint32_t pzw[2];
-    auto gload = [&](int st) {
-        const int k0 = st * GB_K;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + ld_row + 32 * i;
-            pa[i] = m < M ? *(const u32x4 *)(x + (size_t)m * K + k0 + ld_seg * 8) : (u32x4){0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int wc = wc0 + ld_seg * 4;  // nw % 4 == 0: all four words valid or none
-            pb[i] = wc < nw ? *(const u32x4 *)(qw + (size_t)(k0 + ld_row + 32 * i) * nw + wc) : (u32x4){0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int g = (k0 + 32 * ks) / G;
-            ps4[ks] = col_ok ? *(const u32x4 *)(sc + (size_t)g * N + 8 * wcol) : (u32x4){0, 0, 0, 0};
-            pzw[ks] = (!SYM && col_ok) ? qz[(size_t)g * nw + wcol] : 0x88888888u;
-        }
-    };
-    auto swrite = [&](int buf) {
-        unsigned char *A = lds + buf * G_STAGE;
-        unsigned char *B = A + GA_BYTES;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4 *)(A + (ld_row + 32 * i) * GA_PITCH + ld_seg * 16) = pa[i];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = ld_row + 32 * i;
-            *(u32x4 *)(B + r * GB_PITCH + gseg(r, ld_seg) * 16) = pb[i];
-        }
-    };
-
-    f32x4 acc[4][8];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[mt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    ZeroConsts<DT> zc;
-    uint32_t sc2[8];
-    float sf[8];
+    uint32_t zc[4], sc2[4];
+    float zf[4], sf[4];
     int gcur = -1;
-    u32x4 cs4[2];
-    uint32_t czw[2];
 
+    // dequantisation constants of this lane's 4 columns for k-step (st, ks)
+    auto load_consts = [&](int st, int ks) {
+        const int g = (st * GB_K + 32 * ks) / G;
+        if (g == gcur) return;
+        gcur = g;
+        const unsigned char *Mt = Bbase + (st % GB_BUFS) * GB_BYTES + GB_WORDS;
+        const uint32_t s_lo2 = *(const uint32_t *)(Mt + ks * (GB_N * 2) + wcl * 16 + 4 * h);
+        const uint32_t s_hi2 = *(const uint32_t *)(Mt + ks * (GB_N * 2) + wcl * 16 + 4 * h + 8);
+        const uint32_t zw = SYM ? 0x88888888u : *(const uint32_t *)(Mt + GM_SCALES + ks * (GB_N / 2) + wcl * 4);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = gemm_col(u) + 2 * h;  // this lane's column of MFMA u
+            const uint32_t z = (zw >> (4 * col_nibble(t))) & 0xFu;
+            const uint32_t sb = ((u >> 1) ? s_hi2 : s_lo2) >> (16 * (u & 1)) & 0xFFFFu;
+            if (DT == DT_F16) {
+                zc[u] = h ? zconst_f16<1>(z) : zconst_f16<0>(z);
+                sc2[u] = sb | (sb << 16);
+            } else {
+                const float s = bf16_bits_to_f32(sb);
+                sf[u] = h ? s * 0.0625f : s;
+                zf[u] = (float)z * s;
+            }
+        }
+    };
+    // packed words of k-step (st, ks): 8 consecutive k-rows of this lane's word-column
+    auto load_words = [&](int st, int ks, uint32_t (&w)[8]) {
+        const unsigned char *B = Bbase + (st % GB_BUFS) * GB_BYTES;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int r = 32 * ks + 8 * gq + e;
+            w[e] = *(const uint32_t *)(B + r * GB_PITCH + bseg(r, wcl >> 2) * 16 + (wcl & 3) * 4);
+        }
+    };
+    // B operand of MFMA u (4 registers = 8 k of one column) from paired words
+    auto dequant = [&](const uint32_t (&px)[4], const uint32_t (&py)[4], int u) {
+        u32x4 bop;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t src = (u & 1) ? py[p] : px[p];
+            const uint32_t v = (u & 2) ? (src >> 8) : src;
+            if (DT == DT_F16) {
+                // exact (q - z): lo nibble h16 - (1024+z); hi nibble h16/16 - (64+z)
+                const f16x2 q16 = bit_as<f16x2>((v & nmask) | 0x64006400u);
+                const f16x2 d = q16 * bit_as<f16x2>(mul2) + bit_as<f16x2>(zc[u]);
+                bop[p] = bit_as<uint32_t>(d * bit_as<f16x2>(sc2[u]));
+            } else {
+                const uint32_t m = v & nmask;
+                const float w0 = __builtin_fmaf((float)(m & 0xFFu), sf[u], -zf[u]);
+                const float w1 = __builtin_fmaf((float)((m >> 16) & 0xFFu), sf[u], -zf[u]);
+                bop[p] = (uint32_t)bit_as<uint16_t>((__bf16)w0) | ((uint32_t)bit_as<uint16_t>((__bf16)w1) << 16);
+            }
+        }
+        return bop;
+    };
+    auto pair_words = [&](const uint32_t (&w)[8], uint32_t (&px)[4], uint32_t (&py)[4]) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            px[p] = pair_x(w[2 * p], w[2 * p + 1]);
+            py[p] = pair_y(w[2 * p], w[2 * p + 1]);
+        }
+    };
+    auto load_a = [&](const unsigned char *A, int ks, int mt) {
+        const int r = wm * 128 + 16 * mt + j;
+        return *(const u32x4 *)(A + r * GA_PITCH + aseg(r, 4 * ks + gq) * 16);
+    };
+
+    u32x4 bc[4];  // B operands of the current k-step
     if (s_lo < s_hi) {
-        gload(s_lo);
-        swrite(0);
-        cs4[0] = ps4[0];
-        cs4[1] = ps4[1];
-        czw[0] = pzw[0];
-        czw[1] = pzw[1];
+        copyB(s_lo);
+        copyA(s_lo, 0);
+        if (s_lo + 1 < s_hi) copyB(s_lo + 1);
+        wait_vm_all();
+        __syncthreads();
+        uint32_t w[8], px[4], py[4];
+        load_words(s_lo, 0, w);
+        load_consts(s_lo, 0);
+        pair_words(w, px, py);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) bc[u] = dequant(px, py, u);
     }
-    __syncthreads();
     for (int st = s_lo; st < s_hi; ++st) {
-        const int buf = (st - s_lo) & 1;
+        const int abuf = (st - s_lo) & 1;
         const bool more = st + 1 < s_hi;
-        if (more) gload(st + 1);
-        const unsigned char *A = lds + buf * G_STAGE;
-        const unsigned char *B = A + GA_BYTES;
+        if (more) copyA(st + 1, abuf ^ 1);
+        if (st + 2 < s_hi) copyB(st + 2);
+        const unsigned char *A = Abase + abuf * GA_BYTES;
+        u32x4 a[8];
+        a[0] = load_a(A, 0, 0);
+        a[1] = load_a(A, 0, 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int g = (st * GB_K + 32 * ks) / G;
-            if (g != gcur) {
-                gcur = g;
-                zero_consts<DT, SYM>(zc, czw[ks]);
+            // the next k-step: (st, 1) or (st + 1, 0).  After the last stage
+            // this dequantises stale (in-bounds) LDS data that is never used,
+            // which keeps the loop body free of branches.
+            const int nst = st + ks, nks = ks ^ 1;
+            uint32_t w[8], px[4], py[4];
+            u32x4 bn[4];
+            load_words(nst, nks, w);
+            load_consts(nst, nks);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const uint32_t b = scale_bits<DT>(cs4[ks], t);
-                    sc2[t] = b | (b << 16);
-                    sf[t] = scale_f32<DT>(cs4[ks], t);
-                }
+            for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[mt][u] = mma<DT>(a[mt], bc[u], acc[mt][u]);
+                // X operands two row tiles ahead (within this stage only)
+                if (mt + 2 < 8) a[mt + 2] = load_a(A, ks, mt + 2);
+                else if (ks == 0) a[mt - 6] = load_a(A, 1, mt - 6);
+                if (mt == 0) pair_words(w, px, py);
+                if (mt & 1) bn[mt >> 1] = dequant(px, py, mt >> 1);
             }
-            u32x4 a[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                a[mt] = *(const u32x4 *)(A + (wm * 64 + 16 * mt + j) * GA_PITCH + (32 * ks + 8 * gq) * 2);
-            uint32_t w[8];
-            const int c = wn * 16 + j;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = 32 * ks + 8 * gq + e;
-                w[e] = *(const uint32_t *)(B + r * GB_PITCH + gseg(r, c >> 2) * 16 + (c & 3) * 4);
-            }
-            uint32_t px[4], py[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                px[p] = pair_x(w[2 * p], w[2 * p + 1]);
-                py[p] = pair_y(w[2 * p], w[2 * p + 1]);
-            }
-#define AWQ4_COL(T_)                                                                                  \
-    {                                                                                                 \
-        u32x4 bop;                                                                                    \
-        _Pragma("unroll") for (int p = 0; p < 4; ++p) bop[p] =                                        \
-            w_pair<DT, T_>(col_src_y(T_) ? py[p] : px[p], zc, sc2[T_], sf[T_]);                       \
-        _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) acc[mt][T_] = mma<DT>(a[mt], bop, acc[mt][T_]); \
-    }
-            AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
-#undef AWQ4_COL
+            for (int u = 0; u < 4; ++u) bc[u] = bn[u];
         }
-        if (more) {
-            swrite(buf ^ 1);
-            cs4[0] = ps4[0];
-            cs4[1] = ps4[1];
-            czw[0] = pzw[0];
-            czw[1] = pzw[1];
-        }
+        wait_vm_all();
         __syncthreads();
     }
 
-    // Epilogue: lane holds rows m0 + 64wm + 16mt + 4gq + r, columns 8*wcol + t.
+    // Epilogue: lane holds rows m0 + 128wm + 16mt + 4gq + r and, for MFMA u,
+    // column 8*wcol + {0,1,4,5}[u] + 2h (pairs u = 0,1 and u = 2,3 adjacent).
     if (!col_ok) return;
-    const int n0 = 8 * wcol;
+    const int n0 = 8 * wcol + 2 * h;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
+            const int m = m0 + wm * 128 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
             if (S == 1) {
-                f32x4 v0 = {acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
-                f32x4 v1 = {acc[mt][4][r], acc[mt][5][r], acc[mt][6][r], acc[mt][7][r]};
-                *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
+                uint16_t *dst = y + (size_t)m * N + n0;
+                *(uint32_t *)dst = (uint32_t)f32_to_out_bits(acc[mt][0][r], DT) |
+                                   ((uint32_t)f32_to_out_bits(acc[mt][1][r], DT) << 16);
+                *(uint32_t *)(dst + 4) = (uint32_t)f32_to_out_bits(acc[mt][2][r], DT) |
+                                         ((uint32_t)f32_to_out_bits(acc[mt][3][r], DT) << 16);
             } else {
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
+                for (int u = 0; u < 4; ++u) {
+                    const int n = n0 + gemm_col(u);
                     int64_t sum;
-                    if (splitk_contribute(&acc64[(size_t)m * N + n0 + t], to_fixed<DT>(acc[mt][t][r]), S, &sum))
-                        y[(size_t)m * N + n0 + t] = f32_to_out_bits(from_fixed<DT>(sum), DT);
+                    if (splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(acc[mt][u][r]), S, &sum))
+                        y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
                 }
             }
         }
