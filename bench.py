@@ -10,12 +10,15 @@ One step = one pass of the whole hot path over synthetic inputs:
             (QKV 4096x6144, O 4096x4096, gate/up 4096x28672, down 14336x4096);
   w4a8    : per-token activation quantisation + W4A8 GEMM on the QQQ shape
             N=8192, K=21760 at M=1 (rotating weights) and M=1024.
-All inputs are resident in HBM before the timed region.  Each phase of a step
-is one HIP graph (captured once, replayed every step), so the GPU runs the
-kernels back to back without waiting on host-side launches; HIP events on the
-replay stream bracket every phase.  `value` is the decode weight bandwidth:
-(qweight + scales + qzeros bytes of the 4 layers) / decode phase time.  The
-prefill TFLOP/s and the W4A8 figures are reported beside it.
+All inputs are resident in HBM before the timed region.  The timed region runs
+exactly K passes of each phase; each phase is one HIP graph holding its K passes
+back to back (weights rotating through the copies), bracketed by HIP events on
+the replay stream, so a graph's launch cost is paid once per phase rather than
+once per pass.  `value` is the decode weight bandwidth: (qweight + scales +
+qzeros bytes of the 4 layers) / decode time per pass.  The prefill TFLOP/s, the
+W4A8 figures, per-layer times (graphs of one layer over rotating weights), the
+read-only bandwidth probe at each decode layer's size and the stated target
+shapes are reported beside it.
 """
 from __future__ import annotations
 
@@ -39,6 +42,9 @@ PREFILL_LAYERS = [("qkv", 4096, 6144), ("o", 4096, 4096), ("gate_up", 4096, 2867
 G = 128
 M_DECODE, M_PREFILL = 1, 2048
 W4A8_K, W4A8_N, W4A8_M = 21760, 8192, (1, 1024)
+CAL_BYTES = 256 * 2 ** 20                       # calibration copy: bytes read and bytes written
+TARGET_SHAPES = [(4096, 4096), (4096, 14336)]   # (K, N): the stated M=1 / M=2048 targets
+M_TARGETS = (1, 2048)
 ROTATE_MB = 600
 KERNEL_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/gemm_w4a16.hip",
                   "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp", "bit_weight_only_awq_amd/csrc/w4a8.hip",
@@ -79,6 +85,55 @@ def load_traffic(name, digest):
     return d.get("bytes_per_launch")
 
 
+def counter_rows(path):
+    """{dispatch id: (kernel name, {counter: value})} from a rocprofv3 counter_collection.csv."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = out.setdefault(int(r["Dispatch_Id"]), (r["Kernel_Name"], {}))
+            d[1][r["Counter_Name"]] = d[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return dict(sorted(out.items()))
+
+
+def traffic_summary(fetch_csv, write_csv, kernel="w4a16_decode", name="w4a16_decode_m1_llama2_7b"):
+    """HBM bytes per launch of `kernel` in a `--profile decode` run: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, one rocprofv3 pass each), each scaled by what
+    the same counter reads for the calibration copy of CAL_BYTES read + CAL_BYTES
+    written that the profile run launches first.  Writes
+    profiles/<name>.traffic.json for bench.py's roofline object."""
+    res = {}
+    for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = counter_rows(path)
+        cal = [i for i, (k, _) in rows.items() if "neg" in k]
+        if not cal:
+            raise SystemExit(f"no calibration copy dispatch in {path}")
+        cal_kib = rows[cal[-1]][1][ctr]
+        factor = CAL_BYTES / (cal_kib * 1024.0)
+        per_layer = {n: [] for n, _, _ in DECODE_LAYERS}
+        launches = [(i, v) for i, (k, v) in rows.items() if i > cal[-1] and kernel in k]
+        for n, (i, v) in enumerate(launches):
+            per_layer[DECODE_LAYERS[n % len(DECODE_LAYERS)][0]].append(v[ctr] * 1024.0 * factor)
+        res[ctr] = {"calibration_kib": cal_kib, "scale": round(factor, 5), "launches": len(launches),
+                    "per_layer_bytes": {n: round(sum(b) / len(b)) for n, b in per_layer.items() if b}}
+    layers = res["FETCH_SIZE"]["per_layer_bytes"]
+    total = {n: layers[n] + res["WRITE_SIZE"]["per_layer_bytes"][n] for n in layers}
+    alg = {n: w4a16_alg_bytes(1, K, N) for n, K, N in DECODE_LAYERS}
+    out = {"kernel": kernel, "workload": "decode GEMV M=1, Llama-2-7B layer set, g128, weights rotated",
+           "bytes_per_launch": round(sum(total.values()) / len(total)),
+           "alg_bytes_per_launch": round(sum(alg.values()) / len(alg)),
+           "per_layer": {n: {"hbm_bytes": total[n], "alg_bytes": alg[n], "ratio": round(total[n] / alg[n], 4)}
+                         for n in total},
+           "counters": res, "source_digest": source_digest(),
+           "command": "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --profile decode; "
+                      "rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --profile decode; "
+                      "python3 bench.py --traffic <fetch csv> <write csv>"}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{name}.traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(budget_s: float):
     """The oracle on the decode workload (M=1 over the Llama-2-7B layer set), run
     on this host's cores until about budget_s seconds of work are done."""
@@ -110,7 +165,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", choices=["decode", "prefill", "w4a8", "targets"], default=None,
+                    help="no timing: run one phase eagerly --profile-reps times (for rocprofv3 counter passes), "
+                         "after a 256 MiB device copy of known size that calibrates the byte counters")
+    ap.add_argument("--profile-reps", type=int, default=3)
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="CPU only: summarise the two counter passes of `--profile decode` into "
+                         "profiles/w4a16_decode_m1_llama2_7b.traffic.json")
     args = ap.parse_args()
+    if args.traffic:
+        traffic_summary(*args.traffic)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the 4-bit GEMM hot path has no "
                                    "multi-GPU component here (the sharding design is described in DESIGN.md)",
@@ -151,10 +216,24 @@ def main():
         w8a.append((M, x, torch.empty(M, W4A8_K, dtype=torch.int8, device=dev),
                     torch.empty(M, dtype=torch.float32, device=dev),
                     torch.empty(M, W4A8_N, dtype=torch.float16, device=dev)))
-    # copy kernel of known size, used to calibrate HBM byte counters in profiling runs
-    cal_src = torch.ones(64 * 2 ** 20 // 2, dtype=torch.float16, device=dev)
-    cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
+    # target shapes: W4A16 and W4A8 at M=1 (weights rotated through >= ROTATE_MB of
+    # copies) and M=2048 on (4096, 4096) and (4096, 14336)
+    tgt = []
+    for K, N in TARGET_SHAPES:
+        c = synthgen.w4a16_case(1, K, N, G, seed=synthgen.seed_for(f"bench|target|w4a16|{K}|{N}"))
+        ncp = max(2, -(-ROTATE_MB * 10 ** 6 // w4a16_weight_bytes(K, N)))
+        base = (c.qweight.to(dev), c.scales.to(dev), c.qzeros.to(dev))
+        wcopies = [base] + [tuple(t.clone() for t in base) for _ in range(ncp - 1)]
+        c8 = synthgen.w4a8_case(1, K, N, -1, seed=synthgen.seed_for(f"bench|target|w4a8|{K}|{N}"))
+        b8 = (c8.b.to(dev), c8.s2.to(dev))
+        w8copies = [b8] + [tuple(t.clone() for t in b8) for _ in range(ncp - 1)]
+        xs = {M: synthgen.activations(M, K, seed=synthgen.seed_for(f"bench|target|x|{M}|{K}")).to(dev)
+              for M in M_TARGETS}
+        tgt.append({"K": K, "N": N, "w": wcopies, "w8": w8copies, "x": xs,
+                    "y": {M: torch.empty(M, N, dtype=torch.float16, device=dev) for M in M_TARGETS},
+                    "a8": {M: torch.empty(M, K, dtype=torch.int8, device=dev) for M in M_TARGETS},
+                    "s1": {M: torch.empty(M, dtype=torch.float32, device=dev) for M in M_TARGETS}})
+    sink = torch.empty(awq.ops.STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
 
     def run_decode(r, layers=None):
         for li in (layers if layers is not None else range(len(DECODE_LAYERS))):
@@ -173,11 +252,52 @@ def main():
             awq.quant_act(x, a8, s1)
             awq.w4a8_gemm(a8, b, s1, s2, out=y)
 
+    def run_target(t, M, kind, r=0):
+        x, y = t["x"][M], t["y"][M]
+        if kind == "w4a16":
+            qw, sc, qz = t["w"][r % len(t["w"])]
+            (awq.gemv_w4a16 if M <= 8 else awq.gemm_w4a16)(x, qw, sc, qz, G, out=y)
+        else:
+            b, s2 = t["w8"][r % len(t["w8"])]
+            awq.quant_act(x, t["a8"][M], t["s1"][M])
+            awq.w4a8_gemm(t["a8"][M], b, t["s1"][M], s2, out=y)
+
+    def run_targets():
+        for t in tgt:
+            for M in M_TARGETS:
+                for kind in ("w4a16", "w4a8"):
+                    run_target(t, M, kind)
+
     # every op once eagerly: allocates the shared workspace before capture
     run_decode(0)
     run_prefill()
     run_w4a8(0)
+    run_targets()
     torch.cuda.synchronize()
+
+    if args.profile:
+        # copy kernel of known size first (an elementwise negation: 256 MiB read,
+        # 256 MiB written): the counters it produces calibrate the HBM byte
+        # counts of the phase that follows
+        cal_src = torch.ones(CAL_BYTES // 2, dtype=torch.float16, device=dev)
+        cal_dst = torch.empty_like(cal_src)
+        for _ in range(2):
+            torch.neg(cal_src, out=cal_dst)
+        torch.cuda.synchronize()
+        del cal_src, cal_dst
+        for rep in range(args.profile_reps):
+            if args.profile == "decode":
+                for r in range(n_copies):
+                    run_decode(r)
+            elif args.profile == "prefill":
+                run_prefill()
+            elif args.profile == "w4a8":
+                run_w4a8(rep % w8_copies)
+            else:
+                run_targets()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": args.profile, "reps": args.profile_reps, "decode_weight_copies": n_copies}))
+        return
 
     cap = torch.cuda.Stream(dev)
 
@@ -187,43 +307,40 @@ def main():
             fn()
         return g
 
-    g_dec = [capture(lambda r=r: run_decode(r)) for r in range(n_copies)]
-    g_pre = capture(run_prefill)
-    g_w8 = [capture(lambda r=r: run_w4a8(r)) for r in range(w8_copies)]
-    torch.cuda.synchronize()
-
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, rec):
-        e = [ev() for _ in range(4)]
-        e[0].record(stream)
-        g_dec[i % n_copies].replay()
-        e[1].record(stream)
-        g_pre.replay()
-        e[2].record(stream)
-        g_w8[i % w8_copies].replay()
-        e[3].record(stream)
-        if rec is not None:
-            rec.append(e)
-
+    # warm-up passes, eagerly
     for i in range(args.warmup):
-        step(i, None)
+        run_decode(i % n_copies)
+        run_prefill()
+        run_w4a8(i % w8_copies)
     torch.cuda.synchronize()
-    rec = []
-    t0, t1 = ev(), ev()
+
+    # Timed region: exactly K passes of each phase.  Each phase is one HIP graph
+    # holding its K passes back to back (weights rotate through the copies), so
+    # the per-graph launch cost is paid once per phase, not once per pass.
+    K_ = args.steps
+    g_dec = capture(lambda: [run_decode((args.warmup + i) % n_copies) for i in range(K_)])
+    g_pre = capture(lambda: [run_prefill() for _ in range(K_)])
+    g_w8 = capture(lambda: [run_w4a8((args.warmup + i) % w8_copies) for i in range(K_)])
+    torch.cuda.synchronize()
+    e = [ev() for _ in range(4)]
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, rec)
-    t1.record(stream)
+    e[0].record(stream)
+    g_dec.replay()
+    e[1].record(stream)
+    g_pre.replay()
+    e[2].record(stream)
+    g_w8.replay()
+    e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / args.steps
-    K_ = args.steps
-    t_dec = sum(e[0].elapsed_time(e[1]) for e in rec) / 1e3 / K_   # seconds per step
-    t_pre = sum(e[1].elapsed_time(e[2]) for e in rec) / 1e3 / K_
-    t_w8 = sum(e[2].elapsed_time(e[3]) for e in rec) / 1e3 / K_
+    t_dec = e[0].elapsed_time(e[1]) / 1e3 / K_   # seconds per pass
+    t_pre = e[1].elapsed_time(e[2]) / 1e3 / K_
+    t_w8 = e[2].elapsed_time(e[3]) / 1e3 / K_
+    ms_step = e[0].elapsed_time(e[3]) / K_
+    del g_dec, g_pre, g_w8
 
     # per-layer / per-kernel times (outside the timed steps): one graph per
     # layer with launches over rotating weight copies, replayed a few times
@@ -262,6 +379,40 @@ def main():
                             "frac_hbm": round(w4a8_alg_bytes(M, W4A8_K, W4A8_N) / tg / 1e9 / HBM_PEAK_GBS, 4),
                             "frac_i8_mfma": round(ops / tg / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
 
+    # achievable read rate at each decode layer's byte count: the bandwidth probe
+    # streaming the same packed-weight tensors (same rotation)
+    for li, (name, K, N) in enumerate(DECODE_LAYERS):
+        t = per_launch(lambda li=li: [awq.stream_read(decode[r][li][1], sink) for r in range(n_copies)], n_copies)
+        nb = K * N // 2
+        dec_layer[name]["stream_read_us"] = round(t * 1e6, 3)
+        dec_layer[name]["stream_read_GBs"] = round(nb / t / 1e9, 1)
+        dec_layer[name]["frac_of_stream"] = round(dec_layer[name]["weight_GBs"] / (nb / t / 1e9), 4)
+
+    targets = {}
+    for t in tgt:
+        K, N = t["K"], t["N"]
+        for M in M_TARGETS:
+            ncp = len(t["w"]) if M == 1 else 1
+            for kind in ("w4a16", "w4a8"):
+                tt = per_launch(lambda t=t, M=M, kind=kind, ncp=ncp: [run_target(t, M, kind, r) for r in range(ncp)],
+                                ncp, reps=4 if M == 1 else 3)
+                key = f"{kind} M={M} K={K} N={N}"
+                ops = 2 * M * N * K
+                if kind == "w4a16":
+                    ab = w4a16_alg_bytes(M, K, N)
+                    peak = MFMA_F16_PEAK_TFLOPS
+                else:
+                    ab = w4a8_alg_bytes(M, K, N) + 3 * M * K  # + the quant pass (reads x fp16, writes a8)
+                    peak = MFMA_I8_PEAK_TOPS
+                r = {"us": round(tt * 1e6, 2)}
+                if M == 1:
+                    r["alg_GBs"] = round(ab / tt / 1e9, 1)
+                    r["frac_hbm"] = round(ab / tt / 1e9 / HBM_PEAK_GBS, 4)
+                else:
+                    r["T_per_s"] = round(ops / tt / 1e12, 1)
+                    r["frac_mfma"] = round(ops / tt / 1e12 / peak, 4)
+                targets[key] = r
+
     digest = source_digest()
     dec_alg = sum(w4a16_alg_bytes(M_DECODE, K, N) for _, K, N in DECODE_LAYERS)
     achieved = dec_alg / t_dec / 1e9
@@ -286,6 +437,7 @@ def main():
                           "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "per_layer": pre_layer},
            "w4a8_n8192_k21760": w8_res,
+           "targets": {"note": "W4A8 times include the activation-quantisation launch", **targets},
            "phases_us": {"decode": round(t_dec * 1e6, 2), "prefill": round(t_pre * 1e6, 2),
                          "w4a8": round(t_w8 * 1e6, 2)}}
     if not args.no_cpu_baseline:

@@ -6,7 +6,7 @@ a GPU; calling an op needs the built library and a gfx950 device.
 """
 from ._lib import AWQError, lib  # noqa: F401
 from .ops import (gemm_w4a16, gemv_w4a16, linear_w4a16, linear_w4a8, pack, quant_act,  # noqa: F401
-                  unpack, w4a8_gemm, workspace_bytes)
+                  stream_read, unpack, w4a8_gemm, workspace_bytes)
 
 __all__ = ["AWQError", "lib", "gemm_w4a16", "gemv_w4a16", "linear_w4a16", "linear_w4a8", "pack", "quant_act",
-           "unpack", "w4a8_gemm", "workspace_bytes"]
+           "stream_read", "unpack", "w4a8_gemm", "workspace_bytes"]

@@ -203,6 +203,12 @@ int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, in
     return hip_status(launch_unpack(packed, vals, rows, cols, layout, static_cast<hipStream_t>(stream)));
 }
 
+int awq_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream) {
+    if (!src || !sink || bytes <= 0 || bytes % 16 != 0) return AWQ_EINVAL;
+    if (!aligned16(src) || !aligned16(sink)) return AWQ_EALIGN;
+    return hip_status(launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 size_t awq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int group_size, int split_k) {
     if (op == AWQ_OP_GEMM_W4A16 || op == AWQ_OP_GEMV_W4A16) {
         int64_t dummy = 16;  // any aligned non-null value: only shapes are checked here

@@ -70,6 +70,10 @@ hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t
 hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
+// read-only bandwidth probe: at most kStreamMaxBlocks workgroups, one sink
+// word per wave
+constexpr int64_t kStreamMaxBlocks = 2048;
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t st);
 hipError_t launch_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int layout,
                        int32_t *clamp_count, hipStream_t st);
 hipError_t launch_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, int layout,

@@ -167,3 +167,21 @@ def linear_w4a8(x, b, s2, s3=None, group_size: int = -1):
     """Quantise the activations per token, then the W4A8 GEMM."""
     a8, s1 = quant_act(x)
     return w4a8_gemm(a8, b, s1, s2, s3, group_size)
+
+
+# ----------------------------------------------------------------------------- measurement helper
+
+STREAM_SINK_WORDS = 8192
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Read every byte of `src` once on the GPU (bandwidth probe; not part of the
+    method).  Returns the int32 sink of per-wave checksums."""
+    _need_cuda(src, sink)
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(STREAM_SINK_WORDS, dtype=torch.int32, device=src.device)
+    if not src.is_contiguous() or sink.numel() < STREAM_SINK_WORDS or sink.dtype != torch.int32:
+        raise ValueError("stream_read needs a contiguous source and an int32 sink of STREAM_SINK_WORDS words")
+    L.check("awq_stream_read", L.lib().awq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(src.device)))
+    return sink

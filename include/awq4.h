@@ -188,6 +188,20 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
               const void *s3_f16, void *y_f16, int32_t *acc_out, int64_t M, int64_t N,
               int64_t K, int group_size, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * awq_stream_read -- measurement helper, not a step of the method: reads
+ * `bytes` bytes at `src` once (16-byte loads spread over up to 2048
+ * workgroups) and writes an XOR checksum per wave to `sink`, so that the
+ * achievable device-memory read rate at the size of a layer's weights can be
+ * timed beside the GEMV that streams them.
+ *   src:   device, 16-byte aligned, bytes > 0 and bytes % 16 == 0.
+ *   sink:  device uint32 [AWQ_STREAM_SINK_WORDS], overwritten (contents are
+ *          meaningless beyond keeping the loads alive).
+ * Errors: AWQ_EINVAL, AWQ_EALIGN, AWQ_EHIP.
+ */
+#define AWQ_STREAM_SINK_WORDS 8192
+int awq_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,12 @@ def test_pack_validation():
     assert lib.awq_pack(None, None, 0, 8, L.AWQ_LAYOUT_N8, None, None) == L.AWQ_OK  # empty: no-op
     assert lib.awq_unpack(A, A, 8, -8, L.AWQ_LAYOUT_N8, None) == L.AWQ_EINVAL
     assert lib.awq_unpack(None, None, 8, 0, L.W4A8_LAYOUT_K8, None) == L.AWQ_OK
+
+
+def test_stream_read_validation():
+    lib = L.lib()
+    assert lib.awq_stream_read(None, 16, A, None) == L.AWQ_EINVAL
+    assert lib.awq_stream_read(A, 0, A, None) == L.AWQ_EINVAL
+    assert lib.awq_stream_read(A, 24, A, None) == L.AWQ_EINVAL
+    assert lib.awq_stream_read(A, 16, None, None) == L.AWQ_EINVAL
+    assert lib.awq_stream_read(MIS, 16, A, None) == L.AWQ_EALIGN
