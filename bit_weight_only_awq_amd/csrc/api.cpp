@@ -150,7 +150,6 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     hipError_t e;
     switch (p.kind) {
         case 0: e = launch_w4a16_decode(a, p, st); break;
-        case 2: e = launch_w4a16_stream(a, p, st); break;
         case 3: e = launch_w4a16_gemm(a, p, st); break;
         default: e = launch_w4a16_tiled(a, p, st); break;
     }

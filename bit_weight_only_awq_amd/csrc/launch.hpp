@@ -22,11 +22,11 @@ struct W4A16Args {
 
 // Kernel choice and grid for one W4A16 call (pure function of the shape).
 struct W4A16Plan {
-    int kind;     // 0 = decode (chunk) kernel, 1 = tiled kernel, 2 = streaming decode kernel,
+    int kind;     // 0 = decode (chunk) kernel, 1 = tiled kernel,
                   // 3 = LDS-pipelined GEMM (large M)
-    int blk;      // decode: word-columns per lane (1, 2, 4)
-    int cs;       // decode: 32-k steps per wave chunk (1, 2, 4)
-    int waves;    // decode: waves per workgroup (4, 8)
+    int blk;      // decode: word-columns per lane (1, 2)
+    int cs;       // decode: 32-k steps per wave chunk (1, 2)
+    int waves;    // decode: waves per workgroup (4)
     int mt;       // tiled: row tiles per wave (1, 2, 4)
     int tiles_n;  // grid x
     int tiles_m;  // tiled: grid y
@@ -65,7 +65,6 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
 W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);
 
 hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
-hipError_t launch_w4a16_stream(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st);

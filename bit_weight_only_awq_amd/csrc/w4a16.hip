@@ -35,79 +35,51 @@
 
 namespace awq4 {
 
-// Workgroup epilogue of the decode kernels: reduce the 4 waves' partials
-// (waves 1..3 park theirs in LDS, red[wave-1][m][c]; wave 0 adds them in wave
-// order), then either write the output (no split) or contribute the
-// workgroup's M x COLS partial to the counting accumulators (split-K).
+// Workgroup epilogue of the decode kernels: every wave parks its M x COLS
+// partial in LDS (red[wave][m][c]); after one barrier each thread adds the
+// WAVES partials of its elements in wave order (a fixed order, so the result
+// is deterministic) and either writes the output (no split) or contributes the
+// sum to the counting accumulators (split-K; device.hpp).
 template <int BLK, int DT, int WAVES = 4>
 __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red, uint16_t *__restrict__ y,
                                                 uint64_t *__restrict__ acc64, int M, int N, int wave, int gq,
-                                                int j, int wcol0, bool col_ok, int tile) {
+                                                int j, int tile) {
     constexpr int COLS = 128 * BLK;
-    // With split-K the sum is parked in slot 0 (each lane of wave 0
-    // overwrites only entries it has just read) for the whole workgroup to
-    // add out.
-    float *slot = red;
-    if (wave > 0) {
+    const int total = M * COLS;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * gq + r;
-            if (m < M) {
-#pragma unroll
-                for (int b = 0; b < BLK; ++b) {
-                    float *dst = red + ((size_t)(wave - 1) * M + m) * COLS + 8 * (j * BLK + b);
-                    *(f32x4 *)dst = (f32x4){acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
-                    *(f32x4 *)(dst + 4) = (f32x4){acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * gq + r;
-            if (m >= M) continue;
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * gq + r;
+        if (m < M) {
 #pragma unroll
             for (int b = 0; b < BLK; ++b) {
-                f32x4 v0 = {acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
-                f32x4 v1 = {acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
-#pragma unroll
-                for (int w = 0; w < WAVES - 1; ++w) {
-                    const float *src = red + ((size_t)w * M + m) * COLS + 8 * (j * BLK + b);
-                    v0 += *(const f32x4 *)src;
-                    v1 += *(const f32x4 *)(src + 4);
-                }
-                const int n0 = 8 * (wcol0 + b);
-                if (gridDim.y == 1) {
-                    if (col_ok) *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
-                } else {
-                    float *dst = slot + (size_t)m * COLS + 8 * (j * BLK + b);
-                    *(f32x4 *)dst = v0;
-                    *(f32x4 *)(dst + 4) = v1;
-                }
+                float *dst = red + (size_t)wave * total + (size_t)m * COLS + 8 * (j * BLK + b);
+                *(f32x4 *)dst = (f32x4){acc[b][0][r], acc[b][1][r], acc[b][2][r], acc[b][3][r]};
+                *(f32x4 *)(dst + 4) = (f32x4){acc[b][4][r], acc[b][5][r], acc[b][6][r], acc[b][7][r]};
             }
         }
     }
-    if (gridDim.y == 1) return;
     __syncthreads();
-    // every thread contributes a share of the workgroup's M x COLS partial;
-    // the final contribution to an element writes it out
     const int n_base = tile * COLS;
-    const int total = M * COLS;
     for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int n = n_base + c;
-        int64_t sum;
-        if (n < N && splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(slot[idx]), gridDim.y, &sum))
-            y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
+        if (n >= N) continue;
+        float v = red[idx];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += red[(size_t)w * total + idx];
+        if (gridDim.y == 1) {
+            y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
+        } else {
+            int64_t sum;
+            if (splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(v), gridDim.y, &sum))
+                y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
+        }
     }
 }
 
-
 // ===========================================================================
 // Decode kernel.  grid = (column tiles, ceil(chunks / WAVES)), 64*WAVES
-// threads.  Dynamic LDS: (WAVES-1) * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
+// threads.  Dynamic LDS: WAVES * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
 // one counting accumulator per output element, acc64[M][N] (device.hpp).
 // The launch bound asks for 4 waves per SIMD (<= 128 registers): the whole
 // weight stream of a layer must be in flight at once, and this fits without
@@ -232,134 +204,7 @@ __global__ __launch_bounds__(64 * WAVES, 4) void w4a16_decode(const uint16_t *__
         }
     }
 
-    decode_epilogue<BLK, DT, WAVES>(acc, red, y, acc64, M, N, wave, gq, j, wcol0, col_ok, tile);
-}
-
-// ===========================================================================
-// Streaming decode kernel.  grid = (column tiles, S), 256 threads; the 4
-// waves split the workgroup's K slice into contiguous runs of 32-k steps and
-// each wave keeps the next step's weights in flight while it computes the
-// current one (the loop is unrolled by two, alternating two register sets).
-// fp16: per step, tmp = sum(x q 2^-24) and rs = sum(x) come from the matrix
-// cores and acc += s*(2^24 tmp - z rs) on the live rows; bf16: the operand is
-// (q - z) * s rounded once and accumulates directly.
-// Dynamic LDS: 3 * M * (128*BLK) floats (the decode epilogue).
-template <int BLK, int DT>
-struct StreamStep {
-    uint32_t w[8][BLK];
-    u32x4 a;
-    u32x4 s4[BLK];
-    uint32_t zw[BLK];
-};
-
-template <int BLK, int DT, bool SYM>
-__device__ __forceinline__ void stream_load(StreamStep<BLK, DT> &d, const uint16_t *__restrict__ x,
-                                            const uint32_t *__restrict__ qw, const uint16_t *__restrict__ sc,
-                                            const uint32_t *__restrict__ qz, int st, int M, int N, int K, int G,
-                                            int nw, int j, int gq, int wcol0, bool col_ok) {
-    const int k0 = st * 32;
-    const int g = k0 / G;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) load_words<BLK, true>(qw + (size_t)(k0 + 8 * gq + e) * nw + wcol0, col_ok, d.w[e]);
-    d.a = (j < M) ? *(const u32x4 *)(x + (size_t)j * K + k0 + 8 * gq) : (u32x4){0, 0, 0, 0};
-#pragma unroll
-    for (int b = 0; b < BLK; ++b) {
-        d.s4[b] = col_ok ? *(const u32x4 *)(sc + (size_t)g * N + 8 * (wcol0 + b)) : (u32x4){0, 0, 0, 0};
-        d.zw[b] = (!SYM && col_ok) ? qz[(size_t)g * nw + wcol0 + b] : 0x88888888u;
-    }
-}
-
-template <int BLK, int DT, bool SYM>
-__device__ __forceinline__ void stream_compute(const StreamStep<BLK, DT> &d, f32x4 (&acc)[BLK][8], int M, int gq) {
-    if (DT == DT_F16) {
-        const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 rs = mfma_f16(d.a, ones, zero);
-#pragma unroll
-        for (int b = 0; b < BLK; ++b) {
-            uint32_t px[4], py[4], px8[4], py8[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                px[p] = pair_x(d.w[2 * p][b], d.w[2 * p + 1][b]);
-                py[p] = pair_y(d.w[2 * p][b], d.w[2 * p + 1][b]);
-                px8[p] = px[p] >> 8;
-                py8[p] = py[p] >> 8;
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                u32x4 bop;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t src = col_src_y(t) ? (col_shift(t) ? py8[p] : py[p]) : (col_shift(t) ? px8[p] : px[p]);
-                    bop[p] = src & (col_hi(t) ? 0x00F000F0u : 0x000F000Fu);
-                }
-                const f32x4 tmp = mfma_f16(d.a, bop, zero);
-                const float st = scale_f32<DT>(d.s4[b], t);
-                const float zt = SYM ? 8.0f : (float)((d.zw[b] >> (4 * col_nibble(t))) & 0xFu);
-                const float at = st * (col_hi(t) ? 1048576.0f : 16777216.0f);  // s * 2^20 or s * 2^24
-                const float bt = st * zt;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * gq + r < M) acc[b][t][r] = __builtin_fmaf(tmp[r], at, __builtin_fmaf(-bt, rs[r], acc[b][t][r]));
-            }
-        }
-    } else {
-#pragma unroll
-        for (int b = 0; b < BLK; ++b) {
-            ZeroConsts<DT> zc;
-            zero_consts<DT, SYM>(zc, d.zw[b]);
-            uint32_t px[4], py[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                px[p] = pair_x(d.w[2 * p][b], d.w[2 * p + 1][b]);
-                py[p] = pair_y(d.w[2 * p][b], d.w[2 * p + 1][b]);
-            }
-#define AWQ4_COL(T_)                                                                            \
-    {                                                                                           \
-        const float sf = scale_f32<DT>(d.s4[b], T_);                                            \
-        u32x4 bop;                                                                              \
-        _Pragma("unroll") for (int p = 0; p < 4; ++p) bop[p] =                                  \
-            w_pair<DT, T_>(col_src_y(T_) ? py[p] : px[p], zc, 0u, sf);                          \
-        acc[b][T_] = mma<DT>(d.a, bop, acc[b][T_]);                                             \
-    }
-            AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
-#undef AWQ4_COL
-        }
-    }
-}
-
-template <int BLK, int DT, bool SYM>
-__global__ __launch_bounds__(256) void w4a16_stream(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
-                                                    const uint16_t *__restrict__ sc,
-                                                    const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
-                                                    uint64_t *__restrict__ acc64, int M, int N, int K, int G) {
-    extern __shared__ float red[];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = lane & 15, gq = lane >> 4;
-    const int nw = N >> 3;
-    const int tile = blockIdx.x;
-    const int wcol0 = tile * 16 * BLK + j * BLK;
-    const bool col_ok = wcol0 < nw;
-    const int T = K >> 5, S = gridDim.y, split = blockIdx.y;
-    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
-    const int w_lo = s_lo + (s_hi - s_lo) * wave / 4, w_hi = s_lo + (s_hi - s_lo) * (wave + 1) / 4;
-
-    f32x4 acc[BLK][8];
-#pragma unroll
-    for (int b = 0; b < BLK; ++b)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[b][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    StreamStep<BLK, DT> d0, d1;
-    if (w_lo < w_hi) stream_load<BLK, DT, SYM>(d0, x, qw, sc, qz, w_lo, M, N, K, G, nw, j, gq, wcol0, col_ok);
-    for (int st = w_lo; st < w_hi; st += 2) {
-        if (st + 1 < w_hi) stream_load<BLK, DT, SYM>(d1, x, qw, sc, qz, st + 1, M, N, K, G, nw, j, gq, wcol0, col_ok);
-        stream_compute<BLK, DT, SYM>(d0, acc, M, gq);
-        if (st + 1 >= w_hi) break;
-        if (st + 2 < w_hi) stream_load<BLK, DT, SYM>(d0, x, qw, sc, qz, st + 2, M, N, K, G, nw, j, gq, wcol0, col_ok);
-        stream_compute<BLK, DT, SYM>(d1, acc, M, gq);
-    }
-    decode_epilogue<BLK, DT>(acc, red, y, acc64, M, N, wave, gq, j, wcol0, col_ok, tile);
+    decode_epilogue<BLK, DT, WAVES>(acc, red, y, acc64, M, N, wave, gq, j, tile);
 }
 
 // ===========================================================================
@@ -487,7 +332,7 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
 template <int BLK, int CS, int DT, bool SYM, int WAVES>
 static hipError_t launch_decode_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     dim3 grid(p.tiles_n, p.splits);
-    const size_t lds = (size_t)(WAVES - 1) * a.M * 128 * BLK * sizeof(float);
+    const size_t lds = (size_t)WAVES * a.M * 128 * BLK * sizeof(float);
     hipLaunchKernelGGL((w4a16_decode<BLK, CS, DT, SYM, WAVES>), grid, dim3(64 * WAVES), lds, st,
                        (const uint16_t *)a.x, (const uint32_t *)a.qweight, (const uint16_t *)a.scales,
                        (const uint32_t *)a.qzeros, (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G);
@@ -509,38 +354,10 @@ hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream
         case 412: return launch_decode_dt<1, 2, 4>(a, p, st);
         case 421: return launch_decode_dt<2, 1, 4>(a, p, st);
         case 422: return launch_decode_dt<2, 2, 4>(a, p, st);
-        case 424: return launch_decode_dt<2, 4, 4>(a, p, st);
-        case 821: return launch_decode_dt<2, 1, 8>(a, p, st);
-        case 822: return launch_decode_dt<2, 2, 8>(a, p, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int BLK, int DT, bool SYM>
-static hipError_t launch_stream_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
-    dim3 grid(p.tiles_n, p.splits);
-    const size_t lds = (size_t)3 * a.M * 128 * BLK * sizeof(float);
-    hipLaunchKernelGGL((w4a16_stream<BLK, DT, SYM>), grid, dim3(256), lds, st, (const uint16_t *)a.x,
-                       (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
-                       (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G);
-    return hipGetLastError();
-}
-
-template <int BLK>
-static hipError_t launch_stream_dt(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
-    const bool sym = a.qzeros == nullptr;
-    if (a.dtype == DT_F16) return sym ? launch_stream_t<BLK, DT_F16, true>(a, p, st)
-                                      : launch_stream_t<BLK, DT_F16, false>(a, p, st);
-    return sym ? launch_stream_t<BLK, DT_BF16, true>(a, p, st) : launch_stream_t<BLK, DT_BF16, false>(a, p, st);
-}
-
-hipError_t launch_w4a16_stream(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
-    switch (p.blk) {
-        case 1: return launch_stream_dt<1>(a, p, st);
-        case 2: return launch_stream_dt<2>(a, p, st);
-        default: return hipErrorInvalidValue;
-    }
-}
 
 template <int MTW, int DT, bool SYM>
 static hipError_t launch_tiled_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
