@@ -39,6 +39,11 @@
  *    int8 and the whole-K accumulation stays an exact int32; per-channel is the
  *    case with no s3 (w8 = q).
  *  - A row whose fp16 scale s1 rounds to zero quantises to all zeros.
+ *
+ * Parity unpinned: compatibility with real AWQ checkpoints and QQQ exports
+ * (how real files apply the order map, and QQQ's own weight layout).  No such
+ * file or packing source is available; every function here is pinned against
+ * the pages' definitions and the mathematics only.
  */
 #include <math.h>
 #include <pthread.h>
