@@ -49,9 +49,9 @@ struct W4A8Args {
 };
 
 struct W4A8Plan {
-    int kind;  // 0 = skinny, 1 = tiled
+    int kind;  // 0 = skinny, 1 = tiled, 2 = LDS-pipelined GEMM (large M)
     int blk;   // skinny: 64-column sets per lane-row (1, 2)
-    int mt;    // row tiles (skinny: M <= 16*mt; tiled: per wave)
+    int mt;    // row tiles (skinny: M <= 16*mt; tiled and LDS GEMM: per wave)
     int tiles_n, tiles_m, splits;
     size_t workspace_bytes;
     uint64_t *acc;
@@ -67,6 +67,7 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);
 hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
+hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 // read-only bandwidth probe: at most kStreamMaxBlocks workgroups, one sink

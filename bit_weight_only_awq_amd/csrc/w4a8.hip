@@ -329,6 +329,7 @@ static hipError_t launch_tiled8(const W4A8Args &a, const W4A8Plan &p, hipStream_
 }
 
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    if (p.kind == 2) return launch_w4a8_gemm_lds(a, p, st);
     const bool grp = a.s3 != nullptr;
     if (p.kind == 0) {
         switch (p.blk * 10 + p.mt) {
