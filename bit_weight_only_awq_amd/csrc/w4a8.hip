@@ -25,7 +25,8 @@
 namespace awq4 {
 
 // ---------------------------------------------------------------------------
-// Activation quantisation: one workgroup (256 threads) per row.
+// Activation quantisation, general form (any K): one workgroup (256 threads)
+// per row, two passes over the row.
 __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ a8,
                                                          float *__restrict__ s1, int K) {
     __shared__ uint32_t wmax[4];
@@ -74,7 +75,97 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restr
     }
 }
 
+// Quantised value of x (fp16 bits) with scale s: rint(x / s) (half to even)
+// clamped to int8, without a divide.  For fp16 x and s the exact quotient is
+// either a half-integer or at least 2^-12 away from one, and x * r with r
+// within a few ulps of 1/s is within 2^-15 of it, so rint(x * r) is the
+// correctly rounded integer except at exact ties; the residual
+// d = x - q0 * s (exact in one FMA) detects those (|d| == s/2) and moves an
+// odd q0 to the even neighbour.  Checked exhaustively against the correctly
+// rounded fp32 divide for every reachable s, every fp16 x and reciprocals up
+// to 3 ulps off.
+__device__ __forceinline__ uint32_t quant_one(uint32_t h, float s, float r, float hs) {
+    const float f = f16_bits_to_f32(h);
+    float q0 = rintf(f * r);
+    const float d = __builtin_fmaf(-q0, s, f);
+    if (fabsf(d) == hs && (((int)q0) & 1)) q0 += d > 0.0f ? 1.0f : -1.0f;
+    q0 = fminf(fmaxf(q0, -128.0f), 127.0f);
+    return (uint32_t)(int32_t)q0 & 0xFFu;
+}
+
+// Register-resident quantisation: one workgroup of T threads per row, each
+// thread holding NV chunks of 8 values (row length K <= 8 * NV * T, K % 8 ==
+// 0), so the row is read from memory once.
+template <int NV, int T>
+__global__ __launch_bounds__(T) void w4a8_quant_rows(const uint16_t *__restrict__ x, int8_t *__restrict__ a8,
+                                                     float *__restrict__ s1, int K) {
+    __shared__ uint32_t wmax[T / 64];
+    const int m = blockIdx.x;
+    const uint16_t *row = x + (size_t)m * K;
+    int8_t *out = a8 + (size_t)m * K;
+    u32x4 v[NV];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int k = 8 * (threadIdx.x + i * T);
+        v[i] = k < K ? *(const u32x4 *)(row + k) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) mx = max(mx, max(v[i][p] & 0x7FFFu, (v[i][p] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = wmax[0];
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) mx = max(mx, wmax[w]);
+    const float amax = f16_bits_to_f32(mx);
+    const float q32 = amax / 127.0f;  // correctly rounded fp32 divide, once per row
+    const float s = (float)(f16)q32;  // to fp16 (nearest even) and back
+    if (threadIdx.x == 0) s1[m] = s;
+    const float r = __builtin_amdgcn_rcpf(s), hs = 0.5f * s;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int k = 8 * (threadIdx.x + i * T);
+        if (k >= K) break;
+        u32x2 o = {0, 0};
+        if (s != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[e >> 2] |= quant_one((v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, s, r, hs) << (8 * (e & 3));
+        }
+        *(u32x2 *)(out + k) = o;
+    }
+}
+
+template <int NV, int T>
+static hipError_t launch_quant_rows(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st) {
+    hipLaunchKernelGGL((w4a8_quant_rows<NV, T>), dim3((unsigned)M), dim3(T), 0, st, (const uint16_t *)x, a8, s1,
+                       (int)K);
+    return hipGetLastError();
+}
+
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st) {
+    if (K % 8 == 0) {
+        if (K <= 8 * 256 * 4) {
+            switch ((K + 2047) / 2048) {
+                case 1: return launch_quant_rows<1, 256>(x, a8, s1, M, K, st);
+                case 2: return launch_quant_rows<2, 256>(x, a8, s1, M, K, st);
+                case 3: return launch_quant_rows<3, 256>(x, a8, s1, M, K, st);
+                default: return launch_quant_rows<4, 256>(x, a8, s1, M, K, st);
+            }
+        }
+        if (K <= 8 * 1024 * 16) {
+            const int64_t nv = (K + 8191) / 8192;
+            if (nv <= 2) return launch_quant_rows<2, 1024>(x, a8, s1, M, K, st);
+            if (nv <= 3) return launch_quant_rows<3, 1024>(x, a8, s1, M, K, st);
+            if (nv <= 4) return launch_quant_rows<4, 1024>(x, a8, s1, M, K, st);
+            if (nv <= 6) return launch_quant_rows<6, 1024>(x, a8, s1, M, K, st);
+            if (nv <= 8) return launch_quant_rows<8, 1024>(x, a8, s1, M, K, st);
+            if (nv <= 12) return launch_quant_rows<12, 1024>(x, a8, s1, M, K, st);
+            return launch_quant_rows<16, 1024>(x, a8, s1, M, K, st);
+        }
+    }
     hipLaunchKernelGGL(w4a8_quant_kernel, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a8, s1, (int)K);
     return hipGetLastError();
 }

@@ -28,6 +28,26 @@ def test_quant_act_bit_exact(M, K):
     _quant_check(x.to(torch.float16))
 
 
+@pytest.mark.parametrize("K", [8192, 8200, 40968, 131072, 131080])
+def test_quant_act_row_lengths(K):
+    """Row lengths at the boundaries of the register-resident variants (and
+    past them, where the two-pass kernel takes over)."""
+    x = synthgen.activations(3, K, seed=K)
+    x = x * torch.tensor([1e-3, 1.0, 30.0], dtype=torch.float16)[:, None]
+    _quant_check(x.to(torch.float16))
+
+
+@pytest.mark.parametrize("K", [4096, 21760])
+def test_quant_act_ties(K):
+    """Rows made of exact ties: amax 127 (s1 = 1) with half-integer values, and
+    amax 63.5 (s1 = 0.5) with quarter-integer values."""
+    g = torch.Generator().manual_seed(K)
+    r1 = (torch.randint(-254, 255, (K,), generator=g).float() / 2)
+    r2 = (torch.randint(-254, 255, (K,), generator=g).float() / 4)
+    r1[0], r2[0] = 127.0, 63.5
+    _quant_check(torch.stack([r1, r2]).to(torch.float16))
+
+
 def test_quant_act_edge_rows():
     """Worked examples, a zero row, a subnormal-scale row (clamp active) and
     ties: bit-exact with the oracle."""
