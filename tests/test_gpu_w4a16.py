@@ -59,6 +59,16 @@ def test_gemm_llama3_8b_sampled(M, K, N):
     check_fp(yg, y64, "f16", f"gemm M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("K,N", [(4096, 4096), (4096, 14336)])
+@pytest.mark.parametrize("M", [1, 2048])
+def test_target_shapes(M, K, N):
+    """The stated target shapes, at M=1 through the GEMV entry and at M=2048."""
+    c = synthgen.w4a16_case(M, K, N, 128, x_rows=None)
+    rows = None if M == 1 else sample_rows(M, seed=N)
+    yg, y64, _ = _run(c, "gemv" if M == 1 else "gemm", rows=rows)
+    check_fp(yg, y64, "f16", f"target M={M} K={K} N={N}")
+
+
 @pytest.mark.parametrize("sym", [False, True])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("G", [32, 64, 128])
