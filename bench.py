@@ -48,7 +48,9 @@ M_TARGETS = (1, 2048)
 ROTATE_MB = 600
 KERNEL_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/gemm_w4a16.hip",
                   "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp", "bit_weight_only_awq_amd/csrc/w4a8.hip",
-                  "bit_weight_only_awq_amd/csrc/device.hpp", "bit_weight_only_awq_amd/csrc/api.cpp"]
+                  "bit_weight_only_awq_amd/csrc/gemm_w4a8.hip", "bit_weight_only_awq_amd/csrc/stream.hip",
+                  "bit_weight_only_awq_amd/csrc/device.hpp", "bit_weight_only_awq_amd/csrc/launch.hpp",
+                  "bit_weight_only_awq_amd/csrc/api.cpp"]
 
 
 def w4a16_weight_bytes(K, N, G=G, sym=False):
@@ -62,6 +64,12 @@ def w4a16_alg_bytes(M, K, N, G=G):
 
 def w4a8_alg_bytes(M, K, N):
     return K * N // 2 + N * 2 + M * K + 4 * M + 2 * M * N
+
+
+# sources the decode kernel is built from (its traffic counters stay valid while these are unchanged)
+DECODE_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp",
+                  "bit_weight_only_awq_amd/csrc/device.hpp", "bit_weight_only_awq_amd/csrc/launch.hpp",
+                  "bit_weight_only_awq_amd/csrc/api.cpp"]
 
 
 def source_digest(files=KERNEL_SOURCES):
@@ -124,7 +132,7 @@ def traffic_summary(fetch_csv, write_csv, kernel="w4a16_decode", name="w4a16_dec
            "alg_bytes_per_launch": round(sum(alg.values()) / len(alg)),
            "per_layer": {n: {"hbm_bytes": total[n], "alg_bytes": alg[n], "ratio": round(total[n] / alg[n], 4)}
                          for n in total},
-           "counters": res, "source_digest": source_digest(),
+           "counters": res, "source_digest": source_digest(DECODE_SOURCES),
            "command": "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --profile decode; "
                       "rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --profile decode; "
                       "python3 bench.py --traffic <fetch csv> <write csv>"}
@@ -430,7 +438,7 @@ def main():
            "roofline": {"kernel": "w4a16_decode (decode GEMV, M=1, 4 Llama-2-7B layers back to back)",
                         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": load_traffic("w4a16_decode_m1_llama2_7b", digest),
+                        "traffic": load_traffic("w4a16_decode_m1_llama2_7b", source_digest(DECODE_SOURCES)),
                         "avg_launch_us": round(t_dec / len(DECODE_LAYERS) * 1e6, 3),
                         "per_layer": dec_layer},
            "gemm_m2048": {"kernel": "w4a16_gemm (prefill GEMM, M=2048, 4 Llama-3-8B layers back to back)",
