@@ -106,13 +106,12 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         p.splits = (int)std::max<int64_t>(1, s);
     }
     if (M >= 128) {
-        // LDS-pipelined int8 GEMM: (32 * mt) x 128 workgroup tiles, K in stages of 64
+        // LDS-pipelined int8 GEMM: 128 x 128 workgroup tiles, K in stages of 64
         p.kind = 2;
         p.blk = 1;
-        // 256-row tiles only where they still give two workgroups per CU
-        p.mt = cdiv(M, 256) * cdiv(N, 128) >= 512 ? 8 : 4;
+        p.mt = 4;
         p.tiles_n = (int)cdiv(N, 128);
-        p.tiles_m = (int)cdiv(M, 32 * p.mt);
+        p.tiles_m = (int)cdiv(M, 128);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         int64_t s = 1;
         if (tiles < 256) s = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, T / 4));

@@ -113,6 +113,20 @@ __device__ __forceinline__ uint16_t f32_to_out_bits(float v, int dt) {
 }
 
 // ---------------------------------------------------------------------------
+// XCD-aware tile order.  Workgroups are dispatched round-robin over the 8
+// XCDs (workgroup i of a launch runs on XCD i % 8), and each XCD has its own
+// L2.  Tile `tile_of_xcd_order(i, T)` gives XCD x a contiguous run of the T
+// tiles (in row-major tile order, so the workgroups of one XCD share X row
+// blocks in that XCD's L2) instead of every eighth tile.  A bijection of
+// 0..T-1 for any T.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int tile_of_xcd_order(int i, int T) {
+    const int x = i % kXcds, l = i / kXcds;
+    const int q = T / kXcds, r = T % kXcds;
+    return x * q + min(x, r) + l;
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core wrappers.
 __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(bit_as<f16x8>(a), bit_as<f16x8>(b), c, 0, 0, 0);

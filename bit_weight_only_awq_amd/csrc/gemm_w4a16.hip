@@ -72,7 +72,9 @@ __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict_
     const int j = lane & 15, gq = lane >> 4, h = j >> 3;
     const int wm = wave >> 1, wn = wave & 1;
     const int nw = N >> 3;
-    const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
+    // logical tile of this workgroup (XCD-aware order over the tiles_n x tiles_m grid)
+    const int tile = tile_of_xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    const int tn = tile % gridDim.x, tm = tile / gridDim.x, split = blockIdx.z;
     const int m0 = tm * GB_M, wc0 = tn * (GB_N / 8);
     const int T = K / GB_K;
     const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);

@@ -5,31 +5,27 @@
 // per token and s2 per channel on the output, per-group scales in addition
 // for grouped weights -- here integer s3 folded into the int8 weights).
 //
-// Workgroup tile (32*MT) x 128, K in stages of 64 (one 16x16x64 step); 4
-// waves in a 2 x 2 grid, each owning (16*MT) x 64 outputs: MT row tiles x 4
-// column MFMAs.  Lane j of a wave reads 16 bytes = 4 consecutive columns of
-// two K8 word rows, which give the B operands of its 4 MFMAs (output column
-// = 64*wn + 4j + u).  a8 rows, packed words and (grouped) s3 rows are copied
-// straight from global memory into LDS by the direct-to-LDS loads: a8 one
-// stage ahead in two buffers, words and s3 two stages ahead in three, so one
-// wait and one barrier end each stage.
+// The int4 -> int8 step costs two VALU instructions per word, so a 64 x 64
+// wave tile keeps the VALU far below the matrix cores; what bounds this
+// kernel is LDS latency, which the copy ring and the operand prefetch hide.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace awq4 {
 
-constexpr int W8_N = 128, W8_K = 64;
-constexpr int W8_APITCH = W8_K;                  // 64 bytes of a8 per row (4 segments, swizzled)
-constexpr int W8_WORDS = (W8_K / 8) * W8_N * 4;  // 8 word rows x 128 columns x 4 B = 4096
-constexpr int W8_S3 = 2 * W8_N * 2;              // s3 of the stage's two 32-k halves: 2 x 128 x fp16
-constexpr int W8_BBYTES = W8_WORDS + W8_S3;      // 4608 per word buffer
-constexpr int W8_ABUFS = 2, W8_BBUFS = 3;
+constexpr int W8_M = 128, W8_N = 128, W8_K = 64;
+constexpr int W8_RING = 4;                         // stages per LDS ring (copied three ahead)
+constexpr int W8_APITCH = W8_K;                    // 64 bytes of a8 per row (4 segments, swizzled)
+constexpr int W8_ABYTES = W8_M * W8_APITCH;        // 8192 per stage
+constexpr int W8_WORDS = (W8_K / 8) * W8_N * 4;    // 8 word rows x 128 columns x 4 B = 4096
+constexpr int W8_S3 = 2 * W8_N * 2;                // s3 of the stage's two 32-k halves: 2 x 128 x fp16
 
-template <int MT>
-struct W8Tile {
-    static constexpr int M = 32 * MT;
-    static constexpr int ABYTES = M * W8_APITCH;
-    static constexpr int LDS = W8_ABUFS * ABYTES + W8_BBUFS * W8_BBYTES;
+template <bool GROUP>
+struct W8Layout {
+    static constexpr int BBYTES = W8_WORDS + (GROUP ? W8_S3 : 0);
+    static constexpr int OFF_B = W8_RING * W8_ABYTES;
+    static constexpr int LDS = OFF_B + W8_RING * BBYTES;  // 49152 (per channel) / 51200 (grouped)
+    static constexpr int COPIES = 3 + (GROUP ? 1 : 0);      // copies per wave and stage
 };
 
 // a8 rows: 16-byte segment s of row r is stored at s ^ ((r >> 1) & 3), so the
@@ -64,35 +60,44 @@ __device__ __forceinline__ u32x4 b8_operand(uint32_t w0, uint32_t w1, uint32_t s
     return b;
 }
 
-template <int MT, bool GROUP>
+// Workgroup tile 128 x 128, K in stages of 64 (one 16x16x64 step); 4 waves in
+// a 2 x 2 grid, each owning 64 x 64 outputs: 4 row tiles x 4 column MFMAs.
+// Lane j reads 16 bytes = 4 consecutive columns of two K8 word rows, which
+// give the B operands of its 4 MFMAs (output column = 64 wn + 4j + u).
+// a8 rows, word rows and (grouped) s3 rows are copied into 4-slot LDS rings
+// three stages ahead; each stage waits only for the copies older than its
+// own, so the next stage is always readable and its operands are loaded while
+// the current stage's MFMAs run.
+template <bool GROUP>
 __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                        const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                        const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                        int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
                                                        int M, int N, int K, int G, int S) {
-    using T = W8Tile<MT>;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[T::LDS];
-    unsigned char *const Abase = lds;
-    unsigned char *const Bbase = lds + W8_ABUFS * T::ABYTES;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    using L = W8Layout<GROUP>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[L::LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int j = lane & 15, gq = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
-    const int m0 = tm * T::M, n0 = tn * W8_N;
+    // logical tile of this workgroup (XCD-aware order over the tiles_n x tiles_m grid)
+    const int tile = tile_of_xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    const int tn = tile % gridDim.x, tm = tile / gridDim.x, split = blockIdx.z;
+    const int m0 = tm * W8_M, n0 = tn * W8_N;
     const int Tst = K / W8_K;
     const int s_lo = (int)((int64_t)Tst * split / S), s_hi = (int)((int64_t)Tst * (split + 1) / S);
 
-    // Copy assignment.  a8: wave w copies rows (M/4) w + 16 i + lane/4, lane%4
-    // being the stored segment position; rows past M repeat row M-1 (their
-    // outputs are never stored).  Words: wave w copies word rows 2w and 2w+1,
-    // lane%32 being the 4-column segment; columns past N repeat the last 4.
-    constexpr int AROWS_W = T::M / 4;  // rows per wave
-    constexpr int ACOPIES = AROWS_W / 16;
+    // Copy assignment.  a8: wave w copies rows 32w + 16i + lane/4 (i < 2),
+    // lane%4 being the stored segment position; rows past M repeat row M-1
+    // (their outputs are never stored).  Words: wave w copies word rows 2w and
+    // 2w+1, lane%32 being the 4-column segment; columns past N repeat the last
+    // 4.  s3 (grouped): wave w, lanes 0..7, copies 16-byte segments 8w..8w+7 of
+    // the stage's two s3 rows (half h = segment / 16).
     const int8_t *const ag = a8 + (size_t)m0 * K;
-    uint32_t aoff[ACOPIES];
+    uint32_t aoff[2];
 #pragma unroll
-    for (int i = 0; i < ACOPIES; ++i) {
-        const int r = AROWS_W * wave + 16 * i + (lane >> 2);
+    for (int i = 0; i < 2; ++i) {
+        const int r = 32 * wave + 16 * i + (lane >> 2);
         const int m = min(m0 + r, M - 1);
         aoff[i] = (uint32_t)((m - m0) * K + 16 * a8seg(r, lane & 3));
     }
@@ -100,72 +105,93 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     {
         const int r = 2 * wave + (lane >> 5);
         const int c = min(n0 + 4 * (lane & 31), N - 4);
-        boff = (uint32_t)(r * N + c);
+        boff = (uint32_t)((r * N + c) * 4);
     }
-    // s3 (grouped): wave 0 lanes 0..31, half h = lane/16, 8 columns each
-    const int s3_h = (lane >> 4) & 1;
-    const int s3_c = min(n0 + 8 * (lane & 15), N - 8);
+    const int s3_seg = 8 * wave + (lane & 7);
+    const int s3_h = s3_seg >> 4;
+    const uint32_t s3_off = (uint32_t)(2 * min(n0 + 8 * (s3_seg & 15), N - 8));
 
-    auto copyA = [&](int st, int buf) {
+    auto copy_stage = [&](int st, int slot) {
+        unsigned char *A = lds + slot * W8_ABYTES + 32 * wave * W8_APITCH;
         const int8_t *src = ag + (size_t)st * W8_K;
-        unsigned char *dst = Abase + buf * T::ABYTES + AROWS_W * wave * W8_APITCH;
 #pragma unroll
-        for (int i = 0; i < ACOPIES; ++i) dma16_w8(src + aoff[i], dst + 16 * i * W8_APITCH);
-    };
-    auto copyB = [&](int st) {
-        unsigned char *dst = Bbase + (st % W8_BBUFS) * W8_BBYTES;
-        dma16_w8(bq + (size_t)st * (W8_K / 8) * N + boff, dst + 2 * wave * (W8_N * 4));
-        if (GROUP && wave == 0 && lane < 32) {
+        for (int i = 0; i < 2; ++i) dma16_w8(src + aoff[i], A + 16 * i * W8_APITCH);
+        unsigned char *B = lds + L::OFF_B + slot * L::BBYTES;
+        dma16_w8((const char *)bq + (size_t)st * (W8_K / 8) * N * 4 + boff, B + 2 * wave * (W8_N * 4));
+        if (GROUP && lane < 8) {
             const int g = (st * W8_K + 32 * s3_h) / G;
-            dma16_w8(s3 + (size_t)g * N + s3_c, dst + W8_WORDS);
+            dma16_w8((const char *)(s3 + (size_t)g * N) + s3_off, B + W8_WORDS + 16 * s3_seg);
         }
     };
 
-    i32x4 acc[MT][4];
+    i32x4 acc[4][4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[mt][u] = (i32x4){0, 0, 0, 0};
 
     const int cl = 64 * wn + 4 * j;  // this lane's first column within the tile
-    if (s_lo < s_hi) {
-        copyB(s_lo);
-        copyA(s_lo, 0);
-        if (s_lo + 1 < s_hi) copyB(s_lo + 1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-    }
-    for (int st = s_lo; st < s_hi; ++st) {
-        const int abuf = (st - s_lo) & 1;
-        if (st + 1 < s_hi) copyA(st + 1, abuf ^ 1);
-        if (st + 2 < s_hi) copyB(st + 2);
-        const unsigned char *A = Abase + abuf * T::ABYTES;
-        const unsigned char *B = Bbase + (st % W8_BBUFS) * W8_BBYTES;
-        const u32x4 w0 = *(const u32x4 *)(B + (2 * gq) * (W8_N * 4) + cl * 4);
-        const u32x4 w1 = *(const u32x4 *)(B + (2 * gq + 1) * (W8_N * 4) + cl * 4);
+    const uint32_t a_off = (uint32_t)((wm * 64 + j) * W8_APITCH + a8seg(j, gq) * 16);
+    const uint32_t w_off = (uint32_t)(L::OFF_B + (2 * gq) * (W8_N * 4) + cl * 4);
+    const uint32_t g_off = (uint32_t)(L::OFF_B + W8_WORDS + (gq >> 1) * (W8_N * 2) + cl * 2);
+
+    // operands of the stage in ring slot `slot`
+    struct Ops {
+        u32x4 a[4];
+        u32x4 b[4];
+    };
+    auto load_ops = [&](int slot, Ops &o) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            o.a[mt] = *(const u32x4 *)(lds + slot * W8_ABYTES + a_off + mt * 16 * W8_APITCH);
+        const u32x4 w0 = *(const u32x4 *)(lds + slot * L::BBYTES + w_off);
+        const u32x4 w1 = *(const u32x4 *)(lds + slot * L::BBYTES + w_off + W8_N * 4);
         uint32_t g3[4] = {16u, 16u, 16u, 16u};
         if (GROUP) {
-            const u32x2 sv = *(const u32x2 *)(B + W8_WORDS + (gq >> 1) * (W8_N * 2) + cl * 2);
+            const u32x2 sv = *(const u32x2 *)(lds + slot * L::BBYTES + g_off);
 #pragma unroll
             for (int u = 0; u < 4; ++u) g3[u] = (uint32_t)f16_bits_to_f32((sv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
         }
-        u32x4 a[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int r = wm * 16 * MT + 16 * mt + j;
-            a[mt] = *(const u32x4 *)(A + r * W8_APITCH + a8seg(r, gq) * 16);
-        }
+        for (int u = 0; u < 4; ++u) o.b[u] = b8_operand<GROUP>(w0[u], w1[u], g3[u]);
+    };
+    // Stage st (its operands already in `cur`): load stage st + 1 into `nxt`
+    // while the 16 MFMAs run, then wait for the copies older than this
+    // stage's and cross the barrier.  Copies: stage st + 3 into the slot of
+    // stage st - 1 (finished before the last barrier); near the end the last
+    // stage is copied again into that slot, never read as data, so every
+    // stage issues the same copies and the wait count is fixed.
+    auto stage = [&](int st, Ops &cur, Ops &nxt) {
+        copy_stage(min(st + W8_RING - 1, s_hi - 1), (st - s_lo + W8_RING - 1) & (W8_RING - 1));
+        load_ops((st + 1 - s_lo) & (W8_RING - 1), nxt);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const u32x4 bop = b8_operand<GROUP>(w0[u], w1[u], g3[u]);
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt][u] = mfma_i8(a[mt], bop, acc[mt][u]);
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+            for (int u = 0; u < 4; ++u) acc[mt][u] = mfma_i8(cur.a[mt], cur.b[u], acc[mt][u]);
+        if (L::COPIES == 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0F73);                 // vmcnt(3)
+        // no memory fence (it would wait for every copy); the clobber keeps
+        // LDS accesses from moving across the barrier
+        asm volatile("s_barrier" ::: "memory");
+    };
+
+    if (s_lo < s_hi) {
+        Ops o0, o1;
+#pragma unroll
+        for (int d = 0; d < W8_RING - 1; ++d)
+            if (s_lo + d < s_hi) copy_stage(s_lo + d, d);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+        load_ops(0, o0);
+        int st = s_lo;
+        for (; st + 2 <= s_hi; st += 2) {
+            stage(st, o0, o1);
+            stage(st + 1, o1, o0);
+        }
+        if (st < s_hi) stage(st, o0, o1);
     }
 
-    // Epilogue: lane holds rows m0 + 16 MT wm + 16 mt + 4 gq + r, columns
+    // Epilogue: lane holds rows m0 + 64 wm + 16 mt + 4 gq + r, columns
     // n0 + cl + u (u = 0..3, adjacent).  Per-channel accumulators carry the
     // x16 of the upper-nibble int8 and are divided exactly.
     const int nc = n0 + cl;
@@ -174,10 +200,10 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
 #pragma unroll
     for (int u = 0; u < 4; ++u) s2f[u] = f16_bits_to_f32(s2[nc + u]);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm * 16 * MT + 16 * mt + 4 * gq + r;
+            const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
             const float s1m = s1[m];
             if (S == 1) {
@@ -205,21 +231,16 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         }
 }
 
-template <int MT, bool GROUP>
+template <bool GROUP>
 static hipError_t launch_lds8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    hipLaunchKernelGGL((w4a8_gemm_lds<MT, GROUP>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
+    hipLaunchKernelGGL((w4a8_gemm_lds<GROUP>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
                        (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    const bool grp = a.s3 != nullptr;
-    switch (p.mt) {
-        case 4: return grp ? launch_lds8<4, true>(a, p, st) : launch_lds8<4, false>(a, p, st);
-        case 8: return grp ? launch_lds8<8, true>(a, p, st) : launch_lds8<8, false>(a, p, st);
-        default: return hipErrorInvalidValue;
-    }
+    return a.s3 != nullptr ? launch_lds8<true>(a, p, st) : launch_lds8<false>(a, p, st);
 }
 
 }  // namespace awq4
