@@ -69,6 +69,9 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         if (tiles < 128) s = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, stages / 4));
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
+        // no more workgroups than CUs: two wave groups per workgroup split K
+        // inside it (twice the waves per SIMD, no extra atomics)
+        p.ksplit = tiles * p.splits <= 256 && stages / p.splits >= 4 ? 2 : 1;
     }
     (void)tiles;
     p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;

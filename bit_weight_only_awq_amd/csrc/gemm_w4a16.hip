@@ -59,16 +59,24 @@ __device__ __forceinline__ void dma16(const void *src, void *dst) {
 // LDS copies included).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int DT, bool SYM>
-__global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
-                                                     const uint16_t *__restrict__ sc,
-                                                     const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
-                                                     uint64_t *__restrict__ acc64, int M, int N, int K, int G,
-                                                     int S) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[G_LDS];
+// KS = 2: the workgroup holds two groups of 4 waves that share the output
+// tile and split its K range (each with its own LDS ring); group 1 hands its
+// accumulators to group 0 through LDS at the end.  This doubles the waves per
+// SIMD for layers with no more tiles than CUs.
+template <int DT, bool SYM, int KS>
+__global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *__restrict__ x,
+                                                                const uint32_t *__restrict__ qw,
+                                                                const uint16_t *__restrict__ sc,
+                                                                const uint32_t *__restrict__ qz,
+                                                                uint16_t *__restrict__ y, uint64_t *__restrict__ acc64,
+                                                                int M, int N, int K, int G, int S) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds_all[KS * G_LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = KS == 1 ? 0 : (wv >> 2), wave = wv & 3;
+    unsigned char *const lds = lds_all + grp * G_LDS;
     unsigned char *const Abase = lds;
     unsigned char *const Bbase = lds + GA_BUFS * GA_BYTES;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, gq = lane >> 4, h = j >> 3;
     const int wm = wave >> 1, wn = wave & 1;
     const int nw = N >> 3;
@@ -77,7 +85,12 @@ __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict_
     const int tn = tile % gridDim.x, tm = tile / gridDim.x, split = blockIdx.z;
     const int m0 = tm * GB_M, wc0 = tn * (GB_N / 8);
     const int T = K / GB_K;
-    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
+    // stages of this workgroup, then of this group: group 0 takes the first
+    // ceil(n/2), group 1 the rest; both pass `iters` loop barriers (group 1
+    // adds an idle one when n is odd), so their barriers pair up
+    const int w_lo = (int)((int64_t)T * split / S), w_hi = (int)((int64_t)T * (split + 1) / S);
+    const int iters = (w_hi - w_lo + KS - 1) / KS;
+    const int s_lo = w_lo + grp * iters, s_hi = min(w_hi, s_lo + iters);
 
     // Copy assignment (byte offsets from the workgroup's corner; all fit in
     // 32 bits: at most 256 X rows and 64 k-rows of words are addressed).
@@ -216,8 +229,10 @@ __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict_
         copyB(s_lo);
         copyA(s_lo, 0);
         if (s_lo + 1 < s_hi) copyB(s_lo + 1);
-        wait_vm_all();
-        __syncthreads();
+    }
+    wait_vm_all();
+    __syncthreads();
+    if (s_lo < s_hi) {
         uint32_t w[8], px[4], py[4];
         load_words(s_lo, 0, w);
         load_consts(s_lo, 0);
@@ -263,10 +278,8 @@ __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict_
 
     // Epilogue: lane holds rows m0 + 128wm + 16mt + 4gq + r and, for MFMA u,
     // column 8*wcol + {0,1,4,5}[u] + 2h (pairs u = 0,1 and u = 2,3 adjacent).
-    if (!col_ok) return;
     const int n0 = 8 * wcol + 2 * h;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    auto emit = [&](int mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + wm * 128 + 16 * mt + 4 * gq + r;
@@ -287,21 +300,70 @@ __global__ __launch_bounds__(256, 2) void w4a16_gemm(const uint16_t *__restrict_
                 }
             }
         }
+    };
+    if (KS == 1) {
+        if (!col_ok) return;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) emit(mt);
+        return;
+    }
+    // group 1's idle iteration (odd stage count): its barrier only
+    for (int k = s_hi - s_lo; k < iters; ++k) __syncthreads();
+    // Both groups hold partial sums of the whole tile.  Group 0 finishes row
+    // tiles 0..3 and group 1 row tiles 4..7: each parks the other half in
+    // LDS (both rings are free once the last barrier has passed) and adds
+    // the half parked by the other group, always as group 0 + group 1.
+    f32x4 *xfer = (f32x4 *)lds_all + (size_t)wave * 16 * 64 + lane;
+    f32x4 *const mine = xfer + grp * 4 * 16 * 64, *const theirs = xfer + (grp ^ 1) * 4 * 16 * 64;
+    if (grp == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) mine[(mt * 4 + u) * 64] = acc[4 + mt][u];
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) mine[(mt * 4 + u) * 64] = acc[mt][u];
+    }
+    __syncthreads();
+    if (!col_ok) return;
+    if (grp == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[mt][u] += theirs[(mt * 4 + u) * 64];
+            emit(mt);
+        }
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[4 + mt][u] = theirs[(mt * 4 + u) * 64] + acc[4 + mt][u];
+            emit(4 + mt);
+        }
+    }
 }
 
-template <int DT, bool SYM>
+template <int DT, bool SYM, int KS>
 static hipError_t launch_gemm_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
-    hipLaunchKernelGGL((w4a16_gemm<DT, SYM>), grid, dim3(256), 0, st, (const uint16_t *)a.x,
+    hipLaunchKernelGGL((w4a16_gemm<DT, SYM, KS>), grid, dim3(256 * KS), 0, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
                        (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 
-hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+template <int KS>
+static hipError_t launch_gemm_ks(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     const bool sym = a.qzeros == nullptr;
-    if (a.dtype == DT_F16) return sym ? launch_gemm_t<DT_F16, true>(a, p, st) : launch_gemm_t<DT_F16, false>(a, p, st);
-    return sym ? launch_gemm_t<DT_BF16, true>(a, p, st) : launch_gemm_t<DT_BF16, false>(a, p, st);
+    if (a.dtype == DT_F16)
+        return sym ? launch_gemm_t<DT_F16, true, KS>(a, p, st) : launch_gemm_t<DT_F16, false, KS>(a, p, st);
+    return sym ? launch_gemm_t<DT_BF16, true, KS>(a, p, st) : launch_gemm_t<DT_BF16, false, KS>(a, p, st);
+}
+
+hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    return p.ksplit == 2 ? launch_gemm_ks<2>(a, p, st) : launch_gemm_ks<1>(a, p, st);
 }
 
 }  // namespace awq4

@@ -28,6 +28,7 @@ struct W4A16Plan {
     int cs;       // decode: 32-k steps per wave chunk (1, 2)
     int waves;    // decode: waves per workgroup (4)
     int mt;       // tiled: row tiles per wave (1, 2, 4)
+    int ksplit;   // LDS GEMM: groups of 4 waves per workgroup splitting K (1, 2)
     int tiles_n;  // grid x
     int tiles_m;  // tiled: grid y
     int splits;   // workgroups along K (1 = none); decode: grid y

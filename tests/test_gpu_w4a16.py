@@ -127,6 +127,17 @@ def test_ragged_and_small_shapes(M, K, N, G):
         check_fp(yg, y64, "f16", f"ragged gemv {M}x{K}x{N} g{G}")
 
 
+@pytest.mark.parametrize("M,K,N,G,split", [(200, 1216, 256, 64, 0), (200, 1216, 256, 64, 3), (130, 1216, 384, 32, 0),
+                                           (256, 1152, 4096, 128, 0), (513, 4096, 1032, 128, 0), (300, 640, 640, 64, 0)])
+def test_gemm_few_tiles(M, K, N, G, split):
+    """Layers with no more tiles than CUs: the workgroup's two wave groups
+    split its K stages, odd stage counts included (19 stages over 4 splits:
+    5 per workgroup, so one group idles through a barrier)."""
+    c = synthgen.w4a16_case(M, K, N, G)
+    yg, y64, _ = _run(c, split_k=split)
+    check_fp(yg, y64, "f16", f"few-tile gemm {M}x{K}x{N} g{G} split={split}")
+
+
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 16, 128])
 def test_explicit_split_k(split):
     c = synthgen.w4a16_case(4, 4096, 1024, 128)
