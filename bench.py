@@ -43,6 +43,7 @@ G = 128
 M_DECODE, M_PREFILL = 1, 2048
 W4A8_K, W4A8_N, W4A8_M = 21760, 8192, (1, 1024)
 CAL_BYTES = 256 * 2 ** 20                       # calibration copy: bytes read and bytes written
+PER_LAUNCH_MIN = 64   # launches per graph in the per-layer timings
 TARGET_SHAPES = [(4096, 4096), (4096, 14336)]   # (K, N): the stated M=1 / M=2048 targets
 M_TARGETS = (1, 2048)
 ROTATE_MB = 600
@@ -351,9 +352,12 @@ def main():
     del g_dec, g_pre, g_w8
 
     # per-layer / per-kernel times (outside the timed steps): one graph per
-    # layer with launches over rotating weight copies, replayed a few times
+    # layer with launches over rotating weight copies, replayed a few times.
+    # A graph holds at least PER_LAUNCH_MIN launches (the rotation repeated),
+    # so that the replay's own start-up cost is spread thin.
     def per_launch(fn, launches, reps=4):
-        g = capture(fn)
+        inner = max(1, -(-PER_LAUNCH_MIN // launches))
+        g = capture(lambda: [fn() for _ in range(inner)])
         g.replay()
         torch.cuda.synchronize()
         a, b = ev(), ev()
@@ -362,7 +366,7 @@ def main():
             g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / 1e3 / (reps * launches)
+        return a.elapsed_time(b) / 1e3 / (reps * launches * inner)
 
     dec_layer = {}
     for li, (name, K, N) in enumerate(DECODE_LAYERS):

@@ -21,6 +21,9 @@ static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// workgroups of the CS <= 2 decode kernel resident at once (4 per CU)
+constexpr int64_t kDecodeResidentWGs = 4 * 256;
+
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry) {
     (void)gemv_entry;
     W4A16Plan p{};
@@ -37,6 +40,12 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.tiles_n = (int)cdiv(nw, 16 * p.blk);
         p.tiles_m = 1;
         p.splits = (int)cdiv(K / (32 * p.cs), p.waves);
+        // more workgroups than stay resident (4 per CU): one 128-k group per
+        // wave instead, so that the layer still runs in a single round
+        if (G % 128 == 0 && (int64_t)p.tiles_n * p.splits > kDecodeResidentWGs) {
+            p.cs = 4;
+            p.splits = (int)cdiv(K / 128, p.waves);
+        }
         tiles = p.tiles_n;
     }
     if (M > 16 || p.splits > kMaxSplitK) {

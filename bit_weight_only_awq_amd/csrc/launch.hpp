@@ -25,7 +25,7 @@ struct W4A16Plan {
     int kind;     // 0 = decode (chunk) kernel, 1 = tiled kernel,
                   // 3 = LDS-pipelined GEMM (large M)
     int blk;      // decode: word-columns per lane (1, 2)
-    int cs;       // decode: 32-k steps per wave chunk (1, 2)
+    int cs;       // decode: 32-k steps per wave chunk (1, 2, 4)
     int waves;    // decode: waves per workgroup (4)
     int mt;       // tiled: row tiles per wave (1, 2, 4)
     int ksplit;   // LDS GEMM: groups of 4 waves per workgroup splitting K (1, 2)

@@ -81,11 +81,14 @@ __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red
 // Decode kernel.  grid = (column tiles, ceil(chunks / WAVES)), 64*WAVES
 // threads.  Dynamic LDS: WAVES * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
 // one counting accumulator per output element, acc64[M][N] (device.hpp).
-// The launch bound asks for 4 waves per SIMD (<= 128 registers): the whole
-// weight stream of a layer must be in flight at once, and this fits without
-// spills (measured faster than the compiler's own 3-wave allocation).
+// The launch bound asks for 4 waves per SIMD (<= 128 registers) at CS <= 2:
+// the whole weight stream of a layer must be in flight at once, and this fits
+// without spills (measured faster than the compiler's own 3-wave allocation).
+// CS = 4 (one 128-k group per wave, about 140 registers, 3 waves per SIMD)
+// halves the workgroup count for layers whose CS = 2 grid would not be
+// resident all at once, so that they still run as a single round.
 template <int BLK, int CS, int DT, bool SYM, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 4) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
+__global__ __launch_bounds__(64 * WAVES, CS >= 4 ? 2 : 4) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
                                                     const uint16_t *__restrict__ sc,
                                                     const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
                                                     uint64_t *__restrict__ acc64, int M, int N, int K, int G) {
@@ -97,6 +100,9 @@ __global__ __launch_bounds__(64 * WAVES, 4) void w4a16_decode(const uint16_t *__
     const int tile = blockIdx.x;
     const int wcol0 = tile * 16 * BLK + j * BLK;  // lane's first word-column
     const bool col_ok = wcol0 < nw;
+    // lanes past the last word-column load the last in-bounds words instead
+    // (their sums are never stored), so that every load is unconditional
+    const int wld = col_ok ? wcol0 : nw - BLK;
     const int chunk = blockIdx.y * WAVES + wave;
     const bool active = chunk < K / CK;
 
@@ -109,24 +115,34 @@ __global__ __launch_bounds__(64 * WAVES, 4) void w4a16_decode(const uint16_t *__
     if (active) {
         const int k0 = chunk * CK;
         const int g = k0 / G;  // the chunk lies inside one group
-        // every load of the chunk is issued before any is used
+        // every load of the chunk is issued before any is used; the scales,
+        // zero points and activations go first, so that they do not queue
+        // behind the weight stream
+        u32x4 s4[BLK];
+        uint32_t zw[BLK];
+#pragma unroll
+        for (int b = 0; b < BLK; ++b) {
+            s4[b] = *(const u32x4 *)(sc + (size_t)g * N + 8 * (wld + b));
+            zw[b] = SYM ? 0x88888888u : qz[(size_t)g * nw + wld + b];
+        }
+        u32x4 a[CS];
+        const int xr = j < M ? j : 0;  // rows past M read row 0 and are zeroed below
+#pragma unroll
+        for (int s = 0; s < CS; ++s) a[s] = *(const u32x4 *)(x + (size_t)xr * K + k0 + 32 * s + 8 * gq);
+        // keep the issue order: the scheduler would otherwise sink the small
+        // loads next to their late use, a whole memory round trip later
+        __builtin_amdgcn_sched_barrier(0);
         uint32_t w[CS][8][BLK];
 #pragma unroll
         for (int s = 0; s < CS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                load_words<BLK, true>(qw + (size_t)(k0 + 32 * s + 8 * gq + e) * nw + wcol0, col_ok, w[s][e]);
-        u32x4 s4[BLK];
-        uint32_t zw[BLK];
+                load_words<BLK, true>(qw + (size_t)(k0 + 32 * s + 8 * gq + e) * nw + wld, true, w[s][e]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j >= M) {
 #pragma unroll
-        for (int b = 0; b < BLK; ++b) {
-            s4[b] = col_ok ? *(const u32x4 *)(sc + (size_t)g * N + 8 * (wcol0 + b)) : (u32x4){0, 0, 0, 0};
-            zw[b] = (!SYM && col_ok) ? qz[(size_t)g * nw + wcol0 + b] : 0x88888888u;
+            for (int s = 0; s < CS; ++s) a[s] = (u32x4){0, 0, 0, 0};
         }
-        u32x4 a[CS];
-#pragma unroll
-        for (int s = 0; s < CS; ++s)
-            a[s] = (j < M) ? *(const u32x4 *)(x + (size_t)j * K + k0 + 32 * s + 8 * gq) : (u32x4){0, 0, 0, 0};
 
         if (DT == DT_F16) {
             // B operand = the masked nibble pair itself, read as fp16
@@ -163,16 +179,23 @@ __global__ __launch_bounds__(64 * WAVES, 4) void w4a16_decode(const uint16_t *__
                     AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
 #undef AWQ4_COL
                 }
+                float at[8], bt[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const float st = scale_f32<DT>(s4[b], t);
                     const float zt = SYM ? 8.0f : (float)((zw[b] >> (4 * col_nibble(t))) & 0xFu);
-                    const float at = st * (col_hi(t) ? 1048576.0f : 16777216.0f);  // s * 2^20 or s * 2^24
-                    const float bt = st * zt;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (4 * gq + r < M) acc[b][t][r] = __builtin_fmaf(acc[b][t][r], at, -bt * rs[r]);
+                    at[t] = st * (col_hi(t) ? 1048576.0f : 16777216.0f);  // s * 2^20 or s * 2^24
+                    bt[t] = st * zt;
                 }
+                // only the first min(M, 4) of a lane's rows can be live (the
+                // rows past M are zero and never stored): a uniform bound
+                // instead of a per-lane row test
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (r < M) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) acc[b][t][r] = __builtin_fmaf(acc[b][t][r], at[t], -bt[t] * rs[r]);
+                    }
             }
         } else {
 #pragma unroll
@@ -198,8 +221,15 @@ __global__ __launch_bounds__(64 * WAVES, 4) void w4a16_decode(const uint16_t *__
 #undef AWQ4_COL
                 }
                 // the group scale, once per chunk, on the fp32 sums
+                float st[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) acc[b][t] *= scale_f32<DT>(s4[b], t);
+                for (int t = 0; t < 8; ++t) st[t] = scale_f32<DT>(s4[b], t);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (r < M) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) acc[b][t][r] *= st[t];
+                    }
             }
         }
     }
@@ -354,6 +384,8 @@ hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream
         case 412: return launch_decode_dt<1, 2, 4>(a, p, st);
         case 421: return launch_decode_dt<2, 1, 4>(a, p, st);
         case 422: return launch_decode_dt<2, 2, 4>(a, p, st);
+        case 414: return launch_decode_dt<1, 4, 4>(a, p, st);
+        case 424: return launch_decode_dt<2, 4, 4>(a, p, st);
         default: return hipErrorInvalidValue;
     }
 }

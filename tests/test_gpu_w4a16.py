@@ -127,6 +127,17 @@ def test_ragged_and_small_shapes(M, K, N, G):
         check_fp(yg, y64, "f16", f"ragged gemv {M}x{K}x{N} g{G}")
 
 
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("M", [1, 5])
+def test_gemv_one_group_per_wave(M, dtype, sym):
+    """A layer whose decode grid would not stay resident at 64-k chunks
+    (Llama-3-8B gate_up, N = 28672): each wave then covers one 128-k group."""
+    c = synthgen.w4a16_case(M, 4096, 28672, 128, dtype=dtype, sym=sym)
+    yg, y64, _ = _run(c, "gemv")
+    check_fp(yg, y64, dtype, f"gemv 128-k chunks M={M} {dtype} sym={sym}")
+
+
 @pytest.mark.parametrize("M,K,N,G,split", [(200, 1216, 256, 64, 0), (200, 1216, 256, 64, 3), (130, 1216, 384, 32, 0),
                                            (256, 1152, 4096, 128, 0), (513, 4096, 1032, 128, 0), (300, 640, 640, 64, 0)])
 def test_gemm_few_tiles(M, K, N, G, split):
