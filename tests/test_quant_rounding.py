@@ -1,0 +1,32 @@
+"""Host check (no GPU): the divide-free rounding of the W4A8 activation
+quantiser equals clamp(rint(x / s)) for every scale the quantiser can produce
+and every fp16 x it can meet, with the reciprocal off by up to one ulp
+(quant_rounding_check.c states the argument)."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CLANG = shutil.which("clang") or "/opt/rocm/llvm/bin/clang"
+SLICES = 8
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    if not os.path.exists(CLANG):
+        pytest.skip("no clang to build the host checker")
+    exe = str(tmp_path_factory.mktemp("qround") / "quant_rounding_check")
+    subprocess.run([CLANG, "-O2", "-o", exe, os.path.join(HERE, "quant_rounding_check.c"), "-lm"], check=True)
+    return exe
+
+
+def test_divide_free_rounding_exhaustive(checker):
+    procs = [subprocess.Popen([checker, str(i), str(SLICES), "1"], stdout=subprocess.PIPE, text=True)
+             for i in range(SLICES)]
+    outs = [(p.communicate()[0], p.returncode) for p in procs]
+    for out, rc in outs:
+        assert rc == 0, out
+    total = sum(int(o.split(":")[1].split()[0]) for o, _ in outs)
+    assert total > 2_000_000_000  # every reachable (s, x) pair, three reciprocals each
