@@ -67,7 +67,9 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
         p.splits = (int)std::min<int64_t>(p.splits, kMaxSplitK);
     }
-    if (M >= 128 && K % 64 == 0 && N % 32 == 0) {
+    // buffer-descriptor copies address X and the packed words with 32-bit offsets
+    const bool fits_rsrc = M * K * 2 < (int64_t(1) << 31) && K * (N / 2) < (int64_t(1) << 31);
+    if (M >= 128 && K % 64 == 0 && N % 32 == 0 && fits_rsrc) {
         // LDS-pipelined GEMM: 256 x 128 workgroup tiles, K in stages of 64
         p.kind = 3;
         p.tiles_n = (int)cdiv(N, 128);

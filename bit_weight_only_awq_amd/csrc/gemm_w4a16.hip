@@ -55,6 +55,16 @@ __device__ __forceinline__ void dma16(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
                                      (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
 }
+// The same copy through a buffer descriptor: address = base + voff (per lane,
+// loop-invariant) + soff (wave-uniform stage offset), so a copy costs no
+// vector arithmetic.  Offsets past num_records read as zero.
+constexpr int kBufDword3 = 0x00020000;  // raw 32-bit buffer, no format conversion
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, kBufDword3);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
 // Wait until every vector-memory load of this wave has landed (the direct
 // LDS copies included).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -100,6 +110,11 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     // the stored segment; word-columns past the end repeat the last 4.
     const char *const xg = (const char *)(x + (size_t)m0 * K);
     const char *const wg = (const char *)(qw + wc0);
+    // descriptors over the rest of X from row m0 and of the packed words from
+    // word-column wc0 (the planner keeps both under 2^31 bytes)
+    const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(xg, (int64_t)(M - m0) * K * 2);
+    const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(wg, (int64_t)K * nw * 4 - (int64_t)wc0 * 4);
+    const int lg = __builtin_ctz(G);  // G is 32, 64 or 128
     uint32_t xoff[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -126,16 +141,15 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     }
 
     auto copyA = [&](int st, int buf) {
-        const char *src = xg + (size_t)st * (GB_K * 2);
         unsigned char *dst = Abase + buf * GA_BYTES + 64 * wave * GA_PITCH;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dma16(src + xoff[i], dst + 8 * i * GA_PITCH);
+        for (int i = 0; i < 8; ++i) dma16_buf(xrs, xoff[i], (uint32_t)st * (GB_K * 2), dst + 8 * i * GA_PITCH);
     };
     auto copyB = [&](int st) {
         unsigned char *dst = Bbase + (st % GB_BUFS) * GB_BYTES;
-        dma16(wg + (size_t)st * GB_K * nw * 4 + woff, dst + 16 * wave * GB_PITCH);
+        dma16_buf(wrs, woff, (uint32_t)st * (GB_K * 4) * (uint32_t)nw, dst + 16 * wave * GB_PITCH);
         if (lane < meta_lanes) {
-            const int g = (st * GB_K + 32 * meta_ks) / G;
+            const int g = (st * GB_K + 32 * meta_ks) >> lg;
             const void *src = lane < 32 ? (const void *)(sc + (size_t)g * N + 8 * meta_col)
                                         : (const void *)(qz + (size_t)g * nw + meta_col);
             dma16(src, dst + GB_WORDS);
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
 
     // dequantisation constants of this lane's 4 columns for k-step (st, ks)
     auto load_consts = [&](int st, int ks) {
-        const int g = (st * GB_K + 32 * ks) / G;
+        const int g = (st * GB_K + 32 * ks) >> lg;
         if (g == gcur) return;
         gcur = g;
         const unsigned char *Mt = Bbase + (st % GB_BUFS) * GB_BYTES + GB_WORDS;

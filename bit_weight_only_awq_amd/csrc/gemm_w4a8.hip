@@ -14,7 +14,10 @@
 namespace awq4 {
 
 constexpr int W8_M = 128, W8_N = 128, W8_K = 64;
-constexpr int W8_RING = 4;                         // stages per LDS ring (copied three ahead)
+#ifndef AWQ4_W8_RING
+#define AWQ4_W8_RING 4
+#endif
+constexpr int W8_RING = AWQ4_W8_RING;              // stages per LDS ring (copied W8_RING - 1 ahead)
 constexpr int W8_APITCH = W8_K;                    // 64 bytes of a8 per row (4 segments, swizzled)
 constexpr int W8_ABYTES = W8_M * W8_APITCH;        // 8192 per stage
 constexpr int W8_WORDS = (W8_K / 8) * W8_N * 4;    // 8 word rows x 128 columns x 4 B = 4096
@@ -28,9 +31,12 @@ struct W8Layout {
     static constexpr int COPIES = 3 + (GROUP ? 1 : 0);      // copies per wave and stage
 };
 
-// a8 rows: 16-byte segment s of row r is stored at s ^ ((r >> 1) & 3), so the
-// 8 rows read by a lane octet fall on 8 distinct 16-byte bank groups.
-__device__ __forceinline__ int a8seg(int r, int s) { return s ^ ((r >> 1) & 3); }
+// a8 rows: 16-byte segment s of row r is stored at s ^ f(r), f(r) = ((r >> 1)
+// ^ (r >> 2)) & 3.  The 16 rows read by one operand load (a row per lane,
+// same segment) then fall on distinct 16-byte bank groups whether the LDS
+// serves 8 lanes over 32 banks or 16 lanes over 64 banks per cycle: rows
+// 2 apart (and rows 4 apart) always get different f.
+__device__ __forceinline__ int a8seg(int r, int s) { return s ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
 __device__ __forceinline__ void dma16_w8(const void *src, void *dst) {
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
@@ -144,8 +150,12 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
             o.a[mt] = *(const u32x4 *)(lds + slot * W8_ABYTES + a_off + mt * 16 * W8_APITCH);
-        const u32x4 w0 = *(const u32x4 *)(lds + slot * L::BBYTES + w_off);
-        const u32x4 w1 = *(const u32x4 *)(lds + slot * L::BBYTES + w_off + W8_N * 4);
+        // 16-byte aligned (the compiler cannot see it through the ring
+        // arithmetic and would split each quad into 4-byte pairs, which
+        // collide across lane groups)
+        const u32x4 *wq = (const u32x4 *)__builtin_assume_aligned(lds + slot * L::BBYTES + w_off, 16);
+        const u32x4 w0 = wq[0];
+        const u32x4 w1 = wq[W8_N / 4];
         uint32_t g3[4] = {16u, 16u, 16u, 16u};
         if (GROUP) {
             const u32x2 sv = *(const u32x2 *)(lds + slot * L::BBYTES + g_off);
@@ -162,14 +172,15 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     // stage is copied again into that slot, never read as data, so every
     // stage issues the same copies and the wait count is fixed.
     auto stage = [&](int st, Ops &cur, Ops &nxt) {
-        copy_stage(min(st + W8_RING - 1, s_hi - 1), (st - s_lo + W8_RING - 1) & (W8_RING - 1));
-        load_ops((st + 1 - s_lo) & (W8_RING - 1), nxt);
+        copy_stage(min(st + W8_RING - 1, s_hi - 1), (st - s_lo + W8_RING - 1) % W8_RING);
+        load_ops((st + 1 - s_lo) % W8_RING, nxt);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[mt][u] = mfma_i8(cur.a[mt], cur.b[u], acc[mt][u]);
-        if (L::COPIES == 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-        else __builtin_amdgcn_s_waitcnt(0x0F73);                 // vmcnt(3)
+        // copies still allowed in flight: those of stages st + 3 .. st + W8_RING - 1
+        constexpr int kInFlight = (W8_RING - 3) * L::COPIES;
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (kInFlight & 15) | ((kInFlight >> 4) << 14));
         // no memory fence (it would wait for every copy); the clobber keeps
         // LDS accesses from moving across the barrier
         asm volatile("s_barrier" ::: "memory");
