@@ -7,21 +7,20 @@
 // activation type, fp32 accumulation on the matrix cores.
 //
 // Workgroup tile 256 (M) x 128 (N), K in stages of 64 (two 32-k steps); 4
-// waves in a 2 x 2 grid, each owning 128 x 64 outputs: 8 row tiles x 4 column
-// MFMAs of 16x16x32 per k-step.  A wave's 64 columns are 8 packed
-// word-columns; lanes j and j+8 read the same words and take the low / high
-// nibble of each byte, so every dequantised B operand feeds 8 MFMAs (the
-// dequantisation is the VALU work that bounds this kernel).  Column of MFMA u
-// in lane j: 8 * word_column + {0,1,4,5}[u] + 2 * (j >> 3).
+// waves side by side along N, each owning 256 x 32 outputs: 16 row tiles x 2
+// column MFMAs of 16x16x32 per k-step.  A wave's 32 columns are 4 packed
+// word-columns; the 4 lanes that share a word-column each take two adjacent
+// columns of it, so every dequantised B operand feeds 16 MFMAs (about two
+// VALU instructions per MFMA in the main loop, which the issue port hides).
 //
 // Data movement: every stage's X rows and packed words (with the stage's
 // scales and zero points) are copied straight from global memory into LDS by
-// the direct-to-LDS loads, with no register staging.  X has two LDS buffers
-// and is copied one stage ahead; the packed words and metadata have three and
-// are copied two stages ahead, so the words of the next k-step are always
-// readable.  Each wave software-pipelines its k-steps: while the 32 MFMAs of
-// step q run, it dequantises the B operands of step q+1 and reads the X
-// operands two row tiles ahead.  One wait and one barrier end each stage.
+// direct-to-LDS buffer loads, with no register staging.  X has two LDS
+// buffers and is copied one stage ahead; the packed words and metadata have
+// three and are copied two stages ahead, so the words of the next k-step are
+// always readable.  Each wave software-pipelines its k-steps: while the 32
+// MFMAs of step q run, it dequantises the B operands of step q+1 and reads the
+// X operands six row tiles ahead.  One wait and one barrier end each stage.
 #include "device.hpp"
 #include "launch.hpp"
 #include "w4a16_ops.hpp"
@@ -37,14 +36,19 @@ constexpr int GM_SCALES = 2 * GB_N * 2;            // scales of both k-steps: 2 
 constexpr int GM_ZEROS = 2 * (GB_N / 8) * 4;       // zero words of both k-steps: 2 x 16 x 4 B
 constexpr int GB_BYTES = GB_WORDS + GM_SCALES + GM_ZEROS;  // 4736 per word/metadata buffer
 constexpr int GA_BUFS = 2, GB_BUFS = 3;
+#ifndef AWQ4_PREF_A
+#define AWQ4_PREF_A 6
+#endif
+constexpr int kPrefA = AWQ4_PREF_A;  // X operand reads run this many row tiles ahead of the MFMAs
 constexpr int G_LDS = GA_BUFS * GA_BYTES + GB_BUFS * GB_BYTES;  // 79744: two workgroups fit in 160 KB
 
 // X rows: 16-byte segment s of row r is stored at position s ^ (r & 7), so the
 // 8 rows read by a lane octet cover all banks.
 __device__ __forceinline__ int aseg(int r, int s) { return s ^ (r & 7); }
-// Packed words: segment s (4 words) of k-row r is stored at s ^ 2*((r>>3)&1),
-// so the two lane groups of a half-wave (rows 8 apart) use disjoint banks.
-__device__ __forceinline__ int bseg(int r, int s) { return s ^ (((r >> 3) & 1) << 1); }
+// Packed words: segment s (4 words) of k-row r is stored at s ^ ((r>>3)&3):
+// one word read serves rows 8 apart (lane groups gq = 0..3), which then sit
+// in four different 16-byte segments, i.e. on disjoint banks.
+__device__ __forceinline__ int bseg(int r, int s) { return s ^ ((r >> 3) & 3); }
 
 // Output columns of MFMA u relative to the lane's word-column (before + 2h).
 __host__ __device__ constexpr int gemm_col(int u) { return (u & 1) + ((u >> 1) << 2); }
@@ -70,9 +74,9 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t vof
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // KS = 2: the workgroup holds two groups of 4 waves that share the output
-// tile and split its K range (each with its own LDS ring); group 1 hands its
-// accumulators to group 0 through LDS at the end.  This doubles the waves per
-// SIMD for layers with no more tiles than CUs.
+// tile and split its K range (each with its own LDS ring); the groups trade
+// partial sums through LDS at the end.  This doubles the waves per SIMD for
+// layers with no more tiles than CUs.
 template <int DT, bool SYM, int KS>
 __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *__restrict__ x,
                                                                 const uint32_t *__restrict__ qw,
@@ -87,8 +91,7 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     unsigned char *const lds = lds_all + grp * G_LDS;
     unsigned char *const Abase = lds;
     unsigned char *const Bbase = lds + GA_BUFS * GA_BYTES;
-    const int j = lane & 15, gq = lane >> 4, h = j >> 3;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int j = lane & 15, gq = lane >> 4;
     const int nw = N >> 3;
     // logical tile of this workgroup (XCD-aware order over the tiles_n x tiles_m grid)
     const int tile = tile_of_xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
@@ -156,43 +159,53 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         }
     };
 
-    f32x4 acc[8][4];
+    f32x4 acc[16][2];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 16; ++mt)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[mt][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 2; ++u) acc[mt][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // per-lane nibble selection: low nibble (h = 0) or high nibble (h = 1)
-    const uint32_t nmask = h ? 0x00F000F0u : 0x000F000Fu;
-    const uint32_t mul2 = h ? 0x2C002C00u : 0x3C003C00u;  // fp16 (1/16, 1/16) or (1, 1)
-    const int wcl = wn * 8 + (j & 7);  // word-column within the workgroup tile
+    // Lane j takes columns 2*pi and 2*pi + 1 (pi = j % 4) of word-column
+    // 4 * wave + j / 4: the first comes from pair_x, the second from pair_y,
+    // both at nibble position pi (byte pi / 2 of each half, low or high
+    // nibble).  The byte shift is folded into the per-lane v_perm selectors
+    // (selector 0x0C gives a zero byte; the mask below drops that byte
+    // anyway).
+    const int c4 = j >> 2, pi = j & 3;
+    const int hi = pi & 1;
+    const uint32_t shift_sel = (pi & 2) ? 0x00010001u : 0u;
+    const uint32_t selx = 0x0C040C00u + shift_sel, sely = 0x0C060C02u + shift_sel;
+    const uint32_t nmask = hi ? 0x00F000F0u : 0x000F000Fu;
+    const uint32_t mul2 = hi ? 0x2C002C00u : 0x3C003C00u;  // fp16 (1/16, 1/16) or (1, 1)
+    const uint32_t zbase = hi ? 0xD400u : 0xE400u;         // -(64 + z) or -(1024 + z)
+    const int zsh = hi ? 4 : 0;
+    const int wcl = 4 * wave + c4;  // word-column within the workgroup tile
     const int wcol = wc0 + wcl;
     const bool col_ok = wcol < nw;
-    uint32_t zc[4], sc2[4];
-    float zf[4], sf[4];
+    uint32_t zc[2], sc2[2];
+    float zf[2], sf[2];
     int gcur = -1;
 
-    // dequantisation constants of this lane's 4 columns for k-step (st, ks)
+    // dequantisation constants of this lane's 2 columns for k-step (st, ks)
     auto load_consts = [&](int st, int ks) {
         const int g = (st * GB_K + 32 * ks) >> lg;
         if (g == gcur) return;
         gcur = g;
         const unsigned char *Mt = Bbase + (st % GB_BUFS) * GB_BYTES + GB_WORDS;
-        const uint32_t s_lo2 = *(const uint32_t *)(Mt + ks * (GB_N * 2) + wcl * 16 + 4 * h);
-        const uint32_t s_hi2 = *(const uint32_t *)(Mt + ks * (GB_N * 2) + wcl * 16 + 4 * h + 8);
+        const uint32_t s2 = *(const uint32_t *)(Mt + ks * (GB_N * 2) + wcl * 16 + 4 * pi);
         const uint32_t zw = SYM ? 0x88888888u : *(const uint32_t *)(Mt + GM_SCALES + ks * (GB_N / 2) + wcl * 4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = gemm_col(u) + 2 * h;  // this lane's column of MFMA u
-            const uint32_t z = (zw >> (4 * col_nibble(t))) & 0xFu;
-            const uint32_t sb = ((u >> 1) ? s_hi2 : s_lo2) >> (16 * (u & 1)) & 0xFFFFu;
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t z = (zw >> (4 * pi + 16 * u)) & 0xFu;  // nibble of column 2 pi + u
+            const uint32_t sb = (s2 >> (16 * u)) & 0xFFFFu;
             if (DT == DT_F16) {
-                zc[u] = h ? zconst_f16<1>(z) : zconst_f16<0>(z);
+                const uint32_t h = zbase | (z << zsh);
+                zc[u] = h | (h << 16);
                 sc2[u] = sb | (sb << 16);
             } else {
-                const float s = bf16_bits_to_f32(sb);
-                sf[u] = h ? s * 0.0625f : s;
-                zf[u] = (float)z * s;
+                const float sv = bf16_bits_to_f32(sb);
+                sf[u] = hi ? sv * 0.0625f : sv;
+                zf[u] = (float)z * sv;
             }
         }
     };
@@ -202,16 +215,15 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int r = 32 * ks + 8 * gq + e;
-            w[e] = *(const uint32_t *)(B + r * GB_PITCH + bseg(r, wcl >> 2) * 16 + (wcl & 3) * 4);
+            w[e] = *(const uint32_t *)(B + r * GB_PITCH + bseg(r, wave) * 16 + c4 * 4);
         }
     };
     // B operand of MFMA u (4 registers = 8 k of one column) from paired words
-    auto dequant = [&](const uint32_t (&px)[4], const uint32_t (&py)[4], int u) {
+    auto dequant = [&](const uint32_t (&pr)[4], int u) {
         u32x4 bop;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const uint32_t src = (u & 1) ? py[p] : px[p];
-            const uint32_t v = (u & 2) ? (src >> 8) : src;
+            const uint32_t v = pr[p];
             if (DT == DT_F16) {
                 // exact (q - z): lo nibble h16 - (1024+z); hi nibble h16/16 - (64+z)
                 const f16x2 q16 = bit_as<f16x2>((v & nmask) | 0x64006400u);
@@ -229,16 +241,16 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     auto pair_words = [&](const uint32_t (&w)[8], uint32_t (&px)[4], uint32_t (&py)[4]) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            px[p] = pair_x(w[2 * p], w[2 * p + 1]);
-            py[p] = pair_y(w[2 * p], w[2 * p + 1]);
+            px[p] = perm_b32(w[2 * p + 1], w[2 * p], selx);
+            py[p] = perm_b32(w[2 * p + 1], w[2 * p], sely);
         }
     };
     auto load_a = [&](const unsigned char *A, int ks, int mt) {
-        const int r = wm * 128 + 16 * mt + j;
+        const int r = 16 * mt + j;
         return *(const u32x4 *)(A + r * GA_PITCH + aseg(r, 4 * ks + gq) * 16);
     };
 
-    u32x4 bc[4];  // B operands of the current k-step
+    u32x4 bc[2];  // B operands of the current k-step
     if (s_lo < s_hi) {
         copyB(s_lo);
         copyA(s_lo, 0);
@@ -251,8 +263,8 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         load_words(s_lo, 0, w);
         load_consts(s_lo, 0);
         pair_words(w, px, py);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) bc[u] = dequant(px, py, u);
+        bc[0] = dequant(px, 0);
+        bc[1] = dequant(py, 1);
     }
     for (int st = s_lo; st < s_hi; ++st) {
         const int abuf = (st - s_lo) & 1;
@@ -260,9 +272,9 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         if (more) copyA(st + 1, abuf ^ 1);
         if (st + 2 < s_hi) copyB(st + 2);
         const unsigned char *A = Abase + abuf * GA_BYTES;
-        u32x4 a[8];
-        a[0] = load_a(A, 0, 0);
-        a[1] = load_a(A, 0, 1);
+        u32x4 a[16];
+#pragma unroll
+        for (int mt = 0; mt < kPrefA; ++mt) a[mt] = load_a(A, 0, mt);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             // the next k-step: (st, 1) or (st + 1, 0).  After the last stage
@@ -270,44 +282,42 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
             // which keeps the loop body free of branches.
             const int nst = st + ks, nks = ks ^ 1;
             uint32_t w[8], px[4], py[4];
-            u32x4 bn[4];
+            u32x4 bn[2];
             load_words(nst, nks, w);
             load_consts(nst, nks);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
+            for (int mt = 0; mt < 16; ++mt) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[mt][u] = mma<DT>(a[mt], bc[u], acc[mt][u]);
-                // X operands two row tiles ahead (within this stage only)
-                if (mt + 2 < 8) a[mt + 2] = load_a(A, ks, mt + 2);
-                else if (ks == 0) a[mt - 6] = load_a(A, 1, mt - 6);
-                if (mt == 0) pair_words(w, px, py);
-                if (mt & 1) bn[mt >> 1] = dequant(px, py, mt >> 1);
+                for (int u = 0; u < 2; ++u) acc[mt][u] = mma<DT>(a[mt], bc[u], acc[mt][u]);
+                // X operands kPrefA row tiles ahead (within this stage only)
+                if (mt + kPrefA < 16) a[mt + kPrefA] = load_a(A, ks, mt + kPrefA);
+                else if (ks == 0) a[mt + kPrefA - 16] = load_a(A, 1, mt + kPrefA - 16);
+                if (mt == 1) pair_words(w, px, py);
+                if (mt == 5) bn[0] = dequant(px, 0);
+                if (mt == 9) bn[1] = dequant(py, 1);
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) bc[u] = bn[u];
+            bc[0] = bn[0];
+            bc[1] = bn[1];
         }
         wait_vm_all();
         __syncthreads();
     }
 
-    // Epilogue: lane holds rows m0 + 128wm + 16mt + 4gq + r and, for MFMA u,
-    // column 8*wcol + {0,1,4,5}[u] + 2h (pairs u = 0,1 and u = 2,3 adjacent).
-    const int n0 = 8 * wcol + 2 * h;
+    // Epilogue: lane holds rows m0 + 16mt + 4gq + r and columns 8*wcol + 2pi
+    // (MFMA 0) and 8*wcol + 2pi + 1 (MFMA 1).
+    const int n0 = 8 * wcol + 2 * pi;
     auto emit = [&](int mt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm * 128 + 16 * mt + 4 * gq + r;
+            const int m = m0 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
             if (S == 1) {
-                uint16_t *dst = y + (size_t)m * N + n0;
-                *(uint32_t *)dst = (uint32_t)f32_to_out_bits(acc[mt][0][r], DT) |
-                                   ((uint32_t)f32_to_out_bits(acc[mt][1][r], DT) << 16);
-                *(uint32_t *)(dst + 4) = (uint32_t)f32_to_out_bits(acc[mt][2][r], DT) |
-                                         ((uint32_t)f32_to_out_bits(acc[mt][3][r], DT) << 16);
+                *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(acc[mt][0][r], DT) |
+                                                        ((uint32_t)f32_to_out_bits(acc[mt][1][r], DT) << 16);
             } else {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int n = n0 + gemm_col(u);
+                for (int u = 0; u < 2; ++u) {
+                    const int n = n0 + u;
                     int64_t sum;
                     if (splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(acc[mt][u][r]), S, &sum))
                         y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
@@ -318,43 +328,43 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     if (KS == 1) {
         if (!col_ok) return;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) emit(mt);
+        for (int mt = 0; mt < 16; ++mt) emit(mt);
         return;
     }
     // group 1's idle iteration (odd stage count): its barrier only
     for (int k = s_hi - s_lo; k < iters; ++k) __syncthreads();
     // Both groups hold partial sums of the whole tile.  Group 0 finishes row
-    // tiles 0..3 and group 1 row tiles 4..7: each parks the other half in
+    // tiles 0..7 and group 1 row tiles 8..15: each parks the other half in
     // LDS (both rings are free once the last barrier has passed) and adds
     // the half parked by the other group, always as group 0 + group 1.
     f32x4 *xfer = (f32x4 *)lds_all + (size_t)wave * 16 * 64 + lane;
     f32x4 *const mine = xfer + grp * 4 * 16 * 64, *const theirs = xfer + (grp ^ 1) * 4 * 16 * 64;
     if (grp == 0) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) mine[(mt * 4 + u) * 64] = acc[4 + mt][u];
+            for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[8 + mt][u];
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int u = 0; u < 4; ++u) mine[(mt * 4 + u) * 64] = acc[mt][u];
+            for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[mt][u];
     }
     __syncthreads();
     if (!col_ok) return;
     if (grp == 0) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc[mt][u] += theirs[(mt * 4 + u) * 64];
+            for (int u = 0; u < 2; ++u) acc[mt][u] += theirs[(mt * 2 + u) * 64];
             emit(mt);
         }
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc[4 + mt][u] = theirs[(mt * 4 + u) * 64] + acc[4 + mt][u];
-            emit(4 + mt);
+            for (int u = 0; u < 2; ++u) acc[8 + mt][u] = theirs[(mt * 2 + u) * 64] + acc[8 + mt][u];
+            emit(8 + mt);
         }
     }
 }

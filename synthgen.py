@@ -77,6 +77,13 @@ def activations(M: int, K: int, dtype: str = "f16", seed: int = 0) -> torch.Tens
     return torch.randn(M, K, generator=g, dtype=torch.float32).to(_DT[dtype])
 
 
+def activations_on(device, M: int, K: int, dtype: str = "f16", seed: int = 0) -> torch.Tensor:
+    """Standard-normal activations drawn directly on `device` (for inputs too
+    large to build on the host); the same seed gives the same tensor."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    return torch.randn(M, K, generator=g, dtype=torch.float32, device=device).to(_DT[dtype])
+
+
 @dataclass
 class W4A8Case:
     x: torch.Tensor        # [M, K] fp16 activations (quantised per token by the method)

@@ -138,6 +138,24 @@ def test_gemv_one_group_per_wave(M, dtype, sym):
     check_fp(yg, y64, dtype, f"gemv 128-k chunks M={M} {dtype} sym={sym}")
 
 
+@pytest.mark.parametrize("M", [65535, 65536])
+def test_gemm_activation_bytes_at_2_31(M):
+    """X of just under 2^31 bytes runs the LDS GEMM with copy offsets close to
+    2^31; at exactly 2^31 bytes the planner hands the call to the tiled kernel.
+    Checked on sampled rows, the last ones included."""
+    K, N, G = 16384, 32, 128
+    c = synthgen.w4a16_case(1, K, N, G)
+    x = synthgen.activations_on(dev(), M, K, seed=synthgen.seed_for(f"x-2^31|{M}"))
+    qw, s, qz = to_dev(c.qweight, c.scales, c.qzeros)
+    y = awq.gemm_w4a16(x, qw, s, qz, G)
+    torch.cuda.synchronize()
+    rows = torch.tensor(sorted(set(sample_rows(M, seed=3).tolist()) | {M - 1, M - 2, 0}))
+    xs = x[rows.to(x.device)].cpu()
+    del x
+    y64 = orc().w4a16(xs, c.qweight, c.scales, c.qzeros, G, F16, nthreads=THREADS)
+    check_fp(y.cpu()[rows], y64, "f16", f"gemm M={M} K={K} N={N}")
+
+
 @pytest.mark.parametrize("M,K,N,G,split", [(200, 1216, 256, 64, 0), (200, 1216, 256, 64, 3), (130, 1216, 384, 32, 0),
                                            (256, 1152, 4096, 128, 0), (513, 4096, 1032, 128, 0), (300, 640, 640, 64, 0)])
 def test_gemm_few_tiles(M, K, N, G, split):
