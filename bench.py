@@ -174,6 +174,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparator", action="store_true", help="skip the dense fp16 GEMM comparator")
     ap.add_argument("--profile", choices=["decode", "prefill", "w4a8", "targets"], default=None,
                     help="no timing: run one phase eagerly --profile-reps times (for rocprofv3 counter passes), "
                          "after a 256 MiB device copy of known size that calibrates the byte counters")
@@ -255,11 +256,12 @@ def main():
             awq.gemm_w4a16(x, qw, s, qz, G, out=y)
 
     def run_w4a8(r, which=None):
+        # the whole layer per call: per-token quantisation fused into the GEMM
+        # at M = 1, quantisation then GEMM otherwise (w4a8_linear)
         b, s2 = w8w[r]
         for i in (which if which is not None else range(len(w8a))):
             M, x, a8, s1, y = w8a[i]
-            awq.quant_act(x, a8, s1)
-            awq.w4a8_gemm(a8, b, s1, s2, out=y)
+            awq.linear_w4a8(x, b, s2, out=y, a8=a8, s1=s1)
 
     def run_target(t, M, kind, r=0):
         x, y = t["x"][M], t["y"][M]
@@ -268,8 +270,7 @@ def main():
             (awq.gemv_w4a16 if M <= 8 else awq.gemm_w4a16)(x, qw, sc, qz, G, out=y)
         else:
             b, s2 = t["w8"][r % len(t["w8"])]
-            awq.quant_act(x, t["a8"][M], t["s1"][M])
-            awq.w4a8_gemm(t["a8"][M], b, t["s1"][M], s2, out=y)
+            awq.linear_w4a8(x, b, s2, out=y, a8=t["a8"][M], s1=t["s1"][M])
 
     def run_targets():
         for t in tgt:
@@ -379,13 +380,31 @@ def main():
         t = per_launch(lambda li=li: run_prefill([li]), 1, reps=3)
         pre_layer[name] = {"K": K, "N": N, "us": round(t * 1e6, 2),
                            "TFLOPs": round(2 * M_PREFILL * N * K / t / 1e12, 1)}
+    # comparator, not a library path: the vendor dense fp16 GEMM (hipBLASLt via
+    # torch.matmul) on the same M=2048 shapes with weights already dequantised
+    # to fp16 (4x the weight memory; the dequantisation is left out)
+    dense = {}
+    if not args.no_comparator:
+        dshapes = [(name, K, N) for name, K, N in PREFILL_LAYERS] + \
+                  [(f"target {K}x{N}", K, N) for K, N in TARGET_SHAPES]
+        for name, K, N in dshapes:
+            xd = synthgen.activations(M_PREFILL, K, seed=synthgen.seed_for(f"bench|dense|x|{K}")).to(dev)
+            wd = (synthgen.activations(K, N, seed=synthgen.seed_for(f"bench|dense|w|{K}|{N}")) * 0.02).to(dev)
+            yd = torch.empty(M_PREFILL, N, dtype=torch.float16, device=dev)
+            torch.matmul(xd, wd, out=yd)
+            t = per_launch(lambda xd=xd, wd=wd, yd=yd: torch.matmul(xd, wd, out=yd), 1, reps=3)
+            dense[name] = {"K": K, "N": N, "us": round(t * 1e6, 2),
+                           "TFLOPs": round(2 * M_PREFILL * N * K / t / 1e12, 1)}
+            del xd, wd, yd
     w8_res = {}
     for i, (M, *_r) in enumerate(w8a):
         tq = per_launch(lambda i=i: [awq.quant_act(w8a[i][1], w8a[i][2], w8a[i][3]) for _ in range(4)], 4)
         tg = per_launch(lambda i=i: [awq.w4a8_gemm(w8a[i][2], w8w[r][0], w8a[i][3], w8w[r][1], out=w8a[i][4])
                                      for r in range(w8_copies)], w8_copies)
+        tl = per_launch(lambda i=i: [run_w4a8(r, [i]) for r in range(w8_copies)], w8_copies)
         ops = 2 * M * W4A8_N * W4A8_K
-        w8_res[f"M={M}"] = {"quant_us": round(tq * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
+        w8_res[f"M={M}"] = {"layer_us": round(tl * 1e6, 2), "fused_quant": M == 1,
+                            "quant_us": round(tq * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
                             "gemm_TOPs": round(ops / tg / 1e12, 2),
                             "gemm_weight_GBs": round((W4A8_K * W4A8_N // 2 + 2 * W4A8_N) / tg / 1e9, 1),
                             "frac_hbm": round(w4a8_alg_bytes(M, W4A8_K, W4A8_N) / tg / 1e9 / HBM_PEAK_GBS, 4),
@@ -449,7 +468,10 @@ def main():
                           "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "per_layer": pre_layer},
            "w4a8_n8192_k21760": w8_res,
-           "targets": {"note": "W4A8 times include the activation-quantisation launch", **targets},
+           "comparator_dense_fp16_m2048": {"note": "vendor dense fp16 GEMM (hipBLASLt via torch.matmul) on "
+                                                   "pre-dequantised weights; context, not a library path",
+                                           **dense},
+           "targets": {"note": "W4A8 times are whole-layer calls (w4a8_linear): activation quantisation included, fused into the GEMM at M=1", **targets},
            "phases_us": {"decode": round(t_dec * 1e6, 2), "prefill": round(t_pre * 1e6, 2),
                          "w4a8": round(t_w8 * 1e6, 2)}}
     if not args.no_cpu_baseline:

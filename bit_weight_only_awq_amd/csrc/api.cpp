@@ -89,6 +89,14 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
     return p;
 }
 
+// The fused-quantisation path of w4a8_linear: one activation row (measured:
+// the fused form saves the quantisation launch at M = 1 but is slower from
+// M = 4 on, where every workgroup re-reads and re-quantises several rows),
+// K <= 32768, and the int8 row of each wave's K range in LDS.
+bool w4a8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p) {
+    return p.kind == 0 && p.mt == 1 && M == 1 && K <= 32768 && w4a8_fused_lds_bytes(M, K, p.blk, p.splits) <= 64 * 1024;
+}
+
 W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
     (void)G;
     W4A8Plan p{};
@@ -298,6 +306,39 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
     }
     W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
     return hip_status(launch_w4a8(a, p, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packed, const void *s2_f16,
+                const void *s3_f16, void *y_f16, int32_t *acc_out, int64_t M, int64_t N, int64_t K, int group_size,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    if (!x_f16 || !a8 || !s1 || !b_packed || !s2_f16 || !y_f16) return AWQ_EINVAL;
+    if (M < 1 || N < 8 || K < 1 || M > kMaxDim || N > kMaxDim) return AWQ_EINVAL;
+    if (N % 8) return AWQ_EINVAL;
+    if (group_size == -1) {
+        if (s3_f16) return AWQ_EINVAL;
+    } else {
+        if (group_size != 32 && group_size != 64 && group_size != 128) return AWQ_EINVAL;
+        if (!s3_f16 || K % group_size) return AWQ_EINVAL;
+    }
+    if (K % 64 || K > 131072) return AWQ_EUNSUPPORTED;
+    if (!aligned16(x_f16) || !aligned16(a8) || !aligned16(s1) || !aligned16(b_packed) || !aligned16(s2_f16) ||
+        !aligned16(y_f16))
+        return AWQ_EALIGN;
+    if ((s3_f16 && !aligned16(s3_f16)) || (acc_out && !aligned16(acc_out))) return AWQ_EALIGN;
+    W4A8Plan p = plan_w4a8(M, N, K, group_size);
+    int rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
+    if (rc != AWQ_OK) return rc;
+    if (p.splits > 1) p.acc = static_cast<uint64_t *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
+    if (w4a8_fuses_quant(M, K, p)) {
+        a.x = x_f16;
+        a.s1_out = s1;
+        return hip_status(launch_w4a8_fused(a, p, st));
+    }
+    rc = hip_status(launch_w4a8_quant(x_f16, a8, s1, M, K, st));
+    if (rc != AWQ_OK) return rc;
+    return hip_status(launch_w4a8(a, p, st));
 }
 
 }  // extern "C"

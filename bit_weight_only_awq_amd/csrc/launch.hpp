@@ -38,7 +38,7 @@ struct W4A16Plan {
 };
 
 struct W4A8Args {
-    const int8_t *a8;
+    const int8_t *a8;  // int8 activations (unused by the fused kernel)
     const int32_t *b;
     const float *s1;
     const void *s2;
@@ -47,6 +47,9 @@ struct W4A8Args {
     int32_t *acc_out;  // may be nullptr
     int64_t M, N, K;
     int G;  // -1 = per-channel
+    // fused quantisation (w4a8_linear): fp16 activations and the s1 output
+    const void *x = nullptr;
+    float *s1_out = nullptr;
 };
 
 struct W4A8Plan {
@@ -64,6 +67,7 @@ constexpr int kMaxSplitK = 255;
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry);
 W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);
+bool w4a8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p);
 
 hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
@@ -71,6 +75,10 @@ hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
+// skinny W4A8 GEMM with the per-token quantisation fused in (plan kind 0,
+// mt 1); its dynamic LDS and per-wave int8 row area
+hipError_t launch_w4a8_fused(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
+size_t w4a8_fused_lds_bytes(int64_t M, int64_t K, int blk, int splits);
 // read-only bandwidth probe: at most kStreamMaxBlocks workgroups, one sink
 // word per wave
 constexpr int64_t kStreamMaxBlocks = 2048;

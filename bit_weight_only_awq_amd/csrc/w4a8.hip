@@ -201,6 +201,15 @@ __device__ __forceinline__ uint32_t s3_int(const uint16_t *__restrict__ s3, size
 
 // Final value of one output: undo the x16 of per-channel weights, scale, store.
 template <bool GROUP>
+__device__ __forceinline__ void w4a8_store_s(int32_t acc, int m, int n, int N, float s1m,
+                                             const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
+                                             int32_t *__restrict__ acc_out) {
+    const int32_t a = GROUP ? acc : (acc >> 4);  // exact: per-channel acc is a multiple of 16
+    const float v = (float)a * s1m * f16_bits_to_f32(s2[n]);
+    y[(size_t)m * N + n] = bit_as<uint16_t>((f16)v);
+    if (acc_out) acc_out[(size_t)m * N + n] = a;
+}
+template <bool GROUP>
 __device__ __forceinline__ void w4a8_store(int32_t acc, int m, int n, int N, const float *__restrict__ s1,
                                            const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
                                            int32_t *__restrict__ acc_out) {
@@ -214,12 +223,26 @@ __device__ __forceinline__ void w4a8_store(int32_t acc, int m, int n, int N, con
 // Skinny W4A8 kernel: M <= 16*MT; 4 waves split the K slice of a 64*BLK
 // column tile; LDS reduce (int32, exact); split-K over grid y through exact
 // counting atomics (device.hpp).
-template <int BLK, int MT, bool GROUP>
-__global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
-                                                   const float *__restrict__ s1, const uint16_t *__restrict__ s2,
+//
+// FUSED (M <= 16, the activation rows small enough to read whole per
+// workgroup): the kernel takes the fp16 activations x instead of a8 and does
+// the per-token quantisation itself, with exactly the arithmetic of
+// w4a8_quant_rows.  Every workgroup reduces the abs-max of all M rows (an LDS
+// max over its 256 threads), derives s1, and each wave quantises the rows'
+// values of its own K range cooperatively (one 8-value chunk per lane at a
+// time) into LDS, from where its main loop reads the int8 operands.  The
+// int8 activations never go through HBM and the separate launch disappears.
+// Workgroup (0, 0) writes s1.  Dynamic LDS: the reduction area, then 32 row
+// maxima and 32 scales, then per wave `qa_stride` bytes of int8 rows laid out
+// [step][row][64].
+template <int BLK, int MT, bool GROUP, bool FUSED>
+__global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8, const uint16_t *__restrict__ x16,
+                                                   const uint32_t *__restrict__ bq,
+                                                   const float *__restrict__ s1, float *__restrict__ s1_out,
+                                                   const uint16_t *__restrict__ s2,
                                                    const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                    int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
-                                                   int M, int N, int K, int G, int S) {
+                                                   int M, int N, int K, int G, int S, int qa_stride) {
     extern __shared__ int32_t ired[];
     constexpr int COLS = 64 * BLK;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -228,12 +251,71 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
     const int T = K >> 6;  // 64-k steps
     const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
     const int w_lo = s_lo + (s_hi - s_lo) * wave / 4, w_hi = s_lo + (s_hi - s_lo) * (wave + 1) / 4;
+    uint32_t *const rmax = (uint32_t *)(ired + 4 * M * COLS);
+    float *const srow = (float *)(rmax + 32);
+    unsigned char *const qa = (unsigned char *)(srow + 32) + (size_t)wave * qa_stride;
     int ncol[BLK];
     bool ok[BLK];
 #pragma unroll
     for (int b = 0; b < BLK; ++b) {
         ncol[b] = tile * COLS + 64 * b + 4 * j;
         ok[b] = ncol[b] < N;  // N % 8 == 0 and the 4 columns start at a multiple of 4
+    }
+    // words of 64-k step st for this lane's 4 columns of each set (zero past N)
+    auto load_w = [&](int st, u32x4 (&w0)[BLK], u32x4 (&w1)[BLK]) {
+        const int kb = (st * 64 + 16 * gq) >> 3;
+#pragma unroll
+        for (int b = 0; b < BLK; ++b) {
+            if (ok[b]) {
+                w0[b] = __builtin_nontemporal_load((const u32x4 *)(bq + (size_t)kb * N + ncol[b]));
+                w1[b] = __builtin_nontemporal_load((const u32x4 *)(bq + (size_t)(kb + 1) * N + ncol[b]));
+            } else {
+                w0[b] = (u32x4){0, 0, 0, 0};
+                w1[b] = (u32x4){0, 0, 0, 0};
+            }
+        }
+    };
+    if (FUSED) {
+        if (threadIdx.x < 32) rmax[threadIdx.x] = 0;
+        __syncthreads();
+        // |x| as an integer: for finite fp16 the magnitude order equals the
+        // order of the low 15 bits
+        const int K8 = K >> 3;
+        for (int m = 0; m < M; ++m) {
+            uint32_t mx = 0;
+            for (int c = threadIdx.x; c < K8; c += 256) {
+                const u32x4 v = *(const u32x4 *)(x16 + (size_t)m * K + 8 * c);
+#pragma unroll
+                for (int p = 0; p < 4; ++p) mx = max(mx, max(v[p] & 0x7FFFu, (v[p] >> 16) & 0x7FFFu));
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+            if (lane == 0) atomicMax(&rmax[m], mx);
+        }
+        __syncthreads();
+        if (threadIdx.x < M) {
+            const float amax = f16_bits_to_f32(rmax[threadIdx.x]);
+            const float q32 = amax / 127.0f;  // correctly rounded fp32 divide
+            const float sv = (float)(f16)q32;  // to fp16 (nearest even) and back
+            srow[threadIdx.x] = sv;
+            if (tile == 0 && split == 0) s1_out[threadIdx.x] = sv;
+        }
+        __syncthreads();
+        // this wave's K range, row by row, 8 values per lane and chunk
+        const int nst = w_hi - w_lo, per_row = nst * 8;
+        for (int c = lane; c < M * per_row; c += 64) {
+            const int m = c / per_row, cc = c - m * per_row;
+            const u32x4 v = *(const u32x4 *)(x16 + (size_t)m * K + 64 * w_lo + 8 * cc);
+            const float sv = srow[m];
+            u32x2 o = {0, 0};
+            if (sv != 0.0f) {
+                const float r = __builtin_amdgcn_rcpf(sv), hs = 0.5f * sv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    o[e >> 2] |= quant_one((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, sv, r, hs) << (8 * (e & 3));
+            }
+            *(u32x2 *)(qa + ((size_t)(cc >> 3) * M + m) * 64 + (cc & 7) * 8) = o;
+        }
     }
     i32x4 acc[MT][BLK][4];
 #pragma unroll
@@ -245,23 +327,15 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
 
     for (int st = w_lo; st < w_hi; ++st) {
         const int k0 = st * 64 + 16 * gq;  // this lane group's 16 k
-        const int kb = k0 >> 3;
         u32x4 w0[BLK], w1[BLK];
-#pragma unroll
-        for (int b = 0; b < BLK; ++b) {
-            if (ok[b]) {
-                w0[b] = __builtin_nontemporal_load((const u32x4 *)(bq + (size_t)kb * N + ncol[b]));
-                w1[b] = __builtin_nontemporal_load((const u32x4 *)(bq + (size_t)(kb + 1) * N + ncol[b]));
-            } else {
-                w0[b] = (u32x4){0, 0, 0, 0};
-                w1[b] = (u32x4){0, 0, 0, 0};
-            }
-        }
+        load_w(st, w0, w1);
         u32x4 a[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = 16 * mt + j;
-            a[mt] = (m < M) ? *(const u32x4 *)(a8 + (size_t)m * K + k0) : (u32x4){0, 0, 0, 0};
+            if (m >= M) a[mt] = (u32x4){0, 0, 0, 0};
+            else if (FUSED) a[mt] = *(const u32x4 *)(qa + ((size_t)(st - w_lo) * M + m) * 64 + 16 * gq);
+            else a[mt] = *(const u32x4 *)(a8 + (size_t)m * K + k0);
         }
 #pragma unroll
         for (int b = 0; b < BLK; ++b) {
@@ -302,10 +376,11 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
         const int n = n_base + c;
         if (n >= N) continue;
         int64_t sum;
+        const float s1m = FUSED ? srow[m] : s1[m];
         if (S == 1)
-            w4a8_store<GROUP>(v, m, n, N, s1, s2, y, acc_out);
+            w4a8_store_s<GROUP>(v, m, n, N, s1m, s2, y, acc_out);
         else if (splitk_contribute(&acc64[(size_t)m * N + n], v, S, &sum))
-            w4a8_store<GROUP>((int32_t)sum, m, n, N, s1, s2, y, acc_out);
+            w4a8_store_s<GROUP>((int32_t)sum, m, n, N, s1m, s2, y, acc_out);
     }
 }
 
@@ -400,13 +475,26 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
 }
 
 // ---------------------------------------------------------------------------
-template <int BLK, int MT, bool GROUP>
+// int8 rows of one wave's K range in the fused skinny kernel: at most
+// ceil(ceil(T / S) / 4) steps of M rows x 64 bytes
+int64_t w4a8_fused_qa_stride(int64_t M, int64_t K, int splits) {
+    const int64_t T = K / 64, per_wg = (T + splits - 1) / splits;
+    return ((per_wg + 3) / 4) * M * 64;
+}
+size_t w4a8_fused_lds_bytes(int64_t M, int64_t K, int blk, int splits) {
+    return (size_t)4 * M * 64 * blk * sizeof(int32_t) + 64 * sizeof(uint32_t) +
+           4 * (size_t)w4a8_fused_qa_stride(M, K, splits);
+}
+
+template <int BLK, int MT, bool GROUP, bool FUSED>
 static hipError_t launch_skinny8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    size_t lds = (size_t)4 * a.M * 64 * BLK * sizeof(int32_t);
-    hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
-                       (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
-                       (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G,
-                       p.splits);
+    const int qa_stride = FUSED ? (int)w4a8_fused_qa_stride(a.M, a.K, p.splits) : 0;
+    const size_t lds = FUSED ? w4a8_fused_lds_bytes(a.M, a.K, BLK, p.splits)
+                             : (size_t)4 * a.M * 64 * BLK * sizeof(int32_t) + 64 * sizeof(uint32_t);
+    hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP, FUSED>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
+                       (const uint16_t *)a.x, (const uint32_t *)a.b, a.s1, a.s1_out, (const uint16_t *)a.s2,
+                       (const uint16_t *)a.s3, (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K,
+                       a.G, p.splits, qa_stride);
     return hipGetLastError();
 }
 
@@ -424,9 +512,9 @@ hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     const bool grp = a.s3 != nullptr;
     if (p.kind == 0) {
         switch (p.blk * 10 + p.mt) {
-            case 11: return grp ? launch_skinny8<1, 1, true>(a, p, st) : launch_skinny8<1, 1, false>(a, p, st);
-            case 21: return grp ? launch_skinny8<2, 1, true>(a, p, st) : launch_skinny8<2, 1, false>(a, p, st);
-            case 12: return grp ? launch_skinny8<1, 2, true>(a, p, st) : launch_skinny8<1, 2, false>(a, p, st);
+            case 11: return grp ? launch_skinny8<1, 1, true, false>(a, p, st) : launch_skinny8<1, 1, false, false>(a, p, st);
+            case 21: return grp ? launch_skinny8<2, 1, true, false>(a, p, st) : launch_skinny8<2, 1, false, false>(a, p, st);
+            case 12: return grp ? launch_skinny8<1, 2, true, false>(a, p, st) : launch_skinny8<1, 2, false, false>(a, p, st);
             default: return hipErrorInvalidValue;
         }
     }
@@ -436,6 +524,13 @@ hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
         case 4: return grp ? launch_tiled8<4, true>(a, p, st) : launch_tiled8<4, false>(a, p, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_w4a8_fused(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    const bool grp = a.s3 != nullptr;
+    if (p.kind != 0 || p.mt != 1) return hipErrorInvalidValue;
+    if (p.blk == 2) return grp ? launch_skinny8<2, 1, true, true>(a, p, st) : launch_skinny8<2, 1, false, true>(a, p, st);
+    return grp ? launch_skinny8<1, 1, true, true>(a, p, st) : launch_skinny8<1, 1, false, true>(a, p, st);
 }
 
 }  // namespace awq4

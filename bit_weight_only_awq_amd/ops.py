@@ -163,10 +163,28 @@ def w4a8_gemm(a8, b, s1, s2, s3=None, group_size: int = -1, want_acc: bool = Fal
     return (out, acc) if want_acc else out
 
 
-def linear_w4a8(x, b, s2, s3=None, group_size: int = -1):
-    """Quantise the activations per token, then the W4A8 GEMM."""
-    a8, s1 = quant_act(x)
-    return w4a8_gemm(a8, b, s1, s2, s3, group_size)
+def linear_w4a8(x, b, s2, s3=None, group_size: int = -1, want_acc: bool = False, out=None, a8=None, s1=None):
+    """The whole W4A8 layer in one call (w4a8_linear): per-token quantisation of
+    x, then the W4A8 GEMM, fused into one kernel for small batches.  Returns y,
+    or (y, s1, acc) with want_acc.  `a8` is scratch for the two-step path."""
+    _need_cuda(x, b, s2, s3, out, a8, s1)
+    if x.dtype != torch.float16:
+        raise ValueError("W4A8 activations must be fp16")
+    M, K = x.shape
+    N = b.shape[1]
+    if a8 is None:
+        a8 = torch.empty(M, K, dtype=torch.int8, device=x.device)
+    if s1 is None:
+        s1 = torch.empty(M, dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.float16, device=x.device)
+    acc = torch.empty(M, N, dtype=torch.int32, device=x.device) if want_acc else None
+    need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size)
+    ws = WORKSPACE.get(x.device, need)
+    L.check("w4a8_linear", L.lib().w4a8_linear(_ptr(x), _ptr(a8), _ptr(s1), _ptr(b), _ptr(s2), _ptr(s3), _ptr(out),
+                                               _ptr(acc), M, N, K, group_size, _ptr(ws),
+                                               0 if ws is None else ws.numel(), _stream(x.device)))
+    return (out, s1, acc) if want_acc else out
 
 
 # ----------------------------------------------------------------------------- measurement helper

@@ -189,6 +189,26 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
               int64_t K, int group_size, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * w4a8_linear -- the whole W4A8 layer in one call: w4a8_quant_act of x
+ * followed by w4a8_gemm, with identical results (y, s1 and acc_out bit for
+ * bit).  The pages note that quantising activations in a separate kernel
+ * costs performance ([P5]); for a single token (M == 1, K <= 32768) the
+ * quantisation runs inside the GEMM kernel: every workgroup reads the
+ * activation row, derives s1 and quantises its own K range into LDS, so the
+ * int8 activations never travel through device memory and there is one
+ * launch.  Otherwise the two steps run back to back.
+ *   x:   device fp16 [M, K].
+ *   a8:  device int8 [M, K], scratch: holds the quantised activations when
+ *        the two-step path runs, left untouched by the fused path.
+ *   s1:  device fp32 [M], written (the per-token scales).
+ *   other arguments, layouts, workspace and errors: as w4a8_gemm.
+ */
+int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packed,
+                const void *s2_f16, const void *s3_f16, void *y_f16, int32_t *acc_out,
+                int64_t M, int64_t N, int64_t K, int group_size, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/*
  * awq_stream_read -- measurement helper, not a step of the method: reads
  * `bytes` bytes at `src` once (16-byte loads spread over up to 2048
  * workgroups) and writes an XOR checksum per wave to `sink`, so that the

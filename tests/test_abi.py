@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_hot_path_calls():
     names = declared_functions()
     for n in ("awq_pack", "awq_unpack", "awq_gemm_w4a16", "awq_gemv_w4a16", "w4a8_quant_act", "w4a8_gemm",
-              "awq_workspace_bytes", "awq_status_str", "awq_version"):
+              "w4a8_linear", "awq_workspace_bytes", "awq_status_str", "awq_version"):
         assert n in names, n
 
 
@@ -118,6 +118,25 @@ def test_w4a8_validation():
     assert lib.w4a8_quant_act(None, A, A, 1, 16, None) == L.AWQ_EINVAL
     assert lib.w4a8_quant_act(A, A, A, 0, 16, None) == L.AWQ_EINVAL
     assert lib.w4a8_quant_act(MIS, A, A, 1, 16, None) == L.AWQ_EALIGN
+
+
+def test_w4a8_linear_validation():
+    lib = L.lib()
+
+    def f(x=A, a8=A, s1=A, b=A, s2=A, s3=None, y=A, acc=None, M=1, N=8192, K=21760, G=-1, ws=None, wsb=0):
+        return lib.w4a8_linear(x, a8, s1, b, s2, s3, y, acc, M, N, K, G, ws, wsb, None)
+
+    assert f(x=None) == L.AWQ_EINVAL
+    assert f(a8=None) == L.AWQ_EINVAL          # scratch for the two-step path is required
+    assert f(s1=None) == L.AWQ_EINVAL
+    assert f(M=0) == L.AWQ_EINVAL
+    assert f(N=12) == L.AWQ_EINVAL
+    assert f(G=128) == L.AWQ_EINVAL            # grouped without s3
+    assert f(s3=A, G=48) == L.AWQ_EINVAL
+    assert f(K=21700) == L.AWQ_EUNSUPPORTED    # K % 64
+    assert f(x=MIS) == L.AWQ_EALIGN
+    assert f(s1=MIS) == L.AWQ_EALIGN
+    assert f() == L.AWQ_EWORKSPACE             # the decode split needs a workspace
 
 
 def test_pack_validation():

@@ -117,3 +117,55 @@ def test_w4a8_deterministic():
     torch.cuda.synchronize()
     for yy in ys[1:]:
         assert torch.equal(yy, ys[0])
+
+
+@pytest.mark.parametrize("G", [-1, 128])
+@pytest.mark.parametrize("M,K,N", [(1, 21760, 8192), (1, 4096, 4096), (1, 4096, 14336), (2, 16384, 4096),
+                                   (3, 4096, 1032), (5, 64, 8), (16, 2048, 512), (16, 2112, 512),
+                                   (2, 21760, 8192), (17, 128, 136), (300, 4096, 1032)])
+def test_linear_matches_quant_then_gemm(M, K, N, G):
+    """w4a8_linear (quantisation fused into the GEMM for M <= 16 and M*K <=
+    32768, the two launches otherwise) gives y, s1 and the int32 accumulators
+    bit for bit as w4a8_quant_act followed by w4a8_gemm; rows span magnitudes
+    (a zero row and exact ties included) so every rounding case is met."""
+    if G > 0 and K % G:
+        pytest.skip("K not a multiple of G")
+    c = synthgen.w4a8_case(M, K, N, G)
+    xc = c.x.clone()
+    xc = xc * torch.logspace(-3, 2, M).to(torch.float16)[:, None]
+    if M >= 3:
+        xc[1] = 0
+        xc[2, : K // 2] = torch.arange(K // 2, dtype=torch.float32).remainder(255).sub(127).div(2).to(torch.float16)
+        xc[2, 0] = 127
+    x, b, s2, s3 = to_dev(xc.to(torch.float16), c.b, c.s2, c.s3)
+    a8, s1 = awq.quant_act(x)
+    y1, acc1 = awq.w4a8_gemm(a8, b, s1, s2, s3, G, want_acc=True)
+    y2, s1b, acc2 = awq.linear_w4a8(x, b, s2, s3, G, want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1b.view(torch.int32), s1.view(torch.int32))
+    assert torch.equal(acc2, acc1)
+    assert torch.equal(y2.view(torch.int16), y1.view(torch.int16))
+    # and against the oracle, from the oracle's own quantisation of x
+    ea8, es1 = orc().quant_act(xc.to(torch.float16))
+    rows = np.arange(M) if M <= 16 else sample_rows(M, seed=M)
+    eacc, y64 = orc().w4a8(ea8[rows], c.b, es1[rows], c.s2, c.s3, G, nthreads=THREADS)
+    assert np.array_equal(acc2.cpu().numpy()[rows].astype(np.int64), eacc)
+    # the rows span five decades, so outputs reach the hundreds: y is one fp16
+    # rounding of acc * s1 * s2 (fp32), i.e. within half an fp16 ulp of the
+    # fp64 value (plus the fp32 product's own rounding)
+    yg = y2.cpu()[torch.as_tensor(rows)].double().numpy()
+    assert np.all(np.abs(yg - y64) <= 2.0 ** -11 * np.abs(y64) * (1 + 2.0 ** -20) + 2.0 ** -25), \
+        f"w4a8_linear M={M} K={K} N={N} G={G}: y beyond one fp16 rounding of the exact value"
+
+
+def test_linear_repeated_calls_and_split_workspace():
+    """Back-to-back fused calls of different shapes share the split-K workspace
+    and leave it re-armed; results stay identical to the two-step path."""
+    for (M, K, N) in [(1, 21760, 8192), (1, 4096, 4096), (4, 8192, 14336), (1, 21760, 8192)]:
+        c = synthgen.w4a8_case(M, K, N, -1)
+        x, b, s2 = to_dev(c.x, c.b, c.s2)
+        a8, s1 = awq.quant_act(x)
+        y1 = awq.w4a8_gemm(a8, b, s1, s2)
+        y2 = awq.linear_w4a8(x, b, s2)
+        torch.cuda.synchronize()
+        assert torch.equal(y2.view(torch.int16), y1.view(torch.int16)), (M, K, N)
