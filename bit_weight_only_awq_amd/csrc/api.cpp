@@ -59,9 +59,12 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         int64_t s = 1;
         if (tiles < 256) {
+            // at most 4 K splits: each adds an M x N partial tile to write,
+            // read and clear, which costs more than it saves beyond that
+            // (measured on the Llama-3-8B layers at M = 64)
             s = cdiv(kTargetWorkgroups, tiles);
             s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
-            s = std::min<int64_t>(s, 16);
+            s = std::min<int64_t>(s, 4);
         }
         p.splits = (int)std::max<int64_t>(1, s);
         if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
@@ -76,16 +79,22 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.tiles_m = (int)cdiv(M, 256);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         const int64_t stages = K / 64;
-        int64_t s = 1;
-        if (tiles < 128) s = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, stages / 4));
+        // K splits only for few tiles (measured at M = 128..1024 on the
+        // Llama-3-8B layers: the partial tiles cost more than a third split
+        // saves); the in-workgroup K split below adds parallelism for free
+        int64_t s = tiles <= 32 ? 4 : tiles <= 64 ? 2 : 1;
+        s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 4));
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
         // no more workgroups than CUs: two wave groups per workgroup split K
         // inside it (twice the waves per SIMD, no extra atomics)
         p.ksplit = tiles * p.splits <= 256 && stages / p.splits >= 4 ? 2 : 1;
     }
-    (void)tiles;
-    p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;
+    if (p.splits > 1)
+        p.workspace_bytes = p.kind == 0 ? (size_t)M * N * sizeof(uint64_t)
+                                        : (size_t)split_tiles_bytes((int64_t)p.tiles_n * p.tiles_m, p.splits, M, N);
+    else
+        p.workspace_bytes = 0;
     return p;
 }
 
@@ -123,7 +132,7 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         if (tiles < 256) {
             s = cdiv(kTargetWorkgroups, tiles);
             s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
-            s = std::min<int64_t>(s, 16);
+            s = std::min<int64_t>(s, 4);  // partial tiles: see the W4A16 tiled kernel
         }
         p.splits = (int)std::max<int64_t>(1, s);
     }
@@ -140,7 +149,16 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
     }
     (void)tiles;
-    p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;
+    // the small-M kernel (M <= 32) keeps one counting atomic per output
+    // element: a single round trip at the end, measured faster there than
+    // partial tiles up to M = 32; the larger kernels reduce by partial tiles
+    p.tilered = p.kind != 0;
+    if (p.splits <= 1)
+        p.workspace_bytes = 0;
+    else if (!p.tilered)
+        p.workspace_bytes = (size_t)M * N * sizeof(uint64_t);
+    else
+        p.workspace_bytes = (size_t)split_tiles_bytes((int64_t)p.tiles_n * p.tiles_m, p.splits, M, N);
     return p;
 }
 

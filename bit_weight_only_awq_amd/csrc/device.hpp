@@ -24,6 +24,7 @@ typedef _Float16 f16;
 typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -190,6 +191,40 @@ __device__ __forceinline__ bool splitk_contribute(uint64_t *acc, int64_t value, 
     *total = (int64_t)(now & kValueMask) - (int64_t)S * kBias;
     __hip_atomic_store(acc, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K by partial tiles, for the GEMM kernels: their outputs have far too
+// many elements for one device-scope atomic each.  Workspace layout: one
+// uint32 arrival counter per output tile (rounded up to 256 bytes), then fp32
+// partials [S][M][N]; all zero between calls.
+//
+// Per workgroup: every thread stores its partial elements of the tile into
+// slot `split`; split_tile_last() then (after a barrier, which waits for
+// every store of the workgroup) releases them at device scope and counts the
+// tile's arrival with one atomic.  The workgroup that completes the count
+// acquires and returns true: it sums, for each of its elements, the S
+// partials in split order (so the result does not depend on which split
+// arrives last), writes the output and zeroes every partial of the tile; the
+// counter is re-armed at once.  Only this one atomic per workgroup and two
+// fences are needed, against one atomic per output element and split.
+// (The workspace sizes, split_counters_bytes / split_tiles_bytes, are in
+// launch.hpp, shared with the host-side planner.)
+
+__device__ __forceinline__ bool split_tile_last(uint32_t *cnt, int S) {
+    __shared__ uint32_t last_flag;
+    __syncthreads();  // every partial store of the workgroup has completed
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t last = old == (uint32_t)(S - 1) ? 1u : 0u;
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = last;
+    }
+    __syncthreads();
+    const bool last = last_flag != 0;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return last;
 }
 
 }  // namespace awq4

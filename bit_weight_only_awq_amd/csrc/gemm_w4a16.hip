@@ -304,31 +304,49 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     }
 
     // Epilogue: lane holds rows m0 + 16mt + 4gq + r and columns 8*wcol + 2pi
-    // (MFMA 0) and 8*wcol + 2pi + 1 (MFMA 1).
+    // (MFMA 0) and 8*wcol + 2pi + 1 (MFMA 1).  Without a K split it writes the
+    // output; with one, each split stores its partial tile and the tile's last
+    // split sums them in split order (device.hpp).
     const int n0 = 8 * wcol + 2 * pi;
+    uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
+    float *const part = (float *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N;
     auto emit = [&](int mt) {
+        if (!col_ok) return;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
-            if (S == 1) {
+            if (S == 1)
                 *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(acc[mt][0][r], DT) |
                                                         ((uint32_t)f32_to_out_bits(acc[mt][1][r], DT) << 16);
-            } else {
+            else
+                *(f32x2 *)(part + split * slot + (size_t)m * N + n0) = (f32x2){acc[mt][0][r], acc[mt][1][r]};
+        }
+    };
+    auto finish = [&](int mt) {
+        if (!col_ok) return;
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int n = n0 + u;
-                    int64_t sum;
-                    if (splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(acc[mt][u][r]), S, &sum))
-                        y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
-                }
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 16 * mt + 4 * gq + r;
+            if (m >= M) continue;
+            f32x2 v = {0.f, 0.f};
+            for (int s = 0; s < S; ++s) {
+                f32x2 *src = (f32x2 *)(part + s * slot + (size_t)m * N + n0);
+                v += *src;
+                *src = (f32x2){0.f, 0.f};
             }
+            *(uint32_t *)(y + (size_t)m * N + n0) =
+                (uint32_t)f32_to_out_bits(v[0], DT) | ((uint32_t)f32_to_out_bits(v[1], DT) << 16);
         }
     };
     if (KS == 1) {
-        if (!col_ok) return;
 #pragma unroll
         for (int mt = 0; mt < 16; ++mt) emit(mt);
+        if (S > 1 && split_tile_last(cnt, S)) {
+#pragma unroll
+            for (int mt = 0; mt < 16; ++mt) finish(mt);
+        }
         return;
     }
     // group 1's idle iteration (odd stage count): its barrier only
@@ -351,7 +369,6 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
             for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[mt][u];
     }
     __syncthreads();
-    if (!col_ok) return;
     if (grp == 0) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
@@ -365,6 +382,15 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
 #pragma unroll
             for (int u = 0; u < 2; ++u) acc[8 + mt][u] = theirs[(mt * 2 + u) * 64] + acc[8 + mt][u];
             emit(8 + mt);
+        }
+    }
+    if (S > 1 && split_tile_last(cnt, S)) {
+        if (grp == 0) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) finish(mt);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) finish(8 + mt);
         }
     }
 }

@@ -206,39 +206,66 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     // n0 + cl + u (u = 0..3, adjacent).  Per-channel accumulators carry the
     // x16 of the upper-nibble int8 and are divided exactly.
     const int nc = n0 + cl;
-    if (nc >= N) return;
-    float s2f[4];
+    const bool col_ok = nc < N;
+    float s2f[4] = {0.f, 0.f, 0.f, 0.f};
+    if (col_ok) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) s2f[u] = f16_bits_to_f32(s2[nc + u]);
+        for (int u = 0; u < 4; ++u) s2f[u] = f16_bits_to_f32(s2[nc + u]);
+    }
+    auto store4 = [&](int m, i32x4 accv) {
+        const float s1m = s1[m];
+        int32_t v[4];
+        uint16_t o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = GROUP ? accv[u] : (accv[u] >> 4);
+            o[u] = bit_as<uint16_t>((f16)((float)v[u] * s1m * s2f[u]));
+        }
+        *(u32x2 *)(y + (size_t)m * N + nc) = (u32x2){(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                     (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+        if (acc_out) *(i32x4 *)(acc_out + (size_t)m * N + nc) = (i32x4){v[0], v[1], v[2], v[3]};
+    };
+    if (S == 1) {
+        if (!col_ok) return;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
+                if (m < M) store4(m, (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
+            }
+        return;
+    }
+    // Split-K by partial tiles (device.hpp); int32 partials, so the sum is
+    // exact in any order.
+    uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
+    int32_t *const part = (int32_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N;
+    if (col_ok) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
+                if (m < M)
+                    *(i32x4 *)(part + split * slot + (size_t)m * N + nc) =
+                        (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+            }
+    }
+    if (!split_tile_last(cnt, S) || !col_ok) return;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
-            const float s1m = s1[m];
-            if (S == 1) {
-                int32_t v[4];
-                uint16_t o[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    v[u] = GROUP ? acc[mt][u][r] : (acc[mt][u][r] >> 4);
-                    o[u] = bit_as<uint16_t>((f16)((float)v[u] * s1m * s2f[u]));
-                }
-                *(u32x2 *)(y + (size_t)m * N + nc) = (u32x2){(uint32_t)o[0] | ((uint32_t)o[1] << 16),
-                                                             (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
-                if (acc_out) *(i32x4 *)(acc_out + (size_t)m * N + nc) = (i32x4){v[0], v[1], v[2], v[3]};
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    int64_t sum;
-                    if (splitk_contribute(&acc64[(size_t)m * N + nc + u], acc[mt][u][r], S, &sum)) {
-                        const int32_t v = GROUP ? (int32_t)sum : ((int32_t)sum >> 4);
-                        y[(size_t)m * N + nc + u] = bit_as<uint16_t>((f16)((float)v * s1m * s2f[u]));
-                        if (acc_out) acc_out[(size_t)m * N + nc + u] = v;
-                    }
-                }
+            i32x4 v = {0, 0, 0, 0};
+            for (int sp = 0; sp < S; ++sp) {
+                i32x4 *src = (i32x4 *)(part + sp * slot + (size_t)m * N + nc);
+                v += *src;
+                *src = (i32x4){0, 0, 0, 0};
             }
+            store4(m, v);
         }
 }
 

@@ -57,13 +57,26 @@ struct W4A8Plan {
     int blk;   // skinny: 64-column sets per lane-row (1, 2)
     int mt;    // row tiles (skinny: M <= 16*mt; tiled and LDS GEMM: per wave)
     int tiles_n, tiles_m, splits;
+    int tilered;  // split-K through partial tiles (else per-element atomics; skinny kernel only)
     size_t workspace_bytes;
     uint64_t *acc;
 };
 
-// Workspace of a split-K launch: one 64-bit counting accumulator per output
-// element (M x N), zero between calls (device.hpp).  Splits are capped at 255.
+// Workspace of a split-K launch, zero between calls (device.hpp): for the
+// decode GEMV and small W4A8 outputs one 64-bit counting accumulator per
+// output element (M x N); for the GEMM kernels per-tile arrival counters and
+// fp32 / int32 partial tiles.  Splits are capped at 255.
 constexpr int kMaxSplitK = 255;
+
+// Partial-tile split-K workspace: uint32 arrival counters, one per output
+// tile, padded to 256 bytes, then S partial [M, N] tiles of 4-byte values.
+constexpr int64_t kSplitCounterAlign = 256;
+__host__ __device__ constexpr int64_t split_counters_bytes(int64_t tiles) {
+    return (tiles * 4 + kSplitCounterAlign - 1) / kSplitCounterAlign * kSplitCounterAlign;
+}
+__host__ __device__ constexpr int64_t split_tiles_bytes(int64_t tiles, int64_t S, int64_t M, int64_t N) {
+    return split_counters_bytes(tiles) + S * M * N * 4;
+}
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry);
 W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);

@@ -340,19 +340,39 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
             }
         return;
     }
-    if (!col_ok) return;
+    // Split-K by partial tiles (device.hpp): store this split's partials,
+    // then the last workgroup of the tile sums all splits in split order.
+    uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
+    float *const part = (float *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N;
+    if (col_ok) {
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m >= M) continue;
+                float *dst = part + split * slot + (size_t)m * N + n0;
+                *(f32x4 *)dst = (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                *(f32x4 *)(dst + 4) = (f32x4){acc[mt][4][r], acc[mt][5][r], acc[mt][6][r], acc[mt][7][r]};
+            }
+    }
+    if (!split_tile_last(cnt, S) || !col_ok) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                int64_t sum;
-                if (splitk_contribute(&acc64[(size_t)m * N + n0 + t], to_fixed<DT>(acc[mt][t][r]), S, &sum))
-                    y[(size_t)m * N + n0 + t] = f32_to_out_bits(from_fixed<DT>(sum), DT);
+            f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < S; ++s) {
+                float *src = part + s * slot + (size_t)m * N + n0;
+                v0 += *(const f32x4 *)src;
+                v1 += *(const f32x4 *)(src + 4);
+                *(f32x4 *)src = (f32x4){0.f, 0.f, 0.f, 0.f};
+                *(f32x4 *)(src + 4) = (f32x4){0.f, 0.f, 0.f, 0.f};
             }
+            *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
         }
 }
 

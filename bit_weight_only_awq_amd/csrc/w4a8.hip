@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
                                                    const uint16_t *__restrict__ s2,
                                                    const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                    int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
-                                                   int M, int N, int K, int G, int S, int qa_stride) {
+                                                   int M, int N, int K, int G, int S, int qa_stride,
+                                                   int tilered) {
     extern __shared__ int32_t ired[];
     constexpr int COLS = 64 * BLK;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -369,6 +370,11 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
     __syncthreads();
     const int total = M * COLS;
     const int n_base = tile * COLS;
+    // split-K: per-element counting atomics when the output is small (one
+    // round trip), partial tiles otherwise (tilered; device.hpp)
+    uint32_t *const cnt = (uint32_t *)acc64 + tile;
+    int32_t *const part = (int32_t *)((char *)acc64 + split_counters_bytes(gridDim.x));
+    const size_t slot = (size_t)M * N;
     for (int idx = threadIdx.x; idx < total; idx += 256) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int32_t v = ired[(size_t)(0 * M + m) * COLS + c] + ired[(size_t)(1 * M + m) * COLS + c] +
@@ -379,8 +385,23 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
         const float s1m = FUSED ? srow[m] : s1[m];
         if (S == 1)
             w4a8_store_s<GROUP>(v, m, n, N, s1m, s2, y, acc_out);
+        else if (tilered)
+            part[split * slot + (size_t)m * N + n] = v;
         else if (splitk_contribute(&acc64[(size_t)m * N + n], v, S, &sum))
             w4a8_store_s<GROUP>((int32_t)sum, m, n, N, s1m, s2, y, acc_out);
+    }
+    if (S == 1 || !tilered || !split_tile_last(cnt, S)) return;
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int m = idx / COLS, c = idx - m * COLS;
+        const int n = n_base + c;
+        if (n >= N) continue;
+        int32_t v = 0;
+        for (int sp = 0; sp < S; ++sp) {
+            int32_t *src = part + sp * slot + (size_t)m * N + n;
+            v += *src;
+            *src = 0;
+        }
+        w4a8_store_s<GROUP>(v, m, n, N, FUSED ? srow[m] : s1[m], s2, y, acc_out);
     }
 }
 
@@ -458,19 +479,37 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
             }
         return;
     }
-    if (!ok) return;
+    // Split-K by partial tiles (device.hpp); int32 partials, so the sum is
+    // exact in any order.
+    uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
+    int32_t *const part = (int32_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N;
+    if (ok) {
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M)
+                    *(i32x4 *)(part + split * slot + (size_t)m * N + ncol) =
+                        (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+            }
+    }
+    if (!split_tile_last(cnt, S) || !ok) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + 16 * mt + 4 * gq + r;
             if (m >= M) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int64_t sum;
-                if (splitk_contribute(&acc64[(size_t)m * N + ncol + i], acc[mt][i][r], S, &sum))
-                    w4a8_store<GROUP>((int32_t)sum, m, ncol + i, N, s1, s2, y, acc_out);
+            i32x4 v = {0, 0, 0, 0};
+            for (int sp = 0; sp < S; ++sp) {
+                i32x4 *src = (i32x4 *)(part + sp * slot + (size_t)m * N + ncol);
+                v += *src;
+                *src = (i32x4){0, 0, 0, 0};
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w4a8_store<GROUP>(v[i], m, ncol + i, N, s1, s2, y, acc_out);
         }
 }
 
@@ -494,7 +533,7 @@ static hipError_t launch_skinny8(const W4A8Args &a, const W4A8Plan &p, hipStream
     hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP, FUSED>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
                        (const uint16_t *)a.x, (const uint32_t *)a.b, a.s1, a.s1_out, (const uint16_t *)a.s2,
                        (const uint16_t *)a.s3, (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K,
-                       a.G, p.splits, qa_stride);
+                       a.G, p.splits, qa_stride, p.tilered);
     return hipGetLastError();
 }
 

@@ -86,8 +86,12 @@ def test_workspace_bytes():
     assert lib.awq_workspace_bytes(op_gemm, 2048, 4096, 4096, 128, 1) == 0
     # a M=1, N=4096 GEMV: one 64-bit counting accumulator per output element
     assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == 4096 * 8
-    # the tiled kernel with an explicit split: same layout
-    assert lib.awq_workspace_bytes(op_gemm, 64, 4096, 4096, 128, 4) == 64 * 4096 * 8
+    # the tiled kernel with an explicit split: per-tile counters (16 tiles of
+    # 64 rows x 256 columns, padded to 256 bytes), then 4 fp32 partial results
+    assert lib.awq_workspace_bytes(op_gemm, 64, 4096, 4096, 128, 4) == 256 + 4 * 64 * 4096 * 4
+    # the LDS GEMM with an explicit split: 8 x 32 tiles of 256 rows x 128
+    # columns
+    assert lib.awq_workspace_bytes(op_gemm, 2048, 4096, 4096, 128, 2) == 1024 + 2 * 2048 * 4096 * 4
     assert lib.awq_workspace_bytes(op8, 1, 8192, 21760, -1, 0) == 8192 * 8
     # automatic split for decode needs a workspace
     assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 0) > 0
