@@ -114,6 +114,47 @@ __device__ __forceinline__ uint16_t f32_to_out_bits(float v, int dt) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS copies of 16 bytes per lane: lane i of the wave writes
+// bytes [16 i, 16 i + 16) after the LDS address `dst` of the first active
+// lane (M0).
+//
+// They are issued from inline assembly on purpose.  The compiler's own form
+// of these copies (the global_load_lds / buffer_load_lds builtins) cannot
+// tell which LDS bytes a copy writes, so it waits for every copy in flight
+// before any later LDS read: a copy issued for the next pipeline stage then
+// stalls the reads of the current one for a whole memory latency.  The
+// compiler does not see these copies at all, so the code that reads their
+// data waits for them itself (wait_vm_all(), then a workgroup barrier).  Its
+// own vector-memory waits stay correct: loads complete in issue order, and a
+// wait computed without the hidden copies only waits for more of them.
+// M0 takes the first active lane's address (as the compiler's own copies do)
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+// from a global address (per lane)
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_address(dst)), "v"(src)
+                 : "memory", "m0");
+}
+// through a buffer descriptor: address = base + voff (per lane) + soff
+// (wave-uniform); offsets past the descriptor's size read as zero
+constexpr int kBufDword3 = 0x00020000;  // raw 32-bit buffer, no format conversion
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, kBufDword3);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *dst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_address(dst)), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+// Wait until every vector-memory load of this wave has landed (the direct
+// LDS copies included).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------------------
 // XCD-aware tile order.  Workgroups are dispatched round-robin over the 8
 // XCDs (workgroup i of a launch runs on XCD i % 8), and each XCD has its own
 // L2.  Tile `tile_of_xcd_order(i, T)` gives XCD x a contiguous run of the T

@@ -53,26 +53,6 @@ __device__ __forceinline__ int bseg(int r, int s) { return s ^ ((r >> 3) & 3); }
 // Output columns of MFMA u relative to the lane's word-column (before + 2h).
 __host__ __device__ constexpr int gemm_col(int u) { return (u & 1) + ((u >> 1) << 2); }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i of the wave writes
-// bytes [16 i, 16 i + 16) after the wave-uniform LDS address `dst`.
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-}
-// The same copy through a buffer descriptor: address = base + voff (per lane,
-// loop-invariant) + soff (wave-uniform stage offset), so a copy costs no
-// vector arithmetic.  Offsets past num_records read as zero.
-constexpr int kBufDword3 = 0x00020000;  // raw 32-bit buffer, no format conversion
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, kBufDword3);
-}
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void *dst) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
-}
-// Wait until every vector-memory load of this wave has landed (the direct
-// LDS copies included).
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
 // KS = 2: the workgroup holds two groups of 4 waves that share the output
 // tile and split its K range (each with its own LDS ring); the groups trade
 // partial sums through LDS at the end.  This doubles the waves per SIMD for

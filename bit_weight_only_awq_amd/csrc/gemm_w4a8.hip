@@ -38,11 +38,6 @@ struct W8Layout {
 // 2 apart (and rows 4 apart) always get different f.
 __device__ __forceinline__ int a8seg(int r, int s) { return s ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
-__device__ __forceinline__ void dma16_w8(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-}
-
 // int8 B operand of one column from two consecutive K8 words (16 k).
 //  per-channel: bytes = 16*q; per-group: bytes = q*s3 (s3 in 1..16), via
 //  u = q + 8 in 0..15: u*s3 + (128 - 8*s3) stays in 0..240 per byte, and
@@ -121,12 +116,12 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         unsigned char *A = lds + slot * W8_ABYTES + 32 * wave * W8_APITCH;
         const int8_t *src = ag + (size_t)st * W8_K;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma16_w8(src + aoff[i], A + 16 * i * W8_APITCH);
+        for (int i = 0; i < 2; ++i) dma16(src + aoff[i], A + 16 * i * W8_APITCH);
         unsigned char *B = lds + L::OFF_B + slot * L::BBYTES;
-        dma16_w8((const char *)bq + (size_t)st * (W8_K / 8) * N * 4 + boff, B + 2 * wave * (W8_N * 4));
+        dma16((const char *)bq + (size_t)st * (W8_K / 8) * N * 4 + boff, B + 2 * wave * (W8_N * 4));
         if (GROUP && lane < 8) {
             const int g = (st * W8_K + 32 * s3_h) / G;
-            dma16_w8((const char *)(s3 + (size_t)g * N) + s3_off, B + W8_WORDS + 16 * s3_seg);
+            dma16((const char *)(s3 + (size_t)g * N) + s3_off, B + W8_WORDS + 16 * s3_seg);
         }
     };
 
