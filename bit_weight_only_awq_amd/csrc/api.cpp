@@ -194,9 +194,8 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     W4A16Plan p = plan_w4a16(M, N, K, G, split_k, gemv);
     rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
     if (rc != AWQ_OK) return rc;
-    if (p.splits > 1) {
-        p.acc = static_cast<uint64_t *>(workspace);
-    }
+    // every plan that needs a workspace (split-K or stream-K) gets it
+    if (p.workspace_bytes > 0) p.acc = static_cast<uint64_t *>(workspace);
     W4A16Args a{x, qweight, scales, qzeros, y, M, N, K, G, dtype};
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;

@@ -393,6 +393,8 @@ static hipError_t launch_gemm_ks(const W4A16Args &a, const W4A16Plan &p, hipStre
 }
 
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    // a K split reduces through the workspace
+    if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
     return p.ksplit == 2 ? launch_gemm_ks<2>(a, p, st) : launch_gemm_ks<1>(a, p, st);
 }
 

@@ -52,6 +52,12 @@ def _w4a16(fn, x=A, qw=A, s=A, qz=A, y=A, M=1, N=4096, K=4096, G=128, dt=0, spli
     return getattr(L.lib(), fn)(x, qw, s, qz, y, M, N, K, G, dt, split, ws, wsb, None)
 
 
+def test_split_gemm_needs_workspace():
+    """A K-split GEMM is refused without its workspace (before any launch)."""
+    assert _w4a16("awq_gemm_w4a16", M=64, N=4096, K=4096) == L.AWQ_EWORKSPACE
+    assert _w4a16("awq_gemm_w4a16", M=64, N=4096, K=4096, ws=A, wsb=1 << 10) == L.AWQ_EWORKSPACE
+
+
 @pytest.mark.parametrize("fn", ["awq_gemm_w4a16", "awq_gemv_w4a16"])
 def test_w4a16_validation(fn):
     E = L
@@ -93,6 +99,8 @@ def test_workspace_bytes():
     # columns
     assert lib.awq_workspace_bytes(op_gemm, 2048, 4096, 4096, 128, 2) == 1024 + 2 * 2048 * 4096 * 4
     assert lib.awq_workspace_bytes(op8, 1, 8192, 21760, -1, 0) == 8192 * 8
+    # one workgroup per tile without a K split: no workspace
+    assert lib.awq_workspace_bytes(op_gemm, 2048, 6144, 4096, 128, 0) == 0
     # automatic split for decode needs a workspace
     assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 0) > 0
     # invalid shapes -> 0
