@@ -275,6 +275,10 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
                 if (mt == 1) pair_words(w, px, py);
                 if (mt == 5) bn[0] = dequant(px, 0);
                 if (mt == 9) bn[1] = dequant(py, 1);
+                // keep each row tile's operand read where it is written: the
+                // scheduler would otherwise sink the reads next to their
+                // MFMAs and lose the prefetch distance
+                __builtin_amdgcn_sched_barrier(0);
             }
             bc[0] = bn[0];
             bc[1] = bn[1];
