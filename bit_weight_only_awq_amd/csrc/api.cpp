@@ -136,7 +136,11 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         }
         p.splits = (int)std::max<int64_t>(1, s);
     }
-    if (M >= 128) {
+    // buffer-descriptor copies address a8, the packed words and s3 with
+    // 32-bit offsets
+    const bool fits_rsrc = M * K < (int64_t(1) << 31) && (K / 8) * N * 4 < (int64_t(1) << 31) &&
+                           (G <= 0 || (K / G) * N * 2 < (int64_t(1) << 31));
+    if (M >= 128 && fits_rsrc) {
         // LDS-pipelined int8 GEMM: 128 x 128 workgroup tiles, K in stages of 64
         p.kind = 2;
         p.blk = 1;

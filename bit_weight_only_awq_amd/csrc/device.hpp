@@ -18,6 +18,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace awq4 {
 
 typedef _Float16 f16;
@@ -32,6 +35,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
+
+// f(std::integral_constant<int, 0>) ... f(std::integral_constant<int, N - 1>),
+// in order: a loop whose index is a compile-time constant in every body
+// (guaranteed unrolling, `if constexpr` on the index).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <typename T, typename F>
 __device__ __forceinline__ T bit_as(F v) {

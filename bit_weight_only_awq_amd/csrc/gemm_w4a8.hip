@@ -94,7 +94,6 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     // 2w+1, lane%32 being the 4-column segment; columns past N repeat the last
     // 4.  s3 (grouped): wave w, lanes 0..7, copies 16-byte segments 8w..8w+7 of
     // the stage's two s3 rows (half h = segment / 16).
-    const int8_t *const ag = a8 + (size_t)m0 * K;
     uint32_t aoff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -109,19 +108,26 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         boff = (uint32_t)((r * N + c) * 4);
     }
     const int s3_seg = 8 * wave + (lane & 7);
-    const int s3_h = s3_seg >> 4;
+    const int s3_h = s3_seg >> 4;  // wave-uniform: waves 0, 1 copy half 0, waves 2, 3 half 1
     const uint32_t s3_off = (uint32_t)(2 * min(n0 + 8 * (s3_seg & 15), N - 8));
+    const int lg = GROUP ? __builtin_ctz(G) : 0;
+    // buffer descriptors (the planner keeps every byte offset under 2^31):
+    // a8 rows from m0, the packed words, the s3 rows; per-lane offsets above,
+    // the stage's offset as a scalar
+    const __amdgpu_buffer_rsrc_t ars = buf_rsrc(a8 + (size_t)m0 * K, (int64_t)(M - m0) * K);
+    const __amdgpu_buffer_rsrc_t brs = buf_rsrc(bq, (int64_t)(K / 8) * N * 4);
+    const __amdgpu_buffer_rsrc_t grs = buf_rsrc(GROUP ? (const void *)s3 : (const void *)bq,
+                                                GROUP ? (int64_t)(K / G) * N * 2 : 0);
 
     auto copy_stage = [&](int st, int slot) {
         unsigned char *A = lds + slot * W8_ABYTES + 32 * wave * W8_APITCH;
-        const int8_t *src = ag + (size_t)st * W8_K;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma16(src + aoff[i], A + 16 * i * W8_APITCH);
+        for (int i = 0; i < 2; ++i) dma16_buf(ars, aoff[i], (uint32_t)(st * W8_K), A + 16 * i * W8_APITCH);
         unsigned char *B = lds + L::OFF_B + slot * L::BBYTES;
-        dma16((const char *)bq + (size_t)st * (W8_K / 8) * N * 4 + boff, B + 2 * wave * (W8_N * 4));
+        dma16_buf(brs, boff, (uint32_t)st * (W8_K / 8) * (uint32_t)N * 4, B + 2 * wave * (W8_N * 4));
         if (GROUP && lane < 8) {
-            const int g = (st * W8_K + 32 * s3_h) / G;
-            dma16((const char *)(s3 + (size_t)g * N) + s3_off, B + W8_WORDS + 16 * s3_seg);
+            const int g = (st * W8_K + 32 * s3_h) >> lg;
+            dma16_buf(grs, s3_off, (uint32_t)g * (uint32_t)N * 2, B + W8_WORDS + 16 * s3_seg);
         }
     };
 
@@ -141,6 +147,11 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         u32x4 a[4];
         u32x4 b[4];
     };
+    // group scale of column cl + u from the stage's two s3 rows
+    auto group_scales = [&](u32x2 sv, uint32_t (&g3)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) g3[u] = (uint32_t)f16_bits_to_f32((sv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
+    };
     auto load_ops = [&](int slot, Ops &o) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
@@ -152,27 +163,42 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         const u32x4 w0 = wq[0];
         const u32x4 w1 = wq[W8_N / 4];
         uint32_t g3[4] = {16u, 16u, 16u, 16u};
-        if (GROUP) {
-            const u32x2 sv = *(const u32x2 *)(lds + slot * L::BBYTES + g_off);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) g3[u] = (uint32_t)f16_bits_to_f32((sv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
-        }
+        if (GROUP) group_scales(*(const u32x2 *)(lds + slot * L::BBYTES + g_off), g3);
 #pragma unroll
         for (int u = 0; u < 4; ++u) o.b[u] = b8_operand<GROUP>(w0[u], w1[u], g3[u]);
     };
-    // Stage st (its operands already in `cur`): load stage st + 1 into `nxt`
-    // while the 16 MFMAs run, then wait for the copies older than this
-    // stage's and cross the barrier.  Copies: stage st + 3 into the slot of
-    // stage st - 1 (finished before the last barrier); near the end the last
-    // stage is copied again into that slot, never read as data, so every
-    // stage issues the same copies and the wait count is fixed.
+    // Stage st (its operands already in `cur`): 16 MFMAs, each in its own
+    // slot; stage st + 1's operands are read in the first slots and its int8
+    // B operands built in the last eight, so that no wave waits on its own
+    // LDS reads.  Then wait for the copies older than this stage's and cross
+    // the barrier.  Copies: stage st + 3 into the slot of stage st - 1
+    // (finished before the last barrier); near the end the last stage is
+    // copied again into that slot, never read as data, so every stage issues
+    // the same copies and the wait count is fixed.
     auto stage = [&](int st, Ops &cur, Ops &nxt) {
-        copy_stage(min(st + W8_RING - 1, s_hi - 1), (st - s_lo + W8_RING - 1) % W8_RING);
-        load_ops((st + 1 - s_lo) % W8_RING, nxt);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[mt][u] = mfma_i8(cur.a[mt], cur.b[u], acc[mt][u]);
+        const unsigned rel = (unsigned)(st - s_lo);
+        copy_stage(min(st + W8_RING - 1, s_hi - 1), (int)((rel + W8_RING - 1) % W8_RING));
+        const unsigned char *nb = lds + ((rel + 1) % W8_RING) * L::BBYTES;
+        const unsigned char *na = lds + ((rel + 1) % W8_RING) * W8_ABYTES + a_off;
+        const u32x4 *wq = (const u32x4 *)__builtin_assume_aligned(nb + w_off, 16);
+        u32x4 w0, w1;
+        u32x2 sv;
+        uint32_t g3[4] = {16u, 16u, 16u, 16u};
+        static_for<16>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int mt = i >> 2, u = i & 3;
+            acc[mt][u] = mfma_i8(cur.a[mt], cur.b[u], acc[mt][u]);
+            if constexpr (i < 4) nxt.a[i] = *(const u32x4 *)(na + i * 16 * W8_APITCH);
+            if constexpr (i == 4) w0 = wq[0];
+            if constexpr (i == 5) w1 = wq[W8_N / 4];
+            if constexpr (i == 6 && GROUP) sv = *(const u32x2 *)(nb + g_off);
+            if constexpr (i == 8 && GROUP) group_scales(sv, g3);
+            if constexpr (i >= 8 && (i & 1) == 0) {
+                constexpr int uu = (i - 8) >> 1;
+                nxt.b[uu] = b8_operand<GROUP>(w0[uu], w1[uu], g3[uu]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
         // copies still allowed in flight: those of stages st + 3 .. st + W8_RING - 1
         constexpr int kInFlight = (W8_RING - 3) * L::COPIES;
         __builtin_amdgcn_s_waitcnt(0x0F70 | (kInFlight & 15) | ((kInFlight >> 4) << 14));
