@@ -112,15 +112,19 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         woff = (uint32_t)((r * nw + wc - wc0) * 4);
     }
     // Metadata (wave 0): lanes 0..31 copy 8 scales each (k-step lane/16,
-    // word-column wc0 + lane%16), lanes 32..39 copy 4 zero words each.
-    const int meta_lanes = wave == 0 ? (SYM ? 32 : 40) : 0;
-    int meta_ks, meta_col;
+    // word-column wc0 + lane%16), lanes 32..39 copy 4 zero words each, through
+    // descriptors over the scale and zero-point arrays: the group of k-step 0
+    // of the stage is a scalar offset, the k-step's step past it (one group
+    // when G = 32) part of the lane's fixed offset.
+    const __amdgpu_buffer_rsrc_t srs = buf_rsrc(sc, (int64_t)(K / G) * N * 2);
+    const __amdgpu_buffer_rsrc_t zrs = buf_rsrc(SYM ? (const void *)sc : (const void *)qz, SYM ? 0 : (int64_t)(K / G) * nw * 4);
+    uint32_t m_voff;
     if (lane < 32) {
-        meta_ks = lane >> 4;
-        meta_col = min(wc0 + (lane & 15), nw - 1);
+        const int meta_ks = lane >> 4, meta_col = min(wc0 + (lane & 15), nw - 1);
+        m_voff = (uint32_t)((((32 * meta_ks) >> lg) * N + 8 * meta_col) * 2);
     } else {
-        meta_ks = (lane - 32) >> 2;
-        meta_col = min(wc0 + 4 * ((lane - 32) & 3), nw - 4);
+        const int meta_ks = (lane - 32) >> 2, meta_col = min(wc0 + 4 * ((lane - 32) & 3), nw - 4);
+        m_voff = (uint32_t)((((32 * meta_ks) >> lg) * nw + meta_col) * 4);
     }
 
     auto copyA = [&](int st, int buf) {
@@ -131,11 +135,10 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     auto copyB = [&](int st) {
         unsigned char *dst = Bbase + (st % GB_BUFS) * GB_BYTES;
         dma16_buf(wrs, woff, (uint32_t)st * (GB_K * 4) * (uint32_t)nw, dst + 16 * wave * GB_PITCH);
-        if (lane < meta_lanes) {
-            const int g = (st * GB_K + 32 * meta_ks) >> lg;
-            const void *src = lane < 32 ? (const void *)(sc + (size_t)g * N + 8 * meta_col)
-                                        : (const void *)(qz + (size_t)g * nw + meta_col);
-            dma16(src, dst + GB_WORDS);
+        if (wave == 0) {
+            const uint32_t g0 = (uint32_t)((st * GB_K) >> lg);
+            if (lane < 32) dma16_buf(srs, m_voff, g0 * (uint32_t)N * 2, dst + GB_WORDS);
+            else if (!SYM && lane < 40) dma16_buf(zrs, m_voff, g0 * (uint32_t)nw * 4, dst + GB_WORDS);
         }
     };
 
