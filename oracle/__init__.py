@@ -89,14 +89,16 @@ class Oracle:
         L.orc_bf16_to_f64.restype = ctypes.c_double
         L.orc_f64_to_f16.argtypes = [ctypes.c_double]
         L.orc_f64_to_f16.restype = ctypes.c_uint16
+        L.orc_f64_to_bf16.argtypes = [ctypes.c_double]
+        L.orc_f64_to_bf16.restype = ctypes.c_uint16
         L.orc_unpack_n8.argtypes = [vp, vp, i64, i64]
         L.orc_pack_n8.argtypes = [vp, vp, i64, i64, vp]
         L.orc_unpack_k8.argtypes = [vp, vp, i64, i64]
         L.orc_pack_k8.argtypes = [vp, vp, i64, i64, vp]
         L.orc_w4a16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, i32]
         L.orc_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp]
-        L.orc_quant_act.argtypes = [vp, i64, i64, vp, vp]
-        L.orc_w4a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, i32]
+        L.orc_quant_act.argtypes = [vp, i64, i64, i32, vp, vp]
+        L.orc_w4a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, i32]
         for f in ("orc_unpack_n8", "orc_pack_n8", "orc_unpack_k8", "orc_pack_k8", "orc_w4a16",
                   "orc_dequant", "orc_quant_act", "orc_w4a8"):
             getattr(L, f).restype = ctypes.c_int
@@ -110,6 +112,9 @@ class Oracle:
 
     def f64_to_f16(self, v: float) -> int:
         return int(self.lib.orc_f64_to_f16(float(v)))
+
+    def f64_to_bf16(self, v: float) -> int:
+        return int(self.lib.orc_f64_to_bf16(float(v)))
 
     # -- packing ---------------------------------------------------------------
     def unpack_n8(self, packed) -> np.ndarray:
@@ -180,16 +185,17 @@ class Oracle:
         return y
 
     # -- W4A8 ------------------------------------------------------------------
-    def quant_act(self, x):
+    def quant_act(self, x, dtype: int = F16):
+        """Per-token int8 quantisation of fp16 (dtype 0) or bf16 (dtype 1) activations."""
         xb = _u16(x)
         M, K = xb.shape
         a8 = np.empty((M, K), np.int8)
         s1 = np.empty((M,), np.float32)
-        assert self.lib.orc_quant_act(_p(xb), M, K, _p(a8), _p(s1)) == 0
+        assert self.lib.orc_quant_act(_p(xb), M, K, int(dtype), _p(a8), _p(s1)) == 0
         return a8, s1
 
     def w4a8(self, a8, b_packed, s1, s2, s3=None, group_size: int = -1, nthreads: int = 1,
-             want_y: bool = True):
+             want_y: bool = True, dtype: int = F16):
         a = np.ascontiguousarray(a8, dtype=np.int8)
         b = _i32(b_packed)
         M, K = a.shape
@@ -201,7 +207,7 @@ class Oracle:
         acc = np.empty((M, N), np.int64)
         y = np.empty((M, N), np.float64) if want_y else None
         rc = self.lib.orc_w4a8(_p(a), _p(b), _p(s1a), _p(s2a), _p(s3a), M, N, K,
-                               int(group_size), _p(acc), _p(y), int(nthreads))
+                               int(group_size), int(dtype), _p(acc), _p(y), int(nthreads))
         if rc:
             raise ValueError("w4a8: bad shape or non-integer group scale")
         return acc, y

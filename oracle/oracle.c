@@ -110,6 +110,38 @@ uint16_t orc_f64_to_f16(double v) {
     return sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)r - 1024);
 }
 
+/* double -> bfloat16 (the top 16 bits of a binary32: 8-bit significand,
+ * binary32's exponent range), round to nearest, ties to even (one rounding of
+ * the double value).  Overflow goes to infinity, NaN to the quiet NaN 0x7fc0. */
+uint16_t orc_f64_to_bf16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return 0x7fc0;
+    /* the largest finite value is (2 - 2^-7) * 2^127; halfway to 2^128 rounds up */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return sign | 0x7f80;
+    if (a < ldexp(1.0, -126)) {
+        /* subnormal range: the quantum is 2^-133; 128 quanta is the smallest
+         * normal, whose encoding is the same integer 0x80. */
+        double r = nearbyint(ldexp(a, 133));
+        return sign | (uint16_t)r;
+    }
+    int e2;
+    frexp(a, &e2);         /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;        /* unbiased exponent */
+    double r = nearbyint(ldexp(a, 7 - E)); /* significand in [128, 256] */
+    if (r == 256.0) {
+        r = 128.0;
+        E += 1;
+    }
+    if (E > 127) return sign | 0x7f80;
+    return sign | (uint16_t)((E + 127) << 7) | (uint16_t)((int)r - 128);
+}
+
+/* a value rounded to the activation type (fp16 = 0, bf16 = 1) and widened back */
+static double round_act(double v, int dtype) {
+    return dtype == 1 ? orc_bf16_to_f64(orc_f64_to_bf16(v)) : orc_f16_to_f64(orc_f64_to_f16(v));
+}
+
 static double decode_act(uint16_t bits, int dtype) {
     return dtype == 1 ? orc_bf16_to_f64(bits) : orc_f16_to_f64(bits);
 }
@@ -301,31 +333,33 @@ int orc_dequant(const int32_t *qweight, const uint16_t *scales, const int32_t *q
 /* W4A8 (QQQ): per-token int8 activations, int4 weights, exact integer  */
 /* accumulation, output scaled by s1[m] * s2[n].                        */
 
-/* Dynamic per-token quantisation of fp16 activations [M, K] ([P5], the
- * dynamic_quant helper):
- *   amax  = max_k |x[m,k]|                         (exact in fp16)
- *   s1    = float( fp16( float(amax) / 127 ) )      (the quotient is taken on
- *                                                    the fp16 tensor, then widened)
+/* Dynamic per-token quantisation of activations [M, K] ([P5], the
+ * dynamic_quant helper), fp16 (dtype 0) or bf16 (dtype 1):
+ *   amax  = max_k |x[m,k]|                          (exact in the activation type)
+ *   s1    = float( act( float(amax) / 127 ) )        (the quotient is taken on the
+ *                                                     activation tensor, then widened)
  *   a8    = clamp( round_half_even( float(x) / s1 ), -128, 127 )   (fp32 divide)
- * A row with s1 == 0 gives a8 = 0. */
-int orc_quant_act(const uint16_t *x, int64_t M, int64_t K, int8_t *a8, float *s1) {
-    if (M < 0 || K <= 0) return ORC_EINVAL;
+ * A row with s1 == 0 gives a8 = 0.  The bf16 form is this library's reading of
+ * how the pages' fp16 recipe carries over to bf16 models (the pages list bf16
+ * as not yet supported). */
+int orc_quant_act(const uint16_t *x, int64_t M, int64_t K, int dtype, int8_t *a8, float *s1) {
+    if (M < 0 || K <= 0 || (dtype != 0 && dtype != 1)) return ORC_EINVAL;
     for (int64_t m = 0; m < M; m++) {
         const uint16_t *row = x + m * K;
         double amax = 0.0;
         for (int64_t k = 0; k < K; k++) {
-            double v = fabs(orc_f16_to_f64(row[k]));
+            double v = fabs(decode_act(row[k], dtype));
             if (v > amax) amax = v;
         }
-        float q32 = (float)amax / 127.0f;                  /* fp32, correctly rounded */
-        float s = (float)orc_f16_to_f64(orc_f64_to_f16((double)q32)); /* to fp16 and back */
+        float q32 = (float)amax / 127.0f;                 /* fp32, correctly rounded */
+        float s = (float)round_act((double)q32, dtype);   /* to the activation type and back */
         s1[m] = s;
         for (int64_t k = 0; k < K; k++) {
             if (s == 0.0f) {
                 a8[m * K + k] = 0;
                 continue;
             }
-            float xf = (float)orc_f16_to_f64(row[k]);
+            float xf = (float)decode_act(row[k], dtype);
             float r = rintf(xf / s); /* round half to even (default rounding mode) */
             if (r < -128.0f) r = -128.0f;
             if (r > 127.0f) r = 127.0f;
@@ -341,7 +375,7 @@ typedef struct {
     const float *s1;
     const uint16_t *s2, *s3;
     int64_t M, N, K;
-    int G;
+    int G, dtype;
     int64_t *acc;
     double *y;
     int64_t n0, n1;
@@ -362,14 +396,14 @@ static void *w4a8_worker(void *arg) {
                 int q = sext4((w >> (4 * i)) & 0xF);
                 int mult = 1;
                 if (t->s3) {
-                    double s3 = orc_f16_to_f64(t->s3[(k / t->G) * N + n]);
+                    double s3 = decode_act(t->s3[(k / t->G) * N + n], t->dtype);
                     mult = (int)s3;
                     if ((double)mult != s3 || mult < 1 || mult > 16) { t->err = 1; mult = 0; }
                 }
                 w8[k] = q * mult;
             }
         }
-        double s2 = orc_f16_to_f64(t->s2[n]);
+        double s2 = decode_act(t->s2[n], t->dtype);
         for (int64_t m = 0; m < t->M; m++) {
             const int8_t *ar = t->a8 + m * K;
             int64_t acc = 0;
@@ -384,11 +418,12 @@ static void *w4a8_worker(void *arg) {
 
 /* acc[m,n] = sum_k a8[m,k] * w8[k,n]  (int64), with w8 = q for per-channel
  * weights (s3 == NULL) or w8 = q * s3[k/G, n] for per-group weights, and
- * Y64[m,n] = acc * s1[m] * s2[n] in double.  Either output may be NULL. */
+ * Y64[m,n] = acc * s1[m] * s2[n] in double; s2 and s3 are fp16 (dtype 0) or
+ * bf16 (dtype 1) bit patterns.  Either output may be NULL. */
 int orc_w4a8(const int8_t *a8, const int32_t *b, const float *s1, const uint16_t *s2,
-             const uint16_t *s3, int64_t M, int64_t N, int64_t K, int G, int64_t *acc,
+             const uint16_t *s3, int64_t M, int64_t N, int64_t K, int G, int dtype, int64_t *acc,
              double *y, int nthreads) {
-    if (M < 0 || N <= 0 || K <= 0 || K % 8) return ORC_EINVAL;
+    if (M < 0 || N <= 0 || K <= 0 || K % 8 || (dtype != 0 && dtype != 1)) return ORC_EINVAL;
     if (s3 && (G <= 0 || K % G)) return ORC_EINVAL;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > N) nthreads = (int)N;
@@ -397,7 +432,7 @@ int orc_w4a8(const int8_t *a8, const int32_t *b, const float *s1, const uint16_t
     for (int i = 0; i < nthreads; i++) {
         w4a8_job *t = &jobs[i];
         t->a8 = a8; t->b = b; t->s1 = s1; t->s2 = s2; t->s3 = s3;
-        t->M = M; t->N = N; t->K = K; t->G = G; t->acc = acc; t->y = y;
+        t->M = M; t->N = N; t->K = K; t->G = G; t->dtype = dtype; t->acc = acc; t->y = y;
         t->n0 = N * i / nthreads;
         t->n1 = N * (i + 1) / nthreads;
     }

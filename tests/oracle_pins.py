@@ -19,6 +19,7 @@ The same pins are run against deliberately broken copies of the oracle
 from __future__ import annotations
 
 import os
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -44,9 +45,9 @@ def _golden_words():
     return rows
 
 
-def _golden_quant():
+def _golden_quant(name="quant_act_examples.txt"):
     rows = []
-    with open(os.path.join(GOLDEN, "quant_act_examples.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):
@@ -164,6 +165,56 @@ def pin_f16_codec(orc):
             exp = arr.astype(np.float16).view(np.uint16)
         enc = np.array([orc.f64_to_f16(float(v)) for v in arr], np.uint16)
         assert np.array_equal(enc, exp), np.flatnonzero(enc != exp)[:5]
+
+
+def _rne_bf16_fraction(fr: Fraction) -> float:
+    """Exact round-to-nearest-even of a non-negative rational to bfloat16 (8-bit
+    significand, binary32 exponent range); inf above the largest finite value."""
+    if fr == 0:
+        return 0.0
+    # exponent e with 2^e <= fr < 2^(e+1): frexp of the nearest double, then
+    # corrected by exact comparisons
+    e = math.frexp(float(fr))[1] - 1
+    while Fraction(2) ** e > fr:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= fr:
+        e += 1
+    quantum = Fraction(2) ** (e - 7) if e >= -126 else Fraction(2) ** -133
+    n = fr / quantum
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    v = lo * quantum
+    return float("inf") if v >= Fraction(2) ** 128 else float(v)
+
+
+def _bf16_bits(vals):
+    return torch.tensor(np.asarray(vals, np.float64), dtype=torch.float64).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def pin_bf16_encode(orc):
+    """The bf16 encoder against exact rational rounding: every finite pattern
+    round-trips, midpoints between neighbours go to the even one, random
+    doubles, and the overflow / subnormal edges."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    fin = np.isfinite(vals)
+    for b, v in zip(bits[fin], vals[fin]):
+        assert orc.f64_to_bf16(float(v)) == int(b) or (v == 0 and orc.f64_to_bf16(float(v)) in (0, 0x8000))
+    pos = np.unique(vals[fin & (vals > 0)])
+    mids = (pos[:-1] + pos[1:]) / 2  # exact in double (both neighbours have 8-bit significands)
+    rng = np.random.default_rng(21)
+    rnd = np.concatenate([np.abs(rng.standard_normal(2000)) * 10.0 ** rng.integers(-40, 38, 2000),
+                          [2.0 ** -133, 1.5 * 2.0 ** -133, 2.5 * 2.0 ** -133, 2.0 ** -134, 2.0 ** -135,
+                           2.0 ** -126, 2.0 ** -126 - 2.0 ** -134, (2 - 2.0 ** -7) * 2.0 ** 127,
+                           (2 - 2.0 ** -8) * 2.0 ** 127, (2 - 2.0 ** -8) * 2.0 ** 127 * (1 - 2.0 ** -40)]])
+    for v in np.concatenate([mids[::7], rnd]):
+        exp = _rne_bf16_fraction(Fraction(float(v)))
+        got = orc.bf16_to_f64(orc.f64_to_bf16(float(v)))
+        assert got == exp, (v, got, exp)
+        assert orc.f64_to_bf16(-float(v)) == orc.f64_to_bf16(float(v)) | 0x8000
 
 
 def pin_bf16_decode(orc):
@@ -357,6 +408,73 @@ def pin_quant_random(orc):
         assert np.array_equal(a8[m], np.clip(q, -128, 127).astype(np.int8))
 
 
+def pin_quant_bf16_examples(orc):
+    for xs, s1, a8 in _golden_quant("quant_act_examples_bf16.txt"):
+        got_a8, got_s1 = orc.quant_act(_bf16_bits([xs]), dtype=1)
+        assert float(got_s1[0]) == s1, (xs, got_s1[0], s1)
+        assert got_a8[0].tolist() == a8, (xs, got_a8[0].tolist(), a8)
+
+
+def pin_quant_bf16_s1_exhaustive(orc):
+    """bf16 activations: s1 = bf16(amax/127) for every positive finite bf16 amax
+    equals the exact rational quotient rounded once to bf16; with a normal s1 the
+    row extremes map to +-127."""
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    x = np.stack([bits, bits | 0x8000], axis=1)
+    a8, s1 = orc.quant_act(x, dtype=1)
+    amax = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    for i in range(len(bits)):
+        exp = _rne_bf16_fraction(Fraction(float(amax[i])) / 127)
+        assert float(s1[i]) == exp, (hex(bits[i]), s1[i], exp)
+    normal = s1 >= 2.0 ** -126
+    assert np.all(a8[normal, 0] == 127) and np.all(a8[normal, 1] == -127)
+
+
+def pin_quant_bf16_random(orc):
+    """Random bf16 rows: a8 equals numpy's fp32 divide + rint + clamp with the pinned s1."""
+    rng = np.random.default_rng(22)
+    xd = rng.standard_normal((5, 700)) * np.array([[1], [0.01], [300], [1e-30], [1]])
+    xd[4, :] = 0
+    xb = _bf16_bits(xd)
+    xv = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    a8, s1 = orc.quant_act(xb, dtype=1)
+    for m in range(xd.shape[0]):
+        exp_s1 = _rne_bf16_fraction(Fraction(float(np.abs(xv[m]).max())) / 127)
+        assert float(s1[m]) == exp_s1
+        if exp_s1 == 0:
+            assert np.all(a8[m] == 0)
+            continue
+        q = np.rint(xv[m].astype(np.float32) / np.float32(exp_s1))
+        assert np.array_equal(a8[m], np.clip(q, -128, 127).astype(np.int8))
+
+
+def pin_w4a8_bf16_scales(orc):
+    """bf16 s2 / s3: the same exact accumulators as fp16 scales of equal value,
+    and Y64 = acc * s1 * s2 with s2 read as bf16 (brute force in rationals)."""
+    rng = np.random.default_rng(23)
+    for G in (-1, 64):
+        M, K, N = 2, 128, 16
+        a8 = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        q = rng.integers(-8, 8, size=(K, N)).astype(np.int8)
+        b, _ = orc.pack_k8(q)
+        s1 = (rng.random(M) * 0.05 + 0.001).astype(np.float32)
+        s2d = 0.002 + 0.018 * rng.random(N)
+        s2b = _bf16_bits(s2d)
+        s3d = None if G < 0 else rng.integers(1, 17, size=(K // G, N)).astype(np.float64)
+        s3b = None if s3d is None else _bf16_bits(s3d)
+        acc, y = orc.w4a8(a8, b, s1, s2b, s3b, G, dtype=1)
+        acc16, _ = orc.w4a8(a8, b, s1, _f16_bits(s2d), None if s3d is None else _f16_bits(s3d), G)
+        assert np.array_equal(acc, acc16)
+        s2v = torch.from_numpy(s2b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+        for m in range(M):
+            for n in range(N):
+                ref = sum(int(a8[m, k]) * int(q[k, n]) * (1 if s3d is None else int(s3d[k // G, n]))
+                          for k in range(K))
+                assert acc[m, n] == ref
+                exp_y = Fraction(ref) * Fraction(float(s1[m])) * Fraction(float(s2v[n]))
+                assert abs(y[m, n] - float(exp_y)) <= 1e-15 * max(1.0, abs(float(exp_y)))
+
+
 def pin_w4a8_bruteforce(orc):
     rng = np.random.default_rng(10)
     for G in (-1, 32, 64):
@@ -398,7 +516,9 @@ def pin_w4a8_group16_is_channel(orc):
 
 ALL_PINS = [
     pin_golden_words, pin_pair_extraction, pin_k8_masks, pin_roundtrip, pin_pack_clamp,
-    pin_f16_codec, pin_bf16_decode, pin_dequant_exhaustive, pin_w4a16_exact_special,
-    pin_w4a16_bruteforce, pin_w4a16_numpy, pin_w4a16_invariants, pin_quant_examples,
-    pin_quant_s1_exhaustive, pin_quant_random, pin_w4a8_bruteforce, pin_w4a8_group16_is_channel,
+    pin_dequant_exhaustive, pin_w4a16_exact_special, pin_w4a16_numpy, pin_w4a16_invariants,
+    pin_quant_examples, pin_quant_bf16_examples, pin_quant_random, pin_quant_bf16_random,
+    pin_w4a8_bruteforce, pin_w4a8_group16_is_channel, pin_w4a8_bf16_scales, pin_bf16_decode,
+    pin_w4a16_bruteforce, pin_f16_codec, pin_bf16_encode, pin_quant_s1_exhaustive,
+    pin_quant_bf16_s1_exhaustive,
 ]
