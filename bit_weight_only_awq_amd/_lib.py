@@ -55,9 +55,9 @@ def lib() -> ctypes.CDLL:
     w4a16 = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, sz, vp]
     L.awq_gemm_w4a16.argtypes = w4a16
     L.awq_gemv_w4a16.argtypes = w4a16
-    L.w4a8_quant_act.argtypes = [vp, vp, vp, i64, i64, vp]
-    L.w4a8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
-    L.w4a8_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    L.w4a8_quant_act.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    L.w4a8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
+    L.w4a8_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     L.awq_stream_read.argtypes = [vp, i64, vp, vp]
     for f in ("awq_pack", "awq_unpack", "awq_gemm_w4a16", "awq_gemv_w4a16", "w4a8_quant_act", "w4a8_gemm", "w4a8_linear",
               "awq_stream_read"):

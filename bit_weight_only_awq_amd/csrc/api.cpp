@@ -229,7 +229,7 @@ const char *awq_status_str(int status) {
     }
 }
 
-int awq_version(void) { return 100; }
+int awq_version(void) { return 101; }
 
 static int check_pack_shape(int64_t rows, int64_t cols, int layout) {
     if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return AWQ_EINVAL;
@@ -295,17 +295,19 @@ int awq_gemv_w4a16(const void *x, const int32_t *qweight, const void *scales, co
                      workspace_bytes, stream, true);
 }
 
-int w4a8_quant_act(const void *x_f16, int8_t *a8, float *s1, int64_t M, int64_t K, void *stream) {
-    if (!x_f16 || !a8 || !s1) return AWQ_EINVAL;
+int w4a8_quant_act(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, void *stream) {
+    if (!x || !a8 || !s1) return AWQ_EINVAL;
     if (M < 1 || K < 1 || M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 30)) return AWQ_EINVAL;
-    if (!aligned16(x_f16) || !aligned16(a8) || !aligned16(s1)) return AWQ_EALIGN;
-    return hip_status(launch_w4a8_quant(x_f16, a8, s1, M, K, static_cast<hipStream_t>(stream)));
+    if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
+    if (!aligned16(x) || !aligned16(a8) || !aligned16(s1)) return AWQ_EALIGN;
+    return hip_status(launch_w4a8_quant(x, a8, s1, M, K, dtype, static_cast<hipStream_t>(stream)));
 }
 
 int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const void *s2_f16, const void *s3_f16,
-              void *y_f16, int32_t *acc_out, int64_t M, int64_t N, int64_t K, int group_size, void *workspace,
-              size_t workspace_bytes, void *stream) {
+              void *y_f16, int32_t *acc_out, int64_t M, int64_t N, int64_t K, int group_size, int dtype,
+              void *workspace, size_t workspace_bytes, void *stream) {
     if (!a8 || !b_packed || !s1 || !s2_f16 || !y_f16) return AWQ_EINVAL;
+    if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
     if (M < 1 || N < 8 || K < 1 || M > kMaxDim || N > kMaxDim) return AWQ_EINVAL;
     if (N % 8) return AWQ_EINVAL;
     if (group_size == -1) {
@@ -326,13 +328,15 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
         p.acc = static_cast<uint64_t *>(workspace);
     }
     W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
+    a.dtype = dtype;
     return hip_status(launch_w4a8(a, p, static_cast<hipStream_t>(stream)));
 }
 
 int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packed, const void *s2_f16,
                 const void *s3_f16, void *y_f16, int32_t *acc_out, int64_t M, int64_t N, int64_t K, int group_size,
-                void *workspace, size_t workspace_bytes, void *stream) {
+                int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     if (!x_f16 || !a8 || !s1 || !b_packed || !s2_f16 || !y_f16) return AWQ_EINVAL;
+    if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
     if (M < 1 || N < 8 || K < 1 || M > kMaxDim || N > kMaxDim) return AWQ_EINVAL;
     if (N % 8) return AWQ_EINVAL;
     if (group_size == -1) {
@@ -352,12 +356,13 @@ int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packe
     if (p.splits > 1) p.acc = static_cast<uint64_t *>(workspace);
     hipStream_t st = static_cast<hipStream_t>(stream);
     W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
-    if (w4a8_fuses_quant(M, K, p)) {
+    a.dtype = dtype;
+    if (dtype == AWQ_DTYPE_F16 && w4a8_fuses_quant(M, K, p)) {
         a.x = x_f16;
         a.s1_out = s1;
         return hip_status(launch_w4a8_fused(a, p, st));
     }
-    rc = hip_status(launch_w4a8_quant(x_f16, a8, s1, M, K, st));
+    rc = hip_status(launch_w4a8_quant(x_f16, a8, s1, M, K, dtype, st));
     if (rc != AWQ_OK) return rc;
     return hip_status(launch_w4a8(a, p, st));
 }

@@ -123,6 +123,11 @@ __device__ __forceinline__ uint32_t dq_bf16(uint32_t v, uint32_t mask, float s_e
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return bit_as<float>(b << 16); }
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) { return (float)bit_as<f16>((uint16_t)b); }
 
+template <int DT>
+__device__ __forceinline__ float act_bits_to_f32(uint32_t b) {
+    return DT == DT_F16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b);
+}
+
 __device__ __forceinline__ uint16_t f32_to_out_bits(float v, int dt) {
     if (dt == DT_BF16) return bit_as<uint16_t>((__bf16)v);
     return bit_as<uint16_t>((f16)v);

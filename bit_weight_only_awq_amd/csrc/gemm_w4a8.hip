@@ -69,7 +69,7 @@ __device__ __forceinline__ u32x4 b8_operand(uint32_t w0, uint32_t w1, uint32_t s
 // three stages ahead; each stage waits only for the copies older than its
 // own, so the next stage is always readable and its operands are loaded while
 // the current stage's MFMAs run.
-template <bool GROUP>
+template <bool GROUP, int DT>
 __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                        const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                        const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     // group scale of column cl + u from the stage's two s3 rows
     auto group_scales = [&](u32x2 sv, uint32_t (&g3)[4]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) g3[u] = (uint32_t)f16_bits_to_f32((sv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
+        for (int u = 0; u < 4; ++u) g3[u] = (uint32_t)act_bits_to_f32<DT>((sv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu);
     };
     auto load_ops = [&](int slot, Ops &o) {
 #pragma unroll
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     float s2f[4] = {0.f, 0.f, 0.f, 0.f};
     if (col_ok) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s2f[u] = f16_bits_to_f32(s2[nc + u]);
+        for (int u = 0; u < 4; ++u) s2f[u] = act_bits_to_f32<DT>(s2[nc + u]);
     }
     auto store4 = [&](int m, i32x4 accv) {
         const float s1m = s1[m];
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             v[u] = GROUP ? accv[u] : (accv[u] >> 4);
-            o[u] = bit_as<uint16_t>((f16)((float)v[u] * s1m * s2f[u]));
+            o[u] = f32_to_out_bits((float)v[u] * s1m * s2f[u], DT);
         }
         *(u32x2 *)(y + (size_t)m * N + nc) = (u32x2){(uint32_t)o[0] | ((uint32_t)o[1] << 16),
                                                      (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
@@ -290,16 +290,17 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         }
 }
 
-template <bool GROUP>
+template <bool GROUP, int DT>
 static hipError_t launch_lds8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    hipLaunchKernelGGL((w4a8_gemm_lds<GROUP>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
+    hipLaunchKernelGGL((w4a8_gemm_lds<GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
                        (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    return a.s3 != nullptr ? launch_lds8<true>(a, p, st) : launch_lds8<false>(a, p, st);
+    if (a.dtype == DT_BF16) return a.s3 != nullptr ? launch_lds8<true, DT_BF16>(a, p, st) : launch_lds8<false, DT_BF16>(a, p, st);
+    return a.s3 != nullptr ? launch_lds8<true, DT_F16>(a, p, st) : launch_lds8<false, DT_F16>(a, p, st);
 }
 
 }  // namespace awq4

@@ -50,6 +50,7 @@ struct W4A8Args {
     // fused quantisation (w4a8_linear): fp16 activations and the s1 output
     const void *x = nullptr;
     float *s1_out = nullptr;
+    int dtype = 0;  // DT_F16 / DT_BF16: activations, s2, s3 and y
 };
 
 struct W4A8Plan {
@@ -86,7 +87,7 @@ hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
-hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st);
+hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 // skinny W4A8 GEMM with the per-token quantisation fused in (plan kind 0,
 // mt 1); its dynamic LDS and per-wave int8 row area

@@ -24,9 +24,17 @@
 
 namespace awq4 {
 
+// Rounding an fp32 value to the activation type (nearest even) and back.
+template <int DT>
+__device__ __forceinline__ float round_to_act(float v) {
+    return DT == DT_F16 ? (float)(f16)v : (float)(__bf16)v;
+}
+
 // ---------------------------------------------------------------------------
 // Activation quantisation, general form (any K): one workgroup (256 threads)
-// per row, two passes over the row.
+// per row, two passes over the row.  fp16 or bf16 activations (for both,
+// the order of finite magnitudes is the order of the low 15 bits).
+template <int DT>
 __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restrict__ x, int8_t *__restrict__ a8,
                                                          float *__restrict__ s1, int K) {
     __shared__ uint32_t wmax[4];
@@ -50,9 +58,9 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restr
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
     __syncthreads();
     mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
-    const float amax = f16_bits_to_f32(mx);
+    const float amax = act_bits_to_f32<DT>(mx);
     const float q32 = amax / 127.0f;        // correctly rounded fp32 divide
-    const float s = (float)(f16)q32;        // to fp16 (nearest even) and back
+    const float s = round_to_act<DT>(q32);  // to the activation type (nearest even) and back
     if (threadIdx.x == 0) s1[m] = s;
     for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
         u32x4 v = *(const u32x4 *)(row + k);
@@ -61,7 +69,7 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restr
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                float r = rintf(f16_bits_to_f32(h) / s);
+                float r = rintf(act_bits_to_f32<DT>(h) / s);
                 r = fminf(fmaxf(r, -128.0f), 127.0f);
                 o[e >> 2] |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * (e & 3));
             }
@@ -70,7 +78,7 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restr
     }
     for (int k = K8 + threadIdx.x; k < K; k += 256) {
         float r = 0.0f;
-        if (s != 0.0f) r = fminf(fmaxf(rintf(f16_bits_to_f32(row[k]) / s), -128.0f), 127.0f);
+        if (s != 0.0f) r = fminf(fmaxf(rintf(act_bits_to_f32<DT>(row[k]) / s), -128.0f), 127.0f);
         out[k] = (int8_t)r;
     }
 }
@@ -96,7 +104,9 @@ __device__ __forceinline__ uint32_t quant_one(uint32_t h, float s, float r, floa
 // Register-resident quantisation: one workgroup of T threads per row, each
 // thread holding NV chunks of 8 values (row length K <= 8 * NV * T, K % 8 ==
 // 0), so the row is read from memory once.
-template <int NV, int T>
+// fp16 uses the divide-free rounding above; bf16 (whose exactness argument
+// would differ) the correctly rounded fp32 divide.
+template <int DT, int NV, int T>
 __global__ __launch_bounds__(T) void w4a8_quant_rows(const uint16_t *__restrict__ x, int8_t *__restrict__ a8,
                                                      float *__restrict__ s1, int K) {
     __shared__ uint32_t wmax[T / 64];
@@ -119,9 +129,9 @@ __global__ __launch_bounds__(T) void w4a8_quant_rows(const uint16_t *__restrict_
     mx = wmax[0];
 #pragma unroll
     for (int w = 1; w < T / 64; ++w) mx = max(mx, wmax[w]);
-    const float amax = f16_bits_to_f32(mx);
-    const float q32 = amax / 127.0f;  // correctly rounded fp32 divide, once per row
-    const float s = (float)(f16)q32;  // to fp16 (nearest even) and back
+    const float amax = act_bits_to_f32<DT>(mx);
+    const float q32 = amax / 127.0f;       // correctly rounded fp32 divide, once per row
+    const float s = round_to_act<DT>(q32);  // to the activation type (nearest even) and back
     if (threadIdx.x == 0) s1[m] = s;
     const float r = __builtin_amdgcn_rcpf(s), hs = 0.5f * s;
 #pragma unroll
@@ -131,42 +141,61 @@ __global__ __launch_bounds__(T) void w4a8_quant_rows(const uint16_t *__restrict_
         u32x2 o = {0, 0};
         if (s != 0.0f) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                o[e >> 2] |= quant_one((v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu, s, r, hs) << (8 * (e & 3));
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t h = (v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                uint32_t q;
+                if (DT == DT_F16) {
+                    q = quant_one(h, s, r, hs);
+                } else {
+                    const float qf = fminf(fmaxf(rintf(act_bits_to_f32<DT>(h) / s), -128.0f), 127.0f);
+                    q = (uint32_t)(int32_t)qf & 0xFFu;
+                }
+                o[e >> 2] |= q << (8 * (e & 3));
+            }
         }
         *(u32x2 *)(out + k) = o;
     }
 }
 
 template <int NV, int T>
-static hipError_t launch_quant_rows(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st) {
-    hipLaunchKernelGGL((w4a8_quant_rows<NV, T>), dim3((unsigned)M), dim3(T), 0, st, (const uint16_t *)x, a8, s1,
-                       (int)K);
+static hipError_t launch_quant_rows(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dt,
+                                    hipStream_t st) {
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL((w4a8_quant_rows<DT_BF16, NV, T>), dim3((unsigned)M), dim3(T), 0, st, (const uint16_t *)x,
+                           a8, s1, (int)K);
+    else
+        hipLaunchKernelGGL((w4a8_quant_rows<DT_F16, NV, T>), dim3((unsigned)M), dim3(T), 0, st, (const uint16_t *)x,
+                           a8, s1, (int)K);
     return hipGetLastError();
 }
 
-hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, hipStream_t st) {
+hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dt, hipStream_t st) {
     if (K % 8 == 0) {
         if (K <= 8 * 256 * 4) {
             switch ((K + 2047) / 2048) {
-                case 1: return launch_quant_rows<1, 256>(x, a8, s1, M, K, st);
-                case 2: return launch_quant_rows<2, 256>(x, a8, s1, M, K, st);
-                case 3: return launch_quant_rows<3, 256>(x, a8, s1, M, K, st);
-                default: return launch_quant_rows<4, 256>(x, a8, s1, M, K, st);
+                case 1: return launch_quant_rows<1, 256>(x, a8, s1, M, K, dt, st);
+                case 2: return launch_quant_rows<2, 256>(x, a8, s1, M, K, dt, st);
+                case 3: return launch_quant_rows<3, 256>(x, a8, s1, M, K, dt, st);
+                default: return launch_quant_rows<4, 256>(x, a8, s1, M, K, dt, st);
             }
         }
         if (K <= 8 * 1024 * 16) {
             const int64_t nv = (K + 8191) / 8192;
-            if (nv <= 2) return launch_quant_rows<2, 1024>(x, a8, s1, M, K, st);
-            if (nv <= 3) return launch_quant_rows<3, 1024>(x, a8, s1, M, K, st);
-            if (nv <= 4) return launch_quant_rows<4, 1024>(x, a8, s1, M, K, st);
-            if (nv <= 6) return launch_quant_rows<6, 1024>(x, a8, s1, M, K, st);
-            if (nv <= 8) return launch_quant_rows<8, 1024>(x, a8, s1, M, K, st);
-            if (nv <= 12) return launch_quant_rows<12, 1024>(x, a8, s1, M, K, st);
-            return launch_quant_rows<16, 1024>(x, a8, s1, M, K, st);
+            if (nv <= 2) return launch_quant_rows<2, 1024>(x, a8, s1, M, K, dt, st);
+            if (nv <= 3) return launch_quant_rows<3, 1024>(x, a8, s1, M, K, dt, st);
+            if (nv <= 4) return launch_quant_rows<4, 1024>(x, a8, s1, M, K, dt, st);
+            if (nv <= 6) return launch_quant_rows<6, 1024>(x, a8, s1, M, K, dt, st);
+            if (nv <= 8) return launch_quant_rows<8, 1024>(x, a8, s1, M, K, dt, st);
+            if (nv <= 12) return launch_quant_rows<12, 1024>(x, a8, s1, M, K, dt, st);
+            return launch_quant_rows<16, 1024>(x, a8, s1, M, K, dt, st);
         }
     }
-    hipLaunchKernelGGL(w4a8_quant_kernel, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a8, s1, (int)K);
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(w4a8_quant_kernel<DT_BF16>, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a8, s1,
+                           (int)K);
+    else
+        hipLaunchKernelGGL(w4a8_quant_kernel<DT_F16>, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a8, s1,
+                           (int)K);
     return hipGetLastError();
 }
 
@@ -195,27 +224,29 @@ __device__ __forceinline__ u32x4 make_b8(uint32_t w0, uint32_t w1, uint32_t s3) 
     return b;
 }
 
+template <int DT>
 __device__ __forceinline__ uint32_t s3_int(const uint16_t *__restrict__ s3, size_t idx) {
-    return (uint32_t)f16_bits_to_f32(s3[idx]);
+    return (uint32_t)act_bits_to_f32<DT>(s3[idx]);
 }
 
-// Final value of one output: undo the x16 of per-channel weights, scale, store.
-template <bool GROUP>
+// Final value of one output: undo the x16 of per-channel weights, scale, store
+// (s2 and y in the activation type).
+template <bool GROUP, int DT>
 __device__ __forceinline__ void w4a8_store_s(int32_t acc, int m, int n, int N, float s1m,
                                              const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
                                              int32_t *__restrict__ acc_out) {
     const int32_t a = GROUP ? acc : (acc >> 4);  // exact: per-channel acc is a multiple of 16
-    const float v = (float)a * s1m * f16_bits_to_f32(s2[n]);
-    y[(size_t)m * N + n] = bit_as<uint16_t>((f16)v);
+    const float v = (float)a * s1m * act_bits_to_f32<DT>(s2[n]);
+    y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
     if (acc_out) acc_out[(size_t)m * N + n] = a;
 }
-template <bool GROUP>
+template <bool GROUP, int DT>
 __device__ __forceinline__ void w4a8_store(int32_t acc, int m, int n, int N, const float *__restrict__ s1,
                                            const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
                                            int32_t *__restrict__ acc_out) {
     const int32_t a = GROUP ? acc : (acc >> 4);  // exact: per-channel acc is a multiple of 16
-    const float v = (float)a * s1[m] * f16_bits_to_f32(s2[n]);
-    y[(size_t)m * N + n] = bit_as<uint16_t>((f16)v);
+    const float v = (float)a * s1[m] * act_bits_to_f32<DT>(s2[n]);
+    y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
     if (acc_out) acc_out[(size_t)m * N + n] = a;
 }
 
@@ -235,7 +266,7 @@ __device__ __forceinline__ void w4a8_store(int32_t acc, int m, int n, int N, con
 // Workgroup (0, 0) writes s1.  Dynamic LDS: the reduction area, then 32 row
 // maxima and 32 scales, then per wave `qa_stride` bytes of int8 rows laid out
 // [step][row][64].
-template <int BLK, int MT, bool GROUP, bool FUSED>
+template <int BLK, int MT, bool GROUP, bool FUSED, int DT>
 __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8, const uint16_t *__restrict__ x16,
                                                    const uint32_t *__restrict__ bq,
                                                    const float *__restrict__ s1, float *__restrict__ s1_out,
@@ -344,7 +375,7 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
             if (GROUP && ok[b]) {
                 const size_t gi = (size_t)(k0 / G) * N + ncol[b];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) g3[i] = s3_int(s3, gi + i);
+                for (int i = 0; i < 4; ++i) g3[i] = s3_int<DT>(s3, gi + i);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -384,11 +415,11 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
         int64_t sum;
         const float s1m = FUSED ? srow[m] : s1[m];
         if (S == 1)
-            w4a8_store_s<GROUP>(v, m, n, N, s1m, s2, y, acc_out);
+            w4a8_store_s<GROUP, DT>(v, m, n, N, s1m, s2, y, acc_out);
         else if (tilered)
             part[split * slot + (size_t)m * N + n] = v;
         else if (splitk_contribute(&acc64[(size_t)m * N + n], v, S, &sum))
-            w4a8_store_s<GROUP>((int32_t)sum, m, n, N, s1m, s2, y, acc_out);
+            w4a8_store_s<GROUP, DT>((int32_t)sum, m, n, N, s1m, s2, y, acc_out);
     }
     if (S == 1 || !tilered || !split_tile_last(cnt, S)) return;
     for (int idx = threadIdx.x; idx < total; idx += 256) {
@@ -401,14 +432,14 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
             v += *src;
             *src = 0;
         }
-        w4a8_store_s<GROUP>(v, m, n, N, FUSED ? srow[m] : s1[m], s2, y, acc_out);
+        w4a8_store_s<GROUP, DT>(v, m, n, N, FUSED ? srow[m] : s1[m], s2, y, acc_out);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Tiled W4A8 kernel: 2 x 2 waves, wave tile (16*MTW) x 64, workgroup tile
 // (32*MTW) x 128; split-K over grid z.
-template <int MTW, bool GROUP>
+template <int MTW, bool GROUP, int DT>
 __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                   const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                   const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
@@ -455,7 +486,7 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
         if (GROUP && ok) {
             const size_t gi = (size_t)(k0 / G) * N + ncol;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) g3[i] = s3_int(s3, gi + i);
+            for (int i = 0; i < 4; ++i) g3[i] = s3_int<DT>(s3, gi + i);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -474,7 +505,7 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
                 const int m = m0 + 16 * mt + 4 * gq + r;
                 if (m < M) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w4a8_store<GROUP>(acc[mt][i][r], m, ncol + i, N, s1, s2, y, acc_out);
+                    for (int i = 0; i < 4; ++i) w4a8_store<GROUP, DT>(acc[mt][i][r], m, ncol + i, N, s1, s2, y, acc_out);
                 }
             }
         return;
@@ -509,7 +540,7 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
                 *src = (i32x4){0, 0, 0, 0};
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w4a8_store<GROUP>(v[i], m, ncol + i, N, s1, s2, y, acc_out);
+            for (int i = 0; i < 4; ++i) w4a8_store<GROUP, DT>(v[i], m, ncol + i, N, s1, s2, y, acc_out);
         }
 }
 
@@ -525,51 +556,61 @@ size_t w4a8_fused_lds_bytes(int64_t M, int64_t K, int blk, int splits) {
            4 * (size_t)w4a8_fused_qa_stride(M, K, splits);
 }
 
-template <int BLK, int MT, bool GROUP, bool FUSED>
+template <int BLK, int MT, bool GROUP, bool FUSED, int DT>
 static hipError_t launch_skinny8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     const int qa_stride = FUSED ? (int)w4a8_fused_qa_stride(a.M, a.K, p.splits) : 0;
     const size_t lds = FUSED ? w4a8_fused_lds_bytes(a.M, a.K, BLK, p.splits)
                              : (size_t)4 * a.M * 64 * BLK * sizeof(int32_t) + 64 * sizeof(uint32_t);
-    hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP, FUSED>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
+    hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP, FUSED, DT>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
                        (const uint16_t *)a.x, (const uint32_t *)a.b, a.s1, a.s1_out, (const uint16_t *)a.s2,
                        (const uint16_t *)a.s3, (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K,
                        a.G, p.splits, qa_stride, p.tilered);
     return hipGetLastError();
 }
 
-template <int MTW, bool GROUP>
+template <int MTW, bool GROUP, int DT>
 static hipError_t launch_tiled8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    hipLaunchKernelGGL((w4a8_tiled<MTW, GROUP>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
+    hipLaunchKernelGGL((w4a8_tiled<MTW, GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
                        (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G,
                        p.splits);
     return hipGetLastError();
 }
 
-hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    if (p.kind == 2) return launch_w4a8_gemm_lds(a, p, st);
-    const bool grp = a.s3 != nullptr;
+template <bool GROUP, int DT>
+static hipError_t launch_w4a8_t(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     if (p.kind == 0) {
         switch (p.blk * 10 + p.mt) {
-            case 11: return grp ? launch_skinny8<1, 1, true, false>(a, p, st) : launch_skinny8<1, 1, false, false>(a, p, st);
-            case 21: return grp ? launch_skinny8<2, 1, true, false>(a, p, st) : launch_skinny8<2, 1, false, false>(a, p, st);
-            case 12: return grp ? launch_skinny8<1, 2, true, false>(a, p, st) : launch_skinny8<1, 2, false, false>(a, p, st);
+            case 11: return launch_skinny8<1, 1, GROUP, false, DT>(a, p, st);
+            case 21: return launch_skinny8<2, 1, GROUP, false, DT>(a, p, st);
+            case 12: return launch_skinny8<1, 2, GROUP, false, DT>(a, p, st);
             default: return hipErrorInvalidValue;
         }
     }
     switch (p.mt) {
-        case 1: return grp ? launch_tiled8<1, true>(a, p, st) : launch_tiled8<1, false>(a, p, st);
-        case 2: return grp ? launch_tiled8<2, true>(a, p, st) : launch_tiled8<2, false>(a, p, st);
-        case 4: return grp ? launch_tiled8<4, true>(a, p, st) : launch_tiled8<4, false>(a, p, st);
+        case 1: return launch_tiled8<1, GROUP, DT>(a, p, st);
+        case 2: return launch_tiled8<2, GROUP, DT>(a, p, st);
+        case 4: return launch_tiled8<4, GROUP, DT>(a, p, st);
         default: return hipErrorInvalidValue;
     }
 }
 
+hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    if (p.kind == 2) return launch_w4a8_gemm_lds(a, p, st);
+    const bool grp = a.s3 != nullptr;
+    if (a.dtype == DT_BF16)
+        return grp ? launch_w4a8_t<true, DT_BF16>(a, p, st) : launch_w4a8_t<false, DT_BF16>(a, p, st);
+    return grp ? launch_w4a8_t<true, DT_F16>(a, p, st) : launch_w4a8_t<false, DT_F16>(a, p, st);
+}
+
+// The fused quantisation is the fp16 activations' (its divide-free rounding
+// is checked for fp16 only); bf16 layers take the two-launch path.
 hipError_t launch_w4a8_fused(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     const bool grp = a.s3 != nullptr;
-    if (p.kind != 0 || p.mt != 1) return hipErrorInvalidValue;
-    if (p.blk == 2) return grp ? launch_skinny8<2, 1, true, true>(a, p, st) : launch_skinny8<2, 1, false, true>(a, p, st);
-    return grp ? launch_skinny8<1, 1, true, true>(a, p, st) : launch_skinny8<1, 1, false, true>(a, p, st);
+    if (p.kind != 0 || p.mt != 1 || a.dtype != DT_F16) return hipErrorInvalidValue;
+    if (p.blk == 2)
+        return grp ? launch_skinny8<2, 1, true, true, DT_F16>(a, p, st) : launch_skinny8<2, 1, false, true, DT_F16>(a, p, st);
+    return grp ? launch_skinny8<1, 1, true, true, DT_F16>(a, p, st) : launch_skinny8<1, 1, false, true, DT_F16>(a, p, st);
 }
 
 }  // namespace awq4

@@ -134,32 +134,36 @@ def linear_w4a16(x, qweight, scales, qzeros, group_size: int = 128, out=None):
 # ----------------------------------------------------------------------------- W4A8
 
 def quant_act(x: torch.Tensor, a8: torch.Tensor | None = None, s1: torch.Tensor | None = None):
-    """Per-token int8 quantisation of fp16 activations -> (a8 int8 [M,K], s1 fp32 [M])."""
+    """Per-token int8 quantisation of fp16 or bf16 activations -> (a8 int8 [M,K], s1 fp32 [M])."""
     _need_cuda(x, a8, s1)
-    if x.dtype != torch.float16:
-        raise ValueError("W4A8 activations must be fp16")
+    if x.dtype not in _F16:
+        raise ValueError("W4A8 activations must be fp16 or bf16")
     M, K = x.shape
     if a8 is None:
         a8 = torch.empty(M, K, dtype=torch.int8, device=x.device)
     if s1 is None:
         s1 = torch.empty(M, dtype=torch.float32, device=x.device)
-    L.check("w4a8_quant_act", L.lib().w4a8_quant_act(_ptr(x), _ptr(a8), _ptr(s1), M, K, _stream(x.device)))
+    L.check("w4a8_quant_act", L.lib().w4a8_quant_act(_ptr(x), _ptr(a8), _ptr(s1), M, K, _F16[x.dtype],
+                                                     _stream(x.device)))
     return a8, s1
 
 
 def w4a8_gemm(a8, b, s1, s2, s3=None, group_size: int = -1, want_acc: bool = False, out=None):
-    """y = fp16(acc * s1 * s2), acc = a8 . w8 (exact int32). Returns y or (y, acc)."""
+    """y = act(acc * s1 * s2), acc = a8 . w8 (exact int32), in the dtype of s2
+    (fp16 or bf16; s3 and y share it). Returns y or (y, acc)."""
     _need_cuda(a8, b, s1, s2, s3, out)
+    if s2.dtype not in _F16 or (s3 is not None and s3.dtype != s2.dtype):
+        raise ValueError("W4A8 scales must be fp16 or bf16, s2 and s3 alike")
     M, K = a8.shape
     N = b.shape[1]
     if out is None:
-        out = torch.empty(M, N, dtype=torch.float16, device=a8.device)
+        out = torch.empty(M, N, dtype=s2.dtype, device=a8.device)
     acc = torch.empty(M, N, dtype=torch.int32, device=a8.device) if want_acc else None
     need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size)
     ws = WORKSPACE.get(a8.device, need)
     L.check("w4a8_gemm", L.lib().w4a8_gemm(_ptr(a8), _ptr(b), _ptr(s1), _ptr(s2), _ptr(s3), _ptr(out), _ptr(acc),
-                                           M, N, K, group_size, _ptr(ws), 0 if ws is None else ws.numel(),
-                                           _stream(a8.device)))
+                                           M, N, K, group_size, _F16[s2.dtype], _ptr(ws),
+                                           0 if ws is None else ws.numel(), _stream(a8.device)))
     return (out, acc) if want_acc else out
 
 
@@ -168,8 +172,8 @@ def linear_w4a8(x, b, s2, s3=None, group_size: int = -1, want_acc: bool = False,
     x, then the W4A8 GEMM, fused into one kernel for small batches.  Returns y,
     or (y, s1, acc) with want_acc.  `a8` is scratch for the two-step path."""
     _need_cuda(x, b, s2, s3, out, a8, s1)
-    if x.dtype != torch.float16:
-        raise ValueError("W4A8 activations must be fp16")
+    if x.dtype not in _F16 or s2.dtype != x.dtype or (s3 is not None and s3.dtype != x.dtype):
+        raise ValueError("W4A8 activations and scales must be fp16 or bf16, all of one type")
     M, K = x.shape
     N = b.shape[1]
     if a8 is None:
@@ -177,12 +181,12 @@ def linear_w4a8(x, b, s2, s3=None, group_size: int = -1, want_acc: bool = False,
     if s1 is None:
         s1 = torch.empty(M, dtype=torch.float32, device=x.device)
     if out is None:
-        out = torch.empty(M, N, dtype=torch.float16, device=x.device)
+        out = torch.empty(M, N, dtype=x.dtype, device=x.device)
     acc = torch.empty(M, N, dtype=torch.int32, device=x.device) if want_acc else None
     need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size)
     ws = WORKSPACE.get(x.device, need)
     L.check("w4a8_linear", L.lib().w4a8_linear(_ptr(x), _ptr(a8), _ptr(s1), _ptr(b), _ptr(s2), _ptr(s3), _ptr(out),
-                                               _ptr(acc), M, N, K, group_size, _ptr(ws),
+                                               _ptr(acc), M, N, K, group_size, _F16[x.dtype], _ptr(ws),
                                                0 if ws is None else ws.numel(), _stream(x.device)))
     return (out, s1, acc) if want_acc else out
 

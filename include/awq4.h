@@ -163,55 +163,60 @@ int awq_gemv_w4a16(const void *x, const int32_t *qweight, const void *scales,
                    size_t workspace_bytes, void *stream);
 
 /*
- * w4a8_quant_act -- dynamic per-token int8 quantisation of fp16 activations
+ * w4a8_quant_act -- dynamic per-token int8 quantisation of activations
  * ([P5], the dynamic_quant helper):
- *   s1[m]   = float( fp16( max_k |x[m,k]| / 127 ) )
+ *   s1[m]   = float( act( max_k |x[m,k]| / 127 ) )
  *   a8[m,k] = clamp( round_half_even( float(x[m,k]) / s1[m] ), -128, 127 )
- * with a correctly rounded fp32 divide; a row whose s1 is 0 gives a8 = 0.
- *   x: device fp16 [M, K]; a8: device int8 [M, K]; s1: device fp32 [M].
- * Errors: AWQ_EINVAL (M, K < 1, pointers), AWQ_EALIGN, AWQ_EHIP.
+ * with a correctly rounded fp32 divide; act() rounds to the activation type
+ * (nearest even); a row whose s1 is 0 gives a8 = 0.  [P5] defines the fp16
+ * form and lists bf16 as not yet supported; for bf16 this library takes the
+ * same recipe with the quotient rounded to bf16.
+ *   x: device fp16 or bf16 [M, K] (dtype AWQ_DTYPE_F16 / AWQ_DTYPE_BF16);
+ *   a8: device int8 [M, K]; s1: device fp32 [M].
+ * Errors: AWQ_EINVAL (M, K < 1, pointers, dtype), AWQ_EALIGN, AWQ_EHIP.
  */
-int w4a8_quant_act(const void *x_f16, int8_t *a8, float *s1, int64_t M, int64_t K, void *stream);
+int w4a8_quant_act(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, void *stream);
 
 /*
  * w4a8_gemm -- QQQ-style W4A8 GEMM ([P5]):
  *   acc[m,n] = sum_k a8[m,k] * w8[k,n]   (exact, int32)
- *   y[m,n]   = fp16( acc[m,n] * s1[m] * s2[n] )   (fp32 arithmetic, RNE)
+ *   y[m,n]   = act( acc[m,n] * s1[m] * s2[n] )   (fp32 arithmetic, RNE)
  * with w8 = q for per-channel weights (s3 == NULL, group_size == -1) and
  * w8 = q * s3[k/G, n] for per-group weights, where s3 holds small integers
- * 1..16 stored as fp16 so that w8 stays an int8.
+ * 1..16 so that w8 stays an int8.  s2, s3 and y are in the activation type
+ * `dtype` (AWQ_DTYPE_F16 or AWQ_DTYPE_BF16; acc does not depend on it).
  *   a8:       device int8 [M, K] (from w4a8_quant_act).
  *   b_packed: device int32 [K/8, N], W4A8_LAYOUT_K8 (q in -8..7).
- *   s1:       device fp32 [M];  s2: device fp16 [N];  s3: device fp16 [K/G, N] or NULL.
- *   y:        device fp16 [M, N].
+ *   s1:       device fp32 [M];  s2: device [N];  s3: device [K/G, N] or NULL.
+ *   y:        device [M, N].
  *   acc_out:  device int32 [M, N] or NULL: if given, the exact accumulators
  *             are written too (for checking).
  *   K % 64 == 0; N % 8 == 0; group_size -1 (per-channel) or one of 32, 64, 128.
- * Errors: AWQ_EINVAL, AWQ_EALIGN, AWQ_EWORKSPACE, AWQ_EUNSUPPORTED
- * (K % 64 != 0), AWQ_EHIP.
+ * Errors: AWQ_EINVAL (also an unknown dtype), AWQ_EALIGN, AWQ_EWORKSPACE,
+ * AWQ_EUNSUPPORTED (K % 64 != 0), AWQ_EHIP.
  */
-int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const void *s2_f16,
-              const void *s3_f16, void *y_f16, int32_t *acc_out, int64_t M, int64_t N,
-              int64_t K, int group_size, void *workspace, size_t workspace_bytes, void *stream);
+int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const void *s2,
+              const void *s3, void *y, int32_t *acc_out, int64_t M, int64_t N,
+              int64_t K, int group_size, int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * w4a8_linear -- the whole W4A8 layer in one call: w4a8_quant_act of x
  * followed by w4a8_gemm, with identical results (y, s1 and acc_out bit for
  * bit).  The pages note that quantising activations in a separate kernel
- * costs performance ([P5]); for a single token (M == 1, K <= 32768) the
+ * costs performance ([P5]); for a single fp16 token (M == 1, K <= 32768) the
  * quantisation runs inside the GEMM kernel: every workgroup reads the
  * activation row, derives s1 and quantises its own K range into LDS, so the
  * int8 activations never travel through device memory and there is one
- * launch.  Otherwise the two steps run back to back.
- *   x:   device fp16 [M, K].
+ * launch.  Otherwise (bf16 included) the two steps run back to back.
+ *   x:   device fp16 or bf16 [M, K] (dtype).
  *   a8:  device int8 [M, K], scratch: holds the quantised activations when
  *        the two-step path runs, left untouched by the fused path.
  *   s1:  device fp32 [M], written (the per-token scales).
  *   other arguments, layouts, workspace and errors: as w4a8_gemm.
  */
-int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packed,
-                const void *s2_f16, const void *s3_f16, void *y_f16, int32_t *acc_out,
-                int64_t M, int64_t N, int64_t K, int group_size, void *workspace,
+int w4a8_linear(const void *x, int8_t *a8, float *s1, const int32_t *b_packed,
+                const void *s2, const void *s3, void *y, int32_t *acc_out,
+                int64_t M, int64_t N, int64_t K, int group_size, int dtype, void *workspace,
                 size_t workspace_bytes, void *stream);
 
 /*

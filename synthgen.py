@@ -86,29 +86,31 @@ def activations_on(device, M: int, K: int, dtype: str = "f16", seed: int = 0) ->
 
 @dataclass
 class W4A8Case:
-    x: torch.Tensor        # [M, K] fp16 activations (quantised per token by the method)
+    x: torch.Tensor        # [M, K] fp16 / bf16 activations (quantised per token by the method)
     b: torch.Tensor        # [K/8, N] int32, K-packed two's-complement int4
-    s2: torch.Tensor       # [N] fp16 per-output-channel scale
-    s3: torch.Tensor | None  # [K/G, N] fp16 integer group scales 1..16, None = per-channel
+    s2: torch.Tensor       # [N] per-output-channel scale, in the activation type
+    s3: torch.Tensor | None  # [K/G, N] integer group scales 1..16 (activation type), None = per-channel
     M: int
     K: int
     N: int
     G: int
     seed: int
+    dtype: str = "f16"
 
 
 def w4a8_case(M: int, K: int, N: int, G: int = -1, seed: int | None = None,
-              x_rows: int | None = None) -> W4A8Case:
+              x_rows: int | None = None, dtype: str = "f16") -> W4A8Case:
     if seed is None:
-        seed = seed_for(case_key("w4a8", M, K, N, G))
+        seed = seed_for(case_key("w4a8", M, K, N, G) if dtype == "f16" else case_key("w4a8", M, K, N, G, dtype))
+    dt = _DT[dtype]
     g = torch.Generator().manual_seed(seed)
     b = _words(g, (K // 8, N))
-    s = (0.002 + 0.018 * torch.rand(N, generator=g, dtype=torch.float32)).to(torch.float16)
+    s = (0.002 + 0.018 * torch.rand(N, generator=g, dtype=torch.float32)).to(dt)
     if G > 0:
-        s3 = torch.randint(1, 17, (K // G, N), generator=g, dtype=torch.int64).to(torch.float16)
-        s2 = s / 16  # a power-of-two division: exact in fp16 for this range
+        s3 = torch.randint(1, 17, (K // G, N), generator=g, dtype=torch.int64).to(dt)
+        s2 = s / 16  # a power-of-two division: exact in fp16 and bf16 for this range
     else:
         s3 = None
         s2 = s
-    x = torch.randn(M if x_rows is None else x_rows, K, generator=g, dtype=torch.float32).to(torch.float16)
-    return W4A8Case(x, b, s2, s3, M, K, N, G, seed)
+    x = torch.randn(M if x_rows is None else x_rows, K, generator=g, dtype=torch.float32).to(dt)
+    return W4A8Case(x, b, s2, s3, M, K, N, G, seed, dtype)

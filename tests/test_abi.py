@@ -39,7 +39,7 @@ def test_status_strings():
         s = lib.awq_status_str(code).decode()
         assert s.startswith("AWQ_")
     assert lib.awq_status_str(12345).decode() == "AWQ_UNKNOWN"
-    assert lib.awq_version() == 100
+    assert lib.awq_version() == 101
 
 
 # Fake "device" pointers: validation only looks at null-ness and alignment, and
@@ -114,8 +114,8 @@ def test_workspace_bytes():
 def test_w4a8_validation():
     lib = L.lib()
 
-    def g(a8=A, b=A, s1=A, s2=A, s3=None, y=A, acc=None, M=1, N=8192, K=21760, G=-1, ws=None, wsb=0):
-        return lib.w4a8_gemm(a8, b, s1, s2, s3, y, acc, M, N, K, G, ws, wsb, None)
+    def g(a8=A, b=A, s1=A, s2=A, s3=None, y=A, acc=None, M=1, N=8192, K=21760, G=-1, dt=0, ws=None, wsb=0):
+        return lib.w4a8_gemm(a8, b, s1, s2, s3, y, acc, M, N, K, G, dt, ws, wsb, None)
 
     assert g(a8=None) == L.AWQ_EINVAL
     assert g(s2=None) == L.AWQ_EINVAL
@@ -127,16 +127,20 @@ def test_w4a8_validation():
     assert g(K=262144) == L.AWQ_EUNSUPPORTED   # int32 accumulator bound
     assert g(acc=MIS) == L.AWQ_EALIGN
     assert g() == L.AWQ_EWORKSPACE             # decode split needs a workspace
-    assert lib.w4a8_quant_act(None, A, A, 1, 16, None) == L.AWQ_EINVAL
-    assert lib.w4a8_quant_act(A, A, A, 0, 16, None) == L.AWQ_EINVAL
-    assert lib.w4a8_quant_act(MIS, A, A, 1, 16, None) == L.AWQ_EALIGN
+    assert g(dt=1) == L.AWQ_EWORKSPACE         # bf16 scales and output: same rules
+    assert g(dt=2) == L.AWQ_EINVAL             # unknown dtype
+    assert lib.w4a8_quant_act(None, A, A, 1, 16, 0, None) == L.AWQ_EINVAL
+    assert lib.w4a8_quant_act(A, A, A, 0, 16, 0, None) == L.AWQ_EINVAL
+    assert lib.w4a8_quant_act(A, A, A, 1, 16, 2, None) == L.AWQ_EINVAL
+    assert lib.w4a8_quant_act(MIS, A, A, 1, 16, 0, None) == L.AWQ_EALIGN
+    assert lib.w4a8_quant_act(MIS, A, A, 1, 16, 1, None) == L.AWQ_EALIGN
 
 
 def test_w4a8_linear_validation():
     lib = L.lib()
 
-    def f(x=A, a8=A, s1=A, b=A, s2=A, s3=None, y=A, acc=None, M=1, N=8192, K=21760, G=-1, ws=None, wsb=0):
-        return lib.w4a8_linear(x, a8, s1, b, s2, s3, y, acc, M, N, K, G, ws, wsb, None)
+    def f(x=A, a8=A, s1=A, b=A, s2=A, s3=None, y=A, acc=None, M=1, N=8192, K=21760, G=-1, dt=0, ws=None, wsb=0):
+        return lib.w4a8_linear(x, a8, s1, b, s2, s3, y, acc, M, N, K, G, dt, ws, wsb, None)
 
     assert f(x=None) == L.AWQ_EINVAL
     assert f(a8=None) == L.AWQ_EINVAL          # scratch for the two-step path is required
@@ -149,6 +153,8 @@ def test_w4a8_linear_validation():
     assert f(x=MIS) == L.AWQ_EALIGN
     assert f(s1=MIS) == L.AWQ_EALIGN
     assert f() == L.AWQ_EWORKSPACE             # the decode split needs a workspace
+    assert f(dt=1) == L.AWQ_EWORKSPACE
+    assert f(dt=-1) == L.AWQ_EINVAL            # unknown dtype
 
 
 def test_pack_validation():
