@@ -396,19 +396,29 @@ def main():
             dense[name] = {"K": K, "N": N, "us": round(t * 1e6, 2),
                            "TFLOPs": round(2 * M_PREFILL * N * K / t / 1e12, 1)}
             del xd, wd, yd
-    w8_res = {}
-    for i, (M, *_r) in enumerate(w8a):
-        tq = per_launch(lambda i=i: [awq.quant_act(w8a[i][1], w8a[i][2], w8a[i][3]) for _ in range(4)], 4)
-        tg = per_launch(lambda i=i: [awq.w4a8_gemm(w8a[i][2], w8w[r][0], w8a[i][3], w8w[r][1], out=w8a[i][4])
-                                     for r in range(w8_copies)], w8_copies)
-        tl = per_launch(lambda i=i: [run_w4a8(r, [i]) for r in range(w8_copies)], w8_copies)
+    def w4a8_times(M, x, a8, s1, y, s2s, fused):
+        tq = per_launch(lambda: [awq.quant_act(x, a8, s1) for _ in range(4)], 4)
+        tg = per_launch(lambda: [awq.w4a8_gemm(a8, w8w[r][0], s1, s2s[r], out=y) for r in range(w8_copies)],
+                        w8_copies)
+        tl = per_launch(lambda: [awq.linear_w4a8(x, w8w[r][0], s2s[r], out=y, a8=a8, s1=s1)
+                                 for r in range(w8_copies)], w8_copies)
         ops = 2 * M * W4A8_N * W4A8_K
-        w8_res[f"M={M}"] = {"layer_us": round(tl * 1e6, 2), "fused_quant": M == 1,
-                            "quant_us": round(tq * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
-                            "gemm_TOPs": round(ops / tg / 1e12, 2),
-                            "gemm_weight_GBs": round((W4A8_K * W4A8_N // 2 + 2 * W4A8_N) / tg / 1e9, 1),
-                            "frac_hbm": round(w4a8_alg_bytes(M, W4A8_K, W4A8_N) / tg / 1e9 / HBM_PEAK_GBS, 4),
-                            "frac_i8_mfma": round(ops / tg / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
+        return {"layer_us": round(tl * 1e6, 2), "fused_quant": fused,
+                "quant_us": round(tq * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
+                "gemm_TOPs": round(ops / tg / 1e12, 2),
+                "gemm_weight_GBs": round((W4A8_K * W4A8_N // 2 + 2 * W4A8_N) / tg / 1e9, 1),
+                "frac_hbm": round(w4a8_alg_bytes(M, W4A8_K, W4A8_N) / tg / 1e9 / HBM_PEAK_GBS, 4),
+                "frac_i8_mfma": round(ops / tg / 1e12 / MFMA_I8_PEAK_TOPS, 4)}
+
+    w8_res = {f"M={M}": w4a8_times(M, x, a8, s1, y, [s2 for _, s2 in w8w], M == 1) for M, x, a8, s1, y in w8a}
+    # the same layers with bf16 activations, scales and output: the fused
+    # quantise-and-GEMM kernel is fp16 only, so every M takes the two steps
+    s2_bf = [s2.to(torch.bfloat16) for _, s2 in w8w]
+    w8_bf = {}
+    for M, x, a8, s1, _y in w8a:
+        w8_bf[f"M={M}"] = w4a8_times(M, x.to(torch.bfloat16), a8, s1,
+                                     torch.empty(M, W4A8_N, dtype=torch.bfloat16, device=dev), s2_bf, False)
+    del s2_bf
 
     # achievable read rate at each decode layer's byte count: the bandwidth probe
     # streaming the same packed-weight tensors (same rotation)
@@ -468,6 +478,7 @@ def main():
                           "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "per_layer": pre_layer},
            "w4a8_n8192_k21760": w8_res,
+           "w4a8_bf16_n8192_k21760": w8_bf,
            "comparator_dense_fp16_m2048": {"note": "vendor dense fp16 GEMM (hipBLASLt via torch.matmul) on "
                                                    "pre-dequantised weights; context, not a library path",
                                            **dense},
