@@ -16,6 +16,10 @@ namespace awq4 {
 
 static constexpr int64_t kMaxDim = int64_t(1) << 20;
 static constexpr int kTargetWorkgroups = 512;  // 256 CUs x 2 workgroups of 4 waves
+// The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, one per CU) are used
+// when they make one nearly full round on the 256 CUs; past one round the
+// 128 x 128 tiles (three 4-wave workgroups per CU) balance better (measured).
+static constexpr int64_t kW8WideMinTiles = 224, kW8WideMaxTiles = 256;
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -141,11 +145,14 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
     const bool fits_rsrc = M * K < (int64_t(1) << 31) && (K / 8) * N * 4 < (int64_t(1) << 31) &&
                            (G <= 0 || (K / G) * N * 2 < (int64_t(1) << 31));
     if (M >= 128 && fits_rsrc) {
-        // LDS-pipelined int8 GEMM: 128 x 128 workgroup tiles, K in stages of 64
+        // LDS-pipelined int8 GEMM, K in stages of 64: 128 x 256 workgroup
+        // tiles (8 waves) when they fill the CUs in one round, else 128 x 128
+        // (4 waves)
         p.kind = 2;
-        p.blk = 1;
+        const int64_t wide = cdiv(N, 256) * cdiv(M, 128);
+        p.blk = (wide >= kW8WideMinTiles && wide <= kW8WideMaxTiles) ? 2 : 1;
         p.mt = 4;
-        p.tiles_n = (int)cdiv(N, 128);
+        p.tiles_n = (int)cdiv(N, 128 * p.blk);
         p.tiles_m = (int)cdiv(M, 128);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         int64_t s = 1;

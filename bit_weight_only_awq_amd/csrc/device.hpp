@@ -189,6 +189,38 @@ __device__ __forceinline__ int tile_of_xcd_order(int i, int T) {
 }
 
 // ---------------------------------------------------------------------------
+// int8 B operand (16 consecutive k of one column) from two consecutive K8
+// words.  Nibble i of a K8 word holds k = [0,4,1,5,2,6,3,7][i], so the low
+// nibbles of its four bytes are k 0..3 and the high nibbles k 4..7.
+//  per-channel: bytes = 16*q (the x16 is divided out of the int32 result);
+//               two instructions per word.
+//  per-group:   bytes = q*s3 with s3 in 1..16.  With u = q + 8 in 0..15,
+//               u*s3 + (128 - 8*s3) lies in 0..240 per byte, so a packed
+//               16-bit multiply-add forms two bytes per half with no carry
+//               between them (full-rate, unlike a 32-bit multiply); flipping
+//               bit 7 then subtracts 128.
+template <bool GROUP>
+__device__ __forceinline__ u32x4 int8_b_operand(uint32_t w0, uint32_t w1, uint32_t s3) {
+    u32x4 b;
+    if (!GROUP) {
+        b[0] = (w0 << 4) & 0xF0F0F0F0u;
+        b[1] = w0 & 0xF0F0F0F0u;
+        b[2] = (w1 << 4) & 0xF0F0F0F0u;
+        b[3] = w1 & 0xF0F0F0F0u;
+    } else {
+        const u16x2 sv = {(uint16_t)s3, (uint16_t)s3};
+        const u16x2 cv = (u16x2){0x8080, 0x8080} - sv * (u16x2){0x0808, 0x0808};
+        auto bytes = [&](uint32_t u) { return bit_as<uint32_t>(bit_as<u16x2>(u) * sv + cv) ^ 0x80808080u; };
+        const uint32_t u0 = w0 ^ 0x88888888u, u1 = w1 ^ 0x88888888u;
+        b[0] = bytes(u0 & 0x0F0F0F0Fu);
+        b[1] = bytes((u0 >> 4) & 0x0F0F0F0Fu);
+        b[2] = bytes(u1 & 0x0F0F0F0Fu);
+        b[3] = bytes((u1 >> 4) & 0x0F0F0F0Fu);
+    }
+    return b;
+}
+
+// ---------------------------------------------------------------------------
 // Matrix-core wrappers.
 __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(bit_as<f16x8>(a), bit_as<f16x8>(b), c, 0, 0, 0);

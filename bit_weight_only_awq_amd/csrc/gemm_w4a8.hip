@@ -13,22 +13,28 @@
 
 namespace awq4 {
 
-constexpr int W8_M = 128, W8_N = 128, W8_K = 64;
+constexpr int W8_M = 128, W8_K = 64;
 #ifndef AWQ4_W8_RING
 #define AWQ4_W8_RING 4
 #endif
 constexpr int W8_RING = AWQ4_W8_RING;              // stages per LDS ring (copied W8_RING - 1 ahead)
 constexpr int W8_APITCH = W8_K;                    // 64 bytes of a8 per row (4 segments, swizzled)
 constexpr int W8_ABYTES = W8_M * W8_APITCH;        // 8192 per stage
-constexpr int W8_WORDS = (W8_K / 8) * W8_N * 4;    // 8 word rows x 128 columns x 4 B = 4096
-constexpr int W8_S3 = 2 * W8_N * 2;                // s3 of the stage's two 32-k halves: 2 x 128 x fp16
 
-template <bool GROUP>
+// NW waves per workgroup in a 2 x (NW/2) grid of 64 x 64 wave tiles: the
+// workgroup tile is 128 x 32*NW (NW = 4: 128 x 128; NW = 8: 128 x 256, which
+// halves the a8 bytes copied per matrix-core instruction).
+template <int NW, bool GROUP>
 struct W8Layout {
-    static constexpr int BBYTES = W8_WORDS + (GROUP ? W8_S3 : 0);
+    static constexpr int WN = 32 * NW;                    // workgroup tile width
+    static constexpr int WORDS = (W8_K / 8) * WN * 4;     // 8 word rows x WN columns x 4 B
+    static constexpr int S3 = 2 * WN * 2;                 // s3 of the stage's two 32-k halves
+    static constexpr int BBYTES = WORDS + (GROUP ? S3 : 0);
     static constexpr int OFF_B = W8_RING * W8_ABYTES;
-    static constexpr int LDS = OFF_B + W8_RING * BBYTES;  // 49152 (per channel) / 51200 (grouped)
-    static constexpr int COPIES = 3 + (GROUP ? 1 : 0);      // copies per wave and stage
+    static constexpr int LDS = OFF_B + W8_RING * BBYTES;  // NW = 4: 49152 / 51200; NW = 8: 65536 / 69632
+    static constexpr int A_COPIES = 8 / NW;               // 16-row a8 copies per wave and stage
+    static constexpr int COPIES = A_COPIES + 1 + (GROUP ? 1 : 0);  // copies per wave and stage
+    static constexpr int WROWS = 256 / WN;                // word rows per wave's word copy
 };
 
 // a8 rows: 16-byte segment s of row r is stored at s ^ f(r), f(r) = ((r >> 1)
@@ -38,49 +44,27 @@ struct W8Layout {
 // 2 apart (and rows 4 apart) always get different f.
 __device__ __forceinline__ int a8seg(int r, int s) { return s ^ (((r >> 1) ^ (r >> 2)) & 3); }
 
-// int8 B operand of one column from two consecutive K8 words (16 k).
-//  per-channel: bytes = 16*q; per-group: bytes = q*s3 (s3 in 1..16), via
-//  u = q + 8 in 0..15: u*s3 + (128 - 8*s3) stays in 0..240 per byte, and
-//  flipping bit 7 subtracts 128.
-template <bool GROUP>
-__device__ __forceinline__ u32x4 b8_operand(uint32_t w0, uint32_t w1, uint32_t s3) {
-    u32x4 b;
-    if (!GROUP) {
-        b[0] = (w0 << 4) & 0xF0F0F0F0u;
-        b[1] = w0 & 0xF0F0F0F0u;
-        b[2] = (w1 << 4) & 0xF0F0F0F0u;
-        b[3] = w1 & 0xF0F0F0F0u;
-    } else {
-        const uint32_t c = (128u - 8u * s3) * 0x01010101u;
-        const uint32_t u0 = w0 ^ 0x88888888u, u1 = w1 ^ 0x88888888u;
-        b[0] = ((u0 & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-        b[1] = (((u0 >> 4) & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-        b[2] = ((u1 & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-        b[3] = (((u1 >> 4) & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-    }
-    return b;
-}
-
-// Workgroup tile 128 x 128, K in stages of 64 (one 16x16x64 step); 4 waves in
-// a 2 x 2 grid, each owning 64 x 64 outputs: 4 row tiles x 4 column MFMAs.
+// Workgroup tile 128 x 32*NW, K in stages of 64 (one 16x16x64 step); NW waves
+// in a 2 x NW/2 grid, each owning 64 x 64 outputs: 4 row tiles x 4 column MFMAs.
 // Lane j reads 16 bytes = 4 consecutive columns of two K8 word rows, which
 // give the B operands of its 4 MFMAs (output column = 64 wn + 4j + u).
 // a8 rows, word rows and (grouped) s3 rows are copied into 4-slot LDS rings
 // three stages ahead; each stage waits only for the copies older than its
 // own, so the next stage is always readable and its operands are loaded while
 // the current stage's MFMAs run.
-template <bool GROUP, int DT>
-__global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
+template <int NW, bool GROUP, int DT>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                        const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                        const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                        int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
                                                        int M, int N, int K, int G, int S) {
-    using L = W8Layout<GROUP>;
+    using L = W8Layout<NW, GROUP>;
+    constexpr int W8_N = L::WN;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::LDS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int j = lane & 15, gq = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     // logical tile of this workgroup (XCD-aware order over the tiles_n x tiles_m grid)
     const int tile = tile_of_xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
     const int tn = tile % gridDim.x, tm = tile / gridDim.x, split = blockIdx.z;
@@ -88,28 +72,29 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     const int Tst = K / W8_K;
     const int s_lo = (int)((int64_t)Tst * split / S), s_hi = (int)((int64_t)Tst * (split + 1) / S);
 
-    // Copy assignment.  a8: wave w copies rows 32w + 16i + lane/4 (i < 2),
-    // lane%4 being the stored segment position; rows past M repeat row M-1
-    // (their outputs are never stored).  Words: wave w copies word rows 2w and
-    // 2w+1, lane%32 being the 4-column segment; columns past N repeat the last
-    // 4.  s3 (grouped): wave w, lanes 0..7, copies 16-byte segments 8w..8w+7 of
-    // the stage's two s3 rows (half h = segment / 16).
-    uint32_t aoff[2];
+    // Copy assignment.  a8: wave w copies rows 16 (A_COPIES w + i) + lane/4
+    // (i < A_COPIES), lane%4 being the stored segment position; rows past M
+    // repeat row M-1 (their outputs are never stored).  Words: wave w copies
+    // word rows WROWS w .. WROWS w + WROWS - 1, lane % (W8_N/4) being the
+    // 4-column segment; columns past N repeat the last 4.  s3 (grouped): wave
+    // w, lanes 0..7, copies 16-byte segments 8w..8w+7 of the stage's two s3
+    // rows (W8_N/8 segments per row).
+    uint32_t aoff[L::A_COPIES];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = 32 * wave + 16 * i + (lane >> 2);
+    for (int i = 0; i < L::A_COPIES; ++i) {
+        const int r = 16 * (L::A_COPIES * wave + i) + (lane >> 2);
         const int m = min(m0 + r, M - 1);
         aoff[i] = (uint32_t)((m - m0) * K + 16 * a8seg(r, lane & 3));
     }
     uint32_t boff;
     {
-        const int r = 2 * wave + (lane >> 5);
-        const int c = min(n0 + 4 * (lane & 31), N - 4);
+        const int r = L::WROWS * wave + lane / (W8_N / 4);
+        const int c = min(n0 + 4 * (lane % (W8_N / 4)), N - 4);
         boff = (uint32_t)((r * N + c) * 4);
     }
     const int s3_seg = 8 * wave + (lane & 7);
-    const int s3_h = s3_seg >> 4;  // wave-uniform: waves 0, 1 copy half 0, waves 2, 3 half 1
-    const uint32_t s3_off = (uint32_t)(2 * min(n0 + 8 * (s3_seg & 15), N - 8));
+    const int s3_h = s3_seg / (W8_N / 8);  // wave-uniform: the first NW/2 waves copy half 0
+    const uint32_t s3_off = (uint32_t)(2 * min(n0 + 8 * (s3_seg % (W8_N / 8)), N - 8));
     const int lg = GROUP ? __builtin_ctz(G) : 0;
     // buffer descriptors (the planner keeps every byte offset under 2^31):
     // a8 rows from m0, the packed words, the s3 rows; per-lane offsets above,
@@ -120,14 +105,15 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
                                                 GROUP ? (int64_t)(K / G) * N * 2 : 0);
 
     auto copy_stage = [&](int st, int slot) {
-        unsigned char *A = lds + slot * W8_ABYTES + 32 * wave * W8_APITCH;
+        unsigned char *A = lds + slot * W8_ABYTES + 16 * L::A_COPIES * wave * W8_APITCH;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma16_buf(ars, aoff[i], (uint32_t)(st * W8_K), A + 16 * i * W8_APITCH);
+        for (int i = 0; i < L::A_COPIES; ++i)
+            dma16_buf(ars, aoff[i], (uint32_t)(st * W8_K), A + 16 * i * W8_APITCH);
         unsigned char *B = lds + L::OFF_B + slot * L::BBYTES;
-        dma16_buf(brs, boff, (uint32_t)st * (W8_K / 8) * (uint32_t)N * 4, B + 2 * wave * (W8_N * 4));
+        dma16_buf(brs, boff, (uint32_t)st * (W8_K / 8) * (uint32_t)N * 4, B + L::WROWS * wave * (W8_N * 4));
         if (GROUP && lane < 8) {
             const int g = (st * W8_K + 32 * s3_h) >> lg;
-            dma16_buf(grs, s3_off, (uint32_t)g * (uint32_t)N * 2, B + W8_WORDS + 16 * s3_seg);
+            dma16_buf(grs, s3_off, (uint32_t)g * (uint32_t)N * 2, B + L::WORDS + 16 * s3_seg);
         }
     };
 
@@ -140,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
     const int cl = 64 * wn + 4 * j;  // this lane's first column within the tile
     const uint32_t a_off = (uint32_t)((wm * 64 + j) * W8_APITCH + a8seg(j, gq) * 16);
     const uint32_t w_off = (uint32_t)(L::OFF_B + (2 * gq) * (W8_N * 4) + cl * 4);
-    const uint32_t g_off = (uint32_t)(L::OFF_B + W8_WORDS + (gq >> 1) * (W8_N * 2) + cl * 2);
+    const uint32_t g_off = (uint32_t)(L::OFF_B + L::WORDS + (gq >> 1) * (W8_N * 2) + cl * 2);
 
     // operands of the stage in ring slot `slot`
     struct Ops {
@@ -165,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         uint32_t g3[4] = {16u, 16u, 16u, 16u};
         if (GROUP) group_scales(*(const u32x2 *)(lds + slot * L::BBYTES + g_off), g3);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o.b[u] = b8_operand<GROUP>(w0[u], w1[u], g3[u]);
+        for (int u = 0; u < 4; ++u) o.b[u] = int8_b_operand<GROUP>(w0[u], w1[u], g3[u]);
     };
     // Stage st (its operands already in `cur`): 16 MFMAs, each in its own
     // slot; stage st + 1's operands are read in the first slots and its int8
@@ -195,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
             if constexpr (i == 8 && GROUP) group_scales(sv, g3);
             if constexpr (i >= 8 && (i & 1) == 0) {
                 constexpr int uu = (i - 8) >> 1;
-                nxt.b[uu] = b8_operand<GROUP>(w0[uu], w1[uu], g3[uu]);
+                nxt.b[uu] = int8_b_operand<GROUP>(w0[uu], w1[uu], g3[uu]);
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -290,17 +276,25 @@ __global__ __launch_bounds__(256, 2) void w4a8_gemm_lds(const int8_t *__restrict
         }
 }
 
-template <bool GROUP, int DT>
+template <int NW, bool GROUP, int DT>
 static hipError_t launch_lds8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    hipLaunchKernelGGL((w4a8_gemm_lds<GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, a.a8,
+    hipLaunchKernelGGL((w4a8_gemm_lds<NW, GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(64 * NW), 0, st,
+                       a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
                        (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 
+template <int NW>
+static hipError_t launch_lds8_nw(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    if (a.dtype == DT_BF16)
+        return a.s3 != nullptr ? launch_lds8<NW, true, DT_BF16>(a, p, st) : launch_lds8<NW, false, DT_BF16>(a, p, st);
+    return a.s3 != nullptr ? launch_lds8<NW, true, DT_F16>(a, p, st) : launch_lds8<NW, false, DT_F16>(a, p, st);
+}
+
+// p.blk: workgroup tile width in 128-column units (1: 128 x 128, 2: 128 x 256)
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    if (a.dtype == DT_BF16) return a.s3 != nullptr ? launch_lds8<true, DT_BF16>(a, p, st) : launch_lds8<false, DT_BF16>(a, p, st);
-    return a.s3 != nullptr ? launch_lds8<true, DT_F16>(a, p, st) : launch_lds8<false, DT_F16>(a, p, st);
+    return p.blk == 2 ? launch_lds8_nw<8>(a, p, st) : launch_lds8_nw<4>(a, p, st);
 }
 
 }  // namespace awq4

@@ -200,30 +200,6 @@ hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, in
 }
 
 // ---------------------------------------------------------------------------
-// int4 -> int8 B operand for one column from two consecutive K8 words.
-//  per-channel: bytes = 16*q  (two instructions per word)
-//  per-group:   bytes = q*s3 with s3 in 1..16: with u = q + 8 in 0..15,
-//               u*s3 + (128 - 8*s3) lies in 0..240 per byte (no carries
-//               between bytes), and flipping bit 7 subtracts 128.
-template <bool GROUP>
-__device__ __forceinline__ u32x4 make_b8(uint32_t w0, uint32_t w1, uint32_t s3) {
-    u32x4 b;
-    if (!GROUP) {
-        b[0] = (w0 << 4) & 0xF0F0F0F0u;
-        b[1] = w0 & 0xF0F0F0F0u;
-        b[2] = (w1 << 4) & 0xF0F0F0F0u;
-        b[3] = w1 & 0xF0F0F0F0u;
-    } else {
-        const uint32_t c = (128u - 8u * s3) * 0x01010101u;
-        const uint32_t u0 = w0 ^ 0x88888888u, u1 = w1 ^ 0x88888888u;
-        b[0] = ((u0 & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-        b[1] = (((u0 >> 4) & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-        b[2] = ((u1 & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-        b[3] = (((u1 >> 4) & 0x0F0F0F0Fu) * s3 + c) ^ 0x80808080u;
-    }
-    return b;
-}
-
 template <int DT>
 __device__ __forceinline__ uint32_t s3_int(const uint16_t *__restrict__ s3, size_t idx) {
     return (uint32_t)act_bits_to_f32<DT>(s3[idx]);
@@ -379,7 +355,7 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                u32x4 bop = make_b8<GROUP>(w0[b][i], w1[b][i], g3[i]);
+                u32x4 bop = int8_b_operand<GROUP>(w0[b][i], w1[b][i], g3[i]);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) acc[mt][b][i] = mfma_i8(a[mt], bop, acc[mt][b][i]);
             }
@@ -490,7 +466,7 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            u32x4 bop = make_b8<GROUP>(w0[i], w1[i], g3[i]);
+            u32x4 bop = int8_b_operand<GROUP>(w0[i], w1[i], g3[i]);
 #pragma unroll
             for (int mt = 0; mt < MTW; ++mt) acc[mt][i] = mfma_i8(a[mt], bop, acc[mt][i]);
         }

@@ -89,7 +89,9 @@ def test_w4a8_qqq_shape(M, G):
 @pytest.mark.parametrize("G", [-1, 32, 64, 128])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2048, 4096, 4096), (1, 4096, 14336), (2048, 4096, 14336),
                                    (300, 4096, 1032), (5, 64, 8),
-                                   (17, 128, 136), (40, 256, 24), (129, 512, 1032), (33, 4096, 520)])
+                                   (17, 128, 136), (40, 256, 24), (129, 512, 1032), (33, 4096, 520),
+                                   # 128 x 256 tiles with a ragged last row and column tile
+                                   (2049, 256, 4104), (4000, 128, 2056)])
 def test_w4a8_shapes(M, K, N, G):
     if G > 0 and K % G:
         pytest.skip("K not a multiple of G")
