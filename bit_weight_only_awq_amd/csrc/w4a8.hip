@@ -83,29 +83,41 @@ __global__ __launch_bounds__(256) void w4a8_quant_kernel(const uint16_t *__restr
     }
 }
 
-// Quantised value of x (fp16 bits) with scale s: rint(x / s) (half to even)
-// clamped to int8, without a divide.  For fp16 x and s the exact quotient is
-// either a half-integer or at least 2^-12 away from one, and x * r with r
-// within a few ulps of 1/s is within 2^-15 of it, so rint(x * r) is the
-// correctly rounded integer except at exact ties; the residual
-// d = x - q0 * s (exact in one FMA) detects those (|d| == s/2) and moves an
-// odd q0 to the even neighbour.  Checked exhaustively against the correctly
-// rounded fp32 divide for every reachable s, every fp16 x and reciprocals up
-// to 3 ulps off.
-__device__ __forceinline__ uint32_t quant_one(uint32_t h, float s, float r, float hs) {
-    const float f = f16_bits_to_f32(h);
-    float q0 = rintf(f * r);
-    const float d = __builtin_fmaf(-q0, s, f);
-    if (fabsf(d) == hs && (((int)q0) & 1)) q0 += d > 0.0f ? 1.0f : -1.0f;
-    q0 = fminf(fmaxf(q0, -128.0f), 127.0f);
-    return (uint32_t)(int32_t)q0 & 0xFFu;
+// int8 codes of 8 fp16 or bf16 values (one 16-byte chunk) for the scale s,
+// given r ~ 1/s: round half to even of x / s, clamped to int8, without a
+// divide.  For x and s of one 16-bit type the exact quotient is a half-integer
+// or at least 2^-12 (fp16) / 2^-9 (bf16) from one, and x * r (r within a few
+// ulps of 1/s) stays within 2^-15 of it.
+// One FMA adds 1536, which rounds x * r to a multiple of 2^-13 (the fp32
+// spacing in [1024, 2048)): exact ties land on the half-integer, every other
+// quotient stays on its own side of it.  The clamp is taken in that shifted
+// range; adding 1.5 * 2^23 - 1536 then rounds to an integer (half to even)
+// held in the low mantissa bits, so the low byte of the sum's bits is the
+// int8 code.  Checked exhaustively against the correctly rounded fp32 divide
+// for every reachable s (bf16: every s >= 2^-126, whose reciprocal is a normal
+// fp32 value; smaller scales take the divide), every x and reciprocals up to
+// 3 ulps off.
+template <int DT>
+__device__ __forceinline__ u32x2 quant8(u32x4 v, float r) {
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float f = act_bits_to_f32<DT>((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(f, r, 1536.0f), 1536.0f - 128.0f, 1536.0f + 127.0f);
+        b[e] = bit_as<uint32_t>(t + (12582912.0f - 1536.0f));
+    }
+    u32x2 o;
+#pragma unroll
+    for (int w = 0; w < 2; ++w)  // low bytes of b[4w .. 4w+3]
+        o[w] = perm_b32(b[4 * w + 1], b[4 * w], 0x0C0C0400u) | perm_b32(b[4 * w + 3], b[4 * w + 2], 0x04000C0Cu);
+    return o;
 }
 
 // Register-resident quantisation: one workgroup of T threads per row, each
 // thread holding NV chunks of 8 values (row length K <= 8 * NV * T, K % 8 ==
 // 0), so the row is read from memory once.
-// fp16 uses the divide-free rounding above; bf16 (whose exactness argument
-// would differ) the correctly rounded fp32 divide.
+// Both types use the divide-free rounding above, except bf16 rows whose
+// scale is below 2^-126 (a subnormal fp32 value), which divide.
 template <int DT, int NV, int T>
 __global__ __launch_bounds__(T) void w4a8_quant_rows(const uint16_t *__restrict__ x, int8_t *__restrict__ a8,
                                                      float *__restrict__ s1, int K) {
@@ -133,24 +145,22 @@ __global__ __launch_bounds__(T) void w4a8_quant_rows(const uint16_t *__restrict_
     const float q32 = amax / 127.0f;       // correctly rounded fp32 divide, once per row
     const float s = round_to_act<DT>(q32);  // to the activation type (nearest even) and back
     if (threadIdx.x == 0) s1[m] = s;
-    const float r = __builtin_amdgcn_rcpf(s), hs = 0.5f * s;
+    const float r = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int k = 8 * (threadIdx.x + i * T);
         if (k >= K) break;
         u32x2 o = {0, 0};
         if (s != 0.0f) {
+            if (DT == DT_F16 || s >= 0x1p-126f) {
+                o = quant8<DT>(v[i], r);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t h = (v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                uint32_t q;
-                if (DT == DT_F16) {
-                    q = quant_one(h, s, r, hs);
-                } else {
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t h = (v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                     const float qf = fminf(fmaxf(rintf(act_bits_to_f32<DT>(h) / s), -128.0f), 127.0f);
-                    q = (uint32_t)(int32_t)qf & 0xFFu;
+                    o[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
                 }
-                o[e >> 2] |= q << (8 * (e & 3));
             }
         }
         *(u32x2 *)(out + k) = o;
@@ -316,12 +326,7 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
             const u32x4 v = *(const u32x4 *)(x16 + (size_t)m * K + 64 * w_lo + 8 * cc);
             const float sv = srow[m];
             u32x2 o = {0, 0};
-            if (sv != 0.0f) {
-                const float r = __builtin_amdgcn_rcpf(sv), hs = 0.5f * sv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    o[e >> 2] |= quant_one((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, sv, r, hs) << (8 * (e & 3));
-            }
+            if (sv != 0.0f) o = quant8<DT_F16>(v, __builtin_amdgcn_rcpf(sv));
             *(u32x2 *)(qa + ((size_t)(cc >> 3) * M + m) * 64 + (cc & 7) * 8) = o;
         }
     }

@@ -1,6 +1,9 @@
 """Host check (no GPU): the divide-free rounding of the W4A8 activation
-quantiser equals clamp(rint(x / s)) for every scale the quantiser can produce
-and every fp16 x it can meet, with the reciprocal off by up to one ulp
+quantiser (the form the kernels compute: one FMA snapping x * r to a
+multiple of 2^-13, a clamp, and the integer read from the low byte after adding
+1.5 * 2^23) equals clamp(rint(x / s)) for every scale the quantiser can produce
+and every fp16 or bf16 x it can meet (bf16 scales of at least 2^-126; smaller
+ones divide), with the reciprocal off by up to one ulp
 (quant_rounding_check.c states the argument)."""
 import os
 import shutil
@@ -22,8 +25,9 @@ def checker(tmp_path_factory):
     return exe
 
 
-def test_divide_free_rounding_exhaustive(checker):
-    procs = [subprocess.Popen([checker, str(i), str(SLICES), "1"], stdout=subprocess.PIPE, text=True)
+@pytest.mark.parametrize("mode", ["2", "3"], ids=["fp16", "bf16"])
+def test_divide_free_rounding_exhaustive(checker, mode):
+    procs = [subprocess.Popen([checker, str(i), str(SLICES), "1", mode], stdout=subprocess.PIPE, text=True)
              for i in range(SLICES)]
     outs = [(p.communicate()[0], p.returncode) for p in procs]
     for out, rc in outs:
