@@ -16,10 +16,12 @@ namespace awq4 {
 
 static constexpr int64_t kMaxDim = int64_t(1) << 20;
 static constexpr int kTargetWorkgroups = 512;  // 256 CUs x 2 workgroups of 4 waves
-// The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, one per CU) are used
-// when they make one nearly full round on the 256 CUs; past one round the
-// 128 x 128 tiles (three 4-wave workgroups per CU) balance better (measured).
-static constexpr int64_t kW8WideMinTiles = 224, kW8WideMaxTiles = 256;
+// The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, two per CU) are used
+// whenever there are at least as many as CUs; with fewer, the 128 x 128 tiles
+// give more workgroups before a K split is needed (measured: M = 512 on
+// (4096, 14336) takes 44 us on 448 narrow tiles, 82 us on 224 wide ones split
+// in two).
+static constexpr int64_t kW8WideMinTiles = 256;
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -146,11 +148,9 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
                            (G <= 0 || (K / G) * N * 2 < (int64_t(1) << 31));
     if (M >= 128 && fits_rsrc) {
         // LDS-pipelined int8 GEMM, K in stages of 64: 128 x 256 workgroup
-        // tiles (8 waves) when they fill the CUs in one round, else 128 x 128
-        // (4 waves)
+        // tiles (8 waves) when there are enough of them, else 128 x 128 (4 waves)
         p.kind = 2;
-        const int64_t wide = cdiv(N, 256) * cdiv(M, 128);
-        p.blk = (wide >= kW8WideMinTiles && wide <= kW8WideMaxTiles) ? 2 : 1;
+        p.blk = cdiv(N, 256) * cdiv(M, 128) >= kW8WideMinTiles ? 2 : 1;
         p.mt = 4;
         p.tiles_n = (int)cdiv(N, 128 * p.blk);
         p.tiles_m = (int)cdiv(M, 128);

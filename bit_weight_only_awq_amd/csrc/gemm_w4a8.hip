@@ -53,7 +53,7 @@ __device__ __forceinline__ int a8seg(int r, int s) { return s ^ (((r >> 1) ^ (r 
 // own, so the next stage is always readable and its operands are loaded while
 // the current stage's MFMAs run.
 template <int NW, bool GROUP, int DT>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
+__global__ __launch_bounds__(64 * NW, 2) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                        const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                        const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                        int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
@@ -153,15 +153,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void w4a8_gemm_lds(const int8_t *_
 #pragma unroll
         for (int u = 0; u < 4; ++u) o.b[u] = int8_b_operand<GROUP>(w0[u], w1[u], g3[u]);
     };
-    // Stage st (its operands already in `cur`): 16 MFMAs, each in its own
-    // slot; stage st + 1's operands are read in the first slots and its int8
-    // B operands built in the last eight, so that no wave waits on its own
-    // LDS reads.  Then wait for the copies older than this stage's and cross
-    // the barrier.  Copies: stage st + 3 into the slot of stage st - 1
-    // (finished before the last barrier); near the end the last stage is
-    // copied again into that slot, never read as data, so every stage issues
-    // the same copies and the wait count is fixed.
-    auto stage = [&](int st, Ops &cur, Ops &nxt) {
+    // Stage st (its operands already in `o`): 16 MFMAs, each in its own slot.
+    // Stage st + 1's packed words are read in the first slots; each a8
+    // operand of stage st + 1 is read into `o` right after the MFMA that last
+    // uses stage st's (slots 3, 7, 11, 15), and each int8 B operand is built
+    // in place after its last use (slots 12..15).  One operand set in place,
+    // not two in turn, keeps the kernel at or under 128 VGPRs (four waves per
+    // SIMD: two 8-wave workgroups per CU), and no wave waits on its own LDS
+    // reads.  Then wait for the copies older than this stage's and cross the
+    // barrier.  Copies: stage st + 3 into the slot of stage st - 1 (finished
+    // before the last barrier); near the end the last stage is copied again
+    // into that slot, never read as data, so every stage issues the same
+    // copies and the wait count is fixed.
+    auto stage = [&](int st, Ops &o) {
         const unsigned rel = (unsigned)(st - s_lo);
         copy_stage(min(st + W8_RING - 1, s_hi - 1), (int)((rel + W8_RING - 1) % W8_RING));
         const unsigned char *nb = lds + ((rel + 1) % W8_RING) * L::BBYTES;
@@ -173,16 +177,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void w4a8_gemm_lds(const int8_t *_
         static_for<16>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             constexpr int mt = i >> 2, u = i & 3;
-            acc[mt][u] = mfma_i8(cur.a[mt], cur.b[u], acc[mt][u]);
-            if constexpr (i < 4) nxt.a[i] = *(const u32x4 *)(na + i * 16 * W8_APITCH);
-            if constexpr (i == 4) w0 = wq[0];
-            if constexpr (i == 5) w1 = wq[W8_N / 4];
-            if constexpr (i == 6 && GROUP) sv = *(const u32x2 *)(nb + g_off);
-            if constexpr (i == 8 && GROUP) group_scales(sv, g3);
-            if constexpr (i >= 8 && (i & 1) == 0) {
-                constexpr int uu = (i - 8) >> 1;
-                nxt.b[uu] = int8_b_operand<GROUP>(w0[uu], w1[uu], g3[uu]);
-            }
+            acc[mt][u] = mfma_i8(o.a[mt], o.b[u], acc[mt][u]);
+            if constexpr (i == 1) w0 = wq[0];
+            if constexpr (i == 2) w1 = wq[W8_N / 4];
+            if constexpr (i == 5 && GROUP) sv = *(const u32x2 *)(nb + g_off);
+            if constexpr (i == 9 && GROUP) group_scales(sv, g3);
+            if constexpr (u == 3) o.a[mt] = *(const u32x4 *)(na + mt * 16 * W8_APITCH);
+            if constexpr (mt == 3) o.b[u] = int8_b_operand<GROUP>(w0[u], w1[u], g3[u]);
             __builtin_amdgcn_sched_barrier(0);
         });
         // copies still allowed in flight: those of stages st + 3 .. st + W8_RING - 1
@@ -194,19 +195,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void w4a8_gemm_lds(const int8_t *_
     };
 
     if (s_lo < s_hi) {
-        Ops o0, o1;
+        Ops o;
 #pragma unroll
         for (int d = 0; d < W8_RING - 1; ++d)
             if (s_lo + d < s_hi) copy_stage(s_lo + d, d);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        load_ops(0, o0);
+        load_ops(0, o);
         int st = s_lo;
-        for (; st + 2 <= s_hi; st += 2) {
-            stage(st, o0, o1);
-            stage(st + 1, o1, o0);
-        }
-        if (st < s_hi) stage(st, o0, o1);
+        for (; st < s_hi; ++st) stage(st, o);
     }
 
     // Epilogue: lane holds rows m0 + 64 wm + 16 mt + 4 gq + r, columns
