@@ -396,6 +396,23 @@ def main():
             dense[name] = {"K": K, "N": N, "us": round(t * 1e6, 2),
                            "TFLOPs": round(2 * M_PREFILL * N * K / t / 1e12, 1)}
             del xd, wd, yd
+    # the vendor dense int8 GEMM (hipBLASLt via torch._int_mm, int32 out) on
+    # the W4A8 shapes with weights already unpacked to int8 (2x the weight
+    # memory; no scales applied): context for the W4A8 GEMM, not a library path
+    dense8 = {}
+    if not args.no_comparator:
+        for M, K, N in [(1024, W4A8_K, W4A8_N)] + [(M_PREFILL, K, N) for K, N in TARGET_SHAPES]:
+            name = f"M={M} K={K} N={N}"
+            try:
+                g8 = torch.Generator().manual_seed(synthgen.seed_for(f"bench|dense8|{M}|{K}|{N}"))
+                a8d = torch.randint(-128, 128, (M, K), generator=g8, dtype=torch.int8).to(dev)
+                w8d = torch.randint(-8, 8, (N, K), generator=g8, dtype=torch.int8).to(dev).t()
+                torch._int_mm(a8d, w8d)
+                t = per_launch(lambda a8d=a8d, w8d=w8d: torch._int_mm(a8d, w8d), 1, reps=3)
+                dense8[name] = {"us": round(t * 1e6, 2), "TOPs": round(2 * M * N * K / t / 1e12, 1)}
+                del a8d, w8d
+            except RuntimeError as e:  # not every torch build has an int8 GEMM
+                dense8[name] = {"error": str(e).splitlines()[0][:120]}
     def w4a8_times(M, x, a8, s1, y, s2s, fused):
         tq = per_launch(lambda: [awq.quant_act(x, a8, s1) for _ in range(4)], 4)
         tg = per_launch(lambda: [awq.w4a8_gemm(a8, w8w[r][0], s1, s2s[r], out=y) for r in range(w8_copies)],
@@ -482,6 +499,9 @@ def main():
            "comparator_dense_fp16_m2048": {"note": "vendor dense fp16 GEMM (hipBLASLt via torch.matmul) on "
                                                    "pre-dequantised weights; context, not a library path",
                                            **dense},
+           "comparator_dense_int8": {"note": "vendor dense int8 GEMM (torch._int_mm, int32 out) on weights "
+                                             "pre-unpacked to int8, no scales; context, not a library path",
+                                     **dense8},
            "targets": {"note": "W4A8 times are whole-layer calls (w4a8_linear): activation quantisation included, fused into the GEMM at M=1", **targets},
            "phases_us": {"decode": round(t_dec * 1e6, 2), "prefill": round(t_pre * 1e6, 2),
                          "w4a8": round(t_w8 * 1e6, 2)}}
