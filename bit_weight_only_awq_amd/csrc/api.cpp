@@ -16,6 +16,12 @@ namespace awq4 {
 
 static constexpr int64_t kMaxDim = int64_t(1) << 20;
 static constexpr int kTargetWorkgroups = 512;  // 256 CUs x 2 workgroups of 4 waves
+// The W4A16 LDS GEMM takes M above 16 (the decode kernel below).  Under 128
+// rows it runs 128-row tiles with deep copy rings and at most 4 K splits
+// (measured on the Llama-3-8B layers at M = 32..128: more splits cost more in
+// partial tiles than they gain, and 256-row tiles with deep rings, at one
+// wave per SIMD, were slower than the large-M configuration from M = 128 up).
+static constexpr int64_t kW16LdsMinM = 16, kW16DeepMaxM = 127, kW16DeepMaxSplits = 4;
 // The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, two per CU) are used
 // whenever there are at least as many as CUs; with fewer, the 128 x 128 tiles
 // give more workgroups before a K split is needed (measured: M = 512 on
@@ -78,23 +84,33 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
     }
     // buffer-descriptor copies address X and the packed words with 32-bit offsets
     const bool fits_rsrc = M * K * 2 < (int64_t(1) << 31) && K * (N / 2) < (int64_t(1) << 31);
-    if (M >= 128 && K % 64 == 0 && N % 32 == 0 && fits_rsrc) {
-        // LDS-pipelined GEMM: 256 x 128 workgroup tiles, K in stages of 64
+    if (M > kW16LdsMinM && K % 64 == 0 && N % 32 == 0 && fits_rsrc) {
+        // LDS-pipelined GEMM: 256-row (M >= 128) or 128-row x 128 workgroup
+        // tiles, K in stages of 64
         p.kind = 3;
+        p.deep = M <= kW16DeepMaxM;
+        p.mt = p.deep ? 8 : 16;
         p.tiles_n = (int)cdiv(N, 128);
-        p.tiles_m = (int)cdiv(M, 256);
+        p.tiles_m = (int)cdiv(M, 16 * p.mt);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         const int64_t stages = K / 64;
-        // K splits only for few tiles (measured at M = 128..1024 on the
-        // Llama-3-8B layers: the partial tiles cost more than a third split
-        // saves); the in-workgroup K split below adds parallelism for free
-        int64_t s = tiles <= 32 ? 4 : tiles <= 64 ? 2 : 1;
-        s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 4));
+        int64_t s;
+        if (p.deep) {
+            // one workgroup per CU: K splits up to one workgroup per CU
+            s = std::min<int64_t>(std::max<int64_t>(1, 256 / tiles), kW16DeepMaxSplits);
+            s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
+        } else {
+            // K splits only for few tiles (measured at M = 128..1024 on the
+            // Llama-3-8B layers: the partial tiles cost more than a third
+            // split saves); the in-workgroup K split below adds parallelism
+            s = tiles <= 32 ? 4 : tiles <= 64 ? 2 : 1;
+            s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 4));
+        }
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
         // no more workgroups than CUs: two wave groups per workgroup split K
         // inside it (twice the waves per SIMD, no extra atomics)
-        p.ksplit = tiles * p.splits <= 256 && stages / p.splits >= 4 ? 2 : 1;
+        p.ksplit = !p.deep && tiles * p.splits <= 256 && stages / p.splits >= 4 ? 2 : 1;
     }
     if (p.splits > 1)
         p.workspace_bytes = p.kind == 0 ? (size_t)M * N * sizeof(uint64_t)

@@ -15,32 +15,43 @@
 //
 // Data movement: every stage's X rows and packed words (with the stage's
 // scales and zero points) are copied straight from global memory into LDS by
-// direct-to-LDS buffer loads, with no register staging.  X has two LDS
-// buffers and is copied one stage ahead; the packed words and metadata have
-// three and are copied two stages ahead, so the words of the next k-step are
-// always readable.  Each wave software-pipelines its k-steps: while the 32
-// MFMAs of step q run, it dequantises the B operands of step q+1 and reads the
-// X operands six row tiles ahead.  One wait and one barrier end each stage.
+// direct-to-LDS buffer loads, with no register staging, into rings of AB X
+// buffers (copied AB - 1 stages ahead) and BB word buffers (BB - 1 ahead).
+// M >= 128 uses AB = 2, BB = 3 (two workgroups per CU); M < 128, whose
+// stages are short and whose words stream from HBM, uses AB = 3, BB = 8 so
+// that more bytes are in flight against the memory latency.  Every stage
+// issues the same copies (near the end the last stage is copied again into
+// a buffer that is no longer read), so the wait that ends a stage has a fixed
+// count: it waits only for what the next stage reads.  Each wave
+// software-pipelines its k-steps: while the MFMAs of step q run, it
+// dequantises the B operands of step q+1 and reads the X operands six row
+// tiles ahead.  One wait and one barrier end each stage.
+//
+// MT = 16 row tiles per wave (256-row workgroup tiles) or 8 (128 rows, for
+// M <= 128, where 256-row tiles would be half padding).
 #include "device.hpp"
 #include "launch.hpp"
 #include "w4a16_ops.hpp"
 
 namespace awq4 {
 
-constexpr int GB_M = 256, GB_N = 128, GB_K = 64;
+constexpr int GB_N = 128, GB_K = 64;
 constexpr int GA_PITCH = GB_K * 2;                 // 128 bytes per X row (8 segments of 16 B, swizzled)
-constexpr int GA_BYTES = GB_M * GA_PITCH;          // 32768 per X buffer
 constexpr int GB_PITCH = (GB_N / 8) * 4;           // 64 bytes per k-row of packed words (16 words)
 constexpr int GB_WORDS = GB_K * GB_PITCH;          // 4096
 constexpr int GM_SCALES = 2 * GB_N * 2;            // scales of both k-steps: 2 x 128 x 2 B
 constexpr int GM_ZEROS = 2 * (GB_N / 8) * 4;       // zero words of both k-steps: 2 x 16 x 4 B
 constexpr int GB_BYTES = GB_WORDS + GM_SCALES + GM_ZEROS;  // 4736 per word/metadata buffer
-constexpr int GA_BUFS = 2, GB_BUFS = 3;
-#ifndef AWQ4_PREF_A
-#define AWQ4_PREF_A 6
-#endif
-constexpr int kPrefA = AWQ4_PREF_A;  // X operand reads run this many row tiles ahead of the MFMAs
-constexpr int G_LDS = GA_BUFS * GA_BYTES + GB_BUFS * GB_BYTES;  // 79744: two workgroups fit in 160 KB
+constexpr int kPrefA = 6;  // X operand reads run this many row tiles ahead of the MFMAs
+
+// LDS ring of one group of 4 waves: AB X buffers of 16*MT rows, BB word buffers
+template <int MT, int AB, int BB>
+struct GRing {
+    static constexpr int M_TILE = 16 * MT;               // workgroup tile rows
+    static constexpr int A_BYTES = M_TILE * GA_PITCH;    // one X buffer
+    static constexpr int LDS = AB * A_BYTES + BB * GB_BYTES;  // (16, 2, 3): 79744, two workgroups per CU
+    static constexpr int A_COPIES = M_TILE / 32;          // 8-row X copies per wave and stage
+};
 
 // X rows: 16-byte segment s of row r is stored at position s ^ (r & 7), so the
 // 8 rows read by a lane octet cover all banks.
@@ -57,20 +68,24 @@ __host__ __device__ constexpr int gemm_col(int u) { return (u & 1) + ((u >> 1) <
 // tile and split its K range (each with its own LDS ring); the groups trade
 // partial sums through LDS at the end.  This doubles the waves per SIMD for
 // layers with no more tiles than CUs.
-template <int DT, bool SYM, int KS>
+template <int DT, bool SYM, int KS, int MT, int AB, int BB>
 __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *__restrict__ x,
                                                                 const uint32_t *__restrict__ qw,
                                                                 const uint16_t *__restrict__ sc,
                                                                 const uint32_t *__restrict__ qz,
                                                                 uint16_t *__restrict__ y, uint64_t *__restrict__ acc64,
                                                                 int M, int N, int K, int G, int S) {
+    using R = GRing<MT, AB, BB>;
+    static_assert(KS == 1 || MT == 16, "the in-workgroup K split hands over half of 16 row tiles");
+    static_assert(AB >= 2 && BB >= 3 && MT > kPrefA, "ring depths and prefetch distance");
+    constexpr int GB_M = R::M_TILE, GA_BYTES = R::A_BYTES, G_LDS = R::LDS;
     __shared__ __attribute__((aligned(16))) unsigned char lds_all[KS * G_LDS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = KS == 1 ? 0 : (wv >> 2), wave = wv & 3;
     unsigned char *const lds = lds_all + grp * G_LDS;
     unsigned char *const Abase = lds;
-    unsigned char *const Bbase = lds + GA_BUFS * GA_BYTES;
+    unsigned char *const Bbase = lds + AB * GA_BYTES;
     const int j = lane & 15, gq = lane >> 4;
     const int nw = N >> 3;
     // logical tile of this workgroup (XCD-aware order over the tiles_n x tiles_m grid)
@@ -87,9 +102,9 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
 
     // Copy assignment (byte offsets from the workgroup's corner; all fit in
     // 32 bits: at most 256 X rows and 64 k-rows of words are addressed).
-    // X: wave w copies rows 64w + 8i + lane/8 (i < 8), lane%8 being the
-    // stored segment position; rows past M repeat row M-1 (their outputs are
-    // never stored).  Words: wave w copies k-rows 16w + lane/4, lane%4 being
+    // X: wave w copies rows (GB_M/4) w + 8i + lane/8 (i < A_COPIES), lane%8
+    // being the stored segment position; rows past M repeat row M-1 (their
+    // outputs are never stored).  Words: wave w copies k-rows 16w + lane/4, lane%4 being
     // the stored segment; word-columns past the end repeat the last 4.
     const char *const xg = (const char *)(x + (size_t)m0 * K);
     const char *const wg = (const char *)(qw + wc0);
@@ -98,10 +113,10 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(xg, (int64_t)(M - m0) * K * 2);
     const __amdgpu_buffer_rsrc_t wrs = buf_rsrc(wg, (int64_t)K * nw * 4 - (int64_t)wc0 * 4);
     const int lg = __builtin_ctz(G);  // G is 32, 64 or 128
-    uint32_t xoff[8];
+    uint32_t xoff[R::A_COPIES];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 64 * wave + 8 * i + (lane >> 3);
+    for (int i = 0; i < R::A_COPIES; ++i) {
+        const int r = (GB_M / 4) * wave + 8 * i + (lane >> 3);
         const int m = min(m0 + r, M - 1);
         xoff[i] = (uint32_t)(((m - m0) * K + 8 * aseg(r, lane & 7)) * 2);
     }
@@ -127,13 +142,15 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         m_voff = (uint32_t)((((32 * meta_ks) >> lg) * nw + meta_col) * 4);
     }
 
+    // copies of stage st into X buffer / word buffer `buf`
     auto copyA = [&](int st, int buf) {
-        unsigned char *dst = Abase + buf * GA_BYTES + 64 * wave * GA_PITCH;
+        unsigned char *dst = Abase + buf * GA_BYTES + (GB_M / 4) * wave * GA_PITCH;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dma16_buf(xrs, xoff[i], (uint32_t)st * (GB_K * 2), dst + 8 * i * GA_PITCH);
+        for (int i = 0; i < R::A_COPIES; ++i)
+            dma16_buf(xrs, xoff[i], (uint32_t)st * (GB_K * 2), dst + 8 * i * GA_PITCH);
     };
-    auto copyB = [&](int st) {
-        unsigned char *dst = Bbase + (st % GB_BUFS) * GB_BYTES;
+    auto copyB = [&](int st, int buf) {
+        unsigned char *dst = Bbase + buf * GB_BYTES;
         dma16_buf(wrs, woff, (uint32_t)st * (GB_K * 4) * (uint32_t)nw, dst + 16 * wave * GB_PITCH);
         if (wave == 0) {
             const uint32_t g0 = (uint32_t)((st * GB_K) >> lg);
@@ -142,9 +159,9 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         }
     };
 
-    f32x4 acc[16][2];
+    f32x4 acc[MT][2];
 #pragma unroll
-    for (int mt = 0; mt < 16; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int u = 0; u < 2; ++u) acc[mt][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -174,7 +191,7 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         const int g = (st * GB_K + 32 * ks) >> lg;
         if (g == gcur) return;
         gcur = g;
-        const unsigned char *Mt = Bbase + (st % GB_BUFS) * GB_BYTES + GB_WORDS;
+        const unsigned char *Mt = Bbase + ((st - s_lo) % BB) * GB_BYTES + GB_WORDS;
         const uint32_t s2 = *(const uint32_t *)(Mt + ks * (GB_N * 2) + wcl * 16 + 4 * pi);
         const uint32_t zw = SYM ? 0x88888888u : *(const uint32_t *)(Mt + GM_SCALES + ks * (GB_N / 2) + wcl * 4);
 #pragma unroll
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     };
     // packed words of k-step (st, ks): 8 consecutive k-rows of this lane's word-column
     auto load_words = [&](int st, int ks, uint32_t (&w)[8]) {
-        const unsigned char *B = Bbase + (st % GB_BUFS) * GB_BYTES;
+        const unsigned char *B = Bbase + ((st - s_lo) % BB) * GB_BYTES;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int r = 32 * ks + 8 * gq + e;
@@ -233,11 +250,22 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         return *(const u32x4 *)(A + r * GA_PITCH + aseg(r, 4 * ks + gq) * 16);
     };
 
+    // copies a stage leaves in flight at its end: those issued after the
+    // latest copy the next stage reads -- X of st + 1, issued at st + 2 - AB,
+    // or the words of st + 2 (read by its second k-step), issued at
+    // st + 3 - BB; within a stage X is issued first
+    constexpr int kA = R::A_COPIES, kB0 = SYM ? 2 : 3;  // wave 0 also copies the scales and zero points
+    constexpr int kSa = 2 - AB, kSb = 3 - BB;            // issue stages relative to st
+    constexpr int kFlight0 = kSa > kSb ? kB0 + (-kSa) * (kA + kB0) : (-kSb) * (kA + kB0);
+    constexpr int kFlight1 = kSa > kSb ? 1 + (-kSa) * (kA + 1) : (-kSb) * (kA + 1);
+    static_assert(kFlight0 < 64 && kFlight1 < 64, "vmcnt holds 6 bits");
+
     u32x4 bc[2];  // B operands of the current k-step
     if (s_lo < s_hi) {
-        copyB(s_lo);
-        copyA(s_lo, 0);
-        if (s_lo + 1 < s_hi) copyB(s_lo + 1);
+#pragma unroll
+        for (int d = 0; d < BB - 1; ++d) copyB(min(s_lo + d, s_hi - 1), d);
+#pragma unroll
+        for (int d = 0; d < AB - 1; ++d) copyA(min(s_lo + d, s_hi - 1), d);
     }
     wait_vm_all();
     __syncthreads();
@@ -250,12 +278,11 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         bc[1] = dequant(py, 1);
     }
     for (int st = s_lo; st < s_hi; ++st) {
-        const int abuf = (st - s_lo) & 1;
-        const bool more = st + 1 < s_hi;
-        if (more) copyA(st + 1, abuf ^ 1);
-        if (st + 2 < s_hi) copyB(st + 2);
-        const unsigned char *A = Abase + abuf * GA_BYTES;
-        u32x4 a[16];
+        const int rel = st - s_lo;
+        copyA(min(st + AB - 1, s_hi - 1), (rel + AB - 1) % AB);
+        copyB(min(st + BB - 1, s_hi - 1), (rel + BB - 1) % BB);
+        const unsigned char *A = Abase + (rel % AB) * GA_BYTES;
+        u32x4 a[MT];
 #pragma unroll
         for (int mt = 0; mt < kPrefA; ++mt) a[mt] = load_a(A, 0, mt);
 #pragma unroll
@@ -269,15 +296,15 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
             load_words(nst, nks, w);
             load_consts(nst, nks);
 #pragma unroll
-            for (int mt = 0; mt < 16; ++mt) {
+            for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) acc[mt][u] = mma<DT>(a[mt], bc[u], acc[mt][u]);
                 // X operands kPrefA row tiles ahead (within this stage only)
-                if (mt + kPrefA < 16) a[mt + kPrefA] = load_a(A, ks, mt + kPrefA);
-                else if (ks == 0) a[mt + kPrefA - 16] = load_a(A, 1, mt + kPrefA - 16);
+                if (mt + kPrefA < MT) a[mt + kPrefA] = load_a(A, ks, mt + kPrefA);
+                else if (ks == 0) a[mt + kPrefA - MT] = load_a(A, 1, mt + kPrefA - MT);
                 if (mt == 1) pair_words(w, px, py);
-                if (mt == 5) bn[0] = dequant(px, 0);
-                if (mt == 9) bn[1] = dequant(py, 1);
+                if (mt == 1 + MT / 4) bn[0] = dequant(px, 0);
+                if (mt == 1 + MT / 2) bn[1] = dequant(py, 1);
                 // keep each row tile's operand read where it is written: the
                 // scheduler would otherwise sink the reads next to their
                 // MFMAs and lose the prefetch distance
@@ -286,9 +313,15 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
             bc[0] = bn[0];
             bc[1] = bn[1];
         }
-        wait_vm_all();
-        __syncthreads();
+        if (wave == 0)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (kFlight0 & 15) | ((kFlight0 >> 4) << 14));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (kFlight1 & 15) | ((kFlight1 >> 4) << 14));
+        // no memory fence (it would wait for every copy); the clobber keeps
+        // LDS accesses from moving across the barrier
+        asm volatile("s_barrier" ::: "memory");
     }
+    wait_vm_all();  // the copies re-issued near the end land before the LDS is reused
 
     // Epilogue: lane holds rows m0 + 16mt + 4gq + r and columns 8*wcol + 2pi
     // (MFMA 0) and 8*wcol + 2pi + 1 (MFMA 1).  Without a K split it writes the
@@ -329,15 +362,16 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     };
     if (KS == 1) {
 #pragma unroll
-        for (int mt = 0; mt < 16; ++mt) emit(mt);
+        for (int mt = 0; mt < MT; ++mt) emit(mt);
         if (S > 1 && split_tile_last(cnt, S)) {
 #pragma unroll
-            for (int mt = 0; mt < 16; ++mt) finish(mt);
+            for (int mt = 0; mt < MT; ++mt) finish(mt);
         }
         return;
     }
     // group 1's idle iteration (odd stage count): its barrier only
     for (int k = s_hi - s_lo; k < iters; ++k) __syncthreads();
+    __syncthreads();  // every wave's copies have landed before the rings are reused
     // Both groups hold partial sums of the whole tile.  Group 0 finishes row
     // tiles 0..7 and group 1 row tiles 8..15: each parks the other half in
     // LDS (both rings are free once the last barrier has passed) and adds
@@ -382,27 +416,32 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     }
 }
 
-template <int DT, bool SYM, int KS>
+template <int DT, bool SYM, int KS, int MT, int AB, int BB>
 static hipError_t launch_gemm_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
-    hipLaunchKernelGGL((w4a16_gemm<DT, SYM, KS>), grid, dim3(256 * KS), 0, st, (const uint16_t *)a.x,
+    hipLaunchKernelGGL((w4a16_gemm<DT, SYM, KS, MT, AB, BB>), grid, dim3(256 * KS), 0, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
                        (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 
-template <int KS>
+template <int KS, int MT, int AB, int BB>
 static hipError_t launch_gemm_ks(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     const bool sym = a.qzeros == nullptr;
     if (a.dtype == DT_F16)
-        return sym ? launch_gemm_t<DT_F16, true, KS>(a, p, st) : launch_gemm_t<DT_F16, false, KS>(a, p, st);
-    return sym ? launch_gemm_t<DT_BF16, true, KS>(a, p, st) : launch_gemm_t<DT_BF16, false, KS>(a, p, st);
+        return sym ? launch_gemm_t<DT_F16, true, KS, MT, AB, BB>(a, p, st)
+                   : launch_gemm_t<DT_F16, false, KS, MT, AB, BB>(a, p, st);
+    return sym ? launch_gemm_t<DT_BF16, true, KS, MT, AB, BB>(a, p, st)
+               : launch_gemm_t<DT_BF16, false, KS, MT, AB, BB>(a, p, st);
 }
 
+// p.deep: 128-row tiles with rings of 3 X and 8 word buffers (M < 128);
+// else 256-row tiles with rings of 2 and 3
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     // a K split reduces through the workspace
     if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
-    return p.ksplit == 2 ? launch_gemm_ks<2>(a, p, st) : launch_gemm_ks<1>(a, p, st);
+    if (p.deep) return launch_gemm_ks<1, 8, 3, 8>(a, p, st);
+    return p.ksplit == 2 ? launch_gemm_ks<2, 16, 2, 3>(a, p, st) : launch_gemm_ks<1, 16, 2, 3>(a, p, st);
 }
 
 }  // namespace awq4

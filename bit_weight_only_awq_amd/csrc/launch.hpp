@@ -27,8 +27,9 @@ struct W4A16Plan {
     int blk;      // decode: word-columns per lane (1, 2)
     int cs;       // decode: 32-k steps per wave chunk (1, 2, 4)
     int waves;    // decode: waves per workgroup (4)
-    int mt;       // tiled: row tiles per wave (1, 2, 4)
+    int mt;       // tiled: row tiles per wave (1, 2, 4); LDS GEMM: 16 or 8
     int ksplit;   // LDS GEMM: groups of 4 waves per workgroup splitting K (1, 2)
+    int deep;     // LDS GEMM: deep copy rings for mid-size M (3 X and 8 word buffers)
     int tiles_n;  // grid x
     int tiles_m;  // tiled: grid y
     int splits;   // workgroups along K (1 = none); decode: grid y
