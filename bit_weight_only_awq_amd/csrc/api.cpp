@@ -99,12 +99,18 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
             // one workgroup per CU: K splits up to one workgroup per CU
             s = std::min<int64_t>(std::max<int64_t>(1, 256 / tiles), kW16DeepMaxSplits);
             s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
-        } else {
-            // K splits only for few tiles (measured at M = 128..1024 on the
-            // Llama-3-8B layers: the partial tiles cost more than a third
-            // split saves); the in-workgroup K split below adds parallelism
+        } else if (M <= 256 - 128) {
+            // M = 128: half-padded 256-row tiles, whose partial tiles are cheap
             s = tiles <= 32 ? 4 : tiles <= 64 ? 2 : 1;
             s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 4));
+        } else {
+            // K splits only for few tiles and long K: about one per 56 stages,
+            // at most 4 (<= 64 tiles) or 2 (<= 128 tiles).  Measured at
+            // M = 192..1024 on the Llama-3-8B layers: each split's partial
+            // tile, summed by one workgroup, costs more than it gains on
+            // K = 4096 and pays for itself on K = 14336.
+            const int64_t cap = tiles <= 64 ? 4 : tiles <= 128 ? 2 : 1;
+            s = std::min<int64_t>(cap, std::max<int64_t>(1, stages / 56));
         }
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
