@@ -172,7 +172,11 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         // LDS-pipelined int8 GEMM, K in stages of 64: 128 x 256 workgroup
         // tiles (8 waves) when there are enough of them, else 128 x 128 (4 waves)
         p.kind = 2;
-        p.blk = cdiv(N, 256) * cdiv(M, 128) >= kW8WideMinTiles ? 2 : 1;
+        const int64_t wide = cdiv(N, 256) * cdiv(M, 128);
+        p.blk = wide >= kW8WideMinTiles ? 2 : 1;
+        // no more wide tiles than CUs: two groups of 8 waves per workgroup
+        // split K inside it (four waves per SIMD instead of two)
+        p.ksplit = p.blk == 2 && wide <= 256 && T >= 8 ? 2 : 1;
         p.mt = 4;
         p.tiles_n = (int)cdiv(N, 128 * p.blk);
         p.tiles_m = (int)cdiv(M, 128);

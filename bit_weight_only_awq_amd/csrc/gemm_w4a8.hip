@@ -46,23 +46,29 @@ __device__ __forceinline__ int a8seg(int r, int s) { return s ^ (((r >> 1) ^ (r 
 
 // Workgroup tile 128 x 32*NW, K in stages of 64 (one 16x16x64 step); NW waves
 // in a 2 x NW/2 grid, each owning 64 x 64 outputs: 4 row tiles x 4 column MFMAs.
+// KS = 2: two such groups of NW waves share the tile and split its K stages,
+// each with its own LDS ring, and add their int32 sums through LDS at the end
+// (twice the waves per SIMD when there are no more tiles than CUs).
 // Lane j reads 16 bytes = 4 consecutive columns of two K8 word rows, which
 // give the B operands of its 4 MFMAs (output column = 64 wn + 4j + u).
 // a8 rows, word rows and (grouped) s3 rows are copied into 4-slot LDS rings
 // three stages ahead; each stage waits only for the copies older than its
 // own, so the next stage is always readable and its operands are loaded while
 // the current stage's MFMAs run.
-template <int NW, bool GROUP, int DT>
-__global__ __launch_bounds__(64 * NW, 2) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
+template <int NW, int KS, bool GROUP, int DT>
+__global__ __launch_bounds__(64 * NW * KS, 2 / KS) void w4a8_gemm_lds(const int8_t *__restrict__ a8, const uint32_t *__restrict__ bq,
                                                        const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                        const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                        int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
                                                        int M, int N, int K, int G, int S) {
     using L = W8Layout<NW, GROUP>;
     constexpr int W8_N = L::WN;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[L::LDS];
+    static_assert(KS * L::LDS >= KS * NW * 8 * 64 * 16, "the K-split handover fits in the rings");
+    __shared__ __attribute__((aligned(16))) unsigned char lds_all[KS * L::LDS];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int grp = KS == 1 ? 0 : wv / NW, wave = wv % NW;
+    unsigned char *const lds = lds_all + grp * L::LDS;
     const int j = lane & 15, gq = lane >> 4;
     const int wm = wave / (NW / 2), wn = wave % (NW / 2);
     // logical tile of this workgroup (XCD-aware order over the tiles_n x tiles_m grid)
@@ -70,7 +76,11 @@ __global__ __launch_bounds__(64 * NW, 2) void w4a8_gemm_lds(const int8_t *__rest
     const int tn = tile % gridDim.x, tm = tile / gridDim.x, split = blockIdx.z;
     const int m0 = tm * W8_M, n0 = tn * W8_N;
     const int Tst = K / W8_K;
-    const int s_lo = (int)((int64_t)Tst * split / S), s_hi = (int)((int64_t)Tst * (split + 1) / S);
+    const int w_lo = (int)((int64_t)Tst * split / S), w_hi = (int)((int64_t)Tst * (split + 1) / S);
+    // stages of this group: group 0 the first ceil(n/KS), group 1 the rest;
+    // both pass `iters` stage barriers (group 1 adds an idle one if n is odd)
+    const int iters = (w_hi - w_lo + KS - 1) / KS;
+    const int s_lo = w_lo + grp * iters, s_hi = min(w_hi, s_lo + iters);
 
     // Copy assignment.  a8: wave w copies rows 16 (A_COPIES w + i) + lane/4
     // (i < A_COPIES), lane%4 being the stored segment position; rows past M
@@ -194,16 +204,17 @@ __global__ __launch_bounds__(64 * NW, 2) void w4a8_gemm_lds(const int8_t *__rest
         asm volatile("s_barrier" ::: "memory");
     };
 
-    if (s_lo < s_hi) {
+    {
         Ops o;
+        if (s_lo < s_hi) {
 #pragma unroll
-        for (int d = 0; d < W8_RING - 1; ++d)
-            if (s_lo + d < s_hi) copy_stage(s_lo + d, d);
+            for (int d = 0; d < W8_RING - 1; ++d)
+                if (s_lo + d < s_hi) copy_stage(s_lo + d, d);
+        }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        load_ops(0, o);
-        int st = s_lo;
-        for (; st < s_hi; ++st) stage(st, o);
+        if (s_lo < s_hi) load_ops(0, o);
+        for (int st = s_lo; st < s_hi; ++st) stage(st, o);
     }
 
     // Epilogue: lane holds rows m0 + 64 wm + 16 mt + 4 gq + r, columns
@@ -229,6 +240,49 @@ __global__ __launch_bounds__(64 * NW, 2) void w4a8_gemm_lds(const int8_t *__rest
                                                      (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
         if (acc_out) *(i32x4 *)(acc_out + (size_t)m * N + nc) = (i32x4){v[0], v[1], v[2], v[3]};
     };
+    if constexpr (KS == 2) {
+        // (S == 1.)  Group 1's idle stage barrier, then both rings are free:
+        // group 0 finishes row tiles 0, 1 of each wave tile and group 1 row
+        // tiles 2, 3; each parks the other pair in LDS and adds the pair
+        // parked for it (int32: exact in any order).
+        for (int k = max(s_hi - s_lo, 0); k < iters; ++k) asm volatile("s_barrier" ::: "memory");
+        wait_vm_all();
+        __syncthreads();
+        i32x4 *const mine = (i32x4 *)lds_all + (size_t)(grp * NW + wave) * 8 * 64 + lane;
+        const i32x4 *const theirs = (const i32x4 *)lds_all + (size_t)((grp ^ 1) * NW + wave) * 8 * 64 + lane;
+        if (grp == 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) mine[(4 * h + u) * 64] = acc[2 + h][u];
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) mine[(4 * h + u) * 64] = acc[h][u];
+        }
+        __syncthreads();
+        if (!col_ok) return;
+        auto finish_pair = [&](auto mt0c) {
+            constexpr int mt0 = decltype(mt0c)::value;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[mt0 + h][u] += theirs[(4 * h + u) * 64];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm * 64 + 16 * (mt0 + h) + 4 * gq + r;
+                    if (m < M)
+                        store4(m, (i32x4){acc[mt0 + h][0][r], acc[mt0 + h][1][r], acc[mt0 + h][2][r],
+                                          acc[mt0 + h][3][r]});
+                }
+        };
+        if (grp == 0) finish_pair(std::integral_constant<int, 0>{});
+        else finish_pair(std::integral_constant<int, 2>{});
+        return;
+    }
     if (S == 1) {
         if (!col_ok) return;
 #pragma unroll
@@ -273,25 +327,33 @@ __global__ __launch_bounds__(64 * NW, 2) void w4a8_gemm_lds(const int8_t *__rest
         }
 }
 
-template <int NW, bool GROUP, int DT>
+template <int NW, int KS, bool GROUP, int DT>
 static hipError_t launch_lds8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    hipLaunchKernelGGL((w4a8_gemm_lds<NW, GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(64 * NW), 0, st,
+    hipLaunchKernelGGL((w4a8_gemm_lds<NW, KS, GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(64 * NW * KS),
+                       0, st,
                        a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
                        (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 
-template <int NW>
+template <int NW, int KS>
 static hipError_t launch_lds8_nw(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     if (a.dtype == DT_BF16)
-        return a.s3 != nullptr ? launch_lds8<NW, true, DT_BF16>(a, p, st) : launch_lds8<NW, false, DT_BF16>(a, p, st);
-    return a.s3 != nullptr ? launch_lds8<NW, true, DT_F16>(a, p, st) : launch_lds8<NW, false, DT_F16>(a, p, st);
+        return a.s3 != nullptr ? launch_lds8<NW, KS, true, DT_BF16>(a, p, st)
+                               : launch_lds8<NW, KS, false, DT_BF16>(a, p, st);
+    return a.s3 != nullptr ? launch_lds8<NW, KS, true, DT_F16>(a, p, st) : launch_lds8<NW, KS, false, DT_F16>(a, p, st);
 }
 
-// p.blk: workgroup tile width in 128-column units (1: 128 x 128, 2: 128 x 256)
+// p.blk: workgroup tile width in 128-column units (1: 128 x 128, 2: 128 x 256);
+// p.ksplit: groups of waves splitting K inside a workgroup (128 x 256 tiles
+// without a K split only)
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
-    return p.blk == 2 ? launch_lds8_nw<8>(a, p, st) : launch_lds8_nw<4>(a, p, st);
+    if (p.blk == 2 && p.ksplit == 2) {
+        if (p.splits != 1) return hipErrorInvalidValue;
+        return launch_lds8_nw<8, 2>(a, p, st);
+    }
+    return p.blk == 2 ? launch_lds8_nw<8, 1>(a, p, st) : launch_lds8_nw<4, 1>(a, p, st);
 }
 
 }  // namespace awq4

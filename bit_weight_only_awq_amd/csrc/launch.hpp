@@ -60,6 +60,7 @@ struct W4A8Plan {
     int mt;    // row tiles (skinny: M <= 16*mt; tiled and LDS GEMM: per wave)
     int tiles_n, tiles_m, splits;
     int tilered;  // split-K through partial tiles (else per-element atomics; skinny kernel only)
+    int ksplit;   // LDS GEMM: groups of waves splitting K inside a workgroup (1, 2)
     size_t workspace_bytes;
     uint64_t *acc;
 };

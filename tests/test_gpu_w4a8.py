@@ -91,7 +91,10 @@ def test_w4a8_qqq_shape(M, G):
                                    (300, 4096, 1032), (5, 64, 8),
                                    (17, 128, 136), (40, 256, 24), (129, 512, 1032), (33, 4096, 520),
                                    # 128 x 256 tiles with a ragged last row and column tile
-                                   (2049, 256, 4104), (4000, 128, 2056)])
+                                   (2049, 256, 4104), (4000, 128, 2056),
+                                   # one 128 x 256 tile per CU (K split inside the workgroup),
+                                   # ragged, with an odd stage count
+                                   (1000, 1088, 8184)])
 def test_w4a8_shapes(M, K, N, G):
     if G > 0 and K % G:
         pytest.skip("K not a multiple of G")
