@@ -34,7 +34,7 @@ static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // workgroups of the CS <= 2 decode kernel resident at once (4 per CU)
-constexpr int64_t kDecodeResidentWGs = 4 * 256;
+constexpr int64_t kDecodeResidentWGs = 4 * 256, kDecodeSmallChunkWGs = 2 * 256;
 
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry) {
     (void)gemv_entry;
@@ -50,6 +50,11 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.cs = G >= 64 ? 2 : 1;
         p.waves = 4;
         p.tiles_n = (int)cdiv(nw, 16 * p.blk);
+        // 32-k chunks when that still gives at most two workgroups per CU:
+        // twice the waves per SIMD on narrow layers (measured at M = 1 on
+        // 4096 x 4096: 5.14 -> 4.88 us; layers past that bound were slower,
+        // and each extra split adds an atomic per output element and row)
+        if (M <= 2 && (int64_t)p.tiles_n * cdiv(K / 32, p.waves) <= kDecodeSmallChunkWGs) p.cs = 1;
         p.tiles_m = 1;
         p.splits = (int)cdiv(K / (32 * p.cs), p.waves);
         // more workgroups than stay resident (4 per CU): one 128-k group per
