@@ -21,7 +21,7 @@ static constexpr int kTargetWorkgroups = 512;  // 256 CUs x 2 workgroups of 4 wa
 // (measured on the Llama-3-8B layers at M = 32..128: more splits cost more in
 // partial tiles than they gain, and 256-row tiles with deep rings, at one
 // wave per SIMD, were slower than the large-M configuration from M = 128 up).
-static constexpr int64_t kW16LdsMinM = 16, kW16DeepMaxM = 127, kW16DeepMaxSplits = 4;
+static constexpr int64_t kW16LdsMinM = 16, kW16DeepMaxM = 127, kW16DeepMaxSplits = 4, kW16TallTilesMin = 129;
 // The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, two per CU) are used
 // whenever there are at least as many as CUs; with fewer, the 128 x 128 tiles
 // give more workgroups before a K split is needed (measured: M = 512 on
@@ -90,11 +90,17 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
     // buffer-descriptor copies address X and the packed words with 32-bit offsets
     const bool fits_rsrc = M * K * 2 < (int64_t(1) << 31) && K * (N / 2) < (int64_t(1) << 31);
     if (M > kW16LdsMinM && K % 64 == 0 && N % 32 == 0 && fits_rsrc) {
-        // LDS-pipelined GEMM: 256-row (M >= 128) or 128-row x 128 workgroup
-        // tiles, K in stages of 64
+        // LDS-pipelined GEMM: 256- or 128-row x 128 workgroup tiles, K in
+        // stages of 64
         p.kind = 3;
         p.deep = M <= kW16DeepMaxM;
-        p.mt = p.deep ? 8 : 16;
+        // 128-row tiles at M <= 128 (256-row ones would be half padding) and
+        // where there would be at most 128 tiles of 256 rows (half the CUs
+        // idle).  Measured on the Llama-3-8B layers at M = 128..2048: o at
+        // M = 256, 56 -> 37 us; down at M = 128, 90 -> 57 us; with more
+        // 256-row tiles than that (qkv at M = 1024, gate/up at M = 256) the
+        // 256-row tiles' better operand reuse wins.
+        p.mt = (M <= 128 || cdiv(N, 128) * cdiv(M, 256) <= kW16TallTilesMin - 1) ? 8 : 16;
         p.tiles_n = (int)cdiv(N, 128);
         p.tiles_m = (int)cdiv(M, 16 * p.mt);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
@@ -104,8 +110,8 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
             // one workgroup per CU: K splits up to one workgroup per CU
             s = std::min<int64_t>(std::max<int64_t>(1, 256 / tiles), kW16DeepMaxSplits);
             s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
-        } else if (M <= 256 - 128) {
-            // M = 128: half-padded 256-row tiles, whose partial tiles are cheap
+        } else if (M <= 128) {
+            // few rows: the partial tiles are small, split by the tile count
             s = tiles <= 32 ? 4 : tiles <= 64 ? 2 : 1;
             s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 4));
         } else {

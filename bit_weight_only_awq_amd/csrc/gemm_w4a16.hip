@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
                                                                 uint16_t *__restrict__ y, uint64_t *__restrict__ acc64,
                                                                 int M, int N, int K, int G, int S) {
     using R = GRing<MT, AB, BB>;
-    static_assert(KS == 1 || MT == 16, "the in-workgroup K split hands over half of 16 row tiles");
+    static_assert(KS == 1 || KS * R::LDS >= 2 * 4 * MT * 64 * 16, "the K-split handover fits in the rings");
     static_assert(AB >= 2 && BB >= 3 && MT > kPrefA, "ring depths and prefetch distance");
     constexpr int GB_M = R::M_TILE, GA_BYTES = R::A_BYTES, G_LDS = R::LDS;
     __shared__ __attribute__((aligned(16))) unsigned char lds_all[KS * G_LDS];
@@ -373,45 +373,47 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     for (int k = s_hi - s_lo; k < iters; ++k) __syncthreads();
     __syncthreads();  // every wave's copies have landed before the rings are reused
     // Both groups hold partial sums of the whole tile.  Group 0 finishes row
-    // tiles 0..7 and group 1 row tiles 8..15: each parks the other half in
-    // LDS (both rings are free once the last barrier has passed) and adds
-    // the half parked by the other group, always as group 0 + group 1.
-    f32x4 *xfer = (f32x4 *)lds_all + (size_t)wave * 16 * 64 + lane;
-    f32x4 *const mine = xfer + grp * 4 * 16 * 64, *const theirs = xfer + (grp ^ 1) * 4 * 16 * 64;
+    // tiles 0..H-1 and group 1 row tiles H..MT-1 (H = MT/2): each parks the
+    // other half in LDS (both rings are free once the last barrier has
+    // passed) and adds the half parked by the other group, always as
+    // group 0 + group 1.
+    constexpr int H = MT / 2;
+    f32x4 *xfer = (f32x4 *)lds_all + (size_t)wave * MT * 64 + lane;
+    f32x4 *const mine = xfer + grp * 4 * MT * 64, *const theirs = xfer + (grp ^ 1) * 4 * MT * 64;
     if (grp == 0) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < H; ++mt)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[8 + mt][u];
+            for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[H + mt][u];
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < H; ++mt)
 #pragma unroll
             for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[mt][u];
     }
     __syncthreads();
     if (grp == 0) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
+        for (int mt = 0; mt < H; ++mt) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) acc[mt][u] += theirs[(mt * 2 + u) * 64];
             emit(mt);
         }
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
+        for (int mt = 0; mt < H; ++mt) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) acc[8 + mt][u] = theirs[(mt * 2 + u) * 64] + acc[8 + mt][u];
-            emit(8 + mt);
+            for (int u = 0; u < 2; ++u) acc[H + mt][u] = theirs[(mt * 2 + u) * 64] + acc[H + mt][u];
+            emit(H + mt);
         }
     }
     if (S > 1 && split_tile_last(cnt, S)) {
         if (grp == 0) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) finish(mt);
+            for (int mt = 0; mt < H; ++mt) finish(mt);
         } else {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) finish(8 + mt);
+            for (int mt = 0; mt < H; ++mt) finish(H + mt);
         }
     }
 }
@@ -436,11 +438,12 @@ static hipError_t launch_gemm_ks(const W4A16Args &a, const W4A16Plan &p, hipStre
 }
 
 // p.deep: 128-row tiles with rings of 3 X and 8 word buffers (M < 128);
-// else 256-row tiles with rings of 2 and 3
+// else 256-row (p.mt = 16) or 128-row (p.mt = 8) tiles with rings of 2 and 3
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     // a K split reduces through the workspace
     if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
     if (p.deep) return launch_gemm_ks<1, 8, 3, 8>(a, p, st);
+    if (p.mt == 8) return p.ksplit == 2 ? launch_gemm_ks<2, 8, 2, 3>(a, p, st) : launch_gemm_ks<1, 8, 2, 3>(a, p, st);
     return p.ksplit == 2 ? launch_gemm_ks<2, 16, 2, 3>(a, p, st) : launch_gemm_ks<1, 16, 2, 3>(a, p, st);
 }
 
