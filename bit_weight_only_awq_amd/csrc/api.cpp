@@ -192,6 +192,8 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         p.tiles_n = (int)cdiv(N, 128 * p.blk);
         p.tiles_m = (int)cdiv(M, 128);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
+        // (more splits measured slower at M = 128..512: every split adds an
+        // M x N int32 partial tile written, read back and cleared)
         int64_t s = 1;
         if (tiles < 256) s = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, T / 4));
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);

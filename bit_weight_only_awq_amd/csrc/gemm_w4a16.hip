@@ -344,29 +344,58 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
                 *(f32x2 *)(part + split * slot + (size_t)m * N + n0) = (f32x2){acc[mt][0][r], acc[mt][1][r]};
         }
     };
-    auto finish = [&](int mt) {
-        if (!col_ok) return;
+    // The tile's last split sums the S partials of row tiles LO..LO+NT-1 in
+    // split order, four row tiles (16 of the lane's rows) at a time: for each
+    // split the loads of those rows are in flight together (S memory round
+    // trips per batch rather than one per row and split); the partials are
+    // cleared after the batch's last load.
+    auto finish4 = [&](auto lo_c) {
+        constexpr int LO = decltype(lo_c)::value;
+        f32x2 v[4][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 16 * mt + 4 * gq + r;
-            if (m >= M) continue;
-            f32x2 v = {0.f, 0.f};
-            for (int s = 0; s < S; ++s) {
-                f32x2 *src = (f32x2 *)(part + s * slot + (size_t)m * N + n0);
-                v += *src;
-                *src = (f32x2){0.f, 0.f};
-            }
-            *(uint32_t *)(y + (size_t)m * N + n0) =
-                (uint32_t)f32_to_out_bits(v[0], DT) | ((uint32_t)f32_to_out_bits(v[1], DT) << 16);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[i][r] = (f32x2){0.f, 0.f};
+        for (int sp = 0; sp < S; ++sp) {
+            const float *base = part + sp * slot + n0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + 16 * (LO + i) + 4 * gq + r;
+                    if (m < M) v[i][r] += *(const f32x2 *)(base + (size_t)m * N);
+                }
         }
+        for (int sp = 0; sp < S; ++sp) {
+            float *base = part + sp * slot + n0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + 16 * (LO + i) + 4 * gq + r;
+                    if (m < M) *(f32x2 *)(base + (size_t)m * N) = (f32x2){0.f, 0.f};
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * (LO + i) + 4 * gq + r;
+                if (m < M)
+                    *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(v[i][r][0], DT) |
+                                                            ((uint32_t)f32_to_out_bits(v[i][r][1], DT) << 16);
+            }
+    };
+    auto finish = [&](auto lo_c, auto nt_c) {
+        constexpr int LO = decltype(lo_c)::value, NT = decltype(nt_c)::value;
+        static_assert(NT % 4 == 0, "row tiles in batches of four");
+        if (!col_ok) return;
+        static_for<NT / 4>([&](auto bc) { finish4(std::integral_constant<int, LO + 4 * decltype(bc)::value>{}); });
     };
     if (KS == 1) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) emit(mt);
-        if (S > 1 && split_tile_last(cnt, S)) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) finish(mt);
-        }
+        if (S > 1 && split_tile_last(cnt, S)) finish(std::integral_constant<int, 0>{}, std::integral_constant<int, MT>{});
         return;
     }
     // group 1's idle iteration (odd stage count): its barrier only
@@ -408,13 +437,8 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         }
     }
     if (S > 1 && split_tile_last(cnt, S)) {
-        if (grp == 0) {
-#pragma unroll
-            for (int mt = 0; mt < H; ++mt) finish(mt);
-        } else {
-#pragma unroll
-            for (int mt = 0; mt < H; ++mt) finish(H + mt);
-        }
+        if (grp == 0) finish(std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
+        else finish(std::integral_constant<int, H>{}, std::integral_constant<int, H>{});
     }
 }
 

@@ -311,20 +311,44 @@ __global__ __launch_bounds__(64 * NW * KS, 2 / KS) void w4a8_gemm_lds(const int8
             }
     }
     if (!split_tile_last(cnt, S) || !col_ok) return;
+    // the last split sums the partials, one row tile (4 of the lane's rows)
+    // at a time: per split, the loads of those rows are in flight together;
+    // the partials are cleared after the batch's last load
+    static_for<4>([&](auto bc) {
+        constexpr int MT0 = decltype(bc)::value;
+        i32x4 v[1][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int h = 0; h < 1; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-            if (m >= M) continue;
-            i32x4 v = {0, 0, 0, 0};
-            for (int sp = 0; sp < S; ++sp) {
-                i32x4 *src = (i32x4 *)(part + sp * slot + (size_t)m * N + nc);
-                v += *src;
-                *src = (i32x4){0, 0, 0, 0};
-            }
-            store4(m, v);
+            for (int r = 0; r < 4; ++r) v[h][r] = (i32x4){0, 0, 0, 0};
+        for (int sp = 0; sp < S; ++sp) {
+            const int32_t *base = part + sp * slot + nc;
+#pragma unroll
+            for (int h = 0; h < 1; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm * 64 + 16 * (MT0 + h) + 4 * gq + r;
+                    if (m < M) v[h][r] += *(const i32x4 *)(base + (size_t)m * N);
+                }
         }
+        for (int sp = 0; sp < S; ++sp) {
+            int32_t *base = part + sp * slot + nc;
+#pragma unroll
+            for (int h = 0; h < 1; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + wm * 64 + 16 * (MT0 + h) + 4 * gq + r;
+                    if (m < M) *(i32x4 *)(base + (size_t)m * N) = (i32x4){0, 0, 0, 0};
+                }
+        }
+#pragma unroll
+        for (int h = 0; h < 1; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + wm * 64 + 16 * (MT0 + h) + 4 * gq + r;
+                if (m < M) store4(m, v[h][r]);
+            }
+    });
 }
 
 template <int NW, int KS, bool GROUP, int DT>

@@ -358,22 +358,43 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
             }
     }
     if (!split_tile_last(cnt, S) || !col_ok) return;
+    // the last split sums the partials in split order, two of the lane's rows
+    // at a time: per split, the loads of those rows are in flight together;
+    // the partials are cleared after the batch's last load
 #pragma unroll
-    for (int mt = 0; mt < MTW; ++mt)
+    for (int b = 0; b < 2 * MTW; ++b) {
+        const int mt = b >> 1, r0 = 2 * (b & 1);
+        f32x4 v0[2], v1[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 16 * mt + 4 * gq + r;
-            if (m >= M) continue;
-            f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < S; ++s) {
-                float *src = part + s * slot + (size_t)m * N + n0;
-                v0 += *(const f32x4 *)src;
-                v1 += *(const f32x4 *)(src + 4);
-                *(f32x4 *)src = (f32x4){0.f, 0.f, 0.f, 0.f};
-                *(f32x4 *)(src + 4) = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < 2; ++r) v0[r] = v1[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S; ++s) {
+            const float *base = part + s * slot + n0;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r0 + r;
+                if (m < M) {
+                    v0[r] += *(const f32x4 *)(base + (size_t)m * N);
+                    v1[r] += *(const f32x4 *)(base + (size_t)m * N + 4);
+                }
             }
-            *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0, v1);
         }
+        for (int s = 0; s < S; ++s) {
+            float *base = part + s * slot + n0;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r0 + r;
+                if (m < M) {
+                    *(f32x4 *)(base + (size_t)m * N) = (f32x4){0.f, 0.f, 0.f, 0.f};
+                    *(f32x4 *)(base + (size_t)m * N + 4) = (f32x4){0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int m = m0 + 16 * mt + 4 * gq + r0 + r;
+            if (m < M) *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0[r], v1[r]);
+        }
+    }
 }
 
 // ===========================================================================

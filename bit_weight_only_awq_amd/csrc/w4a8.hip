@@ -508,21 +508,39 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
             }
     }
     if (!split_tile_last(cnt, S) || !ok) return;
+    // the last split sums the partials, one row tile (4 of the lane's rows)
+    // at a time: per split, the loads of those rows are in flight together;
+    // the partials are cleared after the batch's last load
 #pragma unroll
-    for (int mt = 0; mt < MTW; ++mt)
+    for (int mt = 0; mt < MTW; ++mt) {
+        i32x4 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (i32x4){0, 0, 0, 0};
+        for (int sp = 0; sp < S; ++sp) {
+            const int32_t *base = part + sp * slot + ncol;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M) v[r] += *(const i32x4 *)(base + (size_t)m * N);
+            }
+        }
+        for (int sp = 0; sp < S; ++sp) {
+            int32_t *base = part + sp * slot + ncol;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M) *(i32x4 *)(base + (size_t)m * N) = (i32x4){0, 0, 0, 0};
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = m0 + 16 * mt + 4 * gq + r;
-            if (m >= M) continue;
-            i32x4 v = {0, 0, 0, 0};
-            for (int sp = 0; sp < S; ++sp) {
-                i32x4 *src = (i32x4 *)(part + sp * slot + (size_t)m * N + ncol);
-                v += *src;
-                *src = (i32x4){0, 0, 0, 0};
-            }
+            if (m < M) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) w4a8_store<GROUP, DT>(v[i], m, ncol + i, N, s1, s2, y, acc_out);
+                for (int i = 0; i < 4; ++i) w4a8_store<GROUP, DT>(v[r][i], m, ncol + i, N, s1, s2, y, acc_out);
+            }
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
