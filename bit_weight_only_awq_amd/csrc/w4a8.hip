@@ -559,7 +559,7 @@ template <int BLK, int MT, bool GROUP, bool FUSED, int DT>
 static hipError_t launch_skinny8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     const int qa_stride = FUSED ? (int)w4a8_fused_qa_stride(a.M, a.K, p.splits) : 0;
     const size_t lds = FUSED ? w4a8_fused_lds_bytes(a.M, a.K, BLK, p.splits)
-                             : (size_t)4 * a.M * 64 * BLK * sizeof(int32_t) + 64 * sizeof(uint32_t);
+                             : (size_t)4 * a.M * 64 * BLK * sizeof(int32_t);  // wave partials only
     hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP, FUSED, DT>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
                        (const uint16_t *)a.x, (const uint32_t *)a.b, a.s1, a.s1_out, (const uint16_t *)a.s2,
                        (const uint16_t *)a.s3, (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K,
@@ -583,6 +583,7 @@ static hipError_t launch_w4a8_t(const W4A8Args &a, const W4A8Plan &p, hipStream_
             case 11: return launch_skinny8<1, 1, GROUP, false, DT>(a, p, st);
             case 21: return launch_skinny8<2, 1, GROUP, false, DT>(a, p, st);
             case 12: return launch_skinny8<1, 2, GROUP, false, DT>(a, p, st);
+            case 14: return launch_skinny8<1, 4, GROUP, false, DT>(a, p, st);
             default: return hipErrorInvalidValue;
         }
     }

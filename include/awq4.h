@@ -110,10 +110,10 @@ int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, in
  * Workspace rules ([P2]: one workspace per device, reused by every layer):
  *  - it is caller-owned, 16-byte aligned, and may be shared by any number of
  *    calls that are ordered on one stream;
- *  - a split-K decode GEMV, or a W4A8 call with M <= 32, uses one 64-bit
+ *  - a split-K decode GEMV, or a W4A8 call with M <= 64, uses one 64-bit
  *    counting accumulator per output element (M x N); the last
  *    contribution to an element writes the output and clears it;
- *  - the GEMM kernels (M > 16 for W4A16, M > 32 for W4A8) use one 32-bit
+ *  - the GEMM kernels (M > 16 for W4A16, M > 64 for W4A8) use one 32-bit
  *    arrival counter per output tile (padded to 256 bytes) followed by S
  *    partial [M, N] results of 4 bytes each (fp32 for W4A16, int32 for
  *    W4A8); the last workgroup of a tile to arrive adds the S partials in
