@@ -14,10 +14,7 @@
 namespace awq4 {
 
 constexpr int W8_M = 128, W8_K = 64;
-#ifndef AWQ4_W8_RING
-#define AWQ4_W8_RING 4
-#endif
-constexpr int W8_RING = AWQ4_W8_RING;              // stages per LDS ring (copied W8_RING - 1 ahead)
+constexpr int W8_RING = 4;                         // stages per LDS ring (copied W8_RING - 1 ahead)
 constexpr int W8_APITCH = W8_K;                    // 64 bytes of a8 per row (4 segments, swizzled)
 constexpr int W8_ABYTES = W8_M * W8_APITCH;        // 8192 per stage
 

@@ -157,7 +157,9 @@ def test_gemm_activation_bytes_at_2_31(M):
 
 
 @pytest.mark.parametrize("M,K,N,G,split", [(200, 1216, 256, 64, 0), (200, 1216, 256, 64, 3), (130, 1216, 384, 32, 0),
-                                           (256, 1152, 4096, 128, 0), (513, 4096, 1032, 128, 0), (300, 640, 640, 64, 0)])
+                                           (256, 1152, 4096, 128, 0), (513, 4096, 1032, 128, 0), (300, 640, 640, 64, 0),
+                                           # 128-row tiles above M = 128, 65 stages, with and without K splits
+                                           (300, 4160, 1032, 64, 0), (300, 4160, 1032, 64, 2)])
 def test_gemm_few_tiles(M, K, N, G, split):
     """Layers with no more tiles than CUs: the workgroup's two wave groups
     split its K stages, odd stage counts included (19 stages over 4 splits:
