@@ -55,6 +55,12 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         // 4096 x 4096: 5.14 -> 4.88 us; layers past that bound were slower,
         // and each extra split adds an atomic per output element and row)
         if (M <= 2 && (int64_t)p.tiles_n * cdiv(K / 32, p.waves) <= kDecodeSmallChunkWGs) p.cs = 1;
+        // M >= 4: one 128-k group per wave when that still gives three
+        // quarters of the CUs a workgroup -- half the K splits, so half the
+        // per-element atomics, which grow with M (measured at M = 16: down
+        // 11008 x 4096 35.2 -> 21.0 us, qkv 4096 x 6144 16.2 -> 14.7 us;
+        // 4096 x 4096, with 128 such workgroups, was slower)
+        if (M >= 4 && G % 128 == 0 && (int64_t)p.tiles_n * cdiv(K / 128, p.waves) >= 192) p.cs = 4;
         p.tiles_m = 1;
         p.splits = (int)cdiv(K / (32 * p.cs), p.waves);
         // more workgroups than stay resident (4 per CU): one 128-k group per
