@@ -412,7 +412,7 @@ int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packe
     hipStream_t st = static_cast<hipStream_t>(stream);
     W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
     a.dtype = dtype;
-    if (dtype == AWQ_DTYPE_F16 && w4a8_fuses_quant(M, K, p)) {
+    if (w4a8_fuses_quant(M, K, p)) {
         a.x = x_f16;
         a.s1_out = s1;
         return hip_status(launch_w4a8_fused(a, p, st));

@@ -48,7 +48,7 @@ struct W4A8Args {
     int32_t *acc_out;  // may be nullptr
     int64_t M, N, K;
     int G;  // -1 = per-channel
-    // fused quantisation (w4a8_linear): fp16 activations and the s1 output
+    // fused quantisation (w4a8_linear): fp16 or bf16 activations and the s1 output
     const void *x = nullptr;
     float *s1_out = nullptr;
     int dtype = 0;  // DT_F16 / DT_BF16: activations, s2, s3 and y

@@ -113,6 +113,20 @@ __device__ __forceinline__ u32x2 quant8(u32x4 v, float r) {
     return o;
 }
 
+// The same codes through the correctly rounded fp32 divide (bf16 scales
+// below 2^-126, whose reciprocal is not a normal fp32 value).
+template <int DT>
+__device__ __forceinline__ u32x2 quant8_div(u32x4 v, float s) {
+    u32x2 o = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const float qf = fminf(fmaxf(rintf(act_bits_to_f32<DT>(h) / s), -128.0f), 127.0f);
+        o[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
+    }
+    return o;
+}
+
 // Register-resident quantisation: one workgroup of T threads per row, each
 // thread holding NV chunks of 8 values (row length K <= 8 * NV * T, K % 8 ==
 // 0), so the row is read from memory once.
@@ -152,16 +166,7 @@ __global__ __launch_bounds__(T) void w4a8_quant_rows(const uint16_t *__restrict_
         if (k >= K) break;
         u32x2 o = {0, 0};
         if (s != 0.0f) {
-            if (DT == DT_F16 || s >= 0x1p-126f) {
-                o = quant8<DT>(v[i], r);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t h = (v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                    const float qf = fminf(fmaxf(rintf(act_bits_to_f32<DT>(h) / s), -128.0f), 127.0f);
-                    o[e >> 2] |= ((uint32_t)(int32_t)qf & 0xFFu) << (8 * (e & 3));
-                }
-            }
+            o = (DT == DT_F16 || s >= 0x1p-126f) ? quant8<DT>(v[i], r) : quant8_div<DT>(v[i], s);
         }
         *(u32x2 *)(out + k) = o;
     }
@@ -296,8 +301,8 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
     if (FUSED) {
         if (threadIdx.x < 32) rmax[threadIdx.x] = 0;
         __syncthreads();
-        // |x| as an integer: for finite fp16 the magnitude order equals the
-        // order of the low 15 bits
+        // |x| as an integer: for finite fp16 and bf16 the magnitude order
+        // equals the order of the low 15 bits
         const int K8 = K >> 3;
         for (int m = 0; m < M; ++m) {
             uint32_t mx = 0;
@@ -312,9 +317,9 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
         }
         __syncthreads();
         if (threadIdx.x < M) {
-            const float amax = f16_bits_to_f32(rmax[threadIdx.x]);
-            const float q32 = amax / 127.0f;  // correctly rounded fp32 divide
-            const float sv = (float)(f16)q32;  // to fp16 (nearest even) and back
+            const float amax = act_bits_to_f32<DT>(rmax[threadIdx.x]);
+            const float q32 = amax / 127.0f;       // correctly rounded fp32 divide
+            const float sv = round_to_act<DT>(q32);  // to the activation type (nearest even) and back
             srow[threadIdx.x] = sv;
             if (tile == 0 && split == 0) s1_out[threadIdx.x] = sv;
         }
@@ -326,7 +331,8 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
             const u32x4 v = *(const u32x4 *)(x16 + (size_t)m * K + 64 * w_lo + 8 * cc);
             const float sv = srow[m];
             u32x2 o = {0, 0};
-            if (sv != 0.0f) o = quant8<DT_F16>(v, __builtin_amdgcn_rcpf(sv));
+            if (sv != 0.0f)
+                o = (DT == DT_F16 || sv >= 0x1p-126f) ? quant8<DT>(v, __builtin_amdgcn_rcpf(sv)) : quant8_div<DT>(v, sv);
             *(u32x2 *)(qa + ((size_t)(cc >> 3) * M + m) * 64 + (cc & 7) * 8) = o;
         }
     }
@@ -603,14 +609,19 @@ hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     return grp ? launch_w4a8_t<true, DT_F16>(a, p, st) : launch_w4a8_t<false, DT_F16>(a, p, st);
 }
 
-// The fused quantisation is the fp16 activations' (its divide-free rounding
-// is checked for fp16 only); bf16 layers take the two-launch path.
-hipError_t launch_w4a8_fused(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+// The fused quantisation of one fp16 or bf16 token (the same codes as
+// w4a8_quant_rows, through the same rounding).
+template <int DT>
+static hipError_t launch_w4a8_fused_t(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     const bool grp = a.s3 != nullptr;
-    if (p.kind != 0 || p.mt != 1 || a.dtype != DT_F16) return hipErrorInvalidValue;
     if (p.blk == 2)
-        return grp ? launch_skinny8<2, 1, true, true, DT_F16>(a, p, st) : launch_skinny8<2, 1, false, true, DT_F16>(a, p, st);
-    return grp ? launch_skinny8<1, 1, true, true, DT_F16>(a, p, st) : launch_skinny8<1, 1, false, true, DT_F16>(a, p, st);
+        return grp ? launch_skinny8<2, 1, true, true, DT>(a, p, st) : launch_skinny8<2, 1, false, true, DT>(a, p, st);
+    return grp ? launch_skinny8<1, 1, true, true, DT>(a, p, st) : launch_skinny8<1, 1, false, true, DT>(a, p, st);
+}
+
+hipError_t launch_w4a8_fused(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    if (p.kind != 0 || p.mt != 1) return hipErrorInvalidValue;
+    return a.dtype == DT_BF16 ? launch_w4a8_fused_t<DT_BF16>(a, p, st) : launch_w4a8_fused_t<DT_F16>(a, p, st);
 }
 
 }  // namespace awq4

@@ -203,11 +203,11 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
  * w4a8_linear -- the whole W4A8 layer in one call: w4a8_quant_act of x
  * followed by w4a8_gemm, with identical results (y, s1 and acc_out bit for
  * bit).  The pages note that quantising activations in a separate kernel
- * costs performance ([P5]); for a single fp16 token (M == 1, K <= 32768) the
- * quantisation runs inside the GEMM kernel: every workgroup reads the
- * activation row, derives s1 and quantises its own K range into LDS, so the
- * int8 activations never travel through device memory and there is one
- * launch.  Otherwise (bf16 included) the two steps run back to back.
+ * costs performance ([P5]); for a single token (M == 1, K <= 32768, fp16 or
+ * bf16) the quantisation runs inside the GEMM kernel: every workgroup reads
+ * the activation row, derives s1 and quantises its own K range into LDS, so
+ * the int8 activations never travel through device memory and there is one
+ * launch.  Otherwise the two steps run back to back.
  *   x:   device fp16 or bf16 [M, K] (dtype).
  *   a8:  device int8 [M, K], scratch: holds the quantised activations when
  *        the two-step path runs, left untouched by the fused path.

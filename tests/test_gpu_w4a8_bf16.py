@@ -106,6 +106,28 @@ def test_linear_w4a8_bf16_matches_two_steps(M):
     assert torch.equal(acc1, acc2) and torch.equal(s1, s1b) and torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("G", [-1, 128])
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -124])
+def test_linear_w4a8_bf16_fused_token(G, scale):
+    """One bf16 token on the QQQ shape runs the fused quantise-and-GEMM
+    kernel: a8 (read back through acc), s1 and y equal the two launches bit
+    for bit, and s1 the oracle's.  At 2^-124 the row's s1 is a subnormal fp32
+    value, which the fused kernel quantises through the divide."""
+    c = synthgen.w4a8_case(1, 21760, 8192, G, dtype="bf16")
+    xs = (c.x.double() * scale).to(torch.bfloat16)
+    x, b, s2 = to_dev(xs, c.b, c.s2)
+    s3 = None if c.s3 is None else to_dev(c.s3)[0]
+    a8, s1 = awq.quant_act(x)
+    y1, acc1 = awq.w4a8_gemm(a8, b, s1, s2, s3, G, want_acc=True)
+    y2, s1b, acc2 = awq.linear_w4a8(x, b, s2, s3, G, want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s1b) and torch.equal(acc1, acc2) and torch.equal(y1, y2)
+    _, es1 = orc().quant_act(xs, dtype=BF16)
+    assert np.array_equal(s1b.cpu().numpy().view(np.uint32), es1.view(np.uint32))
+    if scale != 1.0:
+        assert 0.0 < float(s1b.cpu()[0]) < 2.0 ** -126
+
+
 def test_w4a8_bf16_acc_equals_fp16():
     """The int32 accumulators do not depend on the scale type."""
     c = synthgen.w4a8_case(64, 4096, 1024, 64, dtype="bf16")
