@@ -305,6 +305,39 @@ def pin_w4a16_bruteforce(orc):
             assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), (G, sym)
 
 
+def _bf16_values(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16) \
+        .to(torch.float64).numpy()
+
+
+def pin_w4a16_bf16(orc):
+    """bf16 activations and scales (the dtype branch of the W4A16 oracle):
+    a brute force straight from the packed words with exact fractions of the
+    bf16 values, and the exact special case z = 0, s = 2^-3, x in {-1, 0, 1}
+    written as bf16 bit patterns.  Values are chosen so that reading a bf16
+    pattern as fp16 (or the reverse) changes the result."""
+    rng = np.random.default_rng(24)
+    for G in (32, 128):
+        for sym in (False, True):
+            M, K, N = 2, G, 16
+            xb = _bf16_bits(rng.standard_normal((M, K)) * 3.0)
+            qw = rng.integers(0, 2 ** 32, size=(K, N // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+            qz = None if sym else rng.integers(0, 2 ** 32, size=(K // G, N // 8),
+                                                dtype=np.uint64).astype(np.uint32).view(np.int32)
+            sb = _bf16_bits(0.002 + 0.018 * rng.random((K // G, N)))
+            y = orc.w4a16(xb, qw, sb, qz, G, dtype=1)
+            ref = _brute_w4a16(_bf16_values(xb), qw, _bf16_values(sb), qz, G)
+            assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), (G, sym)
+    M, K, N, G = 3, 128, 32, 128
+    X = rng.integers(-1, 2, size=(M, K)).astype(np.int64)
+    Q = rng.integers(0, 16, size=(K, N)).astype(np.int64)
+    qw, _ = orc.pack_n8(Q.astype(np.uint8))
+    qz, _ = orc.pack_n8(np.zeros((K // G, N), np.uint8))
+    s = np.full((K // G, N), 0x3E00, np.uint16)  # bf16 0.125
+    y = orc.w4a16(_bf16_bits(X.astype(np.float64)), qw, s, qz, G, dtype=1)
+    assert np.array_equal(y, (X @ Q).astype(np.float64) / 8.0)
+
+
 def pin_w4a16_numpy(orc):
     """fp64 matmul by numpy on the oracle's dequantised W agrees with the oracle."""
     rng = np.random.default_rng(7)
@@ -519,6 +552,6 @@ ALL_PINS = [
     pin_dequant_exhaustive, pin_w4a16_exact_special, pin_w4a16_numpy, pin_w4a16_invariants,
     pin_quant_examples, pin_quant_bf16_examples, pin_quant_random, pin_quant_bf16_random,
     pin_w4a8_bruteforce, pin_w4a8_group16_is_channel, pin_w4a8_bf16_scales, pin_bf16_decode,
-    pin_w4a16_bruteforce, pin_f16_codec, pin_bf16_encode, pin_quant_s1_exhaustive,
+    pin_w4a16_bruteforce, pin_w4a16_bf16, pin_f16_codec, pin_bf16_encode, pin_quant_s1_exhaustive,
     pin_quant_bf16_s1_exhaustive,
 ]

@@ -40,6 +40,10 @@ MUTANTS = {
     "f16_ties_away": ("double r = nearbyint(ldexp(a, 10 - E));",
                       "double r = floor(ldexp(a, 10 - E) + 0.5);"),
     "pack_no_clamp": ("if (v > 15) {\n                    v = 15;", "if (v > 15) {\n                    v = v & 15;"),
+    "w4a16_act_dtype_ignored": ("for (int64_t i = 0; i < M * K; i++) xd[i] = decode_act(x[i], dtype);",
+                                "for (int64_t i = 0; i < M * K; i++) xd[i] = decode_act(x[i], 0);"),
+    "w4a16_scale_dtype_ignored": ("double s = decode_act(t->scales[g * t->N + 8 * j + col], t->dtype);",
+                                  "double s = decode_act(t->scales[g * t->N + 8 * j + col], 0);"),
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
 }
 
