@@ -29,6 +29,13 @@ AWQ_OP_W4A8_GEMM = 2
 _lib = None
 
 
+class PlanInfo(ctypes.Structure):
+    """awq_plan_t: how the library would launch a call (awq_plan_info)."""
+    _fields_ = [("kernel", ctypes.c_int), ("tiles_n", ctypes.c_int), ("tiles_m", ctypes.c_int),
+                ("splits", ctypes.c_int), ("row_tiles", ctypes.c_int), ("ksplit", ctypes.c_int),
+                ("cu_count", ctypes.c_int), ("workspace_bytes", ctypes.c_int64)]
+
+
 class AWQError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
@@ -59,8 +66,9 @@ def lib() -> ctypes.CDLL:
     L.w4a8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     L.w4a8_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     L.awq_stream_read.argtypes = [vp, i64, vp, vp]
+    L.awq_plan_info.argtypes = [i32, i64, i64, i64, i32, i32, i32, ctypes.POINTER(PlanInfo)]
     for f in ("awq_pack", "awq_unpack", "awq_gemm_w4a16", "awq_gemv_w4a16", "w4a8_quant_act", "w4a8_gemm", "w4a8_linear",
-              "awq_stream_read"):
+              "awq_stream_read", "awq_plan_info"):
         getattr(L, f).restype = i32
     _lib = L
     return L

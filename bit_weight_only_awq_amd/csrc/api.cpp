@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 
 #include "../../include/awq4.h"
@@ -15,29 +16,65 @@
 namespace awq4 {
 
 static constexpr int64_t kMaxDim = int64_t(1) << 20;
-static constexpr int kTargetWorkgroups = 512;  // 256 CUs x 2 workgroups of 4 waves
+// The planners below size grids from the device's compute-unit count (cus):
+// two workgroups of 4 waves per CU is the target fill of the tiled kernels.
+static int64_t target_workgroups(const DeviceProps &d) { return 2 * (int64_t)d.cus; }
 // The W4A16 LDS GEMM takes M above 16 (the decode kernel below).  Under 128
 // rows it runs 128-row tiles with deep copy rings and at most 4 K splits
 // (measured on the Llama-3-8B layers at M = 32..128: more splits cost more in
 // partial tiles than they gain, and 256-row tiles with deep rings, at one
 // wave per SIMD, were slower than the large-M configuration from M = 128 up).
-static constexpr int64_t kW16LdsMinM = 16, kW16DeepMaxM = 127, kW16DeepMaxSplits = 4, kW16TallTilesMin = 129;
+static constexpr int64_t kW16LdsMinM = 16, kW16DeepMaxM = 127, kW16DeepMaxSplits = 4;
 // The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, two per CU) are used
 // whenever there are at least as many as CUs; with fewer, the 128 x 128 tiles
 // give more workgroups before a K split is needed (measured: M = 512 on
 // (4096, 14336) takes 44 us on 448 narrow tiles, 82 us on 224 wide ones split
 // in two).
-static constexpr int64_t kW8WideMinTiles = 256;
+// Largest W4A8 K: the kernels multiply int8 activations (down to -128) by
+// int8 weight bytes 16 q (down to -128), so |acc| <= 2^14 K must stay below
+// 2^31: K < 2^17, and K % 64 == 0 makes that K <= 131008.
+static constexpr int64_t kW8MaxK = 131072 - 64;
+
+// Once-per-device property cache.  The first call on a device asks HIP for
+// its compute-unit count; later calls read the cached value (lock-free: a
+// racing first call stores the same number).  With no device visible (the
+// validation-only case) the planners assume a whole MI355X.
+static constexpr int kMaxDevices = 64;
+static std::atomic<int> g_device_cus[kMaxDevices];
+
+static DeviceProps props_of_device(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return DeviceProps{kDefaultCUs};
+    int cus = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = kDefaultCUs;
+        g_device_cus[dev].store(v, std::memory_order_relaxed);
+        cus = v;
+    }
+    return DeviceProps{cus};
+}
+
+// properties of the device that `stream` belongs to (the current device for
+// the null stream)
+static DeviceProps stream_props(void *stream) {
+    int dev = -1;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &d) == hipSuccess) dev = (int)d;
+    }
+    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return DeviceProps{kDefaultCUs};
+    return props_of_device(dev);
+}
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 static size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// workgroups of the CS <= 2 decode kernel resident at once (4 per CU)
-constexpr int64_t kDecodeResidentWGs = 4 * 256, kDecodeSmallChunkWGs = 2 * 256;
-
-W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry) {
-    (void)gemv_entry;
+W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dtype, const DeviceProps &d) {
+    const int64_t cus = d.cus;
+    // workgroups of the CS <= 2 decode kernel resident at once (4 per CU)
+    const int64_t decode_resident_wgs = 4 * cus, decode_small_chunk_wgs = 2 * cus;
     W4A16Plan p{};
     const int64_t nw = N / 8;
     const int64_t T = K / 32;
@@ -54,18 +91,18 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         // twice the waves per SIMD on narrow layers (measured at M = 1 on
         // 4096 x 4096: 5.14 -> 4.88 us; layers past that bound were slower,
         // and each extra split adds an atomic per output element and row)
-        if (M <= 2 && (int64_t)p.tiles_n * cdiv(K / 32, p.waves) <= kDecodeSmallChunkWGs) p.cs = 1;
+        if (M <= 2 && (int64_t)p.tiles_n * cdiv(K / 32, p.waves) <= decode_small_chunk_wgs) p.cs = 1;
         // M >= 4: one 128-k group per wave when that still gives three
         // quarters of the CUs a workgroup -- half the K splits, so half the
         // per-element atomics, which grow with M (measured at M = 16: down
         // 11008 x 4096 35.2 -> 21.0 us, qkv 4096 x 6144 16.2 -> 14.7 us;
         // 4096 x 4096, with 128 such workgroups, was slower)
-        if (M >= 4 && G % 128 == 0 && (int64_t)p.tiles_n * cdiv(K / 128, p.waves) >= 192) p.cs = 4;
+        if (M >= 4 && G % 128 == 0 && (int64_t)p.tiles_n * cdiv(K / 128, p.waves) >= 3 * cus / 4) p.cs = 4;
         p.tiles_m = 1;
         p.splits = (int)cdiv(K / (32 * p.cs), p.waves);
         // more workgroups than stay resident (4 per CU): one 128-k group per
         // wave instead, so that the layer still runs in a single round
-        if (G % 128 == 0 && (int64_t)p.tiles_n * p.splits > kDecodeResidentWGs) {
+        if (G % 128 == 0 && (int64_t)p.tiles_n * p.splits > decode_resident_wgs) {
             p.cs = 4;
             p.splits = (int)cdiv(K / 128, p.waves);
         }
@@ -81,11 +118,11 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         p.tiles_m = (int)cdiv(M, bm);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         int64_t s = 1;
-        if (tiles < 256) {
+        if (tiles < cus) {
             // at most 4 K splits: each adds an M x N partial tile to write,
             // read and clear, which costs more than it saves beyond that
             // (measured on the Llama-3-8B layers at M = 64)
-            s = cdiv(kTargetWorkgroups, tiles);
+            s = cdiv(target_workgroups(d), tiles);
             s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
             s = std::min<int64_t>(s, 4);
         }
@@ -106,7 +143,7 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         // M = 256, 56 -> 37 us; down at M = 128, 90 -> 57 us; with more
         // 256-row tiles than that (qkv at M = 1024, gate/up at M = 256) the
         // 256-row tiles' better operand reuse wins.
-        p.mt = (M <= 128 || cdiv(N, 128) * cdiv(M, 256) <= kW16TallTilesMin - 1) ? 8 : 16;
+        p.mt = (M <= 128 || cdiv(N, 128) * cdiv(M, 256) <= cus / 2) ? 8 : 16;
         p.tiles_n = (int)cdiv(N, 128);
         p.tiles_m = (int)cdiv(M, 16 * p.mt);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
@@ -114,7 +151,7 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
         int64_t s;
         if (p.deep) {
             // one workgroup per CU: K splits up to one workgroup per CU
-            s = std::min<int64_t>(std::max<int64_t>(1, 256 / tiles), kW16DeepMaxSplits);
+            s = std::min<int64_t>(std::max<int64_t>(1, cus / tiles), kW16DeepMaxSplits);
             s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
         } else if (M <= 128) {
             // few rows: the partial tiles are small, split by the tile count
@@ -126,20 +163,26 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool g
             // M = 192..1024 on the Llama-3-8B layers: each split's partial
             // tile, summed by one workgroup, costs more than it gains on
             // K = 4096 and pays for itself on K = 14336.
-            const int64_t cap = tiles <= 64 ? 4 : tiles <= 128 ? 2 : 1;
+            const int64_t cap = tiles <= cus / 4 ? 4 : tiles <= cus / 2 ? 2 : 1;
             s = std::min<int64_t>(cap, std::max<int64_t>(1, stages / 56));
         }
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
         // no more workgroups than CUs: two wave groups per workgroup split K
         // inside it (twice the waves per SIMD, no extra atomics)
-        p.ksplit = !p.deep && tiles * p.splits <= 256 && stages / p.splits >= 4 ? 2 : 1;
+        p.ksplit = !p.deep && tiles * p.splits <= cus && stages / p.splits >= 4 ? 2 : 1;
     }
-    if (p.splits > 1)
-        p.workspace_bytes = p.kind == 0 ? (size_t)M * N * sizeof(uint64_t)
-                                        : (size_t)split_tiles_bytes((int64_t)p.tiles_n * p.tiles_m, p.splits, M, N);
-    else
+    if (p.splits <= 1) {
         p.workspace_bytes = 0;
+    } else if (p.kind == 0) {
+        // decode: counting accumulators (fp16) or per-tile partials (bf16)
+        const size_t atomics = (size_t)M * N * sizeof(uint64_t);
+        const size_t tiles_ws = (size_t)split_tiles_bytes(p.tiles_n, p.splits, M, N);
+        p.workspace_bytes = dtype == AWQ_DTYPE_F16 ? atomics
+                            : dtype == AWQ_DTYPE_BF16 ? tiles_ws : std::max(atomics, tiles_ws);
+    } else {
+        p.workspace_bytes = (size_t)split_tiles_bytes((int64_t)p.tiles_n * p.tiles_m, p.splits, M, N);
+    }
     return p;
 }
 
@@ -151,8 +194,8 @@ bool w4a8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p) {
     return p.kind == 0 && p.mt == 1 && M == 1 && K <= 32768 && w4a8_fused_lds_bytes(M, K, p.blk, p.splits) <= 64 * 1024;
 }
 
-W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
-    (void)G;
+W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d) {
+    const int64_t cus = d.cus;
     W4A8Plan p{};
     const int64_t T = K / 64;
     int64_t tiles;
@@ -166,7 +209,7 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         p.tiles_n = (int)cdiv(N, 64 * p.blk);
         p.tiles_m = 1;
         tiles = p.tiles_n;
-        int64_t s = cdiv(kTargetWorkgroups, tiles);
+        int64_t s = cdiv(target_workgroups(d), tiles);
         s = std::min<int64_t>(s, std::max<int64_t>(1, T / 4));
         p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
     } else {
@@ -177,8 +220,8 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         p.tiles_m = (int)cdiv(M, 32 * p.mt);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         int64_t s = 1;
-        if (tiles < 256) {
-            s = cdiv(kTargetWorkgroups, tiles);
+        if (tiles < cus) {
+            s = cdiv(target_workgroups(d), tiles);
             s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
             s = std::min<int64_t>(s, 4);  // partial tiles: see the W4A16 tiled kernel
         }
@@ -193,10 +236,10 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         // tiles (8 waves) when there are enough of them, else 128 x 128 (4 waves)
         p.kind = 2;
         const int64_t wide = cdiv(N, 256) * cdiv(M, 128);
-        p.blk = wide >= kW8WideMinTiles ? 2 : 1;
+        p.blk = wide >= cus ? 2 : 1;
         // no more wide tiles than CUs: two groups of 8 waves per workgroup
         // split K inside it (four waves per SIMD instead of two)
-        p.ksplit = p.blk == 2 && wide <= 256 && T >= 8 ? 2 : 1;
+        p.ksplit = p.blk == 2 && wide <= cus && T >= 8 ? 2 : 1;
         p.mt = 4;
         p.tiles_n = (int)cdiv(N, 128 * p.blk);
         p.tiles_m = (int)cdiv(M, 128);
@@ -204,7 +247,7 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G) {
         // (more splits measured slower at M = 128..512: every split adds an
         // M x N int32 partial tile written, read back and cleared)
         int64_t s = 1;
-        if (tiles < 256) s = std::min<int64_t>(cdiv(256, tiles), std::max<int64_t>(1, T / 4));
+        if (tiles < cus) s = std::min<int64_t>(cdiv(cus, tiles), std::max<int64_t>(1, T / 4));
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
     }
     (void)tiles;
@@ -250,7 +293,7 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     int rc = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, G, dtype, split_k);
     if (rc != AWQ_OK) return rc;
     if (gemv && M > 8) return AWQ_EUNSUPPORTED;
-    W4A16Plan p = plan_w4a16(M, N, K, G, split_k, gemv);
+    W4A16Plan p = plan_w4a16(M, N, K, G, split_k, dtype, stream_props(stream));
     rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
     if (rc != AWQ_OK) return rc;
     // every plan that needs a workspace (split-K or stream-K) gets it
@@ -325,15 +368,43 @@ size_t awq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int group_si
                         AWQ_DTYPE_F16, split_k) == AWQ_EINVAL)
             return 0;
         if (op == AWQ_OP_GEMV_W4A16 && M > 8) return 0;
-        return plan_w4a16(M, N, K, group_size, split_k, op == AWQ_OP_GEMV_W4A16).workspace_bytes;
+        return plan_w4a16(M, N, K, group_size, split_k, -1, stream_props(nullptr)).workspace_bytes;
     }
     if (op == AWQ_OP_W4A8_GEMM) {
-        if (M < 1 || N < 8 || N % 8 || K < 64 || K % 64 || M > kMaxDim || N > kMaxDim || K > 131072) return 0;
+        if (M < 1 || N < 8 || N % 8 || K < 64 || K % 64 || M > kMaxDim || N > kMaxDim || K > kW8MaxK) return 0;
         if (group_size != -1 && ((group_size != 32 && group_size != 64 && group_size != 128) || K % group_size))
             return 0;
-        return plan_w4a8(M, N, K, group_size).workspace_bytes;
+        return plan_w4a8(M, N, K, group_size, stream_props(nullptr)).workspace_bytes;
     }
     return 0;
+}
+
+int awq_plan_info(int op, int64_t M, int64_t N, int64_t K, int group_size, int split_k, int cu_count,
+                  awq_plan_t *out) {
+    if (!out || cu_count < 0) return AWQ_EINVAL;
+    const DeviceProps d = cu_count > 0 ? DeviceProps{cu_count} : stream_props(nullptr);
+    if (op == AWQ_OP_GEMM_W4A16 || op == AWQ_OP_GEMV_W4A16) {
+        int64_t dummy = 16;
+        int rc = check_w4a16(&dummy, (const int32_t *)&dummy, &dummy, nullptr, &dummy, M, N, K, group_size,
+                             AWQ_DTYPE_F16, split_k);
+        if (rc != AWQ_OK) return rc;
+        if (op == AWQ_OP_GEMV_W4A16 && M > 8) return AWQ_EUNSUPPORTED;
+        const W4A16Plan p = plan_w4a16(M, N, K, group_size, split_k, -1, d);
+        *out = awq_plan_t{p.kind, p.tiles_n, p.tiles_m, p.splits, p.mt, std::max(1, p.ksplit), d.cus,
+                          (int64_t)p.workspace_bytes};
+        return AWQ_OK;
+    }
+    if (op == AWQ_OP_W4A8_GEMM) {
+        if (M < 1 || N < 8 || N % 8 || M > kMaxDim || N > kMaxDim) return AWQ_EINVAL;
+        if (group_size != -1 && ((group_size != 32 && group_size != 64 && group_size != 128) || K % group_size))
+            return AWQ_EINVAL;
+        if (K < 64 || K % 64 || K > kW8MaxK) return AWQ_EUNSUPPORTED;
+        const W4A8Plan p = plan_w4a8(M, N, K, group_size, d);
+        *out = awq_plan_t{p.kind, p.tiles_n, p.tiles_m, p.splits, p.mt, std::max(1, p.ksplit), d.cus,
+                          (int64_t)p.workspace_bytes};
+        return AWQ_OK;
+    }
+    return AWQ_EINVAL;
 }
 
 int awq_gemm_w4a16(const void *x, const int32_t *qweight, const void *scales, const int32_t *qzeros, void *y,
@@ -372,11 +443,11 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
         if (!s3_f16 || K % group_size) return AWQ_EINVAL;
     }
     // 64 k per matrix-core step; |acc| <= 128 * 128 * K must stay below 2^31
-    if (K % 64 || K > 131072) return AWQ_EUNSUPPORTED;
+    if (K % 64 || K > kW8MaxK) return AWQ_EUNSUPPORTED;
     if (!aligned16(a8) || !aligned16(b_packed) || !aligned16(s1) || !aligned16(s2_f16) || !aligned16(y_f16))
         return AWQ_EALIGN;
     if ((s3_f16 && !aligned16(s3_f16)) || (acc_out && !aligned16(acc_out))) return AWQ_EALIGN;
-    W4A8Plan p = plan_w4a8(M, N, K, group_size);
+    W4A8Plan p = plan_w4a8(M, N, K, group_size, stream_props(stream));
     int rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
     if (rc != AWQ_OK) return rc;
     if (p.splits > 1) {
@@ -400,12 +471,12 @@ int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packe
         if (group_size != 32 && group_size != 64 && group_size != 128) return AWQ_EINVAL;
         if (!s3_f16 || K % group_size) return AWQ_EINVAL;
     }
-    if (K % 64 || K > 131072) return AWQ_EUNSUPPORTED;
+    if (K % 64 || K > kW8MaxK) return AWQ_EUNSUPPORTED;
     if (!aligned16(x_f16) || !aligned16(a8) || !aligned16(s1) || !aligned16(b_packed) || !aligned16(s2_f16) ||
         !aligned16(y_f16))
         return AWQ_EALIGN;
     if ((s3_f16 && !aligned16(s3_f16)) || (acc_out && !aligned16(acc_out))) return AWQ_EALIGN;
-    W4A8Plan p = plan_w4a8(M, N, K, group_size);
+    W4A8Plan p = plan_w4a8(M, N, K, group_size, stream_props(stream));
     int rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
     if (rc != AWQ_OK) return rc;
     if (p.splits > 1) p.acc = static_cast<uint64_t *>(workspace);

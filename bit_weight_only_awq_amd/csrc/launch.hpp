@@ -81,8 +81,17 @@ __host__ __device__ constexpr int64_t split_tiles_bytes(int64_t tiles, int64_t S
     return split_counters_bytes(tiles) + S * M * N * 4;
 }
 
-W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, bool gemv_entry);
-W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G);
+// What the launch planners need to know about the device a call runs on,
+// queried once per device (api.cpp) and passed to the pure planners.
+struct DeviceProps {
+    int cus;  // compute units (256 on a whole MI355X; fewer on a partition)
+};
+constexpr int kDefaultCUs = 256;
+
+// dtype: DT_F16 / DT_BF16 (the decode kernel's split-K workspace depends on
+// it), or -1 for a workspace large enough for either
+W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dtype, const DeviceProps &d);
+W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d);
 bool w4a8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p);
 
 hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);

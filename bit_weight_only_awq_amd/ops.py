@@ -6,6 +6,7 @@ workspace through torch, and passes raw pointers and the current stream.
 """
 from __future__ import annotations
 
+import ctypes
 import threading
 
 import torch
@@ -35,31 +36,51 @@ def _need_cuda(*ts):
 # ----------------------------------------------------------------------------- workspace
 
 class Workspace:
-    """One zero-initialised workspace per device, grown on demand and shared by
-    every call ordered on one stream (the library leaves its counters zero)."""
+    """One zero-initialised workspace per (device, stream), grown on demand and
+    shared by every call ordered on that stream (the library leaves its
+    counters zero after each call).  Calls on different streams may overlap in
+    time, so each stream gets its own buffer; a grown buffer is zero-filled on
+    the stream that will use it, and the caching allocator keeps the old one
+    alive until the work queued on that stream before the swap has run."""
 
     def __init__(self):
-        self._bufs: dict[int, torch.Tensor] = {}
+        self._bufs: dict[tuple[int, int], torch.Tensor] = {}
         self._lock = threading.Lock()
 
     def get(self, device: torch.device, nbytes: int) -> torch.Tensor | None:
         if nbytes == 0:
             return None
         idx = device.index if device.index is not None else torch.cuda.current_device()
+        stream = torch.cuda.current_stream(idx)
+        key = (idx, stream.cuda_stream)
         with self._lock:
-            buf = self._bufs.get(idx)
+            buf = self._bufs.get(key)
             if buf is None or buf.numel() < nbytes:
                 size = max(nbytes, 2 * (buf.numel() if buf is not None else 0), 1 << 20)
-                buf = torch.zeros(size, dtype=torch.uint8, device=torch.device("cuda", idx))
-                self._bufs[idx] = buf
+                with torch.cuda.stream(stream):
+                    buf = torch.zeros(size, dtype=torch.uint8, device=torch.device("cuda", idx))
+                self._bufs[key] = buf
             return buf
 
 
 WORKSPACE = Workspace()
 
 
-def workspace_bytes(op: int, M: int, N: int, K: int, group_size: int, split_k: int = 0) -> int:
-    return int(L.lib().awq_workspace_bytes(op, M, N, K, group_size, split_k))
+def workspace_bytes(op: int, M: int, N: int, K: int, group_size: int, split_k: int = 0,
+                    device: torch.device | None = None) -> int:
+    """Workspace bytes of a call on `device` (the current device if None)."""
+    if device is None:
+        return int(L.lib().awq_workspace_bytes(op, M, N, K, group_size, split_k))
+    with torch.cuda.device(device):
+        return int(L.lib().awq_workspace_bytes(op, M, N, K, group_size, split_k))
+
+
+def plan_info(op: int, M: int, N: int, K: int, group_size: int, split_k: int = 0, cu_count: int = 0) -> dict:
+    """How the library would launch a call (awq_plan_info); cu_count 0 = the current device."""
+    info = L.PlanInfo()
+    L.check("awq_plan_info", L.lib().awq_plan_info(op, M, N, K, group_size, split_k, cu_count,
+                                                   ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in L.PlanInfo._fields_}
 
 
 # ----------------------------------------------------------------------------- packing
@@ -106,7 +127,7 @@ def _w4a16(fn_name: str, op: int, x, qweight, scales, qzeros, group_size, split_
     N = qweight.shape[1] * 8
     if out is None:
         out = torch.empty(M, N, dtype=x.dtype, device=x.device)
-    need = workspace_bytes(op, M, N, K, group_size, split_k)
+    need = workspace_bytes(op, M, N, K, group_size, split_k, x.device)
     ws = WORKSPACE.get(x.device, need)
     fn = getattr(L.lib(), fn_name)
     L.check(fn_name, fn(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out), M, N, K, group_size,
@@ -159,7 +180,7 @@ def w4a8_gemm(a8, b, s1, s2, s3=None, group_size: int = -1, want_acc: bool = Fal
     if out is None:
         out = torch.empty(M, N, dtype=s2.dtype, device=a8.device)
     acc = torch.empty(M, N, dtype=torch.int32, device=a8.device) if want_acc else None
-    need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size)
+    need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size, 0, a8.device)
     ws = WORKSPACE.get(a8.device, need)
     L.check("w4a8_gemm", L.lib().w4a8_gemm(_ptr(a8), _ptr(b), _ptr(s1), _ptr(s2), _ptr(s3), _ptr(out), _ptr(acc),
                                            M, N, K, group_size, _F16[s2.dtype], _ptr(ws),
@@ -183,7 +204,7 @@ def linear_w4a8(x, b, s2, s3=None, group_size: int = -1, want_acc: bool = False,
     if out is None:
         out = torch.empty(M, N, dtype=x.dtype, device=x.device)
     acc = torch.empty(M, N, dtype=torch.int32, device=x.device) if want_acc else None
-    need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size)
+    need = workspace_bytes(L.AWQ_OP_W4A8_GEMM, M, N, K, group_size, 0, x.device)
     ws = WORKSPACE.get(x.device, need)
     L.check("w4a8_linear", L.lib().w4a8_linear(_ptr(x), _ptr(a8), _ptr(s1), _ptr(b), _ptr(s2), _ptr(s3), _ptr(out),
                                                _ptr(acc), M, N, K, group_size, _F16[x.dtype], _ptr(ws),

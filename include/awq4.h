@@ -105,15 +105,17 @@ int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, in
 
 /*
  * awq_workspace_bytes -- bytes of device workspace the given call needs
- * (0 if none).  split_k as passed to the call (0 = automatic).  For W4A8,
- * group_size is the one passed to w4a8_gemm.
+ * (0 if none) on the current device.  split_k as passed to the call
+ * (0 = automatic).  For W4A8, group_size is the one passed to w4a8_gemm.
  * Workspace rules ([P2]: one workspace per device, reused by every layer):
  *  - it is caller-owned, 16-byte aligned, and may be shared by any number of
  *    calls that are ordered on one stream;
- *  - a split-K decode GEMV, or a W4A8 call with M <= 64, uses one 64-bit
- *    counting accumulator per output element (M x N); the last
- *    contribution to an element writes the output and clears it;
- *  - the GEMM kernels (M > 16 for W4A16, M > 64 for W4A8) use one 32-bit
+ *  - a split-K fp16 decode GEMV, or a W4A8 call with M <= 64, uses one
+ *    64-bit counting accumulator per output element (M x N); the last
+ *    contribution to an element writes the output and clears it (the size
+ *    returned for the W4A16 calls covers both activation dtypes);
+ *  - a split-K bf16 decode GEMV and the GEMM kernels (M > 16 for W4A16,
+ *    M > 64 for W4A8) use one 32-bit
  *    arrival counter per output tile (padded to 256 bytes) followed by S
  *    partial [M, N] results of 4 bytes each (fp32 for W4A16, int32 for
  *    W4A8); the last workgroup of a tile to arrive adds the S partials in
@@ -125,6 +127,34 @@ int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, in
  * Returns 0 for invalid arguments.
  */
 size_t awq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int group_size, int split_k);
+
+/*
+ * awq_plan_info -- how a call would be launched, without launching it: the
+ * kernel, grid and workspace the library's planner picks for the given shape
+ * on a device with `cu_count` compute units (0 = the current device, queried
+ * once per device and cached; a whole MI355X, 256, when no device is
+ * visible).  The planners size their grids from this count, so a partitioned
+ * or smaller part gets grids of its own size.  Needs no GPU when cu_count > 0.
+ *   op: AWQ_OP_*; other arguments as for the call (group_size -1 = W4A8
+ *   per-channel).
+ *   out: host pointer, written on success.
+ * Errors: the validation status the call itself would return for the shape
+ * (AWQ_EINVAL, AWQ_EUNSUPPORTED), or AWQ_EINVAL for a NULL out or a negative
+ * cu_count.
+ */
+typedef struct {
+    int kernel;    /* W4A16: 0 decode GEMV, 1 register-tiled GEMM, 3 LDS-pipelined GEMM;
+                      W4A8: 0 skinny split-K, 1 register-tiled, 2 LDS-pipelined */
+    int tiles_n;   /* workgroup tiles along N */
+    int tiles_m;   /* workgroup tiles along M */
+    int splits;    /* workgroups along K (1 = no split) */
+    int row_tiles; /* 16-row matrix-core tiles per wave or workgroup column */
+    int ksplit;    /* wave groups splitting K inside one workgroup (1 or 2) */
+    int cu_count;  /* the compute-unit count the plan was made for */
+    int64_t workspace_bytes;
+} awq_plan_t;
+int awq_plan_info(int op, int64_t M, int64_t N, int64_t K, int group_size, int split_k, int cu_count,
+                  awq_plan_t *out);
 
 /*
  * awq_gemm_w4a16 -- Y = X . dequant(qweight, qzeros, scales) for any M >= 1
@@ -191,9 +221,11 @@ int w4a8_quant_act(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, i
  *   y:        device [M, N].
  *   acc_out:  device int32 [M, N] or NULL: if given, the exact accumulators
  *             are written too (for checking).
- *   K % 64 == 0; N % 8 == 0; group_size -1 (per-channel) or one of 32, 64, 128.
+ *   K % 64 == 0 and K <= 131008 (so that the int32 accumulator, which
+ *   holds up to 2^14 * K, cannot wrap); N % 8 == 0; group_size -1
+ *   (per-channel) or one of 32, 64, 128.
  * Errors: AWQ_EINVAL (also an unknown dtype), AWQ_EALIGN, AWQ_EWORKSPACE,
- * AWQ_EUNSUPPORTED (K % 64 != 0), AWQ_EHIP.
+ * AWQ_EUNSUPPORTED (K % 64 != 0 or K > 131008), AWQ_EHIP.
  */
 int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const void *s2,
               const void *s3, void *y, int32_t *acc_out, int64_t M, int64_t N,

@@ -90,8 +90,10 @@ def test_workspace_bytes():
     op_gemm, op_gemv, op8 = L.AWQ_OP_GEMM_W4A16, L.AWQ_OP_GEMV_W4A16, L.AWQ_OP_W4A8_GEMM
     # no split requested -> no workspace
     assert lib.awq_workspace_bytes(op_gemm, 2048, 4096, 4096, 128, 1) == 0
-    # a M=1, N=4096 GEMV: one 64-bit counting accumulator per output element
-    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == 4096 * 8
+    # a M=1, N=4096 GEMV (32 K splits of 128 k, 16 column tiles): the larger of
+    # one 64-bit counting accumulator per output element (fp16) and 16 tile
+    # counters (256 bytes) + 32 fp32 partial rows (bf16)
+    assert lib.awq_workspace_bytes(op_gemv, 1, 4096, 4096, 128, 8) == max(4096 * 8, 256 + 32 * 4096 * 4)
     # the tiled kernel with an explicit split: per-tile counters (16 tiles of
     # 64 rows x 256 columns, padded to 256 bytes), then 4 fp32 partial results
     assert lib.awq_workspace_bytes(op_gemm, 64, 4096, 4096, 128, 4) == 256 + 4 * 64 * 4096 * 4
@@ -108,6 +110,8 @@ def test_workspace_bytes():
     assert lib.awq_workspace_bytes(op_gemm, 1, 4095, 4096, 128, 0) == 0
     assert lib.awq_workspace_bytes(op8, 1, 8192, 21760, -1, 0) > 0
     assert lib.awq_workspace_bytes(op8, 1, 8192, 21700, -1, 0) == 0
+    assert lib.awq_workspace_bytes(op8, 1, 64, 131072, -1, 0) == 0
+    assert lib.awq_workspace_bytes(op8, 1, 64, 131008, -1, 0) > 0
     assert lib.awq_workspace_bytes(99, 1, 8192, 4096, 128, 0) == 0
 
 
@@ -125,6 +129,8 @@ def test_w4a8_validation():
     assert g(s3=A, G=48) == L.AWQ_EINVAL
     assert g(K=21700) == L.AWQ_EUNSUPPORTED    # K % 64
     assert g(K=262144) == L.AWQ_EUNSUPPORTED   # int32 accumulator bound
+    assert g(K=131072) == L.AWQ_EUNSUPPORTED   # 2^14 * K would reach 2^31 exactly
+    assert g(K=131008) == L.AWQ_EWORKSPACE     # the largest K: accepted (then needs its workspace)
     assert g(acc=MIS) == L.AWQ_EALIGN
     assert g() == L.AWQ_EWORKSPACE             # decode split needs a workspace
     assert g(dt=1) == L.AWQ_EWORKSPACE         # bf16 scales and output: same rules
@@ -150,6 +156,8 @@ def test_w4a8_linear_validation():
     assert f(G=128) == L.AWQ_EINVAL            # grouped without s3
     assert f(s3=A, G=48) == L.AWQ_EINVAL
     assert f(K=21700) == L.AWQ_EUNSUPPORTED    # K % 64
+    assert f(K=131072) == L.AWQ_EUNSUPPORTED   # int32 accumulator bound
+    assert f(K=131008) == L.AWQ_EWORKSPACE
     assert f(x=MIS) == L.AWQ_EALIGN
     assert f(s1=MIS) == L.AWQ_EALIGN
     assert f() == L.AWQ_EWORKSPACE             # the decode split needs a workspace
@@ -176,3 +184,70 @@ def test_stream_read_validation():
     assert lib.awq_stream_read(A, 24, A, None) == L.AWQ_EINVAL
     assert lib.awq_stream_read(A, 16, None, None) == L.AWQ_EINVAL
     assert lib.awq_stream_read(MIS, 16, A, None) == L.AWQ_EALIGN
+
+
+def _plan(op, M, N, K, G=128, split=0, cus=256):
+    info = L.PlanInfo()
+    rc = L.lib().awq_plan_info(op, M, N, K, G, split, cus, ctypes.byref(info))
+    assert rc == L.AWQ_OK, rc
+    return info
+
+
+def test_plan_info_validation():
+    lib = L.lib()
+    info = L.PlanInfo()
+    assert lib.awq_plan_info(L.AWQ_OP_GEMM_W4A16, 1, 4096, 4096, 128, 0, 256, None) == L.AWQ_EINVAL
+    assert lib.awq_plan_info(L.AWQ_OP_GEMM_W4A16, 1, 4096, 4096, 128, 0, -1, ctypes.byref(info)) == L.AWQ_EINVAL
+    assert lib.awq_plan_info(L.AWQ_OP_GEMV_W4A16, 9, 4096, 4096, 128, 0, 256, ctypes.byref(info)) == \
+        L.AWQ_EUNSUPPORTED
+    assert lib.awq_plan_info(L.AWQ_OP_W4A8_GEMM, 1, 4096, 21700, -1, 0, 256, ctypes.byref(info)) == \
+        L.AWQ_EUNSUPPORTED
+    assert lib.awq_plan_info(99, 1, 4096, 4096, 128, 0, 256, ctypes.byref(info)) == L.AWQ_EINVAL
+
+
+def test_plan_matches_workspace_query():
+    """awq_workspace_bytes (no device here: a whole MI355X) agrees with the plan at 256 CUs."""
+    lib = L.lib()
+    for op, M, N, K, G in ((L.AWQ_OP_GEMV_W4A16, 1, 4096, 4096, 128), (L.AWQ_OP_GEMM_W4A16, 64, 4096, 4096, 128),
+                           (L.AWQ_OP_GEMM_W4A16, 2048, 4096, 14336, 128), (L.AWQ_OP_W4A8_GEMM, 1, 8192, 21760, -1),
+                           (L.AWQ_OP_W4A8_GEMM, 256, 8192, 21760, 128)):
+        assert _plan(op, M, N, K, G).workspace_bytes == lib.awq_workspace_bytes(op, M, N, K, G, 0)
+
+
+def test_plan_sizes_grids_from_the_cu_count():
+    """The planners size their grids from the device's compute units: a whole
+    MI355X (256 CUs) and a quarter of one (64 CUs) get different plans, each
+    filling its own device."""
+    gemm, gemv, w8 = L.AWQ_OP_GEMM_W4A16, L.AWQ_OP_GEMV_W4A16, L.AWQ_OP_W4A8_GEMM
+    # M = 1024 on 4096 x 4096: 128 tiles of 256 rows would leave half of 256
+    # CUs idle, so 128-row tiles (256 of them, K split inside the workgroup);
+    # on 64 CUs the 256-row tiles already fill the device twice over
+    big, small = _plan(gemm, 1024, 4096, 4096, cus=256), _plan(gemm, 1024, 4096, 4096, cus=64)
+    assert (big.kernel, small.kernel) == (3, 3)
+    assert big.cu_count == 256 and small.cu_count == 64
+    assert big.row_tiles == 8 and big.tiles_n * big.tiles_m == 256 and big.ksplit == 2
+    assert small.row_tiles == 16 and small.tiles_n * small.tiles_m == 128 and small.ksplit == 1
+    # M = 2048: 256 tiles of 256 rows; one per CU on 256 CUs (two wave groups
+    # split K inside each), four per CU on 64 CUs (no in-workgroup split)
+    big, small = _plan(gemm, 2048, 4096, 4096, cus=256), _plan(gemm, 2048, 4096, 4096, cus=64)
+    assert big.row_tiles == 16 and big.ksplit == 2 and small.row_tiles == 16 and small.ksplit == 1
+    # decode GEMV at M = 1 on 4096 x 4096: 32-k chunks while they give at most
+    # two workgroups per CU -- on 64 CUs the grid stays at 64-k chunks
+    big, small = _plan(gemv, 1, 4096, 4096, cus=256), _plan(gemv, 1, 4096, 4096, cus=64)
+    assert big.kernel == 0 and small.kernel == 0
+    assert big.splits == 32 and small.splits == 16
+    # W4A8 at M = 2048 on (4096, 4096): 256 tiles of 128 x 256, K split inside
+    # the workgroup only when there are no more of them than CUs
+    big, small = _plan(w8, 2048, 4096, 4096, -1, cus=256), _plan(w8, 2048, 4096, 4096, -1, cus=64)
+    assert big.kernel == 2 and small.kernel == 2
+    assert big.tiles_n * big.tiles_m == 256 and big.ksplit == 2
+    assert small.tiles_n * small.tiles_m == 256 and small.ksplit == 1
+    # every plan is valid at any CU count
+    for cus in (8, 32, 64, 80, 128, 256, 304):
+        for op, M, N, K, G in ((gemv, 1, 4096, 11008, 128), (gemv, 8, 22016, 4096, 64), (gemm, 16, 3072, 768, 128),
+                               (gemm, 64, 6144, 4096, 128), (gemm, 4096, 28672, 4096, 128),
+                               (gemm, 300, 136, 4096, 32), (w8, 1, 8192, 21760, -1), (w8, 64, 8192, 21760, 128),
+                               (w8, 1024, 8192, 21760, -1)):
+            p = _plan(op, M, N, K, G, cus=cus)
+            assert 1 <= p.splits <= 255 and p.tiles_n >= 1 and p.tiles_m >= 1 and p.ksplit in (1, 2)
+            assert (p.splits > 1) == (p.workspace_bytes > 0), (cus, op, M, N, K)
