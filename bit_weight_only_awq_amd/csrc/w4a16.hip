@@ -24,7 +24,8 @@
 //    and scale are applied once per chunk on the fp32 sums.  bf16: the B
 //    operand is the exact integer (q - z), scaled once per chunk.  The 4 waves of a
 //    workgroup (4 consecutive chunks) are reduced through LDS, workgroups
-//    along K through counting fixed-point atomics (device.hpp).
+//    along K through counting fixed-point atomics (fp16) or per-tile fp32
+//    partials (bf16; device.hpp).
 //  * tiled kernel (prefill): a workgroup of 4 waves (2 x 2) owns a
 //    (2*16*MTW) x 256 output tile; each wave runs the full K of its slice with
 //    MTW row tiles x 8 column MFMAs per 32-k step, B = (q - z) * s rounded
@@ -38,8 +39,15 @@ namespace awq4 {
 // Workgroup epilogue of the decode kernels: every wave parks its M x COLS
 // partial in LDS (red[wave][m][c]); after one barrier each thread adds the
 // WAVES partials of its elements in wave order (a fixed order, so the result
-// is deterministic) and either writes the output (no split) or contributes the
-// sum to the counting accumulators (split-K; device.hpp).
+// is deterministic) and either writes the output (no split) or hands the sum
+// to the split-K reduction (device.hpp):
+//  - fp16 outputs: one counting fixed-point accumulator per element (steps of
+//    2^-28, a sixteenth of the finest fp16 spacing, with range 2^19 beyond the
+//    largest fp16; one device-scope round trip per workgroup);
+//  - bf16 outputs: per-tile fp32 partials summed in split order by the last
+//    workgroup of the tile.  bf16 keeps binary32's exponent range, so no
+//    fixed-point step suits every output: a step fine enough for |y| ~ 1e-3
+//    leaves no range for large outputs, and a coarse one loses small outputs.
 template <int BLK, int DT, int WAVES = 4>
 __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red, uint16_t *__restrict__ y,
                                                 uint64_t *__restrict__ acc64, int M, int N, int wave, int gq,
@@ -60,6 +68,10 @@ __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red
     }
     __syncthreads();
     const int n_base = tile * COLS;
+    const int S = gridDim.y;
+    // bf16 split-K: workspace = tile counters, then fp32 partials [S][M][N]
+    float *const part = (float *)((char *)acc64 + split_counters_bytes(gridDim.x));
+    const size_t slot = (size_t)M * N;
     for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int n = n_base + c;
@@ -67,20 +79,37 @@ __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red
         float v = red[idx];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) v += red[(size_t)w * total + idx];
-        if (gridDim.y == 1) {
+        if (S == 1) {
             y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
-        } else {
+        } else if (DT == DT_F16) {
             int64_t sum;
-            if (splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(v), gridDim.y, &sum))
+            if (splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(v), S, &sum))
                 y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
+        } else {
+            part[blockIdx.y * slot + (size_t)m * N + n] = v;
         }
+    }
+    if (DT == DT_F16 || S == 1) return;
+    if (!split_tile_last((uint32_t *)acc64 + tile, S)) return;
+    // the last workgroup of the tile: partials summed in split order, then
+    // cleared (the workspace is zero again after the call)
+    for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
+        const int m = idx / COLS, c = idx - m * COLS;
+        const int n = n_base + c;
+        if (n >= N) continue;
+        float *p = part + (size_t)m * N + n;
+        float v = 0.f;
+        for (int s = 0; s < S; ++s) v += p[s * slot];
+        for (int s = 0; s < S; ++s) p[s * slot] = 0.f;
+        y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
     }
 }
 
 // ===========================================================================
 // Decode kernel.  grid = (column tiles, ceil(chunks / WAVES)), 64*WAVES
 // threads.  Dynamic LDS: WAVES * M * (128*BLK) floats.  Workspace (when gridDim.y > 1):
-// one counting accumulator per output element, acc64[M][N] (device.hpp).
+// fp16, one counting accumulator per output element, acc64[M][N]; bf16, one
+// arrival counter per column tile and fp32 partials [S][M][N] (device.hpp).
 // The launch bound asks for 4 waves per SIMD (<= 128 registers) at CS <= 2:
 // the whole weight stream of a layer must be in flight at once, and this fits
 // without spills (measured faster than the compiler's own 3-wave allocation).

@@ -48,12 +48,15 @@ def check_fp(y_gpu: torch.Tensor, y64: np.ndarray, dtype: str = "f16", what: str
     return rel, mx
 
 
-def sample_rows(M: int, n: int = 12, seed: int = 0) -> np.ndarray:
+def sample_rows(M: int, n: int = 12, seed: int = 0, tile: int = 256) -> np.ndarray:
     """Rows to check with the oracle at sizes it cannot do whole: the first and
-    last rows of the matrix and of a 16-row tile boundary plus random ones."""
+    last rows of the matrix and of a 16-row tile boundary, one random row in
+    every `tile`-row block (so no workgroup row tile goes unchecked), plus
+    random ones."""
     if M <= n + 4:
         return np.arange(M)
     rng = np.random.default_rng(seed)
     fixed = [0, 1, 15, 16, M // 2, M - 17, M - 2, M - 1]
+    per_tile = [b + int(rng.integers(0, min(tile, M - b))) for b in range(0, M, tile)]
     rnd = rng.choice(M, size=n, replace=False)
-    return np.unique(np.concatenate([fixed, rnd]).clip(0, M - 1))
+    return np.unique(np.concatenate([fixed, per_tile, rnd]).clip(0, M - 1))

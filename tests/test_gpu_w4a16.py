@@ -115,6 +115,86 @@ def test_exact_special_case_bit_identical():
                 assert torch.equal(y.cpu(), exp), (M, K, N, entry, split)
 
 
+# (M, K, N, split_k, expected plan: row tiles, wave groups splitting K, K splits)
+MAIN_TILE_CASES = [
+    (2048, 4096, 8192, 0, (16, 1, 1)),   # 512 tiles of 256 x 128: the large-M configuration
+    (2048, 4096, 4096, 0, (16, 2, 1)),   # 256 tiles: two wave groups split K in the workgroup
+    (2048, 4096, 8192, 2, (16, 1, 2)),   # K split through partial tiles
+    (2048, 4096, 4096, 3, (16, 1, 3)),   # three splits, 64 stages (uneven)
+    (1024, 4096, 4096, 0, (8, 2, 1)),    # 128-row tiles where 256-row ones would leave CUs idle
+    (512, 14336, 4096, 0, (8, 2, 2)),    # K = 14336: K split and in-workgroup split together
+    (64, 4096, 4096, 0, (8, 1, 4)),      # deep copy rings below 128 rows
+    (100, 4096, 6144, 0, (8, 1, 4)),     # deep rings, ragged last row tile
+]
+
+
+@pytest.mark.parametrize("M,K,N,split,plan", MAIN_TILE_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_exact_special_case_main_tiles(M, K, N, split, plan, dtype):
+    """The bit-exact special case (z = 0, s = 2^-3, x in {-1, 0, 1}) at full
+    size on every configuration of the LDS GEMM: the exact sums are multiples
+    of 1/8 below 2^21, so the GPU's fp32 accumulation is exact and both sides
+    round the same value once.  Checked on sampled rows (one in every 256-row
+    tile), all columns."""
+    info = awq.plan_info(awq.AWQ_OP_GEMM_W4A16, M, N, K, 128, split)
+    if info["cu_count"] == 256:
+        assert info["kernel"] == 3 and (info["row_tiles"], info["ksplit"], info["splits"]) == plan, info
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    g = torch.Generator().manual_seed(M * 7 + N + split)
+    X = torch.randint(-1, 2, (M, K), generator=g).to(tdt)
+    qw = torch.randint(-(2 ** 31), 2 ** 31, (K, N // 8), generator=g, dtype=torch.int64).to(torch.int32)
+    qz = torch.zeros(K // 128, N // 8, dtype=torch.int32)
+    s = torch.full((K // 128, N), 0.125, dtype=tdt)
+    y = awq.gemm_w4a16(*to_dev(X, qw, s, qz), 128, split_k=split)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, seed=M + N)
+    y64 = orc().w4a16(X[torch.as_tensor(rows)], qw, s, qz, 128, F16 if dtype == "f16" else BF16, nthreads=THREADS)
+    exp = torch.from_numpy(y64).to(tdt)
+    got = y.cpu()[torch.as_tensor(rows)]
+    assert torch.equal(got, exp), (M, K, N, split, dtype, int((got != exp).sum()))
+
+
+def test_gemv_bf16_small_outputs():
+    """bf16 decode outputs of about 1e-3 (scales near 1.5e-6): the split-K sum
+    keeps bf16's relative precision at any magnitude (reading A8's relative
+    bar), on the down layer's 43 K splits and the o layer's 32."""
+    for M, K, N in ((1, 11008, 4096), (4, 4096, 4096), (8, 4096, 1032)):
+        c = synthgen.w4a16_case(M, K, N, 128, dtype="bf16")
+        g = torch.Generator().manual_seed(K + M)
+        c.scales = (1e-6 + 1e-6 * torch.rand(c.scales.shape, generator=g, dtype=torch.float64)).to(torch.bfloat16)
+        yg, y64, _ = _run(c, "gemv")
+        rel, mx = check_fp(yg, y64, "bf16", f"bf16 small outputs M={M} K={K} N={N}")
+        assert np.abs(y64).max() < 0.05 and rel <= 1e-2
+
+
+def test_two_streams_unsynchronised():
+    """Split-K calls on two streams with no synchronisation between them each
+    get their own workspace (keyed by device and stream), and a later call on
+    the first stream still finds its workspace clear."""
+    cases = [synthgen.w4a16_case(1, 4096, 4096, 128, seed=11), synthgen.w4a16_case(64, 4096, 4096, 128, seed=12),
+             synthgen.w4a16_case(2, 11008, 4096, 128, seed=13)]
+    devs = [to_dev(c.x, c.qweight, c.scales, c.qzeros) for c in cases]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            outs.append(("a", awq.gemv_w4a16(*devs[0], 128)))
+        with torch.cuda.stream(s2):
+            outs.append(("b", awq.gemm_w4a16(*devs[1], 128)))
+            outs.append(("c", awq.gemv_w4a16(*devs[2], 128)))
+    with torch.cuda.stream(s1):
+        outs.append(("c", awq.gemv_w4a16(*devs[2], 128)))
+    torch.cuda.synchronize()
+    ref = {k: orc().w4a16(c.x, c.qweight, c.scales, c.qzeros, 128, nthreads=THREADS)
+           for k, c in zip("abc", cases)}
+    first = {}
+    for k, y in outs:
+        check_fp(y.cpu(), ref[k], "f16", f"stream case {k}")
+        first.setdefault(k, y)
+        assert torch.equal(y, first[k]), k
+
+
 @pytest.mark.parametrize("M,K,N,G", [(1, 32, 8, 32), (5, 96, 24, 32), (17, 64, 136, 64), (33, 128, 264, 128),
                                      (100, 192, 72, 64), (129, 256, 1032, 128), (2, 4096, 8, 128),
                                      (300, 128, 40, 32)])

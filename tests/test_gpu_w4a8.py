@@ -174,3 +174,66 @@ def test_linear_repeated_calls_and_split_workspace():
         y2 = awq.linear_w4a8(x, b, s2)
         torch.cuda.synchronize()
         assert torch.equal(y2.view(torch.int16), y1.view(torch.int16)), (M, K, N)
+
+
+# (M, K, N, G, expected plan: tiles_n, tiles_m, wave groups splitting K, K splits)
+LDS_CASES = [
+    (2048, 4096, 8192, -1, (32, 16, 1, 1)),   # 128 x 256 tiles (8 waves), two per CU
+    (2048, 4096, 4096, -1, (16, 16, 2, 1)),   # one 128 x 256 tile per CU: K split inside the workgroup
+    (1024, 4096, 4096, 128, (32, 8, 1, 1)),   # 128 x 128 tiles (4 waves), per group
+    (256, 4096, 4096, -1, (32, 2, 1, 4)),     # few tiles: K split through int32 partial tiles
+    (300, 4096, 1032, 64, (9, 3, 1, 10)),     # ragged rows and columns, split, per group
+]
+
+
+@pytest.mark.parametrize("M,K,N,G,plan", LDS_CASES, ids=lambda v: str(v))
+def test_lds_gemm_output_bit_exact(M, K, N, G, plan):
+    """The LDS-pipelined W4A8 GEMM's fp16 output is one rounding of
+    acc * s1 * s2: with power-of-two s1 and s2 and |acc| < 2^24 that product
+    is exact in fp32, so y must equal the oracle's fp64 value rounded once,
+    bit for bit (and acc exactly), on every tile configuration."""
+    info = awq.plan_info(awq.AWQ_OP_W4A8_GEMM, M, N, K, G)
+    if info["cu_count"] == 256:
+        assert info["kernel"] == 2 and (info["tiles_n"], info["tiles_m"], info["ksplit"], info["splits"]) == plan, info
+    g = torch.Generator().manual_seed(M + N + K)
+    a8 = torch.randint(-128, 128, (M, K), generator=g, dtype=torch.int64).to(torch.int8)
+    s1 = torch.pow(2.0, -torch.randint(5, 12, (M,), generator=g).to(torch.float32))
+    c = synthgen.w4a8_case(1, K, N, G)
+    s2 = torch.pow(2.0, -torch.randint(3, 9, (N,), generator=g).to(torch.float32)).to(torch.float16)
+    y, acc = awq.w4a8_gemm(*to_dev(a8, c.b, s1, s2, c.s3), G, want_acc=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, seed=M, tile=128)
+    eacc, y64 = orc().w4a8(a8.numpy()[rows], c.b, s1.numpy()[rows], s2, c.s3, G, nthreads=THREADS)
+    assert np.abs(eacc).max() < 2 ** 24
+    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), eacc)
+    exp = torch.from_numpy(y64).to(torch.float16)
+    got = y.cpu()[torch.as_tensor(rows)]
+    assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), int((got != exp).sum())
+
+
+def test_w4a8_largest_k_all_minimum():
+    """K = 131008, the largest K the library accepts: a row of -2^-14 quantises
+    to s1 = 2^-21 and a8 = -128 everywhere, and with every weight -8 the
+    kernels' int32 sum of (-128) * (16 * -8) reaches 2^14 * K = 2146435072,
+    just below 2^31.  The accumulators must come back exact (acc = 1024 K),
+    through the two-step layer call and the separate calls alike."""
+    M, K, N = 2, 131008, 64
+    x = torch.full((M, K), -(2.0 ** -14), dtype=torch.float16)
+    x[1] = synthgen.activations(1, K, seed=5)[0]
+    b = torch.full((K // 8, N), -0x77777778, dtype=torch.int32)  # 0x88888888: every nibble -8
+    s2 = (0.002 + 0.018 * torch.rand(N, generator=torch.Generator().manual_seed(1))).to(torch.float16)
+    xd, bd, s2d = to_dev(x, b, s2)
+    y1, s1b, acc1 = awq.linear_w4a8(xd, bd, s2d, want_acc=True)
+    a8, s1 = awq.quant_act(xd)
+    y2, acc2 = awq.w4a8_gemm(a8, bd, s1, s2d, want_acc=True)
+    torch.cuda.synchronize()
+    ea8, es1 = orc().quant_act(x)
+    assert float(es1[0]) == 2.0 ** -21 and np.all(ea8[0] == -128)
+    assert np.array_equal(a8.cpu().numpy(), ea8)
+    eacc, y64 = orc().w4a8(ea8, b, es1, s2, nthreads=THREADS)
+    assert eacc[0, 0] == 1024 * K
+    for acc, y in ((acc1, y1), (acc2, y2)):
+        assert np.array_equal(acc.cpu().numpy().astype(np.int64), eacc)
+        exp = torch.from_numpy(y64).to(torch.float16)
+        assert torch.equal(y.cpu()[0], exp[0])  # acc * s1 * s2 with s1 a power of two: one rounding
+        check_fp(y.cpu()[1:], y64[1:], "f16", "largest K, random row")
