@@ -25,6 +25,7 @@ W4A8_LAYOUT_K8 = 1
 AWQ_OP_GEMM_W4A16 = 0
 AWQ_OP_GEMV_W4A16 = 1
 AWQ_OP_W4A8_GEMM = 2
+AWQ_STATIC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -62,13 +63,14 @@ def lib() -> ctypes.CDLL:
     w4a16 = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, sz, vp]
     L.awq_gemm_w4a16.argtypes = w4a16
     L.awq_gemv_w4a16.argtypes = w4a16
+    L.awq_gemv_w4a16_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     L.w4a8_quant_act.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.w4a8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     L.w4a8_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     L.awq_stream_read.argtypes = [vp, i64, vp, vp]
     L.awq_plan_info.argtypes = [i32, i64, i64, i64, i32, i32, i32, ctypes.POINTER(PlanInfo)]
     for f in ("awq_pack", "awq_unpack", "awq_gemm_w4a16", "awq_gemv_w4a16", "w4a8_quant_act", "w4a8_gemm", "w4a8_linear",
-              "awq_stream_read", "awq_plan_info"):
+              "awq_stream_read", "awq_plan_info", "awq_gemv_w4a16_static"):
         getattr(L, f).restype = i32
     _lib = L
     return L

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/awq4.h"
 #include "launch.hpp"
@@ -55,16 +56,66 @@ static DeviceProps props_of_device(int dev) {
     return DeviceProps{cus};
 }
 
-// properties of the device that `stream` belongs to (the current device for
-// the null stream)
-static DeviceProps stream_props(void *stream) {
+// the device that `stream` belongs to (the current device for the null
+// stream), or -1 when none can be found
+static int stream_device(void *stream) {
     int dev = -1;
     if (stream) {
         hipDevice_t d;
         if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &d) == hipSuccess) dev = (int)d;
     }
-    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return DeviceProps{kDefaultCUs};
-    return props_of_device(dev);
+    if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return -1;
+    return dev;
+}
+
+// properties of the device that `stream` belongs to
+static DeviceProps stream_props(void *stream) {
+    const int dev = stream_device(stream);
+    return dev < 0 ? DeviceProps{kDefaultCUs} : props_of_device(dev);
+}
+
+// ---------------------------------------------------------------------------
+// Static split-K scratch of the no-allocation decode entry point
+// (awq_gemv_w4a16_static).  Each device that loads the library holds its own
+// copy until the process ends.  In host code `scratch` only names the array:
+// its device address comes from hipGetSymbolAddress, taken once per device
+// with that device current and kept in g_scratch; kernels and clears use that
+// address, never the name.
+constexpr size_t kScratchBytes = AWQ_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchSlot {
+    std::atomic<void *> ptr{nullptr};
+    std::atomic<int> cleared{0};  // a clear has been enqueued outside graph capture
+};
+static ScratchSlot g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// fills n 16-byte words with zero (a kernel rather than a memset, so that a
+// clear recorded into a graph replays correctly)
+__global__ void scratch_zero(uint4 *p, size_t n) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+static int scratch_of_device(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices) return AWQ_EHIP;
+    void *p = g_scratch[dev].ptr.load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].ptr.load(std::memory_order_acquire);
+        if (!p) {
+            int cur = -1;
+            if (hipGetDevice(&cur) != hipSuccess) return AWQ_EHIP;
+            if (cur != dev && hipSetDevice(dev) != hipSuccess) return AWQ_EHIP;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (cur != dev) (void)hipSetDevice(cur);
+            if (e != hipSuccess || !p) return AWQ_EHIP;
+            g_scratch[dev].ptr.store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return AWQ_OK;
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -419,6 +470,36 @@ int awq_gemv_w4a16(const void *x, const int32_t *qweight, const void *scales, co
                    size_t workspace_bytes, void *stream) {
     return run_w4a16(x, qweight, scales, qzeros, y, M, N, K, group_size, dtype, split_k, workspace,
                      workspace_bytes, stream, true);
+}
+
+int awq_gemv_w4a16_static(const void *x, const int32_t *qweight, const void *scales, const int32_t *qzeros,
+                          void *y, int64_t M, int64_t N, int64_t K, int group_size, int dtype, void *stream) {
+    int rc = check_w4a16(x, qweight, scales, qzeros, y, M, N, K, group_size, dtype, 0);
+    if (rc != AWQ_OK) return rc;
+    if (M > 8) return AWQ_EUNSUPPORTED;
+    const int dev = stream_device(stream);
+    if (dev < 0) return AWQ_EHIP;
+    W4A16Plan p = plan_w4a16(M, N, K, group_size, 0, dtype, props_of_device(dev));
+    if (p.workspace_bytes > kScratchBytes) return AWQ_EWORKSPACE;
+    void *ws = nullptr;
+    rc = scratch_of_device(dev, &ws);
+    if (rc != AWQ_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // The split-K kernels need the scratch zero (they leave it zero after
+    // every call).  Until a clear has been enqueued on this device outside
+    // graph capture, clear it first; a clear recorded into a graph runs only
+    // when the graph does, so it does not count.
+    if (!g_scratch[dev].cleared.load(std::memory_order_acquire)) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) != hipSuccess) return AWQ_EHIP;
+        hipLaunchKernelGGL(scratch_zero, dim3(256), dim3(256), 0, st, static_cast<uint4 *>(ws),
+                           kScratchBytes / sizeof(uint4));
+        if (hipGetLastError() != hipSuccess) return AWQ_EHIP;
+        if (cs == hipStreamCaptureStatusNone) g_scratch[dev].cleared.store(1, std::memory_order_release);
+    }
+    if (p.workspace_bytes > 0) p.acc = static_cast<uint64_t *>(ws);
+    W4A16Args a{x, qweight, scales, qzeros, y, M, N, K, group_size, dtype};
+    return hip_status(p.kind == 0 ? launch_w4a16_decode(a, p, st) : launch_w4a16_tiled(a, p, st));
 }
 
 int w4a8_quant_act(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, void *stream) {

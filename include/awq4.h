@@ -193,6 +193,32 @@ int awq_gemv_w4a16(const void *x, const int32_t *qweight, const void *scales,
                    size_t workspace_bytes, void *stream);
 
 /*
+ * awq_gemv_w4a16_static -- awq_gemv_w4a16 for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same kernels, results and argument rules,
+ * without a workspace argument.  The split-K reduction runs in a static
+ * scratch array of 16 MiB (AWQ_STATIC_SCRATCH_BYTES) that each device holds
+ * from the library's load until the process ends; the call itself allocates
+ * and frees nothing.
+ *   Its first call on a device looks up that device's copy of the array and
+ *   enqueues a clear of it on `stream` ahead of the GEMV (again on each later
+ *   call until one runs outside graph capture, since a clear recorded into a
+ *   graph runs only with the graph).
+ *   Every call on one device shares that device's array, which the kernels
+ *   leave zero after each call: calls that overlap in time on one device
+ *   (different streams, or a graph replayed beside an eager call) race and
+ *   must be ordered by the caller.
+ * Errors: as awq_gemv_w4a16 (AWQ_EUNSUPPORTED for M > 8), plus
+ * AWQ_EWORKSPACE when the call's split-K reduction needs more than
+ * AWQ_STATIC_SCRATCH_BYTES (awq_plan_info reports the need), and AWQ_EHIP if
+ * the device or its copy of the array cannot be found.
+ */
+#define AWQ_STATIC_SCRATCH_BYTES (16u << 20)
+int awq_gemv_w4a16_static(const void *x, const int32_t *qweight, const void *scales,
+                          const int32_t *qzeros, void *y, int64_t M, int64_t N, int64_t K,
+                          int group_size, int dtype, void *stream);
+
+/*
  * w4a8_quant_act -- dynamic per-token int8 quantisation of activations
  * ([P5], the dynamic_quant helper):
  *   s1[m]   = float( act( max_k |x[m,k]| / 127 ) )
