@@ -48,6 +48,7 @@ TARGET_SHAPES = [(4096, 4096), (4096, 14336)]   # (K, N): the stated M=1 / M=204
 M_TARGETS = (1, 2048)
 ROTATE_MB = 600
 KERNEL_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/gemm_w4a16.hip",
+                  "bit_weight_only_awq_amd/csrc/dequant.hip",
                   "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp", "bit_weight_only_awq_amd/csrc/w4a8.hip",
                   "bit_weight_only_awq_amd/csrc/gemm_w4a8.hip", "bit_weight_only_awq_amd/csrc/stream.hip",
                   "bit_weight_only_awq_amd/csrc/device.hpp", "bit_weight_only_awq_amd/csrc/launch.hpp",
@@ -145,7 +146,12 @@ def traffic_summary(fetch_csv, write_csv, kernel="w4a16_decode", name="w4a16_dec
 
 def cpu_baseline(budget_s: float):
     """The oracle on the decode workload (M=1 over the Llama-2-7B layer set), run
-    on this host's cores until about budget_s seconds of work are done."""
+    on this host's cores until about budget_s seconds of work are done; beside
+    it, the oracle on the prefill workload (the Llama-3-8B layer set at M=2048)
+    on a seeded subset of 256 of the 2048 rows (its time scaled to the full
+    layer, labelled as scaled), and one decode pass on a single thread."""
+    import torch
+
     import oracle
     import synthgen
     orc = oracle.get()
@@ -162,9 +168,191 @@ def cpu_baseline(budget_s: float):
             break
     dt = time.perf_counter() - t0
     mb = sum(w4a16_weight_bytes(K, N) for _, K, N in DECODE_LAYERS) / 1e6
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"decode M=1 on the Llama-2-7B layer set (4 layers, {mb:.1f} MB of weights) x {reps} "
-                      f"passes in {dt:.1f} s; fp64 scalar C oracle on {cores} threads"}
+    out = {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+           "sample": f"decode M=1 on the Llama-2-7B layer set (4 layers, {mb:.1f} MB of weights) x {reps} "
+                     f"passes in {dt:.1f} s; fp64 scalar C oracle on {cores} threads"}
+    # one decode pass, single-threaded
+    t0 = time.perf_counter()
+    for c in cases:
+        orc.w4a16(c.x, c.qweight, c.scales, c.qzeros, G, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    out["single_thread"] = {"value": round(mb / 1e3 / dt1, 4), "unit": "GB/s", "cores": 1,
+                            "sample": f"one decode pass (4 layers) in {dt1:.1f} s"}
+    # prefill: 256 of the 2048 rows of each layer, time scaled by 2048 / 256
+    rows, flops, tg = 256, 0.0, 0.0
+    for name, K, N in PREFILL_LAYERS:
+        c = synthgen.w4a16_case(M_PREFILL, K, N, G, seed=synthgen.seed_for(f"bench|prefill|{name}"),
+                                x_rows=M_PREFILL)
+        g = torch.Generator().manual_seed(synthgen.seed_for(f"cpu|rows|{name}"))
+        sel = torch.randperm(M_PREFILL, generator=g)[:rows].sort().values
+        t0 = time.perf_counter()
+        orc.w4a16(c.x[sel], c.qweight, c.scales, c.qzeros, G, nthreads=cores)
+        tg += (time.perf_counter() - t0) * (M_PREFILL / rows)
+        flops += 2.0 * M_PREFILL * N * K
+    out["gemm_m2048"] = {"value": round(flops / tg / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "scaled": True,
+                         "sample": f"prefill GEMM M=2048 on the Llama-3-8B layer set, a seeded subset of {rows} "
+                                   f"rows per layer; time scaled by {M_PREFILL // rows} to {tg:.1f} s for the "
+                                   f"whole pass"}
+    return out
+
+
+def roof_frac(t, flops, alg_bytes, peak_t):
+    """Fraction of the roofline: the time at min(MFMA peak, intensity x HBM) over the measured time."""
+    t_roof = max(flops / (peak_t * 1e12), alg_bytes / (HBM_PEAK_GBS * 1e9))
+    return round(t_roof / t, 4), ("mfma" if flops / (peak_t * 1e12) >= alg_bytes / (HBM_PEAK_GBS * 1e9) else "hbm")
+
+
+def config_sweeps(awq, synthgen, torch, dev, per_launch, decode, n_copies, comparator):
+    """Every configuration of the workloads beyond the headline step, timed per
+    layer (graphs of one layer; weights rotated through >= ROTATE_MB of copies
+    wherever the weights dominate the bytes, so they stream from HBM):
+      cfg0: opt-125m fc1 (M=16, K=768, N=3072; fits in L2, absolute time);
+      cfg1: decode GEMV M in {1, 2, 4, 8} on the Llama-2-7B layer set;
+      cfg2: prefill GEMM M in {64, 256, 1024, 2048, 4096} on the Llama-3-8B
+            layer set, with the dequantise + vendor dense GEMM route beside it
+            for M >= 256;
+      cfg3: K=4096, N=14336, M in {1, 512} x G in {32, 64, 128} x {fp16, bf16}
+            x {zero point, symmetric};
+      cfg4: W4A8 on the QQQ shape, M in {1, 16, 64, 256, 1024}, per-channel
+            and g128 (whole layer: quantisation + GEMM; and the GEMM alone).
+    Each entry carries the fraction of min(MFMA peak, intensity x HBM) it reaches."""
+    f16 = torch.float16
+    res = {}
+
+    def rotate(tensors, nbytes):
+        ncp = max(2, -(-ROTATE_MB * 10 ** 6 // nbytes))
+        return [tuple(tensors)] + [tuple(t.clone() for t in tensors) for _ in range(ncp - 1)]
+
+    # cfg0
+    c = synthgen.w4a16_case(16, 768, 3072, 128, seed=0)
+    x0, q0, s0, z0 = (t.to(dev) for t in (c.x, c.qweight, c.scales, c.qzeros))
+    y0 = torch.empty(16, 3072, dtype=f16, device=dev)
+    t = per_launch(lambda: awq.gemm_w4a16(x0, q0, s0, z0, 128, out=y0), 1)
+    res["cfg0_opt125m_fc1_M16"] = {"us": round(t * 1e6, 2), "TFLOPs": round(2 * 16 * 768 * 3072 / t / 1e12, 2),
+                                   "note": "1.35 MB: served from L2, launch-latency bound; absolute time"}
+
+    # cfg1: the decode copies already rotate the Llama-2-7B weights
+    cfg1 = {}
+    for M in (1, 2, 4, 8):
+        for li, (name, K, N) in enumerate(DECODE_LAYERS):
+            x = synthgen.activations(M, K, seed=synthgen.seed_for(f"bench|cfg1|{M}|{K}")).to(dev)
+            y = torch.empty(M, N, dtype=f16, device=dev)
+            t = per_launch(lambda x=x, y=y, li=li: [awq.gemv_w4a16(x, decode[r][li][1], decode[r][li][2],
+                                                                   decode[r][li][3], G, out=y)
+                                                    for r in range(n_copies)], n_copies)
+            ab = w4a16_alg_bytes(M, K, N)
+            fr, bound = roof_frac(t, 2 * M * N * K, ab, MFMA_F16_PEAK_TFLOPS)
+            cfg1[f"M={M} {name} {K}x{N}"] = {"us": round(t * 1e6, 2),
+                                             "weight_GBs": round(w4a16_weight_bytes(K, N) / t / 1e9, 1),
+                                             "frac_roofline": fr, "bound": bound}
+    res["cfg1_decode_llama2_7b"] = cfg1
+
+    # cfg2
+    cfg2 = {}
+    xs = {K: synthgen.activations(4096, K, seed=synthgen.seed_for(f"bench|cfg2|x|{K}")).to(dev)
+          for K in {K for _, K, _ in PREFILL_LAYERS}}
+    for name, K, N in PREFILL_LAYERS:
+        cw = synthgen.w4a16_case(1, K, N, G, seed=synthgen.seed_for(f"bench|cfg2|w|{name}"))
+        base = tuple(t.to(dev) for t in (cw.qweight, cw.scales, cw.qzeros))
+        copies = rotate(base, w4a16_weight_bytes(K, N))
+        ybuf = torch.empty(4096, N, dtype=f16, device=dev)
+        wd = awq.dequant_w4a16(*base, G) if comparator else None
+        for M in (64, 256, 1024, 2048, 4096):
+            x, y = xs[K][:M], ybuf[:M]
+            ncp = len(copies) if M <= 256 else 1
+            t = per_launch(lambda x=x, y=y, ncp=ncp: [awq.gemm_w4a16(x, *copies[r], G, out=y) for r in range(ncp)],
+                           ncp, reps=3)
+            flops = 2 * M * N * K
+            fr, bound = roof_frac(t, flops, w4a16_alg_bytes(M, K, N), MFMA_F16_PEAK_TFLOPS)
+            e = {"us": round(t * 1e6, 2), "TFLOPs": round(flops / t / 1e12, 1), "frac_roofline": fr, "bound": bound,
+                 "weights": "rotated" if ncp > 1 else "one copy (MFMA-bound)"}
+            if comparator and M >= 256:
+                tdq = per_launch(lambda: awq.dequant_w4a16(*base, G, out=wd), 1, reps=3)
+                tmm = per_launch(lambda x=x, y=y: torch.matmul(x, wd, out=y), 1, reps=3)
+                e["dequant_plus_dense"] = {"dequant_us": round(tdq * 1e6, 2), "dense_us": round(tmm * 1e6, 2),
+                                           "total_us": round((tdq + tmm) * 1e6, 2),
+                                           "dense_TFLOPs": round(flops / tmm / 1e12, 1),
+                                           "speedup_of_fused": round((tdq + tmm) / t, 3)}
+            cfg2[f"M={M} {name} {K}x{N}"] = e
+        del copies, wd, ybuf
+    del xs
+    res["cfg2_prefill_llama3_8b"] = cfg2
+
+    # cfg3
+    cfg3 = {}
+    K, N = 4096, 14336
+    x1 = {dt: synthgen.activations(512, K, dtype=dt, seed=synthgen.seed_for(f"bench|cfg3|x|{dt}")).to(dev)
+          for dt in ("f16", "bf16")}
+    for Gv in (32, 64, 128):
+        for sym in (False, True):
+            cw = synthgen.w4a16_case(1, K, N, Gv, sym=sym, seed=synthgen.seed_for(f"bench|cfg3|{Gv}|{sym}"))
+            qw = cw.qweight.to(dev)
+            qz = None if sym else cw.qzeros.to(dev)
+            wb = w4a16_weight_bytes(K, N, Gv, sym)
+            for dt in ("f16", "bf16"):
+                sc = cw.scales.to(torch.bfloat16 if dt == "bf16" else f16).to(dev)
+                copies = rotate((qw, sc) + (() if sym else (qz,)), wb)
+                for M in (1, 512):
+                    x = x1[dt][:M]
+                    y = torch.empty(M, N, dtype=x.dtype, device=dev)
+                    fn = awq.gemv_w4a16 if M == 1 else awq.gemm_w4a16
+                    ncp = len(copies) if M == 1 else 1
+                    t = per_launch(lambda x=x, y=y, fn=fn, ncp=ncp, copies=copies:
+                                   [fn(x, copies[r][0], copies[r][1], None if sym else copies[r][2], Gv, out=y)
+                                    for r in range(ncp)], ncp, reps=3)
+                    ab = wb + M * K * 2 + M * N * 2
+                    fr, bound = roof_frac(t, 2 * M * N * K, ab, MFMA_F16_PEAK_TFLOPS)
+                    cfg3[f"M={M} g{Gv} {dt} {'sym' if sym else 'zp'}"] = {
+                        "us": round(t * 1e6, 2), "frac_roofline": fr, "bound": bound,
+                        **({"weight_GBs": round(wb / t / 1e9, 1)} if M == 1 else
+                           {"TFLOPs": round(2 * M * N * K / t / 1e12, 1)})}
+                del copies
+    del x1
+    res["cfg3_variants_4096x14336"] = cfg3
+
+    # cfg4
+    cfg4 = {}
+    K, N = W4A8_K, W4A8_N
+    for Gv in (-1, 128):
+        c8 = synthgen.w4a8_case(1, K, N, Gv, seed=synthgen.seed_for(f"bench|cfg4|w|{Gv}"))
+        parts = (c8.b.to(dev), c8.s2.to(dev)) + (() if Gv < 0 else (c8.s3.to(dev),))
+        copies = rotate(parts, K * N // 2)
+        for M in (1, 16, 64, 256, 1024):
+            x = synthgen.activations(M, K, seed=synthgen.seed_for(f"bench|cfg4|x|{M}")).to(dev)
+            a8 = torch.empty(M, K, dtype=torch.int8, device=dev)
+            s1 = torch.empty(M, dtype=torch.float32, device=dev)
+            y = torch.empty(M, N, dtype=f16, device=dev)
+            ncp = len(copies) if M <= 64 else 1
+
+            def s3_of(r):
+                return None if Gv < 0 else copies[r][2]
+            tl = per_launch(lambda x=x, y=y, a8=a8, s1=s1, ncp=ncp:
+                            [awq.linear_w4a8(x, copies[r][0], copies[r][1], s3_of(r), Gv, out=y, a8=a8, s1=s1)
+                             for r in range(ncp)], ncp, reps=3)
+            awq.quant_act(x, a8, s1)
+            tg = per_launch(lambda y=y, a8=a8, s1=s1, ncp=ncp:
+                            [awq.w4a8_gemm(a8, copies[r][0], s1, copies[r][1], s3_of(r), Gv, out=y)
+                             for r in range(ncp)], ncp, reps=3)
+            ops = 2 * M * N * K
+            ab = w4a8_alg_bytes(M, K, N) + (0 if Gv < 0 else (K // Gv) * N * 2)
+            fr, bound = roof_frac(tg, ops, ab, MFMA_I8_PEAK_TOPS)
+            frl, _ = roof_frac(tl, ops, ab + 3 * M * K, MFMA_I8_PEAK_TOPS)
+            cfg4[f"M={M} {'per-channel' if Gv < 0 else 'g128'}"] = {
+                "layer_us": round(tl * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
+                "gemm_TOPs": round(ops / tg / 1e12, 1), "gemm_frac_roofline": fr, "layer_frac_roofline": frl,
+                "bound": bound}
+        del copies
+    res["cfg4_w4a8_qqq_n8192_k21760"] = cfg4
+
+    # the read probe over 2 GiB: the asymptotic read rate of the device
+    big = torch.empty(2 ** 31 // 2, dtype=f16, device=dev)
+    big.fill_(1.0)
+    sink = torch.empty(awq.ops.STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+    t = per_launch(lambda: awq.stream_read(big, sink), 1, reps=3)
+    res["stream_read_2GiB"] = {"us": round(t * 1e6, 1), "GBs": round(2 ** 31 / t / 1e9, 1),
+                               "frac_hbm": round(2 ** 31 / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del big
+    return res
 
 
 def main():
@@ -175,6 +363,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true", help="skip the dense fp16 GEMM comparator")
+    ap.add_argument("--no-sweeps", action="store_true", help="skip the per-configuration sweeps")
     ap.add_argument("--profile", choices=["decode", "prefill", "w4a8", "targets"], default=None,
                     help="no timing: run one phase eagerly --profile-reps times (for rocprofv3 counter passes), "
                          "after a 256 MiB device copy of known size that calibrates the byte counters")
@@ -470,6 +659,9 @@ def main():
                     r["frac_mfma"] = round(ops / tt / 1e12 / peak, 4)
                 targets[key] = r
 
+    sweeps = None if args.no_sweeps else config_sweeps(awq, synthgen, torch, dev, per_launch, decode, n_copies,
+                                                       not args.no_comparator)
+
     digest = source_digest()
     dec_alg = sum(w4a16_alg_bytes(M_DECODE, K, N) for _, K, N in DECODE_LAYERS)
     achieved = dec_alg / t_dec / 1e9
@@ -504,6 +696,8 @@ def main():
            "targets": {"note": "W4A8 times are whole-layer calls (w4a8_linear): activation quantisation included, fused into the GEMM at M=1", **targets},
            "phases_us": {"decode": round(t_dec * 1e6, 2), "prefill": round(t_pre * 1e6, 2),
                          "w4a8": round(t_w8 * 1e6, 2)}}
+    if sweeps is not None:
+        out["configs"] = sweeps
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
     print(json.dumps(out), flush=True)

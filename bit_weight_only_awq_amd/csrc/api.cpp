@@ -502,6 +502,16 @@ int awq_gemv_w4a16_static(const void *x, const int32_t *qweight, const void *sca
     return hip_status(p.kind == 0 ? launch_w4a16_decode(a, p, st) : launch_w4a16_tiled(a, p, st));
 }
 
+int awq_dequant_w4a16(const int32_t *qweight, const void *scales, const int32_t *qzeros, void *w, int64_t N,
+                      int64_t K, int group_size, int dtype, void *stream) {
+    int64_t dummy = 16;  // stands in for x and y, which this call does not have
+    int rc = check_w4a16(&dummy, qweight, scales, qzeros, w ? w : nullptr, 1, N, K, group_size, dtype, 0);
+    if (rc != AWQ_OK) return rc;
+    if ((K / 8) * ((N / 8 + 255) / 256) >= (int64_t(1) << 31)) return AWQ_EUNSUPPORTED;
+    return hip_status(launch_w4a16_dequant(qweight, scales, qzeros, w, N, K, group_size, dtype,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int w4a8_quant_act(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, void *stream) {
     if (!x || !a8 || !s1) return AWQ_EINVAL;
     if (M < 1 || K < 1 || M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 30)) return AWQ_EINVAL;

@@ -320,4 +320,29 @@ __device__ __forceinline__ bool split_tile_last(uint32_t *cnt, int S) {
     return last;
 }
 
+// The same completion for partials exchanged only through agent-scope atomic
+// stores and loads, for launches with many workgroups (the decode GEMV).
+// An agent-scope release fence writes back the issuing XCD's whole L2 (the
+// write-back of plain stores that other XCDs must see); one per workgroup of
+// a ~1000-workgroup decode launch measured 4-5x the kernel's own time.
+// Agent-scope atomic stores go through to the device-wide coherence point
+// themselves, so here each thread only waits until its own partial stores
+// have completed before the workgroup's counting atomic, and the workgroup
+// that completes the count reads the partials with agent-scope atomic loads
+// (issued after it has seen the count, through the barrier), which do not
+// read stale L2 lines.
+__device__ __forceinline__ bool split_tile_last_atomic(uint32_t *cnt, int S) {
+    __shared__ uint32_t last_flag;
+    wait_vm_all();    // this thread's partial stores have completed
+    __syncthreads();  // ... and every other thread's
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t last = old == (uint32_t)(S - 1) ? 1u : 0u;
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = last;
+    }
+    __syncthreads();
+    return last_flag != 0;
+}
+
 }  // namespace awq4

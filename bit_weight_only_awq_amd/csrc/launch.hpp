@@ -108,6 +108,9 @@ size_t w4a8_fused_lds_bytes(int64_t M, int64_t K, int blk, int splits);
 // word per wave
 constexpr int64_t kStreamMaxBlocks = 2048;
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, hipStream_t st);
+// dense [K, N] fp16/bf16 copy of the dequantised weights (a comparator's operand)
+hipError_t launch_w4a16_dequant(const int32_t *qweight, const void *scales, const int32_t *qzeros, void *w, int64_t N,
+                                int64_t K, int G, int dtype, hipStream_t st);
 hipError_t launch_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int layout,
                        int32_t *clamp_count, hipStream_t st);
 hipError_t launch_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, int layout,

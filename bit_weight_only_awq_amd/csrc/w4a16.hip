@@ -45,7 +45,8 @@ namespace awq4 {
 //    2^-28, a sixteenth of the finest fp16 spacing, with range 2^19 beyond the
 //    largest fp16; one device-scope round trip per workgroup);
 //  - bf16 outputs: per-tile fp32 partials summed in split order by the last
-//    workgroup of the tile.  bf16 keeps binary32's exponent range, so no
+//    workgroup of the tile, exchanged through agent-scope atomic stores and
+//    loads (no L2 write-back per workgroup; device.hpp).  bf16 keeps binary32's exponent range, so no
 //    fixed-point step suits every output: a step fine enough for |y| ~ 1e-3
 //    leaves no range for large outputs, and a coarse one loses small outputs.
 template <int BLK, int DT, int WAVES = 4>
@@ -86,21 +87,34 @@ __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red
             if (splitk_contribute(&acc64[(size_t)m * N + n], to_fixed<DT>(v), S, &sum))
                 y[(size_t)m * N + n] = f32_to_out_bits(from_fixed<DT>(sum), DT);
         } else {
-            part[blockIdx.y * slot + (size_t)m * N + n] = v;
+            __hip_atomic_store(&part[blockIdx.y * slot + (size_t)m * N + n], v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     if (DT == DT_F16 || S == 1) return;
-    if (!split_tile_last((uint32_t *)acc64 + tile, S)) return;
+    if (!split_tile_last_atomic((uint32_t *)acc64 + tile, S)) return;
     // the last workgroup of the tile: partials summed in split order, then
-    // cleared (the workspace is zero again after the call)
+    // cleared (the workspace is zero again after the call).  The loads of a
+    // batch of splits are all issued before the first is added, so the sum
+    // costs one memory round trip per batch rather than one per split.
+    constexpr int kBatch = 16;
     for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int n = n_base + c;
         if (n >= N) continue;
         float *p = part + (size_t)m * N + n;
         float v = 0.f;
-        for (int s = 0; s < S; ++s) v += p[s * slot];
-        for (int s = 0; s < S; ++s) p[s * slot] = 0.f;
+        for (int s0 = 0; s0 < S; s0 += kBatch) {
+            float b[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                b[i] = s0 + i < S ? __hip_atomic_load(&p[(size_t)(s0 + i) * slot], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0.f;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) v += b[i];
+        }
+        for (int s = 0; s < S; ++s) __hip_atomic_store(&p[(size_t)s * slot], 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
     }
 }

@@ -152,6 +152,21 @@ def linear_w4a16(x, qweight, scales, qzeros, group_size: int = 128, out=None):
     return gemv_w4a16(x, qweight, scales, qzeros, group_size, out=out)
 
 
+def dequant_w4a16(qweight, scales, qzeros, group_size: int = 128, out=None):
+    """Dense W = (q - z) * s, [K, N] in the scales' dtype (one rounding per
+    element): the weight operand of a dense vendor GEMM, for comparison."""
+    _need_cuda(qweight, scales, qzeros, out)
+    if scales.dtype not in _F16:
+        raise ValueError("scales must be fp16 or bf16")
+    K, N = qweight.shape[0], qweight.shape[1] * 8
+    if out is None:
+        out = torch.empty(K, N, dtype=scales.dtype, device=qweight.device)
+    L.check("awq_dequant_w4a16", L.lib().awq_dequant_w4a16(_ptr(qweight), _ptr(scales), _ptr(qzeros), _ptr(out), N,
+                                                           K, group_size, _F16[scales.dtype],
+                                                           _stream(qweight.device)))
+    return out
+
+
 # ----------------------------------------------------------------------------- W4A8
 
 def quant_act(x: torch.Tensor, a8: torch.Tensor | None = None, s1: torch.Tensor | None = None):

@@ -193,6 +193,20 @@ int awq_gemv_w4a16(const void *x, const int32_t *qweight, const void *scales,
                    size_t workspace_bytes, void *stream);
 
 /*
+ * awq_dequant_w4a16 -- the dense weight matrix W[k,n] = (q - z) * s rounded
+ * once (to nearest even) to the activation dtype, [K, N] row-major: the
+ * operand a dense vendor GEMM needs for the "dequantise, then call the dense
+ * BLAS GEMM for long sequences" route of the [P1] TODO list.  Not used by the
+ * 4-bit GEMM calls; provided for comparison and export.
+ *   qweight, scales, qzeros, group_size, dtype: as awq_gemm_w4a16 (qzeros
+ *   NULL = symmetric, z = 8).
+ *   w: device, [K, N] fp16 or bf16, written.
+ * Errors: AWQ_EINVAL, AWQ_EALIGN, AWQ_EHIP.
+ */
+int awq_dequant_w4a16(const int32_t *qweight, const void *scales, const int32_t *qzeros, void *w,
+                      int64_t N, int64_t K, int group_size, int dtype, void *stream);
+
+/*
  * awq_gemv_w4a16_static -- awq_gemv_w4a16 for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation): the same kernels, results and argument rules,

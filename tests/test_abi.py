@@ -251,3 +251,13 @@ def test_plan_sizes_grids_from_the_cu_count():
             p = _plan(op, M, N, K, G, cus=cus)
             assert 1 <= p.splits <= 255 and p.tiles_n >= 1 and p.tiles_m >= 1 and p.ksplit in (1, 2)
             assert (p.splits > 1) == (p.workspace_bytes > 0), (cus, op, M, N, K)
+
+
+def test_dequant_validation():
+    lib = L.lib()
+    assert lib.awq_dequant_w4a16(A, A, A, None, 4096, 4096, 128, 0, None) == L.AWQ_EINVAL   # no output
+    assert lib.awq_dequant_w4a16(None, A, A, A, 4096, 4096, 128, 0, None) == L.AWQ_EINVAL
+    assert lib.awq_dequant_w4a16(A, A, A, A, 4092, 4096, 128, 0, None) == L.AWQ_EINVAL      # N % 8
+    assert lib.awq_dequant_w4a16(A, A, A, A, 4096, 4000, 128, 0, None) == L.AWQ_EINVAL      # K % G
+    assert lib.awq_dequant_w4a16(A, A, A, A, 4096, 4096, 128, 5, None) == L.AWQ_EINVAL      # dtype
+    assert lib.awq_dequant_w4a16(A, A, A, MIS, 4096, 4096, 128, 0, None) == L.AWQ_EALIGN
