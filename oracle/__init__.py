@@ -99,8 +99,14 @@ class Oracle:
         L.orc_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp]
         L.orc_quant_act.argtypes = [vp, i64, i64, i32, vp, vp]
         L.orc_w4a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, i32]
+        L.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_to_f64.restype = ctypes.c_double
+        L.orc_f64_to_e4m3.argtypes = [ctypes.c_double]
+        L.orc_f64_to_e4m3.restype = ctypes.c_uint8
+        L.orc_quant_act_fp8.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        L.orc_w4a8_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         for f in ("orc_unpack_n8", "orc_pack_n8", "orc_unpack_k8", "orc_pack_k8", "orc_w4a16",
-                  "orc_dequant", "orc_quant_act", "orc_w4a8"):
+                  "orc_dequant", "orc_quant_act", "orc_w4a8", "orc_quant_act_fp8", "orc_w4a8_fp8"):
             getattr(L, f).restype = ctypes.c_int
 
     # -- scalar formats ------------------------------------------------------
@@ -210,6 +216,40 @@ class Oracle:
                                int(group_size), int(dtype), _p(acc), _p(y), int(nthreads))
         if rc:
             raise ValueError("w4a8: bad shape or non-integer group scale")
+        return acc, y
+
+
+    # -- INT4-FP8 W4A8 -----------------------------------------------------------
+    def e4m3_to_f64(self, code: int) -> float:
+        return self.lib.orc_e4m3_to_f64(int(code) & 0xFF)
+
+    def f64_to_e4m3(self, v: float) -> int:
+        return int(self.lib.orc_f64_to_e4m3(float(v)))
+
+    def quant_act_fp8(self, x, dtype: int = F16):
+        """Per-token E4M3 quantisation -> (codes uint8 [M,K], s1 fp32 [M], asum fp32 [M])."""
+        xb = _u16(x)
+        M, K = xb.shape
+        a = np.empty((M, K), np.uint8)
+        s1 = np.empty((M,), np.float32)
+        asum = np.empty((M,), np.float32)
+        assert self.lib.orc_quant_act_fp8(_p(xb), M, K, int(dtype), _p(a), _p(s1), _p(asum)) == 0
+        return a, s1, asum
+
+    def w4a8_fp8(self, a, b_packed, s1, s2, dtype: int = F16, want_y: bool = True):
+        """(acc fp64 [M,N] exact, Y64 fp64 [M,N]) of the INT4-FP8 W4A8 GEMM."""
+        ac = np.ascontiguousarray(a, dtype=np.uint8)
+        b = _i32(b_packed)
+        M, K = ac.shape
+        kb, N = b.shape
+        assert kb * 8 == K
+        s1a = np.ascontiguousarray(s1, dtype=np.float32)
+        s2a = _u16(s2)
+        acc = np.empty((M, N), np.float64)
+        y = np.empty((M, N), np.float64) if want_y else None
+        rc = self.lib.orc_w4a8_fp8(_p(ac), _p(b), _p(s1a), _p(s2a), M, N, K, int(dtype), _p(acc), _p(y))
+        if rc:
+            raise ValueError("w4a8_fp8: bad shape")
         return acc, y
 
 

@@ -39,6 +39,9 @@
  *    int8 and the whole-K accumulation stays an exact int32; per-channel is the
  *    case with no s3 (w8 = q).
  *  - A row whose fp16 scale s1 rounds to zero quantises to all zeros.
+ *  - INT4-FP8 (the QQQ authors' announced follow-up, named only): the int8
+ *    recipe with OCP FP8 E4M3 codes and 448 in place of int8 codes and 127,
+ *    round to nearest even with saturation at +-448, per-channel scales.
  *
  * Parity unpinned: compatibility with real AWQ checkpoints and QQQ exports
  * (how real files apply the order map, and QQQ's own weight layout).  No such
@@ -366,6 +369,119 @@ int orc_quant_act(const uint16_t *x, int64_t M, int64_t K, int dtype, int8_t *a8
             a8[m * K + k] = (int8_t)r;
         }
     }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* INT4-FP8 W4A8 ([P5]: the authors' announced follow-up, "INT4-FP8 QQQ  */
+/* (W4A8)"; the pages give no more than its name).  Reading: the int8     */
+/* recipe with the int8 code replaced by an OCP FP8 E4M3 code (1 sign,    */
+/* 4 exponent bits with bias 7, 3 mantissa bits; no infinities, largest   */
+/* finite 448; the all-ones pattern is NaN), the divisor 127 replaced by  */
+/* 448, rounding to nearest even with saturation at +-448; int4 weights   */
+/* are exact in E4M3; per-channel scales only.                            */
+
+/* E4M3 code -> double (exact). */
+double orc_e4m3_to_f64(uint8_t c) {
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9); /* subnormal: m * 2^-9 */
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* double -> E4M3, round to nearest, ties to even, saturating at +-448
+ * (the value is clamped into [-448, 448] first); NaN -> 0x7f. */
+uint8_t orc_f64_to_e4m3(double v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (isnan(v)) return 0x7f;
+    if (a > 448.0) a = 448.0;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: quantum 2^-9; 8 quanta is the smallest normal,
+         * whose code is the same integer 0x08 */
+        double r = nearbyint(ldexp(a, 9));
+        return sign | (uint8_t)r;
+    }
+    int e2;
+    frexp(a, &e2);        /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;       /* unbiased exponent, -6..8 */
+    double r = nearbyint(ldexp(a, 3 - E)); /* significand in [8, 16] */
+    if (r == 16.0) {
+        r = 8.0;
+        E += 1;
+    }
+    return sign | (uint8_t)((E + 7) << 3) | (uint8_t)((int)r - 8);
+}
+
+/* Per-token FP8 quantisation of activations [M, K] (fp16 dtype 0, bf16 1):
+ *   amax  = max_k |x[m,k]|
+ *   s1    = float( act( float(amax) / 448 ) )        (fp32 divide, rounded to the activation type)
+ *   a[m,k]= e4m3( clamp( float(x) / s1, -448, 448 ) ) (fp32 divide, nearest even)
+ *   asum  = float( sum_k e4m3_value(a[m,k]) )        (the exact sum, rounded once)
+ * A row with s1 == 0 gives codes 0 and asum 0.  asum is the row sum of the
+ * quantised activations, which the GPU GEMM needs (it stores the weights with
+ * an offset of 8). */
+int orc_quant_act_fp8(const uint16_t *x, int64_t M, int64_t K, int dtype, uint8_t *a, float *s1,
+                      float *asum) {
+    if (M < 0 || K <= 0 || (dtype != 0 && dtype != 1)) return ORC_EINVAL;
+    for (int64_t m = 0; m < M; m++) {
+        const uint16_t *row = x + m * K;
+        double amax = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            double mag = fabs(decode_act(row[k], dtype));
+            if (mag > amax) amax = mag;
+        }
+        float quot = (float)amax / 448.0f;
+        float s = (float)round_act((double)quot, dtype);
+        s1[m] = s;
+        double sum = 0.0; /* exact: multiples of 2^-9 below 2^53 * 2^-9 */
+        for (int64_t k = 0; k < K; k++) {
+            uint8_t c = 0;
+            if (s != 0.0f) {
+                float q = (float)decode_act(row[k], dtype) / s;
+                if (q > 448.0f) q = 448.0f;
+                if (q < -448.0f) q = -448.0f;
+                c = orc_f64_to_e4m3((double)q);
+            }
+            a[m * K + k] = c;
+            sum += orc_e4m3_to_f64(c);
+        }
+        asum[m] = (float)sum;
+    }
+    return ORC_OK;
+}
+
+/* acc[m,n] = sum_k e4m3_value(a[m,k]) * q[k,n]   (exact in double: every
+ * product is a multiple of 2^-9 and every partial sum stays far below 2^44)
+ * Y64[m,n] = acc * s1[m] * s2[n], with q the K8-packed int4 weights and s2
+ * per output channel (fp16 dtype 0 / bf16 dtype 1).  Either output may be
+ * NULL. */
+int orc_w4a8_fp8(const uint8_t *a, const int32_t *b, const float *s1, const uint16_t *s2, int64_t M,
+                 int64_t N, int64_t K, int dtype, double *acc, double *y) {
+    if (M < 0 || N <= 0 || K <= 0 || K % 8 || (dtype != 0 && dtype != 1)) return ORC_EINVAL;
+    double *av = (double *)malloc(sizeof(double) * (size_t)(M * K + 1));
+    int *q = (int *)malloc(sizeof(int) * (size_t)K);
+    if (!av || !q) { free(av); free(q); return ORC_EINVAL; }
+    for (int64_t i = 0; i < M * K; i++) av[i] = orc_e4m3_to_f64(a[i]);
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t kb = 0; kb < K / 8; kb++) {
+            uint32_t w = (uint32_t)b[kb * N + n];
+            for (int i = 0; i < 8; i++) q[8 * kb + K8_ORDER[i]] = sext4((w >> (4 * i)) & 0xF);
+        }
+        double s2n = decode_act(s2[n], dtype);
+        for (int64_t m = 0; m < M; m++) {
+            double sacc = 0.0;
+            for (int64_t k = 0; k < K; k++) sacc += av[m * K + k] * (double)q[k];
+            if (acc) acc[m * N + n] = sacc;
+            if (y) y[m * N + n] = sacc * (double)s1[m] * s2n;
+        }
+    }
+    free(av);
+    free(q);
     return ORC_OK;
 }
 

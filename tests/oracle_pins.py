@@ -547,11 +547,193 @@ def pin_w4a8_group16_is_channel(orc):
     assert 128 * 128 * 21760 < 2 ** 31
 
 
+# ----------------------------------------------------------------------------- INT4-FP8 W4A8
+
+def _e4m3_torch(codes):
+    """Library decode of E4M3 codes (torch's float8_e4m3fn)."""
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _e4m3_exact(fr: Fraction) -> int:
+    """Round-to-nearest-even of a rational to E4M3, saturating at 448: the
+    candidate grid written out from the format (quantum 2^-9 below 2^-6, else
+    2^(e-3) in [2^e, 2^(e+1)))."""
+    neg = fr < 0
+    a = -fr if neg else fr
+    if a >= 448:
+        return (0x80 if neg else 0) | 0x7E
+    if a < Fraction(1, 64):
+        quantum, e = Fraction(1, 512), None
+    else:
+        e = 0
+        while Fraction(2) ** (e + 1) <= a:
+            e += 1
+        while Fraction(2) ** e > a:
+            e -= 1
+        quantum = Fraction(2) ** (e - 3)
+    n = a / quantum
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    v = lo * quantum
+    if v == 0:
+        return 0x80 if neg else 0
+    # encode the (exactly representable) value v
+    if v < Fraction(1, 64):
+        code = int(v * 512)
+    else:
+        e = 0
+        while Fraction(2) ** (e + 1) <= v:
+            e += 1
+        while Fraction(2) ** e > v:
+            e -= 1
+        code = ((e + 7) << 3) | int(v / Fraction(2) ** (e - 3) - 8)
+    return (0x80 if neg else 0) | code
+
+
+def pin_e4m3_decode(orc):
+    """Every E4M3 code decodes as torch's float8_e4m3fn does (NaN at 0x7f and 0xff)."""
+    ref = _e4m3_torch(np.arange(256))
+    got = np.array([orc.e4m3_to_f64(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.flatnonzero(np.isnan(ref)).tolist() == [0x7F, 0xFF]
+
+
+def pin_e4m3_encode(orc):
+    """The encoder: every finite code round-trips, every midpoint goes to the
+    even neighbour (exact rationals), random values match exact rounding and
+    torch's float32 -> float8_e4m3fn cast, and values beyond 448 saturate."""
+    vals = _e4m3_torch(np.arange(256))
+    for c in range(256):
+        if not np.isnan(vals[c]):
+            assert orc.f64_to_e4m3(float(vals[c])) == c, hex(c)
+    pos = np.unique(vals[(vals > 0) & ~np.isnan(vals)])
+    mids = np.concatenate([[pos[0] / 2], (pos[:-1] + pos[1:]) / 2])
+    for v in mids:
+        exp = _e4m3_exact(Fraction(float(v)))
+        assert orc.f64_to_e4m3(float(v)) == exp and orc.f64_to_e4m3(-float(v)) == exp | 0x80, v
+    rng = np.random.default_rng(31)
+    rnd = (rng.standard_normal(3000) * 10.0 ** rng.integers(-4, 3, 3000)).astype(np.float32)
+    rnd = rnd[np.abs(rnd) <= 448]
+    tor = torch.from_numpy(rnd).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for v, t in zip(rnd, tor):
+        exp = _e4m3_exact(Fraction(float(v)))
+        got = orc.f64_to_e4m3(float(v))
+        assert got == exp and (got == int(t) or float(v) == 0), (float(v), hex(got), hex(exp), hex(int(t)))
+    for v, c in ((448.0, 0x7E), (463.9, 0x7E), (464.0, 0x7E), (1e30, 0x7E), (-1e30, 0xFE), (-448.0, 0xFE)):
+        assert orc.f64_to_e4m3(v) == c, v
+    assert orc.f64_to_e4m3(float("nan")) == 0x7F
+
+
+def _golden_fp8():
+    rows = []
+    with open(os.path.join(GOLDEN, "quant_act_fp8_examples.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            lhs, rhs = line.split("->")
+            dt, xs = lhs.split()
+            s1, codes, asum = rhs.split()
+            rows.append((0 if dt == "f16" else 1, [float(v) for v in xs.split(",")], float(s1),
+                         [int(c, 16) for c in codes.split(",")], float(asum)))
+    return rows
+
+
+def pin_quant_fp8_examples(orc):
+    for dt, xs, s1, codes, asum in _golden_fp8():
+        xb = _f16_bits([xs]) if dt == 0 else _bf16_bits([xs])
+        a, got_s1, got_sum = orc.quant_act_fp8(xb, dtype=dt)
+        assert float(got_s1[0]) == s1, (xs, got_s1[0], s1)
+        assert a[0].tolist() == codes, (xs, [hex(c) for c in a[0]], [hex(c) for c in codes])
+        assert float(got_sum[0]) == asum, (xs, got_sum[0], asum)
+
+
+def pin_quant_fp8_s1_exhaustive(orc):
+    """s1 = fp16(amax/448) for every positive finite fp16 amax equals the exact
+    quotient rounded once; with a normal s1 the row extremes map to +-448."""
+    bits = np.arange(1, 0x7C00, dtype=np.uint16)
+    x = np.stack([bits, bits | 0x8000], axis=1)
+    a, s1, asum = orc.quant_act_fp8(x)
+    amax = bits.view(np.float16).astype(np.float64)
+    for i in range(len(bits)):
+        assert float(s1[i]) == _rne_f16_fraction(Fraction(float(amax[i])) / 448), hex(bits[i])
+    normal = s1 >= 2.0 ** -14
+    assert np.all(a[normal, 0] == 0x7E) and np.all(a[normal, 1] == 0xFE)
+    assert np.all(asum[normal] == 0)
+
+
+def pin_quant_fp8_random(orc):
+    """Random fp16 and bf16 rows: codes equal torch's cast of the clamped fp32
+    quotient, and asum is the exact sum of the codes' values rounded once."""
+    rng = np.random.default_rng(32)
+    for dt in (0, 1):
+        xd = rng.standard_normal((5, 600)) * np.array([[1], [0.01], [30], [1e-3], [1]])
+        xd[4, :] = 0
+        xb = _f16_bits(xd) if dt == 0 else _bf16_bits(xd)
+        xv = xb.view(np.float16).astype(np.float64) if dt == 0 else \
+            torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+        a, s1, asum = orc.quant_act_fp8(xb, dtype=dt)
+        for m in range(xd.shape[0]):
+            amax = Fraction(float(np.abs(xv[m]).max())) / 448
+            exp_s1 = _rne_f16_fraction(amax) if dt == 0 else _rne_bf16_fraction(amax)
+            assert float(s1[m]) == exp_s1
+            if exp_s1 == 0:
+                assert np.all(a[m] == 0) and asum[m] == 0
+                continue
+            q = np.clip(xv[m].astype(np.float32) / np.float32(exp_s1), -448, 448).astype(np.float32)
+            tor = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(a[m], tor), m
+            exact = sum(Fraction(float(v)) for v in _e4m3_torch(a[m]))
+            assert float(asum[m]) == float(np.float32(float(exact)))
+
+
+def pin_w4a8_fp8_bruteforce(orc):
+    """acc and Y64 straight from packed words and codes, in exact rationals."""
+    rng = np.random.default_rng(33)
+    M, K, N = 3, 64, 8
+    a = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    q = rng.integers(-8, 8, size=(K, N)).astype(np.int8)
+    b, _ = orc.pack_k8(q)
+    s1 = (rng.random(M) * 0.05 + 0.001).astype(np.float32)
+    s2 = (0.002 + 0.018 * rng.random(N)).astype(np.float16)
+    acc, y = orc.w4a8_fp8(a, b, s1, s2.view(np.uint16))
+    av = _e4m3_torch(a)
+    for m in range(M):
+        for n in range(N):
+            ref = sum(Fraction(float(av[m, k])) * int(q[k, n]) for k in range(K))
+            assert acc[m, n] == float(ref)
+            exp_y = ref * Fraction(float(s1[m])) * Fraction(float(s2[n]))
+            assert abs(y[m, n] - float(exp_y)) <= 1e-15 * max(1.0, abs(float(exp_y)))
+
+
+def pin_w4a8_fp8_integer_codes(orc):
+    """Codes of the integers -16..16 (all exact in E4M3) give the same
+    accumulators as the int8 W4A8 oracle on those integers: the two routines
+    agree where both are defined."""
+    rng = np.random.default_rng(34)
+    M, K, N = 4, 256, 24
+    ints = rng.integers(-16, 17, size=(M, K))
+    codes = np.array([[orc.f64_to_e4m3(float(v)) for v in row] for row in ints], np.uint8)
+    b = rng.integers(0, 2 ** 32, size=(K // 8, N), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    s1 = np.ones(M, np.float32)
+    s2 = np.full(N, 0.5, np.float16)
+    acc8, _ = orc.w4a8(ints.astype(np.int8), b, s1, s2.view(np.uint16))
+    acc, y = orc.w4a8_fp8(codes, b, s1, s2.view(np.uint16))
+    assert np.array_equal(acc, acc8.astype(np.float64))
+    assert np.array_equal(y, acc8 * 0.5)
+
+
 ALL_PINS = [
     pin_golden_words, pin_pair_extraction, pin_k8_masks, pin_roundtrip, pin_pack_clamp,
     pin_dequant_exhaustive, pin_w4a16_exact_special, pin_w4a16_numpy, pin_w4a16_invariants,
     pin_quant_examples, pin_quant_bf16_examples, pin_quant_random, pin_quant_bf16_random,
     pin_w4a8_bruteforce, pin_w4a8_group16_is_channel, pin_w4a8_bf16_scales, pin_bf16_decode,
     pin_w4a16_bruteforce, pin_w4a16_bf16, pin_f16_codec, pin_bf16_encode, pin_quant_s1_exhaustive,
-    pin_quant_bf16_s1_exhaustive,
+    pin_quant_bf16_s1_exhaustive, pin_e4m3_decode, pin_e4m3_encode, pin_quant_fp8_examples,
+    pin_w4a8_fp8_bruteforce, pin_w4a8_fp8_integer_codes, pin_quant_fp8_random, pin_quant_fp8_s1_exhaustive,
 ]

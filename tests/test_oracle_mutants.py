@@ -44,6 +44,19 @@ MUTANTS = {
                                 "for (int64_t i = 0; i < M * K; i++) xd[i] = decode_act(x[i], 0);"),
     "w4a16_scale_dtype_ignored": ("double s = decode_act(t->scales[g * t->N + 8 * j + col], t->dtype);",
                                   "double s = decode_act(t->scales[g * t->N + 8 * j + col], 0);"),
+    "e4m3_bias": ("v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */",
+                  "v = ldexp((double)(8 + m), e - 11); /* (1 + m/8) * 2^(e-7) */"),
+    "e4m3_subnormal_quantum": ("v = ldexp((double)m, -9); /* subnormal: m * 2^-9 */",
+                               "v = ldexp((double)m, -10); /* subnormal: m * 2^-9 */"),
+    "e4m3_no_saturation": ("if (a > 448.0) a = 448.0;", "if (a > 480.0) a = 480.0;"),
+    "e4m3_ties_away": ("double r = nearbyint(ldexp(a, 3 - E));", "double r = floor(ldexp(a, 3 - E) + 0.5);"),
+    "fp8_divisor_127": ("float quot = (float)amax / 448.0f;", "float quot = (float)amax / 127.0f;"),
+    "fp8_s1_not_rounded": ("float s = (float)round_act((double)quot, dtype);", "float s = quot;"),
+    "fp8_input_dtype_ignored": ("double mag = fabs(decode_act(row[k], dtype));", "double mag = fabs(decode_act(row[k], 0));"),
+    "fp8_asum_magnitudes": ("sum += orc_e4m3_to_f64(c);", "sum += fabs(orc_e4m3_to_f64(c));"),
+    "fp8_gemm_s1_dropped": ("if (y) y[m * N + n] = sacc * (double)s1[m] * s2n;", "if (y) y[m * N + n] = sacc * s2n;"),
+    "fp8_gemm_k8_order": ("for (int i = 0; i < 8; i++) q[8 * kb + K8_ORDER[i]] = sext4((w >> (4 * i)) & 0xF);",
+                          "for (int i = 0; i < 8; i++) q[8 * kb + i] = sext4((w >> (4 * i)) & 0xF);"),
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
 }
 
