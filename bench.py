@@ -50,6 +50,7 @@ ROTATE_MB = 600
 KERNEL_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/gemm_w4a16.hip",
                   "bit_weight_only_awq_amd/csrc/dequant.hip",
                   "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp", "bit_weight_only_awq_amd/csrc/w4a8.hip",
+                  "bit_weight_only_awq_amd/csrc/w4a8_fp8.hip",
                   "bit_weight_only_awq_amd/csrc/gemm_w4a8.hip", "bit_weight_only_awq_amd/csrc/stream.hip",
                   "bit_weight_only_awq_amd/csrc/device.hpp", "bit_weight_only_awq_amd/csrc/launch.hpp",
                   "bit_weight_only_awq_amd/csrc/api.cpp"]
@@ -343,6 +344,36 @@ def config_sweeps(awq, synthgen, torch, dev, per_launch, decode, n_copies, compa
                 "bound": bound}
         del copies
     res["cfg4_w4a8_qqq_n8192_k21760"] = cfg4
+
+    # INT4-FP8 W4A8 (E4M3 activations) on the QQQ shape and the target shapes:
+    # quantisation and GEMM timed separately; the GEMM's roofline is the fp8
+    # matrix-core peak (5033 TFLOP/s dense), weights rotated at M <= 64
+    fp8 = {}
+    shapes = [(M, W4A8_K, W4A8_N) for M in (1, 16, 64, 256, 1024)] + \
+             [(M, K, N) for K, N in TARGET_SHAPES for M in M_TARGETS]
+    wsets = {}
+    for M, K, N in shapes:
+        if (K, N) not in wsets:
+            c8 = synthgen.w4a8_case(1, K, N, -1, seed=synthgen.seed_for(f"bench|fp8|w|{K}|{N}"))
+            wsets[(K, N)] = rotate((c8.b.to(dev), c8.s2.to(dev)), K * N // 2)
+        copies = wsets[(K, N)]
+        x = synthgen.activations(M, K, seed=synthgen.seed_for(f"bench|fp8|x|{M}|{K}")).to(dev)
+        a, s1, asum = awq.quant_act_fp8(x)
+        y = torch.empty(M, N, dtype=f16, device=dev)
+        ncp = len(copies) if M <= 64 else 1
+        tq = per_launch(lambda x=x, a=a, s1=s1, asum=asum: awq.quant_act_fp8(x, a, s1, asum), 1, reps=3)
+        tg = per_launch(lambda a=a, s1=s1, asum=asum, y=y, ncp=ncp, copies=copies:
+                        [awq.w4a8_fp8_gemm(a, copies[r][0], s1, asum, copies[r][1], out=y) for r in range(ncp)],
+                        ncp, reps=3)
+        flops = 2 * M * N * K
+        ab = w4a8_alg_bytes(M, K, N) + 4 * M  # + asum
+        fr, bound = roof_frac(tg, flops, ab, MFMA_I8_PEAK_TOPS)
+        fp8[f"M={M} K={K} N={N}"] = {"quant_us": round(tq * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
+                                     "layer_us": round((tq + tg) * 1e6, 2),
+                                     "gemm_TFLOPs": round(flops / tg / 1e12, 1), "gemm_frac_roofline": fr,
+                                     "bound": bound}
+    del wsets
+    res["w4a8_int4_fp8"] = fp8
 
     # the read probe over 2 GiB: the asymptotic read rate of the device
     big = torch.empty(2 ** 31 // 2, dtype=f16, device=dev)

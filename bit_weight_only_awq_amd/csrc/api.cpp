@@ -315,6 +315,49 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d)
     return p;
 }
 
+W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d) {
+    const int64_t cus = d.cus;
+    W4A8Plan p{};
+    const int64_t T = K / 128;  // 128-k steps
+    int64_t tiles;
+    if (M <= 64) {
+        // split-K skinny kernel, counting fixed-point accumulators
+        p.kind = 0;
+        p.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+        p.blk = (M <= 16 && N % 128 == 0) ? 2 : 1;
+        p.tiles_n = (int)cdiv(N, 64 * p.blk);
+        p.tiles_m = 1;
+        tiles = p.tiles_n;
+        int64_t s = cdiv(target_workgroups(d), tiles);
+        s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
+        p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+        p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;
+    } else {
+        // register-tiled kernel, K split through per-tile fp32 partials
+        p.kind = 1;
+        p.blk = 1;
+        p.mt = M >= 128 ? 4 : 2;
+        p.tiles_n = (int)cdiv(N, 128);
+        p.tiles_m = (int)cdiv(M, 32 * p.mt);
+        tiles = (int64_t)p.tiles_n * p.tiles_m;
+        int64_t s = 1;
+        if (tiles < cus) s = std::min<int64_t>({cdiv(target_workgroups(d), tiles), std::max<int64_t>(1, T / 2), 4});
+        p.splits = (int)std::max<int64_t>(1, s);
+        p.tilered = 1;
+        p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(tiles, p.splits, M, N) : 0;
+    }
+    return p;
+}
+
+// INT4-FP8 shapes: K in 128-k matrix-core steps; the skinny kernel's
+// fixed-point split-K sum holds |sum a u 2^-9| <= 13.2 K below 2^27
+static int check_fp8_shape(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 8 || K < 1 || M > kMaxDim || N > kMaxDim) return AWQ_EINVAL;
+    if (N % 8) return AWQ_EINVAL;
+    if (K % 128 || K > kW8MaxK) return AWQ_EUNSUPPORTED;
+    return AWQ_OK;
+}
+
 static int check_w4a16(const void *x, const int32_t *qweight, const void *scales, const int32_t *qzeros, void *y,
                        int64_t M, int64_t N, int64_t K, int G, int dtype, int split_k) {
     if (!x || !qweight || !scales || !y) return AWQ_EINVAL;
@@ -421,6 +464,10 @@ size_t awq_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int group_si
         if (op == AWQ_OP_GEMV_W4A16 && M > 8) return 0;
         return plan_w4a16(M, N, K, group_size, split_k, -1, stream_props(nullptr)).workspace_bytes;
     }
+    if (op == AWQ_OP_W4A8_FP8_GEMM) {
+        if (check_fp8_shape(M, N, K) != AWQ_OK) return 0;
+        return plan_w4a8_fp8(M, N, K, stream_props(nullptr)).workspace_bytes;
+    }
     if (op == AWQ_OP_W4A8_GEMM) {
         if (M < 1 || N < 8 || N % 8 || K < 64 || K % 64 || M > kMaxDim || N > kMaxDim || K > kW8MaxK) return 0;
         if (group_size != -1 && ((group_size != 32 && group_size != 64 && group_size != 128) || K % group_size))
@@ -443,6 +490,13 @@ int awq_plan_info(int op, int64_t M, int64_t N, int64_t K, int group_size, int s
         const W4A16Plan p = plan_w4a16(M, N, K, group_size, split_k, -1, d);
         *out = awq_plan_t{p.kind, p.tiles_n, p.tiles_m, p.splits, p.mt, std::max(1, p.ksplit), d.cus,
                           (int64_t)p.workspace_bytes};
+        return AWQ_OK;
+    }
+    if (op == AWQ_OP_W4A8_FP8_GEMM) {
+        const int rc = check_fp8_shape(M, N, K);
+        if (rc != AWQ_OK) return rc;
+        const W4A8Plan p = plan_w4a8_fp8(M, N, K, d);
+        *out = awq_plan_t{p.kind, p.tiles_n, p.tiles_m, p.splits, p.mt, 1, d.cus, (int64_t)p.workspace_bytes};
         return AWQ_OK;
     }
     if (op == AWQ_OP_W4A8_GEMM) {
@@ -547,6 +601,33 @@ int w4a8_gemm(const int8_t *a8, const int32_t *b_packed, const float *s1, const 
     W4A8Args a{a8, b_packed, s1, s2_f16, s3_f16, y_f16, acc_out, M, N, K, group_size};
     a.dtype = dtype;
     return hip_status(launch_w4a8(a, p, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_fp8_quant_act(const void *x, uint8_t *a, float *s1, float *asum, int64_t M, int64_t K, int dtype,
+                       void *stream) {
+    if (!x || !a || !s1 || !asum) return AWQ_EINVAL;
+    if (M < 1 || K < 1 || M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 30)) return AWQ_EINVAL;
+    if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
+    if (!aligned16(x) || !aligned16(a) || !aligned16(s1) || !aligned16(asum)) return AWQ_EALIGN;
+    return hip_status(launch_w4a8_fp8_quant(x, a, s1, asum, M, K, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int w4a8_fp8_gemm(const uint8_t *a, const int32_t *b_packed, const float *s1, const float *asum, const void *s2,
+                  void *y, float *acc_out, int64_t M, int64_t N, int64_t K, int dtype, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    if (!a || !b_packed || !s1 || !asum || !s2 || !y) return AWQ_EINVAL;
+    if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
+    int rc = check_fp8_shape(M, N, K);
+    if (rc != AWQ_OK) return rc;
+    if (!aligned16(a) || !aligned16(b_packed) || !aligned16(s1) || !aligned16(asum) || !aligned16(s2) ||
+        !aligned16(y) || (acc_out && !aligned16(acc_out)))
+        return AWQ_EALIGN;
+    W4A8Plan p = plan_w4a8_fp8(M, N, K, stream_props(stream));
+    rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
+    if (rc != AWQ_OK) return rc;
+    if (p.splits > 1) p.acc = static_cast<uint64_t *>(workspace);
+    W4A8Fp8Args g{a, b_packed, s1, asum, s2, y, acc_out, M, N, K, dtype};
+    return hip_status(launch_w4a8_fp8(g, p, static_cast<hipStream_t>(stream)));
 }
 
 int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packed, const void *s2_f16,

@@ -54,6 +54,19 @@ struct W4A8Args {
     int dtype = 0;  // DT_F16 / DT_BF16: activations, s2, s3 and y
 };
 
+// INT4-FP8 W4A8 (E4M3 activation codes, per-channel int4 weights)
+struct W4A8Fp8Args {
+    const uint8_t *a;     // E4M3 codes [M, K]
+    const int32_t *b;     // K8-packed int4 [K/8, N]
+    const float *s1;      // [M]
+    const float *asum;    // [M], row sums of the codes' values
+    const void *s2;       // [N], activation type
+    void *y;              // [M, N], activation type
+    float *acc_out;       // [M, N] fp32 sum_k a q, or nullptr
+    int64_t M, N, K;
+    int dtype;
+};
+
 struct W4A8Plan {
     int kind;  // 0 = skinny, 1 = tiled, 2 = LDS-pipelined GEMM (large M)
     int blk;   // skinny: 64-column sets per lane-row (1, 2)
@@ -92,6 +105,8 @@ constexpr int kDefaultCUs = 256;
 // it), or -1 for a workspace large enough for either
 W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dtype, const DeviceProps &d);
 W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d);
+// INT4-FP8: kind 0 = skinny split-K (M <= 64), 1 = register-tiled
+W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d);
 bool w4a8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p);
 
 hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
@@ -100,6 +115,9 @@ hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
+hipError_t launch_w4a8_fp8_quant(const void *x, uint8_t *a, float *s1, float *asum, int64_t M, int64_t K, int dt,
+                                 hipStream_t st);
+hipError_t launch_w4a8_fp8(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st);
 // skinny W4A8 GEMM with the per-token quantisation fused in (plan kind 0,
 // mt 1); its dynamic LDS and per-wave int8 row area
 hipError_t launch_w4a8_fused(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);

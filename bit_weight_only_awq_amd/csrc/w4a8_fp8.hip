@@ -1,0 +1,419 @@
+// w4a8_fp8.hip -- INT4-FP8 W4A8 on gfx950: per-token OCP FP8 (E4M3)
+// activations x symmetric int4 weights on the fp8 matrix cores.
+//
+// The QQQ pull request "Support W4A8 quantization for vllm" names "INT4-FP8
+// QQQ (W4A8)" as its authors' next step and says nothing more; this library's
+// reading is the int8 recipe of that page with E4M3 codes and 448 (the largest
+// finite E4M3 value) in place of int8 codes and 127, rounded to nearest even
+// and saturated at +-448, per-channel weight scales:
+//   s1[m]    = act(amax_m / 448)                  (fp32 divide, rounded to the activation type)
+//   a[m,k]   = e4m3(clamp(x[m,k] / s1[m], +-448))  (fp32 divide)
+//   y[m,n]   = act((sum_k a[m,k] q[k,n]) * s1[m] * s2[n])
+//
+// Weights: the W4A8 K-packed layout.  The matrix cores take the weights as
+// E4M3 *codes equal to the offset-binary nibble u = q + 8*: a code u in 0..15
+// is the value u * 2^-9 (subnormal below 8, the lowest binade from 8 on), so
+// the B operand is two masks per packed word, as for int8, and the products
+// a * u * 2^-9 are exact.  The epilogue turns the sum back into
+// sum a q = 2^9 * sum(a u 2^-9) - 8 * sum_k a, with the row sums of the
+// activation codes (asum) that the quantiser writes beside s1.
+//
+// Matrix-core operand model (v_mfma_scale_f32_16x16x128_f8f6f4, unit scales):
+// lane l supplies row / column l % 16 and 32 consecutive k, chunk l / 16, as
+// eight registers of four codes; the C layout is that of the 16x16 MFMAs.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace awq4 {
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 code of |q| <= 448 (not NaN), round to nearest, ties to even.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+    const uint32_t u = bit_as<uint32_t>(q);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a < 0x3C800000u) {
+        // below 2^-6: multiples of 2^-9 (the scaling by 512 is exact)
+        code = (uint32_t)__builtin_rintf(bit_as<float>(a) * 512.0f);
+    } else {
+        // round the fp32 significand to 3 bits (nearest even), then rebias
+        // the exponent from 127 to 7; a carry moves into the exponent
+        const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+        code = r - ((127u - 7u) << 3);
+    }
+    return sign | code;
+}
+
+// Value of an E4M3 code in units of 2^-9 (an exact integer, |v| <= 229376).
+__device__ __forceinline__ int32_t e4m3_units(uint32_t c) {
+    const int32_t e = (c >> 3) & 15, m = c & 7;
+    const int32_t v = e == 0 ? m : (8 + m) << (e - 1);
+    return (c & 0x80u) ? -v : v;
+}
+
+template <int DT>
+__device__ __forceinline__ float round_act_f(float v) {
+    return DT == DT_F16 ? (float)(f16)v : (float)(__bf16)v;
+}
+
+// ---------------------------------------------------------------------------
+// Quantisation: one workgroup of 256 threads per row, two passes over the row
+// (abs-max, then codes).  The row sum of the codes' values is accumulated
+// exactly as an integer in units of 2^-9 and rounded once to fp32.
+template <int DT>
+__global__ __launch_bounds__(256) void w4a8_fp8_quant(const uint16_t *__restrict__ x, uint8_t *__restrict__ a,
+                                                      float *__restrict__ s1, float *__restrict__ asum, int K) {
+    __shared__ uint32_t wmax[4];
+    __shared__ long long wsum[4];
+    const int m = blockIdx.x;
+    const uint16_t *row = x + (size_t)m * K;
+    uint8_t *out = a + (size_t)m * K;
+    const int K8 = (K & 7) ? 0 : K;
+    uint32_t mx = 0;
+    for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
+        const u32x4 v = *(const u32x4 *)(row + k);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) mx = max(mx, max(v[p] & 0x7FFFu, (v[p] >> 16) & 0x7FFFu));
+    }
+    for (int k = K8 + threadIdx.x; k < K; k += 256) mx = max(mx, (uint32_t)row[k] & 0x7FFFu);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const float amax = act_bits_to_f32<DT>(mx);
+    const float s = round_act_f<DT>(amax / 448.0f);  // correctly rounded fp32 divide, then the activation type
+    long long sum = 0;
+    auto code_of = [&](uint32_t h) -> uint32_t {
+        if (s == 0.0f) return 0u;
+        const float q = fminf(fmaxf(act_bits_to_f32<DT>(h) / s, -448.0f), 448.0f);
+        return e4m3_code(q);
+    };
+    for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
+        const u32x4 v = *(const u32x4 *)(row + k);
+        u32x2 o = {0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t c = code_of((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            sum += e4m3_units(c);
+            o[e >> 2] |= c << (8 * (e & 3));
+        }
+        *(u32x2 *)(out + k) = o;
+    }
+    for (int k = K8 + threadIdx.x; k < K; k += 256) {
+        const uint32_t c = code_of(row[k]);
+        sum += e4m3_units(c);
+        out[k] = (uint8_t)c;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const long long tot = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        s1[m] = s;
+        asum[m] = (float)tot * 0x1p-9f;  // one rounding (int64 -> fp32), then an exact power of two
+    }
+}
+
+hipError_t launch_w4a8_fp8_quant(const void *x, uint8_t *a, float *s1, float *asum, int64_t M, int64_t K, int dt,
+                                 hipStream_t st) {
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL(w4a8_fp8_quant<DT_BF16>, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a, s1,
+                           asum, (int)K);
+    else
+        hipLaunchKernelGGL(w4a8_fp8_quant<DT_F16>, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a, s1,
+                           asum, (int)K);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Operands.  B: 32 consecutive k of one column from four consecutive K8 words
+// (nibble 2b of a word holds k = b and nibble 2b+1 holds k = 4 + b, so after
+// the offset the low nibbles of the four bytes are k 0..3 and the high ones
+// k 4..7).
+__device__ __forceinline__ i32x8 fp8_b_operand(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    const uint32_t u0 = w0 ^ 0x88888888u, u1 = w1 ^ 0x88888888u, u2 = w2 ^ 0x88888888u, u3 = w3 ^ 0x88888888u;
+    i32x8 b;
+    b[0] = (int32_t)(u0 & 0x0F0F0F0Fu);
+    b[1] = (int32_t)((u0 >> 4) & 0x0F0F0F0Fu);
+    b[2] = (int32_t)(u1 & 0x0F0F0F0Fu);
+    b[3] = (int32_t)((u1 >> 4) & 0x0F0F0F0Fu);
+    b[4] = (int32_t)(u2 & 0x0F0F0F0Fu);
+    b[5] = (int32_t)((u2 >> 4) & 0x0F0F0F0Fu);
+    b[6] = (int32_t)(u3 & 0x0F0F0F0Fu);
+    b[7] = (int32_t)((u3 >> 4) & 0x0F0F0F0Fu);
+    return b;
+}
+
+__device__ __forceinline__ i32x8 load_a32(const uint8_t *p) {
+    const u32x4 lo = *(const u32x4 *)p, hi = *(const u32x4 *)(p + 16);
+    return (i32x8){(int32_t)lo[0], (int32_t)lo[1], (int32_t)lo[2], (int32_t)lo[3],
+                   (int32_t)hi[0], (int32_t)hi[1], (int32_t)hi[2], (int32_t)hi[3]};
+}
+
+__device__ __forceinline__ f32x4 mfma_fp8(i32x8 a, i32x8 b, f32x4 c) {
+    // A and B in E4M3 (format 0), unit E8M0 scales (127)
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Final value of one output from its sum t = sum_k a u 2^-9.
+template <int DT>
+__device__ __forceinline__ void fp8_store(float t, int m, int n, int N, const float *__restrict__ s1,
+                                          const float *__restrict__ asum, const uint16_t *__restrict__ s2,
+                                          uint16_t *__restrict__ y, float *__restrict__ acc_out) {
+    const float d = __builtin_fmaf(512.0f, t, -8.0f * asum[m]);  // sum a q, one rounding
+    y[(size_t)m * N + n] = f32_to_out_bits(d * s1[m] * act_bits_to_f32<DT>(s2[n]), DT);
+    if (acc_out) acc_out[(size_t)m * N + n] = d;
+}
+
+// Fixed-point resolution of the split-K sum of t: 2^-20 (range 2^27 > 13.2 K).
+constexpr double kFp8Fixed = 1048576.0;
+
+// ---------------------------------------------------------------------------
+// Skinny kernel: M <= 16*MT; 4 waves split the K slice of a 64*BLK column tile
+// (128-k steps); LDS reduce in wave order; split-K over grid y through the
+// counting fixed-point accumulators (device.hpp).
+template <int BLK, int MT, int DT>
+__global__ __launch_bounds__(256) void w4a8_fp8_skinny(const uint8_t *__restrict__ a, const uint32_t *__restrict__ bq,
+                                                       const float *__restrict__ s1, const float *__restrict__ asum,
+                                                       const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
+                                                       float *__restrict__ acc_out, uint64_t *__restrict__ acc64,
+                                                       int M, int N, int K, int S) {
+    extern __shared__ float fred[];
+    constexpr int COLS = 64 * BLK;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, gq = lane >> 4;
+    const int tile = blockIdx.x, split = blockIdx.y;
+    const int T = K >> 7;  // 128-k steps
+    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
+    const int w_lo = s_lo + (s_hi - s_lo) * wave / 4, w_hi = s_lo + (s_hi - s_lo) * (wave + 1) / 4;
+    int ncol[BLK];
+    bool ok[BLK];
+#pragma unroll
+    for (int b = 0; b < BLK; ++b) {
+        ncol[b] = tile * COLS + 64 * b + 4 * j;
+        ok[b] = ncol[b] < N;
+    }
+    f32x4 acc[MT][BLK][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int b = 0; b < BLK; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][b][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    for (int st = w_lo; st < w_hi; ++st) {
+        const int k0 = st * 128 + 32 * gq;  // this lane group's 32 k
+        const int kb = k0 >> 3;
+        u32x4 w[BLK][4];
+#pragma unroll
+        for (int b = 0; b < BLK; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[b][e] = ok[b] ? __builtin_nontemporal_load((const u32x4 *)(bq + (size_t)(kb + e) * N + ncol[b]))
+                                : (u32x4){0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+        i32x8 av[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int m = 16 * mt + j;
+            av[mt] = m < M ? load_a32(a + (size_t)m * K + k0) : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int b = 0; b < BLK; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const i32x8 bop = fp8_b_operand(w[b][0][i], w[b][1][i], w[b][2][i], w[b][3][i]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt][b][i] = mfma_fp8(av[mt], bop, acc[mt][b][i]);
+            }
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * mt + 4 * gq + r;
+            if (m < M) {
+#pragma unroll
+                for (int b = 0; b < BLK; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) fred[((size_t)wave * M + m) * COLS + 64 * b + 4 * j + i] = acc[mt][b][i][r];
+            }
+        }
+    __syncthreads();
+    const int total = M * COLS;
+    const int n_base = tile * COLS;
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int m = idx / COLS, c = idx - m * COLS;
+        const int n = n_base + c;
+        if (n >= N) continue;
+        const float v = ((fred[(size_t)(0 * M + m) * COLS + c] + fred[(size_t)(1 * M + m) * COLS + c]) +
+                         fred[(size_t)(2 * M + m) * COLS + c]) + fred[(size_t)(3 * M + m) * COLS + c];
+        if (S == 1) {
+            fp8_store<DT>(v, m, n, N, s1, asum, s2, y, acc_out);
+        } else {
+            const double lim = (double)(kBias - 1);
+            const int64_t fx = (int64_t)__builtin_rint(fmin(fmax((double)v * kFp8Fixed, -lim), lim));
+            int64_t sum;
+            if (splitk_contribute(&acc64[(size_t)m * N + n], fx, S, &sum))
+                fp8_store<DT>((float)((double)sum * (1.0 / kFp8Fixed)), m, n, N, s1, asum, s2, y, acc_out);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel: 2 x 2 waves, wave tile (16*MTW) x 64, workgroup tile
+// (32*MTW) x 128; 128-k steps; split-K over grid z through per-tile fp32
+// partials summed in split order (device.hpp).
+template <int MTW, int DT>
+__global__ __launch_bounds__(256) void w4a8_fp8_tiled(const uint8_t *__restrict__ a, const uint32_t *__restrict__ bq,
+                                                      const float *__restrict__ s1, const float *__restrict__ asum,
+                                                      const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
+                                                      float *__restrict__ acc_out, uint64_t *__restrict__ ws, int M,
+                                                      int N, int K, int S) {
+    constexpr int BM = 32 * MTW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = lane & 15, gq = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
+    const int ncol = tn * 128 + wn * 64 + 4 * j;
+    const bool ok = ncol < N;
+    const int m0 = tm * BM + wm * 16 * MTW;
+    const int T = K >> 7;
+    const int s_lo = (int)((int64_t)T * split / S), s_hi = (int)((int64_t)T * (split + 1) / S);
+    f32x4 acc[MTW][4];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    bool row_ok[MTW];
+    const uint8_t *arow[MTW];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+        const int m = m0 + 16 * mt + j;
+        row_ok[mt] = m < M;
+        arow[mt] = a + (size_t)(row_ok[mt] ? m : 0) * K + 32 * gq;
+    }
+    for (int st = s_lo; st < s_hi; ++st) {
+        const int kb = (st * 128 + 32 * gq) >> 3;
+        u32x4 w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = ok ? *(const u32x4 *)(bq + (size_t)(kb + e) * N + ncol)
+                      : (u32x4){0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+        i32x8 av[MTW];
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+            av[mt] = row_ok[mt] ? load_a32(arow[mt] + st * 128) : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const i32x8 bop = fp8_b_operand(w[0][i], w[1][i], w[2][i], w[3][i]);
+#pragma unroll
+            for (int mt = 0; mt < MTW; ++mt) acc[mt][i] = mfma_fp8(av[mt], bop, acc[mt][i]);
+        }
+    }
+    if (S == 1) {
+        if (!ok) return;
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) fp8_store<DT>(acc[mt][i][r], m, ncol + i, N, s1, asum, s2, y, acc_out);
+                }
+            }
+        return;
+    }
+    uint32_t *const cnt = (uint32_t *)ws + (tn + gridDim.x * tm);
+    float *const part = (float *)((char *)ws + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N;
+    if (ok) {
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M)
+                    *(f32x4 *)(part + split * slot + (size_t)m * N + ncol) =
+                        (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+            }
+    }
+    if (!split_tile_last(cnt, S) || !ok) return;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+        f32x4 v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < S; ++sp) {
+            const float *base = part + sp * slot + ncol;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M) v[r] += *(const f32x4 *)(base + (size_t)m * N);
+            }
+        }
+        for (int sp = 0; sp < S; ++sp) {
+            float *base = part + sp * slot + ncol;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 16 * mt + 4 * gq + r;
+                if (m < M) *(f32x4 *)(base + (size_t)m * N) = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 16 * mt + 4 * gq + r;
+            if (m < M) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) fp8_store<DT>(v[r][i], m, ncol + i, N, s1, asum, s2, y, acc_out);
+            }
+        }
+    }
+}
+
+template <int BLK, int MT, int DT>
+static hipError_t launch_fp8_skinny(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st) {
+    const size_t lds = (size_t)4 * g.M * 64 * BLK * sizeof(float);
+    hipLaunchKernelGGL((w4a8_fp8_skinny<BLK, MT, DT>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, g.a,
+                       (const uint32_t *)g.b, g.s1, g.asum, (const uint16_t *)g.s2, (uint16_t *)g.y, g.acc_out, p.acc,
+                       (int)g.M, (int)g.N, (int)g.K, p.splits);
+    return hipGetLastError();
+}
+
+template <int MTW, int DT>
+static hipError_t launch_fp8_tiled(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st) {
+    hipLaunchKernelGGL((w4a8_fp8_tiled<MTW, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(256), 0, st, g.a,
+                       (const uint32_t *)g.b, g.s1, g.asum, (const uint16_t *)g.s2, (uint16_t *)g.y, g.acc_out, p.acc,
+                       (int)g.M, (int)g.N, (int)g.K, p.splits);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_fp8_dt(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st) {
+    if (p.kind == 0) {
+        switch (p.blk * 10 + p.mt) {
+            case 11: return launch_fp8_skinny<1, 1, DT>(g, p, st);
+            case 21: return launch_fp8_skinny<2, 1, DT>(g, p, st);
+            case 12: return launch_fp8_skinny<1, 2, DT>(g, p, st);
+            case 14: return launch_fp8_skinny<1, 4, DT>(g, p, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
+    switch (p.mt) {
+        case 2: return launch_fp8_tiled<2, DT>(g, p, st);
+        case 4: return launch_fp8_tiled<4, DT>(g, p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_w4a8_fp8(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st) {
+    return g.dtype == DT_BF16 ? launch_fp8_dt<DT_BF16>(g, p, st) : launch_fp8_dt<DT_F16>(g, p, st);
+}
+
+}  // namespace awq4

@@ -227,6 +227,41 @@ def linear_w4a8(x, b, s2, s3=None, group_size: int = -1, want_acc: bool = False,
     return (out, s1, acc) if want_acc else out
 
 
+# ----------------------------------------------------------------------------- INT4-FP8 W4A8
+
+def quant_act_fp8(x: torch.Tensor, a=None, s1=None, asum=None):
+    """Per-token E4M3 quantisation -> (codes uint8 [M,K], s1 fp32 [M], asum fp32 [M])."""
+    _need_cuda(x, a, s1, asum)
+    if x.dtype not in _F16:
+        raise ValueError("activations must be fp16 or bf16")
+    M, K = x.shape
+    a = torch.empty(M, K, dtype=torch.uint8, device=x.device) if a is None else a
+    s1 = torch.empty(M, dtype=torch.float32, device=x.device) if s1 is None else s1
+    asum = torch.empty(M, dtype=torch.float32, device=x.device) if asum is None else asum
+    L.check("w4a8_fp8_quant_act", L.lib().w4a8_fp8_quant_act(_ptr(x), _ptr(a), _ptr(s1), _ptr(asum), M, K,
+                                                             _F16[x.dtype], _stream(x.device)))
+    return a, s1, asum
+
+
+def w4a8_fp8_gemm(a, b, s1, asum, s2, want_acc: bool = False, out=None):
+    """y = act(acc * s1 * s2), acc = sum_k e4m3(a) q (fp32 on the fp8 matrix
+    cores), in the dtype of s2.  Returns y or (y, acc)."""
+    _need_cuda(a, b, s1, asum, s2, out)
+    if s2.dtype not in _F16:
+        raise ValueError("s2 must be fp16 or bf16")
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty(M, N, dtype=s2.dtype, device=a.device)
+    acc = torch.empty(M, N, dtype=torch.float32, device=a.device) if want_acc else None
+    need = workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, M, N, K, -1, 0, a.device)
+    ws = WORKSPACE.get(a.device, need)
+    L.check("w4a8_fp8_gemm", L.lib().w4a8_fp8_gemm(_ptr(a), _ptr(b), _ptr(s1), _ptr(asum), _ptr(s2), _ptr(out),
+                                                   _ptr(acc), M, N, K, _F16[s2.dtype], _ptr(ws),
+                                                   0 if ws is None else ws.numel(), _stream(a.device)))
+    return (out, acc) if want_acc else out
+
+
 # ----------------------------------------------------------------------------- measurement helper
 
 STREAM_SINK_WORDS = 8192

@@ -72,6 +72,7 @@ extern "C" {
 #define AWQ_OP_GEMM_W4A16 0
 #define AWQ_OP_GEMV_W4A16 1
 #define AWQ_OP_W4A8_GEMM 2
+#define AWQ_OP_W4A8_FP8_GEMM 3
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *awq_status_str(int status);
@@ -290,6 +291,43 @@ int w4a8_linear(const void *x, int8_t *a8, float *s1, const int32_t *b_packed,
                 const void *s2, const void *s3, void *y, int32_t *acc_out,
                 int64_t M, int64_t N, int64_t K, int group_size, int dtype, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/*
+ * INT4-FP8 W4A8.  [P5] names "INT4-FP8 QQQ (W4A8)" as its authors' next step
+ * and gives nothing more; this library takes the int8 recipe above with OCP
+ * FP8 E4M3 activation codes (sign, 4 exponent bits biased by 7, 3 mantissa
+ * bits; largest finite value 448; 0x7f and 0xff are NaN and never produced)
+ * and 448 in place of the int8 codes and 127, per-channel scales only.
+ *
+ * w4a8_fp8_quant_act -- per-token E4M3 quantisation:
+ *   s1[m]   = float( act( max_k |x[m,k]| / 448 ) )   (correctly rounded fp32
+ *             divide, then rounded to the activation type)
+ *   a[m,k]  = e4m3( clamp( float(x[m,k]) / s1[m], -448, 448 ) )  (fp32
+ *             divide, round to nearest even); a row whose s1 is 0 gives codes 0
+ *   asum[m] = float( sum_k value(a[m,k]) )  (the exact sum, rounded once; the
+ *             GEMM needs it)
+ *   x: device fp16/bf16 [M, K] (dtype); a: device uint8 [M, K];
+ *   s1, asum: device fp32 [M].
+ * Errors: AWQ_EINVAL, AWQ_EALIGN, AWQ_EHIP.
+ */
+int w4a8_fp8_quant_act(const void *x, uint8_t *a, float *s1, float *asum, int64_t M, int64_t K, int dtype,
+                       void *stream);
+
+/*
+ * w4a8_fp8_gemm -- y[m,n] = act( acc[m,n] * s1[m] * s2[n] ) with
+ * acc[m,n] = sum_k value(a[m,k]) * q[k,n], accumulated in fp32 on the fp8
+ * matrix cores (not exact: compare within a tolerance).
+ *   a, s1, asum: from w4a8_fp8_quant_act; b_packed: int32 [K/8, N],
+ *   W4A8_LAYOUT_K8 (q in -8..7); s2: device [N] and y: device [M, N] in the
+ *   activation type `dtype`; acc_out: device fp32 [M, N] or NULL (the fp32
+ *   sums, for checking).
+ *   K % 128 == 0 and K <= 131008; N % 8 == 0.  Workspace as for w4a8_gemm
+ *   (op AWQ_OP_W4A8_FP8_GEMM in awq_workspace_bytes).
+ * Errors: AWQ_EINVAL, AWQ_EALIGN, AWQ_EWORKSPACE, AWQ_EUNSUPPORTED (K), AWQ_EHIP.
+ */
+int w4a8_fp8_gemm(const uint8_t *a, const int32_t *b_packed, const float *s1, const float *asum,
+                  const void *s2, void *y, float *acc_out, int64_t M, int64_t N, int64_t K, int dtype,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * awq_stream_read -- measurement helper, not a step of the method: reads

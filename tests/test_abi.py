@@ -261,3 +261,25 @@ def test_dequant_validation():
     assert lib.awq_dequant_w4a16(A, A, A, A, 4096, 4000, 128, 0, None) == L.AWQ_EINVAL      # K % G
     assert lib.awq_dequant_w4a16(A, A, A, A, 4096, 4096, 128, 5, None) == L.AWQ_EINVAL      # dtype
     assert lib.awq_dequant_w4a16(A, A, A, MIS, 4096, 4096, 128, 0, None) == L.AWQ_EALIGN
+
+
+def test_fp8_validation():
+    lib = L.lib()
+
+    def g(a=A, b=A, s1=A, asum=A, s2=A, y=A, acc=None, M=1, N=8192, K=21760, dt=0, ws=None, wsb=0):
+        return lib.w4a8_fp8_gemm(a, b, s1, asum, s2, y, acc, M, N, K, dt, ws, wsb, None)
+
+    assert g(a=None) == L.AWQ_EINVAL
+    assert g(asum=None) == L.AWQ_EINVAL
+    assert g(N=12) == L.AWQ_EINVAL
+    assert g(K=21760 + 64) == L.AWQ_EUNSUPPORTED   # K % 128
+    assert g(K=131072) == L.AWQ_EUNSUPPORTED
+    assert g(dt=2) == L.AWQ_EINVAL
+    assert g(acc=MIS) == L.AWQ_EALIGN
+    assert g() == L.AWQ_EWORKSPACE                  # split-K needs its workspace
+    assert lib.awq_workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, 1, 8192, 21760, -1, 0) == 8192 * 8
+    assert lib.awq_workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, 1, 8192, 21824, -1, 0) == 0
+    assert lib.w4a8_fp8_quant_act(None, A, A, A, 1, 16, 0, None) == L.AWQ_EINVAL
+    assert lib.w4a8_fp8_quant_act(A, A, A, None, 1, 16, 0, None) == L.AWQ_EINVAL
+    assert lib.w4a8_fp8_quant_act(A, A, A, A, 1, 16, 3, None) == L.AWQ_EINVAL
+    assert lib.w4a8_fp8_quant_act(A, A, MIS, A, 1, 16, 0, None) == L.AWQ_EALIGN
