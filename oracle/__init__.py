@@ -99,6 +99,9 @@ class Oracle:
         L.orc_dequant.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp]
         L.orc_quant_act.argtypes = [vp, i64, i64, i32, vp, vp]
         L.orc_w4a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, i32]
+        L.orc_unpack_v2.argtypes = [vp, vp, i64, i64]
+        L.orc_pack_v2.argtypes = [vp, vp, i64, i64, vp]
+        L.orc_w4a16_v2.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_to_f64.restype = ctypes.c_double
         L.orc_f64_to_e4m3.argtypes = [ctypes.c_double]
@@ -106,7 +109,8 @@ class Oracle:
         L.orc_quant_act_fp8.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         L.orc_w4a8_fp8.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp]
         for f in ("orc_unpack_n8", "orc_pack_n8", "orc_unpack_k8", "orc_pack_k8", "orc_w4a16",
-                  "orc_dequant", "orc_quant_act", "orc_w4a8", "orc_quant_act_fp8", "orc_w4a8_fp8"):
+                  "orc_dequant", "orc_quant_act", "orc_w4a8", "orc_quant_act_fp8", "orc_w4a8_fp8",
+                  "orc_unpack_v2", "orc_pack_v2", "orc_w4a16_v2"):
             getattr(L, f).restype = ctypes.c_int
 
     # -- scalar formats ------------------------------------------------------
@@ -218,6 +222,43 @@ class Oracle:
             raise ValueError("w4a8: bad shape or non-integer group scale")
         return acc, y
 
+
+    # -- second AWQ packing -------------------------------------------------------
+    def unpack_v2(self, packed, cols: int) -> np.ndarray:
+        """Identity-order words [rows, ceil(cols/8)] -> values [rows, cols]."""
+        p = _i32(packed)
+        rows = p.shape[0]
+        assert p.shape[1] == (cols + 7) // 8
+        out = np.empty((rows, cols), np.uint8)
+        assert self.lib.orc_unpack_v2(_p(p), _p(out), rows, cols) == 0
+        return out
+
+    def pack_v2(self, vals):
+        v = np.ascontiguousarray(vals, dtype=np.uint8)
+        rows, cols = v.shape
+        out = np.empty((rows, (cols + 7) // 8), np.int32)
+        n_bad = ctypes.c_int64(0)
+        assert self.lib.orc_pack_v2(_p(v), _p(out), rows, cols, ctypes.byref(n_bad)) == 0
+        return out, int(n_bad.value)
+
+    def w4a16_v2(self, x, qweight, scales, qzeros, group_size: int, dtype: int = F16) -> np.ndarray:
+        """Y64 from weights in the second AWQ packing (qweight [K, N/8] identity
+        order, scales [K/G, N], qzeros [N, ceil(K/G/8)] or None)."""
+        xb = _u16(x)
+        qw = _i32(qweight)
+        K, wc = qw.shape
+        N = wc * 8
+        M = xb.shape[0]
+        s = _u16(scales)
+        assert s.shape == (K // group_size, N)
+        qz = _i32(qzeros) if qzeros is not None else None
+        if qz is not None:
+            assert qz.shape == (N, (K // group_size + 7) // 8)
+        y = np.empty((M, N), np.float64)
+        rc = self.lib.orc_w4a16_v2(_p(xb), _p(qw), _p(s), _p(qz), M, N, K, group_size, dtype, _p(y))
+        if rc:
+            raise ValueError("w4a16_v2: bad shape")
+        return y
 
     # -- INT4-FP8 W4A8 -----------------------------------------------------------
     def e4m3_to_f64(self, code: int) -> float:

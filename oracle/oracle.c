@@ -39,6 +39,9 @@
  *    int8 and the whole-K accumulation stays an exact int32; per-channel is the
  *    case with no s3 (w8 = q).
  *  - A row whose fp16 scale s1 rounds to zero quantises to all zeros.
+ *  - Second AWQ packing (named by its differences only): identity order map,
+ *    qweight [K, N/8] and scales [K/G, N] as before, qzeros [N, ceil(K/G/8)]
+ *    packed along the groups with the nibbles past the last group skipped.
  *  - INT4-FP8 (the QQQ authors' announced follow-up, named only): the int8
  *    recipe with OCP FP8 E4M3 codes and 448 in place of int8 codes and 127,
  *    round to nearest even with saturation at +-448, per-channel scales.
@@ -369,6 +372,74 @@ int orc_quant_act(const uint16_t *x, int64_t M, int64_t K, int dtype, int8_t *a8
             a8[m * K + k] = (int8_t)r;
         }
     }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Second AWQ packing ([P1]: the reviewer's list of differences of the   */
+/* newer llm-awq format: order map [0,1,...,7] instead of                 */
+/* [0,2,4,6,1,3,5,7]; some zeros skipped during packing; a zeros width    */
+/* from calculate_zeros_width giving other shapes).  Reading, changing    */
+/* only what the list names: qweight [K, N/8] with nibble i of word j     */
+/* holding column 8j + i; scales [K/G, N] as before; qzeros [N, ZW] with  */
+/* ZW = ceil((K/G) / 8) words per output channel, nibble i of word j      */
+/* holding the zero point of group 8j + i, the nibbles past the last      */
+/* group skipped (left 0).                                                */
+
+/* words [rows, ceil(cols/8)] -> values [rows, cols] (identity order; nibbles
+ * past the last column ignored) */
+int orc_unpack_v2(const int32_t *packed, uint8_t *vals, int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0) return ORC_EINVAL;
+    int64_t wc = (cols + 7) / 8;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            vals[r * cols + c] = (uint8_t)(((uint32_t)packed[r * wc + c / 8] >> (4 * (c % 8))) & 0xF);
+    return ORC_OK;
+}
+
+/* values [rows, cols] -> words [rows, ceil(cols/8)]; nibbles past the last
+ * column stay 0 (skipped); values above 15 are clamped and counted */
+int orc_pack_v2(const uint8_t *vals, int32_t *packed, int64_t rows, int64_t cols, int64_t *n_clamped) {
+    if (rows < 0 || cols < 0) return ORC_EINVAL;
+    int64_t wc = (cols + 7) / 8, bad = 0;
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t j = 0; j < wc; j++) {
+            uint32_t word = 0;
+            for (int i = 0; i < 8; i++) {
+                int64_t c = 8 * j + i;
+                if (c >= cols) continue; /* skipped */
+                unsigned v = vals[r * cols + c];
+                if (v > 15) { v = 15; bad++; }
+                word |= (uint32_t)v << (4 * i);
+            }
+            packed[r * wc + j] = (int32_t)word;
+        }
+    if (n_clamped) *n_clamped = bad;
+    return ORC_OK;
+}
+
+/* Y64 = X . W with W[k,n] = (q[k,n] - z[n,k/G]) * s[k/G,n] read straight from
+ * the second packing (qzeros NULL: z = 8), in double, summed in k order. */
+int orc_w4a16_v2(const uint16_t *x, const int32_t *qweight, const uint16_t *scales, const int32_t *qzeros,
+                 int64_t M, int64_t N, int64_t K, int G, int dtype, double *y) {
+    if (check_w4a16_shape(M, N, K, G)) return ORC_EINVAL;
+    int64_t wc = N / 8, groups = K / G, zw = (groups + 7) / 8;
+    double *w = (double *)malloc(sizeof(double) * (size_t)K);
+    if (!w) return ORC_EINVAL;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            int64_t g = k / G;
+            int q = (int)(((uint32_t)qweight[k * wc + n / 8] >> (4 * (n % 8))) & 0xF);
+            int z = qzeros ? (int)(((uint32_t)qzeros[n * zw + g / 8] >> (4 * (g % 8))) & 0xF) : 8;
+            w[k] = (double)(q - z) * decode_act(scales[g * N + n], dtype);
+        }
+        for (int64_t m = 0; m < M; m++) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; k++) acc += decode_act(x[m * K + k], dtype) * w[k];
+            y[m * N + n] = acc;
+        }
+    }
+    free(w);
     return ORC_OK;
 }
 

@@ -41,7 +41,8 @@ def _golden_words():
             if not line or line.startswith("#"):
                 continue
             kind, vals, word = line.split()
-            rows.append((kind, [int(v) for v in vals.split(",")], int(word, 16)))
+            words = [int(w, 16) for w in word.split(",")]
+            rows.append((kind, [int(v) for v in vals.split(",")], words if kind == "v2" else words[0]))
     return rows
 
 
@@ -71,7 +72,13 @@ def _f16_bits(vals):
 
 def pin_golden_words(orc):
     for kind, vals, word in _golden_words():
-        if kind == "n8":
+        if kind == "v2":
+            packed, bad = orc.pack_v2(np.array([vals], np.uint8))
+            assert bad == 0
+            assert _u32(packed)[0].tolist() == word, (vals, [hex(int(w)) for w in _u32(packed)[0]])
+            back = orc.unpack_v2(np.array([word], np.uint32).view(np.int32), len(vals))
+            assert back[0].tolist() == vals
+        elif kind == "n8":
             packed, bad = orc.pack_n8(np.array([vals], np.uint8))
             assert bad == 0
             assert int(_u32(packed)[0, 0]) == word, (vals, hex(int(_u32(packed)[0, 0])), hex(word))
@@ -547,6 +554,72 @@ def pin_w4a8_group16_is_channel(orc):
     assert 128 * 128 * 21760 < 2 ** 31
 
 
+# ----------------------------------------------------------------------------- second AWQ packing
+
+def pin_v2_roundtrip(orc):
+    """Identity-order packing round-trips, ragged rows included, and leaves the
+    nibbles past the last value zero (skipped)."""
+    rng = np.random.default_rng(41)
+    for cols in (8, 3, 11, 32, 43):
+        v = rng.integers(0, 16, size=(5, cols), dtype=np.uint8)
+        p, bad = orc.pack_v2(v)
+        assert bad == 0 and np.array_equal(orc.unpack_v2(p, cols), v)
+        used = cols % 8
+        if used:
+            assert np.all((_u32(p[:, -1]) >> (4 * used)) == 0)
+        # element c sits in word c // 8 at nibble c % 8
+        c = cols - 1
+        assert np.array_equal((_u32(p[:, c // 8]) >> (4 * (c % 8))) & 0xF, v[:, c].astype(np.int64))
+
+
+def _brute_w4a16_v2(x, qweight, scales_f, qzeros, G):
+    M, K = x.shape
+    N = qweight.shape[1] * 8
+    y = np.empty((M, N))
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                g = k // G
+                qv = (int(qweight[k, n // 8]) & 0xFFFFFFFF) >> (4 * (n % 8)) & 0xF
+                zv = 8 if qzeros is None else (int(qzeros[n, g // 8]) & 0xFFFFFFFF) >> (4 * (g % 8)) & 0xF
+                acc += Fraction(float(x[m, k])) * (qv - zv) * Fraction(float(scales_f[g, n]))
+            y[m, n] = float(acc)
+    return y
+
+
+def pin_w4a16_v2_bruteforce(orc):
+    rng = np.random.default_rng(42)
+    for G, K in ((32, 96), (64, 640)):   # 3 and 10 groups: ragged zero words
+        for sym in (False, True):
+            M, N = 2, 16
+            x = rng.standard_normal((M, K)).astype(np.float16)
+            qw = rng.integers(0, 2 ** 32, size=(K, N // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+            zw = (K // G + 7) // 8
+            qz = None if sym else orc.pack_v2(rng.integers(0, 16, size=(N, K // G), dtype=np.uint8))[0]
+            s = (0.002 + 0.018 * rng.random((K // G, N))).astype(np.float16)
+            y = orc.w4a16_v2(x.view(np.uint16), qw, s.view(np.uint16), qz, G)
+            ref = _brute_w4a16_v2(x.astype(np.float64), qw, s.astype(np.float64), qz, G)
+            assert qz is None or qz.shape == (N, zw)
+            assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max()), (G, sym)
+
+
+def pin_w4a16_v2_matches_first_packing(orc):
+    """The same logical weights in either packing give the same Y, bit for
+    bit (the first packing's words built from the values by its own packer)."""
+    rng = np.random.default_rng(43)
+    M, K, N, G = 3, 384, 24, 128
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(K // G, N), dtype=np.uint8)
+    s = (0.002 + 0.018 * rng.random((K // G, N))).astype(np.float16)
+    x = rng.standard_normal((M, K)).astype(np.float16)
+    y1 = orc.w4a16(x.view(np.uint16), orc.pack_n8(q)[0], s.view(np.uint16), orc.pack_n8(z)[0], G)
+    y2 = orc.w4a16_v2(x.view(np.uint16), orc.pack_v2(q)[0], s.view(np.uint16), orc.pack_v2(z.T.copy())[0], G)
+    assert np.array_equal(y1, y2)
+    assert np.array_equal(orc.w4a16_v2(x.view(np.uint16), orc.pack_v2(q)[0], s.view(np.uint16), None, G),
+                          orc.w4a16(x.view(np.uint16), orc.pack_n8(q)[0], s.view(np.uint16), None, G))
+
+
 # ----------------------------------------------------------------------------- INT4-FP8 W4A8
 
 def _e4m3_torch(codes):
@@ -736,4 +809,5 @@ ALL_PINS = [
     pin_w4a16_bruteforce, pin_w4a16_bf16, pin_f16_codec, pin_bf16_encode, pin_quant_s1_exhaustive,
     pin_quant_bf16_s1_exhaustive, pin_e4m3_decode, pin_e4m3_encode, pin_quant_fp8_examples,
     pin_w4a8_fp8_bruteforce, pin_w4a8_fp8_integer_codes, pin_quant_fp8_random, pin_quant_fp8_s1_exhaustive,
+    pin_v2_roundtrip, pin_w4a16_v2_bruteforce, pin_w4a16_v2_matches_first_packing,
 ]

@@ -57,6 +57,11 @@ MUTANTS = {
     "fp8_gemm_s1_dropped": ("if (y) y[m * N + n] = sacc * (double)s1[m] * s2n;", "if (y) y[m * N + n] = sacc * s2n;"),
     "fp8_gemm_k8_order": ("for (int i = 0; i < 8; i++) q[8 * kb + K8_ORDER[i]] = sext4((w >> (4 * i)) & 0xF);",
                           "for (int i = 0; i < 8; i++) q[8 * kb + i] = sext4((w >> (4 * i)) & 0xF);"),
+    "v2_order_reversed": ("int q = (int)(((uint32_t)qweight[k * wc + n / 8] >> (4 * (n % 8))) & 0xF);",
+                          "int q = (int)(((uint32_t)qweight[k * wc + n / 8] >> (4 * (7 - n % 8))) & 0xF);"),
+    "v2_zero_nibble": ("(int)(((uint32_t)qzeros[n * zw + g / 8] >> (4 * (g % 8))) & 0xF)",
+                       "(int)(((uint32_t)qzeros[n * zw + g / 8] >> (4 * (g % 4))) & 0xF)"),
+    "v2_pack_order": ("word |= (uint32_t)v << (4 * i);", "word |= (uint32_t)v << (4 * (7 - i));"),
     "bf16_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
 }
 
