@@ -22,6 +22,7 @@ AWQ_DTYPE_F16 = 0
 AWQ_DTYPE_BF16 = 1
 AWQ_LAYOUT_N8 = 0
 W4A8_LAYOUT_K8 = 1
+AWQ_LAYOUT_V2 = 2
 AWQ_OP_GEMM_W4A16 = 0
 AWQ_OP_GEMV_W4A16 = 1
 AWQ_OP_W4A8_GEMM = 2
@@ -66,6 +67,7 @@ def lib() -> ctypes.CDLL:
     L.awq_gemv_w4a16.argtypes = w4a16
     L.awq_gemv_w4a16_static.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     L.awq_dequant_w4a16.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp]
+    L.awq_repack_v2.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     L.w4a8_fp8_quant_act.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     L.w4a8_fp8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
     L.w4a8_quant_act.argtypes = [vp, vp, vp, i64, i64, i32, vp]
@@ -75,7 +77,7 @@ def lib() -> ctypes.CDLL:
     L.awq_plan_info.argtypes = [i32, i64, i64, i64, i32, i32, i32, ctypes.POINTER(PlanInfo)]
     for f in ("awq_pack", "awq_unpack", "awq_gemm_w4a16", "awq_gemv_w4a16", "w4a8_quant_act", "w4a8_gemm", "w4a8_linear",
               "awq_stream_read", "awq_plan_info", "awq_gemv_w4a16_static",
-              "awq_dequant_w4a16", "w4a8_fp8_quant_act", "w4a8_fp8_gemm"):
+              "awq_dequant_w4a16", "w4a8_fp8_quant_act", "w4a8_fp8_gemm", "awq_repack_v2"):
         getattr(L, f).restype = i32
     _lib = L
     return L

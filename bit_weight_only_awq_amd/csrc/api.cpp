@@ -425,6 +425,7 @@ int awq_version(void) { return 101; }
 
 static int check_pack_shape(int64_t rows, int64_t cols, int layout) {
     if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return AWQ_EINVAL;
+    if (layout == AWQ_LAYOUT_V2) return AWQ_OK;
     if (layout == AWQ_LAYOUT_N8) return cols % 8 ? AWQ_EINVAL : AWQ_OK;
     if (layout == W4A8_LAYOUT_K8) return rows % 8 ? AWQ_EINVAL : AWQ_OK;
     return AWQ_EINVAL;
@@ -447,6 +448,18 @@ int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, in
     if (!vals || !packed) return AWQ_EINVAL;
     if (!aligned16(vals) || !aligned16(packed)) return AWQ_EALIGN;
     return hip_status(launch_unpack(packed, vals, rows, cols, layout, static_cast<hipStream_t>(stream)));
+}
+
+int awq_repack_v2(const int32_t *qweight_v2, const int32_t *qzeros_v2, int32_t *qweight, int32_t *qzeros, int64_t N,
+                  int64_t K, int group_size, void *stream) {
+    if (!qweight_v2 || !qweight || (qzeros_v2 && !qzeros)) return AWQ_EINVAL;
+    if (N < 8 || K < 1 || N > kMaxDim || K > kMaxDim || N % 8) return AWQ_EINVAL;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return AWQ_EINVAL;
+    if (K % group_size) return AWQ_EINVAL;
+    if (!aligned16(qweight_v2) || !aligned16(qweight)) return AWQ_EALIGN;
+    if (qzeros_v2 && (!aligned16(qzeros_v2) || !aligned16(qzeros))) return AWQ_EALIGN;
+    return hip_status(launch_repack_v2(qweight_v2, qzeros_v2, qweight, qzeros, N, K, group_size,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 int awq_stream_read(const void *src, int64_t bytes, uint32_t *sink, void *stream) {

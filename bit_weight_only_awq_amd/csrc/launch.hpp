@@ -131,6 +131,8 @@ hipError_t launch_w4a16_dequant(const int32_t *qweight, const void *scales, cons
                                 int64_t K, int G, int dtype, hipStream_t st);
 hipError_t launch_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int layout,
                        int32_t *clamp_count, hipStream_t st);
+hipError_t launch_repack_v2(const int32_t *qweight_v2, const int32_t *qzeros_v2, int32_t *qweight, int32_t *qzeros,
+                            int64_t N, int64_t K, int G, hipStream_t st);
 hipError_t launch_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, int layout,
                          hipStream_t st);
 

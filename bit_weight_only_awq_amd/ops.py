@@ -86,11 +86,15 @@ def plan_info(op: int, M: int, N: int, K: int, group_size: int, split_k: int = 0
 # ----------------------------------------------------------------------------- packing
 
 def pack(vals: torch.Tensor, layout: str = "n8", clamp_count: torch.Tensor | None = None) -> torch.Tensor:
-    """Pack 4-bit values: layout "n8" (AWQ, uint8 [rows, cols] -> int32 [rows, cols/8])
+    """Pack 4-bit values: layout "n8" (AWQ, uint8 [rows, cols] -> int32 [rows, cols/8]),
+    "v2" (the newer AWQ packing, identity order, int32 [rows, ceil(cols/8)])
     or "k8" (W4A8, int8 [K, N] -> int32 [K/8, N])."""
     _need_cuda(vals, clamp_count)
     rows, cols = vals.shape
-    if layout == "n8":
+    if layout == "v2":
+        out = torch.empty(rows, (cols + 7) // 8, dtype=torch.int32, device=vals.device)
+        lay = L.AWQ_LAYOUT_V2
+    elif layout == "n8":
         out = torch.empty(rows, cols // 8, dtype=torch.int32, device=vals.device)
         lay = L.AWQ_LAYOUT_N8
     else:
@@ -101,9 +105,15 @@ def pack(vals: torch.Tensor, layout: str = "n8", clamp_count: torch.Tensor | Non
     return out
 
 
-def unpack(packed: torch.Tensor, layout: str = "n8") -> torch.Tensor:
+def unpack(packed: torch.Tensor, layout: str = "n8", cols: int | None = None) -> torch.Tensor:
+    """Inverse of pack; layout "v2" takes the number of values per row (default: all 8 per word)."""
     _need_cuda(packed)
-    if layout == "n8":
+    if layout == "v2":
+        rows = packed.shape[0]
+        cols = packed.shape[1] * 8 if cols is None else cols
+        out = torch.empty(rows, cols, dtype=torch.uint8, device=packed.device)
+        lay = L.AWQ_LAYOUT_V2
+    elif layout == "n8":
         rows, cols = packed.shape[0], packed.shape[1] * 8
         out = torch.empty(rows, cols, dtype=torch.uint8, device=packed.device)
         lay = L.AWQ_LAYOUT_N8
@@ -113,6 +123,19 @@ def unpack(packed: torch.Tensor, layout: str = "n8") -> torch.Tensor:
         lay = L.W4A8_LAYOUT_K8
     L.check("awq_unpack", L.lib().awq_unpack(_ptr(packed), _ptr(out), rows, cols, lay, _stream(packed.device)))
     return out
+
+
+def repack_v2(qweight_v2: torch.Tensor, qzeros_v2: torch.Tensor | None, group_size: int = 128):
+    """Weights in the newer AWQ packing -> (qweight, qzeros) in the format the
+    GEMM / GEMV calls take (awq_repack_v2); scales are shared by both formats."""
+    _need_cuda(qweight_v2, qzeros_v2)
+    K, N = qweight_v2.shape[0], qweight_v2.shape[1] * 8
+    qweight = torch.empty_like(qweight_v2)
+    qzeros = None if qzeros_v2 is None else torch.empty(K // group_size, N // 8, dtype=torch.int32,
+                                                        device=qweight_v2.device)
+    L.check("awq_repack_v2", L.lib().awq_repack_v2(_ptr(qweight_v2), _ptr(qzeros_v2), _ptr(qweight), _ptr(qzeros),
+                                                   N, K, group_size, _stream(qweight_v2.device)))
+    return qweight, qzeros
 
 
 # ----------------------------------------------------------------------------- W4A16

@@ -68,6 +68,11 @@ extern "C" {
                             nibble i of word [kb][n] holds k = 8kb + {0,4,1,5,2,6,3,7}[i],
                             two's complement (this library's own layout) */
 
+#define AWQ_LAYOUT_V2 2   /* the newer AWQ packing ([P1], list of differences; this library's reading):
+                            uint8 vals [rows, cols] in 0..15 -> int32 [rows, ceil(cols/8)];
+                            nibble i of word [r][j] holds column 8j + i (identity order map),
+                            nibbles past the last column are left 0 (skipped); any cols */
+
 /* Operation ids for awq_workspace_bytes. */
 #define AWQ_OP_GEMM_W4A16 0
 #define AWQ_OP_GEMV_W4A16 1
@@ -92,7 +97,8 @@ int awq_version(void);
  *                which the caller zeroes beforehand.
  * rows == 0 or cols == 0 is a no-op that returns AWQ_OK.
  * Errors: AWQ_EINVAL if a pointer is NULL, rows/cols < 0, cols % 8 (N8) or
- * rows % 8 (K8) is non-zero, or the layout is unknown.
+ * rows % 8 (K8) is non-zero, or the layout is unknown.  AWQ_LAYOUT_V2 takes
+ * any cols.
  */
 int awq_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int layout,
              int32_t *clamp_count, void *stream);
@@ -103,6 +109,25 @@ int awq_pack(const void *vals, int32_t *packed, int64_t rows, int64_t cols, int 
  */
 int awq_unpack(const int32_t *packed, void *vals, int64_t rows, int64_t cols, int layout,
                void *stream);
+
+/*
+ * awq_repack_v2 -- weights in the newer AWQ packing ([P1]: identity order
+ * map, zero points packed per output channel along the groups with unused
+ * nibbles skipped, a zeros width of ceil(groups / 8) words) rewritten into
+ * the first-generation format that the GEMM and GEMV calls take, bit for bit
+ * the same logical values.  A checkpoint in the newer format is repacked
+ * once at load; the scales are the same [K/G, N] tensor in both.
+ *   qweight_v2: device int32 [K, N/8], AWQ_LAYOUT_V2 along each row.
+ *   qzeros_v2:  device int32 [N, ceil((K/G)/8)], AWQ_LAYOUT_V2 along each
+ *               output channel's groups; NULL = symmetric (then qzeros is
+ *               not written).
+ *   qweight:    device int32 [K, N/8], AWQ_LAYOUT_N8 (written).
+ *   qzeros:     device int32 [K/G, N/8], AWQ_LAYOUT_N8 (written).
+ * Errors: AWQ_EINVAL (shapes, G, NULL qzeros with non-NULL qzeros_v2),
+ * AWQ_EALIGN, AWQ_EHIP.
+ */
+int awq_repack_v2(const int32_t *qweight_v2, const int32_t *qzeros_v2, int32_t *qweight, int32_t *qzeros,
+                  int64_t N, int64_t K, int group_size, void *stream);
 
 /*
  * awq_workspace_bytes -- bytes of device workspace the given call needs

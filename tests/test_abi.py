@@ -283,3 +283,16 @@ def test_fp8_validation():
     assert lib.w4a8_fp8_quant_act(A, A, A, None, 1, 16, 0, None) == L.AWQ_EINVAL
     assert lib.w4a8_fp8_quant_act(A, A, A, A, 1, 16, 3, None) == L.AWQ_EINVAL
     assert lib.w4a8_fp8_quant_act(A, A, MIS, A, 1, 16, 0, None) == L.AWQ_EALIGN
+
+
+def test_repack_v2_validation():
+    lib = L.lib()
+    assert lib.awq_repack_v2(None, A, A, A, 4096, 4096, 128, None) == L.AWQ_EINVAL
+    assert lib.awq_repack_v2(A, A, A, None, 4096, 4096, 128, None) == L.AWQ_EINVAL  # zeros given, no output
+    assert lib.awq_repack_v2(A, None, A, None, 4092, 4096, 128, None) == L.AWQ_EINVAL  # N % 8
+    assert lib.awq_repack_v2(A, None, A, None, 4096, 4000, 128, None) == L.AWQ_EINVAL  # K % G
+    assert lib.awq_repack_v2(A, None, A, None, 4096, 4096, 48, None) == L.AWQ_EINVAL
+    assert lib.awq_repack_v2(MIS, None, A, None, 4096, 4096, 128, None) == L.AWQ_EALIGN
+    # the newer layout takes any row length
+    assert lib.awq_pack(None, None, 0, 43, L.AWQ_LAYOUT_V2, None, None) == L.AWQ_OK
+    assert lib.awq_pack(MIS, A, 4, 43, L.AWQ_LAYOUT_V2, None, None) == L.AWQ_EALIGN
