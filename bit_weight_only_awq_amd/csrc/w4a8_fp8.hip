@@ -118,8 +118,86 @@ __global__ __launch_bounds__(256) void w4a8_fp8_quant(const uint16_t *__restrict
     }
 }
 
+// Register-resident form: one workgroup of T threads per row, each thread
+// holding NV chunks of 8 values (K % 8 == 0, K <= 8 * NV * T), so the row is
+// read from memory once and a single token's row is spread over up to 1024
+// threads.
+template <int DT, int NV, int T>
+__global__ __launch_bounds__(T) void w4a8_fp8_quant_rows(const uint16_t *__restrict__ x, uint8_t *__restrict__ a,
+                                                         float *__restrict__ s1, float *__restrict__ asum, int K) {
+    __shared__ uint32_t wmax[T / 64];
+    __shared__ long long wsum[T / 64];
+    const int m = blockIdx.x;
+    const uint16_t *row = x + (size_t)m * K;
+    uint8_t *out = a + (size_t)m * K;
+    u32x4 v[NV];
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int k = 8 * (threadIdx.x + i * T);
+        v[i] = k < K ? *(const u32x4 *)(row + k) : (u32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) mx = max(mx, max(v[i][p] & 0x7FFFu, (v[i][p] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = wmax[0];
+#pragma unroll
+    for (int w = 1; w < T / 64; ++w) mx = max(mx, wmax[w]);
+    const float s = round_act_f<DT>(act_bits_to_f32<DT>(mx) / 448.0f);
+    long long sum = 0;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int k = 8 * (threadIdx.x + i * T);
+        if (k >= K) break;
+        u32x2 o = {0, 0};
+        if (s != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float q = fminf(fmaxf(act_bits_to_f32<DT>((v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) / s,
+                                            -448.0f), 448.0f);
+                const uint32_t c = e4m3_code(q);
+                sum += e4m3_units(c);
+                o[e >> 2] |= c << (8 * (e & 3));
+            }
+        }
+        *(u32x2 *)(out + k) = o;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        long long tot = 0;
+#pragma unroll
+        for (int w = 0; w < T / 64; ++w) tot += wsum[w];
+        s1[m] = s;
+        asum[m] = (float)tot * 0x1p-9f;
+    }
+}
+
+template <int NV, int T>
+static hipError_t launch_fp8_rows(const void *x, uint8_t *a, float *s1, float *asum, int64_t M, int64_t K, int dt,
+                                  hipStream_t st) {
+    if (dt == DT_BF16)
+        hipLaunchKernelGGL((w4a8_fp8_quant_rows<DT_BF16, NV, T>), dim3((unsigned)M), dim3(T), 0, st,
+                           (const uint16_t *)x, a, s1, asum, (int)K);
+    else
+        hipLaunchKernelGGL((w4a8_fp8_quant_rows<DT_F16, NV, T>), dim3((unsigned)M), dim3(T), 0, st,
+                           (const uint16_t *)x, a, s1, asum, (int)K);
+    return hipGetLastError();
+}
+
 hipError_t launch_w4a8_fp8_quant(const void *x, uint8_t *a, float *s1, float *asum, int64_t M, int64_t K, int dt,
                                  hipStream_t st) {
+    if (K % 8 == 0 && K <= 8 * 1024 * 8) {
+        if (K <= 8 * 256 * 2) return launch_fp8_rows<2, 256>(x, a, s1, asum, M, K, dt, st);
+        if (K <= 8 * 1024 * 2) return launch_fp8_rows<2, 1024>(x, a, s1, asum, M, K, dt, st);
+        if (K <= 8 * 1024 * 4) return launch_fp8_rows<4, 1024>(x, a, s1, asum, M, K, dt, st);
+        return launch_fp8_rows<8, 1024>(x, a, s1, asum, M, K, dt, st);
+    }
     if (dt == DT_BF16)
         hipLaunchKernelGGL(w4a8_fp8_quant<DT_BF16>, dim3((unsigned)M), dim3(256), 0, st, (const uint16_t *)x, a, s1,
                            asum, (int)K);

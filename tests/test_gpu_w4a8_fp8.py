@@ -50,7 +50,7 @@ def test_fp8_quant_every_value_per_binade(dt):
 
 
 @pytest.mark.parametrize("dt", [0, 1])
-@pytest.mark.parametrize("M,K", [(1, 21760), (16, 4096), (64, 21760), (3, 7), (5, 1000), (2, 131072)])
+@pytest.mark.parametrize("M,K", [(1, 21760), (16, 4096), (64, 21760), (3, 7), (5, 1000), (2, 131072), (4, 32768), (2, 65536), (3, 8200)])
 def test_fp8_quant_rows(M, K, dt):
     x = synthgen.activations(M, K, seed=M * 7 + K).float()
     x = x * torch.logspace(-4, 3, M)[:, None]
