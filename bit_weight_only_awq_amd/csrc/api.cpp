@@ -20,12 +20,9 @@ static constexpr int64_t kMaxDim = int64_t(1) << 20;
 // The planners below size grids from the device's compute-unit count (cus):
 // two workgroups of 4 waves per CU is the target fill of the tiled kernels.
 static int64_t target_workgroups(const DeviceProps &d) { return 2 * (int64_t)d.cus; }
-// The W4A16 LDS GEMM takes M above 16 (the decode kernel below).  Under 128
-// rows it runs 128-row tiles with deep copy rings and at most 4 K splits
-// (measured on the Llama-3-8B layers at M = 32..128: more splits cost more in
-// partial tiles than they gain, and 256-row tiles with deep rings, at one
-// wave per SIMD, were slower than the large-M configuration from M = 128 up).
-static constexpr int64_t kW16LdsMinM = 16, kW16DeepMaxM = 127, kW16DeepMaxSplits = 4;
+// The W4A16 LDS GEMM takes M above 16 where the decode and mid-size kernels
+// do not (the decode kernel below).
+static constexpr int64_t kW16LdsMinM = 16;
 // The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, two per CU) are used
 // whenever there are at least as many as CUs; with fewer, the 128 x 128 tiles
 // give more workgroups before a K split is needed (measured: M = 512 on
@@ -181,13 +178,44 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
         p.splits = (int)std::min<int64_t>(p.splits, kMaxSplitK);
     }
+    // 16 < M <= 64: the mid-size kernel (decode-shaped, up to four 16-row
+    // tiles, every weight load of the layer in flight at once; 8 waves of
+    // 32*cs k per workgroup, so the K splits are K / (256 cs)) while its grid
+    // runs in at most two rounds at up to 32 rows (two workgroups per CU) or
+    // one round above (one per CU); on wider or deeper layers the X rows
+    // re-read by every 128-column tile and the partial tiles cost more than
+    // the LDS GEMM saves.  Measured on the Llama-3-8B layers against the LDS
+    // GEMM (two wave groups splitting K): M = 32 qkv 19.4 us, o 17.0, down
+    // 45.1 (about 33, 30 and 55 in the LDS GEMM); M = 64 o 26.4 (30); gate/up
+    // at M = 32 (3.5 rounds) 49.0 against 44.5.
+    if (M > 16 && M <= 64 && split_k == 0) {
+        const int cs = G >= 64 ? 2 : 1;
+        const int64_t splits = cdiv(K / (32 * cs), 8);
+        const int64_t wgs = cdiv(N, 128) * splits;
+        if (splits <= kMaxSplitK && (M <= 32 ? wgs <= 4 * cus : wgs <= cus)) {
+            p.kind = 4;
+            p.blk = 1;
+            p.cs = cs;
+            p.waves = 8;
+            p.mt = M <= 32 ? 2 : 4;
+            p.ksplit = 1;
+            p.tiles_n = (int)cdiv(N, 128);
+            p.tiles_m = 1;
+            p.splits = (int)splits;
+            p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(p.tiles_n, p.splits, M, N) : 0;
+            return p;
+        }
+    }
     // buffer-descriptor copies address X and the packed words with 32-bit offsets
     const bool fits_rsrc = M * K * 2 < (int64_t(1) << 31) && K * (N / 2) < (int64_t(1) << 31);
     if (M > kW16LdsMinM && K % 64 == 0 && N % 32 == 0 && fits_rsrc) {
         // LDS-pipelined GEMM: 256- or 128-row x 128 workgroup tiles, K in
         // stages of 64
         p.kind = 3;
-        p.deep = M <= kW16DeepMaxM;
+        // (below 128 rows: the 128-row tiles with two wave groups splitting
+        // K; copy rings 8 word slots deep at one workgroup per CU measured
+        // slower on every Llama-3-8B layer -- M = 64: gate/up 69.3 vs
+        // 45.6 us, down 83.7 vs 61.8; M = 96: qkv 55.3 vs 36.6, o 40.5 vs 30.5)
         // 128-row tiles at M <= 128 (256-row ones would be half padding) and
         // where there would be at most 128 tiles of 256 rows (half the CUs
         // idle).  Measured on the Llama-3-8B layers at M = 128..2048: o at
@@ -200,11 +228,7 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         const int64_t stages = K / 64;
         int64_t s;
-        if (p.deep) {
-            // one workgroup per CU: K splits up to one workgroup per CU
-            s = std::min<int64_t>(std::max<int64_t>(1, cus / tiles), kW16DeepMaxSplits);
-            s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 8));
-        } else if (M <= 128) {
+        if (M <= 128) {
             // few rows: the partial tiles are small, split by the tile count
             s = tiles <= 32 ? 4 : tiles <= 64 ? 2 : 1;
             s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 4));
@@ -221,7 +245,7 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
         // no more workgroups than CUs: two wave groups per workgroup split K
         // inside it (twice the waves per SIMD, no extra atomics)
-        p.ksplit = !p.deep && tiles * p.splits <= cus && stages / p.splits >= 4 ? 2 : 1;
+        p.ksplit = tiles * p.splits <= cus && stages / p.splits >= 4 ? 2 : 1;
     }
     if (p.splits <= 1) {
         p.workspace_bytes = 0;
@@ -398,6 +422,7 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     switch (p.kind) {
         case 0: e = launch_w4a16_decode(a, p, st); break;
         case 3: e = launch_w4a16_gemm(a, p, st); break;
+        case 4: e = launch_w4a16_midm(a, p, st); break;
         default: e = launch_w4a16_tiled(a, p, st); break;
     }
     return hip_status(e);

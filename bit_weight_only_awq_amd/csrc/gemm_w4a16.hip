@@ -17,9 +17,9 @@
 // scales and zero points) are copied straight from global memory into LDS by
 // direct-to-LDS buffer loads, with no register staging, into rings of AB X
 // buffers (copied AB - 1 stages ahead) and BB word buffers (BB - 1 ahead).
-// M >= 128 uses AB = 2, BB = 3 (two workgroups per CU); M < 128, whose
-// stages are short and whose words stream from HBM, uses AB = 3, BB = 8 so
-// that more bytes are in flight against the memory latency.  Every stage
+// The launches use AB = 2, BB = 3 (two workgroups per CU; deeper word
+// rings at one workgroup per CU measured slower, also below 128 rows, where
+// the mid-size kernel or the two-group K split serves better).  Every stage
 // issues the same copies (near the end the last stage is copied again into
 // a buffer that is no longer read), so the wait that ends a stage has a fixed
 // count: it waits only for what the next stage reads.  Each wave
@@ -461,12 +461,11 @@ static hipError_t launch_gemm_ks(const W4A16Args &a, const W4A16Plan &p, hipStre
                : launch_gemm_t<DT_BF16, false, KS, MT, AB, BB>(a, p, st);
 }
 
-// p.deep: 128-row tiles with rings of 3 X and 8 word buffers (M < 128);
-// else 256-row (p.mt = 16) or 128-row (p.mt = 8) tiles with rings of 2 and 3
+// 256-row (p.mt = 16) or 128-row (p.mt = 8) tiles with rings of 2 X and 3
+// word buffers
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     // a K split reduces through the workspace
     if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
-    if (p.deep) return launch_gemm_ks<1, 8, 3, 8>(a, p, st);
     if (p.mt == 8) return p.ksplit == 2 ? launch_gemm_ks<2, 8, 2, 3>(a, p, st) : launch_gemm_ks<1, 8, 2, 3>(a, p, st);
     return p.ksplit == 2 ? launch_gemm_ks<2, 16, 2, 3>(a, p, st) : launch_gemm_ks<1, 16, 2, 3>(a, p, st);
 }

@@ -123,8 +123,8 @@ MAIN_TILE_CASES = [
     (2048, 4096, 4096, 3, (16, 1, 3)),   # three splits, 64 stages (uneven)
     (1024, 4096, 4096, 0, (8, 2, 1)),    # 128-row tiles where 256-row ones would leave CUs idle
     (512, 14336, 4096, 0, (8, 2, 2)),    # K = 14336: K split and in-workgroup split together
-    (64, 4096, 4096, 0, (8, 1, 4)),      # deep copy rings below 128 rows
-    (100, 4096, 6144, 0, (8, 1, 4)),     # deep rings, ragged last row tile
+    (96, 4096, 4096, 0, (8, 2, 4)),      # below 128 rows: 128-row tiles, K split both ways
+    (100, 4096, 6144, 0, (8, 2, 2)),     # the same with a ragged last row tile
 ]
 
 
@@ -152,6 +152,42 @@ def test_exact_special_case_main_tiles(M, K, N, split, plan, dtype):
     exp = torch.from_numpy(y64).to(tdt)
     got = y.cpu()[torch.as_tensor(rows)]
     assert torch.equal(got, exp), (M, K, N, split, dtype, int((got != exp).sum()))
+
+
+# (M, K, N, G): the mid-size kernel (16 < M <= 64), 2 and 4 row tiles, 64-k and
+# 32-k chunks, ragged group counts and K splits from 8 to 28
+MIDM_CASES = [(64, 4096, 4096, 128), (33, 4096, 4096, 128), (17, 11008, 4096, 128), (32, 14336, 4096, 128),
+              (64, 4096, 1032, 32), (40, 640, 264, 64), (32, 4096, 14336, 128), (20, 4096, 6144, 64)]
+
+
+@pytest.mark.parametrize("M,K,N,G", MIDM_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_exact_special_case_midm(M, K, N, G, dtype):
+    """The bit-exact special case on the mid-size kernel, all rows: its
+    subnormal-operand sums, per-chunk zero/scale step, LDS tree and split-K
+    exchange must reproduce the exact multiples of 1/8."""
+    info = awq.plan_info(awq.AWQ_OP_GEMM_W4A16, M, N, K, G)
+    assert info["kernel"] == 4 and info["row_tiles"] == (2 if M <= 32 else 4), info
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    g = torch.Generator().manual_seed(M * 11 + N + K)
+    X = torch.randint(-1, 2, (M, K), generator=g).to(tdt)
+    qw = torch.randint(-(2 ** 31), 2 ** 31, (K, N // 8), generator=g, dtype=torch.int64).to(torch.int32)
+    qz = torch.zeros(K // G, N // 8, dtype=torch.int32)
+    s = torch.full((K // G, N), 0.125, dtype=tdt)
+    y = awq.gemm_w4a16(*to_dev(X, qw, s, qz), G)
+    torch.cuda.synchronize()
+    y64 = orc().w4a16(X, qw, s, qz, G, F16 if dtype == "f16" else BF16, nthreads=THREADS)
+    exp = torch.from_numpy(y64).to(tdt)
+    assert torch.equal(y.cpu(), exp), (M, K, N, G, dtype, int((y.cpu() != exp).sum()))
+
+
+@pytest.mark.parametrize("M,K,N,G", MIDM_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("sym", [False, True])
+def test_midm_random(M, K, N, G, dtype, sym):
+    c = synthgen.w4a16_case(M, K, N, G, dtype=dtype, sym=sym)
+    yg, y64, _ = _run(c)
+    check_fp(yg, y64, dtype, f"mid-size M={M} K={K} N={N} G={G} {dtype} sym={sym}")
 
 
 def test_gemv_bf16_small_outputs():
