@@ -48,7 +48,7 @@ TARGET_SHAPES = [(4096, 4096), (4096, 14336)]   # (K, N): the stated M=1 / M=204
 M_TARGETS = (1, 2048)
 ROTATE_MB = 600
 KERNEL_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/gemm_w4a16.hip",
-                  "bit_weight_only_awq_amd/csrc/dequant.hip",
+                  "bit_weight_only_awq_amd/csrc/dequant.hip", "bit_weight_only_awq_amd/csrc/stream_w4a16.hip",
                   "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp", "bit_weight_only_awq_amd/csrc/w4a8.hip",
                   "bit_weight_only_awq_amd/csrc/w4a8_fp8.hip",
                   "bit_weight_only_awq_amd/csrc/gemm_w4a8.hip", "bit_weight_only_awq_amd/csrc/stream.hip",

@@ -178,33 +178,42 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         if (split_k > 0) p.splits = (int)std::min<int64_t>(split_k, T);
         p.splits = (int)std::min<int64_t>(p.splits, kMaxSplitK);
     }
-    // 16 < M <= 64: the mid-size kernel (decode-shaped, up to four 16-row
-    // tiles, every weight load of the layer in flight at once; 8 waves of
-    // 32*cs k per workgroup, so the K splits are K / (256 cs)) while its grid
-    // runs in at most two rounds at up to 32 rows (two workgroups per CU) or
-    // one round above (one per CU); on wider or deeper layers the X rows
-    // re-read by every 128-column tile and the partial tiles cost more than
-    // the LDS GEMM saves.  Measured on the Llama-3-8B layers against the LDS
-    // GEMM (two wave groups splitting K): M = 32 qkv 19.4 us, o 17.0, down
-    // 45.1 (about 33, 30 and 55 in the LDS GEMM); M = 64 o 26.4 (30); gate/up
-    // at M = 32 (3.5 rounds) 49.0 against 44.5.
-    if (M > 16 && M <= 64 && split_k == 0) {
+    // 8 < M <= 64: the streaming kernel (measured against the decode kernel
+    // at M = 8 and 16 on the Llama-2-7B layers: level at 8, 1.3-1.6x faster at
+    // 16, where the decode kernel's per-element atomics dominate).
+    // The K split S trades the per-CU stream (weights plus the X rows every
+    // column tile reads again, divided over S workgroups; a CU sustains about
+    // 25 GB/s with all CUs busy) against the partial tiles the last workgroup
+    // of a column tile sums (S x rows x 128 fp32 at about 40 GB/s): the S
+    // in [1, CUs / tiles] (every workgroup resident at once, every wave with a
+    // chunk) with the least estimated time.
+    if (M > 8 && M <= 64) {
         const int cs = G >= 64 ? 2 : 1;
-        const int64_t splits = cdiv(K / (32 * cs), 8);
-        const int64_t wgs = cdiv(N, 128) * splits;
-        if (splits <= kMaxSplitK && (M <= 32 ? wgs <= 4 * cus : wgs <= cus)) {
-            p.kind = 4;
-            p.blk = 1;
-            p.cs = cs;
-            p.waves = 8;
-            p.mt = M <= 32 ? 2 : 4;
-            p.ksplit = 1;
-            p.tiles_n = (int)cdiv(N, 128);
-            p.tiles_m = 1;
-            p.splits = (int)splits;
-            p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(p.tiles_n, p.splits, M, N) : 0;
-            return p;
+        const int mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+        const int wv = kStreamWaves(mt);
+        const int64_t tiles_n = cdiv(N, 128);
+        const int64_t chunks = K / (32 * cs);
+        const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(cus / tiles_n, chunks / wv));
+        const double rows = 16.0 * mt;
+        const double stream_bytes = (double)K * (64 + 2 * rows), tail_bytes = rows * 128 * 4;
+        int64_t s = 1;
+        double best = 0;
+        for (int64_t c = 1; c <= smax; ++c) {
+            const double t = stream_bytes / c / 25.0 + c * tail_bytes / 40.0;
+            if (c == 1 || t < best) best = t, s = c;
         }
+        if (split_k > 0) s = std::min<int64_t>(split_k, chunks);
+        p.kind = 5;
+        p.blk = 1;
+        p.cs = cs;
+        p.waves = wv;
+        p.mt = mt;
+        p.ksplit = 1;
+        p.tiles_n = (int)tiles_n;
+        p.tiles_m = 1;
+        p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
+        p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(p.tiles_n, p.splits, M, N) : 0;
+        return p;
     }
     // buffer-descriptor copies address X and the packed words with 32-bit offsets
     const bool fits_rsrc = M * K * 2 < (int64_t(1) << 31) && K * (N / 2) < (int64_t(1) << 31);
@@ -422,7 +431,7 @@ static int run_w4a16(const void *x, const int32_t *qweight, const void *scales, 
     switch (p.kind) {
         case 0: e = launch_w4a16_decode(a, p, st); break;
         case 3: e = launch_w4a16_gemm(a, p, st); break;
-        case 4: e = launch_w4a16_midm(a, p, st); break;
+        case 5: e = launch_w4a16_stream(a, p, st); break;
         default: e = launch_w4a16_tiled(a, p, st); break;
     }
     return hip_status(e);

@@ -133,6 +133,14 @@ __device__ __forceinline__ uint16_t f32_to_out_bits(float v, int dt) {
     return bit_as<uint16_t>((f16)v);
 }
 
+// Two fp32 values as one 64-bit word (x in the low half), for 64-bit atomics.
+__device__ __forceinline__ uint64_t pack_f32x2(float2 v) {
+    return (uint64_t)bit_as<uint32_t>(v.x) | ((uint64_t)bit_as<uint32_t>(v.y) << 32);
+}
+__device__ __forceinline__ float2 unpack_f32x2(uint64_t w) {
+    return make_float2(bit_as<float>((uint32_t)w), bit_as<float>((uint32_t)(w >> 32)));
+}
+
 // ---------------------------------------------------------------------------
 // Direct global -> LDS copies of 16 bytes per lane: lane i of the wave writes
 // bytes [16 i, 16 i + 16) after the LDS address `dst` of the first active

@@ -23,7 +23,7 @@ struct W4A16Args {
 // Kernel choice and grid for one W4A16 call (pure function of the shape).
 struct W4A16Plan {
     int kind;     // 0 = decode (chunk) kernel, 1 = tiled kernel,
-                  // 3 = LDS-pipelined GEMM (large M), 4 = mid-size kernel (16 < M <= 64)
+                  // 3 = LDS-pipelined GEMM (large M), 5 = streaming kernel (8 < M <= 64)
     int blk;      // decode: word-columns per lane (1, 2)
     int cs;       // decode: 32-k steps per wave chunk (1, 2, 4)
     int waves;    // decode: waves per workgroup (4)
@@ -111,7 +111,10 @@ bool w4a8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p);
 hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
-hipError_t launch_w4a16_midm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
+// streaming kernel (plan kind 5): waves per workgroup for MT 16-row tiles --
+// eight waves up to 32 rows, four 512-register waves at 64
+constexpr int kStreamWaves(int mt) { return mt >= 4 ? 4 : 8; }
+hipError_t launch_w4a16_stream(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);

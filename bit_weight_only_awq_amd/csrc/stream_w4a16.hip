@@ -1,0 +1,348 @@
+// stream_w4a16.hip -- AWQ W4A16 for 8 < M <= 64 on gfx950: the streaming kernel.
+//
+// Method as in w4a16.hip (vLLM pull request "Speed up AWQ 2.5x with updated
+// kernel": the first-generation AWQ order map; w = (q - z) * s, z = 8 when
+// symmetric per the AutoAWQ pull request "Marlin symmetric quantization and
+// inference").
+//
+// A workgroup owns a column tile of 128 outputs and a range of the K
+// chunks (32 * CS consecutive k inside one quantisation group); grid y = S
+// splits of the chunks.  Its WV waves take the range's chunks in turn (wave
+// w: chunks w, w + WV, ..., so at any time the waves read WV consecutive
+// chunks of the tile) and keep two chunks' loads in flight in a register
+// ring, so that the grid fits the GPU in one round with few K splits and the
+// weight stream never drains between chunks.  Lanes are laid out as in the
+// decode kernel: lane (j, gq) holds word-column j of the tile (8 outputs) at
+// the 8 k-rows 8 gq + e of each 32-k step.  Per chunk, the exact (q - z) products
+// are summed on the matrix cores (MT 16-row tiles of X) and scaled once in
+// fp32.  The waves' tiles are then added through LDS in a fixed tree and the
+// S workgroups of a column tile exchange fp32 partials, the last one adding
+// them in split order -- so the result does not depend on timing.
+#include "device.hpp"
+#include "launch.hpp"
+#include "w4a16_ops.hpp"
+
+namespace awq4 {
+
+// The workgroup's M x COLS tile sum, parked in LDS (row-major, COLS floats a
+// row), goes out: written directly when the K range is not split (S == 1);
+// otherwise handed over as fp32 partials exchanged through agent-scope atomic
+// stores and loads (device.hpp: split_tile_last_atomic), the last workgroup of
+// the column tile adding them in split order and clearing them.
+template <int NT, int DT, int COLS>
+__device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_t *__restrict__ y,
+                                                       uint64_t *__restrict__ ws, int M, int N, int tile, int S) {
+    // Everything moves as column pairs: N is a multiple of 8, so a pair never
+    // straddles the last column, and the output and the partial area (after
+    // the counters, 256-byte aligned) take 4- and 8-byte accesses.
+    const int n_base = tile * COLS;
+    const int pairs = M * COLS / 2;
+    auto pair_at = [&](int pi) { return (size_t)(pi / (COLS / 2)) * (N / 2) + n_base / 2 + pi % (COLS / 2); };
+    auto pair_ok = [&](int pi) { return pi < pairs && n_base + 2 * (pi % (COLS / 2)) < N; };
+    auto out_pair = [&](size_t at, float2 v) {
+        *(uint32_t *)(y + 2 * at) = (uint32_t)f32_to_out_bits(v.x, DT) | ((uint32_t)f32_to_out_bits(v.y, DT) << 16);
+    };
+    if (S == 1) {
+        for (int pi = threadIdx.x; pi < pairs; pi += NT)
+            if (pair_ok(pi)) out_pair(pair_at(pi), *(const float2 *)(red + 2 * pi));
+        return;
+    }
+    // one 64-bit agent-scope atomic per pair and split
+    uint64_t *const part = (uint64_t *)((char *)ws + split_counters_bytes(gridDim.x));
+    const size_t slot = (size_t)M * N / 2;  // pairs per split
+    for (int pi = threadIdx.x; pi < pairs; pi += NT)
+        if (pair_ok(pi)) {
+            const float2 v = *(const float2 *)(red + 2 * pi);
+            __hip_atomic_store(&part[blockIdx.y * slot + pair_at(pi)], pack_f32x2(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    if (!split_tile_last_atomic((uint32_t *)ws + tile, S)) return;
+    // The last workgroup of the column tile sums the partials in split order.
+    // Each thread takes kP pairs at a time and issues the loads of a batch of
+    // kB splits for all of them before adding, so a pass costs one round trip
+    // per batch instead of one per pair and batch.
+    constexpr int kP = 8, kB = 4;
+    for (int p0 = threadIdx.x; p0 < pairs; p0 += kP * NT) {
+        float2 v[kP];
+#pragma unroll
+        for (int q = 0; q < kP; ++q) v[q] = make_float2(0.f, 0.f);
+        for (int s0 = 0; s0 < S; s0 += kB) {
+            uint64_t b[kP][kB];
+#pragma unroll
+            for (int q = 0; q < kP; ++q) {
+                const int pi = p0 + q * NT;
+                const bool ok = pair_ok(pi);
+#pragma unroll
+                for (int i = 0; i < kB; ++i)
+                    b[q][i] = ok && s0 + i < S ? __hip_atomic_load(&part[(size_t)(s0 + i) * slot + pair_at(pi)],
+                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                               : 0ull;
+            }
+#pragma unroll
+            for (int q = 0; q < kP; ++q)
+#pragma unroll
+                for (int i = 0; i < kB; ++i) {
+                    const float2 f = unpack_f32x2(b[q][i]);
+                    v[q].x += f.x;
+                    v[q].y += f.y;
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < kP; ++q) {
+            const int pi = p0 + q * NT;
+            if (!pair_ok(pi)) continue;
+            const size_t at = pair_at(pi);
+            for (int s = 0; s < S; ++s)
+                __hip_atomic_store(&part[(size_t)s * slot + at], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            out_pair(at, v[q]);
+        }
+    }
+}
+
+// One chunk's loads: scales and zero points of its group, MT row tiles of X
+// (from L2: every column tile reads the same rows), the packed words.
+template <int MT, int CS>
+struct StreamBuf {
+    u32x4 s4;
+    uint32_t zw;
+    u32x4 a[MT][CS];
+    uint32_t w[CS][8];
+};
+
+// Per-lane byte offsets of a wave's loads, fixed for the whole kernel; the
+// chunk's own offsets (its k0 and group) are uniform, so each load is a
+// scalar base plus one of these, with no per-load 64-bit address arithmetic.
+template <int MT>
+struct StreamOffsets {
+    uint32_t w;      // packed word of row 8 gq, word-column wld
+    uint32_t s;      // 8 scales of word-column wld
+    uint32_t z;      // zero-point word of word-column wld
+    uint32_t x[MT];  // X row 16 mt + j (row 0 past M), k offset 8 gq
+};
+
+template <int MT, int CS, bool SYM>
+__device__ __forceinline__ void stream_issue(StreamBuf<MT, CS> &b, const StreamOffsets<MT> &o,
+                                             const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
+                                             const uint16_t *__restrict__ sc, const uint32_t *__restrict__ qz,
+                                             int chunk, int lgG, int N, int nw) {
+    const int k0 = chunk * 32 * CS;
+    const int g = k0 >> lgG;  // the chunk lies inside one group
+    auto at = [](const void *base, uint32_t off) { return (const char *)base + off; };
+    b.s4 = *(const u32x4 *)at(sc + (size_t)g * N, o.s);
+    b.zw = SYM ? 0x88888888u : *(const uint32_t *)at(qz + (size_t)g * nw, o.z);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < CS; ++s) b.a[mt][s] = *(const u32x4 *)at(x + k0 + 32 * s, o.x[mt]);
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            b.w[s][e] = __builtin_nontemporal_load((const uint32_t *)at(qw + (size_t)(k0 + 32 * s + e) * nw, o.w));
+}
+
+// One chunk into the accumulators.  B = the exact integer (q - z) in the
+// activation type; for each column MFMA the chunk's CS k-steps are summed in a
+// small fp32 temporary that is then scaled by s once and added (so no weight
+// is rounded and the scale is applied in fp32, as in the decode kernel).
+template <int MT, int CS, int DT, bool SYM>
+__device__ __forceinline__ void stream_compute(const StreamBuf<MT, CS> &b, f32x4 (&acc)[MT][8]) {
+    ZeroConsts<DT> zc;
+    zero_consts<DT, SYM>(zc, b.zw);
+    uint32_t px[CS][4], py[CS][4];
+#pragma unroll
+    for (int s = 0; s < CS; ++s)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            px[s][p] = pair_x(b.w[s][2 * p], b.w[s][2 * p + 1]);
+            py[s][p] = pair_y(b.w[s][2 * p], b.w[s][2 * p + 1]);
+        }
+    static_for<8>([&](auto tc) {
+        constexpr int T = decltype(tc)::value;
+        f32x4 t[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) t[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < CS; ++s) {
+            u32x4 bop;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) bop[p] = qz_pair<DT, T>(col_src_y(T) ? py[s][p] : px[s][p], zc);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) t[mt] = mma<DT>(b.a[mt][s], bop, t[mt]);
+        }
+        const float st = scale_f32<DT>(b.s4, T);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mt][T][r] = __builtin_fmaf(t[mt][r], st, acc[mt][T][r]);
+        // two groups of four columns: bounds how many temporaries the
+        // scheduler keeps live at once (all eight spill a few registers)
+        if (T == 3) __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// Keeps a buffer's loads where they are issued, a chunk ahead of their use:
+// the empty asm statement stops the optimiser from sinking them next to it,
+// the scheduling barrier stops the instruction scheduler from pulling the
+// next chunk's arithmetic, and so its waits, above them.
+__device__ __forceinline__ void prefetch_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MT, int CS, int WV, int DT, bool SYM>
+__global__ __launch_bounds__(64 * WV, 1) void w4a16_stream(const uint16_t *__restrict__ x,
+                                                          const uint32_t *__restrict__ qw,
+                                                          const uint16_t *__restrict__ sc,
+                                                          const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
+                                                          uint64_t *__restrict__ ws, int M, int N, int K, int lgG) {
+    constexpr int ROWS = 16 * MT, COLS = 128;
+    // tree reduction area: WV/2 partial tiles of ROWS x COLS floats
+    __shared__ __attribute__((aligned(16))) float red[(WV / 2) * ROWS * COLS];
+    const int lane = threadIdx.x & 63;
+    // the wave index in a scalar register: the chunk loop below is uniform
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = lane & 15, gq = lane >> 4;
+    const int nw = N >> 3;
+    // A wave reads 64 bytes of each packed k-row; the other half of that
+    // 128-byte line belongs to the neighbouring tile.  Neighbouring tiles go
+    // to one XCD, so that the line is fetched into one L2 instead of two.
+    // (Two word-columns per lane, whole lines per wave, measured slower: the
+    // doubled accumulators cost half the waves per CU.)
+    const int tile = tile_of_xcd_order(blockIdx.x, gridDim.x);
+    const int wcol = tile * 16 + j;
+    const int wld = wcol < nw ? wcol : nw - 1;  // past the last word-column: in-bounds words, sums never stored
+    // this workgroup's chunks [c_lo, c_hi) and this wave's share of them
+    const int S = gridDim.y;
+    const int nchunks = K / (32 * CS);
+    const int per = (nchunks + S - 1) / S;
+    const int c_lo = blockIdx.y * per;
+    const int c_hi = min(nchunks, c_lo + per);
+    const int n = c_hi - c_lo > wave ? (c_hi - c_lo - wave + WV - 1) / WV : 0;
+    // (the per-lane parts stay small: 8 k-rows of packed words, and at most
+    // 64 rows of X -- rows past M read row 0, their sums never stored)
+    StreamOffsets<MT> off;
+    off.w = (uint32_t)(8 * gq * nw + wld) * 4u;
+    off.s = (uint32_t)wld * 16u;
+    off.z = (uint32_t)wld * 4u;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int row = 16 * mt + j;
+        off.x[mt] = (uint32_t)((row < M ? row : 0) * K + 8 * gq) * 2u;
+    }
+
+    f32x4 acc[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[mt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // Two chunks in flight: chunk i + 2 is issued while chunk i + 1 is
+    // computed.  The loop runs while both of its prefetches exist; the last
+    // one or two chunks are finished after it, so that no load is issued past
+    // the wave's last chunk.
+    auto chunk_of = [&](int i) { return c_lo + wave + i * WV; };
+    StreamBuf<MT, CS> b0, b1;
+    if (n == 1) {
+        stream_issue<MT, CS, SYM>(b0, off, x, qw, sc, qz, chunk_of(0), lgG, N, nw);
+        stream_compute<MT, CS, DT, SYM>(b0, acc);
+    } else if (n >= 2) {
+        stream_issue<MT, CS, SYM>(b0, off, x, qw, sc, qz, chunk_of(0), lgG, N, nw);
+        stream_issue<MT, CS, SYM>(b1, off, x, qw, sc, qz, chunk_of(1), lgG, N, nw);
+        prefetch_fence();
+        int i = 0;
+        for (; i + 3 < n; i += 2) {
+            stream_compute<MT, CS, DT, SYM>(b0, acc);
+            stream_issue<MT, CS, SYM>(b0, off, x, qw, sc, qz, chunk_of(i + 2), lgG, N, nw);
+            prefetch_fence();
+            stream_compute<MT, CS, DT, SYM>(b1, acc);
+            stream_issue<MT, CS, SYM>(b1, off, x, qw, sc, qz, chunk_of(i + 3), lgG, N, nw);
+            prefetch_fence();
+        }
+        // chunks i and i + 1 are in flight; n - i is 2 or 3
+        stream_compute<MT, CS, DT, SYM>(b0, acc);
+        if (i + 2 < n) {
+            stream_issue<MT, CS, SYM>(b0, off, x, qw, sc, qz, chunk_of(i + 2), lgG, N, nw);
+            prefetch_fence();
+            stream_compute<MT, CS, DT, SYM>(b1, acc);
+            stream_compute<MT, CS, DT, SYM>(b0, acc);
+        } else {
+            stream_compute<MT, CS, DT, SYM>(b1, acc);
+        }
+    }
+
+    // Lane holds rows 16 mt + 4 gq + r and columns 8 j + t of the tile.
+    auto slot_of = [&](int sl, int mt, int r) {
+        return red + ((size_t)sl * ROWS + 16 * mt + 4 * gq + r) * COLS + 8 * j;
+    };
+    auto park = [&](int sl) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float *d = slot_of(sl, mt, r);
+                const f32x4(&v)[8] = acc[mt];
+                *(f32x4 *)d = (f32x4){v[0][r], v[1][r], v[2][r], v[3][r]};
+                *(f32x4 *)(d + 4) = (f32x4){v[4][r], v[5][r], v[6][r], v[7][r]};
+            }
+    };
+    // waves [h, 2h) hand their tiles to waves [0, h), h = WV/2, ..., 1
+#pragma unroll
+    for (int h = WV / 2; h >= 1; h >>= 1) {
+        if (wave >= h && wave < 2 * h) park(wave - h);
+        __syncthreads();
+        if (wave < h) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float *d = slot_of(wave, mt, r);
+                    const f32x4 v0 = *(const f32x4 *)d, v1 = *(const f32x4 *)(d + 4);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        acc[mt][t][r] += v0[t];
+                        acc[mt][4 + t][r] += v1[t];
+                    }
+                }
+        }
+        __syncthreads();
+    }
+    // wave 0 holds the workgroup's sum: park it for all threads
+    if (wave == 0) park(0);
+    __syncthreads();
+    tile_store_or_exchange<64 * WV, DT, COLS>(red, y, ws, M, N, tile, S);
+}
+
+template <int MT, int CS, int DT, bool SYM>
+static hipError_t launch_stream_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    constexpr int WV = kStreamWaves(MT);
+    if (p.waves != WV || (p.splits > 1 && p.acc == nullptr)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((w4a16_stream<MT, CS, WV, DT, SYM>), dim3(p.tiles_n, p.splits), dim3(64 * WV), 0, st,
+                       (const uint16_t *)a.x, (const uint32_t *)a.qweight, (const uint16_t *)a.scales,
+                       (const uint32_t *)a.qzeros, (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K,
+                       __builtin_ctz((unsigned)a.G));
+    return hipGetLastError();
+}
+
+template <int MT, int CS>
+static hipError_t launch_stream_dt(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    const bool sym = a.qzeros == nullptr;
+    if (a.dtype == DT_F16)
+        return sym ? launch_stream_t<MT, CS, DT_F16, true>(a, p, st) : launch_stream_t<MT, CS, DT_F16, false>(a, p, st);
+    return sym ? launch_stream_t<MT, CS, DT_BF16, true>(a, p, st) : launch_stream_t<MT, CS, DT_BF16, false>(a, p, st);
+}
+
+// p.mt: 16-row tiles (1, 2, 4); p.cs: 32-k steps per chunk (1, 2)
+hipError_t launch_w4a16_stream(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
+    switch (p.mt * 10 + p.cs) {
+        case 11: return launch_stream_dt<1, 1>(a, p, st);
+        case 12: return launch_stream_dt<1, 2>(a, p, st);
+        case 21: return launch_stream_dt<2, 1>(a, p, st);
+        case 22: return launch_stream_dt<2, 2>(a, p, st);
+        case 41: return launch_stream_dt<4, 1>(a, p, st);
+        case 42: return launch_stream_dt<4, 2>(a, p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace awq4

@@ -45,7 +45,8 @@ __device__ __forceinline__ uint32_t qz_pair(uint32_t src, const ZeroConsts<DT> &
     const uint32_t v = col_shift(t) ? (src >> 8) : src;
     if (DT == DT_F16) {
         const uint32_t mask = col_hi(t) ? 0x00F000F0u : 0x000F000Fu;
-        f16x2 h = bit_as<f16x2>((v & mask) | 0x64006400u);
+        // (v & mask) | 0x64006400 in one three-input bitwise op
+        f16x2 h = bit_as<f16x2>(__builtin_amdgcn_bitop3_b32(v, mask, 0x64006400u, 0xEA));
         f16x2 z = bit_as<f16x2>(c.zc[t]);
         f16x2 d;
         if (col_hi(t)) {

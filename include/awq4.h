@@ -140,7 +140,7 @@ int awq_repack_v2(const int32_t *qweight_v2, const int32_t *qzeros_v2, int32_t *
  *    64-bit counting accumulator per output element (M x N); the last
  *    contribution to an element writes the output and clears it (the size
  *    returned for the W4A16 calls covers both activation dtypes);
- *  - a split-K bf16 decode GEMV and the GEMM kernels (M > 16 for W4A16,
+ *  - a split-K bf16 decode GEMV and the GEMM kernels (M > 8 for W4A16,
  *    M > 64 for W4A8) use one 32-bit
  *    arrival counter per output tile (padded to 256 bytes) followed by S
  *    partial [M, N] results of 4 bytes each (fp32 for W4A16, int32 for
@@ -193,12 +193,15 @@ int awq_plan_info(int op, int64_t M, int64_t N, int64_t K, int group_size, int s
  *   y:       device, [M, N] in the activation dtype (written, not accumulated).
  *   group_size G in {32, 64, 128}; K % G == 0; N % 8 == 0; M, N, K >= 1.
  *   split_k: number of K slices reduced through the workspace (0 = chosen by
- *            the library, 1 = none, at most min(K/32, 255)).  For M <= 16
+ *            the library, 1 = none, at most min(K/32, 255)).  For M <= 8
  *            the library's decode kernel fixes the K split itself and
  *            ignores split_k.
- * Numerics: each weight is dequantised exactly to (q - z) and multiplied by s
- * with one rounding to the activation dtype; products accumulate in fp32 on
- * the matrix cores; the output is rounded to nearest even.
+ * Numerics: M <= 64 -- the exact (q - z) products are summed in fp32 on the
+ * matrix cores and scaled by s in fp32 once per chunk (32 to 128 consecutive
+ * k inside one group); M > 64 --
+ * each weight is dequantised exactly to (q - z) and multiplied by s with one
+ * rounding to the activation dtype, products accumulating in fp32.  The
+ * output is rounded to nearest even.
  * Errors: AWQ_EINVAL (shapes, pointers, dtype, G), AWQ_EALIGN, AWQ_EWORKSPACE,
  * AWQ_EHIP.
  */

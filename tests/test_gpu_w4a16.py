@@ -154,20 +154,26 @@ def test_exact_special_case_main_tiles(M, K, N, split, plan, dtype):
     assert torch.equal(got, exp), (M, K, N, split, dtype, int((got != exp).sum()))
 
 
-# (M, K, N, G): the mid-size kernel (16 < M <= 64), 2 and 4 row tiles, 64-k and
-# 32-k chunks, ragged group counts and K splits from 8 to 28
-MIDM_CASES = [(64, 4096, 4096, 128), (33, 4096, 4096, 128), (17, 11008, 4096, 128), (32, 14336, 4096, 128),
-              (64, 4096, 1032, 32), (40, 640, 264, 64), (32, 4096, 14336, 128), (20, 4096, 6144, 64)]
+# (M, K, N, G): the streaming kernel (8 < M <= 64): 1, 2 and 4 row tiles,
+# 64-k and 32-k chunks, ragged last column tiles, one to fourteen chunks per
+# wave (every path of the register ring), K splits from 1 to 8
+STREAM_CASES = [(64, 4096, 4096, 128), (33, 4096, 4096, 128), (17, 11008, 4096, 128), (32, 14336, 4096, 128),
+                (64, 4096, 1032, 32), (40, 640, 264, 64), (32, 4096, 14336, 128), (20, 4096, 6144, 64),
+                (9, 4096, 4096, 128), (16, 11008, 4096, 128), (12, 640, 264, 32), (64, 14336, 4096, 128)]
 
 
-@pytest.mark.parametrize("M,K,N,G", MIDM_CASES, ids=lambda v: str(v))
+def _stream_rows(M):
+    return 1 if M <= 16 else 2 if M <= 32 else 4
+
+
+@pytest.mark.parametrize("M,K,N,G", STREAM_CASES, ids=lambda v: str(v))
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_exact_special_case_midm(M, K, N, G, dtype):
-    """The bit-exact special case on the mid-size kernel, all rows: its
-    subnormal-operand sums, per-chunk zero/scale step, LDS tree and split-K
-    exchange must reproduce the exact multiples of 1/8."""
+def test_exact_special_case_stream(M, K, N, G, dtype):
+    """The bit-exact special case on the streaming kernel, all rows: its exact
+    (q - z) sums, per-chunk scale step, LDS tree and split-K exchange must
+    reproduce the exact multiples of 1/8."""
     info = awq.plan_info(awq.AWQ_OP_GEMM_W4A16, M, N, K, G)
-    assert info["kernel"] == 4 and info["row_tiles"] == (2 if M <= 32 else 4), info
+    assert info["kernel"] == 5 and info["row_tiles"] == _stream_rows(M), info
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
     g = torch.Generator().manual_seed(M * 11 + N + K)
     X = torch.randint(-1, 2, (M, K), generator=g).to(tdt)
@@ -181,13 +187,33 @@ def test_exact_special_case_midm(M, K, N, G, dtype):
     assert torch.equal(y.cpu(), exp), (M, K, N, G, dtype, int((y.cpu() != exp).sum()))
 
 
-@pytest.mark.parametrize("M,K,N,G", MIDM_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("M,K,N,G", STREAM_CASES, ids=lambda v: str(v))
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("sym", [False, True])
-def test_midm_random(M, K, N, G, dtype, sym):
+def test_stream_random(M, K, N, G, dtype, sym):
     c = synthgen.w4a16_case(M, K, N, G, dtype=dtype, sym=sym)
     yg, y64, _ = _run(c)
-    check_fp(yg, y64, dtype, f"mid-size M={M} K={K} N={N} G={G} {dtype} sym={sym}")
+    check_fp(yg, y64, dtype, f"streaming M={M} K={K} N={N} G={G} {dtype} sym={sym}")
+
+
+@pytest.mark.parametrize("M,K,N,G,split", [(40, 640, 264, 64, 6), (12, 640, 264, 32, 7), (64, 4096, 4096, 128, 1),
+                                           (24, 4096, 4096, 128, 13), (48, 11008, 4096, 128, 3)])
+def test_stream_explicit_splits(M, K, N, G, split):
+    """Explicit K splits on the streaming kernel, including splits that leave
+    the last workgroups of a column tile without a chunk (640/64 = 10 chunks
+    over 6 splits: ceil(10/6) = 2 each, the sixth empty) -- they still count
+    in the split exchange -- and the unsplit path; exact special case."""
+    info = awq.plan_info(awq.AWQ_OP_GEMM_W4A16, M, N, K, G, split)
+    assert info["kernel"] == 5 and info["splits"] == split, info
+    g = torch.Generator().manual_seed(M + N + split)
+    X = torch.randint(-1, 2, (M, K), generator=g).to(torch.float16)
+    qw = torch.randint(-(2 ** 31), 2 ** 31, (K, N // 8), generator=g, dtype=torch.int64).to(torch.int32)
+    qz = torch.randint(0, 2 ** 31, (K // G, N // 8), generator=g, dtype=torch.int64).to(torch.int32)
+    s = torch.full((K // G, N), 0.25, dtype=torch.float16)
+    y = awq.gemm_w4a16(*to_dev(X, qw, s, qz), G, split_k=split)
+    torch.cuda.synchronize()
+    exp = torch.from_numpy(orc().w4a16(X, qw, s, qz, G, F16, nthreads=THREADS)).to(torch.float16)
+    assert torch.equal(y.cpu(), exp), (M, K, N, G, split, int((y.cpu() != exp).sum()))
 
 
 def test_gemv_bf16_small_outputs():
