@@ -69,10 +69,21 @@ def w4a8_alg_bytes(M, K, N):
     return K * N // 2 + N * 2 + M * K + 4 * M + 2 * M * N
 
 
-# sources the decode kernel is built from (its traffic counters stay valid while these are unchanged)
+# sources the decode kernel is built from; its traffic counters stay valid while
+# these and its launch plans for the decode layers (decode_digest) are unchanged
 DECODE_SOURCES = ["bit_weight_only_awq_amd/csrc/w4a16.hip", "bit_weight_only_awq_amd/csrc/w4a16_ops.hpp",
-                  "bit_weight_only_awq_amd/csrc/device.hpp", "bit_weight_only_awq_amd/csrc/launch.hpp",
-                  "bit_weight_only_awq_amd/csrc/api.cpp"]
+                  "bit_weight_only_awq_amd/csrc/device.hpp"]
+
+
+def decode_digest():
+    """Digest of what the decode traffic depends on: the decode kernel's sources
+    and the plans (grid, K split, chunking) of the four decode layers on a whole
+    MI355X, so that planner changes elsewhere do not invalidate it."""
+    import bit_weight_only_awq_amd as awq
+    plans = [awq.plan_info(awq.AWQ_OP_GEMV_W4A16, M_DECODE, N, K, G, cu_count=256) for _, K, N in DECODE_LAYERS]
+    h = hashlib.sha256(source_digest(DECODE_SOURCES).encode())
+    h.update(json.dumps(plans, sort_keys=True).encode())
+    return h.hexdigest()[:16]
 
 
 def source_digest(files=KERNEL_SOURCES):
@@ -107,6 +118,73 @@ def counter_rows(path):
     return dict(sorted(out.items()))
 
 
+def pmc_summary(kernel, labels, paths):
+    """CPU only: the counters of the last len(labels) `kernel` dispatches (the
+    last repetition of a --profile run, one dispatch per label, in order) in
+    rocprofv3 counter_collection.csv files (one per --pmc pass), summed over
+    the chip; byte counters scaled by the calibration copy the --profile run
+    launches first.  Prints one table per dispatch."""
+    import csv
+    out = [dict() for _ in labels]
+    shape = [None] * len(labels)
+    factors = {}
+    for path in paths:
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        disp = {}
+        for r in rows:
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                                        "wg": int(r["Workgroup_Size"]), "c": {}})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for d in disp.values():
+            if "neg" in d["name"]:
+                for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                    if ctr in d["c"]:
+                        factors[ctr] = CAL_BYTES / (d["c"][ctr] * 1024.0)
+        mine = [disp[i] for i in sorted(disp) if kernel in disp[i]["name"]][-len(labels):]
+        if len(mine) != len(labels):
+            raise SystemExit(f"{path}: {len(mine)} {kernel} dispatches, {len(labels)} labels")
+        for k, d in enumerate(mine):
+            out[k].update(d["c"])
+            shape[k] = (d["name"].split("(")[0], d["grid"] // d["wg"], d["wg"])
+    for lab, (name, wgs, wg), c in zip(labels, shape, out):
+        print(f"{lab}: {name}  {wgs} workgroups x {wg} threads")
+        for ctr in sorted(c):
+            v = c[ctr]
+            extra = ""
+            if ctr in factors:
+                extra = f"   ({v * 1024.0 * factors[ctr] / 1e6:.2f} MB after calibration x{factors[ctr]:.4f})"
+            print(f"  {ctr:28s} {v:12.4e}{extra}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
+            busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * c["GRBM_GUI_ACTIVE"] / 8)
+            print(f"  matrix cores busy: {100 * busy:.1f} % of the cycles (1024 SIMDs, GRBM over 8 XCDs)")
+
+
+def trace_summary(trace_csv):
+    """CPU only: per-kernel and per-launch-shape durations from a rocprofv3
+    --kernel-trace kernel_trace.csv (all dispatches of the run)."""
+    import csv
+    import statistics
+    per_kernel, per_shape = {}, {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"].split("(")[0][:60]
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            wg = (int(r["Workgroup_Size_X"]), int(r["Workgroup_Size_Y"]), int(r["Workgroup_Size_Z"]))
+            grid = tuple(int(r[f"Grid_Size_{a}"]) // w for a, w in zip("XYZ", wg))
+            per_kernel.setdefault(name, []).append(us)
+            per_shape.setdefault((name, grid, wg[0] * wg[1] * wg[2]), []).append(us)
+    total = sum(sum(v) for v in per_kernel.values())
+    print(f"{'kernel':60s} {'calls':>7s} {'avg_us':>9s} {'pct':>7s}")
+    for name, v in sorted(per_kernel.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{name:60s} {len(v):7d} {sum(v) / len(v):9.2f} {100 * sum(v) / total:7.2f}")
+    print()
+    print(f"{'kernel':48s} {'grid (wg x,y,z)':>16s} {'block':>6s} {'calls':>6s} {'median':>9s} {'min':>9s}")
+    for (name, grid, blk), v in sorted(per_shape.items()):
+        print(f"{name[:48]:48s} {','.join(map(str, grid)):>16s} {blk:6d} {len(v):6d} "
+              f"{statistics.median(v):9.2f} {min(v):9.2f}")
+
+
 def traffic_summary(fetch_csv, write_csv, kernel="w4a16_decode", name="w4a16_decode_m1_llama2_7b"):
     """HBM bytes per launch of `kernel` in a `--profile decode` run: FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch, one rocprofv3 pass each), each scaled by what
@@ -135,7 +213,7 @@ def traffic_summary(fetch_csv, write_csv, kernel="w4a16_decode", name="w4a16_dec
            "alg_bytes_per_launch": round(sum(alg.values()) / len(alg)),
            "per_layer": {n: {"hbm_bytes": total[n], "alg_bytes": alg[n], "ratio": round(total[n] / alg[n], 4)}
                          for n in total},
-           "counters": res, "source_digest": source_digest(DECODE_SOURCES),
+           "counters": res, "source_digest": decode_digest(),
            "command": "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --profile decode; "
                       "rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --profile decode; "
                       "python3 bench.py --traffic <fetch csv> <write csv>"}
@@ -402,9 +480,20 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="CPU only: summarise the two counter passes of `--profile decode` into "
                          "profiles/w4a16_decode_m1_llama2_7b.traffic.json")
+    ap.add_argument("--pmc-summary", nargs="+", metavar=("KERNEL LABELS", "CSV"),
+                    help="CPU only: print the counters of the last KERNEL dispatches, one per comma-separated "
+                         "label, from counter CSVs of a --profile run (one per --pmc pass)")
+    ap.add_argument("--trace-summary", metavar="TRACE_CSV",
+                    help="CPU only: per-kernel and per-launch-shape durations from a rocprofv3 kernel_trace.csv")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.traffic:
         traffic_summary(*args.traffic)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1].split(","), args.pmc_summary[2:])
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the 4-bit GEMM hot path has no "
@@ -710,7 +799,7 @@ def main():
            "roofline": {"kernel": "w4a16_decode (decode GEMV, M=1, 4 Llama-2-7B layers back to back)",
                         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": load_traffic("w4a16_decode_m1_llama2_7b", source_digest(DECODE_SOURCES)),
+                        "traffic": load_traffic("w4a16_decode_m1_llama2_7b", decode_digest()),
                         "avg_launch_us": round(t_dec / len(DECODE_LAYERS) * 1e6, 3),
                         "per_layer": dec_layer},
            "gemm_m2048": {"kernel": "w4a16_gemm (prefill GEMM, M=2048, 4 Llama-3-8B layers back to back)",
