@@ -20,9 +20,9 @@ static constexpr int64_t kMaxDim = int64_t(1) << 20;
 // The planners below size grids from the device's compute-unit count (cus):
 // two workgroups of 4 waves per CU is the target fill of the tiled kernels.
 static int64_t target_workgroups(const DeviceProps &d) { return 2 * (int64_t)d.cus; }
-// The W4A16 LDS GEMM takes M above 16 where the decode and mid-size kernels
-// do not (the decode kernel below).
-static constexpr int64_t kW16LdsMinM = 16;
+// The W4A16 LDS GEMM takes M above 64 (the decode kernel takes M <= 8, the
+// streaming kernel 8 < M <= 64).
+static constexpr int64_t kW16LdsMinM = 64;
 // The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, two per CU) are used
 // whenever there are at least as many as CUs; with fewer, the 128 x 128 tiles
 // give more workgroups before a K split is needed (measured: M = 512 on
@@ -127,7 +127,7 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
     const int64_t nw = N / 8;
     const int64_t T = K / 32;
     int64_t tiles;
-    if (M <= 16) {
+    if (M <= 8) {
         // decode kernel: one 32*cs-wide K chunk per wave, 4 chunks per
         // workgroup; the K split is fixed by the chunking (split_k is ignored)
         p.kind = 0;
@@ -156,7 +156,7 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         }
         tiles = p.tiles_n;
     }
-    if (M > 16 || p.splits > kMaxSplitK) {
+    if (M > 8 || p.splits > kMaxSplitK) {
         p.kind = 1;
         p.blk = 1;
         p.cs = 1;
