@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libawq4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["pack.hip", "dequant.hip", "w4a16.hip", "stream_w4a16.hip", "gemm_w4a16.hip", "w4a8.hip", "w4a8_fp8.hip", "gemm_w4a8.hip", "stream.hip", "api.cpp"]
+SOURCES = ["pack.hip", "dequant.hip", "w4a16.hip", "stream_w4a16.hip", "gemm_w4a16.hip", "w4a8.hip", "w4a8_fp8.hip", "gemm_w4a8_fp8.hip", "gemm_w4a8.hip", "stream.hip", "api.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops (the host
 # pass does not know the feature and warns; that is expected).

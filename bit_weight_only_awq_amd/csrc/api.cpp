@@ -379,6 +379,24 @@ W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d) {
         p.tilered = 1;
         p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(tiles, p.splits, M, N) : 0;
     }
+    // LDS-pipelined GEMM from 128 rows: 128 x 256 tiles, 128-k stages; a K
+    // split through per-tile fp32 partials only when tiles are fewer than CUs.
+    // (Buffer-descriptor copies address the codes and the packed words with
+    // 32-bit offsets.)
+    const bool fits_rsrc = M * K < (int64_t(1) << 31) && (K / 8) * N * 4 < (int64_t(1) << 31);
+    if (M >= 128 && fits_rsrc) {
+        p.kind = 2;
+        p.blk = 2;
+        p.mt = 4;
+        p.tiles_n = (int)cdiv(N, 256);
+        p.tiles_m = (int)cdiv(M, 128);
+        tiles = (int64_t)p.tiles_n * p.tiles_m;
+        int64_t s = 1;
+        if (tiles < cus) s = std::min<int64_t>(cdiv(cus, tiles), std::max<int64_t>(1, T / 4));
+        p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
+        p.tilered = 1;
+        p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(tiles, p.splits, M, N) : 0;
+    }
     return p;
 }
 

@@ -279,6 +279,16 @@ def test_fp8_validation():
     assert g() == L.AWQ_EWORKSPACE                  # split-K needs its workspace
     assert lib.awq_workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, 1, 8192, 21760, -1, 0) == 8192 * 8
     assert lib.awq_workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, 1, 8192, 21824, -1, 0) == 0
+    # the kernels by M: skinny up to 64 rows, register-tiled below 128, the
+    # LDS-pipelined GEMM (128 x 256 tiles) from 128, split only with fewer
+    # tiles than CUs
+    fp8 = L.AWQ_OP_W4A8_FP8_GEMM
+    assert [_plan(fp8, M, 8192, 21760, -1).kernel for M in (64, 100, 128, 1024)] == [0, 1, 2, 2]
+    p = _plan(fp8, 1024, 8192, 21760, -1)
+    assert (p.tiles_n, p.tiles_m, p.splits, p.workspace_bytes) == (32, 8, 1, 0)
+    p = _plan(fp8, 256, 8192, 21760, -1)
+    assert p.tiles_n * p.tiles_m == 64 and p.splits == 4
+    assert p.workspace_bytes == lib.awq_workspace_bytes(fp8, 256, 8192, 21760, -1, 0) > 256 * 8192 * 4 * 4
     assert lib.w4a8_fp8_quant_act(None, A, A, A, 1, 16, 0, None) == L.AWQ_EINVAL
     assert lib.w4a8_fp8_quant_act(A, A, A, None, 1, 16, 0, None) == L.AWQ_EINVAL
     assert lib.w4a8_fp8_quant_act(A, A, A, A, 1, 16, 3, None) == L.AWQ_EINVAL
