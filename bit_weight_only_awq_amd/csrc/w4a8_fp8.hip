@@ -58,6 +58,58 @@ __device__ __forceinline__ float round_act_f(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// The quotient x / s without a divide per value.  Per row: r = RN(1 / s') by
+// one divide; per value q0 = RN(x' r), e = x' - q0 s' (exact, one FMA) and
+// q = RN(q0 + e r), Markstein's correction, which is the correctly rounded
+// quotient when nothing underflows; x' and s' are x and s times 2^64 on bf16
+// rows with s < 2^-60 (exact, the same quotient), so that every x whose
+// quotient can reach the smallest E4M3 subnormal stays far above the range
+// where e would round.  Checked on the host for every scale the quantiser can
+// produce and every fp16 / bf16 value it can meet: the E4M3 code of the
+// clamped q equals that of the clamped correctly rounded quotient in every
+// case.  Rows with s = 0, s below 2^-126 (bf16 only) or s not finite take
+// the divide.
+template <int DT>
+struct Fp8Quotient {
+    float sc, ss, r;
+    bool exact_divide;
+    __device__ __forceinline__ explicit Fp8Quotient(float s) {
+        sc = (DT == DT_BF16 && s < 0x1p-60f) ? 0x1p64f : 1.0f;
+        ss = s * sc;
+        exact_divide = !(s >= 0x1p-126f && s <= 3.4028234663852886e38f);
+        r = exact_divide ? 0.0f : 1.0f / ss;
+    }
+    // clamp(x / s, +-448) for exact_divide == false.  The sign is x's: the
+    // correction can turn a zero quotient's sign (-0 + 0 = +0), and the E4M3
+    // code keeps it.
+    __device__ __forceinline__ float q(float x) const {
+        const float xs = DT == DT_BF16 ? x * sc : x;
+        const float q0 = xs * r;
+        const float e = __builtin_fmaf(-q0, ss, xs);
+        return __builtin_amdgcn_fmed3f(__builtin_copysignf(__builtin_fmaf(e, r, q0), x), -448.0f, 448.0f);
+    }
+};
+
+// E4M3 codes of the clamped quotients of four 16-bit activation patterns
+// (h01: values 0, 1 in its halves; h23: values 2, 3), one byte each, by the
+// matrix-core generation's fp32 -> OCP E4M3 conversion (round to nearest
+// even; the same code as e4m3_code for every |q| <= 448, both signs,
+// subnormals included -- checked on the device over all such fp32 values).
+template <int DT>
+__device__ __forceinline__ uint32_t fp8_codes4(const Fp8Quotient<DT> &f, uint32_t h01, uint32_t h23) {
+    const float q0 = f.q(act_bits_to_f32<DT>(h01 & 0xFFFFu)), q1 = f.q(act_bits_to_f32<DT>(h01 >> 16));
+    const float q2 = f.q(act_bits_to_f32<DT>(h23 & 0xFFFFu)), q3 = f.q(act_bits_to_f32<DT>(h23 >> 16));
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+}
+
+// Sum of the values of four E4M3 codes (one a byte), in units of 2^-9.
+__device__ __forceinline__ int32_t e4m3_units4(uint32_t w) {
+    return e4m3_units(w & 0xFFu) + e4m3_units((w >> 8) & 0xFFu) + e4m3_units((w >> 16) & 0xFFu) +
+           e4m3_units(w >> 24);
+}
+
+// ---------------------------------------------------------------------------
 // Quantisation: one workgroup of 256 threads per row, two passes over the row
 // (abs-max, then codes).  The row sum of the codes' values is accumulated
 // exactly as an integer in units of 2^-9 and rounded once to fp32.
@@ -84,22 +136,37 @@ __global__ __launch_bounds__(256) void w4a8_fp8_quant(const uint16_t *__restrict
     mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
     const float amax = act_bits_to_f32<DT>(mx);
     const float s = round_act_f<DT>(amax / 448.0f);  // correctly rounded fp32 divide, then the activation type
+    const Fp8Quotient<DT> fq(s);
     long long sum = 0;
     auto code_of = [&](uint32_t h) -> uint32_t {
         if (s == 0.0f) return 0u;
+        if (!fq.exact_divide) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fq.q(act_bits_to_f32<DT>(h)), 0.0f, 0,
+                                                                              false) & 0xFFu;
         const float q = fminf(fmaxf(act_bits_to_f32<DT>(h) / s, -448.0f), 448.0f);
         return e4m3_code(q);
     };
-    for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
-        const u32x4 v = *(const u32x4 *)(row + k);
-        u32x2 o = {0, 0};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t c = code_of((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-            sum += e4m3_units(c);
-            o[e >> 2] |= c << (8 * (e & 3));
+    if (s != 0.0f && !fq.exact_divide) {
+        // (per thread at most 512 values of at most 229376 units: int32)
+        int32_t part = 0;
+        for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
+            const u32x4 v = *(const u32x4 *)(row + k);
+            const u32x2 o = {fp8_codes4<DT>(fq, v[0], v[1]), fp8_codes4<DT>(fq, v[2], v[3])};
+            part += e4m3_units4(o[0]) + e4m3_units4(o[1]);
+            *(u32x2 *)(out + k) = o;
         }
-        *(u32x2 *)(out + k) = o;
+        sum = part;
+    } else {
+        for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
+            const u32x4 v = *(const u32x4 *)(row + k);
+            u32x2 o = {0, 0};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t c = code_of((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                sum += e4m3_units(c);
+                o[e >> 2] |= c << (8 * (e & 3));
+            }
+            *(u32x2 *)(out + k) = o;
+        }
     }
     for (int k = K8 + threadIdx.x; k < K; k += 256) {
         const uint32_t c = code_of(row[k]);
@@ -146,23 +213,37 @@ __global__ __launch_bounds__(T) void w4a8_fp8_quant_rows(const uint16_t *__restr
 #pragma unroll
     for (int w = 1; w < T / 64; ++w) mx = max(mx, wmax[w]);
     const float s = round_act_f<DT>(act_bits_to_f32<DT>(mx) / 448.0f);
+    const Fp8Quotient<DT> fq(s);
     long long sum = 0;
+    if (!fq.exact_divide) {
+        int32_t part = 0;  // at most 8 NV values of at most 229376 units
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int k = 8 * (threadIdx.x + i * T);
-        if (k >= K) break;
-        u32x2 o = {0, 0};
-        if (s != 0.0f) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float q = fminf(fmaxf(act_bits_to_f32<DT>((v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) / s,
-                                            -448.0f), 448.0f);
-                const uint32_t c = e4m3_code(q);
-                sum += e4m3_units(c);
-                o[e >> 2] |= c << (8 * (e & 3));
-            }
+        for (int i = 0; i < NV; ++i) {
+            const int k = 8 * (threadIdx.x + i * T);
+            if (k >= K) break;
+            const u32x2 o = {fp8_codes4<DT>(fq, v[i][0], v[i][1]), fp8_codes4<DT>(fq, v[i][2], v[i][3])};
+            part += e4m3_units4(o[0]) + e4m3_units4(o[1]);
+            *(u32x2 *)(out + k) = o;
         }
-        *(u32x2 *)(out + k) = o;
+        sum = part;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int k = 8 * (threadIdx.x + i * T);
+            if (k >= K) break;
+            u32x2 o = {0, 0};
+            if (s != 0.0f) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float q = fminf(
+                        fmaxf(act_bits_to_f32<DT>((v[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu) / s, -448.0f), 448.0f);
+                    const uint32_t c = e4m3_code(q);
+                    sum += e4m3_units(c);
+                    o[e >> 2] |= c << (8 * (e & 3));
+                }
+            }
+            *(u32x2 *)(out + k) = o;
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
