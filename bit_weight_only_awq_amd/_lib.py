@@ -36,7 +36,7 @@ class PlanInfo(ctypes.Structure):
     """awq_plan_t: how the library would launch a call (awq_plan_info)."""
     _fields_ = [("kernel", ctypes.c_int), ("tiles_n", ctypes.c_int), ("tiles_m", ctypes.c_int),
                 ("splits", ctypes.c_int), ("row_tiles", ctypes.c_int), ("ksplit", ctypes.c_int),
-                ("cu_count", ctypes.c_int), ("workspace_bytes", ctypes.c_int64)]
+                ("cu_count", ctypes.c_int), ("workspace_bytes", ctypes.c_int64), ("tile_cols", ctypes.c_int)]
 
 
 class AWQError(RuntimeError):

@@ -35,22 +35,29 @@
 
 namespace awq4 {
 
-constexpr int GB_N = 128, GB_K = 64;
-constexpr int GA_PITCH = GB_K * 2;                 // 128 bytes per X row (8 segments of 16 B, swizzled)
-constexpr int GB_PITCH = (GB_N / 8) * 4;           // 64 bytes per k-row of packed words (16 words)
-constexpr int GB_WORDS = GB_K * GB_PITCH;          // 4096
-constexpr int GM_SCALES = 2 * GB_N * 2;            // scales of both k-steps: 2 x 128 x 2 B
-constexpr int GM_ZEROS = 2 * (GB_N / 8) * 4;       // zero words of both k-steps: 2 x 16 x 4 B
-constexpr int GB_BYTES = GB_WORDS + GM_SCALES + GM_ZEROS;  // 4736 per word/metadata buffer
-constexpr int kPrefA = 6;  // X operand reads run this many row tiles ahead of the MFMAs
+constexpr int GB_K = 64;
+constexpr int GA_PITCH = GB_K * 2;  // 128 bytes per X row (8 segments of 16 B, swizzled)
+constexpr int kPrefA = 6;           // X operand reads run this many row tiles ahead of the MFMAs
 
-// LDS ring of one group of 4 waves: AB X buffers of 16*MT rows, BB word buffers
-template <int MT, int AB, int BB>
+// LDS ring of one group of WN waves (side by side along N, 32 columns each):
+// AB X buffers of 16*MT rows, BB buffers of packed words with the stage's
+// scales and zero points
+template <int MT, int AB, int BB, int WN>
 struct GRing {
-    static constexpr int M_TILE = 16 * MT;               // workgroup tile rows
-    static constexpr int A_BYTES = M_TILE * GA_PITCH;    // one X buffer
-    static constexpr int LDS = AB * A_BYTES + BB * GB_BYTES;  // (16, 2, 3): 79744, two workgroups per CU
-    static constexpr int A_COPIES = M_TILE / 32;          // 8-row X copies per wave and stage
+    static constexpr int N_TILE = 32 * WN;                // workgroup tile columns
+    static constexpr int WC = N_TILE / 8;                 // word-columns per tile
+    static constexpr int B_PITCH = WC * 4;                // bytes per k-row of packed words
+    static constexpr int B_WORDS = GB_K * B_PITCH;
+    static constexpr int M_SCALES = 2 * N_TILE * 2;       // scales of both k-steps
+    static constexpr int M_ZEROS = 2 * WC * 4;            // zero words of both k-steps
+    static constexpr int B_BYTES = B_WORDS + M_SCALES + M_ZEROS;  // 4736 (WN = 4), 9472 (WN = 8)
+    static constexpr int B_ROWS = 1024 / B_PITCH;         // k-rows per 1 KB word copy (16 or 8)
+    static constexpr int M_TILE = 16 * MT;                // workgroup tile rows
+    static constexpr int A_BYTES = M_TILE * GA_PITCH;     // one X buffer
+    // (16, 2, 3, 4): 79744, two workgroups per CU; (16, 2, 3, 8): 93952, one
+    static constexpr int LDS = AB * A_BYTES + BB * B_BYTES;
+    static constexpr int A_COPIES = M_TILE / (8 * WN);    // 8-row X copies per wave and stage
+    static_assert(B_ROWS * WN == GB_K && A_COPIES * 8 * WN == M_TILE, "whole copies, one word copy per wave");
 };
 
 // X rows: 16-byte segment s of row r is stored at position s ^ (r & 7), so the
@@ -58,31 +65,37 @@ struct GRing {
 __device__ __forceinline__ int aseg(int r, int s) { return s ^ (r & 7); }
 // Packed words: segment s (4 words) of k-row r is stored at s ^ ((r>>3)&3):
 // one word read serves rows 8 apart (lane groups gq = 0..3), which then sit
-// in four different 16-byte segments, i.e. on disjoint banks.
+// in four different 16-byte segments, i.e. on disjoint banks (a k-row has 4
+// or 8 segments; the XOR stays inside them).
 __device__ __forceinline__ int bseg(int r, int s) { return s ^ ((r >> 3) & 3); }
 
 // Output columns of MFMA u relative to the lane's word-column (before + 2h).
 __host__ __device__ constexpr int gemm_col(int u) { return (u & 1) + ((u >> 1) << 2); }
 
-// KS = 2: the workgroup holds two groups of 4 waves that share the output
-// tile and split its K range (each with its own LDS ring); the groups trade
-// partial sums through LDS at the end.  This doubles the waves per SIMD for
-// layers with no more tiles than CUs.
-template <int DT, bool SYM, int KS, int MT, int AB, int BB>
-__global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *__restrict__ x,
+// WN = 4: 128-column tiles, two workgroups per CU; WN = 8: 256-column tiles
+// (one workgroup of 8 waves per CU), which halve the X bytes copied per
+// multiply-add.
+// KS = 2 (WN = 4 only): the workgroup holds two groups of 4 waves that share
+// the output tile and split its K range (each with its own LDS ring); the
+// groups trade partial sums through LDS at the end.  This doubles the waves
+// per SIMD for layers with no more tiles than CUs.
+template <int DT, bool SYM, int KS, int MT, int AB, int BB, int WN>
+__global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : 3 - KS) void w4a16_gemm(const uint16_t *__restrict__ x,
                                                                 const uint32_t *__restrict__ qw,
                                                                 const uint16_t *__restrict__ sc,
                                                                 const uint32_t *__restrict__ qz,
                                                                 uint16_t *__restrict__ y, uint64_t *__restrict__ acc64,
                                                                 int M, int N, int K, int G, int S) {
-    using R = GRing<MT, AB, BB>;
-    static_assert(KS == 1 || KS * R::LDS >= 2 * 4 * MT * 64 * 16, "the K-split handover fits in the rings");
+    using R = GRing<MT, AB, BB, WN>;
+    static_assert(KS == 1 || (WN == 4 && KS * R::LDS >= 2 * 4 * MT * 64 * 16), "the K-split handover fits in the rings");
     static_assert(AB >= 2 && BB >= 3 && MT > kPrefA, "ring depths and prefetch distance");
     constexpr int GB_M = R::M_TILE, GA_BYTES = R::A_BYTES, G_LDS = R::LDS;
+    constexpr int GB_N = R::N_TILE, GB_PITCH = R::B_PITCH, GB_WORDS = R::B_WORDS, GM_SCALES = R::M_SCALES;
+    constexpr int GB_BYTES = R::B_BYTES, WC = R::WC;
     __shared__ __attribute__((aligned(16))) unsigned char lds_all[KS * G_LDS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = KS == 1 ? 0 : (wv >> 2), wave = wv & 3;
+    const int grp = KS == 1 ? 0 : wv / WN, wave = wv % WN;
     unsigned char *const lds = lds_all + grp * G_LDS;
     unsigned char *const Abase = lds;
     unsigned char *const Bbase = lds + AB * GA_BYTES;
@@ -91,7 +104,7 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     // logical tile of this workgroup (XCD-aware order over the tiles_n x tiles_m grid)
     const int tile = tile_of_xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
     const int tn = tile % gridDim.x, tm = tile / gridDim.x, split = blockIdx.z;
-    const int m0 = tm * GB_M, wc0 = tn * (GB_N / 8);
+    const int m0 = tm * GB_M, wc0 = tn * WC;
     const int T = K / GB_K;
     // stages of this workgroup, then of this group: group 0 takes the first
     // ceil(n/2), group 1 the rest; both pass `iters` loop barriers (group 1
@@ -102,10 +115,11 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
 
     // Copy assignment (byte offsets from the workgroup's corner; all fit in
     // 32 bits: at most 256 X rows and 64 k-rows of words are addressed).
-    // X: wave w copies rows (GB_M/4) w + 8i + lane/8 (i < A_COPIES), lane%8
+    // X: wave w copies rows (GB_M/WN) w + 8i + lane/8 (i < A_COPIES), lane%8
     // being the stored segment position; rows past M repeat row M-1 (their
-    // outputs are never stored).  Words: wave w copies k-rows 16w + lane/4, lane%4 being
-    // the stored segment; word-columns past the end repeat the last 4.
+    // outputs are never stored).  Words: wave w copies k-rows B_ROWS w +
+    // lane/(WC/4), lane%(WC/4) being the stored segment; word-columns past
+    // the end repeat the last 4.
     const char *const xg = (const char *)(x + (size_t)m0 * K);
     const char *const wg = (const char *)(qw + wc0);
     // descriptors over the rest of X from row m0 and of the packed words from
@@ -116,47 +130,52 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     uint32_t xoff[R::A_COPIES];
 #pragma unroll
     for (int i = 0; i < R::A_COPIES; ++i) {
-        const int r = (GB_M / 4) * wave + 8 * i + (lane >> 3);
+        const int r = (GB_M / WN) * wave + 8 * i + (lane >> 3);
         const int m = min(m0 + r, M - 1);
         xoff[i] = (uint32_t)(((m - m0) * K + 8 * aseg(r, lane & 7)) * 2);
     }
     uint32_t woff;
     {
-        const int r = 16 * wave + (lane >> 2);
-        const int wc = min(wc0 + 4 * bseg(r, lane & 3), nw - 4);
+        const int r = R::B_ROWS * wave + lane / (WC / 4);
+        const int wc = min(wc0 + 4 * bseg(r, lane % (WC / 4)), nw - 4);
         woff = (uint32_t)((r * nw + wc - wc0) * 4);
     }
-    // Metadata (wave 0): lanes 0..31 copy 8 scales each (k-step lane/16,
-    // word-column wc0 + lane%16), lanes 32..39 copy 4 zero words each, through
-    // descriptors over the scale and zero-point arrays: the group of k-step 0
-    // of the stage is a scalar offset, the k-step's step past it (one group
-    // when G = 32) part of the lane's fixed offset.
+    // Metadata: 2 WC lanes copy 8 scales each (k-step lane/WC, word-column
+    // wc0 + lane%WC), WC/2 lanes 4 zero words each (k-step l/(WC/4), word-
+    // columns wc0 + 4 (l%(WC/4)) on), through descriptors over the scale and
+    // zero-point arrays: the group of k-step 0 of the stage is a scalar offset,
+    // the k-step's step past it (one group when G = 32) part of the lane's
+    // fixed offset.  WN = 4: wave 0, lanes 0..31 and 32..39 (the zero copy's
+    // LDS position follows from the lane number); WN = 8: wave 0 all lanes
+    // (scales), wave 1 lanes 0..15 (zero points).
     const __amdgpu_buffer_rsrc_t srs = buf_rsrc(sc, (int64_t)(K / G) * N * 2);
     const __amdgpu_buffer_rsrc_t zrs = buf_rsrc(SYM ? (const void *)sc : (const void *)qz, SYM ? 0 : (int64_t)(K / G) * nw * 4);
-    uint32_t m_voff;
-    if (lane < 32) {
-        const int meta_ks = lane >> 4, meta_col = min(wc0 + (lane & 15), nw - 1);
+    const bool zero_wave = WN == 8 ? wave == 1 : wave == 0;
+    const int zl = WN == 8 ? lane : lane - 2 * WC;  // zero-copy lane number
+    const bool scale_lane = wave == 0 && lane < 2 * WC;
+    const bool zero_lane = !SYM && zero_wave && zl >= 0 && zl < WC / 2;
+    uint32_t m_voff = 0;
+    if (scale_lane) {
+        const int meta_ks = lane / WC, meta_col = min(wc0 + lane % WC, nw - 1);
         m_voff = (uint32_t)((((32 * meta_ks) >> lg) * N + 8 * meta_col) * 2);
-    } else {
-        const int meta_ks = (lane - 32) >> 2, meta_col = min(wc0 + 4 * ((lane - 32) & 3), nw - 4);
+    } else if (zero_lane) {
+        const int meta_ks = zl / (WC / 4), meta_col = min(wc0 + 4 * (zl % (WC / 4)), nw - 4);
         m_voff = (uint32_t)((((32 * meta_ks) >> lg) * nw + meta_col) * 4);
     }
 
     // copies of stage st into X buffer / word buffer `buf`
     auto copyA = [&](int st, int buf) {
-        unsigned char *dst = Abase + buf * GA_BYTES + (GB_M / 4) * wave * GA_PITCH;
+        unsigned char *dst = Abase + buf * GA_BYTES + (GB_M / WN) * wave * GA_PITCH;
 #pragma unroll
         for (int i = 0; i < R::A_COPIES; ++i)
             dma16_buf(xrs, xoff[i], (uint32_t)st * (GB_K * 2), dst + 8 * i * GA_PITCH);
     };
     auto copyB = [&](int st, int buf) {
         unsigned char *dst = Bbase + buf * GB_BYTES;
-        dma16_buf(wrs, woff, (uint32_t)st * (GB_K * 4) * (uint32_t)nw, dst + 16 * wave * GB_PITCH);
-        if (wave == 0) {
-            const uint32_t g0 = (uint32_t)((st * GB_K) >> lg);
-            if (lane < 32) dma16_buf(srs, m_voff, g0 * (uint32_t)N * 2, dst + GB_WORDS);
-            else if (!SYM && lane < 40) dma16_buf(zrs, m_voff, g0 * (uint32_t)nw * 4, dst + GB_WORDS);
-        }
+        dma16_buf(wrs, woff, (uint32_t)st * (GB_K * 4) * (uint32_t)nw, dst + R::B_ROWS * wave * GB_PITCH);
+        const uint32_t g0 = (uint32_t)((st * GB_K) >> lg);
+        if (scale_lane) dma16_buf(srs, m_voff, g0 * (uint32_t)N * 2, dst + GB_WORDS);
+        else if (zero_lane) dma16_buf(zrs, m_voff, g0 * (uint32_t)nw * 4, dst + (WN == 8 ? GB_WORDS + GM_SCALES : GB_WORDS));
     };
 
     f32x4 acc[MT][2];
@@ -250,11 +269,23 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
         return *(const u32x4 *)(A + r * GA_PITCH + aseg(r, 4 * ks + gq) * 16);
     };
 
-    // copies a stage leaves in flight at its end: those issued after the
+    // Every wave issues its copies at the top of each stage (X AB - 1 and
+    // words BB - 1 stages ahead).  (Measured alternatives, for 8 waves per
+    // CU: a vector-memory instruction waiting to issue also holds up the
+    // matrix-core issue of its SIMD, so the burst costs about 10 cycles per
+    // 1 KB copy on the CU; copies spread between the matrix-core instructions
+    // stalled them longer -- gate/up at M = 2048 1017 -> 915 TFLOP/s --
+    // and copies issued by half the waves after their last matrix-core
+    // instruction, with rings one stage deeper, gained nothing: the other
+    // half cannot keep the matrix cores busy alone.)
+    // Copies a stage leaves in flight at its end: those issued after the
     // latest copy the next stage reads -- X of st + 1, issued at st + 2 - AB,
     // or the words of st + 2 (read by its second k-step), issued at
-    // st + 3 - BB; within a stage X is issued first
-    constexpr int kA = R::A_COPIES, kB0 = SYM ? 2 : 3;  // wave 0 also copies the scales and zero points
+    // st + 3 - BB; within a stage X is issued first.  The metadata waves
+    // (wave 0; WN = 8 with zero points: waves 0 and 1) issue one more copy
+    // per stage (wave 0 with WN = 4 and zero points: two).
+    constexpr int kA = R::A_COPIES, kB0 = WN == 8 ? 2 : (SYM ? 2 : 3);
+    const bool meta_wave = wave == 0 || (WN == 8 && !SYM && wave == 1);
     constexpr int kSa = 2 - AB, kSb = 3 - BB;            // issue stages relative to st
     constexpr int kFlight0 = kSa > kSb ? kB0 + (-kSa) * (kA + kB0) : (-kSb) * (kA + kB0);
     constexpr int kFlight1 = kSa > kSb ? 1 + (-kSa) * (kA + 1) : (-kSb) * (kA + 1);
@@ -279,8 +310,10 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     }
     for (int st = s_lo; st < s_hi; ++st) {
         const int rel = st - s_lo;
-        copyA(min(st + AB - 1, s_hi - 1), (rel + AB - 1) % AB);
-        copyB(min(st + BB - 1, s_hi - 1), (rel + BB - 1) % BB);
+        const int ast = min(st + AB - 1, s_hi - 1), abuf = (rel + AB - 1) % AB;
+        const int bst = min(st + BB - 1, s_hi - 1), bbuf = (rel + BB - 1) % BB;
+        copyA(ast, abuf);
+        copyB(bst, bbuf);
         const unsigned char *A = Abase + (rel % AB) * GA_BYTES;
         u32x4 a[MT];
 #pragma unroll
@@ -313,7 +346,7 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
             bc[0] = bn[0];
             bc[1] = bn[1];
         }
-        if (wave == 0)
+        if (meta_wave)
             __builtin_amdgcn_s_waitcnt(0x0F70 | (kFlight0 & 15) | ((kFlight0 >> 4) << 14));
         else
             __builtin_amdgcn_s_waitcnt(0x0F70 | (kFlight1 & 15) | ((kFlight1 >> 4) << 14));
@@ -442,32 +475,37 @@ __global__ __launch_bounds__(256 * KS, 3 - KS) void w4a16_gemm(const uint16_t *_
     }
 }
 
-template <int DT, bool SYM, int KS, int MT, int AB, int BB>
+template <int DT, bool SYM, int KS, int MT, int AB, int BB, int WN>
 static hipError_t launch_gemm_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
-    hipLaunchKernelGGL((w4a16_gemm<DT, SYM, KS, MT, AB, BB>), grid, dim3(256 * KS), 0, st, (const uint16_t *)a.x,
+    hipLaunchKernelGGL((w4a16_gemm<DT, SYM, KS, MT, AB, BB, WN>), grid, dim3(64 * WN * KS), 0, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
                        (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
     return hipGetLastError();
 }
 
-template <int KS, int MT, int AB, int BB>
+template <int KS, int MT, int AB, int BB, int WN>
 static hipError_t launch_gemm_ks(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     const bool sym = a.qzeros == nullptr;
     if (a.dtype == DT_F16)
-        return sym ? launch_gemm_t<DT_F16, true, KS, MT, AB, BB>(a, p, st)
-                   : launch_gemm_t<DT_F16, false, KS, MT, AB, BB>(a, p, st);
-    return sym ? launch_gemm_t<DT_BF16, true, KS, MT, AB, BB>(a, p, st)
-               : launch_gemm_t<DT_BF16, false, KS, MT, AB, BB>(a, p, st);
+        return sym ? launch_gemm_t<DT_F16, true, KS, MT, AB, BB, WN>(a, p, st)
+                   : launch_gemm_t<DT_F16, false, KS, MT, AB, BB, WN>(a, p, st);
+    return sym ? launch_gemm_t<DT_BF16, true, KS, MT, AB, BB, WN>(a, p, st)
+               : launch_gemm_t<DT_BF16, false, KS, MT, AB, BB, WN>(a, p, st);
 }
 
-// 256-row (p.mt = 16) or 128-row (p.mt = 8) tiles with rings of 2 X and 3
-// word buffers
+// 256-row (p.mt = 16) or 128-row (p.mt = 8) tiles, 128 columns wide
+// (p.wn = 4) or, for 256-row tiles without a K-split group, 256 (p.wn = 8);
+// rings of 2 X and 3 word buffers
 hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     // a K split reduces through the workspace
     if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
-    if (p.mt == 8) return p.ksplit == 2 ? launch_gemm_ks<2, 8, 2, 3>(a, p, st) : launch_gemm_ks<1, 8, 2, 3>(a, p, st);
-    return p.ksplit == 2 ? launch_gemm_ks<2, 16, 2, 3>(a, p, st) : launch_gemm_ks<1, 16, 2, 3>(a, p, st);
+    if (p.wn == 8) {
+        if (p.mt != 16 || p.ksplit != 1) return hipErrorInvalidValue;
+        return launch_gemm_ks<1, 16, 2, 3, 8>(a, p, st);
+    }
+    if (p.mt == 8) return p.ksplit == 2 ? launch_gemm_ks<2, 8, 2, 3, 4>(a, p, st) : launch_gemm_ks<1, 8, 2, 3, 4>(a, p, st);
+    return p.ksplit == 2 ? launch_gemm_ks<2, 16, 2, 3, 4>(a, p, st) : launch_gemm_ks<1, 16, 2, 3, 4>(a, p, st);
 }
 
 }  // namespace awq4

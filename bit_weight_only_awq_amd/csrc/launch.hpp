@@ -29,6 +29,7 @@ struct W4A16Plan {
     int waves;    // decode: waves per workgroup (4)
     int mt;       // tiled: row tiles per wave (1, 2, 4); LDS GEMM: 16 or 8
     int ksplit;   // LDS GEMM: groups of 4 waves per workgroup splitting K (1, 2)
+    int wn;       // LDS GEMM: waves along N, 32 columns each (4: 128-column tiles, 8: 256)
     int tiles_n;  // grid x
     int tiles_m;  // tiled: grid y
     int splits;   // workgroups along K (1 = none); decode: grid y

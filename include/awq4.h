@@ -178,6 +178,8 @@ typedef struct {
     int ksplit;    /* wave groups splitting K inside one workgroup (1 or 2) */
     int cu_count;  /* the compute-unit count the plan was made for */
     int64_t workspace_bytes;
+    int tile_cols; /* LDS-pipelined GEMMs: output columns per workgroup tile (128 or 256);
+                      0 for the other kernels */
 } awq_plan_t;
 int awq_plan_info(int op, int64_t M, int64_t N, int64_t K, int group_size, int split_k, int cu_count,
                   awq_plan_t *out);

@@ -219,18 +219,26 @@ def test_plan_sizes_grids_from_the_cu_count():
     MI355X (256 CUs) and a quarter of one (64 CUs) get different plans, each
     filling its own device."""
     gemm, gemv, w8 = L.AWQ_OP_GEMM_W4A16, L.AWQ_OP_GEMV_W4A16, L.AWQ_OP_W4A8_GEMM
-    # M = 1024 on 4096 x 4096: 128 tiles of 256 rows would leave half of 256
+    # M = 1024 on 4096 x 4096: 128 tiles of 256 x 128 would leave half of 256
     # CUs idle, so 128-row tiles (256 of them, K split inside the workgroup);
-    # on 64 CUs the 256-row tiles already fill the device twice over
+    # on 64 CUs 256 x 256 tiles already give every CU one (64 of them)
     big, small = _plan(gemm, 1024, 4096, 4096, cus=256), _plan(gemm, 1024, 4096, 4096, cus=64)
     assert (big.kernel, small.kernel) == (3, 3)
     assert big.cu_count == 256 and small.cu_count == 64
-    assert big.row_tiles == 8 and big.tiles_n * big.tiles_m == 256 and big.ksplit == 2
-    assert small.row_tiles == 16 and small.tiles_n * small.tiles_m == 128 and small.ksplit == 1
-    # M = 2048: 256 tiles of 256 rows; one per CU on 256 CUs (two wave groups
-    # split K inside each), four per CU on 64 CUs (no in-workgroup split)
+    assert big.row_tiles == 8 and big.tile_cols == 128 and big.tiles_n * big.tiles_m == 256 and big.ksplit == 2
+    assert small.row_tiles == 16 and small.tile_cols == 256 and small.tiles_n * small.tiles_m == 64
+    assert small.ksplit == 1
+    # M = 2048: 256 tiles of 256 x 128, one per CU on 256 CUs (two wave groups
+    # split K inside each); on 64 CUs two tiles of 256 x 256 per CU
     big, small = _plan(gemm, 2048, 4096, 4096, cus=256), _plan(gemm, 2048, 4096, 4096, cus=64)
-    assert big.row_tiles == 16 and big.ksplit == 2 and small.row_tiles == 16 and small.ksplit == 1
+    assert big.row_tiles == 16 and big.ksplit == 2 and big.tile_cols == 128
+    assert small.row_tiles == 16 and small.ksplit == 1 and small.tile_cols == 256
+    # 256 x 256 tiles wherever more than half the CUs get one: (4096, 14336)
+    # at M = 2048 has 448 of them; an explicit K split keeps 128 columns
+    wide = _plan(gemm, 2048, 14336, 4096, cus=256)
+    assert (wide.tile_cols, wide.tiles_n, wide.tiles_m, wide.splits, wide.ksplit) == (256, 56, 8, 1, 1)
+    assert _plan(gemm, 2048, 14336, 4096, split=2).tile_cols == 128
+    assert _plan(gemm, 4, 4096, 4096, cus=256).tile_cols == 0
     # decode GEMV at M = 1 on 4096 x 4096: 32-k chunks while they give at most
     # two workgroups per CU -- on 64 CUs the grid stays at 64-k chunks
     big, small = _plan(gemv, 1, 4096, 4096, cus=256), _plan(gemv, 1, 4096, 4096, cus=64)

@@ -72,7 +72,7 @@ def test_target_shapes(M, K, N):
 @pytest.mark.parametrize("sym", [False, True])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("G", [32, 64, 128])
-@pytest.mark.parametrize("M", [1, 512])
+@pytest.mark.parametrize("M", [1, 512, 1024])
 def test_group_dtype_sym_variants(M, G, dtype, sym):
     c = synthgen.w4a16_case(M, 4096, 14336, G, dtype=dtype, sym=sym)
     rows = None if M == 1 else sample_rows(M, seed=G)
@@ -115,16 +115,18 @@ def test_exact_special_case_bit_identical():
                 assert torch.equal(y.cpu(), exp), (M, K, N, entry, split)
 
 
-# (M, K, N, split_k, expected plan: row tiles, wave groups splitting K, K splits)
+# (M, K, N, split_k, expected plan: row tiles, wave groups splitting K, K
+# splits, tile columns)
 MAIN_TILE_CASES = [
-    (2048, 4096, 8192, 0, (16, 1, 1)),   # 512 tiles of 256 x 128: the large-M configuration
-    (2048, 4096, 4096, 0, (16, 2, 1)),   # 256 tiles: two wave groups split K in the workgroup
-    (2048, 4096, 8192, 2, (16, 1, 2)),   # K split through partial tiles
-    (2048, 4096, 4096, 3, (16, 1, 3)),   # three splits, 64 stages (uneven)
-    (1024, 4096, 4096, 0, (8, 2, 1)),    # 128-row tiles where 256-row ones would leave CUs idle
-    (512, 14336, 4096, 0, (8, 2, 2)),    # K = 14336: K split and in-workgroup split together
-    (96, 4096, 4096, 0, (8, 2, 4)),      # below 128 rows: 128-row tiles, K split both ways
-    (100, 4096, 6144, 0, (8, 2, 2)),     # the same with a ragged last row tile
+    (2048, 4096, 8192, 0, (16, 1, 1, 256)),  # 256 tiles of 256 x 256: the large-M configuration
+    (2200, 4096, 4384, 0, (16, 1, 1, 256)),  # the same, ragged: last row tile 152 rows, last column tile 32
+    (2048, 4096, 4096, 0, (16, 2, 1, 128)),  # 256 tiles of 256 x 128: two wave groups split K in the workgroup
+    (2048, 4096, 8192, 2, (16, 1, 2, 128)),  # K split through partial tiles
+    (2048, 4096, 4096, 3, (16, 1, 3, 128)),  # three splits, 64 stages (uneven)
+    (1024, 4096, 4096, 0, (8, 2, 1, 128)),   # 128-row tiles where 256-row ones would leave CUs idle
+    (512, 14336, 4096, 0, (8, 2, 2, 128)),   # K = 14336: K split and in-workgroup split together
+    (96, 4096, 4096, 0, (8, 2, 4, 128)),     # below 128 rows: 128-row tiles, K split both ways
+    (100, 4096, 6144, 0, (8, 2, 2, 128)),    # the same with a ragged last row tile
 ]
 
 
@@ -138,7 +140,8 @@ def test_exact_special_case_main_tiles(M, K, N, split, plan, dtype):
     tile), all columns."""
     info = awq.plan_info(awq.AWQ_OP_GEMM_W4A16, M, N, K, 128, split)
     if info["cu_count"] == 256:
-        assert info["kernel"] == 3 and (info["row_tiles"], info["ksplit"], info["splits"]) == plan, info
+        assert info["kernel"] == 3, info
+        assert (info["row_tiles"], info["ksplit"], info["splits"], info["tile_cols"]) == plan, info
     tdt = torch.float16 if dtype == "f16" else torch.bfloat16
     g = torch.Generator().manual_seed(M * 7 + N + split)
     X = torch.randint(-1, 2, (M, K), generator=g).to(tdt)
