@@ -236,20 +236,19 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         p.tiles_m = (int)cdiv(M, 16 * p.mt);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         const int64_t stages = K / 64;
-        int64_t s;
-        if (M <= 128) {
-            // few rows: the partial tiles are small, split by the tile count
-            s = tiles <= 32 ? 4 : tiles <= 64 ? 2 : 1;
-            s = std::min<int64_t>(s, std::max<int64_t>(1, stages / 4));
-        } else {
-            // K splits only for few tiles and long K: about one per 56 stages,
-            // at most 4 (<= 64 tiles) or 2 (<= 128 tiles).  Measured at
-            // M = 192..1024 on the Llama-3-8B layers: each split's partial
-            // tile, summed by one workgroup, costs more than it gains on
-            // K = 4096 and pays for itself on K = 14336.
-            const int64_t cap = tiles <= cus / 4 ? 4 : tiles <= cus / 2 ? 2 : 1;
-            s = std::min<int64_t>(cap, std::max<int64_t>(1, stages / 56));
-        }
+        // K splits fill the CUs: about one workgroup (two wave groups) per CU,
+        // at most one split per 16 stages and 8 in all; where that leaves
+        // one split, long K (>= 128 stages) on 128-row tiles, at most one
+        // tile per CU, still takes 3-4 splits of single-group workgroups.
+        // Measured on the Llama-3-8B layers at M = 96..4096 (explicit splits
+        // 1..8): M = 256 qkv 40 -> 32 us (2 splits), o 38 -> 27 us (4),
+        // M = 96 down 115 -> 39 us (8), M = 768 down 136 -> 107 us and
+        // M = 1024 down 145 -> 136 us (4 and 3, single group); 256-row tiles
+        // at M = 2048 gain nothing from them (down 239 vs 245 us).
+        const int64_t smax = std::min<int64_t>(8, std::max<int64_t>(1, stages / 16));
+        int64_t s = std::min<int64_t>(smax, std::max<int64_t>(1, cus / tiles));
+        if (s == 1 && p.mt == 8 && stages >= 128 && tiles <= cus)
+            s = std::min<int64_t>(4, std::max<int64_t>(1, 3 * cus / tiles));
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
         // no more workgroups than CUs: two wave groups per workgroup split K

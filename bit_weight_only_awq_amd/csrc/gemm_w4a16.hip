@@ -358,12 +358,14 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : 3 - KS) void w4a16_gemm
 
     // Epilogue: lane holds rows m0 + 16mt + 4gq + r and columns 8*wcol + 2pi
     // (MFMA 0) and 8*wcol + 2pi + 1 (MFMA 1).  Without a K split it writes the
-    // output; with one, each split stores its partial tile and the tile's last
-    // split sums them in split order (device.hpp).
+    // output; with one, each split stores its partial tile as column pairs
+    // with agent-scope atomic stores and the tile's last split sums them in
+    // split order (split_tile_last_atomic: no cache write-back fences, which
+    // cost more than the split saved).
     const int n0 = 8 * wcol + 2 * pi;
     uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
-    float *const part = (float *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
-    const size_t slot = (size_t)M * N;
+    uint64_t *const part = (uint64_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N / 2;  // column pairs per split
     auto emit = [&](int mt) {
         if (!col_ok) return;
 #pragma unroll
@@ -374,61 +376,79 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : 3 - KS) void w4a16_gemm
                 *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(acc[mt][0][r], DT) |
                                                         ((uint32_t)f32_to_out_bits(acc[mt][1][r], DT) << 16);
             else
-                *(f32x2 *)(part + split * slot + (size_t)m * N + n0) = (f32x2){acc[mt][0][r], acc[mt][1][r]};
+                __hip_atomic_store(part + split * slot + ((size_t)m * N + n0) / 2,
+                                   pack_f32x2(make_float2(acc[mt][0][r], acc[mt][1][r])), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     };
     // The tile's last split sums the S partials of row tiles LO..LO+NT-1 in
-    // split order, four row tiles (16 of the lane's rows) at a time: for each
-    // split the loads of those rows are in flight together (S memory round
-    // trips per batch rather than one per row and split); the partials are
-    // cleared after the batch's last load.
-    auto finish4 = [&](auto lo_c) {
+    // split order, two row tiles (8 of the lane's rows) at a time: the loads
+    // of four splits for those rows are in flight together (one memory round
+    // trip per four splits and pair of row tiles; the +0 terms that pad the
+    // last batch leave every sum unchanged), then the partials are cleared.
+    constexpr int kFB = 4;  // splits per batch of loads
+    auto finish2 = [&](auto lo_c) {
         constexpr int LO = decltype(lo_c)::value;
-        f32x2 v[4][4];
+        f32x2 v[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[i][r] = (f32x2){0.f, 0.f};
-        for (int sp = 0; sp < S; ++sp) {
-            const float *base = part + sp * slot + n0;
+            for (int r = 0; r < 4; ++r) v[t][r] = (f32x2){0.f, 0.f};
+        for (int s0 = 0; s0 < S; s0 += kFB) {
+            uint64_t b[kFB][2][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kFB; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + 16 * (LO + i) + 4 * gq + r;
-                    if (m < M) v[i][r] += *(const f32x2 *)(base + (size_t)m * N);
-                }
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = m0 + 16 * (LO + t) + 4 * gq + r;
+                        b[i][t][r] = s0 + i < S && m < M
+                                         ? __hip_atomic_load(part + (s0 + i) * slot + ((size_t)m * N + n0) / 2,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                         : 0ull;
+                    }
+#pragma unroll
+            for (int i = 0; i < kFB; ++i)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float2 f = unpack_f32x2(b[i][t][r]);
+                        v[t][r] += (f32x2){f.x, f.y};
+                    }
         }
         for (int sp = 0; sp < S; ++sp) {
-            float *base = part + sp * slot + n0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + 16 * (LO + i) + 4 * gq + r;
-                    if (m < M) *(f32x2 *)(base + (size_t)m * N) = (f32x2){0.f, 0.f};
+                    const int m = m0 + 16 * (LO + t) + 4 * gq + r;
+                    if (m < M)
+                        __hip_atomic_store(part + sp * slot + ((size_t)m * N + n0) / 2, 0ull, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
                 }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * (LO + i) + 4 * gq + r;
+                const int m = m0 + 16 * (LO + t) + 4 * gq + r;
                 if (m < M)
-                    *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(v[i][r][0], DT) |
-                                                            ((uint32_t)f32_to_out_bits(v[i][r][1], DT) << 16);
+                    *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(v[t][r][0], DT) |
+                                                            ((uint32_t)f32_to_out_bits(v[t][r][1], DT) << 16);
             }
     };
     auto finish = [&](auto lo_c, auto nt_c) {
         constexpr int LO = decltype(lo_c)::value, NT = decltype(nt_c)::value;
-        static_assert(NT % 4 == 0, "row tiles in batches of four");
+        static_assert(NT % 2 == 0, "row tiles in pairs");
         if (!col_ok) return;
-        static_for<NT / 4>([&](auto bc) { finish4(std::integral_constant<int, LO + 4 * decltype(bc)::value>{}); });
+        static_for<NT / 2>([&](auto bc) { finish2(std::integral_constant<int, LO + 2 * decltype(bc)::value>{}); });
     };
     if (KS == 1) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) emit(mt);
-        if (S > 1 && split_tile_last(cnt, S)) finish(std::integral_constant<int, 0>{}, std::integral_constant<int, MT>{});
+        if (S > 1 && split_tile_last_atomic(cnt, S)) finish(std::integral_constant<int, 0>{}, std::integral_constant<int, MT>{});
         return;
     }
     // group 1's idle iteration (odd stage count): its barrier only
@@ -469,7 +489,7 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : 3 - KS) void w4a16_gemm
             emit(H + mt);
         }
     }
-    if (S > 1 && split_tile_last(cnt, S)) {
+    if (S > 1 && split_tile_last_atomic(cnt, S)) {
         if (grp == 0) finish(std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
         else finish(std::integral_constant<int, H>{}, std::integral_constant<int, H>{});
     }
