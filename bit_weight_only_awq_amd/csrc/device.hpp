@@ -298,47 +298,25 @@ __device__ __forceinline__ bool splitk_contribute(uint64_t *acc, int64_t value, 
 // Split-K by partial tiles, for the GEMM kernels: their outputs have far too
 // many elements for one device-scope atomic each.  Workspace layout: one
 // uint32 arrival counter per output tile (rounded up to 256 bytes), then fp32
-// partials [S][M][N]; all zero between calls.
+// or int32 partials [S][M][N]; all zero between calls.
 //
 // Per workgroup: every thread stores its partial elements of the tile into
-// slot `split`; split_tile_last() then (after a barrier, which waits for
-// every store of the workgroup) releases them at device scope and counts the
-// tile's arrival with one atomic.  The workgroup that completes the count
-// acquires and returns true: it sums, for each of its elements, the S
-// partials in split order (so the result does not depend on which split
-// arrives last), writes the output and zeroes every partial of the tile; the
-// counter is re-armed at once.  Only this one atomic per workgroup and two
-// fences are needed, against one atomic per output element and split.
+// slot `split` with agent-scope atomic stores, which go through to the
+// device-wide coherence point themselves; split_tile_last_atomic() then waits
+// until every store of the workgroup has completed and counts the tile's
+// arrival with one atomic.  The workgroup that completes the count returns
+// true: it reads the partials with agent-scope atomic loads (issued after it
+// has seen the count, through the barrier), which do not read stale L2
+// lines, sums them for each of its elements in split order (so the result
+// does not depend on which split arrives last), writes the output and zeroes
+// every partial of the tile; the counter is re-armed at once.  One atomic per
+// workgroup, against one per output element and split, and no fence: an
+// agent-scope release fence writes back the issuing XCD's whole L2 (the
+// write-back plain stores would need before other XCDs could read them), and
+// one per workgroup measured several times the kernels' own time -- 4-5x on
+// a ~1000-workgroup decode launch, and more than a K split saves in the GEMMs.
 // (The workspace sizes, split_counters_bytes / split_tiles_bytes, are in
 // launch.hpp, shared with the host-side planner.)
-
-__device__ __forceinline__ bool split_tile_last(uint32_t *cnt, int S) {
-    __shared__ uint32_t last_flag;
-    __syncthreads();  // every partial store of the workgroup has completed
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t last = old == (uint32_t)(S - 1) ? 1u : 0u;
-        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = last;
-    }
-    __syncthreads();
-    const bool last = last_flag != 0;
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return last;
-}
-
-// The same completion for partials exchanged only through agent-scope atomic
-// stores and loads, for launches with many workgroups (the decode GEMV).
-// An agent-scope release fence writes back the issuing XCD's whole L2 (the
-// write-back of plain stores that other XCDs must see); one per workgroup of
-// a ~1000-workgroup decode launch measured 4-5x the kernel's own time.
-// Agent-scope atomic stores go through to the device-wide coherence point
-// themselves, so here each thread only waits until its own partial stores
-// have completed before the workgroup's counting atomic, and the workgroup
-// that completes the count reads the partials with agent-scope atomic loads
-// (issued after it has seen the count, through the barrier), which do not
-// read stale L2 lines.
 __device__ __forceinline__ bool split_tile_last_atomic(uint32_t *cnt, int S) {
     __shared__ uint32_t last_flag;
     wait_vm_all();    // this thread's partial stores have completed
@@ -351,6 +329,57 @@ __device__ __forceinline__ bool split_tile_last_atomic(uint32_t *cnt, int S) {
     }
     __syncthreads();
     return last_flag != 0;
+}
+
+// Partial tiles of 16-byte vectors (4 int32 or 4 fp32) for the exchange
+// above: each vector moves as two 64-bit agent-scope atomics (p 8-byte
+// aligned).  part_sum adds, in split order, the S partials of R vectors
+// (addr(s, i) = the uint64_t address of vector i of split s; vectors with
+// !valid(i) are skipped and left zero), with the loads of kB splits in
+// flight together (four unless a kernel's register budget asks for fewer):
+// one memory round trip per kB splits rather than one per split.  The +0 terms that pad the last batch change no sum: the running
+// sums start at +0 and so are never -0.  part_clear_all then zeroes every
+// partial read, which leaves the workspace as the next call expects it.
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+template <typename V>
+__device__ __forceinline__ void part_put(uint64_t *p, V v) {
+    const u64x2 w = bit_as<u64x2>(v);
+    __hip_atomic_store(p, w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 1, w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V part_get(uint64_t *p) {
+    u64x2 w;
+    w[0] = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w[1] = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return bit_as<V>(w);
+}
+template <int R, int kB = 4, typename V, typename Addr, typename Valid>
+__device__ __forceinline__ void part_sum(V (&v)[R], int S, Addr addr, Valid valid) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) v[i] = V{};
+    for (int s0 = 0; s0 < S; s0 += kB) {
+        V b[kB][R];
+#pragma unroll
+        for (int k = 0; k < kB; ++k)
+#pragma unroll
+            for (int i = 0; i < R; ++i) b[k][i] = s0 + k < S && valid(i) ? part_get<V>(addr(s0 + k, i)) : V{};
+#pragma unroll
+        for (int k = 0; k < kB; ++k)
+#pragma unroll
+            for (int i = 0; i < R; ++i) v[i] += b[k][i];
+    }
+}
+template <int R, typename Addr, typename Valid>
+__device__ __forceinline__ void part_clear_all(int S, Addr addr, Valid valid) {
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+            if (valid(i)) {
+                uint64_t *p = addr(s, i);
+                __hip_atomic_store(p, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(p + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
 }
 
 }  // namespace awq4

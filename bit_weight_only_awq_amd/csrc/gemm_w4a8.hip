@@ -291,60 +291,35 @@ __global__ __launch_bounds__(64 * NW * KS, 2 / KS) void w4a8_gemm_lds(const int8
             }
         return;
     }
-    // Split-K by partial tiles (device.hpp); int32 partials, so the sum is
-    // exact in any order.
+    // Split-K by partial tiles exchanged through agent-scope atomics
+    // (device.hpp); int32 partials, so the sum is exact in any order.
     uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
-    int32_t *const part = (int32_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
-    const size_t slot = (size_t)M * N;
+    uint64_t *const part = (uint64_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N / 2;  // 64-bit words per split
+    auto at = [&](int sp, int m) { return part + sp * slot + ((size_t)m * N + nc) / 2; };
     if (col_ok) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-                if (m < M)
-                    *(i32x4 *)(part + split * slot + (size_t)m * N + nc) =
-                        (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                if (m < M) part_put(at(split, m), (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
             }
     }
-    if (!split_tile_last(cnt, S) || !col_ok) return;
-    // the last split sums the partials, one row tile (4 of the lane's rows)
-    // at a time: per split, the loads of those rows are in flight together;
-    // the partials are cleared after the batch's last load
+    if (!split_tile_last_atomic(cnt, S) || !col_ok) return;
+    // the last split sums the partials one row tile (4 of the lane's rows)
+    // at a time, then clears them
     static_for<4>([&](auto bc) {
         constexpr int MT0 = decltype(bc)::value;
-        i32x4 v[1][4];
+        auto row = [&](int r) { return m0 + wm * 64 + 16 * MT0 + 4 * gq + r; };
+        auto addr = [&](int sp, int r) { return at(sp, row(r)); };
+        auto valid = [&](int r) { return row(r) < M; };
+        i32x4 v[4];
+        part_sum<4, 1>(v, S, addr, valid);
+        part_clear_all<4>(S, addr, valid);
 #pragma unroll
-        for (int h = 0; h < 1; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[h][r] = (i32x4){0, 0, 0, 0};
-        for (int sp = 0; sp < S; ++sp) {
-            const int32_t *base = part + sp * slot + nc;
-#pragma unroll
-            for (int h = 0; h < 1; ++h)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + wm * 64 + 16 * (MT0 + h) + 4 * gq + r;
-                    if (m < M) v[h][r] += *(const i32x4 *)(base + (size_t)m * N);
-                }
-        }
-        for (int sp = 0; sp < S; ++sp) {
-            int32_t *base = part + sp * slot + nc;
-#pragma unroll
-            for (int h = 0; h < 1; ++h)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + wm * 64 + 16 * (MT0 + h) + 4 * gq + r;
-                    if (m < M) *(i32x4 *)(base + (size_t)m * N) = (i32x4){0, 0, 0, 0};
-                }
-        }
-#pragma unroll
-        for (int h = 0; h < 1; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + 16 * (MT0 + h) + 4 * gq + r;
-                if (m < M) store4(m, v[h][r]);
-            }
+        for (int r = 0; r < 4; ++r)
+            if (valid(r)) store4(row(r), v[r]);
     });
 }
 

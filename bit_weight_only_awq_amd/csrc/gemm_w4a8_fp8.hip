@@ -201,49 +201,34 @@ __global__ __launch_bounds__(64 * F8_NW, 1) void w4a8_fp8_gemm_lds(const uint8_t
             }
         return;
     }
-    // Split-K by partial tiles (device.hpp), fp32, summed in split order.
+    // Split-K by partial tiles exchanged through agent-scope atomics
+    // (device.hpp), fp32, summed in split order.
     uint32_t *const cnt = (uint32_t *)ws + (tn + gridDim.x * tm);
-    float *const part = (float *)((char *)ws + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
-    const size_t slot = (size_t)M * N;
+    uint64_t *const part = (uint64_t *)((char *)ws + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N / 2;  // 64-bit words per split
+    auto at = [&](int sp, int m) { return part + sp * slot + ((size_t)m * N + nc) / 2; };
     if (col_ok) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-                if (m < M)
-                    *(f32x4 *)(part + split * slot + (size_t)m * N + nc) =
-                        (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                if (m < M) part_put(at(split, m), (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
             }
     }
-    if (!split_tile_last(cnt, S) || !col_ok) return;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    if (!split_tile_last_atomic(cnt, S) || !col_ok) return;
+    static_for<4>([&](auto bc) {
+        constexpr int MT0 = decltype(bc)::value;
+        auto row = [&](int r) { return m0 + wm * 64 + 16 * MT0 + 4 * gq + r; };
+        auto addr = [&](int sp, int r) { return at(sp, row(r)); };
+        auto valid = [&](int r) { return row(r) < M; };
         f32x4 v[4];
+        part_sum<4, 2>(v, S, addr, valid);
+        part_clear_all<4>(S, addr, valid);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < S; ++sp) {
-            const float *base = part + sp * slot + nc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-                if (m < M) v[r] += *(const f32x4 *)(base + (size_t)m * N);
-            }
-        }
-        for (int sp = 0; sp < S; ++sp) {
-            float *base = part + sp * slot + nc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-                if (m < M) *(f32x4 *)(base + (size_t)m * N) = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-            if (m < M) store4(m, v[r]);
-        }
-    }
+        for (int r = 0; r < 4; ++r)
+            if (valid(r)) store4(row(r), v[r]);
+    });
 }
 
 template <int DT>

@@ -72,7 +72,7 @@ struct W4A8Plan {
     int blk;   // skinny: 64-column sets per lane-row (1, 2)
     int mt;    // row tiles (skinny: M <= 16*mt; tiled and LDS GEMM: per wave)
     int tiles_n, tiles_m, splits;
-    int tilered;  // split-K through partial tiles (else per-element atomics; skinny kernel only)
+    int tilered;  // split-K through partial tiles (tiled and LDS kernels), else per-element atomics (skinny)
     int ksplit;   // LDS GEMM: groups of waves splitting K inside a workgroup (1, 2)
     size_t workspace_bytes;
     uint64_t *acc;

@@ -383,11 +383,13 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
             }
         return;
     }
-    // Split-K by partial tiles (device.hpp): store this split's partials,
-    // then the last workgroup of the tile sums all splits in split order.
+    // Split-K by partial tiles exchanged through agent-scope atomics
+    // (device.hpp): store this split's partials, then the last workgroup of
+    // the tile sums all splits in split order.
     uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
-    float *const part = (float *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
-    const size_t slot = (size_t)M * N;
+    uint64_t *const part = (uint64_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N / 2;  // 64-bit words per split
+    auto at = [&](int sp, int m) { return part + sp * slot + ((size_t)m * N + n0) / 2; };
     if (col_ok) {
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
@@ -395,48 +397,25 @@ __global__ __launch_bounds__(256) void w4a16_tiled(const uint16_t *__restrict__ 
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + 16 * mt + 4 * gq + r;
                 if (m >= M) continue;
-                float *dst = part + split * slot + (size_t)m * N + n0;
-                *(f32x4 *)dst = (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
-                *(f32x4 *)(dst + 4) = (f32x4){acc[mt][4][r], acc[mt][5][r], acc[mt][6][r], acc[mt][7][r]};
+                part_put(at(split, m), (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
+                part_put(at(split, m) + 2, (f32x4){acc[mt][4][r], acc[mt][5][r], acc[mt][6][r], acc[mt][7][r]});
             }
     }
-    if (!split_tile_last(cnt, S) || !col_ok) return;
-    // the last split sums the partials in split order, two of the lane's rows
-    // at a time: per split, the loads of those rows are in flight together;
-    // the partials are cleared after the batch's last load
+    if (!split_tile_last_atomic(cnt, S) || !col_ok) return;
+    // the last split sums the partials in split order, two of the lane's
+    // rows (four 16-byte vectors) at a time, then clears them
 #pragma unroll
     for (int b = 0; b < 2 * MTW; ++b) {
         const int mt = b >> 1, r0 = 2 * (b & 1);
-        f32x4 v0[2], v1[2];
+        auto row = [&](int i) { return m0 + 16 * mt + 4 * gq + r0 + (i >> 1); };
+        auto addr = [&](int sp, int i) { return at(sp, row(i)) + 2 * (i & 1); };
+        auto valid = [&](int i) { return row(i) < M; };
+        f32x4 v[4];
+        part_sum<4, 1>(v, S, addr, valid);
+        part_clear_all<4>(S, addr, valid);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) v0[r] = v1[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < S; ++s) {
-            const float *base = part + s * slot + n0;
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r0 + r;
-                if (m < M) {
-                    v0[r] += *(const f32x4 *)(base + (size_t)m * N);
-                    v1[r] += *(const f32x4 *)(base + (size_t)m * N + 4);
-                }
-            }
-        }
-        for (int s = 0; s < S; ++s) {
-            float *base = part + s * slot + n0;
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r0 + r;
-                if (m < M) {
-                    *(f32x4 *)(base + (size_t)m * N) = (f32x4){0.f, 0.f, 0.f, 0.f};
-                    *(f32x4 *)(base + (size_t)m * N + 4) = (f32x4){0.f, 0.f, 0.f, 0.f};
-                }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int m = m0 + 16 * mt + 4 * gq + r0 + r;
-            if (m < M) *(u32x4 *)(y + (size_t)m * N + n0) = pack8_out<DT>(v0[r], v1[r]);
-        }
+        for (int r = 0; r < 2; ++r)
+            if (valid(2 * r)) *(u32x4 *)(y + (size_t)row(2 * r) * N + n0) = pack8_out<DT>(v[2 * r], v[2 * r + 1]);
     }
 }
 

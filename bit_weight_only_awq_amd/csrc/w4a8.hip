@@ -264,8 +264,7 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
                                                    const uint16_t *__restrict__ s2,
                                                    const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                    int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
-                                                   int M, int N, int K, int G, int S, int qa_stride,
-                                                   int tilered) {
+                                                   int M, int N, int K, int G, int S, int qa_stride) {
     extern __shared__ int32_t ired[];
     constexpr int COLS = 64 * BLK;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -388,11 +387,7 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
     __syncthreads();
     const int total = M * COLS;
     const int n_base = tile * COLS;
-    // split-K: per-element counting atomics when the output is small (one
-    // round trip), partial tiles otherwise (tilered; device.hpp)
-    uint32_t *const cnt = (uint32_t *)acc64 + tile;
-    int32_t *const part = (int32_t *)((char *)acc64 + split_counters_bytes(gridDim.x));
-    const size_t slot = (size_t)M * N;
+    // split-K: per-element counting atomics (one round trip at the end)
     for (int idx = threadIdx.x; idx < total; idx += 256) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int32_t v = ired[(size_t)(0 * M + m) * COLS + c] + ired[(size_t)(1 * M + m) * COLS + c] +
@@ -403,23 +398,8 @@ __global__ __launch_bounds__(256) void w4a8_skinny(const int8_t *__restrict__ a8
         const float s1m = FUSED ? srow[m] : s1[m];
         if (S == 1)
             w4a8_store_s<GROUP, DT>(v, m, n, N, s1m, s2, y, acc_out);
-        else if (tilered)
-            part[split * slot + (size_t)m * N + n] = v;
         else if (splitk_contribute(&acc64[(size_t)m * N + n], v, S, &sum))
             w4a8_store_s<GROUP, DT>((int32_t)sum, m, n, N, s1m, s2, y, acc_out);
-    }
-    if (S == 1 || !tilered || !split_tile_last(cnt, S)) return;
-    for (int idx = threadIdx.x; idx < total; idx += 256) {
-        const int m = idx / COLS, c = idx - m * COLS;
-        const int n = n_base + c;
-        if (n >= N) continue;
-        int32_t v = 0;
-        for (int sp = 0; sp < S; ++sp) {
-            int32_t *src = part + sp * slot + (size_t)m * N + n;
-            v += *src;
-            *src = 0;
-        }
-        w4a8_store_s<GROUP, DT>(v, m, n, N, FUSED ? srow[m] : s1[m], s2, y, acc_out);
     }
 }
 
@@ -497,54 +477,37 @@ __global__ __launch_bounds__(256) void w4a8_tiled(const int8_t *__restrict__ a8,
             }
         return;
     }
-    // Split-K by partial tiles (device.hpp); int32 partials, so the sum is
-    // exact in any order.
+    // Split-K by partial tiles exchanged through agent-scope atomics
+    // (device.hpp); int32 partials, so the sum is exact in any order.
     uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
-    int32_t *const part = (int32_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
-    const size_t slot = (size_t)M * N;
+    uint64_t *const part = (uint64_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N / 2;  // 64-bit words per split
+    auto at = [&](int sp, int m) { return part + sp * slot + ((size_t)m * N + ncol) / 2; };
     if (ok) {
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M)
-                    *(i32x4 *)(part + split * slot + (size_t)m * N + ncol) =
-                        (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                if (m < M) part_put(at(split, m), (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
             }
     }
-    if (!split_tile_last(cnt, S) || !ok) return;
-    // the last split sums the partials, one row tile (4 of the lane's rows)
-    // at a time: per split, the loads of those rows are in flight together;
-    // the partials are cleared after the batch's last load
+    if (!split_tile_last_atomic(cnt, S) || !ok) return;
+    // the last split sums the partials one row tile (4 of the lane's rows)
+    // at a time, then clears them
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
+        auto row = [&](int r) { return m0 + 16 * mt + 4 * gq + r; };
+        auto addr = [&](int sp, int r) { return at(sp, row(r)); };
+        auto valid = [&](int r) { return row(r) < M; };
         i32x4 v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (i32x4){0, 0, 0, 0};
-        for (int sp = 0; sp < S; ++sp) {
-            const int32_t *base = part + sp * slot + ncol;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M) v[r] += *(const i32x4 *)(base + (size_t)m * N);
-            }
-        }
-        for (int sp = 0; sp < S; ++sp) {
-            int32_t *base = part + sp * slot + ncol;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M) *(i32x4 *)(base + (size_t)m * N) = (i32x4){0, 0, 0, 0};
-            }
-        }
+        part_sum<4, 1>(v, S, addr, valid);
+        part_clear_all<4>(S, addr, valid);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 16 * mt + 4 * gq + r;
-            if (m < M) {
+            if (!valid(r)) continue;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w4a8_store<GROUP, DT>(v[r][i], m, ncol + i, N, s1, s2, y, acc_out);
-            }
+            for (int i = 0; i < 4; ++i) w4a8_store<GROUP, DT>(v[r][i], row(r), ncol + i, N, s1, s2, y, acc_out);
         }
     }
 }
@@ -569,7 +532,7 @@ static hipError_t launch_skinny8(const W4A8Args &a, const W4A8Plan &p, hipStream
     hipLaunchKernelGGL((w4a8_skinny<BLK, MT, GROUP, FUSED, DT>), dim3(p.tiles_n, p.splits), dim3(256), lds, st, a.a8,
                        (const uint16_t *)a.x, (const uint32_t *)a.b, a.s1, a.s1_out, (const uint16_t *)a.s2,
                        (const uint16_t *)a.s3, (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K,
-                       a.G, p.splits, qa_stride, p.tilered);
+                       a.G, p.splits, qa_stride);
     return hipGetLastError();
 }
 

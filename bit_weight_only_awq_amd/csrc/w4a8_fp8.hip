@@ -447,49 +447,35 @@ __global__ __launch_bounds__(256) void w4a8_fp8_tiled(const uint8_t *__restrict_
             }
         return;
     }
+    // Split-K by partial tiles exchanged through agent-scope atomics
+    // (device.hpp), fp32, summed in split order.
     uint32_t *const cnt = (uint32_t *)ws + (tn + gridDim.x * tm);
-    float *const part = (float *)((char *)ws + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
-    const size_t slot = (size_t)M * N;
+    uint64_t *const part = (uint64_t *)((char *)ws + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
+    const size_t slot = (size_t)M * N / 2;  // 64-bit words per split
+    auto at = [&](int sp, int m) { return part + sp * slot + ((size_t)m * N + ncol) / 2; };
     if (ok) {
 #pragma unroll
         for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M)
-                    *(f32x4 *)(part + split * slot + (size_t)m * N + ncol) =
-                        (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                if (m < M) part_put(at(split, m), (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
             }
     }
-    if (!split_tile_last(cnt, S) || !ok) return;
+    if (!split_tile_last_atomic(cnt, S) || !ok) return;
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt) {
+        auto row = [&](int r) { return m0 + 16 * mt + 4 * gq + r; };
+        auto addr = [&](int sp, int r) { return at(sp, row(r)); };
+        auto valid = [&](int r) { return row(r) < M; };
         f32x4 v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        for (int sp = 0; sp < S; ++sp) {
-            const float *base = part + sp * slot + ncol;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M) v[r] += *(const f32x4 *)(base + (size_t)m * N);
-            }
-        }
-        for (int sp = 0; sp < S; ++sp) {
-            float *base = part + sp * slot + ncol;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * mt + 4 * gq + r;
-                if (m < M) *(f32x4 *)(base + (size_t)m * N) = (f32x4){0.f, 0.f, 0.f, 0.f};
-            }
-        }
+        part_sum<4, 1>(v, S, addr, valid);
+        part_clear_all<4>(S, addr, valid);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 16 * mt + 4 * gq + r;
-            if (m < M) {
+            if (!valid(r)) continue;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) fp8_store<DT>(v[r][i], m, ncol + i, N, s1, asum, s2, y, acc_out);
-            }
+            for (int i = 0; i < 4; ++i) fp8_store<DT>(v[r][i], row(r), ncol + i, N, s1, asum, s2, y, acc_out);
         }
     }
 }
