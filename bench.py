@@ -214,9 +214,12 @@ def traffic_summary(fetch_csv, write_csv, kernel="w4a16_decode", name="w4a16_dec
            "per_layer": {n: {"hbm_bytes": total[n], "alg_bytes": alg[n], "ratio": round(total[n] / alg[n], 4)}
                          for n in total},
            "counters": res, "source_digest": decode_digest(),
-           "command": "rocprofv3 --pmc FETCH_SIZE -- python3 bench.py --profile decode; "
-                      "rocprofv3 --pmc WRITE_SIZE -- python3 bench.py --profile decode; "
-                      "python3 bench.py --traffic <fetch csv> <write csv>"}
+           "command": ("rocprofv3 --pmc FETCH_SIZE -d gpurun_out/m/dfetch -o run --output-format csv "
+                       "-- python3 bench.py --profile decode; "
+                       "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/m/dwrite -o run --output-format csv "
+                       "-- python3 bench.py --profile decode; "
+                       "python3 bench.py --traffic gpurun_out/m/dfetch/run_counter_collection.csv "
+                       "gpurun_out/m/dwrite/run_counter_collection.csv")}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"{name}.traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
