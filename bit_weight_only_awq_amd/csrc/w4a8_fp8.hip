@@ -103,10 +103,16 @@ __device__ __forceinline__ uint32_t fp8_codes4(const Fp8Quotient<DT> &f, uint32_
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
 }
 
-// Sum of the values of four E4M3 codes (one a byte), in units of 2^-9.
-__device__ __forceinline__ int32_t e4m3_units4(uint32_t w) {
-    return e4m3_units(w & 0xFFu) + e4m3_units((w >> 8) & 0xFFu) + e4m3_units((w >> 16) & 0xFFu) +
-           e4m3_units(w >> 24);
+// Sum of the values of eight E4M3 codes (one a byte of lo, hi), in units of
+// 2^-9, through the hardware's fp8 -> fp32 decode (the same OCP E4M3 format
+// as the encode above).  Exact: every value is a multiple of 2^-9 of
+// magnitude at most 448, so every partial sum of the eight is a multiple of
+// 2^-9 below 2^24 units and fp32 holds it.
+__device__ __forceinline__ int32_t e4m3_units8(uint32_t lo, uint32_t hi) {
+    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+    const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+    const float v = ((a[0] + a[1]) + (b[0] + b[1])) + ((c[0] + c[1]) + (d[0] + d[1]));
+    return (int32_t)(v * 512.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(256) void w4a8_fp8_quant(const uint16_t *__restrict
         for (int k = 8 * threadIdx.x; k < K8; k += 8 * 256) {
             const u32x4 v = *(const u32x4 *)(row + k);
             const u32x2 o = {fp8_codes4<DT>(fq, v[0], v[1]), fp8_codes4<DT>(fq, v[2], v[3])};
-            part += e4m3_units4(o[0]) + e4m3_units4(o[1]);
+            part += e4m3_units8(o[0], o[1]);
             *(u32x2 *)(out + k) = o;
         }
         sum = part;
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(T) void w4a8_fp8_quant_rows(const uint16_t *__restr
             const int k = 8 * (threadIdx.x + i * T);
             if (k >= K) break;
             const u32x2 o = {fp8_codes4<DT>(fq, v[i][0], v[i][1]), fp8_codes4<DT>(fq, v[i][2], v[i][3])};
-            part += e4m3_units4(o[0]) + e4m3_units4(o[1]);
+            part += e4m3_units8(o[0], o[1]);
             *(u32x2 *)(out + k) = o;
         }
         sum = part;
