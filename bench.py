@@ -427,8 +427,10 @@ def config_sweeps(awq, synthgen, torch, dev, per_launch, decode, n_copies, compa
     res["cfg4_w4a8_qqq_n8192_k21760"] = cfg4
 
     # INT4-FP8 W4A8 (E4M3 activations) on the QQQ shape and the target shapes:
-    # quantisation and GEMM timed separately; the GEMM's roofline is the fp8
-    # matrix-core peak (5033 TFLOP/s dense), weights rotated at M <= 64
+    # quantisation and GEMM timed separately, and the whole layer through
+    # w4a8_fp8_linear (one fused kernel for a single token); the GEMM's
+    # roofline is the fp8 matrix-core peak (5033 TFLOP/s dense), weights
+    # rotated at M <= 64
     fp8 = {}
     shapes = [(M, W4A8_K, W4A8_N) for M in (1, 16, 64, 256, 1024)] + \
              [(M, K, N) for K, N in TARGET_SHAPES for M in M_TARGETS]
@@ -446,11 +448,14 @@ def config_sweeps(awq, synthgen, torch, dev, per_launch, decode, n_copies, compa
         tg = per_launch(lambda a=a, s1=s1, asum=asum, y=y, ncp=ncp, copies=copies:
                         [awq.w4a8_fp8_gemm(a, copies[r][0], s1, asum, copies[r][1], out=y) for r in range(ncp)],
                         ncp, reps=3)
+        tl = per_launch(lambda x=x, a=a, s1=s1, asum=asum, y=y, ncp=ncp, copies=copies:
+                        [awq.linear_w4a8_fp8(x, copies[r][0], copies[r][1], out=y, a=a, s1=s1, asum=asum)
+                         for r in range(ncp)], ncp, reps=3)
         flops = 2 * M * N * K
         ab = w4a8_alg_bytes(M, K, N) + 4 * M  # + asum
         fr, bound = roof_frac(tg, flops, ab, MFMA_I8_PEAK_TOPS)
         fp8[f"M={M} K={K} N={N}"] = {"quant_us": round(tq * 1e6, 2), "gemm_us": round(tg * 1e6, 2),
-                                     "layer_us": round((tq + tg) * 1e6, 2),
+                                     "layer_us": round(tl * 1e6, 2), "fused_quant": M == 1,
                                      "gemm_TFLOPs": round(flops / tg / 1e12, 1), "gemm_frac_roofline": fr,
                                      "bound": bound}
     del wsets

@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
     L.awq_repack_v2.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     L.w4a8_fp8_quant_act.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
     L.w4a8_fp8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    L.w4a8_fp8_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
     L.w4a8_quant_act.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.w4a8_gemm.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
     L.w4a8_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, sz, vp]
@@ -77,7 +78,7 @@ def lib() -> ctypes.CDLL:
     L.awq_plan_info.argtypes = [i32, i64, i64, i64, i32, i32, i32, ctypes.POINTER(PlanInfo)]
     for f in ("awq_pack", "awq_unpack", "awq_gemm_w4a16", "awq_gemv_w4a16", "w4a8_quant_act", "w4a8_gemm", "w4a8_linear",
               "awq_stream_read", "awq_plan_info", "awq_gemv_w4a16_static",
-              "awq_dequant_w4a16", "w4a8_fp8_quant_act", "w4a8_fp8_gemm", "awq_repack_v2"):
+              "awq_dequant_w4a16", "w4a8_fp8_quant_act", "w4a8_fp8_gemm", "w4a8_fp8_linear", "awq_repack_v2"):
         getattr(L, f).restype = i32
     _lib = L
     return L

@@ -706,6 +706,28 @@ int w4a8_fp8_gemm(const uint8_t *a, const int32_t *b_packed, const float *s1, co
     return hip_status(launch_w4a8_fp8(g, p, static_cast<hipStream_t>(stream)));
 }
 
+int w4a8_fp8_linear(const void *x, uint8_t *a, float *s1, float *asum, const int32_t *b_packed, const void *s2,
+                    void *y, float *acc_out, int64_t M, int64_t N, int64_t K, int dtype, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    if (!x || !a || !s1 || !asum || !b_packed || !s2 || !y) return AWQ_EINVAL;
+    if (dtype != AWQ_DTYPE_F16 && dtype != AWQ_DTYPE_BF16) return AWQ_EINVAL;
+    int rc = check_fp8_shape(M, N, K);
+    if (rc != AWQ_OK) return rc;
+    if (!aligned16(x) || !aligned16(a) || !aligned16(s1) || !aligned16(asum) || !aligned16(b_packed) ||
+        !aligned16(s2) || !aligned16(y) || (acc_out && !aligned16(acc_out)))
+        return AWQ_EALIGN;
+    W4A8Plan p = plan_w4a8_fp8(M, N, K, stream_props(stream));
+    rc = check_workspace(workspace, workspace_bytes, p.workspace_bytes);
+    if (rc != AWQ_OK) return rc;
+    if (p.splits > 1) p.acc = static_cast<uint64_t *>(workspace);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    W4A8Fp8Args g{a, b_packed, s1, asum, s2, y, acc_out, M, N, K, dtype};
+    if (w4a8_fp8_fuses_quant(M, K, p)) return hip_status(launch_w4a8_fp8_fused(g, x, s1, p, st));
+    rc = hip_status(launch_w4a8_fp8_quant(x, a, s1, asum, M, K, dtype, st));
+    if (rc != AWQ_OK) return rc;
+    return hip_status(launch_w4a8_fp8(g, p, st));
+}
+
 int w4a8_linear(const void *x_f16, int8_t *a8, float *s1, const int32_t *b_packed, const void *s2_f16,
                 const void *s3_f16, void *y_f16, int32_t *acc_out, int64_t M, int64_t N, int64_t K, int group_size,
                 int dtype, void *workspace, size_t workspace_bytes, void *stream) {

@@ -49,5 +49,12 @@ __device__ __forceinline__ void fp8_store(float t, int m, int n, int N, const fl
     y[(size_t)m * N + n] = f32_to_out_bits(d * s1[m] * act_bits_to_f32<DT>(s2[n]), DT);
     if (acc_out) acc_out[(size_t)m * N + n] = d;
 }
+// The same with sum_k a q already formed (d) and the row's scale s1m.
+template <int DT>
+__device__ __forceinline__ void fp8_store_d(float d, int m, int n, int N, float s1m, const uint16_t *__restrict__ s2,
+                                            uint16_t *__restrict__ y, float *__restrict__ acc_out) {
+    y[(size_t)m * N + n] = f32_to_out_bits(d * s1m * act_bits_to_f32<DT>(s2[n]), DT);
+    if (acc_out) acc_out[(size_t)m * N + n] = d;
+}
 
 }  // namespace awq4

@@ -122,6 +122,12 @@ hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 hipError_t launch_w4a8_fp8_quant(const void *x, uint8_t *a, float *s1, float *asum, int64_t M, int64_t K, int dt,
                                  hipStream_t st);
 hipError_t launch_w4a8_fp8(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st);
+// the INT4-FP8 skinny GEMM with the single token's quantisation fused in
+// (x: the fp16/bf16 activation row; s1_out: its scale, written)
+bool w4a8_fp8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p);
+size_t w4a8_fp8_fused_lds_bytes(int64_t K, int blk, int splits);
+hipError_t launch_w4a8_fp8_fused(const W4A8Fp8Args &g, const void *x, float *s1_out, const W4A8Plan &p,
+                                 hipStream_t st);
 // INT4-FP8 LDS-pipelined GEMM (plan kind 2, M >= 128)
 hipError_t launch_w4a8_fp8_lds(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st);
 // skinny W4A8 GEMM with the per-token quantisation fused in (plan kind 0,

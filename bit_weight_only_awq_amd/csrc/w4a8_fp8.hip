@@ -300,14 +300,31 @@ constexpr double kFp8Fixed = 1048576.0;
 // Skinny kernel: M <= 16*MT; 4 waves split the K slice of a 64*BLK column tile
 // (128-k steps); LDS reduce in wave order; split-K over grid y through the
 // counting fixed-point accumulators (device.hpp).
-template <int BLK, int MT, int DT>
+//
+// FUSED (one token, M == 1): the quantisation runs inside the kernel.  Every
+// workgroup reads the whole activation row for its abs-max, derives s1 as
+// the quantiser does (workgroup (0, 0) writes it out), and quantises only its
+// own K slice into LDS, from where the main loop reads the codes; the E4M3
+// codes never travel through device memory and the separate launch goes.
+// The epilogue needs d = sum_k a q = 512 t - 8 asum (t the matrix-core sum,
+// asum the row sum of the codes' values), and d is linear in the K slices:
+// each workgroup contributes 512 t_s - 8 asum_s of its own slice, so none of
+// them needs the whole row's asum.  In the fixed point of the split-K sum
+// (2^-20 of t) the asum part, 32 U_s (U_s = asum_s in units of 2^-9), is exact;
+// d is then formed once, exactly, and rounded once to fp32 (the two-launch
+// path rounds t to fp32 before forming d: the two differ by at most one fp32
+// rounding of d).  Dynamic LDS: the reduction area, then the slice's codes.
+template <int BLK, int MT, int DT, bool FUSED = false>
 __global__ __launch_bounds__(256) void w4a8_fp8_skinny(const uint8_t *__restrict__ a, const uint32_t *__restrict__ bq,
                                                        const float *__restrict__ s1, const float *__restrict__ asum,
                                                        const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
                                                        float *__restrict__ acc_out, uint64_t *__restrict__ acc64,
-                                                       int M, int N, int K, int S) {
+                                                       int M, int N, int K, int S,
+                                                       const uint16_t *__restrict__ x16 = nullptr,
+                                                       float *__restrict__ s1_out = nullptr) {
     extern __shared__ float fred[];
     constexpr int COLS = 64 * BLK;
+    static_assert(!FUSED || MT == 1, "the fused quantisation takes one row");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = lane & 15, gq = lane >> 4;
     const int tile = blockIdx.x, split = blockIdx.y;
@@ -321,6 +338,59 @@ __global__ __launch_bounds__(256) void w4a8_fp8_skinny(const uint8_t *__restrict
         ncol[b] = tile * COLS + 64 * b + 4 * j;
         ok[b] = ncol[b] < N;
     }
+    // FUSED: the row's scale, this workgroup's codes (LDS, after the
+    // reduction area) and their value sum in units of 2^-9
+    uint8_t *const qa = (uint8_t *)(fred + (size_t)4 * M * COLS);
+    float s1v = 0.0f;
+    int64_t uwg = 0;
+    if constexpr (FUSED) {
+        __shared__ uint32_t wmax[4];
+        __shared__ long long wsum[4];
+        uint32_t mx = 0;
+        for (int c = threadIdx.x; c < (K >> 3); c += 256) {
+            const u32x4 v = *(const u32x4 *)(x16 + 8 * c);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) mx = max(mx, max(v[p] & 0x7FFFu, (v[p] >> 16) & 0x7FFFu));
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+        if (lane == 0) wmax[wave] = mx;
+        __syncthreads();
+        mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+        // the quantiser's own expressions (w4a8_fp8_quant_rows), so s1 and
+        // every code come out the same
+        const float s = round_act_f<DT>(act_bits_to_f32<DT>(mx) / 448.0f);
+        const Fp8Quotient<DT> fq(s);
+        const int k_lo = 128 * s_lo, nc = 16 * (s_hi - s_lo);  // chunks of 8 values
+        int32_t part = 0;  // at most ceil(nc / 256) <= 16 chunks of at most 1835008 units
+        for (int c = threadIdx.x; c < nc; c += 256) {
+            const u32x4 v = *(const u32x4 *)(x16 + k_lo + 8 * c);
+            u32x2 o = {0, 0};
+            if (!fq.exact_divide) {
+                o = (u32x2){fp8_codes4<DT>(fq, v[0], v[1]), fp8_codes4<DT>(fq, v[2], v[3])};
+                part += e4m3_units8(o[0], o[1]);
+            } else if (s != 0.0f) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float q = fminf(
+                        fmaxf(act_bits_to_f32<DT>((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) / s, -448.0f), 448.0f);
+                    const uint32_t cd = e4m3_code(q);
+                    part += e4m3_units(cd);
+                    o[e >> 2] |= cd << (8 * (e & 3));
+                }
+            }
+            *(u32x2 *)(qa + 8 * c) = o;
+        }
+        long long sum = part;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+        if (lane == 0) wsum[wave] = sum;
+        __syncthreads();
+        uwg = (int64_t)wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        s1v = s;
+        if (tile == 0 && split == 0 && threadIdx.x == 0) s1_out[0] = s;
+    }
+
     f32x4 acc[MT][BLK][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -343,7 +413,9 @@ __global__ __launch_bounds__(256) void w4a8_fp8_skinny(const uint8_t *__restrict
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = 16 * mt + j;
-            av[mt] = m < M ? load_a32(a + (size_t)m * K + k0) : (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+            if (m >= M) av[mt] = (i32x8){0, 0, 0, 0, 0, 0, 0, 0};
+            else if (FUSED) av[mt] = *(const i32x8 *)(qa + (k0 - 128 * s_lo));
+            else av[mt] = load_a32(a + (size_t)m * K + k0);
         }
 #pragma unroll
         for (int b = 0; b < BLK; ++b)
@@ -376,7 +448,20 @@ __global__ __launch_bounds__(256) void w4a8_fp8_skinny(const uint8_t *__restrict
         if (n >= N) continue;
         const float v = ((fred[(size_t)(0 * M + m) * COLS + c] + fred[(size_t)(1 * M + m) * COLS + c]) +
                          fred[(size_t)(2 * M + m) * COLS + c]) + fred[(size_t)(3 * M + m) * COLS + c];
-        if (S == 1) {
+        if (FUSED) {
+            // 512 t - 8 asum of this K slice (U in units of 2^-9: 8 asum = U / 64)
+            if (S == 1) {
+                fp8_store_d<DT>((float)((double)v * 512.0 - (double)uwg * (1.0 / 64.0)), m, n, N, s1v, s2, y,
+                                acc_out);
+            } else {
+                const double lim = (double)(kBias - 1);
+                const double fv = __builtin_rint(fmin(fmax((double)v * kFp8Fixed, -lim), lim)) - 32.0 * (double)uwg;
+                const int64_t fx = (int64_t)fmin(fmax(fv, -lim), lim);
+                int64_t sum;
+                if (splitk_contribute(&acc64[(size_t)m * N + n], fx, S, &sum))
+                    fp8_store_d<DT>((float)((double)sum * (512.0 / kFp8Fixed)), m, n, N, s1v, s2, y, acc_out);
+            }
+        } else if (S == 1) {
             fp8_store<DT>(v, m, n, N, s1, asum, s2, y, acc_out);
         } else {
             const double lim = (double)(kBias - 1);
@@ -525,6 +610,37 @@ static hipError_t launch_fp8_dt(const W4A8Fp8Args &g, const W4A8Plan &p, hipStre
 
 hipError_t launch_w4a8_fp8(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st) {
     return g.dtype == DT_BF16 ? launch_fp8_dt<DT_BF16>(g, p, st) : launch_fp8_dt<DT_F16>(g, p, st);
+}
+
+// The fused single-token form (w4a8_fp8_skinny<..., FUSED>): its dynamic LDS,
+// the reduction area and the largest K slice's codes.
+size_t w4a8_fp8_fused_lds_bytes(int64_t K, int blk, int splits) {
+    const int64_t T = K / 128, per = (T + splits - 1) / splits;
+    return (size_t)4 * 64 * blk * sizeof(float) + (size_t)per * 128;
+}
+bool w4a8_fp8_fuses_quant(int64_t M, int64_t K, const W4A8Plan &p) {
+    return M == 1 && p.kind == 0 && p.mt == 1 && w4a8_fp8_fused_lds_bytes(K, p.blk, p.splits) <= 64 * 1024;
+}
+
+template <int BLK, int DT>
+static hipError_t launch_fp8_fused_t(const W4A8Fp8Args &g, const void *x, float *s1_out, const W4A8Plan &p,
+                                     hipStream_t st) {
+    const size_t lds = w4a8_fp8_fused_lds_bytes(g.K, BLK, p.splits);
+    hipLaunchKernelGGL((w4a8_fp8_skinny<BLK, 1, DT, true>), dim3(p.tiles_n, p.splits), dim3(256), lds, st,
+                       (const uint8_t *)nullptr, (const uint32_t *)g.b, (const float *)nullptr,
+                       (const float *)nullptr, (const uint16_t *)g.s2, (uint16_t *)g.y, g.acc_out, p.acc, 1,
+                       (int)g.N, (int)g.K, p.splits, (const uint16_t *)x, s1_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a8_fp8_fused(const W4A8Fp8Args &g, const void *x, float *s1_out, const W4A8Plan &p,
+                                 hipStream_t st) {
+    if (!w4a8_fp8_fuses_quant(g.M, g.K, p) || (p.splits > 1 && p.acc == nullptr)) return hipErrorInvalidValue;
+    if (g.dtype == DT_BF16)
+        return p.blk == 2 ? launch_fp8_fused_t<2, DT_BF16>(g, x, s1_out, p, st)
+                          : launch_fp8_fused_t<1, DT_BF16>(g, x, s1_out, p, st);
+    return p.blk == 2 ? launch_fp8_fused_t<2, DT_F16>(g, x, s1_out, p, st)
+                      : launch_fp8_fused_t<1, DT_F16>(g, x, s1_out, p, st);
 }
 
 }  // namespace awq4

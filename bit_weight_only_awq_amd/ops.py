@@ -285,6 +285,30 @@ def w4a8_fp8_gemm(a, b, s1, asum, s2, want_acc: bool = False, out=None):
     return (out, acc) if want_acc else out
 
 
+def linear_w4a8_fp8(x, b, s2, want_acc: bool = False, out=None, a=None, s1=None, asum=None):
+    """The whole INT4-FP8 layer in one call (w4a8_fp8_linear): per-token E4M3
+    quantisation of x, then the GEMM, one kernel for a single token.  Returns
+    y, or (y, s1, acc) with want_acc.  `a` and `asum` are scratch for the
+    two-step path."""
+    _need_cuda(x, b, s2, out, a, s1, asum)
+    if x.dtype not in _F16 or s2.dtype != x.dtype:
+        raise ValueError("activations and s2 must be fp16 or bf16, of one type")
+    M, K = x.shape
+    N = b.shape[1]
+    a = torch.empty(M, K, dtype=torch.uint8, device=x.device) if a is None else a
+    s1 = torch.empty(M, dtype=torch.float32, device=x.device) if s1 is None else s1
+    asum = torch.empty(M, dtype=torch.float32, device=x.device) if asum is None else asum
+    if out is None:
+        out = torch.empty(M, N, dtype=x.dtype, device=x.device)
+    acc = torch.empty(M, N, dtype=torch.float32, device=x.device) if want_acc else None
+    need = workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, M, N, K, -1, 0, x.device)
+    ws = WORKSPACE.get(x.device, need)
+    L.check("w4a8_fp8_linear", L.lib().w4a8_fp8_linear(_ptr(x), _ptr(a), _ptr(s1), _ptr(asum), _ptr(b), _ptr(s2),
+                                                       _ptr(out), _ptr(acc), M, N, K, _F16[x.dtype], _ptr(ws),
+                                                       0 if ws is None else ws.numel(), _stream(x.device)))
+    return (out, s1, acc) if want_acc else out
+
+
 # ----------------------------------------------------------------------------- measurement helper
 
 STREAM_SINK_WORDS = 8192

@@ -360,6 +360,29 @@ int w4a8_fp8_gemm(const uint8_t *a, const int32_t *b_packed, const float *s1, co
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * w4a8_fp8_linear -- the whole INT4-FP8 layer in one call:
+ * w4a8_fp8_quant_act of x followed by w4a8_fp8_gemm.  As for w4a8_linear
+ * ([P5]: quantising in a separate kernel costs performance), a single token
+ * (M == 1) runs as one kernel: every workgroup reads the activation row,
+ * derives s1 and quantises its own K range into LDS, and the GEMM's epilogue
+ * takes each range's own sum of the codes' values, so no workgroup needs the
+ * whole row's.  s1 and every code are those of w4a8_fp8_quant_act; the output
+ * forms acc = 512 t - 8 asum once from the exact split-K sum, where the
+ * two-launch path first rounds t to fp32 (at most one fp32 rounding of acc
+ * apart; y then at most one rounding of the activation type).  Otherwise the
+ * two steps run back to back.
+ *   x: device fp16/bf16 [M, K] (dtype).
+ *   a, asum: device uint8 [M, K] and fp32 [M], scratch: the codes and row
+ *            sums when the two-step path runs, untouched by the fused path.
+ *   s1: device fp32 [M], written.
+ *   other arguments, layouts, workspace (op AWQ_OP_W4A8_FP8_GEMM) and errors:
+ *   as w4a8_fp8_gemm.
+ */
+int w4a8_fp8_linear(const void *x, uint8_t *a, float *s1, float *asum, const int32_t *b_packed,
+                    const void *s2, void *y, float *acc_out, int64_t M, int64_t N, int64_t K, int dtype,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * awq_stream_read -- measurement helper, not a step of the method: reads
  * `bytes` bytes at `src` once (16-byte loads spread over up to 2048
  * workgroups) and writes an XOR checksum per wave to `sink`, so that the

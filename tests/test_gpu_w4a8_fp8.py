@@ -111,3 +111,84 @@ def test_fp8_deterministic():
         assert torch.equal(yy.view(torch.int16), ys[0].view(torch.int16))
     for yy in y2[1:]:
         assert torch.equal(yy.view(torch.int16), y2[0].view(torch.int16))
+
+
+def _linear_check(M, K, N, dt, x=None, large=False):
+    """w4a8_fp8_linear against the two launches and the oracle.  A single
+    token runs the fused kernel: s1 identical to the quantiser's, acc within
+    one fp32 rounding of the two-launch acc (the fused path forms acc once
+    from the exact split-K sum, the two-launch path rounds t to fp32 first),
+    y within one rounding of the activation type of it; more tokens run the
+    two launches and must match them bit for bit."""
+    c = synthgen.w4a8_case(M, K, N, -1, dtype="f16" if dt == 0 else "bf16")
+    xs = c.x if x is None else x.to(_T[dt])
+    xd, b, s2 = to_dev(xs, c.b, c.s2)
+    y, s1, acc = awq.linear_w4a8_fp8(xd, b, s2, want_acc=True)
+    a2, s12, asum2 = awq.quant_act_fp8(xd)
+    y2, acc2 = awq.w4a8_fp8_gemm(a2, b, s12, asum2, s2, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), s12.cpu().numpy().view(np.uint32))
+    g, g2 = acc.cpu().numpy().astype(np.float64), acc2.cpu().numpy().astype(np.float64)
+    yf, yf2 = y.cpu().double().numpy(), y2.cpu().double().numpy()
+    if M > 1:
+        assert np.array_equal(g, g2) and torch.equal(y.cpu(), y2.cpu())
+    else:
+        asum = np.abs(asum2.cpu().numpy().astype(np.float64))[:, None]
+        # t rounded to fp32 (<= 512 |t| 2^-24 = (|acc| + 8 asum) 2^-24), asum rounded to
+        # fp32 (8 asum 2^-24) and the FMA's rounding on the two-launch side, one
+        # rounding on the fused side
+        bound = (3 * np.abs(g2) + 16 * asum) * 2.0 ** -24 + 1e-30
+        assert np.all(np.abs(g - g2) <= bound), float(np.max(np.abs(g - g2) - bound))
+        ulp = 2.0 ** -10 if dt == 0 else 2.0 ** -7
+        assert np.all(np.abs(yf - yf2) <= np.abs(yf2) * ulp + 2.0 ** -24), float(np.max(np.abs(yf - yf2)))
+    # and against the oracle, from the codes the quantiser produces
+    ea, es1, esum = orc().quant_act_fp8(xs, dt)
+    eacc, y64 = orc().w4a8_fp8(ea, c.b, es1, c.s2, dt)
+    av = np.abs(torch.from_numpy(ea).view(torch.float8_e4m3fn).double().numpy())
+    bound = K * 2.0 ** -24 * 15 * av.sum(axis=1, keepdims=True) + 8 * np.abs(esum[:, None]) * 2.0 ** -23 \
+        + np.abs(eacc) * 2.0 ** -23
+    assert np.all(np.abs(g - eacc) <= bound), float(np.max(np.abs(g - eacc) - bound))
+    if not large:
+        check_fp(y.cpu(), y64, "f16" if dt == 0 else "bf16", f"fp8 linear M={M} K={K} N={N}")
+    else:
+        # outputs far from unit size: the absolute part of the output bar does
+        # not apply.  Per element, acc is held to the fp32-accumulation bound
+        # above (a few largest codes beside many small ones make that bound,
+        # not the output rounding, the larger term); the output to the
+        # relative bar.
+        rel = float(np.linalg.norm(yf - y64) / np.linalg.norm(y64))
+        assert np.all(np.isfinite(yf)) and rel <= 2e-3, rel
+
+
+@pytest.mark.parametrize("dt", [0, 1])
+@pytest.mark.parametrize("M,K,N", [(1, 21760, 8192), (1, 4096, 4096), (1, 4096, 14336), (1, 128, 8), (1, 256, 136),
+                                   (1, 130944, 64), (3, 4096, 1032), (16, 21760, 8192)])
+def test_fp8_linear(M, K, N, dt):
+    _linear_check(M, K, N, dt)
+
+
+@pytest.mark.parametrize("dt", [0, 1])
+@pytest.mark.parametrize("row", ["zero", "tiny", "huge", "ties"])
+def test_fp8_linear_edge_rows(row, dt):
+    """The fused single-token path on the rows that take other branches of the
+    quantiser: all zero (s1 = 0, codes 0), tiny (bf16: s1 below 2^-126, the
+    exactly divided quotients), the largest finite value (s1 at its largest),
+    and values that sit on E4M3 rounding ties after the division by s1 = 1."""
+    K, N = 4096, 1032
+    g = torch.Generator().manual_seed(11 + dt)
+    if row == "zero":
+        x = torch.zeros(1, K)
+    elif row == "tiny":
+        x = torch.randn(1, K, generator=g) * (2.0 ** -130 if dt == 1 else 2.0 ** -20)
+    elif row == "huge":
+        # four entries at the largest fp16 value (bf16: 1e34; its largest would
+        # overflow y in fp32 on either path) set s1 = max / 448; the rest
+        # quantise to small codes, so y stays finite
+        big = 65504.0 if dt == 0 else 1e34
+        x = torch.randn(1, K, generator=g) * 1e-3 * big
+        x[0, torch.randperm(K, generator=g)[:4]] = torch.tensor([1.0, -1.0, 1.0, -1.0]) * big
+    else:
+        # s1 = 448 / 448 = 1: the codes of 1 + (2j + 1) / 16 sit halfway between E4M3 neighbours
+        x = 1.0 + (2 * torch.randint(0, 8, (1, K), generator=g) + 1).float() / 16.0
+        x[0, 0] = 448.0
+    _linear_check(1, K, N, dt, x=x, large=row in ("huge", "ties"))
