@@ -483,7 +483,7 @@ const char *awq_status_str(int status) {
     }
 }
 
-int awq_version(void) { return 101; }
+int awq_version(void) { return 102; }
 
 static int check_pack_shape(int64_t rows, int64_t cols, int layout) {
     if (rows < 0 || cols < 0 || rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) return AWQ_EINVAL;

@@ -39,7 +39,7 @@ def test_status_strings():
         s = lib.awq_status_str(code).decode()
         assert s.startswith("AWQ_")
     assert lib.awq_status_str(12345).decode() == "AWQ_UNKNOWN"
-    assert lib.awq_version() == 101
+    assert lib.awq_version() == 102
 
 
 # Fake "device" pointers: validation only looks at null-ness and alignment, and
