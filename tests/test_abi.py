@@ -261,6 +261,29 @@ def test_plan_sizes_grids_from_the_cu_count():
             assert (p.splits > 1) == (p.workspace_bytes > 0), (cus, op, M, N, K)
 
 
+def test_gemm_k_split_rule():
+    """The LDS GEMM's K split on a whole MI355X: about CUs / tiles splits of
+    two-group workgroups, at most one per 16 stages and 8 in all; long K
+    (>= 128 stages) on 128-row tiles with one tile per CU at most takes 3-4
+    single-group splits; 256-row tiles at M = 2048 take none."""
+    gemm = L.AWQ_OP_GEMM_W4A16
+    want = {  # (M, N, K): (row tiles, tiles, splits, wave groups)
+        (256, 6144, 4096): (8, 96, 2, 2),     # qkv: 96 tiles -> 2 splits
+        (256, 4096, 4096): (8, 64, 4, 2),     # o: 64 tiles -> 4
+        (256, 4096, 14336): (8, 64, 4, 2),    # down
+        (96, 4096, 14336): (8, 32, 8, 2),     # down at 96 rows: 8, the cap
+        (96, 6144, 4096): (8, 48, 4, 2),      # qkv at 96 rows: 5 capped at 64 / 16 stages
+        (256, 28672, 4096): (16, 224, 1, 2),  # gate/up: more tiles than half the CUs, no split
+        (768, 4096, 14336): (8, 192, 4, 1),   # long K, 192 tiles: 4 single-group splits
+        (1024, 4096, 14336): (8, 256, 3, 1),  # long K, 256 tiles: 3
+        (2048, 4096, 14336): (16, 256, 1, 2),  # 256-row tiles: none
+    }
+    for (M, N, K), (mt, tiles, s, ks) in want.items():
+        p = _plan(gemm, M, N, K, 128, cus=256)
+        assert (p.kernel, p.row_tiles, p.tiles_n * p.tiles_m, p.splits, p.ksplit) == (3, mt, tiles, s, ks), (M, N, K)
+        assert p.workspace_bytes == (0 if s == 1 else L.lib().awq_workspace_bytes(gemm, M, N, K, 128, 0))
+
+
 def test_dequant_validation():
     lib = L.lib()
     assert lib.awq_dequant_w4a16(A, A, A, None, 4096, 4096, 128, 0, None) == L.AWQ_EINVAL   # no output
