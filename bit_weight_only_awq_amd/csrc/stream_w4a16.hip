@@ -29,7 +29,7 @@ namespace awq4 {
 // otherwise handed over as fp32 partials exchanged through agent-scope atomic
 // stores and loads (device.hpp: split_tile_last_atomic), the last workgroup of
 // the column tile adding them in split order and clearing them.
-template <int NT, int DT, int COLS>
+template <int NT, int DT, int ROWS, int COLS>
 __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_t *__restrict__ y,
                                                        uint64_t *__restrict__ ws, int M, int N, int tile, int S) {
     // Everything moves as column pairs: N is a multiple of 8, so a pair never
@@ -58,45 +58,59 @@ __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_
         }
     if (!split_tile_last_atomic((uint32_t *)ws + tile, S)) return;
     // The last workgroup of the column tile sums the partials in split order.
-    // Each thread takes kP pairs at a time and issues the loads of a batch of
-    // kB splits for all of them before adding, so a pass costs one round trip
-    // per batch instead of one per pair and batch.
-    constexpr int kP = 8, kB = 4;
-    for (int p0 = threadIdx.x; p0 < pairs; p0 += kP * NT) {
-        float2 v[kP];
+    // Each thread takes all its pairs of the tile at once (kP) and issues the
+    // loads of a batch of kB splits for all of them before adding: about 64
+    // loads in flight per thread, one memory round trip per batch.  These
+    // round trips run on the few CUs that finish a tile, after the rest of
+    // the grid is done, so their number sets the length of the kernel's tail.
+    constexpr int kP = ROWS * COLS / 2 / NT;
+    constexpr int kB = 64 / kP < 1 ? 1 : 64 / kP > 8 ? 8 : 64 / kP;
+    static_assert(kP >= 1 && kP * NT * 2 == ROWS * COLS, "whole pairs per thread");
+    // Every load and store below is a split's base address, the same for the
+    // whole workgroup, plus the pair's byte offset inside the split (a split
+    // holds M * N * 4 < 2^32 bytes), which keeps the addressing out of the
+    // loop's registers.
+    uint32_t off[kP];
+    bool ok[kP];
 #pragma unroll
-        for (int q = 0; q < kP; ++q) v[q] = make_float2(0.f, 0.f);
-        for (int s0 = 0; s0 < S; s0 += kB) {
-            uint64_t b[kP][kB];
+    for (int q = 0; q < kP; ++q) {
+        const int pi = threadIdx.x + q * NT;
+        ok[q] = pair_ok(pi);
+        off[q] = ok[q] ? (uint32_t)pair_at(pi) * 8u : 0u;
+    }
+    auto split_base = [&](int s) { return (char *)(part + (size_t)s * slot); };
+    float2 v[kP];
 #pragma unroll
-            for (int q = 0; q < kP; ++q) {
-                const int pi = p0 + q * NT;
-                const bool ok = pair_ok(pi);
+    for (int q = 0; q < kP; ++q) v[q] = make_float2(0.f, 0.f);
+    for (int s0 = 0; s0 < S; s0 += kB) {
+        uint64_t b[kP][kB];
 #pragma unroll
-                for (int i = 0; i < kB; ++i)
-                    b[q][i] = ok && s0 + i < S ? __hip_atomic_load(&part[(size_t)(s0 + i) * slot + pair_at(pi)],
-                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                               : 0ull;
-            }
+        for (int i = 0; i < kB; ++i) {
+            const char *base = split_base(s0 + i);
 #pragma unroll
             for (int q = 0; q < kP; ++q)
-#pragma unroll
-                for (int i = 0; i < kB; ++i) {
-                    const float2 f = unpack_f32x2(b[q][i]);
-                    v[q].x += f.x;
-                    v[q].y += f.y;
-                }
+                b[q][i] = ok[q] && s0 + i < S ? __hip_atomic_load((const uint64_t *)(base + off[q]), __ATOMIC_RELAXED,
+                                                                  __HIP_MEMORY_SCOPE_AGENT)
+                                              : 0ull;
         }
 #pragma unroll
-        for (int q = 0; q < kP; ++q) {
-            const int pi = p0 + q * NT;
-            if (!pair_ok(pi)) continue;
-            const size_t at = pair_at(pi);
-            for (int s = 0; s < S; ++s)
-                __hip_atomic_store(&part[(size_t)s * slot + at], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            out_pair(at, v[q]);
-        }
+        for (int q = 0; q < kP; ++q)
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                const float2 f = unpack_f32x2(b[q][i]);
+                v[q].x += f.x;
+                v[q].y += f.y;
+            }
     }
+    for (int s = 0; s < S; ++s) {
+        char *base = split_base(s);
+#pragma unroll
+        for (int q = 0; q < kP; ++q)
+            if (ok[q]) __hip_atomic_store((uint64_t *)(base + off[q]), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int q = 0; q < kP; ++q)
+        if (ok[q]) out_pair(off[q] / 8u, v[q]);
 }
 
 // One chunk's loads: scales and zero points of its group, MT row tiles of X
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(64 * WV, 1) void w4a16_stream(const uint16_t *__res
     // wave 0 holds the workgroup's sum: park it for all threads
     if (wave == 0) park(0);
     __syncthreads();
-    tile_store_or_exchange<64 * WV, DT, COLS>(red, y, ws, M, N, tile, S);
+    tile_store_or_exchange<64 * WV, DT, ROWS, COLS>(red, y, ws, M, N, tile, S);
 }
 
 template <int MT, int CS, int DT, bool SYM>

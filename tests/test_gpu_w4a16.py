@@ -202,12 +202,15 @@ def test_stream_random(M, K, N, G, dtype, sym):
 
 
 @pytest.mark.parametrize("M,K,N,G,split", [(40, 640, 264, 64, 6), (12, 640, 264, 32, 7), (64, 4096, 4096, 128, 1),
-                                           (24, 4096, 4096, 128, 13), (48, 11008, 4096, 128, 3)])
+                                           (24, 4096, 4096, 128, 13), (48, 11008, 4096, 128, 3),
+                                           (16, 4096, 1032, 128, 20), (64, 4096, 1032, 32, 9)])
 def test_stream_explicit_splits(M, K, N, G, split):
     """Explicit K splits on the streaming kernel, including splits that leave
     the last workgroups of a column tile without a chunk (640/64 = 10 chunks
     over 6 splits: ceil(10/6) = 2 each, the sixth empty) -- they still count
-    in the split exchange -- and the unsplit path; exact special case."""
+    in the split exchange --, the unsplit path, and more splits than the
+    exchange loads in one batch (4 at 4 row tiles, 8 below; up to three
+    batches); exact special case."""
     info = awq.plan_info(awq.AWQ_OP_GEMM_W4A16, M, N, K, G, split)
     assert info["kernel"] == 5 and info["splits"] == split, info
     g = torch.Generator().manual_seed(M + N + split)
