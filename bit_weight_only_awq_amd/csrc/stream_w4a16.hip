@@ -15,7 +15,7 @@
 // decode kernel: lane (j, gq) holds word-column j of the tile (8 outputs) at
 // the 8 k-rows 8 gq + e of each 32-k step.  Per chunk, the exact (q - z) products
 // are summed on the matrix cores (MT 16-row tiles of X) and scaled once in
-// fp32.  The waves' tiles are then added through LDS in a fixed tree and the
+// fp32.  The waves' tiles are then added through LDS in wave order and the
 // S workgroups of a column tile exchange fp32 partials, the last one adding
 // them in split order -- so the result does not depend on timing.
 #include "device.hpp"
@@ -24,12 +24,25 @@
 
 namespace awq4 {
 
-// The workgroup's M x COLS tile sum, parked in LDS (row-major, COLS floats a
-// row), goes out: written directly when the K range is not split (S == 1);
+// The workgroup's M x COLS tile sum -- the SLOTS tiles its waves parked in
+// LDS (ROWS x COLS floats each, COLS a row in the order lds_col gives), added
+// in slot order -- goes out: written directly when the K range is not split (S == 1);
 // otherwise handed over as fp32 partials exchanged through agent-scope atomic
 // stores and loads (device.hpp: split_tile_last_atomic), the last workgroup of
 // the column tile adding them in split order and clearing them.
-template <int NT, int DT, int ROWS, int COLS>
+// Position of column c inside a parked row.  Lane j holds columns 8j .. 8j+7
+// of its rows and parks them as two 16-byte halves: half h of every lane sits
+// in the h-th half of the row, at the lane's 16-byte slot (4j floats), so the
+// 16 lanes of a row write 16 consecutive slots -- all of the LDS banks, no
+// two lanes of a write on one bank.  (Columns in plain order put lanes j and
+// j+8 on the same banks and the four row groups of a wave on the same ones
+// again: eight-way conflicts, about 3 us of the reduction at 64 rows.)
+template <int COLS>
+__device__ __forceinline__ int lds_col(int c) {
+    return (COLS / 2) * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
+}
+
+template <int NT, int DT, int ROWS, int COLS, int SLOTS>
 __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_t *__restrict__ y,
                                                        uint64_t *__restrict__ ws, int M, int N, int tile, int S) {
     // Everything moves as column pairs: N is a multiple of 8, so a pair never
@@ -39,12 +52,23 @@ __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_
     const int pairs = M * COLS / 2;
     auto pair_at = [&](int pi) { return (size_t)(pi / (COLS / 2)) * (N / 2) + n_base / 2 + pi % (COLS / 2); };
     auto pair_ok = [&](int pi) { return pi < pairs && n_base + 2 * (pi % (COLS / 2)) < N; };
+    auto parked = [&](int pi) {
+        const float *p = red + (pi / (COLS / 2)) * COLS + lds_col<COLS>(2 * (pi % (COLS / 2)));
+        float2 v = *(const float2 *)p;
+#pragma unroll
+        for (int w = 1; w < SLOTS; ++w) {
+            const float2 u = *(const float2 *)(p + w * ROWS * COLS);
+            v.x += u.x;
+            v.y += u.y;
+        }
+        return v;
+    };
     auto out_pair = [&](size_t at, float2 v) {
         *(uint32_t *)(y + 2 * at) = (uint32_t)f32_to_out_bits(v.x, DT) | ((uint32_t)f32_to_out_bits(v.y, DT) << 16);
     };
     if (S == 1) {
         for (int pi = threadIdx.x; pi < pairs; pi += NT)
-            if (pair_ok(pi)) out_pair(pair_at(pi), *(const float2 *)(red + 2 * pi));
+            if (pair_ok(pi)) out_pair(pair_at(pi), parked(pi));
         return;
     }
     // one 64-bit agent-scope atomic per pair and split
@@ -52,7 +76,7 @@ __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_
     const size_t slot = (size_t)M * N / 2;  // pairs per split
     for (int pi = threadIdx.x; pi < pairs; pi += NT)
         if (pair_ok(pi)) {
-            const float2 v = *(const float2 *)(red + 2 * pi);
+            const float2 v = parked(pi);
             __hip_atomic_store(&part[blockIdx.y * slot + pair_at(pi)], pack_f32x2(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -211,8 +235,8 @@ __global__ __launch_bounds__(64 * WV, 1) void w4a16_stream(const uint16_t *__res
                                                           const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
                                                           uint64_t *__restrict__ ws, int M, int N, int K, int lgG) {
     constexpr int ROWS = 16 * MT, COLS = 128;
-    // tree reduction area: WV/2 partial tiles of ROWS x COLS floats
-    __shared__ __attribute__((aligned(16))) float red[(WV / 2) * ROWS * COLS];
+    // one parked ROWS x COLS tile per wave (128 KB at 4 row tiles)
+    __shared__ __attribute__((aligned(16))) float red[WV * ROWS * COLS];
     const int lane = threadIdx.x & 63;
     // the wave index in a scalar register: the chunk loop below is uniform
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,7 +311,7 @@ __global__ __launch_bounds__(64 * WV, 1) void w4a16_stream(const uint16_t *__res
 
     // Lane holds rows 16 mt + 4 gq + r and columns 8 j + t of the tile.
     auto slot_of = [&](int sl, int mt, int r) {
-        return red + ((size_t)sl * ROWS + 16 * mt + 4 * gq + r) * COLS + 8 * j;
+        return red + ((size_t)sl * ROWS + 16 * mt + 4 * gq + r) * COLS + 4 * j;  // lds_col(8 j)
     };
     auto park = [&](int sl) {
 #pragma unroll
@@ -297,34 +321,17 @@ __global__ __launch_bounds__(64 * WV, 1) void w4a16_stream(const uint16_t *__res
                 float *d = slot_of(sl, mt, r);
                 const f32x4(&v)[8] = acc[mt];
                 *(f32x4 *)d = (f32x4){v[0][r], v[1][r], v[2][r], v[3][r]};
-                *(f32x4 *)(d + 4) = (f32x4){v[4][r], v[5][r], v[6][r], v[7][r]};
+                *(f32x4 *)(d + COLS / 2) = (f32x4){v[4][r], v[5][r], v[6][r], v[7][r]};
             }
     };
-    // waves [h, 2h) hand their tiles to waves [0, h), h = WV/2, ..., 1
-#pragma unroll
-    for (int h = WV / 2; h >= 1; h >>= 1) {
-        if (wave >= h && wave < 2 * h) park(wave - h);
-        __syncthreads();
-        if (wave < h) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float *d = slot_of(wave, mt, r);
-                    const f32x4 v0 = *(const f32x4 *)d, v1 = *(const f32x4 *)(d + 4);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        acc[mt][t][r] += v0[t];
-                        acc[mt][4 + t][r] += v1[t];
-                    }
-                }
-        }
-        __syncthreads();
-    }
-    // wave 0 holds the workgroup's sum: park it for all threads
-    if (wave == 0) park(0);
+    // every wave parks its tile in a slot of its own, all at once; the
+    // exchange below adds the WV slots of each element in wave order (a
+    // fixed order: the sum does not depend on timing).  (A tree of wave
+    // pairs, half the LDS, took about 3 us at 64 rows: five dependent LDS
+    // passes with one or two waves at work in each.)
+    park(wave);
     __syncthreads();
-    tile_store_or_exchange<64 * WV, DT, ROWS, COLS>(red, y, ws, M, N, tile, S);
+    tile_store_or_exchange<64 * WV, DT, ROWS, COLS, WV>(red, y, ws, M, N, tile, S);
 }
 
 template <int MT, int CS, int DT, bool SYM>
