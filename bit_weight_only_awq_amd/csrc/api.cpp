@@ -187,7 +187,9 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
     // of a column tile sums (S x rows x 128 fp32 at about 40 GB/s): the S
     // in [1, CUs / tiles] (every workgroup resident at once, every wave with a
     // chunk) with the least estimated time.
-    if (M > 8 && M <= 64) {
+    // (Its split partials are addressed as one buffer of M x N floats per
+    // split, hence M x N x 4 under 2^31 bytes.)
+    if (M > 8 && M <= 64 && M * N * 4 < (int64_t(1) << 31)) {
         const int cs = G >= 64 ? 2 : 1;
         const int mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
         const int wv = kStreamWaves(mt);

@@ -24,117 +24,123 @@
 
 namespace awq4 {
 
-// The workgroup's M x COLS tile sum -- the SLOTS tiles its waves parked in
-// LDS (ROWS x COLS floats each, COLS a row in the order lds_col gives), added
-// in slot order -- goes out: written directly when the K range is not split (S == 1);
-// otherwise handed over as fp32 partials exchanged through agent-scope atomic
-// stores and loads (device.hpp: split_tile_last_atomic), the last workgroup of
-// the column tile adding them in split order and clearing them.
 // Position of column c inside a parked row.  Lane j holds columns 8j .. 8j+7
 // of its rows and parks them as two 16-byte halves: half h of every lane sits
 // in the h-th half of the row, at the lane's 16-byte slot (4j floats), so the
 // 16 lanes of a row write 16 consecutive slots -- all of the LDS banks, no
 // two lanes of a write on one bank.  (Columns in plain order put lanes j and
 // j+8 on the same banks and the four row groups of a wave on the same ones
-// again: eight-way conflicts, about 3 us of the reduction at 64 rows.)
+// again: eight-way conflicts.)
 template <int COLS>
 __device__ __forceinline__ int lds_col(int c) {
     return (COLS / 2) * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
 }
 
+// The workgroup's M x COLS tile sum -- the SLOTS tiles its waves parked in
+// LDS (ROWS x COLS floats each, COLS a row in the order lds_col gives), added
+// in slot order -- goes out: written directly when the K range is not split
+// (S == 1); otherwise handed over as fp32 partials (one M x N array per
+// split after the tile counters, device.hpp: split_tile_last_atomic), the
+// last workgroup of the column tile adding them in split order, clearing
+// them and writing the output.  Everything moves as quads of columns (N is a
+// multiple of 8, so a quad never straddles the last column): 8-byte output
+// stores, 16-byte partial loads and stores.  The partials move with the
+// cache policy of agent-scope atomic loads and stores (sc1: through to the
+// device-wide coherence point), as 16-byte buffer accesses -- half the
+// requests of 8-byte atomics; the tail of the kernel is the last workgroups'
+// partial traffic, so its request count sets the tail's length.
+constexpr int kPartCoherent = 16;  // buffer cache-policy operand: sc1
+
 template <int NT, int DT, int ROWS, int COLS, int SLOTS>
 __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_t *__restrict__ y,
                                                        uint64_t *__restrict__ ws, int M, int N, int tile, int S) {
-    // Everything moves as column pairs: N is a multiple of 8, so a pair never
-    // straddles the last column, and the output and the partial area (after
-    // the counters, 256-byte aligned) take 4- and 8-byte accesses.
+    constexpr int QR = COLS / 4;         // quads per row
+    constexpr int kQ = ROWS * QR / NT;   // quads per thread, whole tile
+    static_assert(kQ >= 1 && kQ * NT == ROWS * QR, "whole quads per thread");
     const int n_base = tile * COLS;
-    const int pairs = M * COLS / 2;
-    auto pair_at = [&](int pi) { return (size_t)(pi / (COLS / 2)) * (N / 2) + n_base / 2 + pi % (COLS / 2); };
-    auto pair_ok = [&](int pi) { return pi < pairs && n_base + 2 * (pi % (COLS / 2)) < N; };
-    auto parked = [&](int pi) {
-        const float *p = red + (pi / (COLS / 2)) * COLS + lds_col<COLS>(2 * (pi % (COLS / 2)));
-        float2 v = *(const float2 *)p;
+    const int quads = M * QR;
+    // thread t takes quads t, t + NT, ...: its sums of the SLOTS parked tiles
+    // and their 16-byte index in an [M, N] array
+    f32x4 v[kQ];
+    bool ok[kQ];
+    uint32_t at[kQ];
 #pragma unroll
-        for (int w = 1; w < SLOTS; ++w) {
-            const float2 u = *(const float2 *)(p + w * ROWS * COLS);
-            v.x += u.x;
-            v.y += u.y;
+    for (int q = 0; q < kQ; ++q) {
+        const int qi = threadIdx.x + q * NT;
+        const int r = qi / QR, c = 4 * (qi % QR);
+        ok[q] = qi < quads && n_base + c < N;
+        at[q] = ok[q] ? (uint32_t)(r * (N / 4) + (n_base + c) / 4) : 0u;
+        v[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (ok[q]) {
+            const float *p = red + r * COLS + lds_col<COLS>(c);
+            v[q] = *(const f32x4 *)p;
+#pragma unroll
+            for (int w = 1; w < SLOTS; ++w) v[q] += *(const f32x4 *)(p + w * ROWS * COLS);
         }
-        return v;
-    };
-    auto out_pair = [&](size_t at, float2 v) {
-        *(uint32_t *)(y + 2 * at) = (uint32_t)f32_to_out_bits(v.x, DT) | ((uint32_t)f32_to_out_bits(v.y, DT) << 16);
+    }
+    auto out_quad = [&](uint32_t a, f32x4 t) {
+        const uint32_t lo = (uint32_t)f32_to_out_bits(t[0], DT) | ((uint32_t)f32_to_out_bits(t[1], DT) << 16);
+        const uint32_t hi = (uint32_t)f32_to_out_bits(t[2], DT) | ((uint32_t)f32_to_out_bits(t[3], DT) << 16);
+        *(uint2 *)(y + 4 * (size_t)a) = make_uint2(lo, hi);
     };
     if (S == 1) {
-        for (int pi = threadIdx.x; pi < pairs; pi += NT)
-            if (pair_ok(pi)) out_pair(pair_at(pi), parked(pi));
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+            if (ok[q]) out_quad(at[q], v[q]);
         return;
     }
-    // one 64-bit agent-scope atomic per pair and split
-    uint64_t *const part = (uint64_t *)((char *)ws + split_counters_bytes(gridDim.x));
-    const size_t slot = (size_t)M * N / 2;  // pairs per split
-    for (int pi = threadIdx.x; pi < pairs; pi += NT)
-        if (pair_ok(pi)) {
-            const float2 v = parked(pi);
-            __hip_atomic_store(&part[blockIdx.y * slot + pair_at(pi)], pack_f32x2(v), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-    if (!split_tile_last_atomic((uint32_t *)ws + tile, S)) return;
-    // The last workgroup of the column tile sums the partials in split order.
-    // Each thread takes all its pairs of the tile at once (kP) and issues the
-    // loads of a batch of kB splits for all of them before adding: about 64
-    // loads in flight per thread, one memory round trip per batch.  These
-    // round trips run on the few CUs that finish a tile, after the rest of
-    // the grid is done, so their number sets the length of the kernel's tail.
-    constexpr int kP = ROWS * COLS / 2 / NT;
-    constexpr int kB = 64 / kP < 1 ? 1 : 64 / kP > 8 ? 8 : 64 / kP;
-    static_assert(kP >= 1 && kP * NT * 2 == ROWS * COLS, "whole pairs per thread");
-    // Every load and store below is a split's base address, the same for the
-    // whole workgroup, plus the pair's byte offset inside the split (a split
-    // holds M * N * 4 < 2^32 bytes), which keeps the addressing out of the
-    // loop's registers.
-    uint32_t off[kP];
-    bool ok[kP];
+    // split s's partials: a buffer over its M x N floats (under 2^31 bytes,
+    // which the planner ensures)
+    char *const part = (char *)ws + split_counters_bytes(gridDim.x);
+    const uint32_t slot_bytes = (uint32_t)M * (uint32_t)N * 4u;
+    auto split_rsrc = [&](int s) { return buf_rsrc(part + (size_t)s * slot_bytes, slot_bytes); };
+    const int own = blockIdx.y;
+    {
+        const __amdgpu_buffer_rsrc_t rs = split_rsrc(own);
 #pragma unroll
-    for (int q = 0; q < kP; ++q) {
-        const int pi = threadIdx.x + q * NT;
-        ok[q] = pair_ok(pi);
-        off[q] = ok[q] ? (uint32_t)pair_at(pi) * 8u : 0u;
+        for (int q = 0; q < kQ; ++q)
+            if (ok[q]) __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v[q]), rs, at[q] * 16u, 0, kPartCoherent);
     }
-    auto split_base = [&](int s) { return (char *)(part + (size_t)s * slot); };
-    float2 v[kP];
+    if (!split_tile_last_atomic((uint32_t *)ws + tile, S)) return;
+    // The last workgroup of the column tile: the other splits' partials of
+    // all its quads, kB splits at a time with every load of a batch issued
+    // before the first add (one memory round trip per batch), added in split
+    // order with its own partial (still in registers) in its place.
+    constexpr int kB = 32 / kQ < 1 ? 1 : 32 / kQ > 8 ? 8 : 32 / kQ;
+    f32x4 sum[kQ];
 #pragma unroll
-    for (int q = 0; q < kP; ++q) v[q] = make_float2(0.f, 0.f);
+    for (int q = 0; q < kQ; ++q) sum[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += kB) {
-        uint64_t b[kP][kB];
+        u32x4 b[kQ][kB];
 #pragma unroll
         for (int i = 0; i < kB; ++i) {
-            const char *base = split_base(s0 + i);
+            const int s = s0 + i;
 #pragma unroll
-            for (int q = 0; q < kP; ++q)
-                b[q][i] = ok[q] && s0 + i < S ? __hip_atomic_load((const uint64_t *)(base + off[q]), __ATOMIC_RELAXED,
-                                                                  __HIP_MEMORY_SCOPE_AGENT)
-                                              : 0ull;
+            for (int q = 0; q < kQ; ++q) b[q][i] = (u32x4){0u, 0u, 0u, 0u};
+            if (s < S && s != own) {
+                const __amdgpu_buffer_rsrc_t rs = split_rsrc(s);
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    if (ok[q]) b[q][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, at[q] * 16u, 0, kPartCoherent);
+            }
         }
 #pragma unroll
-        for (int q = 0; q < kP; ++q)
+        for (int i = 0; i < kB; ++i) {
+            const int s = s0 + i;
+            if (s >= S) break;
 #pragma unroll
-            for (int i = 0; i < kB; ++i) {
-                const float2 f = unpack_f32x2(b[q][i]);
-                v[q].x += f.x;
-                v[q].y += f.y;
-            }
+            for (int q = 0; q < kQ; ++q) sum[q] += s == own ? v[q] : bit_as<f32x4>(b[q][i]);
+        }
     }
     for (int s = 0; s < S; ++s) {
-        char *base = split_base(s);
+        const __amdgpu_buffer_rsrc_t rs = split_rsrc(s);
 #pragma unroll
-        for (int q = 0; q < kP; ++q)
-            if (ok[q]) __hip_atomic_store((uint64_t *)(base + off[q]), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 0; q < kQ; ++q)
+            if (ok[q]) __builtin_amdgcn_raw_buffer_store_b128((u32x4){0u, 0u, 0u, 0u}, rs, at[q] * 16u, 0, kPartCoherent);
     }
 #pragma unroll
-    for (int q = 0; q < kP; ++q)
-        if (ok[q]) out_pair(off[q] / 8u, v[q]);
+    for (int q = 0; q < kQ; ++q)
+        if (ok[q]) out_quad(at[q], sum[q]);
 }
 
 // One chunk's loads: scales and zero points of its group, MT row tiles of X
