@@ -253,6 +253,8 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
             s = std::min<int64_t>(4, std::max<int64_t>(1, 3 * cus / tiles));
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
+        // a split's partials are addressed as one buffer of M x N floats
+        if (M * N * 4 >= (int64_t(1) << 31)) p.splits = 1;
         // no more workgroups than CUs: two wave groups per workgroup split K
         // inside it (twice the waves per SIMD, no extra atomics)
         p.ksplit = tiles * p.splits <= cus && stages / p.splits >= 4 ? 2 : 1;

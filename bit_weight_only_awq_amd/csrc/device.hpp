@@ -331,6 +331,23 @@ __device__ __forceinline__ bool split_tile_last_atomic(uint32_t *cnt, int S) {
     return last_flag != 0;
 }
 
+// Buffer cache-policy operand for split partials: sc1, the policy of the
+// agent-scope atomic loads and stores above (through to the device-wide
+// coherence point), for 16-byte accesses that atomics do not offer.
+constexpr int kPartCoherent = 16;
+
+// The value of the same register in the other lane of the pair (lane ^ 1).
+__device__ __forceinline__ float lane_pair_swap(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
+// Four fp32 outputs as the activation type, packed for one 8-byte store.
+template <int DT>
+__device__ __forceinline__ uint2 quad_out_bits(f32x4 t) {
+    return make_uint2((uint32_t)f32_to_out_bits(t[0], DT) | ((uint32_t)f32_to_out_bits(t[1], DT) << 16),
+                      (uint32_t)f32_to_out_bits(t[2], DT) | ((uint32_t)f32_to_out_bits(t[3], DT) << 16));
+}
+
 // Partial tiles of 16-byte vectors (4 int32 or 4 fp32) for the exchange
 // above: each vector moves as two 64-bit agent-scope atomics (p 8-byte
 // aligned).  part_sum adds, in split order, the S partials of R vectors

@@ -80,7 +80,7 @@ __host__ __device__ constexpr int gemm_col(int u) { return (u & 1) + ((u >> 1) <
 // groups trade partial sums through LDS at the end.  This doubles the waves
 // per SIMD for layers with no more tiles than CUs.
 template <int DT, bool SYM, int KS, int MT, int AB, int BB, int WN>
-__global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : 3 - KS) void w4a16_gemm(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : KS == 2 ? 1 : MT == 8 ? 3 : 2) void w4a16_gemm(const uint16_t *__restrict__ x,
                                                                 const uint32_t *__restrict__ qw,
                                                                 const uint16_t *__restrict__ sc,
                                                                 const uint32_t *__restrict__ qz,
@@ -358,140 +358,158 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : 3 - KS) void w4a16_gemm
 
     // Epilogue: lane holds rows m0 + 16mt + 4gq + r and columns 8*wcol + 2pi
     // (MFMA 0) and 8*wcol + 2pi + 1 (MFMA 1).  Without a K split it writes the
-    // output; with one, each split stores its partial tile as column pairs
-    // with agent-scope atomic stores and the tile's last split sums them in
-    // split order (split_tile_last_atomic: no cache write-back fences, which
-    // cost more than the split saved).
+    // output.  With one, each split stores its partial tile and the tile's
+    // last split sums them in split order (split_tile_last_atomic: no cache
+    // write-back fences, which cost more than the split saved).
+    //
+    // KS = 2: group 1's idle iteration (odd stage count), its barrier only;
+    // then both groups hold partial sums of the whole tile.  Group 0 takes
+    // row tiles 0..H-1 and group 1 row tiles H..MT-1 (H = MT/2): each parks
+    // the other half in LDS (both rings are free once the last barrier has
+    // passed) and adds the half parked by the other group to its own, as
+    // group 0 + group 1.  res = the NTL row tiles this lane finishes, from
+    // row tile lo.  (Picked by value, not by indexing the accumulators with
+    // the group: such an index puts them in scratch.)
+    constexpr int NTL = MT / KS;
+    const int lo = KS == 1 ? 0 : grp * NTL;
+    f32x4 res[NTL][2];
+    if constexpr (KS == 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) res[mt][u] = acc[mt][u];
+    } else {
+        for (int k = s_hi - s_lo; k < iters; ++k) __syncthreads();
+        __syncthreads();  // every wave's copies have landed before the rings are reused
+        f32x4 *xfer = (f32x4 *)lds_all + (size_t)wave * MT * 64 + lane;
+        f32x4 *const mine = xfer + grp * 4 * MT * 64, *const theirs = xfer + (grp ^ 1) * 4 * MT * 64;
+#pragma unroll
+        for (int mt = 0; mt < NTL; ++mt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = grp == 0 ? acc[NTL + mt][u] : acc[mt][u];
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < NTL; ++mt)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                res[mt][u] = theirs[(mt * 2 + u) * 64] + (grp == 0 ? acc[mt][u] : acc[NTL + mt][u]);
+    }
     const int n0 = 8 * wcol + 2 * pi;
     uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
-    uint64_t *const part = (uint64_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
-    const size_t slot = (size_t)M * N / 2;  // column pairs per split
-    auto emit = [&](int mt) {
+    if (S == 1) {
         if (!col_ok) return;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 16 * mt + 4 * gq + r;
-            if (m >= M) continue;
-            if (S == 1)
-                *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(acc[mt][0][r], DT) |
-                                                        ((uint32_t)f32_to_out_bits(acc[mt][1][r], DT) << 16);
-            else
-                __hip_atomic_store(part + split * slot + ((size_t)m * N + n0) / 2,
-                                   pack_f32x2(make_float2(acc[mt][0][r], acc[mt][1][r])), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-    };
-    // The tile's last split sums the S partials of row tiles LO..LO+NT-1 in
-    // split order, two row tiles (8 of the lane's rows) at a time: the loads
-    // of four splits for those rows are in flight together (one memory round
-    // trip per four splits and pair of row tiles; the +0 terms that pad the
-    // last batch leave every sum unchanged), then the partials are cleared.
-    constexpr int kFB = 4;  // splits per batch of loads
-    auto finish2 = [&](auto lo_c) {
-        constexpr int LO = decltype(lo_c)::value;
-        f32x2 v[2][4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[t][r] = (f32x2){0.f, 0.f};
-        for (int s0 = 0; s0 < S; s0 += kFB) {
-            uint64_t b[kFB][2][4];
-#pragma unroll
-            for (int i = 0; i < kFB; ++i)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int m = m0 + 16 * (LO + t) + 4 * gq + r;
-                        b[i][t][r] = s0 + i < S && m < M
-                                         ? __hip_atomic_load(part + (s0 + i) * slot + ((size_t)m * N + n0) / 2,
-                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                         : 0ull;
-                    }
-#pragma unroll
-            for (int i = 0; i < kFB; ++i)
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float2 f = unpack_f32x2(b[i][t][r]);
-                        v[t][r] += (f32x2){f.x, f.y};
-                    }
-        }
-        for (int sp = 0; sp < S; ++sp) {
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + 16 * (LO + t) + 4 * gq + r;
-                    if (m < M)
-                        __hip_atomic_store(part + sp * slot + ((size_t)m * N + n0) / 2, 0ull, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < NTL; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + 16 * (LO + t) + 4 * gq + r;
+                const int m = m0 + 16 * (lo + i) + 4 * gq + r;
                 if (m < M)
-                    *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(v[t][r][0], DT) |
-                                                            ((uint32_t)f32_to_out_bits(v[t][r][1], DT) << 16);
+                    *(uint32_t *)(y + (size_t)m * N + n0) = (uint32_t)f32_to_out_bits(res[i][0][r], DT) |
+                                                            ((uint32_t)f32_to_out_bits(res[i][1][r], DT) << 16);
             }
-    };
-    auto finish = [&](auto lo_c, auto nt_c) {
-        constexpr int LO = decltype(lo_c)::value, NT = decltype(nt_c)::value;
-        static_assert(NT % 2 == 0, "row tiles in pairs");
-        if (!col_ok) return;
-        static_for<NT / 2>([&](auto bc) { finish2(std::integral_constant<int, LO + 2 * decltype(bc)::value>{}); });
-    };
-    if (KS == 1) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) emit(mt);
-        if (S > 1 && split_tile_last_atomic(cnt, S)) finish(std::integral_constant<int, 0>{}, std::integral_constant<int, MT>{});
         return;
     }
-    // group 1's idle iteration (odd stage count): its barrier only
-    for (int k = s_hi - s_lo; k < iters; ++k) __syncthreads();
-    __syncthreads();  // every wave's copies have landed before the rings are reused
-    // Both groups hold partial sums of the whole tile.  Group 0 finishes row
-    // tiles 0..H-1 and group 1 row tiles H..MT-1 (H = MT/2): each parks the
-    // other half in LDS (both rings are free once the last barrier has
-    // passed) and adds the half parked by the other group, always as
-    // group 0 + group 1.
-    constexpr int H = MT / 2;
-    f32x4 *xfer = (f32x4 *)lds_all + (size_t)wave * MT * 64 + lane;
-    f32x4 *const mine = xfer + grp * 4 * MT * 64, *const theirs = xfer + (grp ^ 1) * 4 * MT * 64;
-    if (grp == 0) {
-#pragma unroll
-        for (int mt = 0; mt < H; ++mt)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[H + mt][u];
+    // (256-column tiles never split K: the launcher refuses such a plan, and
+    // the split path below would only add to their register count)
+    if constexpr (WN == 8) {
+        return;
     } else {
+    // K split.  The partials move as column quads, 16 bytes each, with the
+    // cache policy of agent-scope atomics (sc1: through to the device-wide
+    // coherence point): lanes 2k and 2k+1 (pi even, odd) hold columns n0, n0+1
+    // and n0+2, n0+3 of the same rows, and one swap between them (DPP) gives
+    // the even lane rows 2h and the odd lane rows 2h+1 of all four columns.
+    // Quad (i, h) of a lane: row m0 + 16 (LO + i) + 4 gq + 2h + odd, columns
+    // qc .. qc+3.  Split s's partials are an [M, N] fp32 array after the tile
+    // counters (under 2^31 bytes: the planner sees to it).
+    const bool odd = pi & 1;
+    const int qc = n0 - (odd ? 2 : 0);
+    constexpr int NQ = 2 * NTL;
+    // the last split keeps its own quads in registers where they fit beside
+    // the loads (8 quads), else reads them back like the others
+    constexpr bool kKeepOwn = NQ <= 8;
+    // byte offset of quad q in an [M, N] fp32 array, and whether it is stored
+    auto quad_at = [&](int q, bool &ok) {
+        const int m = m0 + 16 * (lo + q / 2) + 4 * gq + 2 * (q % 2) + (odd ? 1 : 0);
+        ok = col_ok && m < M;
+        return ok ? ((uint32_t)m * (uint32_t)N + (uint32_t)qc) * 4u : 0u;
+    };
+    char *const part = (char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y);
+    const uint32_t slot_bytes = (uint32_t)M * (uint32_t)N * 4u;
+    auto split_rsrc = [&](int s) { return buf_rsrc(part + (size_t)s * slot_bytes, slot_bytes); };
+    f32x4 own[kKeepOwn ? NQ : 1];
+    {
+        const __amdgpu_buffer_rsrc_t rs = split_rsrc(split);
 #pragma unroll
-        for (int mt = 0; mt < H; ++mt)
+        for (int i = 0; i < NTL; ++i) {
+            const f32x4 c0 = res[i][0], c1 = res[i][1];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) mine[(mt * 2 + u) * 64] = acc[mt][u];
-    }
-    __syncthreads();
-    if (grp == 0) {
-#pragma unroll
-        for (int mt = 0; mt < H; ++mt) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) acc[mt][u] += theirs[(mt * 2 + u) * 64];
-            emit(mt);
+            for (int h = 0; h < 2; ++h) {
+                const float k0 = odd ? c0[2 * h + 1] : c0[2 * h], k1 = odd ? c1[2 * h + 1] : c1[2 * h];
+                const float g0 = odd ? c0[2 * h] : c0[2 * h + 1], g1 = odd ? c1[2 * h] : c1[2 * h + 1];
+                const float r0 = lane_pair_swap(g0), r1 = lane_pair_swap(g1);
+                const f32x4 v = odd ? (f32x4){r0, r1, k0, k1} : (f32x4){k0, k1, r0, r1};
+                bool ok;
+                const uint32_t off = quad_at(2 * i + h, ok);
+                if (ok) __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v), rs, off, 0, kPartCoherent);
+                if constexpr (kKeepOwn) own[2 * i + h] = v;
+            }
         }
-    } else {
+    }
+    if (!split_tile_last_atomic(cnt, S)) return;
+    // The tile's last split: for 8 quads (four row tiles) at a time, the
+    // splits' partials, kB splits per batch with every load of the batch in
+    // flight before the first add (one memory round trip per batch), added in
+    // split order (its own from registers where kept); then the output is
+    // written and every partial of the tile cleared.
+    constexpr int QC = NQ <= 8 ? NQ : 4;
+    constexpr int kB = 4;
+    static_assert(NQ % QC == 0, "whole quad chunks");
 #pragma unroll
-        for (int mt = 0; mt < H; ++mt) {
+    for (int q0 = 0; q0 < NQ; q0 += QC) {
+        bool ok[QC];
+        uint32_t off[QC];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) acc[H + mt][u] = theirs[(mt * 2 + u) * 64] + acc[H + mt][u];
-            emit(H + mt);
+        for (int q = 0; q < QC; ++q) off[q] = quad_at(q0 + q, ok[q]);
+        f32x4 sum[QC];
+#pragma unroll
+        for (int q = 0; q < QC; ++q) sum[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < S; s0 += kB) {
+            u32x4 b[QC][kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                const int sp = s0 + i;
+#pragma unroll
+                for (int q = 0; q < QC; ++q) b[q][i] = (u32x4){0u, 0u, 0u, 0u};
+                if (sp < S && !(kKeepOwn && sp == split)) {
+                    const __amdgpu_buffer_rsrc_t rs = split_rsrc(sp);
+#pragma unroll
+                    for (int q = 0; q < QC; ++q)
+                        if (ok[q]) b[q][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[q], 0, kPartCoherent);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                const int sp = s0 + i;
+                if (sp >= S) break;
+#pragma unroll
+                for (int q = 0; q < QC; ++q) {
+                    f32x4 add = bit_as<f32x4>(b[q][i]);
+                    if constexpr (kKeepOwn) add = sp == split ? own[q0 + q] : add;
+                    sum[q] += add;
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < QC; ++q)
+            if (ok[q]) *(uint2 *)((char *)y + off[q] / 2) = quad_out_bits<DT>(sum[q]);
+        for (int sp = 0; sp < S; ++sp) {
+            const __amdgpu_buffer_rsrc_t rs = split_rsrc(sp);
+#pragma unroll
+            for (int q = 0; q < QC; ++q)
+                if (ok[q]) __builtin_amdgcn_raw_buffer_store_b128((u32x4){0u, 0u, 0u, 0u}, rs, off[q], 0, kPartCoherent);
         }
     }
-    if (S > 1 && split_tile_last_atomic(cnt, S)) {
-        if (grp == 0) finish(std::integral_constant<int, 0>{}, std::integral_constant<int, H>{});
-        else finish(std::integral_constant<int, H>{}, std::integral_constant<int, H>{});
     }
 }
 
@@ -521,7 +539,7 @@ hipError_t launch_w4a16_gemm(const W4A16Args &a, const W4A16Plan &p, hipStream_t
     // a K split reduces through the workspace
     if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
     if (p.wn == 8) {
-        if (p.mt != 16 || p.ksplit != 1) return hipErrorInvalidValue;
+        if (p.mt != 16 || p.ksplit != 1 || p.splits != 1) return hipErrorInvalidValue;
         return launch_gemm_ks<1, 16, 2, 3, 8>(a, p, st);
     }
     if (p.mt == 8) return p.ksplit == 2 ? launch_gemm_ks<2, 8, 2, 3, 4>(a, p, st) : launch_gemm_ks<1, 8, 2, 3, 4>(a, p, st);

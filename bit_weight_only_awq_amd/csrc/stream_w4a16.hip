@@ -49,7 +49,6 @@ __device__ __forceinline__ int lds_col(int c) {
 // device-wide coherence point), as 16-byte buffer accesses -- half the
 // requests of 8-byte atomics; the tail of the kernel is the last workgroups'
 // partial traffic, so its request count sets the tail's length.
-constexpr int kPartCoherent = 16;  // buffer cache-policy operand: sc1
 
 template <int NT, int DT, int ROWS, int COLS, int SLOTS>
 __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_t *__restrict__ y,
@@ -78,11 +77,7 @@ __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_
             for (int w = 1; w < SLOTS; ++w) v[q] += *(const f32x4 *)(p + w * ROWS * COLS);
         }
     }
-    auto out_quad = [&](uint32_t a, f32x4 t) {
-        const uint32_t lo = (uint32_t)f32_to_out_bits(t[0], DT) | ((uint32_t)f32_to_out_bits(t[1], DT) << 16);
-        const uint32_t hi = (uint32_t)f32_to_out_bits(t[2], DT) | ((uint32_t)f32_to_out_bits(t[3], DT) << 16);
-        *(uint2 *)(y + 4 * (size_t)a) = make_uint2(lo, hi);
-    };
+    auto out_quad = [&](uint32_t a, f32x4 t) { *(uint2 *)(y + 4 * (size_t)a) = quad_out_bits<DT>(t); };
     if (S == 1) {
 #pragma unroll
         for (int q = 0; q < kQ; ++q)
