@@ -154,6 +154,23 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
             p.cs = 4;
             p.splits = (int)cdiv(K / 128, p.waves);
         }
+        // M >= 4: workgroups of 8 waves (chunks chosen by the same rules)
+        // wherever their grid still runs in one round (two per CU, one at
+        // CS = 4): half the K splits, so half the per-element atomics.
+        // Measured on the Llama-2-7B layers: M = 8 qkv 14.9 -> 12.7 us, o
+        // 10.9 -> 8.9, down 14.5 -> 12.9; M = 4 qkv 12.0 -> 10.3, o 8.2 ->
+        // 7.4, down 11.7 -> 10.7; slower at M = 1 (qkv 8.4 -> 9.3) and where
+        // the grid takes two rounds (gate/up at M = 4: 15.1 -> 18.4)
+        if (M >= 4) {
+            int cs8 = G >= 64 ? 2 : 1;
+            if (G % 128 == 0 && (int64_t)p.tiles_n * cdiv(K / 128, 8) >= 3 * cus / 4) cs8 = 4;
+            const int64_t splits8 = cdiv(K / (32 * cs8), 8);
+            if ((int64_t)p.tiles_n * splits8 <= (cs8 >= 4 ? 1 : 2) * cus) {
+                p.waves = 8;
+                p.cs = cs8;
+                p.splits = (int)splits8;
+            }
+        }
         tiles = p.tiles_n;
     }
     if (M > 8 || p.splits > kMaxSplitK) {

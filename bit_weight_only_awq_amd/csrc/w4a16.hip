@@ -129,9 +129,11 @@ __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red
 // without spills (measured faster than the compiler's own 3-wave allocation).
 // CS = 4 (one 128-k group per wave, about 140 registers, 3 waves per SIMD)
 // halves the workgroup count for layers whose CS = 2 grid would not be
-// resident all at once, so that they still run as a single round.
+// resident all at once, so that they still run as a single round.  WAVES = 8
+// (the same waves per SIMD in half as many workgroups) halves the K splits,
+// and so the per-element atomics, which grow with M.
 template <int BLK, int CS, int DT, bool SYM, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, CS >= 4 ? 2 : 4) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
+__global__ __launch_bounds__(64 * WAVES, (CS >= 4 ? 2 : 4) * 4 / WAVES) void w4a16_decode(const uint16_t *__restrict__ x, const uint32_t *__restrict__ qw,
                                                     const uint16_t *__restrict__ sc,
                                                     const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
                                                     uint64_t *__restrict__ acc64, int M, int N, int K, int G) {
@@ -449,6 +451,12 @@ hipError_t launch_w4a16_decode(const W4A16Args &a, const W4A16Plan &p, hipStream
         case 422: return launch_decode_dt<2, 2, 4>(a, p, st);
         case 414: return launch_decode_dt<1, 4, 4>(a, p, st);
         case 424: return launch_decode_dt<2, 4, 4>(a, p, st);
+        case 811: return launch_decode_dt<1, 1, 8>(a, p, st);
+        case 812: return launch_decode_dt<1, 2, 8>(a, p, st);
+        case 821: return launch_decode_dt<2, 1, 8>(a, p, st);
+        case 822: return launch_decode_dt<2, 2, 8>(a, p, st);
+        case 814: return launch_decode_dt<1, 4, 8>(a, p, st);
+        case 824: return launch_decode_dt<2, 4, 8>(a, p, st);
         default: return hipErrorInvalidValue;
     }
 }
