@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdint>
 #include <mutex>
@@ -20,6 +21,20 @@ static constexpr int64_t kMaxDim = int64_t(1) << 20;
 // The planners below size grids from the device's compute-unit count (cus):
 // two workgroups of 4 waves per CU is the target fill of the tiled kernels.
 static int64_t target_workgroups(const DeviceProps &d) { return 2 * (int64_t)d.cus; }
+
+// K splits of the skinny W4A8 kernels (counting atomics, M <= 64): every
+// split adds one atomic per output element, all S of an element landing on
+// one address at about the same time, so their cost grows faster than S * M *
+// N, while long K needs the splits to spread its stream.  The split count
+// that fills the CUs (s) is capped at 2^20 sqrt(K / 4096) / (M N), rounded
+// down.  Measured (int8 GEMM, rotated weights): 4096 x 14336 at M = 64, 3
+// splits 42.5 us, 2 28.5, 1 21.4 (INT4-FP8 39.3 -> 18.4 with 1); at M = 32
+// 19.1 / 18.0 / 16.7; 4096 x 4096 at M = 64, 8 splits 22.5, 4 20.7; the QQQ
+// shape (K = 21760) best at the 4 to 8 that fill the CUs.
+static int64_t skinny_splits(int64_t s, int64_t M, int64_t N, int64_t K) {
+    const double cap = 1048576.0 * std::sqrt((double)K / 4096.0) / ((double)M * (double)N);
+    return std::max<int64_t>(1, std::min<int64_t>(s, (int64_t)cap));
+}
 // The W4A16 LDS GEMM takes M above 64 (the decode kernel takes M <= 8, the
 // streaming kernel 8 < M <= 64).
 static constexpr int64_t kW16LdsMinM = 64;
@@ -326,6 +341,7 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d)
         tiles = p.tiles_n;
         int64_t s = cdiv(target_workgroups(d), tiles);
         s = std::min<int64_t>(s, std::max<int64_t>(1, T / 4));
+        s = skinny_splits(s, M, N, K);
         p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
     } else {
         p.kind = 1;
@@ -394,6 +410,7 @@ W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d) {
         tiles = p.tiles_n;
         int64_t s = cdiv(target_workgroups(d), tiles);
         s = std::min<int64_t>(s, std::max<int64_t>(1, T / 2));
+        s = skinny_splits(s, M, N, K);
         p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
         p.workspace_bytes = p.splits > 1 ? (size_t)M * N * sizeof(uint64_t) : 0;
     } else {

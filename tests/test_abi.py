@@ -284,6 +284,29 @@ def test_gemm_k_split_rule():
         assert p.workspace_bytes == (0 if s == 1 else L.lib().awq_workspace_bytes(gemm, M, N, K, 128, 0))
 
 
+def test_split_caps_of_the_atomic_kernels():
+    """Kernels that reduce K splits through per-element counting atomics cap
+    their splits as M grows: the skinny W4A8 kernels (int8 and INT4-FP8) at
+    2^20 sqrt(K / 4096) / (M N), the decode GEMV with 8-wave workgroups at
+    M >= 4 where that grid still runs in one round (half the splits)."""
+    for op in (L.AWQ_OP_W4A8_GEMM, L.AWQ_OP_W4A8_FP8_GEMM):
+        want = {  # (M, N, K): splits on a whole MI355X
+            (1, 14336, 4096): 5, (32, 14336, 4096): 2, (48, 14336, 4096): 1, (64, 14336, 4096): 1,
+            (48, 4096, 4096): 5, (64, 4096, 4096): 4, (64, 8192, 21760): 4, (16, 8192, 21760): 8,
+        }
+        for (M, N, K), s in want.items():
+            p = _plan(op, M, N, K, -1, cus=256)
+            assert (p.kernel, p.splits) == (0, s), (op, M, N, K, p.splits)
+            assert p.workspace_bytes == (0 if s == 1 else M * N * 8)
+    gemv = L.AWQ_OP_GEMV_W4A16
+    # Llama-2-7B qkv (4096 x 12288): 48 column tiles; 16 splits of 4 waves at
+    # M = 1, 4 splits of 8 waves (128-k chunks) at M = 8; gate/up (4096 x
+    # 22016) keeps 4 waves at M = 8 (8 waves would take two rounds)
+    assert (_plan(gemv, 1, 12288, 4096, 128, cus=256).splits, _plan(gemv, 8, 12288, 4096, 128, cus=256).splits) == (16, 4)
+    assert _plan(gemv, 8, 4096, 4096, 128, cus=256).splits == 8
+    assert _plan(gemv, 8, 22016, 4096, 128, cus=256).splits == 8
+
+
 def test_dequant_validation():
     lib = L.lib()
     assert lib.awq_dequant_w4a16(A, A, A, None, 4096, 4096, 128, 0, None) == L.AWQ_EINVAL   # no output

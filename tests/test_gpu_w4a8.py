@@ -94,7 +94,10 @@ def test_w4a8_qqq_shape(M, G):
                                    (2049, 256, 4104), (4000, 128, 2056),
                                    # one 128 x 256 tile per CU (K split inside the workgroup),
                                    # ragged, with an odd stage count
-                                   (1000, 1088, 8184)])
+                                   (1000, 1088, 8184),
+                                   # the skinny kernel where the atomic cap leaves one split
+                                   # (48 and 64 rows on 4096 x 14336) or five (48 on 4096 x 4096)
+                                   (48, 4096, 14336), (64, 4096, 14336), (48, 4096, 4096)])
 def test_w4a8_shapes(M, K, N, G):
     if G > 0 and K % G:
         pytest.skip("K not a multiple of G")

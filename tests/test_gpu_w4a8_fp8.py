@@ -91,7 +91,9 @@ def test_fp8_qqq_shape(M, dt):
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (2048, 4096, 4096), (1, 4096, 14336), (2048, 4096, 14336),
                                    (5, 128, 8), (17, 256, 136), (33, 384, 520), (65, 512, 264), (129, 512, 1032),
-                                   (300, 4096, 1032), (7, 130944, 64)])
+                                   (300, 4096, 1032), (7, 130944, 64),
+                                   # the skinny kernel with one split (the atomic cap) and with five
+                                   (64, 4096, 14336), (48, 4096, 4096)])
 def test_fp8_shapes(M, K, N):
     rows = None if M <= 300 else sample_rows(M, seed=N)
     _gemm_check(M, K, N, 0, rows=rows)
