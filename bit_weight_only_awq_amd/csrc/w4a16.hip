@@ -22,7 +22,9 @@
 //    across the GPU.  fp16: the B operand is the masked nibble pair read as
 //    fp16 subnormals (exact on the matrix cores, one AND per pair); zero point
 //    and scale are applied once per chunk on the fp32 sums.  bf16: the B
-//    operand is the exact integer (q - z), scaled once per chunk.  The 4 waves of a
+//    operand is the exact integer 128 + q (the nibble ORed into the mantissa
+//    of 128.0), zero point and scale applied once per chunk in the same
+//    way.  The 4 waves of a
 //    workgroup (4 consecutive chunks) are reduced through LDS, workgroups
 //    along K through counting fixed-point atomics (fp16) or per-tile fp32
 //    partials (bf16; device.hpp).
@@ -97,24 +99,26 @@ __device__ __forceinline__ void decode_epilogue(f32x4 (&acc)[BLK][8], float *red
     // cleared (the workspace is zero again after the call).  The loads of a
     // batch of splits are all issued before the first is added, so the sum
     // costs one memory round trip per batch rather than one per split.
-    constexpr int kBatch = 16;
+    // (Each load is a split's base address, the same for the whole
+    // workgroup, plus the element's 32-bit byte offset: a split holds
+    // M * N * 4 < 2^31 bytes.)
+    constexpr int kBatch = 32;
     for (int idx = threadIdx.x; idx < total; idx += 64 * WAVES) {
         const int m = idx / COLS, c = idx - m * COLS;
         const int n = n_base + c;
         if (n >= N) continue;
-        float *p = part + (size_t)m * N + n;
+        const uint32_t off = ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 4u;
+        auto at = [&](int sp) { return (float *)((char *)(part + (size_t)sp * slot) + off); };
         float v = 0.f;
         for (int s0 = 0; s0 < S; s0 += kBatch) {
             float b[kBatch];
 #pragma unroll
             for (int i = 0; i < kBatch; ++i)
-                b[i] = s0 + i < S ? __hip_atomic_load(&p[(size_t)(s0 + i) * slot], __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0.f;
+                b[i] = s0 + i < S ? __hip_atomic_load(at(s0 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
 #pragma unroll
             for (int i = 0; i < kBatch; ++i) v += b[i];
         }
-        for (int s = 0; s < S; ++s) __hip_atomic_store(&p[(size_t)s * slot], 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int sp = 0; sp < S; ++sp) __hip_atomic_store(at(sp), 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         y[(size_t)m * N + n] = f32_to_out_bits(v, DT);
     }
 }
@@ -243,37 +247,58 @@ __global__ __launch_bounds__(64 * WAVES, (CS >= 4 ? 2 : 4) * 4 / WAVES) void w4a
                     }
             }
         } else {
+            // B operand = the exact integer 128 + q as bf16: the nibble ORed
+            // into the mantissa of 128.0 (one bitwise op per pair; an upper
+            // nibble is shifted down first).  The zero point and scale are
+            // applied per chunk on the fp32 sums: s * (sum(x (128 + q)) -
+            // (128 + z) * sum(x)), with sum(x) from one extra MFMA against an
+            // all-ones operand.  Every product is exact in fp32, and the
+            // sums of a chunk keep 2^-24 relative to 128 sum|x|, far below
+            // the bf16 output's rounding.
+            const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+            f32x4 rs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < CS; ++s) rs = mfma_bf16(a[s], ones, rs);
 #pragma unroll
             for (int b = 0; b < BLK; ++b) {
-                ZeroConsts<DT> zc;
-                zero_consts<DT, SYM>(zc, zw[b]);
 #pragma unroll
                 for (int s = 0; s < CS; ++s) {
-                    uint32_t px[4], py[4];
+                    // the pair registers shifted by 0, 4, 8 and 12 bits: the
+                    // wanted nibble of column t then sits at bits 0 and 16
+                    uint32_t px[4][4], py[4][4];
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
-                        px[p] = pair_x(w[s][2 * p][b], w[s][2 * p + 1][b]);
-                        py[p] = pair_y(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                        px[p][0] = pair_x(w[s][2 * p][b], w[s][2 * p + 1][b]);
+                        py[p][0] = pair_y(w[s][2 * p][b], w[s][2 * p + 1][b]);
+#pragma unroll
+                        for (int h = 1; h < 4; ++h) {
+                            px[p][h] = px[p][0] >> (4 * h);
+                            py[p][h] = py[p][0] >> (4 * h);
+                        }
                     }
-#define AWQ4_COL(T_)                                                                        \
-    {                                                                                       \
-        u32x4 bop;                                                                          \
-        _Pragma("unroll") for (int p = 0; p < 4; ++p) bop[p] =                              \
-            qz_pair<DT, T_>(col_src_y(T_) ? py[p] : px[p], zc);                             \
-        acc[b][T_] = mma<DT>(a[s], bop, acc[b][T_]);                                        \
+#define AWQ4_COL(T_)                                                                                \
+    {                                                                                               \
+        constexpr int sh = (col_shift(T_) + 4 * col_hi(T_)) / 4;                                    \
+        u32x4 bop;                                                                                  \
+        _Pragma("unroll") for (int p = 0; p < 4; ++p) bop[p] = __builtin_amdgcn_bitop3_b32(        \
+            col_src_y(T_) ? py[p][sh] : px[p][sh], 0x000F000Fu, 0x43004300u, 0xEA);                 \
+        acc[b][T_] = mfma_bf16(a[s], bop, acc[b][T_]);                                              \
     }
                     AWQ4_COL(0) AWQ4_COL(1) AWQ4_COL(2) AWQ4_COL(3) AWQ4_COL(4) AWQ4_COL(5) AWQ4_COL(6) AWQ4_COL(7)
 #undef AWQ4_COL
                 }
-                // the group scale, once per chunk, on the fp32 sums
-                float st[8];
+                float st[8], bt[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) st[t] = scale_f32<DT>(s4[b], t);
+                for (int t = 0; t < 8; ++t) {
+                    st[t] = scale_f32<DT>(s4[b], t);
+                    const float zt = SYM ? 8.0f : (float)((zw[b] >> (4 * col_nibble(t))) & 0xFu);
+                    bt[t] = st[t] * (128.0f + zt);  // exact: 8 + 8 significant bits
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (r < M) {
 #pragma unroll
-                        for (int t = 0; t < 8; ++t) acc[b][t][r] *= st[t];
+                        for (int t = 0; t < 8; ++t) acc[b][t][r] = __builtin_fmaf(acc[b][t][r], st[t], -bt[t] * rs[r]);
                     }
             }
         }
