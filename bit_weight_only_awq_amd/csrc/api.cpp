@@ -171,12 +171,21 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         }
         // bf16 reduces its splits through per-tile fp32 partials (several
         // memory round trips per workgroup, against one for the fp16
-        // counting atomics), so at M <= 2 it takes one 128-k group per wave:
-        // the fewest splits.  Measured on the Llama-2-7B layers at M = 1: o
-        // 12.0 -> 8.2 us, down 16.3 -> 12.4, qkv 11.4 -> 11.1, gate/up level
-        if (dtype == AWQ_DTYPE_BF16 && M <= 2 && G % 128 == 0) {
-            p.cs = 4;
-            p.splits = (int)cdiv(K / 128, p.waves);
+        // counting atomics), so at M <= 2 it takes the fewest splits: one
+        // 128-k group per wave, or with smaller groups 8-wave workgroups of
+        // group-sized chunks.  Measured at M = 1: Llama-2-7B o 12.0 -> 8.2
+        // us, down 16.3 -> 12.4, qkv 11.4 -> 11.1, gate/up level (g128);
+        // 4096 x 4096 and 11008 x 4096 12.0 -> 8.4 and 16.5 -> 12.5 us (g64),
+        // 12.0 -> 9.4 and 25.8 -> 17.1 us (g32), even where the grid then
+        // takes two rounds
+        if (dtype == AWQ_DTYPE_BF16 && M <= 2) {
+            if (G % 128 == 0) {
+                p.cs = 4;
+            } else {
+                p.waves = 8;
+                p.cs = G >= 64 ? 2 : 1;
+            }
+            p.splits = (int)cdiv(K / (32 * p.cs), p.waves);
         }
         // M >= 4: workgroups of 8 waves (chunks chosen by the same rules)
         // wherever their grid still runs in one round (two per CU, one at
