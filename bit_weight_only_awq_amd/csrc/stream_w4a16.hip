@@ -13,9 +13,9 @@
 // ring, so that the grid fits the GPU in one round with few K splits and the
 // weight stream never drains between chunks.  Lanes are laid out as in the
 // decode kernel: lane (j, gq) holds word-column j of the tile (8 outputs) at
-// the 8 k-rows 8 gq + e of each 32-k step.  Per chunk, the exact (q - z) products
-// are summed on the matrix cores (MT 16-row tiles of X) and scaled once in
-// fp32.  The waves' tiles are then added through LDS in wave order and the
+// the 8 k-rows 8 gq + e of each 32-k step.  The matrix cores multiply MT
+// 16-row tiles of X by B = (q - z) * s rounded once (fp16, four row tiles),
+// or by the exact (q - z) with the chunk's sums scaled once in fp32.  The waves' tiles are then added through LDS in wave order and the
 // S workgroups of a column tile exchange fp32 partials, the last one adding
 // them in split order -- so the result does not depend on timing.
 #include "device.hpp"
@@ -180,10 +180,17 @@ __device__ __forceinline__ void stream_issue(StreamBuf<MT, CS> &b, const StreamO
             b.w[s][e] = __builtin_nontemporal_load((const uint32_t *)at(qw + (size_t)(k0 + 32 * s + e) * nw, o.w));
 }
 
-// One chunk into the accumulators.  B = the exact integer (q - z) in the
-// activation type; for each column MFMA the chunk's CS k-steps are summed in a
-// small fp32 temporary that is then scaled by s once and added (so no weight
-// is rounded and the scale is applied in fp32, as in the decode kernel).
+// One chunk into the accumulators.
+//  fp16 with four row tiles: B = (q - z) * s rounded once to fp16 (the exact
+//  (q - z) from the magic-exponent pair, times the column's scale in both
+//  halves), the MFMAs accumulating straight into acc -- the weights the LDS
+//  GEMM uses.  At 64 rows the fp32 path below costs 128 FMAs a chunk against
+//  64 packed multiplies here: gate/up at M = 64 40.3 -> 36.3 us, down 31.3 ->
+//  29.4; with one or two row tiles the multiplies cost more than the FMAs
+//  they replace (M = 32 gate/up 28.8 -> 29.7 us), so those keep the fp32 path.
+//  Otherwise: B = the exact integer (q - z); for each column MFMA the chunk's
+//  CS k-steps are summed in a small fp32 temporary that is then scaled by s
+//  once and added (no weight is rounded).
 template <int MT, int CS, int DT, bool SYM>
 __device__ __forceinline__ void stream_compute(const StreamBuf<MT, CS> &b, f32x4 (&acc)[MT][8]) {
     ZeroConsts<DT> zc;
@@ -196,28 +203,46 @@ __device__ __forceinline__ void stream_compute(const StreamBuf<MT, CS> &b, f32x4
             px[s][p] = pair_x(b.w[s][2 * p], b.w[s][2 * p + 1]);
             py[s][p] = pair_y(b.w[s][2 * p], b.w[s][2 * p + 1]);
         }
-    static_for<8>([&](auto tc) {
-        constexpr int T = decltype(tc)::value;
-        f32x4 t[MT];
+    if constexpr (DT == DT_F16 && MT >= 4) {
+        static_for<8>([&](auto tc) {
+            constexpr int T = decltype(tc)::value;
+            const uint32_t sb = scale_bits<DT>(b.s4, T);
+            const uint32_t sc2 = sb | (sb << 16);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) t[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < CS; ++s) {
+                u32x4 bop;
 #pragma unroll
-        for (int s = 0; s < CS; ++s) {
-            u32x4 bop;
+                for (int p = 0; p < 4; ++p)
+                    bop[p] = bit_as<uint32_t>(bit_as<f16x2>(qz_pair<DT, T>(col_src_y(T) ? py[s][p] : px[s][p], zc)) *
+                                              bit_as<f16x2>(sc2));
 #pragma unroll
-            for (int p = 0; p < 4; ++p) bop[p] = qz_pair<DT, T>(col_src_y(T) ? py[s][p] : px[s][p], zc);
+                for (int mt = 0; mt < MT; ++mt) acc[mt][T] = mma<DT>(b.a[mt][s], bop, acc[mt][T]);
+            }
+        });
+    } else {
+        static_for<8>([&](auto tc) {
+            constexpr int T = decltype(tc)::value;
+            f32x4 t[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) t[mt] = mma<DT>(b.a[mt][s], bop, t[mt]);
-        }
-        const float st = scale_f32<DT>(b.s4, T);
+            for (int mt = 0; mt < MT; ++mt) t[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int s = 0; s < CS; ++s) {
+                u32x4 bop;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[mt][T][r] = __builtin_fmaf(t[mt][r], st, acc[mt][T][r]);
-        // two groups of four columns: bounds how many temporaries the
-        // scheduler keeps live at once (all eight spill a few registers)
-        if (T == 3) __builtin_amdgcn_sched_barrier(0);
-    });
+                for (int p = 0; p < 4; ++p) bop[p] = qz_pair<DT, T>(col_src_y(T) ? py[s][p] : px[s][p], zc);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) t[mt] = mma<DT>(b.a[mt][s], bop, t[mt]);
+            }
+            const float st = scale_f32<DT>(b.s4, T);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[mt][T][r] = __builtin_fmaf(t[mt][r], st, acc[mt][T][r]);
+            // two groups of four columns: bounds how many temporaries the
+            // scheduler keeps live at once (all eight spill a few registers)
+            if (T == 3) __builtin_amdgcn_sched_barrier(0);
+        });
+    }
 }
 
 // Keeps a buffer's loads where they are issued, a chunk ahead of their use:
