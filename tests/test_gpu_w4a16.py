@@ -129,6 +129,10 @@ MAIN_TILE_CASES = [
     (96, 14336, 4096, 0, (8, 2, 8, 128)),    # eight splits (two load batches in the last workgroup)
     (96, 4096, 4096, 0, (8, 2, 4, 128)),     # below 128 rows: 128-row tiles, K split both ways
     (100, 4096, 6144, 0, (8, 2, 4, 128)),    # the same with a ragged last row tile
+    # K splits with a ragged last column tile (its quads past N never stored)
+    (100, 4096, 4384, 0, (8, 2, 4, 128)),
+    (700, 14336, 4384, 0, (8, 1, 3, 128)),   # single-group splits: 16 quads a lane, two chunks of 8
+    (130, 4096, 4128, 0, (8, 2, 3, 128)),
 ]
 
 
@@ -275,6 +279,19 @@ def test_ragged_and_small_shapes(M, K, N, G):
     if M <= 8:
         yg, y64, _ = _run(c, "gemv")
         check_fp(yg, y64, "f16", f"ragged gemv {M}x{K}x{N} g{G}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_gemv_plans_by_rows_and_dtype(M, G, dtype):
+    """The decode kernel's plans between one and eight rows: 8-wave workgroups
+    (M >= 4 where their grid fits one round; bf16 at M <= 2 with 32- and 64-k
+    groups), one 128-k group per wave (bf16 at M <= 2), on 11008 x 4104 --
+    long K, many splits, a ragged last column tile."""
+    c = synthgen.w4a16_case(M, 11008, 4104, G, dtype=dtype)
+    yg, y64, _ = _run(c, "gemv")
+    check_fp(yg, y64, dtype, f"gemv plans M={M} G={G} {dtype}")
 
 
 @pytest.mark.parametrize("sym", [False, True])
