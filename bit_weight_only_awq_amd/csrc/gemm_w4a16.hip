@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : KS == 2 ? 1 : MT == 8 ?
                                                                 const uint16_t *__restrict__ sc,
                                                                 const uint32_t *__restrict__ qz,
                                                                 uint16_t *__restrict__ y, uint64_t *__restrict__ acc64,
-                                                                int M, int N, int K, int G, int S) {
+                                                                int M, int N, int K, int G, int S, int sep) {
     using R = GRing<MT, AB, BB, WN>;
     static_assert(KS == 1 || (WN == 4 && KS * R::LDS >= 2 * 4 * MT * 64 * 16), "the K-split handover fits in the rings");
     static_assert(AB >= 2 && BB >= 3 && MT > kPrefA, "ring depths and prefetch distance");
@@ -438,6 +438,9 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : KS == 2 ? 1 : MT == 8 ?
     const uint32_t slot_bytes = (uint32_t)M * (uint32_t)N * 4u;
     auto split_rsrc = [&](int s) { return buf_rsrc(part + (size_t)s * slot_bytes, slot_bytes); };
     f32x4 own[kKeepOwn ? NQ : 1];
+    // sep: the reduction kernel launched next adds the splits (plain stores,
+    // made visible by the kernel boundary); else the tile's last split adds
+    // them below.
     {
         const __amdgpu_buffer_rsrc_t rs = split_rsrc(split);
 #pragma unroll
@@ -451,12 +454,15 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : KS == 2 ? 1 : MT == 8 ?
                 const f32x4 v = odd ? (f32x4){r0, r1, k0, k1} : (f32x4){k0, k1, r0, r1};
                 bool ok;
                 const uint32_t off = quad_at(2 * i + h, ok);
-                if (ok) __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v), rs, off, 0, kPartCoherent);
+                if (ok) {
+                    if (sep) __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v), rs, off, 0, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v), rs, off, 0, kPartCoherent);
+                }
                 if constexpr (kKeepOwn) own[2 * i + h] = v;
             }
         }
     }
-    if (!split_tile_last_atomic(cnt, S)) return;
+    if (sep || !split_tile_last_atomic(cnt, S)) return;
     // The tile's last split: for 8 quads (four row tiles) at a time, the
     // splits' partials, kB splits per batch with every load of the batch in
     // flight before the first add (one memory round trip per batch), added in
@@ -513,13 +519,57 @@ __global__ __launch_bounds__(64 * WN * KS, WN == 8 ? 1 : KS == 2 ? 1 : MT == 8 ?
     }
 }
 
+// K-split reduction of the W4A16 GEMM kernels (this one and the streaming
+// kernel) where the partial tiles are large: y = the S fp32 partial [M, N]
+// arrays added in split order from +0 and rounded once to the activation
+// type -- the same sums as the in-kernel exchange -- and the partials then
+// zeroed (the workspace is zero again after the call).  A launch of its own:
+// the kernel boundary makes the partials visible to plain loads, and the
+// reduction is spread over the whole GPU instead of the few CUs that finish
+// the tiles, which move device-coherent data at about 50 GB/s each.  One
+// thread per quad of 4 outputs; the loads of 8 splits in flight together.
+template <int DT>
+__global__ __launch_bounds__(256) void w4a16_split_reduce(f32x4 *__restrict__ part, uint16_t *__restrict__ y,
+                                                          int64_t quads, int S) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= quads) return;
+    f32x4 *const p = part + q;
+    f32x4 v = (f32x4){0.f, 0.f, 0.f, 0.f};
+    constexpr int kB = 8;
+    for (int s0 = 0; s0 < S; s0 += kB) {
+        f32x4 b[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) b[i] = s0 + i < S ? p[(s0 + i) * quads] : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            if (s0 + i < S) v += b[i];
+    }
+    *(uint2 *)(y + 4 * q) = quad_out_bits<DT>(v);
+    for (int s = 0; s < S; ++s) p[s * quads] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+hipError_t launch_w4a16_split_reduce(const W4A16Args &a, const W4A16Plan &p, int64_t tiles, hipStream_t st) {
+    if (p.acc == nullptr || p.splits < 2 || (a.M * a.N) % 4) return hipErrorInvalidValue;
+    f32x4 *const part = (f32x4 *)((char *)p.acc + split_counters_bytes(tiles));
+    const int64_t quads = a.M * a.N / 4;
+    const dim3 grid((unsigned)((quads + 255) / 256));
+    if (a.dtype == DT_F16)
+        hipLaunchKernelGGL(w4a16_split_reduce<DT_F16>, grid, dim3(256), 0, st, part, (uint16_t *)a.y, quads, p.splits);
+    else
+        hipLaunchKernelGGL(w4a16_split_reduce<DT_BF16>, grid, dim3(256), 0, st, part, (uint16_t *)a.y, quads, p.splits);
+    return hipGetLastError();
+}
+
 template <int DT, bool SYM, int KS, int MT, int AB, int BB, int WN>
 static hipError_t launch_gemm_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     dim3 grid(p.tiles_n, p.tiles_m, p.splits);
+    const int sep = split_reduce_apart(p.splits, 16 * MT);
     hipLaunchKernelGGL((w4a16_gemm<DT, SYM, KS, MT, AB, BB, WN>), grid, dim3(64 * WN * KS), 0, st, (const uint16_t *)a.x,
                        (const uint32_t *)a.qweight, (const uint16_t *)a.scales, (const uint32_t *)a.qzeros,
-                       (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
-    return hipGetLastError();
+                       (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits, sep);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !sep) return e;
+    return launch_w4a16_split_reduce(a, p, (int64_t)p.tiles_n * p.tiles_m, st);
 }
 
 template <int KS, int MT, int AB, int BB, int WN>

@@ -116,6 +116,15 @@ hipError_t launch_w4a16_tiled(const W4A16Args &a, const W4A16Plan &p, hipStream_
 // eight waves up to 32 rows, four 512-register waves at 64
 constexpr int kStreamWaves(int mt) { return mt >= 4 ? 4 : 8; }
 hipError_t launch_w4a16_stream(const W4A16Args &a, const W4A16Plan &p, hipStream_t st);
+// K-split reduction of the LDS GEMM and the streaming kernel in a launch of
+// its own (partials after the counters of `tiles` tiles), taken where a
+// tile's partials are large: S splits of `rows`-row tiles, S x rows >= 384.
+// Measured on the Llama-3-8B layers: down at M = 96 and 128 (eight splits of
+// 128 rows) 37.2 -> 31.7 and 42.6 -> 34.8 us, o at M = 64 (six of 64) 18.7 ->
+// 17.2 us; smaller volumes keep the in-kernel exchange, which saves the
+// launch (qkv at M = 32, five splits of 32 rows: 11.9 against 12.2 us).
+constexpr bool split_reduce_apart(int splits, int rows) { return splits > 1 && splits * rows >= 384; }
+hipError_t launch_w4a16_split_reduce(const W4A16Args &a, const W4A16Plan &p, int64_t tiles, hipStream_t st);
 hipError_t launch_w4a8_gemm_lds(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);
 hipError_t launch_w4a8_quant(const void *x, int8_t *a8, float *s1, int64_t M, int64_t K, int dtype, hipStream_t st);
 hipError_t launch_w4a8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st);

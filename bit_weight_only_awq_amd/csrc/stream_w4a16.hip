@@ -40,9 +40,10 @@ __device__ __forceinline__ int lds_col(int c) {
 // LDS (ROWS x COLS floats each, COLS a row in the order lds_col gives), added
 // in slot order -- goes out: written directly when the K range is not split
 // (S == 1); otherwise handed over as fp32 partials (one M x N array per
-// split after the tile counters, device.hpp: split_tile_last_atomic), the
-// last workgroup of the column tile adding them in split order, clearing
-// them and writing the output.  Everything moves as quads of columns (N is a
+// split after the tile counters), added in split order -- by the reduction
+// kernel launched next where they are large (sep), else by the last
+// workgroup of the column tile (device.hpp: split_tile_last_atomic), which
+// also clears them and writes the output.  Everything moves as quads of columns (N is a
 // multiple of 8, so a quad never straddles the last column): 8-byte output
 // stores, 16-byte partial loads and stores.  The partials move with the
 // cache policy of agent-scope atomic loads and stores (sc1: through to the
@@ -52,7 +53,8 @@ __device__ __forceinline__ int lds_col(int c) {
 
 template <int NT, int DT, int ROWS, int COLS, int SLOTS>
 __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_t *__restrict__ y,
-                                                       uint64_t *__restrict__ ws, int M, int N, int tile, int S) {
+                                                       uint64_t *__restrict__ ws, int M, int N, int tile, int S,
+                                                       int sep) {
     constexpr int QR = COLS / 4;         // quads per row
     constexpr int kQ = ROWS * QR / NT;   // quads per thread, whole tile
     static_assert(kQ >= 1 && kQ * NT == ROWS * QR, "whole quads per thread");
@@ -90,13 +92,19 @@ __device__ __forceinline__ void tile_store_or_exchange(const float *red, uint16_
     const uint32_t slot_bytes = (uint32_t)M * (uint32_t)N * 4u;
     auto split_rsrc = [&](int s) { return buf_rsrc(part + (size_t)s * slot_bytes, slot_bytes); };
     const int own = blockIdx.y;
+    // sep: the reduction kernel launched next adds the splits (plain stores,
+    // made visible by the kernel boundary); else the column tile's last
+    // workgroup adds them below.
     {
         const __amdgpu_buffer_rsrc_t rs = split_rsrc(own);
 #pragma unroll
         for (int q = 0; q < kQ; ++q)
-            if (ok[q]) __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v[q]), rs, at[q] * 16u, 0, kPartCoherent);
+            if (ok[q]) {
+                if (sep) __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v[q]), rs, at[q] * 16u, 0, 0);
+                else __builtin_amdgcn_raw_buffer_store_b128(bit_as<u32x4>(v[q]), rs, at[q] * 16u, 0, kPartCoherent);
+            }
     }
-    if (!split_tile_last_atomic((uint32_t *)ws + tile, S)) return;
+    if (sep || !split_tile_last_atomic((uint32_t *)ws + tile, S)) return;
     // The last workgroup of the column tile: the other splits' partials of
     // all its quads, kB splits at a time with every load of a batch issued
     // before the first add (one memory round trip per batch), added in split
@@ -259,7 +267,8 @@ __global__ __launch_bounds__(64 * WV, 1) void w4a16_stream(const uint16_t *__res
                                                           const uint32_t *__restrict__ qw,
                                                           const uint16_t *__restrict__ sc,
                                                           const uint32_t *__restrict__ qz, uint16_t *__restrict__ y,
-                                                          uint64_t *__restrict__ ws, int M, int N, int K, int lgG) {
+                                                          uint64_t *__restrict__ ws, int M, int N, int K, int lgG,
+                                                          int sep) {
     constexpr int ROWS = 16 * MT, COLS = 128;
     // one parked ROWS x COLS tile per wave (128 KB at 4 row tiles)
     __shared__ __attribute__((aligned(16))) float red[WV * ROWS * COLS];
@@ -357,18 +366,21 @@ __global__ __launch_bounds__(64 * WV, 1) void w4a16_stream(const uint16_t *__res
     // passes with one or two waves at work in each.)
     park(wave);
     __syncthreads();
-    tile_store_or_exchange<64 * WV, DT, ROWS, COLS, WV>(red, y, ws, M, N, tile, S);
+    tile_store_or_exchange<64 * WV, DT, ROWS, COLS, WV>(red, y, ws, M, N, tile, S, sep);
 }
 
 template <int MT, int CS, int DT, bool SYM>
 static hipError_t launch_stream_t(const W4A16Args &a, const W4A16Plan &p, hipStream_t st) {
     constexpr int WV = kStreamWaves(MT);
     if (p.waves != WV || (p.splits > 1 && p.acc == nullptr)) return hipErrorInvalidValue;
+    const int sep = split_reduce_apart(p.splits, 16 * MT);
     hipLaunchKernelGGL((w4a16_stream<MT, CS, WV, DT, SYM>), dim3(p.tiles_n, p.splits), dim3(64 * WV), 0, st,
                        (const uint16_t *)a.x, (const uint32_t *)a.qweight, (const uint16_t *)a.scales,
                        (const uint32_t *)a.qzeros, (uint16_t *)a.y, p.acc, (int)a.M, (int)a.N, (int)a.K,
-                       __builtin_ctz((unsigned)a.G));
-    return hipGetLastError();
+                       __builtin_ctz((unsigned)a.G), sep);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !sep) return e;
+    return launch_w4a16_split_reduce(a, p, p.tiles_n, st);
 }
 
 template <int MT, int CS>
