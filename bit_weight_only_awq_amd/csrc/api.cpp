@@ -313,9 +313,16 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         // a K split nor a split group: the X bytes copied per multiply-add
         // halve.  Measured at M = 2048: (4096, 14336) 266 -> 252 us, the
         // Llama-3-8B qkv layer 137 -> 125 us, its gate/up layer unchanged.
+        // Not where the 128-column tiles spread over the CUs at least 1.25x
+        // more evenly (tiles / (CUs x tiles on the busiest CU)): the Llama-3-8B
+        // qkv layer at M = 4096, 384 wide tiles (0.75) against 768 (1.0),
+        // 209 -> 195 us; at 1.14x (gate/up at M = 2048, 896 against 1792)
+        // the two are level.
         p.wn = 4;
         const int64_t wide_tiles = cdiv(N, 256) * p.tiles_m;
-        if (p.mt == 16 && p.ksplit == 1 && p.splits == 1 && N >= 256 && wide_tiles > cus / 2) {
+        const int64_t wide_rounds = cdiv(wide_tiles, cus), narrow_rounds = cdiv(tiles, cus);
+        const bool wide_even = 5 * wide_tiles * narrow_rounds >= 4 * tiles * wide_rounds;
+        if (p.mt == 16 && p.ksplit == 1 && p.splits == 1 && N >= 256 && wide_tiles > cus / 2 && wide_even) {
             p.wn = 8;
             p.tiles_n = (int)cdiv(N, 256);
         }

@@ -284,6 +284,26 @@ def test_gemm_k_split_rule():
         assert p.workspace_bytes == (0 if s == 1 else L.lib().awq_workspace_bytes(gemm, M, N, K, 128, 0))
 
 
+def test_gemm_wide_tile_rule():
+    """256-column tiles for the LDS GEMM where they still give more than half
+    the CUs a tile, without K splits or wave groups, unless the 128-column
+    tiles spread over the CUs at least 1.25x more evenly."""
+    gemm = L.AWQ_OP_GEMM_W4A16
+    want = {  # (M, N, K): (tile columns, tiles, wave groups)
+        (2048, 6144, 4096): (256, 192, 1),    # qkv: 192 wide tiles (0.75) against 384 (0.75)
+        (4096, 6144, 4096): (128, 768, 1),    # qkv: 384 wide tiles (0.75) against 768 (1.0)
+        (2048, 28672, 4096): (256, 896, 1),   # gate/up: 0.875 against 1.0, under 1.25x
+        (4096, 28672, 4096): (256, 1792, 1),  # gate/up: even either way
+        (4096, 4096, 4096): (256, 256, 1),    # o: one wide tile per CU
+        (2048, 14336, 4096): (256, 448, 1),   # the (4096, 14336) target
+        (2048, 4096, 4096): (128, 256, 2),    # o: 128 wide tiles would idle half the CUs
+    }
+    for (M, N, K), (cols, tiles, ks) in want.items():
+        p = _plan(gemm, M, N, K, 128, cus=256)
+        assert (p.kernel, p.row_tiles, p.splits) == (3, 16, 1), (M, N, K)
+        assert (p.tile_cols, p.tiles_n * p.tiles_m, p.ksplit) == (cols, tiles, ks), (M, N, K)
+
+
 def test_split_caps_of_the_atomic_kernels():
     """Kernels that reduce K splits through per-element counting atomics cap
     their splits as M grows: the skinny W4A8 kernels (int8 and INT4-FP8) at

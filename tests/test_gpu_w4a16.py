@@ -121,6 +121,7 @@ MAIN_TILE_CASES = [
     (2048, 4096, 8192, 0, (16, 1, 1, 256)),  # 256 tiles of 256 x 256: the large-M configuration
     (2200, 4096, 4384, 0, (16, 1, 1, 256)),  # the same, ragged: last row tile 152 rows, last column tile 32
     (2048, 4096, 4096, 0, (16, 2, 1, 128)),  # 256 tiles of 256 x 128: two wave groups split K in the workgroup
+    (4096, 4096, 6144, 0, (16, 1, 1, 128)),  # 768 tiles of 256 x 128: more even over the CUs than 384 wide ones
     (2048, 4096, 8192, 2, (16, 1, 2, 128)),  # K split through partial tiles
     (2048, 4096, 4096, 3, (16, 1, 3, 128)),  # three splits, 64 stages (uneven)
     (1024, 4096, 4096, 0, (8, 2, 1, 128)),   # 128-row tiles where 256-row ones would leave CUs idle
