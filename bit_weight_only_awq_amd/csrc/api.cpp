@@ -38,11 +38,6 @@ static int64_t skinny_splits(int64_t s, int64_t M, int64_t N, int64_t K) {
 // The W4A16 LDS GEMM takes M above 64 (the decode kernel takes M <= 8, the
 // streaming kernel 8 < M <= 64).
 static constexpr int64_t kW16LdsMinM = 64;
-// The W4A8 GEMM's 128 x 256 tiles (8-wave workgroups, two per CU) are used
-// whenever there are at least as many as CUs; with fewer, the 128 x 128 tiles
-// give more workgroups before a K split is needed (measured: M = 512 on
-// (4096, 14336) takes 44 us on 448 narrow tiles, 82 us on 224 wide ones split
-// in two).
 // Largest W4A8 K: the kernels multiply int8 activations (down to -128) by
 // int8 weight bytes 16 q (down to -128), so |acc| <= 2^14 K must stay below
 // 2^31: K < 2^17, and K % 64 == 0 makes that K <= 131008.
@@ -389,10 +384,14 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d)
                            (G <= 0 || (K / G) * N * 2 < (int64_t(1) << 31));
     if (M >= 128 && fits_rsrc) {
         // LDS-pipelined int8 GEMM, K in stages of 64: 128 x 256 workgroup
-        // tiles (8 waves) when there are enough of them, else 128 x 128 (4 waves)
+        // tiles (8 waves) where more than half the CUs get one, else 128 x 128
+        // (4 waves).  Measured at M = 384..768: (4096, 14336) at M = 384, 168
+        // wide tiles, 34.7 -> 30.6 us; the QQQ shape at M = 768, 192 of them,
+        // 145 -> 128 us; with 128 (the QQQ shape at M = 512) the narrow tiles
+        // win, 97.6 against 107.7.
         p.kind = 2;
         const int64_t wide = cdiv(N, 256) * cdiv(M, 128);
-        p.blk = wide >= cus ? 2 : 1;
+        p.blk = 2 * wide > cus ? 2 : 1;
         // no more wide tiles than CUs: two groups of 8 waves per workgroup
         // split K inside it (four waves per SIMD instead of two)
         p.ksplit = p.blk == 2 && wide <= cus && T >= 8 ? 2 : 1;
@@ -400,11 +399,20 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d)
         p.tiles_n = (int)cdiv(N, 128 * p.blk);
         p.tiles_m = (int)cdiv(M, 128);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
-        // (more splits measured slower at M = 128..512: every split adds an
-        // M x N int32 partial tile written, read back and cleared)
+        // K splits for the narrow tiles where they leave CUs idle: every split
+        // adds an M x N int32 partial tile written, read back and cleared, so
+        // short K (under 256 stages) takes only whole multiples of the tiles
+        // that fit (CUs / tiles, rounded down) and long K rounds up; at most
+        // 4.  Measured (separate reduction): (4096, 4096) at M = 128 21.0 ->
+        // 16.2 us (4 splits; 8: 20.9), at M = 768 1 split 24.3 against 2 30.5;
+        // (4096, 14336) at M = 256 25.4 against 2 splits 32.6; the QQQ shape
+        // (K = 21760) at M = 128 84 -> 36 us (4), at M = 384 89.3 -> 84.9 (2).
         int64_t s = 1;
-        if (tiles < cus) s = std::min<int64_t>(cdiv(cus, tiles), std::max<int64_t>(1, T / 4));
-        p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
+        if (p.blk == 1 && tiles < cus) {
+            s = T >= 256 ? cdiv(cus, tiles) : cus / tiles;
+            s = std::min<int64_t>({s, 4, std::max<int64_t>(1, T / 16)});
+        }
+        p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplitK));
     }
     (void)tiles;
     // the small-M kernel (M <= 64) keeps one counting atomic per output

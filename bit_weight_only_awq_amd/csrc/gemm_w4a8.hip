@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * NW * KS, 2 / KS) void w4a8_gemm_lds(const int8
                                                        const float *__restrict__ s1, const uint16_t *__restrict__ s2,
                                                        const uint16_t *__restrict__ s3, uint16_t *__restrict__ y,
                                                        int32_t *__restrict__ acc_out, uint64_t *__restrict__ acc64,
-                                                       int M, int N, int K, int G, int S) {
+                                                       int M, int N, int K, int G, int S, int sep) {
     using L = W8Layout<NW, GROUP>;
     constexpr int W8_N = L::WN;
     static_assert(KS * L::LDS >= KS * NW * 8 * 64 * 16, "the K-split handover fits in the rings");
@@ -291,8 +291,10 @@ __global__ __launch_bounds__(64 * NW * KS, 2 / KS) void w4a8_gemm_lds(const int8
             }
         return;
     }
-    // Split-K by partial tiles exchanged through agent-scope atomics
-    // (device.hpp); int32 partials, so the sum is exact in any order.
+    // Split-K by partial tiles (int32, so the sum is exact in any order):
+    // sep = 1, plain 16-byte stores summed by w4a8_split_reduce after the
+    // kernel; sep = 0, exchanged through agent-scope atomics (device.hpp) and
+    // summed by the tile's last split.
     uint32_t *const cnt = (uint32_t *)acc64 + (tn + gridDim.x * tm);
     uint64_t *const part = (uint64_t *)((char *)acc64 + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
     const size_t slot = (size_t)M * N / 2;  // 64-bit words per split
@@ -303,10 +305,14 @@ __global__ __launch_bounds__(64 * NW * KS, 2 / KS) void w4a8_gemm_lds(const int8
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-                if (m < M) part_put(at(split, m), (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
+                const i32x4 v = (i32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                if (m < M) {
+                    if (sep) *(i32x4 *)at(split, m) = v;
+                    else part_put(at(split, m), v);
+                }
             }
     }
-    if (!split_tile_last_atomic(cnt, S) || !col_ok) return;
+    if (sep || !split_tile_last_atomic(cnt, S) || !col_ok) return;
     // the last split sums the partials one row tile (4 of the lane's rows)
     // at a time, then clears them
     static_for<4>([&](auto bc) {
@@ -323,13 +329,58 @@ __global__ __launch_bounds__(64 * NW * KS, 2 / KS) void w4a8_gemm_lds(const int8
     });
 }
 
+// The K splits' int32 partials ([S][M][N] after the tile counters) summed
+// over the whole GPU, one thread per 4 consecutive outputs, with the GEMM's
+// epilogue (the x16 of per-channel weights undone, y = acc s1 s2 rounded
+// once, the optional acc_out), then cleared.  A tile's last split would
+// otherwise move all S partial tiles through one CU at the rate it moves
+// device-coherent data (about 50 GB/s).
+template <bool GROUP, int DT>
+__global__ __launch_bounds__(256) void w4a8_split_reduce(i32x4 *__restrict__ part, const float *__restrict__ s1,
+                                                         const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
+                                                         int32_t *__restrict__ acc_out, int N, int64_t quads, int S) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= quads) return;
+    i32x4 *const p = part + q;
+    i32x4 v = (i32x4){0, 0, 0, 0};
+    constexpr int kB = 8;
+    for (int s0 = 0; s0 < S; s0 += kB) {
+        i32x4 b[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) b[i] = s0 + i < S ? p[(s0 + i) * quads] : (i32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < kB; ++i) v += b[i];
+    }
+    const int64_t m = 4 * q / N;
+    const int nc = (int)(4 * q - m * N);
+    const float s1m = s1[m];
+    int32_t w[4];
+    uint16_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        w[u] = GROUP ? v[u] : (v[u] >> 4);
+        o[u] = f32_to_out_bits((float)w[u] * s1m * act_bits_to_f32<DT>(s2[nc + u]), DT);
+    }
+    *(u32x2 *)(y + 4 * q) = (u32x2){(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+    if (acc_out) *(i32x4 *)(acc_out + 4 * q) = (i32x4){w[0], w[1], w[2], w[3]};
+    for (int s = 0; s < S; ++s) p[s * quads] = (i32x4){0, 0, 0, 0};
+}
+
 template <int NW, int KS, bool GROUP, int DT>
 static hipError_t launch_lds8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
+    const int sep = p.splits > 1;
     hipLaunchKernelGGL((w4a8_gemm_lds<NW, KS, GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(64 * NW * KS),
                        0, st,
                        a.a8,
                        (const uint32_t *)a.b, a.s1, (const uint16_t *)a.s2, (const uint16_t *)a.s3,
-                       (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits);
+                       (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits, sep);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !sep) return e;
+    if (p.acc == nullptr || (a.M * a.N) % 4) return hipErrorInvalidValue;
+    i32x4 *const part = (i32x4 *)((char *)p.acc + split_counters_bytes((int64_t)p.tiles_n * p.tiles_m));
+    const int64_t quads = a.M * a.N / 4;
+    hipLaunchKernelGGL((w4a8_split_reduce<GROUP, DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, part,
+                       a.s1, (const uint16_t *)a.s2, (uint16_t *)a.y, a.acc_out, (int)a.N, quads, p.splits);
     return hipGetLastError();
 }
 

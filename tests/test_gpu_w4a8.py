@@ -185,7 +185,10 @@ LDS_CASES = [
     (2048, 4096, 4096, -1, (16, 16, 2, 1)),   # one 128 x 256 tile per CU: K split inside the workgroup
     (1024, 4096, 4096, 128, (32, 8, 1, 1)),   # 128 x 128 tiles (4 waves), per group
     (256, 4096, 4096, -1, (32, 2, 1, 4)),     # few tiles: K split through int32 partial tiles
-    (300, 4096, 1032, 64, (9, 3, 1, 10)),     # ragged rows and columns, split, per group
+    (300, 4096, 1032, 64, (9, 3, 1, 4)),      # ragged rows and columns, split, per group
+    (128, 4096, 14336, -1, (112, 1, 1, 2)),   # short K: the splits that fit whole (256 // 112)
+    (384, 21760, 8192, -1, (64, 3, 1, 2)),    # long K: rounded up (192 tiles)
+    (384, 4096, 14336, 128, (56, 3, 2, 1)),   # 168 wide tiles: more than half the CUs
 ]
 
 
