@@ -460,8 +460,15 @@ W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d) {
         p.tilered = 1;
         p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(tiles, p.splits, M, N) : 0;
     }
-    // LDS-pipelined GEMM from 128 rows: 128 x 256 tiles, 128-k stages; a K
-    // split through per-tile fp32 partials only when tiles are fewer than CUs.
+    // LDS-pipelined GEMM from 128 rows: 128 x 256 tiles (one workgroup per
+    // CU), 128-k stages; a K split through per-tile fp32 partials where tiles
+    // are fewer than CUs.  Every split adds an M x N partial tile written,
+    // read back and cleared, so the splits are those that fit in one round
+    // (CUs / tiles), at most K / 1024, K / (4 M) and 8.  Measured (separate
+    // reduction) at M = 128..1024: (4096, 4096) at M = 128 64.2 -> 18.8 us (4
+    // splits), at M = 512 28.2 (2) against 31.3 (4), at M = 1024 33.4 (1)
+    // against 36.7 (2); (14336, 4096) at M = 128 120.7 -> 25.7 (8); the QQQ
+    // shape at M = 256 87.3 -> 57.1 (4), at M = 768 181 -> 134 (1).
     // (Buffer-descriptor copies address the codes and the packed words with
     // 32-bit offsets.)
     const bool fits_rsrc = M * K < (int64_t(1) << 31) && (K / 8) * N * 4 < (int64_t(1) << 31);
@@ -473,8 +480,8 @@ W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d) {
         p.tiles_m = (int)cdiv(M, 128);
         tiles = (int64_t)p.tiles_n * p.tiles_m;
         int64_t s = 1;
-        if (tiles < cus) s = std::min<int64_t>(cdiv(cus, tiles), std::max<int64_t>(1, T / 4));
-        p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
+        if (tiles < cus) s = std::min<int64_t>({cus / tiles, K / 1024, K / (4 * M), 8});
+        p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, kMaxSplitK));
         p.tilered = 1;
         p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(tiles, p.splits, M, N) : 0;
     }

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(64 * F8_NW, 1) void w4a8_fp8_gemm_lds(const uint8_t
                                                                   uint16_t *__restrict__ y,
                                                                   float *__restrict__ acc_out,
                                                                   uint64_t *__restrict__ ws, int M, int N, int K,
-                                                                  int S) {
+                                                                  int S, int sep) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[F8_LDS];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -201,8 +201,10 @@ __global__ __launch_bounds__(64 * F8_NW, 1) void w4a8_fp8_gemm_lds(const uint8_t
             }
         return;
     }
-    // Split-K by partial tiles exchanged through agent-scope atomics
-    // (device.hpp), fp32, summed in split order.
+    // Split-K by fp32 partial tiles, summed in split order: sep = 1, plain
+    // 16-byte stores summed by w4a8_fp8_split_reduce after the kernel;
+    // sep = 0, exchanged through agent-scope atomics (device.hpp) and summed
+    // by the tile's last split.
     uint32_t *const cnt = (uint32_t *)ws + (tn + gridDim.x * tm);
     uint64_t *const part = (uint64_t *)((char *)ws + split_counters_bytes((int64_t)gridDim.x * gridDim.y));
     const size_t slot = (size_t)M * N / 2;  // 64-bit words per split
@@ -213,10 +215,14 @@ __global__ __launch_bounds__(64 * F8_NW, 1) void w4a8_fp8_gemm_lds(const uint8_t
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m0 + wm * 64 + 16 * mt + 4 * gq + r;
-                if (m < M) part_put(at(split, m), (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]});
+                const f32x4 v = (f32x4){acc[mt][0][r], acc[mt][1][r], acc[mt][2][r], acc[mt][3][r]};
+                if (m < M) {
+                    if (sep) *(f32x4 *)at(split, m) = v;
+                    else part_put(at(split, m), v);
+                }
             }
     }
-    if (!split_tile_last_atomic(cnt, S) || !col_ok) return;
+    if (sep || !split_tile_last_atomic(cnt, S) || !col_ok) return;
     static_for<4>([&](auto bc) {
         constexpr int MT0 = decltype(bc)::value;
         auto row = [&](int r) { return m0 + wm * 64 + 16 * MT0 + 4 * gq + r; };
@@ -231,12 +237,59 @@ __global__ __launch_bounds__(64 * F8_NW, 1) void w4a8_fp8_gemm_lds(const uint8_t
     });
 }
 
+// The K splits' fp32 partials ([S][M][N] after the tile counters) summed in
+// split order over the whole GPU, one thread per 4 consecutive outputs, with
+// the GEMM's epilogue (sum a q = 512 t - 8 sum_k a, one rounding; y = that
+// s1 s2 rounded once; the optional acc_out), then cleared.  The same sums as
+// a tile's last split would form, without moving every partial through one
+// CU at the rate it moves device-coherent data (about 50 GB/s).
+template <int DT>
+__global__ __launch_bounds__(256) void w4a8_fp8_split_reduce(f32x4 *__restrict__ part, const float *__restrict__ s1,
+                                                             const float *__restrict__ asum,
+                                                             const uint16_t *__restrict__ s2, uint16_t *__restrict__ y,
+                                                             float *__restrict__ acc_out, int N, int64_t quads, int S) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= quads) return;
+    f32x4 *const p = part + q;
+    f32x4 v = (f32x4){0.f, 0.f, 0.f, 0.f};
+    constexpr int kB = 8;
+    for (int s0 = 0; s0 < S; s0 += kB) {
+        f32x4 b[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) b[i] = s0 + i < S ? p[(s0 + i) * quads] : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            if (s0 + i < S) v += b[i];
+    }
+    const int64_t m = 4 * q / N;
+    const int nc = (int)(4 * q - m * N);
+    const float s1m = s1[m], am = -8.0f * asum[m];
+    float d[4];
+    uint16_t o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        d[u] = __builtin_fmaf(512.0f, v[u], am);
+        o[u] = f32_to_out_bits(d[u] * s1m * act_bits_to_f32<DT>(s2[nc + u]), DT);
+    }
+    *(u32x2 *)(y + 4 * q) = (u32x2){(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+    if (acc_out) *(f32x4 *)(acc_out + 4 * q) = (f32x4){d[0], d[1], d[2], d[3]};
+    for (int s = 0; s < S; ++s) p[s * quads] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
 template <int DT>
 static hipError_t launch_fp8_lds_t(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st) {
     if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
+    const int sep = p.splits > 1;
     hipLaunchKernelGGL((w4a8_fp8_gemm_lds<DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(64 * F8_NW), 0, st, g.a,
                        (const uint32_t *)g.b, g.s1, g.asum, (const uint16_t *)g.s2, (uint16_t *)g.y, g.acc_out, p.acc,
-                       (int)g.M, (int)g.N, (int)g.K, p.splits);
+                       (int)g.M, (int)g.N, (int)g.K, p.splits, sep);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !sep) return e;
+    if ((g.M * g.N) % 4) return hipErrorInvalidValue;
+    f32x4 *const part = (f32x4 *)((char *)p.acc + split_counters_bytes((int64_t)p.tiles_n * p.tiles_m));
+    const int64_t quads = g.M * g.N / 4;
+    hipLaunchKernelGGL((w4a8_fp8_split_reduce<DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, part,
+                       g.s1, g.asum, (const uint16_t *)g.s2, (uint16_t *)g.y, g.acc_out, (int)g.N, quads, p.splits);
     return hipGetLastError();
 }
 

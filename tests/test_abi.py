@@ -362,6 +362,11 @@ def test_fp8_validation():
     assert (p.tiles_n, p.tiles_m, p.splits, p.workspace_bytes) == (32, 8, 1, 0)
     p = _plan(fp8, 256, 8192, 21760, -1)
     assert p.tiles_n * p.tiles_m == 64 and p.splits == 4
+    # K splits: those that fit in one round, at most K / 1024, K / (4 M) and 8
+    want = {(128, 4096, 4096): 4, (512, 4096, 4096): 2, (1024, 4096, 4096): 1, (128, 4096, 14336): 8,
+            (384, 4096, 14336): 5, (128, 8192, 21760): 8, (768, 8192, 21760): 1, (256, 14336, 4096): 2}
+    for (M, N, K), s in want.items():
+        assert _plan(fp8, M, N, K, -1).splits == s, (M, N, K)
     assert p.workspace_bytes == lib.awq_workspace_bytes(fp8, 256, 8192, 21760, -1, 0) > 256 * 8192 * 4 * 4
     assert lib.w4a8_fp8_quant_act(None, A, A, A, 1, 16, 0, None) == L.AWQ_EINVAL
     assert lib.w4a8_fp8_quant_act(A, A, A, None, 1, 16, 0, None) == L.AWQ_EINVAL

@@ -93,7 +93,9 @@ def test_fp8_qqq_shape(M, dt):
                                    (5, 128, 8), (17, 256, 136), (33, 384, 520), (65, 512, 264), (129, 512, 1032),
                                    (300, 4096, 1032), (7, 130944, 64),
                                    # the skinny kernel with one split (the atomic cap) and with five
-                                   (64, 4096, 14336), (48, 4096, 4096)])
+                                   (64, 4096, 14336), (48, 4096, 4096),
+                                   # the LDS GEMM's K splits: 8 of 14 stages, 4 of 8, 5 of 112 (uneven)
+                                   (128, 14336, 4096), (256, 4096, 4096), (384, 14336, 4096)])
 def test_fp8_shapes(M, K, N):
     rows = None if M <= 300 else sample_rows(M, seed=N)
     _gemm_check(M, K, N, 0, rows=rows)
