@@ -35,6 +35,9 @@ static int64_t skinny_splits(int64_t s, int64_t M, int64_t N, int64_t K) {
     const double cap = 1048576.0 * std::sqrt((double)K / 4096.0) / ((double)M * (double)N);
     return std::max<int64_t>(1, std::min<int64_t>(s, (int64_t)cap));
 }
+// The W4A8 LDS GEMMs take M above 64, and M above 32 where the skinny
+// kernel's plan (p, made first) splits K.
+static bool lds_rows(int64_t M, const W4A8Plan &p) { return M > 64 || (M > 32 && p.kind == 0 && p.splits > 1); }
 // The W4A16 LDS GEMM takes M above 64 (the decode kernel takes M <= 8, the
 // streaming kernel 8 < M <= 64).
 static constexpr int64_t kW16LdsMinM = 64;
@@ -382,7 +385,16 @@ W4A8Plan plan_w4a8(int64_t M, int64_t N, int64_t K, int G, const DeviceProps &d)
     // 32-bit offsets
     const bool fits_rsrc = M * K < (int64_t(1) << 31) && (K / 8) * N * 4 < (int64_t(1) << 31) &&
                            (G <= 0 || (K / G) * N * 2 < (int64_t(1) << 31));
-    if (M >= 128 && fits_rsrc) {
+    // From 65 rows the LDS-pipelined GEMM (its last row tile padded): the
+    // register-tiled kernel above keeps only shapes past its 32-bit offsets.
+    // Measured at M = 65..127 against it: (4096, 14336) 45-50 -> 22-23 us,
+    // the QQQ shape 67-71 -> 37-38 us (the INT4-FP8 GEMM the same).  From 33
+    // rows also wherever the skinny kernel would split K (its per-element
+    // atomics grow with S M N); cache-cold at M = 48 / 64: (4096, 4096)
+    // 17.5 / 20.7 -> 13.3 / 14.2 us, the QQQ shape 41.2 / 49.4 -> 35.6 /
+    // 36.0, (14336, 4096) 24.0 / 29.8 -> 24.1 / 24.8; with one split
+    // ((4096, 14336)) the two are level (19.3 / 21.2 against 19.6 / 20.7).
+    if (lds_rows(M, p) && fits_rsrc) {
         // LDS-pipelined int8 GEMM, K in stages of 64: 128 x 256 workgroup
         // tiles (8 waves) where more than half the CUs get one, else 128 x 128
         // (4 waves).  Measured at M = 384..768: (4096, 14336) at M = 384, 168
@@ -460,7 +472,7 @@ W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d) {
         p.tilered = 1;
         p.workspace_bytes = p.splits > 1 ? (size_t)split_tiles_bytes(tiles, p.splits, M, N) : 0;
     }
-    // LDS-pipelined GEMM from 128 rows: 128 x 256 tiles (one workgroup per
+    // LDS-pipelined GEMM from 65 rows (as in the int8 planner): 128 x 256 tiles (one workgroup per
     // CU), 128-k stages; a K split through per-tile fp32 partials where tiles
     // are fewer than CUs.  Every split adds an M x N partial tile written,
     // read back and cleared, so the splits are those that fit in one round
@@ -472,7 +484,7 @@ W4A8Plan plan_w4a8_fp8(int64_t M, int64_t N, int64_t K, const DeviceProps &d) {
     // (Buffer-descriptor copies address the codes and the packed words with
     // 32-bit offsets.)
     const bool fits_rsrc = M * K < (int64_t(1) << 31) && (K / 8) * N * 4 < (int64_t(1) << 31);
-    if (M >= 128 && fits_rsrc) {
+    if (lds_rows(M, p) && fits_rsrc) {
         p.kind = 2;
         p.blk = 2;
         p.mt = 4;

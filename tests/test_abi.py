@@ -312,12 +312,15 @@ def test_split_caps_of_the_atomic_kernels():
     for op in (L.AWQ_OP_W4A8_GEMM, L.AWQ_OP_W4A8_FP8_GEMM):
         want = {  # (M, N, K): splits on a whole MI355X
             (1, 14336, 4096): 5, (32, 14336, 4096): 2, (48, 14336, 4096): 1, (64, 14336, 4096): 1,
-            (48, 4096, 4096): 5, (64, 4096, 4096): 4, (64, 8192, 21760): 4, (16, 8192, 21760): 8,
+            (32, 4096, 4096): 8, (16, 8192, 21760): 8, (32, 8192, 21760): 4,
         }
         for (M, N, K), s in want.items():
             p = _plan(op, M, N, K, -1, cus=256)
             assert (p.kernel, p.splits) == (0, s), (op, M, N, K, p.splits)
             assert p.workspace_bytes == (0 if s == 1 else M * N * 8)
+        # from 33 rows the LDS GEMM wherever the skinny kernel would split K
+        for M, N, K in ((48, 4096, 4096), (64, 4096, 4096), (64, 8192, 21760), (33, 4096, 14336)):
+            assert _plan(op, M, N, K, -1, cus=256).kernel == 2, (op, M, N, K)
     gemv = L.AWQ_OP_GEMV_W4A16
     # Llama-2-7B qkv (4096 x 12288): 48 column tiles; 16 splits of 4 waves at
     # M = 1, 4 splits of 8 waves (128-k chunks) at M = 8; gate/up (4096 x
@@ -353,11 +356,15 @@ def test_fp8_validation():
     assert g() == L.AWQ_EWORKSPACE                  # split-K needs its workspace
     assert lib.awq_workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, 1, 8192, 21760, -1, 0) == 8192 * 8
     assert lib.awq_workspace_bytes(L.AWQ_OP_W4A8_FP8_GEMM, 1, 8192, 21824, -1, 0) == 0
-    # the kernels by M: skinny up to 64 rows, register-tiled below 128, the
-    # LDS-pipelined GEMM (128 x 256 tiles) from 128, split only with fewer
-    # tiles than CUs
+    # the kernels by M: skinny up to 64 rows (up to 32 where it would split
+    # K), the LDS-pipelined GEMM (128 x 256 tiles) above, split only with
+    # fewer tiles than CUs
     fp8 = L.AWQ_OP_W4A8_FP8_GEMM
-    assert [_plan(fp8, M, 8192, 21760, -1).kernel for M in (64, 100, 128, 1024)] == [0, 1, 2, 2]
+    assert [_plan(fp8, M, 8192, 21760, -1).kernel for M in (32, 64, 65, 100, 128, 1024)] == [0, 2, 2, 2, 2, 2]
+    # the register-tiled kernel only past the LDS GEMM's 32-bit offsets
+    assert _plan(fp8, 16401, 64, 130944, -1).kernel == 1
+    assert _plan(L.AWQ_OP_W4A8_GEMM, 16400, 64, 131008, -1).kernel == 1
+    assert _plan(L.AWQ_OP_W4A8_GEMM, 100, 8192, 21760, -1).kernel == 2
     p = _plan(fp8, 1024, 8192, 21760, -1)
     assert (p.tiles_n, p.tiles_m, p.splits, p.workspace_bytes) == (32, 8, 1, 0)
     p = _plan(fp8, 256, 8192, 21760, -1)

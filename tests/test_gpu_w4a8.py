@@ -217,6 +217,34 @@ def test_lds_gemm_output_bit_exact(M, K, N, G, plan):
     assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), int((got != exp).sum())
 
 
+def test_register_tiled_kernel_past_the_lds_offsets():
+    """Activation codes of more than 2^31 bytes (M = 16400, K = 131008: 2.1 GB)
+    run the register-tiled kernel, since the LDS GEMM addresses them with
+    32-bit offsets.  Codes drawn on the device from a seeded generator;
+    sampled rows (both ends, one per 256-row block) against the oracle:
+    accumulators exact, fp16 output bit for bit (power-of-two s1 and s2)."""
+    M, K, N = 16400, 131008, 64
+    info = awq.plan_info(awq.AWQ_OP_W4A8_GEMM, M, N, K, -1)
+    assert info["kernel"] == 1, info
+    gen = torch.Generator(device=dev()).manual_seed(16400)
+    a8 = torch.randint(-128, 128, (M, K), generator=gen, device=dev(), dtype=torch.int8)
+    g = torch.Generator().manual_seed(3)
+    s1 = torch.pow(2.0, -torch.randint(5, 12, (M,), generator=g).to(torch.float32))
+    s2 = torch.pow(2.0, -torch.randint(3, 9, (N,), generator=g).to(torch.float32)).to(torch.float16)
+    c = synthgen.w4a8_case(1, K, N, -1)
+    y, acc = awq.w4a8_gemm(a8, *to_dev(c.b, s1, s2), want_acc=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, seed=5, tile=256)
+    ra = a8[torch.as_tensor(rows, device=dev())].cpu().numpy()
+    del a8
+    eacc, y64 = orc().w4a8(ra, c.b, s1.numpy()[rows], s2, None, -1, nthreads=THREADS)
+    assert np.abs(eacc).max() < 2 ** 24
+    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), eacc)
+    exp = torch.from_numpy(y64).to(torch.float16)
+    got = y.cpu()[torch.as_tensor(rows)]
+    assert torch.equal(got.view(torch.int16), exp.view(torch.int16)), int((got != exp).sum())
+
+
 def test_w4a8_largest_k_all_minimum():
     """K = 131008, the largest K the library accepts: a row of -2^-14 quantises
     to s1 = 2^-21 and a8 = -128 everywhere, and with every weight -8 the

@@ -101,6 +101,40 @@ def test_fp8_shapes(M, K, N):
     _gemm_check(M, K, N, 0, rows=rows)
 
 
+def test_fp8_register_tiled_kernel_past_the_lds_offsets():
+    """Activation codes of more than 2^31 bytes (M = 16401, K = 130944) run
+    the register-tiled kernel, since the LDS GEMM addresses them with 32-bit
+    offsets.  Activations drawn on the device from a seeded generator and
+    quantised there; sampled rows (both ends, one per 256-row block) against
+    the oracle: codes, s1 and row sums bit-exact, the sums within the fp32
+    accumulation bound, the output within the fp16 bar."""
+    M, K, N = 16401, 130944, 64
+    info = awq.plan_info(awq.AWQ_OP_W4A8_FP8_GEMM, M, N, K, -1)
+    assert info["kernel"] == 1, info
+    gen = torch.Generator(device=dev()).manual_seed(16401)
+    x = torch.randn((M, K), generator=gen, device=dev(), dtype=torch.float16)
+    c = synthgen.w4a8_case(1, K, N, -1)
+    b, s2 = to_dev(c.b, c.s2)
+    a, s1, asum = awq.quant_act_fp8(x)
+    y, acc = awq.w4a8_fp8_gemm(a, b, s1, asum, s2, want_acc=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, seed=6, tile=256)
+    ridx = torch.as_tensor(rows, device=dev())
+    xr, ar = x[ridx].cpu(), a[ridx].cpu().numpy()
+    del x, a
+    ea, es1, esum = orc().quant_act_fp8(xr, 0)
+    assert np.array_equal(ar, ea)
+    assert np.array_equal(s1.cpu().numpy()[rows].view(np.uint32), es1.view(np.uint32))
+    assert np.array_equal(asum.cpu().numpy()[rows].view(np.uint32), esum.view(np.uint32))
+    eacc, y64 = orc().w4a8_fp8(ea, c.b, es1, c.s2, 0)
+    av = np.abs(torch.from_numpy(ea).view(torch.float8_e4m3fn).double().numpy())
+    bound = K * 2.0 ** -24 * 15 * av.sum(axis=1, keepdims=True) + 8 * np.abs(esum[:, None]) * 2.0 ** -23 \
+        + np.abs(eacc) * 2.0 ** -23
+    gacc = acc.cpu().numpy()[rows].astype(np.float64)
+    assert np.all(np.abs(gacc - eacc) <= bound), float(np.max(np.abs(gacc - eacc) - bound))
+    check_fp(y.cpu()[torch.as_tensor(rows)], y64, "f16", f"fp8 M={M} K={K} N={N}")
+
+
 def test_fp8_deterministic():
     c = synthgen.w4a8_case(4, 21760, 8192, -1)
     x, b, s2 = to_dev(c.x, c.b, c.s2)
