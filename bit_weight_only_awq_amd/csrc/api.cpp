@@ -299,6 +299,12 @@ W4A16Plan plan_w4a16(int64_t M, int64_t N, int64_t K, int G, int split_k, int dt
         int64_t s = std::min<int64_t>(smax, std::max<int64_t>(1, cus / tiles));
         if (s == 1 && p.mt == 8 && stages >= 128 && tiles <= cus)
             s = std::min<int64_t>(4, std::max<int64_t>(1, 3 * cus / tiles));
+        // and where the two-group workgroups would leave more than an eighth
+        // of the CUs idle, single-group splits that give each CU three: down
+        // at M = 384, 96 tiles (192 two-group workgroups), 80.7 -> 68.0 us
+        // with 8 splits (768 workgroups)
+        else if (p.mt == 8 && stages >= 128 && 8 * tiles * s < 7 * cus)
+            s = std::max<int64_t>(s, std::min<int64_t>(smax, 3 * cus / tiles));
         if (split_k > 0) s = std::min<int64_t>(split_k, stages);
         p.splits = (int)std::min<int64_t>(s, kMaxSplitK);
         // a split's partials are addressed as one buffer of M x N floats

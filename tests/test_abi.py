@@ -275,6 +275,7 @@ def test_gemm_k_split_rule():
         (96, 6144, 4096): (8, 48, 4, 2),      # qkv at 96 rows: 5 capped at 64 / 16 stages
         (256, 28672, 4096): (16, 224, 1, 2),  # gate/up: more tiles than half the CUs, no split
         (768, 4096, 14336): (8, 192, 4, 1),   # long K, 192 tiles: 4 single-group splits
+        (384, 4096, 14336): (8, 96, 8, 1),    # long K, 2 two-group splits would idle 64 CUs: 8 single-group
         (1024, 4096, 14336): (8, 256, 3, 1),  # long K, 256 tiles: 3
         (2048, 4096, 14336): (16, 256, 1, 2),  # 256-row tiles: none
     }

@@ -127,6 +127,7 @@ MAIN_TILE_CASES = [
     (1024, 4096, 4096, 0, (8, 2, 1, 128)),   # 128-row tiles where 256-row ones would leave CUs idle
     (512, 14336, 4096, 0, (8, 2, 2, 128)),   # K = 14336: K split and in-workgroup split together
     (768, 14336, 4096, 0, (8, 1, 4, 128)),   # long K on 128-row tiles: four single-group splits
+    (384, 14336, 4096, 0, (8, 1, 8, 128)),   # eight single-group splits where two-group ones idle CUs
     (96, 14336, 4096, 0, (8, 2, 8, 128)),    # eight splits (two load batches in the last workgroup)
     (96, 4096, 4096, 0, (8, 2, 4, 128)),     # below 128 rows: 128-row tiles, K split both ways
     (100, 4096, 6144, 0, (8, 2, 4, 128)),    # the same with a ragged last row tile
