@@ -136,16 +136,20 @@ int awq_repack_v2(const int32_t *qweight_v2, const int32_t *qzeros_v2, int32_t *
  * Workspace rules ([P2]: one workspace per device, reused by every layer):
  *  - it is caller-owned, 16-byte aligned, and may be shared by any number of
  *    calls that are ordered on one stream;
- *  - a split-K fp16 decode GEMV, or a W4A8 call with M <= 64, uses one
- *    64-bit counting accumulator per output element (M x N); the last
- *    contribution to an element writes the output and clears it (the size
- *    returned for the W4A16 calls covers both activation dtypes);
+ *  - a split-K fp16 decode GEMV, or a split-K W4A8 call on the skinny
+ *    kernel (M <= 32), uses one 64-bit counting accumulator per output
+ *    element (M x N); the last contribution to an element writes the output
+ *    and clears it (the size returned for the W4A16 calls covers both
+ *    activation dtypes);
  *  - a split-K bf16 decode GEMV and the GEMM kernels (M > 8 for W4A16,
- *    M > 64 for W4A8) use one 32-bit
+ *    M > 32 for W4A8) use one 32-bit
  *    arrival counter per output tile (padded to 256 bytes) followed by S
  *    partial [M, N] results of 4 bytes each (fp32 for W4A16, int32 for
  *    W4A8); the last workgroup of a tile to arrive adds the S partials in
- *    split order, writes the output, clears them and re-arms the counter;
+ *    split order, writes the output, clears them and re-arms the counter --
+ *    or, where the partials are large (always for the W4A8 GEMMs), a second
+ *    kernel enqueued right after the first on the same stream adds them in
+ *    split order, writes the output and clears them (counters untouched);
  *  - either way the workspace is zero again after every call;
  *  - it must be zero-filled once when allocated; no per-call clearing is
  *    needed;
@@ -198,11 +202,12 @@ int awq_plan_info(int op, int64_t M, int64_t N, int64_t K, int group_size, int s
  *            the library, 1 = none, at most min(K/32, 255)).  For M <= 8
  *            the library's decode kernel fixes the K split itself and
  *            ignores split_k.
- * Numerics: M <= 64 -- the exact (q - z) products are summed in fp32 on the
- * matrix cores and scaled by s in fp32 once per chunk (32 to 128 consecutive
- * k inside one group); M > 64 --
- * each weight is dequantised exactly to (q - z) and multiplied by s with one
- * rounding to the activation dtype, products accumulating in fp32.  The
+ * Numerics: M <= 32, and bf16 up to M = 64 -- the exact (q - z) products
+ * are summed in fp32 on the matrix cores and scaled by s in fp32 once per
+ * chunk (32 to 128 consecutive k inside one group); fp16 at 32 < M <= 64
+ * and M > 64 -- each weight is dequantised exactly to (q - z) and multiplied
+ * by s with one rounding to the activation dtype, products accumulating in
+ * fp32.  The
  * output is rounded to nearest even.
  * Errors: AWQ_EINVAL (shapes, pointers, dtype, G), AWQ_EALIGN, AWQ_EWORKSPACE,
  * AWQ_EHIP.
