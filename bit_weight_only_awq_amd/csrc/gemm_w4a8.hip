@@ -369,6 +369,7 @@ __global__ __launch_bounds__(256) void w4a8_split_reduce(i32x4 *__restrict__ par
 template <int NW, int KS, bool GROUP, int DT>
 static hipError_t launch_lds8(const W4A8Args &a, const W4A8Plan &p, hipStream_t st) {
     const int sep = p.splits > 1;
+    if (sep && (p.acc == nullptr || (a.M * a.N) % 4)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((w4a8_gemm_lds<NW, KS, GROUP, DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(64 * NW * KS),
                        0, st,
                        a.a8,
@@ -376,7 +377,6 @@ static hipError_t launch_lds8(const W4A8Args &a, const W4A8Plan &p, hipStream_t 
                        (uint16_t *)a.y, a.acc_out, p.acc, (int)a.M, (int)a.N, (int)a.K, a.G, p.splits, sep);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !sep) return e;
-    if (p.acc == nullptr || (a.M * a.N) % 4) return hipErrorInvalidValue;
     i32x4 *const part = (i32x4 *)((char *)p.acc + split_counters_bytes((int64_t)p.tiles_n * p.tiles_m));
     const int64_t quads = a.M * a.N / 4;
     hipLaunchKernelGGL((w4a8_split_reduce<GROUP, DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, part,

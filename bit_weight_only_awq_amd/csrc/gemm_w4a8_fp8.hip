@@ -278,14 +278,13 @@ __global__ __launch_bounds__(256) void w4a8_fp8_split_reduce(f32x4 *__restrict__
 
 template <int DT>
 static hipError_t launch_fp8_lds_t(const W4A8Fp8Args &g, const W4A8Plan &p, hipStream_t st) {
-    if (p.splits > 1 && p.acc == nullptr) return hipErrorInvalidValue;
     const int sep = p.splits > 1;
+    if (sep && (p.acc == nullptr || (g.M * g.N) % 4)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((w4a8_fp8_gemm_lds<DT>), dim3(p.tiles_n, p.tiles_m, p.splits), dim3(64 * F8_NW), 0, st, g.a,
                        (const uint32_t *)g.b, g.s1, g.asum, (const uint16_t *)g.s2, (uint16_t *)g.y, g.acc_out, p.acc,
                        (int)g.M, (int)g.N, (int)g.K, p.splits, sep);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !sep) return e;
-    if ((g.M * g.N) % 4) return hipErrorInvalidValue;
     f32x4 *const part = (f32x4 *)((char *)p.acc + split_counters_bytes((int64_t)p.tiles_n * p.tiles_m));
     const int64_t quads = g.M * g.N / 4;
     hipLaunchKernelGGL((w4a8_fp8_split_reduce<DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, part,
